@@ -1,0 +1,237 @@
+"""CPU oracle for exact byte-level BPE tokenization (TEST INFRASTRUCTURE ONLY).
+
+Plain, serial reference implementations of what the GPU path computes (TokTier, arXiv 2607.29678:
+F = E* o G -- a leftmost-first pre-tokenizer G, then byte-level BPE E on every piece independently):
+
+* ``pretokenize``  -- G, a hand-written leftmost-first matcher per regex alternative (oracle.c)
+* ``bpe_encode``   -- E, priority-queue BPE over a linked list (oracle.c)
+* ``encode_batch`` -- F over a batch of documents, with per-document ID offsets
+* ``train``        -- the byte-level BPE trainer that produces the merge lists used as inputs
+* ``textbook_bpe`` -- the exhaustive textbook merge loop in pure Python, for pinning E on tiny inputs
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this package; the
+GPU library never does, and the two share no code.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+from . import unicode_classes
+
+FAMILIES = {"gpt2": 1, "cl100k": 2, "o200k": 3}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_BUILD = os.path.join(_HERE, "_build")
+_SO = os.path.join(_BUILD, "liboracle.so")
+_SRC = os.path.join(_HERE, "oracle.c")
+
+_ERRORS = {
+    -1: "invalid UTF-8",
+    -2: "output capacity exceeded",
+    -3: "unknown family",
+    -4: "bad document offsets",
+    -5: "out of memory",
+    -6: "no alternative matched",
+}
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code):
+        self.code = code
+        super().__init__(_ERRORS.get(code, f"oracle error {code}"))
+
+
+def build(force=True):
+    """Compile oracle.c with gcc into oracle/_build/liboracle.so."""
+    os.makedirs(_BUILD, exist_ok=True)
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-shared", "-fPIC", "-o", tmp, _SRC])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        build(force=True)
+    L = ctypes.CDLL(_SO)
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    L.orc_set_classes.argtypes = [u8p, ctypes.c_uint64]
+    L.orc_set_classes.restype = ctypes.c_int
+    L.orc_pretokenize.argtypes = [ctypes.c_int, u8p, ctypes.c_uint64, u64p, ctypes.c_uint32, u64p,
+                                  ctypes.c_uint64]
+    L.orc_pretokenize.restype = ctypes.c_int64
+    L.orc_bpe_new.argtypes = [u32p, ctypes.c_uint32]
+    L.orc_bpe_new.restype = ctypes.c_void_p
+    L.orc_bpe_free.argtypes = [ctypes.c_void_p]
+    L.orc_bpe_free.restype = None
+    L.orc_bpe_encode.argtypes = [ctypes.c_void_p, u8p, u64p, ctypes.c_uint64, u32p, ctypes.c_uint64,
+                                 u32p]
+    L.orc_bpe_encode.restype = ctypes.c_int64
+    L.orc_train.argtypes = [ctypes.c_int, u8p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                            u32p]
+    L.orc_train.restype = ctypes.c_int64
+    L.orc_encode_batch.argtypes = [ctypes.c_int, ctypes.c_void_p, u8p, ctypes.c_uint64, u64p,
+                                   ctypes.c_uint32, u32p, ctypes.c_uint64, u64p]
+    L.orc_encode_batch.restype = ctypes.c_int64
+    tab = np.ascontiguousarray(unicode_classes.class_table())
+    rc = L.orc_set_classes(tab.ctypes.data_as(u8p), tab.size)
+    if rc:
+        raise RuntimeError(f"orc_set_classes failed: {rc}")
+    _lib = L
+    return L
+
+
+def _p(a, t):
+    return a.ctypes.data_as(ctypes.POINTER(t))
+
+
+def _family(f):
+    return FAMILIES[f] if isinstance(f, str) else int(f)
+
+
+def _as_u8(data):
+    if isinstance(data, np.ndarray):
+        return np.ascontiguousarray(data, dtype=np.uint8)
+    return np.frombuffer(bytes(data), dtype=np.uint8) if len(data) else np.zeros(0, np.uint8)
+
+
+def _offsets(data_len, offsets):
+    if offsets is None:
+        offsets = [0, data_len]
+    return np.ascontiguousarray(offsets, dtype=np.uint64)
+
+
+def pretokenize(family, data, offsets=None):
+    """G over a batch: returns uint64 piece start byte offsets (document order), followed by the
+    batch end, so that piece k is [out[k], out[k+1])."""
+    L = lib()
+    buf = _as_u8(data)
+    offs = _offsets(buf.size, offsets)
+    out = np.zeros(buf.size + 2, dtype=np.uint64)
+    n = L.orc_pretokenize(_family(family), _p(buf, ctypes.c_uint8), buf.size, _p(offs, ctypes.c_uint64),
+                          offs.size - 1, _p(out, ctypes.c_uint64), buf.size + 1)
+    if n < 0:
+        raise OracleError(n)
+    out[n] = buf.size
+    return out[: n + 1].copy()
+
+
+def split(family, text):
+    """G on one string: the list of piece strings (for hand-worked cases)."""
+    data = text.encode("utf-8")
+    st = pretokenize(family, data)
+    return [data[st[k]:st[k + 1]].decode("utf-8") for k in range(len(st) - 1)]
+
+
+class Merges:
+    """A merge list in the oracle's own rank map.  merges[r] = (left_id, right_id) creates 256 + r."""
+
+    def __init__(self, merges):
+        m = np.ascontiguousarray(np.asarray(merges, dtype=np.uint32).reshape(-1, 2))
+        self.merges = m
+        self._h = lib().orc_bpe_new(_p(m, ctypes.c_uint32), m.shape[0])
+        if not self._h:
+            raise MemoryError
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.orc_bpe_free(self._h)
+            self._h = None
+
+    @property
+    def n_merges(self):
+        return self.merges.shape[0]
+
+    def token_bytes(self):
+        """Byte string of every token ID (for decode)."""
+        tb = [bytes([b]) for b in range(256)]
+        for a, b in self.merges:
+            tb.append(tb[a] + tb[b])
+        return tb
+
+
+def bpe_encode(merges, data, piece_starts):
+    """E on every piece [piece_starts[k], piece_starts[k+1]): returns (ids uint32, ntok uint32)."""
+    L = lib()
+    m = merges if isinstance(merges, Merges) else Merges(merges)
+    buf = _as_u8(data)
+    ps = np.ascontiguousarray(piece_starts, dtype=np.uint64)
+    npieces = ps.size - 1
+    out = np.zeros(max(buf.size, 1), dtype=np.uint32)
+    ntok = np.zeros(max(npieces, 1), dtype=np.uint32)
+    n = L.orc_bpe_encode(m._h, _p(buf, ctypes.c_uint8), _p(ps, ctypes.c_uint64), npieces,
+                         _p(out, ctypes.c_uint32), out.size, _p(ntok, ctypes.c_uint32))
+    if n < 0:
+        raise OracleError(n)
+    return out[:n].copy(), ntok[:npieces].copy()
+
+
+def encode_batch(family, merges, data, offsets=None):
+    """F = E* o G over a batch: returns (ids uint32[T], out_offsets uint64[D+1])."""
+    L = lib()
+    m = merges if isinstance(merges, Merges) else Merges(merges)
+    buf = _as_u8(data)
+    offs = _offsets(buf.size, offsets)
+    out = np.zeros(max(buf.size, 1), dtype=np.uint32)
+    oo = np.zeros(offs.size, dtype=np.uint64)
+    n = L.orc_encode_batch(_family(family), m._h, _p(buf, ctypes.c_uint8), buf.size,
+                           _p(offs, ctypes.c_uint64), offs.size - 1, _p(out, ctypes.c_uint32), out.size,
+                           _p(oo, ctypes.c_uint64))
+    if n < 0:
+        raise OracleError(n)
+    return out[:n].copy(), oo
+
+
+def encode(family, merges, text):
+    """F on one string: list of IDs."""
+    ids, _ = encode_batch(family, merges, text.encode("utf-8"))
+    return ids.tolist()
+
+
+def train(family, corpus, n_merges, max_token_bytes=128):
+    """Train a byte-level BPE merge list (uint32[n, 2]) on `corpus` (bytes).  Each step merges the
+    most frequent adjacent pair (counted over the pre-tokenized pieces, at least twice), ties to the
+    smallest (left, right); merges whose token would exceed max_token_bytes are skipped."""
+    L = lib()
+    buf = _as_u8(corpus)
+    out = np.zeros(2 * max(n_merges, 1), dtype=np.uint32)
+    n = L.orc_train(_family(family), _p(buf, ctypes.c_uint8), buf.size, n_merges, max_token_bytes,
+                    _p(out, ctypes.c_uint32))
+    if n < 0:
+        raise OracleError(n)
+    return out[: 2 * n].reshape(-1, 2).copy()
+
+
+def textbook_bpe(merges, piece: bytes):
+    """The textbook loop, written out: while some adjacent pair has a rank, merge the leftmost
+    occurrence of the lowest-ranked pair.  Quadratic; for tiny inputs only."""
+    rank = {}
+    for r, (a, b) in enumerate(np.asarray(merges).reshape(-1, 2).tolist()):
+        rank.setdefault((a, b), r)
+    seq = list(piece)
+    while True:
+        best = None
+        for i in range(len(seq) - 1):
+            r = rank.get((seq[i], seq[i + 1]))
+            if r is not None and (best is None or r < best[0]):
+                best = (r, i)
+        if best is None:
+            return seq
+        r, i = best
+        seq[i:i + 2] = [256 + r]
+
+
+def decode(merges, ids):
+    tb = (merges if isinstance(merges, Merges) else Merges(merges)).token_bytes()
+    return b"".join(tb[i] for i in ids)
