@@ -1,0 +1,13 @@
+"""MI355X-native exact byte-level BPE tokenization (gfx950 HIP kernels behind a C ABI).
+
+The public entry points mirror include/toktier.h; see ``binding`` for the argument conventions.
+"""
+from .binding import (EXPORTS, FAMILIES, TOKTIER_CL100K, TOKTIER_GPT2, TOKTIER_O200K, Tokenizer, ToktierError,
+                      Vocab, lib, toktier_encode_batch, toktier_free_vocab, toktier_last_status,
+                      toktier_load_vocab, toktier_pretokenize_batch, toktier_unicode_table_sha256,
+                      toktier_vocab_info, toktier_workspace_bytes)
+
+__all__ = ["EXPORTS", "FAMILIES", "TOKTIER_CL100K", "TOKTIER_GPT2", "TOKTIER_O200K", "Tokenizer", "ToktierError",
+           "Vocab", "lib", "toktier_encode_batch", "toktier_free_vocab", "toktier_last_status", "toktier_load_vocab",
+           "toktier_pretokenize_batch", "toktier_unicode_table_sha256", "toktier_vocab_info",
+           "toktier_workspace_bytes"]

@@ -1,0 +1,151 @@
+// compact.hip -- output compaction: per-piece ID runs -> one contiguous ID array per batch.
+//
+// TokTier (arXiv 2607.29678), GPU full-tokenization paragraph: the complete path ends with output
+// compaction, and piece counts and output length stay in device memory (no host round trip between
+// kernels).  Here: a single-pass exclusive scan of the per-piece token counts (decoupled look-back,
+// dynamic tile ids), a gather of each piece's IDs into place, and the per-document token offsets
+// (a document starts at the first piece whose start byte is >= its byte offset).
+#include "internal.h"
+
+namespace tt {
+
+__device__ __forceinline__ uint64_t ld_acquire64(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release64(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// tokoff[i] = sum of ntok[0..i) for i in [0, P]; tokoff[P] is the batch's token count
+__global__ __launch_bounds__(SCAN_THREADS) void k_tokscan(uint8_t *ws, Layout L)
+{
+    __shared__ uint32_t s_tile, s_base;
+    __shared__ uint32_t swsum[SCAN_THREADS / 64];
+    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
+    const uint32_t *ntok = (const uint32_t *)(ws + L.ntok);
+    uint32_t *tokoff = (uint32_t *)(ws + L.tokoff);
+    uint64_t *flags = (uint64_t *)(ws + L.sflag);
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
+    if (tid == 0) s_tile = atomicAdd(&ctrl->tile_ctr_scan, 1u);
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    const uint32_t np = ctrl->n_pieces;
+    const uint64_t first = (uint64_t)tile * SCAN_TILE;
+    if (first > np) return;                       // nothing at or below P in this tile
+    const uint64_t i0 = first + (uint64_t)tid * SCAN_PER_THREAD;
+    uint32_t x[SCAN_PER_THREAD], sum = 0;
+#pragma unroll
+    for (int k = 0; k < SCAN_PER_THREAD; ++k) {
+        uint64_t i = i0 + k;
+        x[k] = i < np ? ntok[i] : 0u;
+        sum += x[k];
+    }
+    uint32_t inc = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t y = __shfl_up(inc, d, 64);
+        if (lane >= (uint32_t)d) inc += y;
+    }
+    if (lane == 63) swsum[wid] = inc;
+    __syncthreads();
+    uint32_t before = inc - sum, total = 0;
+    for (uint32_t w = 0; w < SCAN_THREADS / 64; ++w) {
+        if (w < wid) before += swsum[w];
+        total += swsum[w];
+    }
+    if (tid == 0) {
+        uint64_t basev = 0;
+        if (tile > 0) {
+            st_release64(flags + tile, (1ull << 62) | total);
+            int64_t pos = (int64_t)tile - 1;
+            for (;;) {
+                uint64_t f = ld_acquire64(flags + pos);
+                uint32_t flag = (uint32_t)(f >> 62);
+                if (flag == 0) { __builtin_amdgcn_s_sleep(1); continue; }
+                basev += f & ((1ull << 62) - 1);
+                if (flag == 2) break;
+                --pos;
+            }
+        }
+        st_release64(flags + tile, (2ull << 62) | (basev + total));
+        s_base = (uint32_t)basev;
+    }
+    __syncthreads();
+    uint32_t run = s_base + before;
+#pragma unroll
+    for (int k = 0; k < SCAN_PER_THREAD; ++k) {
+        uint64_t i = i0 + k;
+        if (i <= np) tokoff[i] = run;
+        if (i == np) ctrl->n_tokens = run;
+        run += x[k];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_gather(uint8_t *ws, Layout L, uint32_t *__restrict__ out_ids)
+{
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t *ntok = (const uint32_t *)(ws + L.ntok);
+    const uint32_t *tokoff = (const uint32_t *)(ws + L.tokoff);
+    const uint32_t *scratch = (const uint32_t *)(ws + L.scratch);
+    const uint32_t np = ctrl->n_pieces;
+    for (uint32_t p = blockIdx.x * blockDim.x + threadIdx.x; p < np; p += gridDim.x * blockDim.x) {
+        const uint32_t *src = scratch + pstart[p];
+        uint32_t *dst = out_ids + tokoff[p];
+        const uint32_t c = ntok[p];
+        for (uint32_t j = 0; j < c; ++j) dst[j] = src[j];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_docoff(uint8_t *ws, Layout L, const uint64_t *__restrict__ offsets,
+                                               uint32_t n_docs, uint64_t *__restrict__ out_offsets)
+{
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t *tokoff = (const uint32_t *)(ws + L.tokoff);
+    const uint32_t np = ctrl->n_pieces;
+    for (uint64_t d = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; d <= n_docs;
+         d += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t off = offsets[d];
+        uint32_t a = 0, b = np;
+        while (a < b) {
+            uint32_t m = (a + b) >> 1;
+            if ((uint64_t)pstart[m] < off) a = m + 1; else b = m;
+        }
+        out_offsets[d] = tokoff[a];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_export_starts(uint8_t *ws, Layout L, uint64_t n, uint32_t *out)
+{
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t np = ctrl->n_pieces;
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i <= np; i += gridDim.x * blockDim.x)
+        out[i] = i == np ? (uint32_t)n : pstart[i];
+}
+
+hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offsets, hipStream_t s)
+{
+    const Layout &L = b.L;
+    hipLaunchKernelGGL(k_tokscan, dim3(L.n_scan_tiles), dim3(SCAN_THREADS), 0, s, b.ws, L);
+    if (b.n) {
+        uint32_t g = (uint32_t)((b.n + 255) / 256);
+        hipLaunchKernelGGL(k_gather, dim3(g > 4096 ? 4096 : g), dim3(256), 0, s, b.ws, L, out_ids);
+    }
+    uint32_t gd = (uint32_t)((b.n_docs + 1 + 255) / 256);
+    hipLaunchKernelGGL(k_docoff, dim3(gd > 1024 ? 1024 : gd), dim3(256), 0, s, b.ws, L, b.offsets, b.n_docs,
+                       out_offsets);
+    return hipGetLastError();
+}
+
+hipError_t launch_export_starts(const Batch &b, uint32_t *out_starts, hipStream_t s)
+{
+    uint32_t g = (uint32_t)((b.n + 1 + 255) / 256);
+    hipLaunchKernelGGL(k_export_starts, dim3(g > 4096 ? 4096 : g), dim3(256), 0, s, b.ws, b.L, b.n, out_starts);
+    return hipGetLastError();
+}
+
+}  // namespace tt

@@ -1,0 +1,543 @@
+// pretok.hip -- stage 1: regex-exact run decomposition of the pre-tokenizer on gfx950.
+//
+// TokTier (arXiv 2607.29678), GPU pre-tokenization paragraph and Figure 6: every character is
+// classified (letter / number / whitespace / other), maximal same-class runs are formed, and
+// whether a character starts a piece depends only on its offset in the run, a few characters of
+// look-back and per-run aggregates -- so classification is parallel and run summaries come from
+// prefix scans.  Here the per-character rule is a 15-state automaton (the state says what the
+// running leftmost-first match expects next).  Each character's transition function is a 60-bit
+// map (15 nibbles), maps compose associatively, so the state before every character comes from a
+// parallel scan of maps: within a thread, across the workgroup, and across tiles through a
+// decoupled look-back.  The two facts that need the future -- "no CR/LF later in this whitespace
+// run" (where `\s*[\r\n]+` stops) and "only uppercase letters left in this letter run" (where the
+// o200k case rule backtracks) -- come from a backward pass whose per-tile summaries the classify
+// kernel leaves behind.
+//
+// Kernels:  k_init      clear the control block and the look-back flags
+//           k_classify  UTF-8 decode + validation, category lookup, per-byte code, backward
+//                       per-tile summaries                                (1 read, 1 write of n)
+//           k_pieces    backward flags, automaton scan, piece-start bits, piece numbering scan,
+//                       piece start offsets                              (1 read of n, 4 B/piece)
+//           k_bins      piece lengths -> wave / block / giant lists (lane-sized pieces need none)
+#include "internal.h"
+
+#define TT_UCAT_QUAL static __device__ const
+#include "unicode_table.inc"
+
+namespace tt {
+
+// ---------------------------------------------------------------------------------------------
+// small helpers
+
+__device__ __forceinline__ uint32_t utf8_len(uint32_t b)
+{
+    if (b < 0x80u) return 1;
+    if (b >= 0xC2u && b <= 0xDFu) return 2;
+    if (b >= 0xE0u && b <= 0xEFu) return 3;
+    if (b >= 0xF0u && b <= 0xF4u) return 4;
+    return 0;   // continuation byte or never-valid lead
+}
+
+__device__ __forceinline__ uint32_t ucat(uint32_t cp)
+{
+    return tt_ucat_stage2[((uint32_t)tt_ucat_stage1[cp >> 8] << 8) | (cp & 255u)];
+}
+
+// backward map of one character for a boolean carried right-to-left:
+// 0 = pass the value of the next character through, 2 = constant false, 3 = constant true
+enum : uint32_t { BK_KEEP = 0, BK_F = 2, BK_T = 3 };
+
+// NA  = "no CR/LF from here to the end of this whitespace run"   (true outside whitespace)
+// AU  = "only uppercase letters from here to the end of this letter run" (true outside letters)
+__device__ __forceinline__ void backward_maps(uint32_t code, bool eof_next, uint32_t &na, uint32_t &au)
+{
+    uint32_t cat = code & 7u;
+    if (cat != CAT_W) na = BK_T;
+    else if (code & CC_CRLF) na = BK_F;
+    else na = eof_next ? BK_T : BK_KEEP;
+    if (cat == CAT_LU) au = eof_next ? BK_T : BK_KEEP;
+    else if (cat == CAT_LL || cat == CAT_LO || cat == CAT_M) au = BK_F;
+    else au = BK_T;
+}
+
+__device__ __forceinline__ bool is_const_map(uint64_t m)
+{
+    return m == (m & 15u) * NIBBLE_ONES;
+}
+
+// apply a first, then b
+__device__ __forceinline__ uint64_t compose(uint64_t a, uint64_t b)
+{
+    uint32_t a0 = (uint32_t)(a & 15u);
+    if (a == a0 * NIBBLE_ONES) return ((b >> (4u * a0)) & 15u) * NIBBLE_ONES;
+    uint64_t r = 0;
+#pragma unroll
+    for (int s = 0; s < NSTATES; ++s) {
+        uint32_t x = (uint32_t)(a >> (4 * s)) & 15u;
+        r |= ((b >> (4u * x)) & 15ull) << (4 * s);
+    }
+    return r;
+}
+
+__device__ __forceinline__ uint32_t apply_map(uint64_t m, uint32_t s)
+{
+    return (uint32_t)(m >> (4u * s)) & 15u;
+}
+
+__device__ __forceinline__ uint64_t shfl_up64(uint64_t x, int d)
+{
+    uint32_t lo = __shfl_up((uint32_t)x, d, 64), hi = __shfl_up((uint32_t)(x >> 32), d, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t ld_acquire(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_init
+
+__global__ void k_init(uint8_t *ws, Layout L)
+{
+    uint32_t i = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
+    uint32_t *ctrl = (uint32_t *)(ws + L.ctrl);
+    for (uint32_t k = i; k < 64; k += stride) ctrl[k] = 0;
+    uint64_t *a = (uint64_t *)(ws + L.tflag_state), *b = (uint64_t *)(ws + L.tflag_cnt),
+             *c = (uint64_t *)(ws + L.sflag);
+    for (uint32_t k = i; k < L.n_tiles; k += stride) { a[k] = 0; b[k] = 0; }
+    for (uint32_t k = i; k < L.n_scan_tiles; k += stride) c[k] = 0;
+    uint8_t *cc = ws + L.cc + (uint64_t)L.n_tiles * TILE;
+    for (uint32_t k = i; k < HALO; k += stride) cc[k] = CC_EOF;
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_classify: one workgroup per tile (blockIdx.x), 16 bytes per thread
+
+__global__ __launch_bounds__(PRE_THREADS) void k_classify(const uint8_t *__restrict__ bytes,
+                                                          const uint64_t *__restrict__ offsets,
+                                                          uint32_t n_docs, uint64_t n, int family,
+                                                          uint8_t *ws, Layout L)
+{
+    // bytes [lo-4, lo+TILE+8) and their document-start bits
+    constexpr int SPAN = TILE + 12;
+    __shared__ uint8_t sb[SPAN];
+    __shared__ uint32_t sdoc[(SPAN + 31) / 32];
+    __shared__ uint32_t sagg[PRE_THREADS];
+    __shared__ uint32_t s_d0, s_d1;
+
+    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
+    uint8_t *cc = ws + L.cc;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t lo = (uint64_t)blockIdx.x * TILE;
+    const int64_t base = (int64_t)lo - 4;
+
+    for (int j = tid; j < SPAN; j += PRE_THREADS) {
+        int64_t p = base + j;
+        sb[j] = (p >= 0 && (uint64_t)p < n) ? bytes[p] : 0;
+    }
+    for (int j = tid; j < (SPAN + 31) / 32; j += PRE_THREADS) sdoc[j] = 0;
+    if (tid == 0) {
+        // first document start >= base, and first >= base + SPAN (offsets are sorted)
+        uint64_t lo_p = base < 0 ? 0 : (uint64_t)base, hi_p = (uint64_t)(base + SPAN);
+        uint32_t a = 0, b = n_docs + 1;
+        while (a < b) { uint32_t m = (a + b) >> 1; if (offsets[m] < lo_p) a = m + 1; else b = m; }
+        uint32_t d0 = a;
+        b = n_docs + 1;
+        while (a < b) { uint32_t m = (a + b) >> 1; if (offsets[m] < hi_p) a = m + 1; else b = m; }
+        s_d0 = d0;
+        s_d1 = a;
+    }
+    // document offsets must start at 0, never decrease and end at n
+    bool bad_offs = false;
+    for (uint64_t d = (uint64_t)blockIdx.x * PRE_THREADS + tid; d < n_docs;
+         d += (uint64_t)gridDim.x * PRE_THREADS)
+        if (offsets[d] > offsets[d + 1]) bad_offs = true;
+    if (blockIdx.x == 0 && tid == 0 && (offsets[0] != 0 || offsets[n_docs] != n)) bad_offs = true;
+    if (bad_offs) atomicOr(&ctrl->status, ST_BAD_OFFSETS);
+    __syncthreads();
+    for (uint32_t d = s_d0 + tid; d < s_d1; d += PRE_THREADS) {
+        int64_t j = (int64_t)offsets[d] - base;
+        if (j >= 0 && j < SPAN) atomicOr(&sdoc[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+
+    auto docbit = [&](int j) -> bool { return (sdoc[j >> 5] >> (j & 31)) & 1u; };
+
+    bool bad = false;
+    uint32_t na_agg = BK_KEEP, au_agg = BK_KEEP;
+    uint32_t outw[PRE_CHUNK / 4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < PRE_CHUNK; ++k) {
+        const int j = 4 + tid * PRE_CHUNK + k;       // index into sb / sdoc
+        const uint64_t p = lo + tid * PRE_CHUNK + k;
+        uint32_t code;
+        if (p >= n) {
+            code = CC_EOF;
+        } else {
+            const uint32_t c = sb[j];
+            const bool isdoc = docbit(j);
+            if ((c & 0xC0u) == 0x80u) {
+                // continuation: it must be covered by a lead byte 1..3 bytes back in the same doc
+                bool ok = false;
+                if (!isdoc) {
+                    for (int back = 1; back <= 3; ++back) {
+                        if ((int64_t)p - back < 0) break;
+                        uint32_t lead = sb[j - back];
+                        if ((lead & 0xC0u) != 0x80u) { ok = utf8_len(lead) > (uint32_t)back; break; }
+                    }
+                }
+                bad |= !ok;
+                code = CAT_CONT;
+            } else {
+                uint32_t len = utf8_len(c), cp = c;
+                bool ok = len != 0 && p + len <= n;
+                if (ok && len > 1) {
+                    cp = c & (0x7Fu >> len);
+                    for (uint32_t t = 1; t < len; ++t) {
+                        uint32_t cb = sb[j + t];
+                        ok &= ((cb & 0xC0u) == 0x80u) && !docbit(j + t);
+                        cp = (cp << 6) | (cb & 0x3Fu);
+                    }
+                    ok &= !(len == 3 && cp < 0x800u) && !(len == 4 && (cp < 0x10000u || cp > 0x10FFFFu)) &&
+                          !(cp >= 0xD800u && cp <= 0xDFFFu);
+                }
+                bad |= !ok;
+                if (!ok) { len = 1; cp = 0xFFFDu; }
+                uint32_t cat = ucat(cp);
+                code = cat | (isdoc ? CC_DOC : 0u);
+                if (c == '\r' || c == '\n') code |= CC_CRLF;
+                if (c == ' ') code |= CC_SP;
+                if (c == '\'') {
+                    // 's 't 're 've 'm 'll 'd (ASCII; case-insensitive except for the GPT-2 family)
+                    auto letter = [&](uint32_t t) -> uint32_t {
+                        if (p + t >= n || docbit(j + t)) return 0;
+                        uint32_t x = sb[j + t];
+                        if (family != 1 && x >= 'A' && x <= 'Z') x += 32;
+                        return x;
+                    };
+                    uint32_t x1 = letter(1), x2 = letter(2), lc = 0;
+                    if (x1 == 's' || x1 == 't' || x1 == 'm' || x1 == 'd') lc = 1;
+                    else if ((x1 == 'r' && x2 == 'e') || (x1 == 'v' && x2 == 'e') || (x1 == 'l' && x2 == 'l'))
+                        lc = 2;
+                    code |= lc << CC_CONTR_SHIFT;
+                }
+                const uint64_t pn = p + len;
+                const bool eof_next = pn >= n || docbit(j + (int)len);
+                uint32_t na, au;
+                backward_maps(code, eof_next, na, au);
+                if (na_agg == BK_KEEP) na_agg = na;
+                if (au_agg == BK_KEEP) au_agg = au;
+            }
+        }
+        outw[k >> 2] |= code << (8 * (k & 3));
+    }
+    if (bad) atomicOr(&ctrl->status, ST_BAD_UTF8);
+    *(uint4 *)(cc + lo + tid * PRE_CHUNK) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
+
+    // tile summary: the leftmost non-pass-through map of each flag
+    sagg[tid] = na_agg | (au_agg << 2);
+    __syncthreads();
+    if (tid < 64) {
+        uint32_t na = BK_KEEP, au = BK_KEEP;
+        for (int g = 0; g < PRE_THREADS / 64; ++g) {
+            uint32_t x = sagg[g * 64 + tid];
+            uint64_t mna = __ballot((x & 3u) != 0), mau = __ballot((x >> 2) != 0);
+            if (na == BK_KEEP && mna) na = sagg[g * 64 + __ffsll((unsigned long long)mna) - 1] & 3u;
+            if (au == BK_KEEP && mau) au = sagg[g * 64 + __ffsll((unsigned long long)mau) - 1] >> 2;
+        }
+        if (tid == 0) (ws + L.tbwd)[blockIdx.x] = (uint8_t)(na | (au << 2));
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_pieces: dynamic tile ids; per-char automaton context, scans, look-backs, piece starts
+
+// self code of a character (13 values) from its byte code and its NA flag
+__device__ __forceinline__ uint32_t self_code(uint32_t code, bool na)
+{
+    uint32_t cat = code & 7u;
+    switch (cat) {
+    case CAT_LU: return 0;
+    case CAT_LL: return 1;
+    case CAT_LO: return 2;
+    case CAT_N: return 3;
+    case CAT_M: return 4;
+    case CAT_O: {
+        uint32_t lc = (code >> CC_CONTR_SHIFT) & 3u;
+        return lc == 0 ? 5u : (lc == 1 ? 6u : 7u);
+    }
+    default:   // whitespace
+        if (code & CC_CRLF) return 12;
+        if (code & CC_SP) return na ? 11u : 10u;
+        return na ? 9u : 8u;
+    }
+}
+
+__device__ __forceinline__ uint32_t next_code(uint32_t code)
+{
+    if (code == CC_EOF || (code & CC_DOC)) return 5;
+    switch (code & 7u) {
+    case CAT_LU: case CAT_LL: case CAT_LO: return 0;
+    case CAT_N: return 1;
+    case CAT_W: return 2;
+    case CAT_M: return 3;
+    default: return 4;
+    }
+}
+
+__global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, uint8_t *ws, Layout L)
+{
+    __shared__ __align__(16) uint8_t scc[TILE + HALO];
+    __shared__ uint16_t sctx[TILE];
+    __shared__ uint64_t smap[NCTX];
+    __shared__ uint32_t sstart[NCTX];
+    __shared__ uint32_t sbk[PRE_THREADS];
+    __shared__ uint64_t swmap[PRE_THREADS / 64];
+    __shared__ uint32_t swcnt[PRE_THREADS / 64];
+    __shared__ uint32_t s_tile, s_carry, s_entry, s_base;
+
+    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
+    const uint8_t *cc = ws + L.cc;
+    const uint8_t *tbwd = ws + L.tbwd;
+    uint64_t *tfs = (uint64_t *)(ws + L.tflag_state);
+    uint64_t *tfc = (uint64_t *)(ws + L.tflag_cnt);
+    uint32_t *pstart = (uint32_t *)(ws + L.pstart);
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
+
+    if (tid == 0) s_tile = atomicAdd(&ctrl->tile_ctr_pre, 1u);
+    for (int i = tid; i < NCTX; i += PRE_THREADS) { smap[i] = v.fmap[i]; sstart[i] = v.fstart[i]; }
+    __syncthreads();
+    const uint32_t tile = s_tile;
+    const uint64_t lo = (uint64_t)tile * TILE;
+    // the code bytes of the tile and its halo (past the batch end they read CC_EOF)
+    *(uint4 *)(scc + tid * PRE_CHUNK) = *(const uint4 *)(cc + lo + tid * PRE_CHUNK);
+    if (tid < HALO / 4) ((uint32_t *)(scc + TILE))[tid] = ((const uint32_t *)(cc + lo + TILE))[tid];
+
+    // backward carry into this tile: first non-pass-through summary of a later tile
+    if (wid == 0) {
+        uint32_t na = BK_KEEP, au = BK_KEEP;
+        for (uint32_t t0 = tile + 1; na == BK_KEEP || au == BK_KEEP; t0 += 64) {
+            uint32_t t = t0 + lane;
+            uint32_t x = t < L.n_tiles ? (uint32_t)tbwd[t] : (BK_T | (BK_T << 2));
+            uint64_t mna = __ballot((x & 3u) != 0), mau = __ballot((x >> 2) != 0);
+            uint32_t xna = __shfl(x, __ffsll((unsigned long long)mna) - 1, 64);
+            uint32_t xau = __shfl(x, __ffsll((unsigned long long)mau) - 1, 64);
+            if (na == BK_KEEP && mna) na = xna & 3u;
+            if (au == BK_KEEP && mau) au = xau >> 2;
+        }
+        if (lane == 0) s_carry = (na & 1u) | ((au & 1u) << 1);
+    }
+    __syncthreads();
+
+    // per character: backward maps of this thread's chunk
+    const int c0 = tid * PRE_CHUNK;
+    uint32_t code[PRE_CHUNK + 4];
+#pragma unroll
+    for (int k = 0; k < PRE_CHUNK + 4; ++k) code[k] = scc[c0 + k];
+    uint32_t eofn = 0, nxt_code[PRE_CHUNK];
+    uint32_t bna[PRE_CHUNK], bau[PRE_CHUNK];
+    uint32_t agg = BK_KEEP | (BK_KEEP << 2);
+#pragma unroll
+    for (int k = 0; k < PRE_CHUNK; ++k) {
+        // next char: first non-continuation byte after k (within 4 bytes for valid UTF-8)
+        uint32_t nc = code[k + 1];
+        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code[k + 2];
+        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code[k + 3];
+        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code[k + 4];
+        nxt_code[k] = nc;
+        bool isch = code[k] != CC_EOF && (code[k] & 7u) != CAT_CONT;
+        bool en = nc == CC_EOF || (nc & CC_DOC) || (nc & 7u) == CAT_CONT;
+        uint32_t na = BK_KEEP, au = BK_KEEP;
+        if (isch) backward_maps(code[k], en, na, au);
+        bna[k] = na;
+        bau[k] = au;
+        eofn |= (en ? 1u : 0u) << k;
+        if ((agg & 3u) == BK_KEEP) agg = (agg & ~3u) | na;
+        if ((agg >> 2) == BK_KEEP) agg = (agg & 3u) | (au << 2);
+    }
+    // suffix scan over threads: value entering each chunk from its right
+    sbk[tid] = agg;
+    __syncthreads();
+    for (int d = 1; d < PRE_THREADS; d <<= 1) {
+        uint32_t mine = sbk[tid], right = (tid + d < PRE_THREADS) ? sbk[tid + d] : (BK_KEEP | (BK_KEEP << 2));
+        __syncthreads();
+        uint32_t r = mine;
+        if ((r & 3u) == BK_KEEP) r = (r & ~3u) | (right & 3u);
+        if ((r >> 2) == BK_KEEP) r = (r & 3u) | (right & ~3u);
+        sbk[tid] = r;
+        __syncthreads();
+    }
+    uint32_t right = tid + 1 < PRE_THREADS ? sbk[tid + 1] : (BK_KEEP | (BK_KEEP << 2));
+    uint32_t na_val = ((right & 3u) == BK_KEEP) ? (s_carry & 1u) : (right & 1u);
+    uint32_t au_val = ((right >> 2) == BK_KEEP) ? ((s_carry >> 1) & 1u) : ((right >> 2) & 1u);
+
+    // right to left: NA of each char, AU of the char after it; then the automaton context
+    uint64_t m_acc = MAP_IDENTITY;
+    uint32_t ctxs[PRE_CHUNK];
+#pragma unroll
+    for (int k = PRE_CHUNK - 1; k >= 0; --k) {
+        uint32_t au_next = au_val;                  // AU of the next character
+        if (bna[k] != BK_KEEP) na_val = bna[k] & 1u;
+        if (bau[k] != BK_KEEP) au_val = bau[k] & 1u;
+        bool isch = code[k] != CC_EOF && (code[k] & 7u) != CAT_CONT;
+        uint32_t ctx = 0xFFFFu;
+        if (isch) {
+            uint32_t self = self_code(code[k], na_val != 0);
+            uint32_t doc = (code[k] & CC_DOC) ? 1u : 0u;
+            uint32_t nx = ((eofn >> k) & 1u) ? 5u : next_code(nxt_code[k]);
+            ctx = ((self * 2u + doc) * NNEXT + nx) * 2u + au_next;
+        }
+        ctxs[k] = ctx;
+    }
+#pragma unroll
+    for (int k = 0; k < PRE_CHUNK; ++k)
+        if (ctxs[k] != 0xFFFFu) m_acc = compose(m_acc, smap[ctxs[k]]);
+
+    // workgroup scan of maps (exclusive per thread) and the tile's map
+    uint64_t incl = m_acc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint64_t y = shfl_up64(incl, d);
+        if (lane >= (uint32_t)d) incl = compose(y, incl);
+    }
+    if (lane == 63) swmap[wid] = incl;
+    uint64_t excl = shfl_up64(incl, 1);
+    if (lane == 0) excl = MAP_IDENTITY;
+    __syncthreads();
+    uint64_t pre = MAP_IDENTITY, tile_map = MAP_IDENTITY;
+    for (uint32_t w = 0; w < PRE_THREADS / 64; ++w) {
+        if (w < wid) pre = compose(pre, swmap[w]);
+        tile_map = compose(tile_map, swmap[w]);
+    }
+    excl = compose(pre, excl);
+
+    // look-back #1: automaton state entering this tile
+    if (tid == 0) {
+        uint32_t entry = S_ST;
+        if (tile > 0) {
+            st_release(tfs + tile, (1ull << 60) | tile_map);
+            uint64_t acc = MAP_IDENTITY;
+            int64_t pos = (int64_t)tile - 1;
+            for (;;) {
+                uint64_t f = ld_acquire(tfs + pos);
+                uint32_t flag = (uint32_t)(f >> 60);
+                if (flag == 0) { __builtin_amdgcn_s_sleep(1); continue; }
+                if (flag == 2) { entry = apply_map(acc, (uint32_t)(f & 15u)); break; }
+                acc = compose(f & ((1ull << 60) - 1), acc);
+                if (is_const_map(acc)) { entry = (uint32_t)(acc & 15u); break; }
+                --pos;
+            }
+        }
+        st_release(tfs + tile, (2ull << 60) | apply_map(tile_map, entry));
+        s_entry = entry;
+    }
+    __syncthreads();
+
+    // piece starts of this chunk
+    uint32_t s = apply_map(excl, s_entry), mask = 0;
+#pragma unroll
+    for (int k = 0; k < PRE_CHUNK; ++k) {
+        uint32_t ctx = ctxs[k];
+        if (ctx != 0xFFFFu) {
+            mask |= ((sstart[ctx] >> s) & 1u) << k;
+            s = apply_map(smap[ctx], s);
+        }
+    }
+    uint32_t cnt = __popc(mask), icnt = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t y = __shfl_up(icnt, d, 64);
+        if (lane >= (uint32_t)d) icnt += y;
+    }
+    if (lane == 63) swcnt[wid] = icnt;
+    __syncthreads();
+    uint32_t before = icnt - cnt, total = 0;
+    for (uint32_t w = 0; w < PRE_THREADS / 64; ++w) {
+        if (w < wid) before += swcnt[w];
+        total += swcnt[w];
+    }
+
+    // look-back #2: number of pieces before this tile
+    if (tid == 0) {
+        uint64_t basev = 0;
+        if (tile > 0) {
+            st_release(tfc + tile, (1ull << 62) | total);
+            int64_t pos = (int64_t)tile - 1;
+            for (;;) {
+                uint64_t f = ld_acquire(tfc + pos);
+                uint32_t flag = (uint32_t)(f >> 62);
+                if (flag == 0) { __builtin_amdgcn_s_sleep(1); continue; }
+                basev += f & ((1ull << 62) - 1);
+                if (flag == 2) break;
+                --pos;
+            }
+        }
+        st_release(tfc + tile, (2ull << 62) | (basev + total));
+        s_base = (uint32_t)basev;
+        if (tile == L.n_tiles - 1) {
+            ctrl->n_pieces = (uint32_t)(basev + total);
+            pstart[basev + total] = (uint32_t)n;
+        }
+    }
+    __syncthreads();
+    uint32_t o = s_base + before;
+    while (mask) {
+        int k = __ffs(mask) - 1;
+        mask &= mask - 1;
+        pstart[o++] = (uint32_t)(lo + c0 + k);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// k_bins: pieces longer than a lane's limit go to the wave / block / giant lists
+
+__global__ __launch_bounds__(256) void k_bins(uint8_t *ws, Layout L)
+{
+    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    uint32_t *lists[3] = {(uint32_t *)(ws + L.bin_wave), (uint32_t *)(ws + L.bin_block),
+                          (uint32_t *)(ws + L.bin_giant)};
+    const uint32_t np = ctrl->n_pieces;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t lt = (1ull << lane) - 1;
+    for (uint32_t p0 = blockIdx.x * blockDim.x; p0 < np; p0 += gridDim.x * blockDim.x) {
+        uint32_t p = p0 + threadIdx.x;
+        int bin = -1;
+        if (p < np) {
+            uint32_t len = pstart[p + 1] - pstart[p];
+            bin = len <= LANE_MAX ? -1 : (len <= WAVE_MAX ? 0 : (len <= BLOCK_MAX ? 1 : 2));
+        }
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+            uint64_t m = __ballot(bin == b);
+            if (!m) continue;
+            uint32_t leader = __ffsll((unsigned long long)m) - 1, off = 0;
+            if (lane == leader) off = atomicAdd(&ctrl->bin_count[b], (uint32_t)__popcll(m));
+            off = __shfl(off, leader, 64);
+            if (bin == b) lists[b][off + __popcll(m & lt)] = p;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+
+hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s)
+{
+    const Layout &L = b.L;
+    hipLaunchKernelGGL(k_init, dim3(64), dim3(256), 0, s, b.ws, L);
+    if (L.n_tiles == 0) return hipGetLastError();
+    hipLaunchKernelGGL(k_classify, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, b.bytes, b.offsets, b.n_docs,
+                       b.n, v.family, b.ws, L);
+    hipLaunchKernelGGL(k_pieces, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.n, b.ws, L);
+    uint32_t g = (uint32_t)((b.n + 255) / 256);
+    if (g > 2048) g = 2048;
+    hipLaunchKernelGGL(k_bins, dim3(g), dim3(256), 0, s, b.ws, L);
+    return hipGetLastError();
+}
+
+}  // namespace tt

@@ -1,0 +1,406 @@
+// toktier.hip -- host side of the C ABI (include/toktier.h): vocabulary load and validation,
+// device tables, argument checks and the stream-ordered launch chain.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/toktier.h"
+#include "internal.h"
+#include "unicode_table.inc"
+
+using namespace tt;
+
+struct toktier_vocab {
+    int device;
+    int family;
+    uint32_t n_merges;
+    void *dmem;
+    DevVocab dv;
+};
+
+static thread_local std::string g_hip_err;
+
+static int hip_fail(hipError_t e)
+{
+    g_hip_err = hipGetErrorString(e);
+    (void)hipGetLastError();   // clear the sticky error
+    return TOKTIER_E_HIP;
+}
+
+#define HIP_TRY(x)                                 \
+    do {                                           \
+        hipError_t e_ = (x);                       \
+        if (e_ != hipSuccess) return hip_fail(e_); \
+    } while (0)
+
+// ---------------------------------------------------------------------------------------------
+// pre-tokenizer automaton tables.
+//
+// The per-character rule of each family (paper, derivation paragraph: one run rule per regex
+// alternative) as a deterministic automaton over character contexts.  A context is: the
+// character's own code (13 kinds), whether it is the first character of a document, the kind of the
+// next character (6, incl. end of text) and one backward flag.  For each context and each state
+// the table gives the next state and whether a piece starts at the character.  The state before a
+// character is what the running leftmost-first match expects there; at a match start the first
+// alternative that can match (in the family's order) decides the new state.
+
+namespace {
+
+enum Self { SF_LU = 0, SF_LL, SF_LO, SF_N, SF_M, SF_O, SF_AP2, SF_AP3, SF_W0, SF_W1, SF_SP0, SF_SP1,
+            SF_CRLF };
+enum Next { NX_L = 0, NX_N, NX_W, NX_M, NX_O, NX_EOF };
+constexpr int STOP = -1;
+
+struct Ctx {
+    int self, nx;
+    bool allu;   // only uppercase letters from the next character to the end of its letter run
+    bool L() const { return self <= SF_LO; }
+    bool N() const { return self == SF_N; }
+    bool M() const { return self == SF_M; }
+    bool Oany() const { return self >= SF_M && self <= SF_AP3; }      // [^\s\p{L}\p{N}]
+    bool Oprime() const { return self >= SF_O && self <= SF_AP3; }    // other, not a mark
+    bool W() const { return self >= SF_W0; }
+    bool SP() const { return self == SF_SP0 || self == SF_SP1; }
+    bool CRLF() const { return self == SF_CRLF; }
+    bool NA() const { return self == SF_W1 || self == SF_SP1; }       // no CR/LF ahead in the run
+    bool X() const { return !CRLF() && !L() && !N(); }                // [^\r\n\p{L}\p{N}]
+    bool LM() const { return L() || M(); }
+    int contr() const { return self == SF_AP2 ? 2 : (self == SF_AP3 ? 3 : 0); }
+    bool nxL() const { return nx == NX_L; }
+    bool nxLM() const { return nx == NX_L || nx == NX_M; }
+    bool nxOany() const { return nx == NX_M || nx == NX_O; }
+    bool nxW_or_eof() const { return nx == NX_W || nx == NX_EOF; }
+};
+
+int contraction_state(int len) { return len == 2 ? S_C1 : S_C2; }
+
+// whitespace alternatives shared by cl100k and o200k: \s*[\r\n]+ | \s+(?!\S) | \s+
+int ws_dispatch(const Ctx &c)
+{
+    if (!c.NA()) return S_WNL;           // a CR/LF lies ahead in this run (or is this char)
+    return c.nxW_or_eof() ? S_WNS : S_ST;
+}
+
+// o200k letter phases: A = upper|other-letter|mark run, B = lower|other-letter|mark run
+int letter_step(const Ctx &c)
+{
+    if (c.self == SF_LL) return S_LB;
+    if (c.self == SF_LO || c.self == SF_M) return c.allu ? S_LEND : S_LA;
+    return S_LA;   // uppercase
+}
+
+int dispatch(int fam, const Ctx &c)
+{
+    if (fam == TOKTIER_GPT2) {
+        if (c.contr()) return contraction_state(c.contr());
+        if (c.SP() && c.nxL()) return S_LRUN;
+        if (c.SP() && c.nx == NX_N) return S_NALL;
+        if (c.SP() && c.nxOany()) return S_ORUN;
+        if (c.L()) return S_LRUN;
+        if (c.N()) return S_NALL;
+        if (c.Oany()) return S_ORUN;
+        return c.nxW_or_eof() ? S_WNS : S_ST;
+    }
+    if (fam == TOKTIER_CL100K) {
+        if (c.contr()) return contraction_state(c.contr());
+        if (c.X() && c.nxL()) return S_LRUN;
+        if (c.L()) return S_LRUN;
+        if (c.N()) return S_N1;
+        if (c.SP() && c.nxOany()) return S_ORNL;
+        if (c.Oany()) return S_ORNL;
+        return ws_dispatch(c);
+    }
+    // o200k
+    if (c.LM()) return letter_step(c);
+    if (c.X() && c.nxLM()) return S_LA;
+    if (c.N()) return S_N1;
+    if (c.SP() && c.nx == NX_O) return S_ORNL;
+    if (c.Oprime()) return S_ORNL;
+    return ws_dispatch(c);
+}
+
+int cont(int fam, int st, const Ctx &c)
+{
+    switch (st) {
+    case S_ST: return STOP;
+    case S_C1: return S_ST;
+    case S_C2: return S_C1;
+    case S_LRUN: return c.L() ? S_LRUN : STOP;
+    case S_NALL: return c.N() ? S_NALL : STOP;
+    case S_N1: return c.N() ? S_N2 : STOP;
+    case S_N2: return c.N() ? S_ST : STOP;
+    case S_ORUN: return c.Oany() ? S_ORUN : STOP;
+    case S_ORNL: return c.Oany() ? S_ORNL : (c.CRLF() ? S_ONL : STOP);
+    case S_ONL: return c.CRLF() ? S_ONL : STOP;
+    case S_WNL: return (c.W() && !c.NA()) ? S_WNL : STOP;
+    case S_WNS: return (c.W() && c.nxW_or_eof()) ? S_WNS : STOP;
+    case S_LA:
+    case S_LB:
+    case S_LEND:
+        if (c.LM()) {
+            if (st == S_LA) return letter_step(c);
+            if (st == S_LB) return c.self == SF_LU ? STOP : S_LB;
+            return STOP;
+        }
+        // the letter match ends at the end of its run: an optional contraction suffix follows
+        if (c.contr()) return contraction_state(c.contr());
+        return STOP;
+    }
+    (void)fam;
+    return STOP;
+}
+
+void build_tables(int fam, uint64_t *fmap, uint32_t *fstart)
+{
+    for (int self = 0; self < NSELF; ++self)
+        for (int doc = 0; doc < 2; ++doc)
+            for (int nx = 0; nx < NNEXT; ++nx)
+                for (int au = 0; au < 2; ++au) {
+                    Ctx c{self, nx, au != 0};
+                    int idx = ((self * 2 + doc) * NNEXT + nx) * 2 + au;
+                    int d = dispatch(fam, c);
+                    uint64_t m = 0;
+                    uint32_t st = 0;
+                    for (int s = 0; s < NSTATES; ++s) {
+                        int r = doc ? STOP : cont(fam, s, c);
+                        if (r == STOP) { r = d; st |= 1u << s; }
+                        m |= (uint64_t)r << (4 * s);
+                    }
+                    fmap[idx] = m;
+                    fstart[idx] = st;
+                }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+
+extern "C" const char *toktier_status_string(int status)
+{
+    switch (status) {
+    case TOKTIER_OK: return "ok";
+    case TOKTIER_E_INVALID_ARG: return "invalid argument";
+    case TOKTIER_E_BAD_FAMILY: return "unknown pre-tokenizer family";
+    case TOKTIER_E_BAD_MERGES: return "merge list is not rank-consistent, has duplicates or is too large";
+    case TOKTIER_E_INVALID_UTF8: return "input is not valid UTF-8";
+    case TOKTIER_E_CAPACITY: return "output or workspace capacity too small";
+    case TOKTIER_E_HIP: return "HIP runtime error";
+    case TOKTIER_E_OOM: return "out of memory";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char *toktier_last_hip_error(void) { return g_hip_err.c_str(); }
+
+extern "C" const char *toktier_unicode_table_sha256(void) { return TT_UNICODE_TABLE_SHA256; }
+
+extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int family, toktier_vocab **out)
+{
+    if (!out || (n_merges && !merges)) return TOKTIER_E_INVALID_ARG;
+    if (family != TOKTIER_GPT2 && family != TOKTIER_CL100K && family != TOKTIER_O200K) return TOKTIER_E_BAD_FAMILY;
+    if (n_merges > TOKTIER_MAX_MERGES) return TOKTIER_E_BAD_MERGES;
+
+    std::vector<uint32_t> r2(65536, NO_RANK);
+    uint32_t n_general = 0;
+    for (uint32_t r = 0; r < n_merges; ++r) {
+        uint32_t a = merges[2 * r], b = merges[2 * r + 1];
+        if (a >= 256u + r || b >= 256u + r) return TOKTIER_E_BAD_MERGES;   // rank-inconsistent
+        if ((a | b) < 256u) {
+            if (r2[(a << 8) | b] != NO_RANK) return TOKTIER_E_BAD_MERGES;   // duplicate pair
+            r2[(a << 8) | b] = r;
+        } else {
+            ++n_general;
+        }
+    }
+    uint32_t log2cap = 10;
+    while ((1ull << log2cap) < 2ull * n_general) ++log2cap;
+    const uint64_t cap = 1ull << log2cap;
+    std::vector<uint64_t> slots(cap, EMPTY_SLOT);
+    const uint32_t shift = 64 - log2cap;
+    for (uint32_t r = 0; r < n_merges; ++r) {
+        uint32_t a = merges[2 * r], b = merges[2 * r + 1];
+        if ((a | b) < 256u) continue;
+        uint64_t key = ((uint64_t)a << 21) | b;
+        uint64_t h = (key * 0x9E3779B97F4A7C15ull) >> shift;
+        for (;;) {
+            if (slots[h] == EMPTY_SLOT) { slots[h] = (key << 21) | r; break; }
+            if ((slots[h] >> 21) == key) return TOKTIER_E_BAD_MERGES;      // duplicate pair
+            h = (h + 1) & (cap - 1);
+        }
+    }
+    uint64_t fmap[NCTX];
+    uint32_t fstart[NCTX];
+    build_tables(family, fmap, fstart);
+
+    // one device allocation: r2 | slots | merges | fmap | fstart
+    const uint64_t o_r2 = 0, o_slots = align256(65536 * 4), o_merges = o_slots + align256(cap * 8);
+    const uint64_t o_fmap = o_merges + align256(8ull * n_merges + 8);
+    const uint64_t o_fstart = o_fmap + align256(8 * NCTX);
+    const uint64_t total = o_fstart + align256(4 * NCTX);
+
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    void *d = nullptr;
+    hipError_t e = hipMalloc(&d, total);
+    if (e != hipSuccess) {
+        hip_fail(e);
+        return TOKTIER_E_OOM;
+    }
+    uint8_t *base = (uint8_t *)d;
+    hipError_t c1 = hipMemcpy(base + o_r2, r2.data(), 65536 * 4, hipMemcpyHostToDevice);
+    hipError_t c2 = hipMemcpy(base + o_slots, slots.data(), cap * 8, hipMemcpyHostToDevice);
+    hipError_t c3 = n_merges ? hipMemcpy(base + o_merges, merges, 8ull * n_merges, hipMemcpyHostToDevice)
+                             : hipSuccess;
+    hipError_t c4 = hipMemcpy(base + o_fmap, fmap, sizeof(fmap), hipMemcpyHostToDevice);
+    hipError_t c5 = hipMemcpy(base + o_fstart, fstart, sizeof(fstart), hipMemcpyHostToDevice);
+    for (hipError_t ci : {c1, c2, c3, c4, c5})
+        if (ci != hipSuccess) {
+            (void)hipFree(d);
+            return hip_fail(ci);
+        }
+    toktier_vocab *v = (toktier_vocab *)calloc(1, sizeof(toktier_vocab));
+    if (!v) {
+        (void)hipFree(d);
+        return TOKTIER_E_OOM;
+    }
+    v->device = dev;
+    v->family = family;
+    v->n_merges = n_merges;
+    v->dmem = d;
+    v->dv.r2 = (const uint32_t *)(base + o_r2);
+    v->dv.slots = (const uint64_t *)(base + o_slots);
+    v->dv.merges = (const uint32_t *)(base + o_merges);
+    v->dv.fmap = (const uint64_t *)(base + o_fmap);
+    v->dv.fstart = (const uint32_t *)(base + o_fstart);
+    v->dv.mask = (uint32_t)(cap - 1);
+    v->dv.shift = shift;
+    v->dv.n_merges = n_merges;
+    v->dv.family = family;
+    *out = v;
+    return TOKTIER_OK;
+}
+
+extern "C" int toktier_free_vocab(toktier_vocab *v)
+{
+    if (!v) return TOKTIER_OK;
+    hipError_t e = hipDeviceSynchronize();
+    hipError_t f = hipFree(v->dmem);
+    free(v);
+    if (e != hipSuccess) return hip_fail(e);
+    if (f != hipSuccess) return hip_fail(f);
+    return TOKTIER_OK;
+}
+
+extern "C" int toktier_vocab_info(const toktier_vocab *v, uint32_t *n_merges, int *family)
+{
+    if (!v) return TOKTIER_E_INVALID_ARG;
+    if (n_merges) *n_merges = v->n_merges;
+    if (family) *family = v->family;
+    return TOKTIER_OK;
+}
+
+extern "C" int toktier_workspace_bytes(uint64_t total_bytes, uint32_t n_docs, uint64_t *out_bytes)
+{
+    if (!out_bytes || total_bytes >= 0xFFFFFFFFull || n_docs == 0xFFFFFFFFu) return TOKTIER_E_INVALID_ARG;
+    *out_bytes = make_layout(total_bytes).total;
+    return TOKTIER_OK;
+}
+
+namespace {
+
+int check_batch(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets, uint32_t n_docs,
+                uint64_t total_bytes, void *workspace, uint64_t workspace_bytes, Batch *b)
+{
+    if (!v || !offsets || !workspace || n_docs == 0 || n_docs == 0xFFFFFFFFu) return TOKTIER_E_INVALID_ARG;
+    if (total_bytes >= 0xFFFFFFFFull || (total_bytes && !bytes)) return TOKTIER_E_INVALID_ARG;
+    if (((uintptr_t)workspace & 255u) != 0) return TOKTIER_E_INVALID_ARG;
+    Layout L = make_layout(total_bytes);
+    if (workspace_bytes < L.total) return TOKTIER_E_CAPACITY;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev != v->device) return TOKTIER_E_INVALID_ARG;
+    b->bytes = bytes;
+    b->offsets = offsets;
+    b->n_docs = n_docs;
+    b->n = total_bytes;
+    b->ws = (uint8_t *)workspace;
+    b->L = L;
+    return TOKTIER_OK;
+}
+
+// read the control block back (one device-to-host copy) and map device-detected errors
+int read_ctrl(void *workspace, hipStream_t s, Ctrl *out)
+{
+    static thread_local Ctrl *pinned = nullptr;
+    if (!pinned) {
+        hipError_t e = hipHostMalloc((void **)&pinned, sizeof(Ctrl), hipHostMallocDefault);
+        if (e != hipSuccess) {
+            pinned = nullptr;
+            return hip_fail(e);
+        }
+    }
+    HIP_TRY(hipMemcpyAsync(pinned, workspace, sizeof(Ctrl), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    *out = *pinned;
+    if (out->status & ST_BAD_OFFSETS) return TOKTIER_E_INVALID_ARG;
+    if (out->status & ST_BAD_UTF8) return TOKTIER_E_INVALID_UTF8;
+    return TOKTIER_OK;
+}
+
+}  // namespace
+
+extern "C" int toktier_encode_batch(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                                    uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
+                                    uint64_t ids_capacity, uint64_t *out_offsets, void *workspace,
+                                    uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens)
+{
+    Batch b;
+    int rc = check_batch(v, bytes, offsets, n_docs, total_bytes, workspace, workspace_bytes, &b);
+    if (rc) return rc;
+    if (!out_offsets || (total_bytes && !out_ids)) return TOKTIER_E_INVALID_ARG;
+    if (ids_capacity < total_bytes) return TOKTIER_E_CAPACITY;
+    hipStream_t s = (hipStream_t)stream;
+    HIP_TRY(launch_pretokenize(v->dv, b, s));
+    HIP_TRY(launch_bpe(v->dv, b, s));
+    HIP_TRY(launch_compact(b, out_ids, out_offsets, s));
+    if (!out_n_tokens) return TOKTIER_OK;
+    Ctrl c;
+    rc = read_ctrl(workspace, s, &c);
+    if (rc) return rc;
+    *out_n_tokens = c.n_tokens;
+    return TOKTIER_OK;
+}
+
+extern "C" int toktier_pretokenize_batch(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                                         uint32_t n_docs, uint64_t total_bytes, uint32_t *out_piece_starts,
+                                         uint64_t starts_capacity, void *workspace, uint64_t workspace_bytes,
+                                         void *stream, uint64_t *out_n_pieces)
+{
+    Batch b;
+    int rc = check_batch(v, bytes, offsets, n_docs, total_bytes, workspace, workspace_bytes, &b);
+    if (rc) return rc;
+    if (!out_piece_starts || !out_n_pieces) return TOKTIER_E_INVALID_ARG;
+    if (starts_capacity < total_bytes + 1) return TOKTIER_E_CAPACITY;
+    hipStream_t s = (hipStream_t)stream;
+    HIP_TRY(launch_pretokenize(v->dv, b, s));
+    HIP_TRY(launch_export_starts(b, out_piece_starts, s));
+    Ctrl c;
+    rc = read_ctrl(workspace, s, &c);
+    if (rc) return rc;
+    *out_n_pieces = c.n_pieces;
+    return TOKTIER_OK;
+}
+
+extern "C" int toktier_last_status(void *workspace, void *stream, uint64_t *out_n_tokens)
+{
+    if (!workspace) return TOKTIER_E_INVALID_ARG;
+    Ctrl c;
+    int rc = read_ctrl(workspace, (hipStream_t)stream, &c);
+    if (rc) return rc;
+    if (out_n_tokens) *out_n_tokens = c.n_tokens;
+    return TOKTIER_OK;
+}

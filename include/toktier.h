@@ -1,0 +1,157 @@
+/*
+ * toktier.h -- C ABI of the MI355X (gfx950) exact full-request tokenizer.
+ *
+ * The library tokenizes whole requests on one GPU the way a serial GPT-family tokenizer does, bit
+ * for bit (TokTier: Exact Stateful CPU+GPU Tokenization for Agentic LLM Serving, arXiv 2607.29678;
+ * GPU full-tokenization section and Figure 6):
+ *   stage 1  regex-exact run decomposition of the pre-tokenizer: UTF-8 decode, character classes,
+ *            maximal same-class runs and a per-character piece-start rule, all by parallel scans;
+ *   stage 2  byte-level BPE of every piece independently, length-binned, merge ranks looked up in
+ *            a hash table resident in device memory; then compaction of the IDs.
+ * The concatenated IDs equal F = E* o G of the serial tokenizer (summary page, §2.2).
+ *
+ * Conventions shared by every entry point
+ *   - Every function returns an int status: TOKTIER_OK (0) or one of the TOKTIER_E_* codes below;
+ *     toktier_status_string() names it.  A failing call leaves no sticky HIP error behind.
+ *   - "device" pointers are HIP device memory of the device that was current when the vocabulary
+ *     was loaded; "host" pointers are ordinary process memory.
+ *   - All device buffers passed in (input bytes, offsets, outputs, workspace) are owned by the
+ *     caller.  The library owns only the vocabulary handle and the device tables behind it.
+ *   - toktier_encode_batch and toktier_pretokenize_batch allocate nothing: every scratch byte lives
+ *     in the caller's workspace, and all their work is enqueued on the caller's stream.
+ *   - Calls on different streams are independent when they use different workspaces; a workspace
+ *     must not be shared by two calls in flight.  Results never depend on earlier calls.
+ */
+#ifndef TOKTIER_H
+#define TOKTIER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct toktier_vocab toktier_vocab;   /* opaque; immutable after load */
+
+/* Pre-tokenizer rule families (paper: the GPT-2, cl100k and o200k pattern lineages; the exact
+ * alternatives are listed in the library's design notes and implemented by the oracle). */
+enum {
+    TOKTIER_GPT2 = 1,     /* contractions ('s 't 're 've 'm 'll 'd, lowercase), ' ?' + letters,
+                             ' ?' + numbers, ' ?' + other, whitespace with lookahead */
+    TOKTIER_CL100K = 2,   /* case-insensitive contractions, one non-letter prefix + letters, digits
+                             grouped 1-3, other + trailing CR/LF, whitespace up to the last CR/LF */
+    TOKTIER_O200K = 3     /* cl100k plus a case-boundary letter rule (upper* lower+ | upper+ lower*),
+                             marks inside words, contractions as word suffixes */
+};
+
+enum {
+    TOKTIER_OK = 0,
+    TOKTIER_E_INVALID_ARG = 1,   /* null pointer, bad size, bad offsets, wrong device */
+    TOKTIER_E_BAD_FAMILY = 2,    /* family not one of the enum values above */
+    TOKTIER_E_BAD_MERGES = 3,    /* merge list rank-inconsistent, duplicated or too large */
+    TOKTIER_E_INVALID_UTF8 = 4,  /* input bytes are not valid UTF-8 (detected on the device) */
+    TOKTIER_E_CAPACITY = 5,      /* an output or the workspace is smaller than required */
+    TOKTIER_E_HIP = 6,           /* a HIP runtime call failed (see toktier_last_hip_error) */
+    TOKTIER_E_OOM = 7            /* host or device allocation failed while loading a vocabulary */
+};
+
+/* Largest merge count accepted: IDs must stay below 2^21 - 1. */
+#define TOKTIER_MAX_MERGES ((1u << 21) - 257u)
+
+/*
+ * Load a merge list and its rule family; build the device tables on the current HIP device.
+ *   merges    host, uint32[2 * n_merges]: merges[2r], merges[2r+1] are the (left, right) token IDs
+ *             joined by merge rank r, which creates token ID 256 + r (byte-level BPE: IDs 0..255
+ *             are the byte values).  Ranks are the list order; lower rank merges first.
+ *   n_merges  0 .. TOKTIER_MAX_MERGES.
+ *   family    TOKTIER_GPT2 / TOKTIER_CL100K / TOKTIER_O200K.
+ *   out       receives the handle; unchanged on failure.
+ * The list must be rank-consistent: left, right < 256 + r for every rank r, and no (left, right)
+ * pair may appear twice.  The GPU merges every leftmost non-overlapping occurrence of the minimum
+ * rank pair in one round (paper, GPU BPE paragraph); that schedule equals the serial textbook loop
+ * exactly when the list is rank-consistent, so other lists are rejected with TOKTIER_E_BAD_MERGES.
+ * Errors: E_INVALID_ARG, E_BAD_FAMILY, E_BAD_MERGES, E_OOM, E_HIP.  Synchronous.
+ */
+int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int family, toktier_vocab **out);
+
+/* Release a handle and its device tables (synchronizes the device).  NULL is accepted. */
+int toktier_free_vocab(toktier_vocab *v);
+
+/* Vocabulary facts: number of merges and family (either pointer may be NULL). */
+int toktier_vocab_info(const toktier_vocab *v, uint32_t *n_merges, int *family);
+
+/*
+ * Workspace size (bytes) that toktier_encode_batch / toktier_pretokenize_batch need for a batch of
+ * total_bytes input bytes in n_docs documents.  Pure host arithmetic; no device call.
+ * Errors: E_INVALID_ARG (total_bytes >= 2^32 - 1 or n_docs == 0xFFFFFFFF).
+ */
+int toktier_workspace_bytes(uint64_t total_bytes, uint32_t n_docs, uint64_t *out_bytes);
+
+/*
+ * Tokenize a batch of documents (paper: multi-document batches are concatenated and runs are cut
+ * at document boundaries).
+ *   v            vocabulary handle (its device must be the current device).
+ *   bytes        device, uint8[total_bytes]: the documents' UTF-8 text, concatenated.
+ *   offsets      device, uint64[n_docs + 1]: document d is bytes[offsets[d], offsets[d+1]);
+ *                offsets[0] = 0, non-decreasing, offsets[n_docs] = total_bytes.  Empty documents
+ *                are allowed.  Every document is tokenized on its own (its first and last
+ *                characters see the start and end of text).
+ *   n_docs       number of documents (>= 1).
+ *   total_bytes  < 2^32 - 1.
+ *   out_ids      device, uint32[ids_capacity]: receives the token IDs of all documents in order.
+ *   ids_capacity must be >= total_bytes (a token is never shorter than one byte, so this always
+ *                suffices); otherwise TOKTIER_E_CAPACITY before any device work.
+ *   out_offsets  device, uint64[n_docs + 1]: out_offsets[d] is the index in out_ids of document
+ *                d's first token; out_offsets[n_docs] is the total token count.
+ *   workspace    device scratch of at least toktier_workspace_bytes(total_bytes, n_docs) bytes,
+ *                256-byte aligned; contents on entry do not matter.
+ *   stream       hipStream_t (passed as void*); NULL means the default stream.
+ *   out_n_tokens host; if non-NULL the call waits for the stream and stores the token count
+ *                there (one device-to-host read).  If NULL the call returns right after enqueueing
+ *                and the result (and any device-detected error) is only visible through
+ *                out_offsets[n_docs] and a later call to toktier_last_status on the workspace.
+ * Errors: E_INVALID_ARG, E_CAPACITY, E_HIP, and (only when out_n_tokens is non-NULL)
+ *         E_INVALID_UTF8 / E_INVALID_ARG for bad bytes or offsets found on the device; the output
+ *         contents are then unspecified.
+ */
+int toktier_encode_batch(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                         uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
+                         uint64_t ids_capacity, uint64_t *out_offsets, void *workspace,
+                         uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens);
+
+/*
+ * Stage 1 alone, for split-level checks (paper, exactness section: boundaries are compared apart
+ * from IDs because an ID comparison can hide a wrong split).  Runs exactly the pre-tokenization
+ * kernels that toktier_encode_batch runs and copies the piece starts out.
+ *   out_piece_starts  device, uint32[starts_capacity]: byte offset of every piece start in input
+ *                     order, followed by total_bytes as a sentinel.
+ *   starts_capacity   must be >= total_bytes + 1.
+ *   out_n_pieces      host, required: receives the number of pieces (synchronizes the stream).
+ * Other arguments as in toktier_encode_batch.  Errors as in toktier_encode_batch.
+ */
+int toktier_pretokenize_batch(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                              uint32_t n_docs, uint64_t total_bytes, uint32_t *out_piece_starts,
+                              uint64_t starts_capacity, void *workspace, uint64_t workspace_bytes,
+                              void *stream, uint64_t *out_n_pieces);
+
+/*
+ * Status that the device recorded in a workspace during the last call that used it (waits for the
+ * stream).  Lets callers of the asynchronous form (out_n_tokens == NULL) check for invalid input.
+ *   out_n_tokens  host, may be NULL: token count of that call.
+ */
+int toktier_last_status(void *workspace, void *stream, uint64_t *out_n_tokens);
+
+/* Static English text for a status code. */
+const char *toktier_status_string(int status);
+
+/* Text of the last HIP error seen by this thread inside the library (empty if none). */
+const char *toktier_last_hip_error(void);
+
+/* SHA-256 (hex) of the library's frozen Unicode category table. */
+const char *toktier_unicode_table_sha256(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKTIER_H */

@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, bit for bit.
+
+Split level (piece boundaries) and ID level (token IDs and per-document offsets) on the five
+workloads at full size, on fuzz batches of stress strings, and on the edge cases: empty and ragged
+documents, single characters, invalid UTF-8, bad offsets, capacity limits, history independence
+(TokTier, arXiv 2607.29678, shadow-verifier paragraph: a production tokenizer returned different IDs
+after one earlier encode of a long prefix) and batch-composition independence.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import compare_ids, compare_starts
+from workloads import textgen
+
+pytestmark = pytest.mark.gpu
+
+FAMS = ("gpt2", "cl100k", "o200k")
+STRESS = ["a", "B", "s", "t", "r", "e", "1", "٣", " ", "\t", "\r", "\n", "\xa0", "'", ".", "中", "́", "ǅ",
+          "ʰ", "\xbd", "S", "T", "l", "v", "d", "m", "M", "D", "\x85", "\x0c", "　", "\x1c", "ः", "\U0001F600",
+          "/", "9", "E", "R", "V"]
+
+
+def _say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def tt():
+    import torch
+    import exact_bpe_tokenization_amd as tt
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tt.lib()
+    return tt
+
+
+_TOK = {}
+
+
+def tokenizer(tt, vocab_name):
+    if vocab_name not in _TOK:
+        merges, fam = textgen.load_vocab(vocab_name)
+        _TOK[vocab_name] = (tt.Tokenizer(merges, fam), merges, fam)
+    return _TOK[vocab_name]
+
+
+_BARE = {}
+
+
+def bare(tt, fam):
+    """A tokenizer with an empty merge list (for split-level checks of a family)."""
+    if fam not in _BARE:
+        _BARE[fam] = tt.Tokenizer(np.zeros((0, 2), np.uint32), fam)
+    return _BARE[fam]
+
+
+def _batch(strings):
+    return textgen.to_batch(strings)
+
+
+@pytest.mark.parametrize("family", FAMS)
+def test_split_exhaustive_short(tt, family):
+    strings = ["".join(t) for L in range(1, 4) for t in itertools.product(STRESS[:20], repeat=L)]
+    data, offs = _batch(strings)
+    _say("split exhaustive", family, data.size, len(strings))
+    got = bare(tt, family).pretokenize(data.tobytes(), offs)
+    compare_starts(oracle.pretokenize(family, data, offs), got, data)
+
+
+@pytest.mark.parametrize("family", FAMS)
+@pytest.mark.parametrize("seed", [1, 2])
+def test_split_random_stress(tt, family, seed):
+    rng = np.random.default_rng(seed)
+    strings = ["".join(STRESS[int(i)] for i in rng.integers(0, len(STRESS), int(rng.integers(1, 40))))
+               for _ in range(30000)]
+    # some long single-class runs across tile boundaries
+    strings += [" " * 5000 + "x", "\n" * 4097, "a" * 9000, "1" * 10001, "中" * 3000, "A" * 4100 + "b",
+                "\t \t" * 3000 + "\n" + " " * 4096, "Ab" * 5000, "́" * 2000, "'" * 5000 + "s"]
+    data, offs = _batch(strings)
+    _say("split random", family, seed, data.size)
+    got = bare(tt, family).pretokenize(data.tobytes(), offs)
+    compare_starts(oracle.pretokenize(family, data, offs), got, data)
+
+
+@pytest.mark.parametrize("name", list(textgen.WORKLOADS))
+def test_split_workloads(tt, name):
+    fam, voc, data, offs = textgen.workload(name)
+    _say("split workload", name, data.size)
+    got = tokenizer(tt, voc)[0].pretokenize(data.tobytes(), offs)
+    compare_starts(oracle.pretokenize(fam, data, offs), got, data)
+
+
+@pytest.mark.parametrize("name", list(textgen.WORKLOADS))
+@pytest.mark.parametrize("scale", [0.01, 1.0])
+def test_ids_workloads(tt, name, scale):
+    fam, voc, data, offs = textgen.workload(name, scale)
+    tok, merges, _ = tokenizer(tt, voc)
+    _say("ids workload", name, scale, data.size)
+    ids, oo = tok.encode(data.tobytes(), offs)
+    eids, eoo = oracle.encode_batch(fam, merges, data, offs)
+    compare_ids(eids, eoo, ids, oo)
+
+
+@pytest.mark.parametrize("voc", ["v1", "v2", "v3", "v4"])
+def test_ids_invariants(tt, voc):
+    tok, merges, fam = tokenizer(tt, voc)
+    data, offs = _batch([textgen.multilingual(200 + i, 3000 + 17 * i) for i in range(8)])
+    _say("invariants", voc, data.size)
+    ids, oo = tok.encode(data.tobytes(), offs)
+    assert oracle.decode(merges, ids) == data.tobytes()
+    assert ids.size == 0 or int(ids.max()) < 256 + merges.shape[0]
+    eids, eoo = oracle.encode_batch(fam, merges, data, offs)
+    compare_ids(eids, eoo, ids, oo)
+
+
+def test_edge_cases(tt):
+    tok, merges, fam = tokenizer(tt, "v2")
+    cases = [
+        [""], ["", ""], ["a"], [" "], ["\n"], ["", "a", "", "", "bc", ""], ["x" * 4095, "y"], ["z" * 4096],
+        ["q" * 4097], ["中"], ["\U0010FFFF"], ["a'", "s"], ["12", "34"], ["x\n", "\ny"], [" " * 4096 + "a"],
+    ]
+    for strings in cases:
+        data, offs = _batch(strings)
+        _say("edge", [s[:10] for s in strings], data.size)
+        ids, oo = tok.encode(data.tobytes(), offs)
+        eids, eoo = oracle.encode_batch(fam, merges, data, offs)
+        compare_ids(eids, eoo, ids, oo)
+
+
+def test_giant_pieces(tt):
+    tok, merges, fam = tokenizer(tt, "v2")
+    rng = np.random.default_rng(9)
+    az = "abcdefghijklmnopqrstuvwxyz"
+    strings = ["a" * 20000, "".join(az[int(i)] for i in rng.integers(0, 26, 30000)), " " * 20000 + "x",
+               "\t" * 9000, "\r\n" * 6000 + "y", "ab" * 7000]
+    data, offs = _batch(strings)
+    _say("giant", data.size)
+    ids, oo = tok.encode(data.tobytes(), offs)
+    eids, eoo = oracle.encode_batch(fam, merges, data, offs)
+    compare_ids(eids, eoo, ids, oo)
+
+
+def test_history_independence(tt):
+    tok, merges, fam = tokenizer(tt, "v4")
+    x = textgen.agent_transcript(301, 20000).encode()
+    prefix = textgen.agent_transcript(302, 200000).encode()
+    _say("history", len(x), len(prefix))
+    a = tok.encode(x)
+    tok.encode(prefix)
+    tok.encode(prefix + x)
+    b = tok.encode(x)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_batch_composition_independence(tt):
+    tok, merges, fam = tokenizer(tt, "v4")
+    docs = [textgen.agent_transcript(400 + i, 1000 + 977 * i).encode() for i in range(12)]
+    data, offs = _batch([d.decode() for d in docs])
+    _say("composition", data.size)
+    ids, oo = tok.encode(data.tobytes(), offs)
+    for i, d in enumerate(docs):
+        one, _ = tok.encode(d)
+        assert np.array_equal(one, ids[oo[i]:oo[i + 1]]), i
+
+
+@pytest.mark.parametrize("bad", [b"\x80", b"ab\xc0\xafcd", b"\xed\xa0\x80", b"\xf4\x90\x80\x80", b"x\xe4\xb8",
+                                 b"\xff", b"abc\xc3"])
+def test_invalid_utf8(tt, bad):
+    tok, merges, fam = tokenizer(tt, "v2")
+    data = b"hello world " * 1000 + bad + b" tail"
+    _say("invalid utf8", bad)
+    with pytest.raises(tt.ToktierError) as e:
+        tok.encode(data)
+    assert e.value.status == 4
+    # the library stays usable and exact after the error
+    good = b"hello world, it's fine 123"
+    ids, oo = tok.encode(good)
+    eids, eoo = oracle.encode_batch(fam, merges, good)
+    compare_ids(eids, eoo, ids, oo)
+
+
+def test_doc_boundary_inside_char_is_invalid(tt):
+    tok, _, _ = tokenizer(tt, "v2")
+    data = "ab中cd".encode()
+    _say("doc boundary inside char")
+    with pytest.raises(tt.ToktierError) as e:
+        tok.encode(data, [0, 3, len(data)])
+    assert e.value.status == 4
+
+
+def test_bad_offsets_and_capacity(tt):
+    import torch
+    tok, _, _ = tokenizer(tt, "v2")
+    _say("bad offsets")
+    with pytest.raises(tt.ToktierError) as e:
+        tok.encode(b"abcdef", [0, 4, 2, 6])
+    assert e.value.status == 1
+    data = torch.zeros(100, dtype=torch.uint8, device="cuda") + 97
+    offs = torch.tensor([0, 100], dtype=torch.int64, device="cuda")
+    ws = torch.empty(tt.toktier_workspace_bytes(100, 1), dtype=torch.uint8, device="cuda")
+    out_offs = torch.empty(2, dtype=torch.int64, device="cuda")
+    small = torch.empty(99, dtype=torch.int32, device="cuda")
+    with pytest.raises(tt.ToktierError) as e:
+        tt.toktier_encode_batch(tok.vocab, data, offs, small, out_offs, ws)
+    assert e.value.status == 5
+    with pytest.raises(tt.ToktierError) as e:
+        tt.toktier_encode_batch(tok.vocab, data, offs, torch.empty(100, dtype=torch.int32, device="cuda"),
+                                out_offs, ws[:1000])
+    assert e.value.status == 5
+
+
+def test_async_call_and_last_status(tt):
+    import torch
+    tok, merges, fam = tokenizer(tt, "v2")
+    text = textgen.agent_transcript(7, 50000).encode()
+    d = torch.frombuffer(bytearray(text), dtype=torch.uint8).cuda()
+    o = torch.tensor([0, len(text)], dtype=torch.int64, device="cuda")
+    _say("async")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ids, oo, nt = tok.encode_device(d, o, stream=s, sync=False)
+    assert nt is None
+    n = tt.toktier_last_status(tok.workspace[: tt.toktier_workspace_bytes(len(text), 1)], stream=s)
+    eids, eoo = oracle.encode_batch(fam, merges, text)
+    torch.cuda.synchronize()
+    compare_ids(eids, eoo, ids[:n].cpu().numpy().view(np.uint32), oo.cpu().numpy().astype(np.uint64))

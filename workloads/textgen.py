@@ -11,6 +11,7 @@ hashes, timestamps and mixed LF/CRLF line ends (AT), a multilingual mix with CJK
 combining marks, and an adversarial request built from long single-class runs.
 """
 import hashlib
+import os
 
 import numpy as np
 
@@ -437,3 +438,12 @@ def corpus(vocab_name):
     fam, n_merges, gen, size, seed = VOCABS[vocab_name]
     text = globals()[gen](seed, size)
     return text.encode("utf-8")
+
+
+_VOCAB_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "vocabs")
+
+
+def load_vocab(name):
+    """Merge list (uint32[n, 2]) and family of a stored vocabulary (written by oracle/train_vocabs.py)."""
+    with np.load(os.path.join(_VOCAB_DIR, name + ".npz"), allow_pickle=False) as z:
+        return z["merges"].astype(np.uint32), str(z["family"])
