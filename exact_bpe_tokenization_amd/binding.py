@@ -20,8 +20,13 @@ STATUS = {0: "TOKTIER_OK", 1: "TOKTIER_E_INVALID_ARG", 2: "TOKTIER_E_BAD_FAMILY"
 
 # every symbol declared in include/toktier.h
 EXPORTS = ("toktier_load_vocab", "toktier_free_vocab", "toktier_vocab_info", "toktier_workspace_bytes",
-           "toktier_encode_batch", "toktier_pretokenize_batch", "toktier_last_status",
-           "toktier_status_string", "toktier_last_hip_error", "toktier_unicode_table_sha256")
+           "toktier_encode_batch", "toktier_encode_batch_timed", "toktier_pretokenize_batch",
+           "toktier_last_status", "toktier_status_string", "toktier_last_hip_error",
+           "toktier_unicode_table_sha256")
+
+# kernel launches of one encode call, in stream order (TOKTIER_K_* in toktier.h)
+KERNELS = ("init", "classify", "pieces", "bins", "bpe_lane", "bpe_wave", "bpe_block", "bpe_giant", "tokscan",
+           "gather", "docoff")
 
 
 class ToktierError(RuntimeError):
@@ -54,6 +59,7 @@ def lib():
     L.toktier_vocab_info.argtypes = [vp, ctypes.POINTER(u32), ctypes.POINTER(i32)]
     L.toktier_workspace_bytes.argtypes = [u64, u32, u64p]
     L.toktier_encode_batch.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, u64, vp, u64p]
+    L.toktier_encode_batch_timed.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, u64, vp, u64p, vp, vp]
     L.toktier_pretokenize_batch.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, u64, vp, u64p]
     L.toktier_last_status.argtypes = [vp, vp, u64p]
     for f in ("toktier_status_string",):
@@ -149,6 +155,52 @@ def toktier_encode_batch(vocab, data, offsets, out_ids, out_offsets, workspace, 
                                     workspace.numel(), _stream(stream), ctypes.byref(n_tok) if sync else None)
     _check(rc, "toktier_encode_batch")
     return n_tok.value if sync else None
+
+
+def toktier_encode_batch_timed(vocab, data, offsets, out_ids, out_offsets, workspace, events_before,
+                               events_after, stream=None, sync=True):
+    """toktier_encode_batch plus HIP events recorded around each kernel launch.  events_before /
+    events_after: sequences of len(KERNELS) raw hipEvent_t handles (ints) or None."""
+    arr_t = ctypes.c_void_p * len(KERNELS)
+    eb = arr_t(*[e or None for e in events_before]) if events_before is not None else None
+    ea = arr_t(*[e or None for e in events_after]) if events_after is not None else None
+    n_tok = ctypes.c_uint64()
+    rc = lib().toktier_encode_batch_timed(vocab.handle, _ptr(data), _ptr(offsets), offsets.numel() - 1,
+                                          data.numel(), _ptr(out_ids), out_ids.numel(), _ptr(out_offsets),
+                                          _ptr(workspace), workspace.numel(), _stream(stream),
+                                          ctypes.byref(n_tok) if sync else None, eb, ea)
+    _check(rc, "toktier_encode_batch_timed")
+    return n_tok.value if sync else None
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch has loaded (for per-kernel timing)."""
+
+    def __init__(self, count):
+        torch.cuda.init()
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(count):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise ToktierError(6, "hipEventCreate")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        if self._hip.hipEventSynchronize(ctypes.c_void_p(b)) != 0:
+            raise ToktierError(6, "hipEventSynchronize")
+        if self._hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise ToktierError(6, "hipEventElapsedTime")
+        return out.value
+
+    def __del__(self):
+        for h in getattr(self, "handles", []):
+            self._hip.hipEventDestroy(ctypes.c_void_p(h))
 
 
 def toktier_pretokenize_batch(vocab, data, offsets, out_starts, workspace, stream=None):

@@ -7,9 +7,12 @@
 // that pair equals iterated single merges (for rank-consistent merge lists, which the loader
 // enforces); only pairs next to a completed merge need a new lookup.
 //
-//   k_bpe_lane   one lane per piece of <= 16 bytes; sequence and ranks in registers; the textbook
+//   k_bpe_lookup every piece of <= 32 bytes: one probe of a whole-piece table resolves the pieces
+//                that encode to a single token; the rest are listed for
+//   k_bpe_lane   one lane per listed piece (two register-array sizes: <= 16, 17..32 bytes);
+//                sequence and ranks in registers; the textbook
 //                loop (leftmost lowest rank, merge, re-probe the two neighbours)
-//   k_bpe_block  one wavefront (pieces of 17..1024 bytes) or one 256-lane workgroup (up to 4096
+//   k_bpe_block  one wavefront (pieces of 33..1024 bytes) or one 256-lane workgroup (up to 4096
 //                bytes) per piece; sequence in LDS; rounds: block-min of ranks, selection of the
 //                leftmost non-overlapping occurrences, prefix-sum compaction, neighbour re-probes
 //   k_bpe_giant  one 1024-lane workgroup per piece longer than that; the same rounds over device
@@ -25,57 +28,149 @@ constexpr uint32_t PENDING = 0xFFFFFFFEu;
 // ---------------------------------------------------------------------------------------------
 // lane per piece
 
-__global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__restrict__ bytes,
-                                                  uint8_t *ws, Layout L)
+// ---------------------------------------------------------------------------------------------
+// whole-piece lookup: a piece whose BPE result is a single token is found with one probe.  The
+// tables hold exactly the tokens t whose own byte string encodes to [t] (established at load time
+// by these same kernels), so a hit is the exact BPE result.
+
+__device__ __forceinline__ bool whole_piece(const DevVocab &v, const uint8_t *__restrict__ src, uint32_t len,
+                                            uint32_t *id)
+{
+    if (len <= WA_MAX) {
+        if (!v.wa) return false;
+        uint64_t key = (uint64_t)len << 56;
+#pragma unroll
+        for (uint32_t k = 0; k < WA_MAX; ++k)
+            if (k < len) key |= (uint64_t)src[k] << (8 * k);
+        uint32_t h = (uint32_t)wa_hash(key, v.wa_shift);
+        for (;;) {
+            const uint4 sl = v.wa[h];
+            const uint64_t sk = (uint64_t)sl.x | ((uint64_t)sl.y << 32);
+            if (sk == key) { *id = sl.z; return true; }
+            if (sk == 0) return false;
+            h = (h + 1) & v.wa_mask;
+        }
+    }
+    if (!v.wb) return false;
+    uint64_t k4[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (uint32_t k = 0; k < (uint32_t)LANE_MAX; ++k)
+        if (k < len) k4[k >> 3] |= (uint64_t)src[k] << (8 * (k & 7));
+    uint32_t h = (uint32_t)wb_hash(k4[0], k4[1], k4[2], k4[3], len, v.wb_shift);
+    for (;;) {
+        const uint4 c = v.wb[3 * h + 2];
+        if (c.x == 0) return false;
+        if (c.x == len) {
+            const uint4 a = v.wb[3 * h], b = v.wb[3 * h + 1];
+            if (((uint64_t)a.x | ((uint64_t)a.y << 32)) == k4[0] && ((uint64_t)a.z | ((uint64_t)a.w << 32)) == k4[1] &&
+                ((uint64_t)b.x | ((uint64_t)b.y << 32)) == k4[2] && ((uint64_t)b.z | ((uint64_t)b.w << 32)) == k4[3]) {
+                *id = c.y;
+                return true;
+            }
+        }
+        h = (h + 1) & v.wb_mask;
+    }
+}
+
+// every piece of <= 32 bytes: single bytes and whole-piece hits are written directly; the rest go
+// to the two miss lists (<= 16 bytes, 17..32 bytes) for the lane kernels
+__global__ __launch_bounds__(256) void k_bpe_lookup(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
+                                                    Layout L)
+{
+    __shared__ uint32_t scnt[2], sbase[2];
+    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    uint32_t *ntok = (uint32_t *)(ws + L.ntok);
+    uint32_t *scratch = (uint32_t *)(ws + L.scratch);
+    uint32_t *lists[2] = {(uint32_t *)(ws + L.miss16), (uint32_t *)(ws + L.miss32)};
+    const uint32_t np = ctrl->n_pieces;
+    const uint32_t tid = threadIdx.x;
+    for (uint32_t p0 = blockIdx.x * blockDim.x; p0 < np; p0 += gridDim.x * blockDim.x) {
+        if (tid < 2) scnt[tid] = 0;
+        __syncthreads();
+        const uint32_t p = p0 + tid;
+        int miss = -1;
+        if (p < np) {
+            const uint32_t b0 = pstart[p];
+            const uint32_t len = pstart[p + 1] - b0;
+            uint32_t id;
+            if (len == 1) {
+                scratch[b0] = bytes[b0];
+                ntok[p] = 1;
+            } else if (len <= (uint32_t)LANE_MAX) {
+                if (whole_piece(v, bytes + b0, len, &id)) {
+                    scratch[b0] = id;
+                    ntok[p] = 1;
+                } else {
+                    miss = len <= 16 ? 0 : 1;
+                }
+            }
+        }
+        const uint32_t local = miss >= 0 ? atomicAdd(&scnt[miss], 1u) : 0u;
+        __syncthreads();
+        if (tid < 2 && scnt[tid]) sbase[tid] = atomicAdd(&ctrl->miss_count[tid], scnt[tid]);
+        __syncthreads();
+        if (miss >= 0) lists[miss][sbase[miss] + local] = p;
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// lane per piece (pieces the lookup did not resolve)
+
+template <int MAXL>
+__global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
+                                                  Layout L, int which)
 {
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *ntok = (uint32_t *)(ws + L.ntok);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
-    const uint32_t np = ctrl->n_pieces;
-    for (uint32_t p = blockIdx.x * blockDim.x + threadIdx.x; p < np; p += gridDim.x * blockDim.x) {
+    const uint32_t *list = (const uint32_t *)(ws + (which ? L.miss32 : L.miss16));
+    const uint32_t count = ctrl->miss_count[which];
+    for (uint32_t q = blockIdx.x * blockDim.x + threadIdx.x; q < count; q += gridDim.x * blockDim.x) {
+        const uint32_t p = list[q];
         const uint32_t b0 = pstart[p];
         const uint32_t len = pstart[p + 1] - b0;
-        if (len > LANE_MAX) continue;
-        uint32_t id[LANE_MAX], rk[LANE_MAX];
+        uint32_t id[MAXL], rk[MAXL];
 #pragma unroll
-        for (int k = 0; k < LANE_MAX; ++k) id[k] = (uint32_t)k < len ? (uint32_t)bytes[b0 + k] : 0u;
+        for (int k = 0; k < MAXL; ++k) id[k] = (uint32_t)k < len ? (uint32_t)bytes[b0 + k] : 0u;
 #pragma unroll
-        for (int k = 0; k < LANE_MAX; ++k)
-            rk[k] = (uint32_t)(k + 1) < len ? __ldg(v.r2 + ((id[k] << 8) | id[(k + 1) % LANE_MAX])) : NO_RANK;
+        for (int k = 0; k < MAXL; ++k)
+            rk[k] = (uint32_t)(k + 1) < len ? __ldg(v.r2 + ((id[k] << 8) | id[(k + 1) % MAXL])) : NO_RANK;
         uint32_t n = len;
         for (;;) {
             uint32_t best = NO_RANK, pos = 0;
 #pragma unroll
-            for (int k = 0; k < LANE_MAX - 1; ++k)
+            for (int k = 0; k < MAXL - 1; ++k)
                 if (rk[k] < best) { best = rk[k]; pos = k; }
             if (best == NO_RANK) break;
             const uint32_t nid = 256u + best;
             // id[pos] <- nid, drop id[pos+1], shift the tail left
 #pragma unroll
-            for (int j = 0; j < LANE_MAX; ++j) {
-                uint32_t nx_id = j + 1 < LANE_MAX ? id[(j + 1) % LANE_MAX] : 0u;
-                uint32_t nx_rk = j + 1 < LANE_MAX ? rk[(j + 1) % LANE_MAX] : NO_RANK;
+            for (int j = 0; j < MAXL; ++j) {
+                uint32_t nx_id = j + 1 < MAXL ? id[(j + 1) % MAXL] : 0u;
+                uint32_t nx_rk = j + 1 < MAXL ? rk[(j + 1) % MAXL] : NO_RANK;
                 id[j] = (uint32_t)j < pos ? id[j] : ((uint32_t)j == pos ? nid : nx_id);
                 rk[j] = (uint32_t)j < pos ? rk[j] : nx_rk;
             }
             --n;
             uint32_t left = 0, right = 0;
 #pragma unroll
-            for (int j = 0; j < LANE_MAX; ++j) {
+            for (int j = 0; j < MAXL; ++j) {
                 if ((uint32_t)j + 1 == pos) left = id[j];
                 if ((uint32_t)j == pos + 1) right = id[j];
             }
             const uint32_t rl = pos > 0 ? pair_rank(v, left, nid) : NO_RANK;
             const uint32_t rr = pos + 1 < n ? pair_rank(v, nid, right) : NO_RANK;
 #pragma unroll
-            for (int j = 0; j < LANE_MAX; ++j) {
+            for (int j = 0; j < MAXL; ++j) {
                 if ((uint32_t)j + 1 == pos) rk[j] = rl;
                 if ((uint32_t)j == pos) rk[j] = rr;
             }
         }
 #pragma unroll
-        for (int k = 0; k < LANE_MAX; ++k)
+        for (int k = 0; k < MAXL; ++k)
             if ((uint32_t)k < n) scratch[b0 + k] = id[k];
         ntok[p] = n;
     }
@@ -193,15 +288,15 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
                 if (k0 + e < n) lmin = min(lmin, srk[k0 + e]);
             const uint32_t rmin = block_min<NT>(lmin, red);
             if (rmin >= v.n_merges) break;   // NO_RANK: nothing left to merge
-            const bool selfpair = v.merges[2 * rmin] == v.merges[2 * rmin + 1];
             uint32_t hitm = 0;
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 if (k0 + e < n && srk[k0 + e] == rmin) hitm |= 1u << e;
             uint32_t selm = hitm;
-            if (selfpair) {
-                // overlapping occurrences (x, x)(x, x): inside each chain of consecutive hits keep
-                // the ones at an even distance from the chain's start
+            {
+                // leftmost non-overlapping occurrences: consecutive hits only arise for a pair (x, x);
+                // inside each chain of consecutive hits keep the ones at an even distance from the
+                // chain's start (for any other pair every hit starts its own chain)
                 const bool prev_hit = k0 >= 1 && k0 - 1 < n && srk[k0 - 1] == rmin;
                 int32_t last_start = -1;
 #pragma unroll
@@ -262,20 +357,30 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
 }
 
 // ---------------------------------------------------------------------------------------------
-// giant pieces: one workgroup each, sequence double-buffered in device memory
+// giant pieces: one workgroup each; the sequence lives in device memory (double-buffered) and each
+// round streams it through LDS in coalesced tiles, carrying the chain state and the output offset
+// from tile to tile.  The next round's minimum rank is gathered while writing and re-probing.
+
+constexpr int GE = 8;                       // elements per thread per tile
+constexpr int GTILE = GIANT_THREADS * GE;   // 8192
 
 __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const uint8_t *__restrict__ bytes,
                                                              uint8_t *ws, Layout L)
 {
     constexpr int NT = GIANT_THREADS;
+    __shared__ uint32_t sid[GTILE];
+    __shared__ uint32_t srk[GTILE + 1];
+    __shared__ uint8_t ssel[GTILE + 1];
     __shared__ uint32_t red[NT / 64 + 1];
     __shared__ int32_t redi[NT / 64 + 1];
+    __shared__ int32_t s_last_cs;
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *ntok = (uint32_t *)(ws + L.ntok);
     const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
     const uint32_t count = ctrl->bin_count[2];
     const uint32_t tid = threadIdx.x;
+    const uint32_t i0 = tid * GE;
 
     for (uint32_t q = blockIdx.x; q < count; q += gridDim.x) {
         const uint32_t p = list[q];
@@ -284,76 +389,95 @@ __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const u
         uint32_t *idA = (uint32_t *)(ws + L.scratch) + b0, *idB = (uint32_t *)(ws + L.g_ids) + b0;
         uint32_t *rkA = (uint32_t *)(ws + L.g_rank_a) + b0, *rkB = (uint32_t *)(ws + L.g_rank_b) + b0;
         for (uint32_t k = tid; k < n; k += NT) idA[k] = bytes[b0 + k];
-        __syncthreads();
-        for (uint32_t k = tid; k < n; k += NT)
-            rkA[k] = k + 1 < n ? __ldg(v.r2 + ((idA[k] << 8) | idA[k + 1])) : NO_RANK;
-        __syncthreads();
-        for (;;) {
-            const uint32_t E = (n + NT - 1) / NT;
-            const uint32_t k0 = min(n, tid * E), k1 = min(n, k0 + E);
-            uint32_t lmin = NO_RANK;
-            for (uint32_t k = k0; k < k1; ++k) lmin = min(lmin, rkA[k]);
-            const uint32_t rmin = block_min<NT>(lmin, red);
-            if (rmin >= v.n_merges) break;   // NO_RANK: nothing left to merge
-            const bool selfpair = v.merges[2 * rmin] == v.merges[2 * rmin + 1];
-            auto hit = [&](uint32_t k) -> bool { return k < n && rkA[k] == rmin; };
-            // chain starts (only matter for self pairs)
-            int32_t last_start = -1;
-            if (selfpair)
-                for (uint32_t k = k0; k < k1; ++k)
-                    if (hit(k) && !(k >= 1 && hit(k - 1))) last_start = (int32_t)k;
-            const int32_t carry = selfpair ? block_excl_max<NT>(last_start, redi) : -1;
-            // selection of element k given the current chain start
-            int32_t cs = carry;
-            auto sel_at = [&](uint32_t k, int32_t &c) -> bool {
-                bool h = hit(k);
-                if (!selfpair) return h;
-                if (h && !(k >= 1 && hit(k - 1))) c = (int32_t)k;
-                return h && (((int32_t)k - c) & 1) == 0;
-            };
-            // was the element before my range selected?
-            bool prev_sel = false;
-            if (k0 >= 1 && k0 < k1) {
-                int32_t c2 = carry;   // chain start covering k0 - 1 (valid when it is a hit)
-                prev_sel = hit(k0 - 1) && (!selfpair || (((int32_t)(k0 - 1) - c2) & 1) == 0);
-            }
-            uint32_t cnt = 0;
-            {
-                bool ps = prev_sel;
-                int32_t c = cs;
-                for (uint32_t k = k0; k < k1; ++k) {
-                    bool s = sel_at(k, c);
-                    if (!ps) ++cnt;
-                    ps = s;
+        uint32_t lmin = NO_RANK;
+        for (uint32_t k = tid; k < n; k += NT) {
+            uint32_t r = k + 1 < n ? __ldg(v.r2 + ((uint32_t)bytes[b0 + k] << 8 | bytes[b0 + k + 1])) : NO_RANK;
+            rkA[k] = r;
+            lmin = min(lmin, r);
+        }
+        uint32_t rmin = block_min<NT>(lmin, red);   // (contains a barrier: idA/rkA are visible)
+        while (rmin < v.n_merges) {
+            uint32_t out = 0;                  // uniform: output elements written so far
+            bool c_hit = false, c_sel = false; // previous tile's last element
+            int32_t c_cs = -1;                 // chain start of that element (when it is a hit)
+            uint32_t nmin = NO_RANK;
+            for (uint32_t t0 = 0; t0 < n; t0 += GTILE) {
+                const uint32_t cnt_t = min((uint32_t)GTILE, n - t0);
+                for (uint32_t i = tid; i < cnt_t; i += NT) { sid[i] = idA[t0 + i]; srk[i] = rkA[t0 + i]; }
+                if (tid == 0) srk[cnt_t] = t0 + cnt_t < n ? rkA[t0 + cnt_t] : NO_RANK;
+                __syncthreads();
+                // selection: leftmost non-overlapping occurrences of the minimum-rank pair
+                uint32_t hitm = 0;
+#pragma unroll
+                for (int e = 0; e < GE; ++e)
+                    if (i0 + e < cnt_t && srk[i0 + e] == rmin) hitm |= 1u << e;
+                const bool prev_hit = i0 == 0 ? c_hit : (i0 <= cnt_t && srk[i0 - 1] == rmin);
+                int32_t last_start = -1;
+#pragma unroll
+                for (int e = 0; e < GE; ++e) {
+                    bool h = (hitm >> e) & 1u, hp = e ? ((hitm >> (e - 1)) & 1u) : prev_hit;
+                    if (h && !hp) last_start = (int32_t)(t0 + i0 + e);
                 }
-            }
-            uint32_t nnew;
-            const uint32_t off = block_excl_sum<NT>(cnt, red, &nnew);
-            {
-                bool ps = prev_sel;
-                int32_t c = cs;
-                uint32_t o = off;
-                bool s = k0 < k1 ? sel_at(k0, c) : false;
-                for (uint32_t k = k0; k < k1; ++k) {
-                    int32_t cn = c;
-                    bool sn = (k + 1 < n) ? sel_at(k + 1, cn) : false;
-                    if (!ps) {
-                        idB[o] = s ? 256u + rmin : idA[k];
-                        rkB[o] = (s || sn) ? PENDING : rkA[k];
-                        ++o;
-                    }
-                    ps = s;
-                    s = sn;
-                    c = cn;
+                int32_t cs = max(block_excl_max<NT>(last_start, redi), c_hit ? c_cs : -1);
+                uint32_t selm = 0;
+#pragma unroll
+                for (int e = 0; e < GE; ++e) {
+                    bool h = (hitm >> e) & 1u, hp = e ? ((hitm >> (e - 1)) & 1u) : prev_hit;
+                    if (h && !hp) cs = (int32_t)(t0 + i0 + e);
+                    if (h && (((int32_t)(t0 + i0 + e) - cs) & 1) == 0) selm |= 1u << e;
                 }
+#pragma unroll
+                for (int e = 0; e < GE; ++e)
+                    if (i0 + e < cnt_t) ssel[i0 + e] = (selm >> e) & 1u;
+                if (i0 < cnt_t && i0 + GE >= cnt_t) {
+                    // the thread holding the tile's last element: chain state for the next tile, and
+                    // whether the next tile's first element is selected
+                    const uint32_t last = cnt_t - 1 - i0;
+                    const bool lh = (hitm >> last) & 1u;
+                    s_last_cs = lh ? cs : -1;
+                    bool nh = srk[cnt_t] == rmin;
+                    int32_t ncs = lh ? cs : (int32_t)(t0 + cnt_t);
+                    ssel[cnt_t] = nh && (((int32_t)(t0 + cnt_t) - ncs) & 1) == 0;
+                }
+                __syncthreads();
+                uint32_t keepm = 0, cnt = 0;
+#pragma unroll
+                for (int e = 0; e < GE; ++e) {
+                    const uint32_t i = i0 + e;
+                    const bool dropped = i == 0 ? c_sel : (i < cnt_t + 1 && ssel[i - 1]);
+                    if (i < cnt_t && !dropped) { keepm |= 1u << e; ++cnt; }
+                }
+                uint32_t tot;
+                const uint32_t off = block_excl_sum<NT>(cnt, red, &tot);
+                uint32_t o = out + off;
+#pragma unroll
+                for (int e = 0; e < GE; ++e) {
+                    if (!((keepm >> e) & 1u)) continue;
+                    const uint32_t i = i0 + e;
+                    const bool sl = (selm >> e) & 1u;
+                    const uint32_t r = (sl || ssel[i + 1]) ? PENDING : srk[i];
+                    idB[o] = sl ? 256u + rmin : sid[i];
+                    rkB[o] = r;
+                    if (r != PENDING) nmin = min(nmin, r);
+                    ++o;
+                }
+                c_hit = srk[cnt_t - 1] == rmin;
+                c_sel = ssel[cnt_t - 1];
+                c_cs = s_last_cs;
+                out += tot;
+                __syncthreads();
             }
-            __syncthreads();
-            for (uint32_t j = off; j < off + cnt; ++j)
-                if (rkB[j] == PENDING) rkB[j] = j + 1 < nnew ? pair_rank(v, idB[j], idB[j + 1]) : NO_RANK;
-            __syncthreads();
+            // re-probe the pairs next to a merge (their right neighbours are written now)
+            for (uint32_t j = tid; j < out; j += NT) {
+                if (rkB[j] != PENDING) continue;
+                const uint32_t r = j + 1 < out ? pair_rank(v, idB[j], idB[j + 1]) : NO_RANK;
+                rkB[j] = r;
+                nmin = min(nmin, r);
+            }
+            rmin = block_min<NT>(nmin, red);
             uint32_t *t = idA; idA = idB; idB = t;
             t = rkA; rkA = rkB; rkB = t;
-            n = nnew;
+            n = out;
         }
         uint32_t *dst = (uint32_t *)(ws + L.scratch) + b0;
         if (idA != dst)
@@ -365,19 +489,35 @@ __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const u
 
 // ---------------------------------------------------------------------------------------------
 
-hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s)
+hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev)
 {
     const Layout &L = b.L;
     if (b.n == 0) return hipGetLastError();
     uint32_t g = (uint32_t)((b.n + 255) / 256);
-    hipLaunchKernelGGL(k_bpe_lane, dim3(g > 4096 ? 4096 : g), dim3(256), 0, s, v, b.bytes, b.ws, L);
-    uint32_t gw = L.cap_wave < 4096 ? L.cap_wave : 4096;
-    hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
-    uint32_t gb = L.cap_block < 1024 ? L.cap_block : 1024;
-    hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v, b.bytes,
-                       b.ws, L, 1);
-    uint32_t gg = L.cap_giant < 256 ? L.cap_giant : 256;
-    hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
+    {
+        LaunchScope k(ev, 4, s);
+        hipLaunchKernelGGL(k_bpe_lookup, dim3(g > 4096 ? 4096 : g), dim3(256), 0, s, v, b.bytes, b.ws, L);
+        hipLaunchKernelGGL((k_bpe_lane<16>), dim3(g > 2048 ? 2048 : g), dim3(256), 0, s, v, b.bytes, b.ws, L, 0);
+        uint32_t g32 = (uint32_t)((b.n / 17 + 256) / 256);
+        hipLaunchKernelGGL((k_bpe_lane<LANE_MAX>), dim3(g32 > 1024 ? 1024 : g32), dim3(256), 0, s, v, b.bytes, b.ws,
+                           L, 1);
+    }
+    {
+        LaunchScope k(ev, 5, s);
+        uint32_t gw = L.cap_wave < 4096 ? L.cap_wave : 4096;
+        hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
+    }
+    {
+        LaunchScope k(ev, 6, s);
+        uint32_t gb = L.cap_block < 1024 ? L.cap_block : 1024;
+        hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v,
+                           b.bytes, b.ws, L, 1);
+    }
+    {
+        LaunchScope k(ev, 7, s);
+        uint32_t gg = L.cap_giant < 256 ? L.cap_giant : 256;
+        hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
+    }
     return hipGetLastError();
 }
 

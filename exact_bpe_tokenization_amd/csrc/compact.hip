@@ -9,15 +9,6 @@
 
 namespace tt {
 
-__device__ __forceinline__ uint64_t ld_acquire64(const uint64_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_release64(uint64_t *p, uint64_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // tokoff[i] = sum of ntok[0..i) for i in [0, P]; tokoff[P] is the batch's token count
 __global__ __launch_bounds__(SCAN_THREADS) void k_tokscan(uint8_t *ws, Layout L)
 {
@@ -36,12 +27,18 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_tokscan(uint8_t *ws, Layout L)
     if (first > np) return;                       // nothing at or below P in this tile
     const uint64_t i0 = first + (uint64_t)tid * SCAN_PER_THREAD;
     uint32_t x[SCAN_PER_THREAD], sum = 0;
+    if (i0 + SCAN_PER_THREAD <= np) {
 #pragma unroll
-    for (int k = 0; k < SCAN_PER_THREAD; ++k) {
-        uint64_t i = i0 + k;
-        x[k] = i < np ? ntok[i] : 0u;
-        sum += x[k];
+        for (int k = 0; k < SCAN_PER_THREAD; k += 4) {
+            const uint4 w = *(const uint4 *)(ntok + i0 + k);
+            x[k] = w.x; x[k + 1] = w.y; x[k + 2] = w.z; x[k + 3] = w.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < SCAN_PER_THREAD; ++k) x[k] = i0 + k < np ? ntok[i0 + k] : 0u;
     }
+#pragma unroll
+    for (int k = 0; k < SCAN_PER_THREAD; ++k) sum += x[k];
     uint32_t inc = sum;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -55,22 +52,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_tokscan(uint8_t *ws, Layout L)
         if (w < wid) before += swsum[w];
         total += swsum[w];
     }
-    if (tid == 0) {
-        uint64_t basev = 0;
-        if (tile > 0) {
-            st_release64(flags + tile, (1ull << 62) | total);
-            int64_t pos = (int64_t)tile - 1;
-            for (;;) {
-                uint64_t f = ld_acquire64(flags + pos);
-                uint32_t flag = (uint32_t)(f >> 62);
-                if (flag == 0) { __builtin_amdgcn_s_sleep(1); continue; }
-                basev += f & ((1ull << 62) - 1);
-                if (flag == 2) break;
-                --pos;
-            }
+    if (wid == 0) {
+        if (lane == 0 && tile > 0) st_flag(flags + tile, (1ull << 62) | total);
+        const uint64_t basev = tile == 0 ? 0 : lookback_sum(flags, tile);
+        if (lane == 0) {
+            st_flag(flags + tile, (2ull << 62) | (basev + total));
+            s_base = (uint32_t)basev;
         }
-        st_release64(flags + tile, (2ull << 62) | (basev + total));
-        s_base = (uint32_t)basev;
     }
     __syncthreads();
     uint32_t run = s_base + before;
@@ -92,10 +80,32 @@ __global__ __launch_bounds__(256) void k_gather(uint8_t *ws, Layout L, uint32_t 
     const uint32_t *scratch = (const uint32_t *)(ws + L.scratch);
     const uint32_t np = ctrl->n_pieces;
     for (uint32_t p = blockIdx.x * blockDim.x + threadIdx.x; p < np; p += gridDim.x * blockDim.x) {
-        const uint32_t *src = scratch + pstart[p];
+        const uint32_t b0 = pstart[p];
+        if (pstart[p + 1] - b0 > LANE_MAX) continue;       // binned pieces: k_gather_long
+        const uint32_t *src = scratch + b0;
         uint32_t *dst = out_ids + tokoff[p];
         const uint32_t c = ntok[p];
         for (uint32_t j = 0; j < c; ++j) dst[j] = src[j];
+    }
+}
+
+// one workgroup per binned (longer than a lane's limit) piece
+__global__ __launch_bounds__(256) void k_gather_long(uint8_t *ws, Layout L, uint32_t *__restrict__ out_ids)
+{
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t *ntok = (const uint32_t *)(ws + L.ntok);
+    const uint32_t *tokoff = (const uint32_t *)(ws + L.tokoff);
+    const uint32_t *scratch = (const uint32_t *)(ws + L.scratch);
+    const uint32_t c0 = ctrl->bin_count[0], c1 = ctrl->bin_count[1], c2 = ctrl->bin_count[2];
+    const uint32_t *l0 = (const uint32_t *)(ws + L.bin_wave), *l1 = (const uint32_t *)(ws + L.bin_block),
+                   *l2 = (const uint32_t *)(ws + L.bin_giant);
+    for (uint32_t q = blockIdx.x; q < c0 + c1 + c2; q += gridDim.x) {
+        const uint32_t p = q < c0 ? l0[q] : (q < c0 + c1 ? l1[q - c0] : l2[q - c0 - c1]);
+        const uint32_t *src = scratch + pstart[p];
+        uint32_t *dst = out_ids + tokoff[p];
+        const uint32_t c = ntok[p];
+        for (uint32_t j = threadIdx.x; j < c; j += blockDim.x) dst[j] = src[j];
     }
 }
 
@@ -127,17 +137,27 @@ __global__ __launch_bounds__(256) void k_export_starts(uint8_t *ws, Layout L, ui
         out[i] = i == np ? (uint32_t)n : pstart[i];
 }
 
-hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offsets, hipStream_t s)
+hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offsets, hipStream_t s,
+                          const Events *ev)
 {
     const Layout &L = b.L;
-    hipLaunchKernelGGL(k_tokscan, dim3(L.n_scan_tiles), dim3(SCAN_THREADS), 0, s, b.ws, L);
+    {
+        LaunchScope k(ev, 8, s);
+        hipLaunchKernelGGL(k_tokscan, dim3(L.n_scan_tiles), dim3(SCAN_THREADS), 0, s, b.ws, L);
+    }
     if (b.n) {
+        LaunchScope k(ev, 9, s);
         uint32_t g = (uint32_t)((b.n + 255) / 256);
         hipLaunchKernelGGL(k_gather, dim3(g > 4096 ? 4096 : g), dim3(256), 0, s, b.ws, L, out_ids);
+        uint32_t gl = L.cap_wave < 2048 ? L.cap_wave : 2048;
+        hipLaunchKernelGGL(k_gather_long, dim3(gl), dim3(256), 0, s, b.ws, L, out_ids);
     }
-    uint32_t gd = (uint32_t)((b.n_docs + 1 + 255) / 256);
-    hipLaunchKernelGGL(k_docoff, dim3(gd > 1024 ? 1024 : gd), dim3(256), 0, s, b.ws, L, b.offsets, b.n_docs,
-                       out_offsets);
+    {
+        LaunchScope k(ev, 10, s);
+        uint32_t gd = (uint32_t)((b.n_docs + 1 + 255) / 256);
+        hipLaunchKernelGGL(k_docoff, dim3(gd > 1024 ? 1024 : gd), dim3(256), 0, s, b.ws, L, b.offsets, b.n_docs,
+                           out_offsets);
+    }
     return hipGetLastError();
 }
 

@@ -14,11 +14,11 @@ constexpr int HALO = 16;                       // look-ahead bytes past a tile
 
 // token-offset scan: one workgroup per 4096 pieces
 constexpr int SCAN_THREADS = 256;
-constexpr int SCAN_PER_THREAD = 16;
+constexpr int SCAN_PER_THREAD = 32;
 constexpr int SCAN_TILE = SCAN_THREADS * SCAN_PER_THREAD;
 
 // BPE length bins (piece bytes): lane <= LANE_MAX < wave <= WAVE_MAX < block <= BLOCK_MAX < giant
-constexpr int LANE_MAX = 16;
+constexpr int LANE_MAX = 32;      // lane kernels: <= 16 and 17..32 bytes
 constexpr int WAVE_MAX = 1024;
 constexpr int BLOCK_MAX = 4096;
 constexpr int BLOCK_THREADS = 256;
@@ -55,11 +55,72 @@ struct DevVocab {
     const uint32_t *merges;   // 2 * n_merges (left, right)
     const uint64_t *fmap;     // NCTX transition maps
     const uint32_t *fstart;   // NCTX start masks (bit s: a piece starts here when in state s)
+    // whole-piece tables: pieces whose BPE result is one token (NULL while they are being built)
+    const uint4 *wa;          // 2..7 bytes: {key lo, key hi, id, 0}, key = bytes | len << 56
+    const uint4 *wb;          // 8..32 bytes: 3 x uint4 = {k0, k1}, {k2, k3}, {len, id, 0, 0}
     uint32_t mask;
     uint32_t shift;
+    uint32_t wa_mask, wa_shift, wb_mask, wb_shift;
     uint32_t n_merges;
     int family;
 };
+
+// whole-piece keys
+constexpr uint32_t WA_MAX = 7;
+__host__ __device__ __forceinline__ uint64_t wa_hash(uint64_t key, uint32_t shift)
+{
+    return (key * 0x9E3779B97F4A7C15ull) >> shift;
+}
+__host__ __device__ __forceinline__ uint64_t wb_hash(uint64_t k0, uint64_t k1, uint64_t k2, uint64_t k3,
+                                                    uint32_t len, uint32_t shift)
+{
+    uint64_t h = k0 * 0x9E3779B97F4A7C15ull;
+    h ^= (k1 + 0x632BE59BD9B4E019ull) * 0xC2B2AE3D27D4EB4Full;
+    h ^= (k2 + 0x85EBCA77C2B2AE63ull) * 0x165667B19E3779F9ull;
+    h ^= (k3 + len) * 0x27D4EB2F165667C5ull;
+    h ^= h >> 29;
+    return (h * 0x9E3779B97F4A7C15ull) >> shift;
+}
+
+// ---------------------------------------------------------------------------------------------
+// decoupled look-back helpers (one wavefront reads a window of 64 predecessor flags at once)
+
+__device__ __forceinline__ uint64_t ld_flag(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(uint64_t *p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive prefix sum of per-tile counts.  flags[t] = (1 << 62 | aggregate) or (2 << 62 | inclusive
+// prefix); tiles before 0 count as a prefix of 0.  Call with the whole wave 0; returns the sum of
+// all tiles before `tile` (in every lane).
+__device__ __forceinline__ uint64_t lookback_sum(const uint64_t *flags, uint32_t tile)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    uint64_t sum = 0;
+    int64_t top = (int64_t)tile - 1;
+    for (;;) {
+        const int64_t pos = top - (int64_t)lane;
+        const uint64_t f = pos >= 0 ? ld_flag(flags + pos) : (2ull << 62);
+        const uint32_t flag = (uint32_t)(f >> 62);
+        const uint64_t pre = __ballot(flag == 2), nr = __ballot(flag == 0);
+        const uint32_t kp = pre ? (uint32_t)__ffsll((unsigned long long)pre) - 1u : 64u;
+        const uint64_t need = kp >= 63 ? ~0ull : ((2ull << kp) - 1);
+        if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
+        uint64_t v = lane <= kp ? (f & ((1ull << 62) - 1)) : 0;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            uint32_t lo = __shfl_xor((uint32_t)v, d, 64), hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
+            v += ((uint64_t)hi << 32) | lo;
+        }
+        sum += v;
+        if (kp < 64) return sum;
+        top -= 64;
+    }
+}
 
 __device__ __forceinline__ uint32_t pair_rank(const DevVocab &v, uint32_t a, uint32_t b)
 {
@@ -85,7 +146,8 @@ struct Ctrl {
     uint32_t n_pieces;
     uint32_t n_tokens;
     uint32_t bin_count[3];     // wave, block, giant bins
-    uint32_t pad[56];
+    uint32_t miss_count[2];    // pieces the whole-piece tables did not resolve: <= 16, 17..32 bytes
+    uint32_t pad[54];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
@@ -93,7 +155,7 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // workspace layout for n input bytes
 struct Layout {
     uint64_t ctrl, cc, tbwd, tflag_state, tflag_cnt, pstart, ntok, tokoff, scratch, bin_wave,
-        bin_block, bin_giant, g_ids, g_rank_a, g_rank_b, sflag, total;
+        bin_block, bin_giant, miss16, miss32, g_ids, g_rank_a, g_rank_b, sflag, total;
     uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant;
 };
 
@@ -121,6 +183,8 @@ inline Layout make_layout(uint64_t n)
     L.bin_wave = o;    o += align256(4ull * L.cap_wave);
     L.bin_block = o;   o += align256(4ull * L.cap_block);
     L.bin_giant = o;   o += align256(4ull * L.cap_giant);
+    L.miss16 = o;      o += align256(4ull * (n + 1));
+    L.miss32 = o;      o += align256(4ull * (n / 17 + 1));
     L.g_ids = o;       o += align256(4ull * (n + 1));
     L.g_rank_a = o;    o += align256(4ull * (n + 1));
     L.g_rank_b = o;    o += align256(4ull * (n + 1));
@@ -139,9 +203,31 @@ struct Batch {
     Layout L;
 };
 
-hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s);
-hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s);
-hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offsets, hipStream_t s);
+// optional events recorded around each kernel launch (indices: TOKTIER_K_* in toktier.h)
+struct Events {
+    void *const *before;
+    void *const *after;
+};
+
+struct LaunchScope {   // records before[k] on construction and after[k] on destruction
+    const Events *ev;
+    int k;
+    hipStream_t s;
+    LaunchScope(const Events *e, int kk, hipStream_t ss) : ev(e), k(kk), s(ss)
+    {
+        if (ev && ev->before && ev->before[k]) (void)hipEventRecord((hipEvent_t)ev->before[k], s);
+    }
+    ~LaunchScope()
+    {
+        if (ev && ev->after && ev->after[k]) (void)hipEventRecord((hipEvent_t)ev->after[k], s);
+    }
+};
+
+hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
+hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
+hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offsets, hipStream_t s,
+                          const Events *ev);
 hipError_t launch_export_starts(const Batch &b, uint32_t *out_starts, hipStream_t s);
+hipError_t launch_bins(const Batch &b, hipStream_t s, const Events *ev);
 
 }  // namespace tt

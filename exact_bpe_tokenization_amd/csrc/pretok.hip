@@ -40,6 +40,14 @@ __device__ __forceinline__ uint32_t utf8_len(uint32_t b)
 
 __device__ __forceinline__ uint32_t ucat(uint32_t cp)
 {
+    if (cp < 0x80u) {
+        // ASCII without a table load: letters, digits, the six whitespace characters, the rest
+        const uint32_t lc = cp | 32u;
+        if (lc >= 'a' && lc <= 'z') return cp >= 'a' ? CAT_LL : CAT_LU;
+        if (cp >= '0' && cp <= '9') return CAT_N;
+        if (cp == ' ' || (cp >= 9u && cp <= 13u)) return CAT_W;
+        return CAT_O;
+    }
     return tt_ucat_stage2[((uint32_t)tt_ucat_stage1[cp >> 8] << 8) | (cp & 255u)];
 }
 
@@ -90,13 +98,46 @@ __device__ __forceinline__ uint64_t shfl_up64(uint64_t x, int d)
     return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ uint64_t ld_acquire(const uint64_t *p)
+__device__ __forceinline__ uint64_t shfl_down64(uint64_t x, int d)
 {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t lo = __shfl_down((uint32_t)x, d, 64), hi = __shfl_down((uint32_t)(x >> 32), d, 64);
+    return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ void st_release(uint64_t *p, uint64_t v)
+
+__device__ __forceinline__ uint64_t shfl64(uint64_t x, int src)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t lo = __shfl((uint32_t)x, src, 64), hi = __shfl((uint32_t)(x >> 32), src, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Automaton state entering `tile`.  flags[t] = (1 << 60 | map of tile t) or (2 << 60 | state after
+// tile t); the batch starts in S_ST.  Wave 0 reads 64 predecessors per step and composes their maps
+// (farthest first); a prefix state or any constant composition ends the walk.
+__device__ uint32_t lookback_state(const uint64_t *flags, uint32_t tile)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    uint64_t acc = MAP_IDENTITY;
+    int64_t top = (int64_t)tile - 1;
+    for (;;) {
+        const int64_t pos = top - (int64_t)lane;
+        const uint64_t f = pos >= 0 ? ld_flag(flags + pos) : ((2ull << 60) | S_ST);
+        const uint32_t flag = (uint32_t)(f >> 60);
+        const uint64_t pre = __ballot(flag == 2), nr = __ballot(flag == 0);
+        const uint32_t kp = pre ? (uint32_t)__ffsll((unsigned long long)pre) - 1u : 64u;
+        const uint64_t need = kp >= 63 ? ~0ull : ((2ull << kp) - 1);
+        if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
+        uint64_t x = MAP_IDENTITY;
+        if (lane < kp) x = f & ((1ull << 60) - 1);
+        else if (lane == kp) x = (f & 15u) * NIBBLE_ONES;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            uint64_t y = shfl_down64(x, d);
+            if ((lane & (2u * d - 1u)) == 0) x = compose(y, x);
+        }
+        acc = compose(shfl64(x, 0), acc);
+        if (kp < 64 || is_const_map(acc)) return (uint32_t)(acc & 15u);
+        top -= 64;
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -417,24 +458,13 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, 
     excl = compose(pre, excl);
 
     // look-back #1: automaton state entering this tile
-    if (tid == 0) {
-        uint32_t entry = S_ST;
-        if (tile > 0) {
-            st_release(tfs + tile, (1ull << 60) | tile_map);
-            uint64_t acc = MAP_IDENTITY;
-            int64_t pos = (int64_t)tile - 1;
-            for (;;) {
-                uint64_t f = ld_acquire(tfs + pos);
-                uint32_t flag = (uint32_t)(f >> 60);
-                if (flag == 0) { __builtin_amdgcn_s_sleep(1); continue; }
-                if (flag == 2) { entry = apply_map(acc, (uint32_t)(f & 15u)); break; }
-                acc = compose(f & ((1ull << 60) - 1), acc);
-                if (is_const_map(acc)) { entry = (uint32_t)(acc & 15u); break; }
-                --pos;
-            }
+    if (wid == 0) {
+        if (lane == 0 && tile > 0) st_flag(tfs + tile, (1ull << 60) | tile_map);
+        const uint32_t entry = tile == 0 ? (uint32_t)S_ST : lookback_state(tfs, tile);
+        if (lane == 0) {
+            st_flag(tfs + tile, (2ull << 60) | apply_map(tile_map, entry));
+            s_entry = entry;
         }
-        st_release(tfs + tile, (2ull << 60) | apply_map(tile_map, entry));
-        s_entry = entry;
     }
     __syncthreads();
 
@@ -463,25 +493,16 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, 
     }
 
     // look-back #2: number of pieces before this tile
-    if (tid == 0) {
-        uint64_t basev = 0;
-        if (tile > 0) {
-            st_release(tfc + tile, (1ull << 62) | total);
-            int64_t pos = (int64_t)tile - 1;
-            for (;;) {
-                uint64_t f = ld_acquire(tfc + pos);
-                uint32_t flag = (uint32_t)(f >> 62);
-                if (flag == 0) { __builtin_amdgcn_s_sleep(1); continue; }
-                basev += f & ((1ull << 62) - 1);
-                if (flag == 2) break;
-                --pos;
+    if (wid == 0) {
+        if (lane == 0 && tile > 0) st_flag(tfc + tile, (1ull << 62) | total);
+        const uint64_t basev = tile == 0 ? 0 : lookback_sum(tfc, tile);
+        if (lane == 0) {
+            st_flag(tfc + tile, (2ull << 62) | (basev + total));
+            s_base = (uint32_t)basev;
+            if (tile == L.n_tiles - 1) {
+                ctrl->n_pieces = (uint32_t)(basev + total);
+                pstart[basev + total] = (uint32_t)n;
             }
-        }
-        st_release(tfc + tile, (2ull << 62) | (basev + total));
-        s_base = (uint32_t)basev;
-        if (tile == L.n_tiles - 1) {
-            ctrl->n_pieces = (uint32_t)(basev + total);
-            pstart[basev + total] = (uint32_t)n;
         }
     }
     __syncthreads();
@@ -498,45 +519,60 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, 
 
 __global__ __launch_bounds__(256) void k_bins(uint8_t *ws, Layout L)
 {
+    __shared__ uint32_t scnt[3], sbase[3];
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *lists[3] = {(uint32_t *)(ws + L.bin_wave), (uint32_t *)(ws + L.bin_block),
                           (uint32_t *)(ws + L.bin_giant)};
     const uint32_t np = ctrl->n_pieces;
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint64_t lt = (1ull << lane) - 1;
+    const uint32_t tid = threadIdx.x;
     for (uint32_t p0 = blockIdx.x * blockDim.x; p0 < np; p0 += gridDim.x * blockDim.x) {
-        uint32_t p = p0 + threadIdx.x;
+        if (tid < 3) scnt[tid] = 0;
+        __syncthreads();
+        const uint32_t p = p0 + tid;
         int bin = -1;
         if (p < np) {
             uint32_t len = pstart[p + 1] - pstart[p];
             bin = len <= LANE_MAX ? -1 : (len <= WAVE_MAX ? 0 : (len <= BLOCK_MAX ? 1 : 2));
         }
-#pragma unroll
-        for (int b = 0; b < 3; ++b) {
-            uint64_t m = __ballot(bin == b);
-            if (!m) continue;
-            uint32_t leader = __ffsll((unsigned long long)m) - 1, off = 0;
-            if (lane == leader) off = atomicAdd(&ctrl->bin_count[b], (uint32_t)__popcll(m));
-            off = __shfl(off, leader, 64);
-            if (bin == b) lists[b][off + __popcll(m & lt)] = p;
-        }
+        const uint32_t local = bin >= 0 ? atomicAdd(&scnt[bin], 1u) : 0u;
+        __syncthreads();
+        if (tid < 3 && scnt[tid]) sbase[tid] = atomicAdd(&ctrl->bin_count[tid], scnt[tid]);
+        __syncthreads();
+        if (bin >= 0) lists[bin][sbase[bin] + local] = p;
+        __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------------------------
 
-hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s)
+hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev)
 {
     const Layout &L = b.L;
-    hipLaunchKernelGGL(k_init, dim3(64), dim3(256), 0, s, b.ws, L);
+    {
+        LaunchScope k(ev, 0, s);
+        hipLaunchKernelGGL(k_init, dim3(64), dim3(256), 0, s, b.ws, L);
+    }
     if (L.n_tiles == 0) return hipGetLastError();
-    hipLaunchKernelGGL(k_classify, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, b.bytes, b.offsets, b.n_docs,
-                       b.n, v.family, b.ws, L);
-    hipLaunchKernelGGL(k_pieces, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.n, b.ws, L);
+    {
+        LaunchScope k(ev, 1, s);
+        hipLaunchKernelGGL(k_classify, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, b.bytes, b.offsets, b.n_docs,
+                           b.n, v.family, b.ws, L);
+    }
+    {
+        LaunchScope k(ev, 2, s);
+        hipLaunchKernelGGL(k_pieces, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.n, b.ws, L);
+    }
+    return launch_bins(b, s, ev);
+}
+
+hipError_t launch_bins(const Batch &b, hipStream_t s, const Events *ev)
+{
     uint32_t g = (uint32_t)((b.n + 255) / 256);
     if (g > 2048) g = 2048;
-    hipLaunchKernelGGL(k_bins, dim3(g), dim3(256), 0, s, b.ws, L);
+    if (g == 0) return hipGetLastError();
+    LaunchScope k(ev, 3, s);
+    hipLaunchKernelGGL(k_bins, dim3(g), dim3(256), 0, s, b.ws, b.L);
     return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // device tables, argument checks and the stream-ordered launch chain.
 #include <stdio.h>
 #include <stdlib.h>
+#include <stddef.h>
 #include <string.h>
 
 #include <string>
@@ -17,7 +18,8 @@ struct toktier_vocab {
     int device;
     int family;
     uint32_t n_merges;
-    void *dmem;
+    void *dmem;     // pair tables, merges, automaton tables
+    void *dwords;   // whole-piece tables (may be NULL)
     DevVocab dv;
 };
 
@@ -177,6 +179,123 @@ void build_tables(int fam, uint64_t *fmap, uint32_t *fstart)
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
+// whole-piece tables.  A piece whose bytes equal the bytes of token t encodes to [t] exactly when t
+// is "self-reachable": BPE of t's own byte string ends in t.  That is decided here, once per
+// vocabulary, by running the library's GPU BPE kernels over every token's byte string (2..32
+// bytes) with the tables still empty; the tables then hold exactly those tokens.
+
+namespace {
+
+int build_whole_piece_tables(toktier_vocab *v, const uint32_t *merges, uint32_t n_merges)
+{
+    const uint32_t ntok_all = 256 + n_merges;
+    std::vector<uint32_t> len(ntok_all), off(ntok_all + 1);
+    uint64_t total = 0;
+    for (uint32_t t = 0; t < ntok_all; ++t) {
+        len[t] = t < 256 ? 1u : len[merges[2 * (t - 256)]] + len[merges[2 * (t - 256) + 1]];
+        off[t] = (uint32_t)total;
+        total += len[t];
+        if (total > 0xFFFFFFF0ull) return TOKTIER_E_BAD_MERGES;
+    }
+    off[ntok_all] = (uint32_t)total;
+    std::vector<uint8_t> tb(total);
+    for (uint32_t t = 0; t < ntok_all; ++t) {
+        if (t < 256) { tb[off[t]] = (uint8_t)t; continue; }
+        uint32_t a = merges[2 * (t - 256)], b = merges[2 * (t - 256) + 1];
+        memcpy(&tb[off[t]], &tb[off[a]], len[a]);
+        memcpy(&tb[off[t] + len[a]], &tb[off[b]], len[b]);
+    }
+    std::vector<uint32_t> cand, starts;
+    std::vector<uint8_t> batch;
+    for (uint32_t t = 256; t < ntok_all; ++t) {
+        if (len[t] < 2 || len[t] > (uint32_t)LANE_MAX) continue;
+        cand.push_back(t);
+        starts.push_back((uint32_t)batch.size());
+        batch.insert(batch.end(), tb.begin() + off[t], tb.begin() + off[t] + len[t]);
+    }
+    if (cand.empty()) return TOKTIER_OK;
+    const uint32_t npc = (uint32_t)cand.size();
+    starts.push_back((uint32_t)batch.size());
+    const uint64_t N = batch.size();
+    const Layout L = make_layout(N);
+    uint8_t *dbytes = nullptr, *dws = nullptr;
+    hipError_t e = hipMalloc((void **)&dbytes, N);
+    if (e == hipSuccess) e = hipMalloc((void **)&dws, L.total);
+    std::vector<uint32_t> ntok(npc), first(N);
+    if (e == hipSuccess) e = hipMemcpy(dbytes, batch.data(), N, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(dws + L.ctrl, 0, sizeof(Ctrl));
+    if (e == hipSuccess) e = hipMemcpy(dws + L.ctrl + offsetof(Ctrl, n_pieces), &npc, 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+        e = hipMemcpy(dws + L.pstart, starts.data(), 4ull * starts.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess) {
+        Batch b{dbytes, nullptr, 1, N, dws, L};
+        e = launch_bins(b, 0, nullptr);
+        if (e == hipSuccess) e = launch_bpe(v->dv, b, 0, nullptr);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(0);
+    if (e == hipSuccess) e = hipMemcpy(ntok.data(), dws + L.ntok, 4ull * npc, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(first.data(), dws + L.scratch, 4ull * N, hipMemcpyDeviceToHost);
+    if (dbytes) (void)hipFree(dbytes);
+    if (dws) (void)hipFree(dws);
+    if (e != hipSuccess) return hip_fail(e);
+
+    std::vector<uint32_t> short_t, long_t;
+    for (uint32_t i = 0; i < npc; ++i) {
+        if (ntok[i] != 1 || first[starts[i]] != cand[i]) continue;   // not self-reachable
+        (len[cand[i]] <= WA_MAX ? short_t : long_t).push_back(cand[i]);
+    }
+    uint32_t la = 10, lb = 10;
+    while ((1ull << la) < 2ull * short_t.size()) ++la;
+    while ((1ull << lb) < 2ull * long_t.size()) ++lb;
+    const uint64_t ca = 1ull << la, cb = 1ull << lb;
+    std::vector<uint32_t> wa(4 * ca, 0), wb(12 * cb, 0);
+    for (uint32_t t : short_t) {
+        uint64_t key = (uint64_t)len[t] << 56;
+        for (uint32_t k = 0; k < len[t]; ++k) key |= (uint64_t)tb[off[t] + k] << (8 * k);
+        uint64_t h = wa_hash(key, 64 - la);
+        while (wa[4 * h] || wa[4 * h + 1]) h = (h + 1) & (ca - 1);
+        wa[4 * h] = (uint32_t)key;
+        wa[4 * h + 1] = (uint32_t)(key >> 32);
+        wa[4 * h + 2] = t;
+    }
+    for (uint32_t t : long_t) {
+        uint64_t k4[4] = {0, 0, 0, 0};
+        for (uint32_t k = 0; k < len[t]; ++k) k4[k >> 3] |= (uint64_t)tb[off[t] + k] << (8 * (k & 7));
+        uint64_t h = wb_hash(k4[0], k4[1], k4[2], k4[3], len[t], 64 - lb);
+        while (wb[12 * h + 8]) h = (h + 1) & (cb - 1);
+        for (int w = 0; w < 4; ++w) {
+            wb[12 * h + 2 * w] = (uint32_t)k4[w];
+            wb[12 * h + 2 * w + 1] = (uint32_t)(k4[w] >> 32);
+        }
+        wb[12 * h + 8] = len[t];
+        wb[12 * h + 9] = t;
+    }
+    void *d = nullptr;
+    const uint64_t bytes_a = 16 * ca, bytes_b = 48 * cb;
+    e = hipMalloc(&d, bytes_a + bytes_b);
+    if (e != hipSuccess) {
+        hip_fail(e);
+        return TOKTIER_E_OOM;
+    }
+    e = hipMemcpy(d, wa.data(), bytes_a, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy((uint8_t *)d + bytes_a, wb.data(), bytes_b, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return hip_fail(e);
+    }
+    v->dwords = d;
+    v->dv.wa = (const uint4 *)d;
+    v->dv.wb = (const uint4 *)((uint8_t *)d + bytes_a);
+    v->dv.wa_mask = (uint32_t)(ca - 1);
+    v->dv.wa_shift = 64 - la;
+    v->dv.wb_mask = (uint32_t)(cb - 1);
+    v->dv.wb_shift = 64 - lb;
+    return TOKTIER_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
 
 extern "C" const char *toktier_status_string(int status)
 {
@@ -279,6 +398,14 @@ extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int
     v->dv.shift = shift;
     v->dv.n_merges = n_merges;
     v->dv.family = family;
+    v->dv.wa = nullptr;
+    v->dv.wb = nullptr;
+    int rc = build_whole_piece_tables(v, merges, n_merges);
+    if (rc != TOKTIER_OK) {
+        (void)hipFree(v->dmem);
+        free(v);
+        return rc;
+    }
     *out = v;
     return TOKTIER_OK;
 }
@@ -288,6 +415,10 @@ extern "C" int toktier_free_vocab(toktier_vocab *v)
     if (!v) return TOKTIER_OK;
     hipError_t e = hipDeviceSynchronize();
     hipError_t f = hipFree(v->dmem);
+    if (v->dwords) {
+        hipError_t g = hipFree(v->dwords);
+        if (f == hipSuccess) f = g;
+    }
     free(v);
     if (e != hipSuccess) return hip_fail(e);
     if (f != hipSuccess) return hip_fail(f);
@@ -353,10 +484,11 @@ int read_ctrl(void *workspace, hipStream_t s, Ctrl *out)
 
 }  // namespace
 
-extern "C" int toktier_encode_batch(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
-                                    uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
-                                    uint64_t ids_capacity, uint64_t *out_offsets, void *workspace,
-                                    uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens)
+namespace {
+
+int encode_impl(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets, uint32_t n_docs,
+                uint64_t total_bytes, uint32_t *out_ids, uint64_t ids_capacity, uint64_t *out_offsets,
+                void *workspace, uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens, const Events *ev)
 {
     Batch b;
     int rc = check_batch(v, bytes, offsets, n_docs, total_bytes, workspace, workspace_bytes, &b);
@@ -364,15 +496,37 @@ extern "C" int toktier_encode_batch(const toktier_vocab *v, const uint8_t *bytes
     if (!out_offsets || (total_bytes && !out_ids)) return TOKTIER_E_INVALID_ARG;
     if (ids_capacity < total_bytes) return TOKTIER_E_CAPACITY;
     hipStream_t s = (hipStream_t)stream;
-    HIP_TRY(launch_pretokenize(v->dv, b, s));
-    HIP_TRY(launch_bpe(v->dv, b, s));
-    HIP_TRY(launch_compact(b, out_ids, out_offsets, s));
+    HIP_TRY(launch_pretokenize(v->dv, b, s, ev));
+    HIP_TRY(launch_bpe(v->dv, b, s, ev));
+    HIP_TRY(launch_compact(b, out_ids, out_offsets, s, ev));
     if (!out_n_tokens) return TOKTIER_OK;
     Ctrl c;
     rc = read_ctrl(workspace, s, &c);
     if (rc) return rc;
     *out_n_tokens = c.n_tokens;
     return TOKTIER_OK;
+}
+
+}  // namespace
+
+extern "C" int toktier_encode_batch(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                                    uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
+                                    uint64_t ids_capacity, uint64_t *out_offsets, void *workspace,
+                                    uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens)
+{
+    return encode_impl(v, bytes, offsets, n_docs, total_bytes, out_ids, ids_capacity, out_offsets, workspace,
+                       workspace_bytes, stream, out_n_tokens, nullptr);
+}
+
+extern "C" int toktier_encode_batch_timed(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                                          uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
+                                          uint64_t ids_capacity, uint64_t *out_offsets, void *workspace,
+                                          uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens,
+                                          void *const *events_before, void *const *events_after)
+{
+    Events ev{events_before, events_after};
+    return encode_impl(v, bytes, offsets, n_docs, total_bytes, out_ids, ids_capacity, out_offsets, workspace,
+                       workspace_bytes, stream, out_n_tokens, &ev);
 }
 
 extern "C" int toktier_pretokenize_batch(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
@@ -386,7 +540,7 @@ extern "C" int toktier_pretokenize_batch(const toktier_vocab *v, const uint8_t *
     if (!out_piece_starts || !out_n_pieces) return TOKTIER_E_INVALID_ARG;
     if (starts_capacity < total_bytes + 1) return TOKTIER_E_CAPACITY;
     hipStream_t s = (hipStream_t)stream;
-    HIP_TRY(launch_pretokenize(v->dv, b, s));
+    HIP_TRY(launch_pretokenize(v->dv, b, s, nullptr));
     HIP_TRY(launch_export_starts(b, out_piece_starts, s));
     Ctrl c;
     rc = read_ctrl(workspace, s, &c);

@@ -141,6 +141,35 @@ int toktier_pretokenize_batch(const toktier_vocab *v, const uint8_t *bytes, cons
  */
 int toktier_last_status(void *workspace, void *stream, uint64_t *out_n_tokens);
 
+/* Kernel launches of one toktier_encode_batch call, in stream order (indices for the timed form). */
+enum {
+    TOKTIER_K_INIT = 0,       /* clear the control block and look-back flags                  */
+    TOKTIER_K_CLASSIFY,       /* UTF-8 decode, validation, categories, backward summaries     */
+    TOKTIER_K_PIECES,         /* automaton scan, piece starts, piece numbering                */
+    TOKTIER_K_BINS,           /* length bins for pieces longer than a lane's limit            */
+    TOKTIER_K_BPE_LANE,       /* BPE, one lane per piece of <= 16 bytes                       */
+    TOKTIER_K_BPE_WAVE,       /* BPE, one wavefront per piece of 17..1024 bytes               */
+    TOKTIER_K_BPE_BLOCK,      /* BPE, one workgroup per piece of 1025..4096 bytes             */
+    TOKTIER_K_BPE_GIANT,      /* BPE, one workgroup per longer piece, sequence in device memory */
+    TOKTIER_K_TOKSCAN,        /* exclusive scan of per-piece token counts                     */
+    TOKTIER_K_GATHER,         /* per-piece IDs -> contiguous out_ids                          */
+    TOKTIER_K_DOCOFF,         /* per-document token offsets                                   */
+    TOKTIER_K_COUNT
+};
+
+/*
+ * Benchmark hook: exactly toktier_encode_batch, and in addition records caller-created HIP events
+ * (hipEvent_t passed as void*) on the stream immediately before and after each kernel launch:
+ * events_before[k] / events_after[k] for launch k in the enum above.  Either array, and any entry,
+ * may be NULL (not recorded).  Launches that a batch does not need (e.g. every kernel after
+ * TOKTIER_K_INIT when total_bytes == 0) record nothing.  Errors as in toktier_encode_batch.
+ */
+int toktier_encode_batch_timed(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                               uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
+                               uint64_t ids_capacity, uint64_t *out_offsets, void *workspace,
+                               uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens,
+                               void *const *events_before, void *const *events_after);
+
 /* Static English text for a status code. */
 const char *toktier_status_string(int status);
 

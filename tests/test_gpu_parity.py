@@ -226,3 +226,51 @@ def test_async_call_and_last_status(tt):
     eids, eoo = oracle.encode_batch(fam, merges, text)
     torch.cuda.synchronize()
     compare_ids(eids, eoo, ids[:n].cpu().numpy().view(np.uint32), oo.cpu().numpy().astype(np.uint64))
+
+
+
+@pytest.mark.parametrize("voc", ["v1", "v2", "v3", "v4"])
+def test_every_token_string(tt, voc):
+    """Every token's own byte string (the valid-UTF-8 ones) as a document: exercises the whole-piece
+    tables -- hits for tokens whose byte string encodes to themselves, misses falling back to BPE
+    for the others -- against the oracle."""
+    tok, merges, fam = tokenizer(tt, voc)
+    tb = oracle.Merges(merges).token_bytes()
+    texts = []
+    for t in range(256, len(tb)):
+        try:
+            texts.append(tb[t].decode("utf-8"))
+        except UnicodeDecodeError:
+            pass
+    data, offs = textgen.to_batch(texts)
+    _say("token strings", voc, len(texts), data.size)
+    ids, oo = tok.encode(data.tobytes(), offs)
+    eids, eoo = oracle.encode_batch(fam, merges, data, offs)
+    compare_ids(eids, eoo, ids, oo)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_random_merge_lists(tt, seed):
+    """Random rank-consistent merge lists over a small alphabet produce many tokens whose own byte
+    string does not encode to themselves; the whole-piece tables must leave those to BPE."""
+    rng = np.random.default_rng(seed)
+    alpha = [ord(c) for c in "abcd"]
+    ids, seen, merges = list(alpha), set(), []
+    while len(merges) < 400:
+        a, b = ids[int(rng.integers(0, len(ids)))], ids[int(rng.integers(0, len(ids)))]
+        if (a, b) in seen:
+            continue
+        seen.add((a, b))
+        merges.append((a, b))
+        ids.append(255 + len(merges))
+    merges = np.array(merges, dtype=np.uint32)
+    tb = oracle.Merges(merges).token_bytes()
+    words = ["".join(chr(int(c)) for c in rng.choice(alpha, int(rng.integers(1, 40)))) for _ in range(3000)]
+    words += [tb[t].decode() for t in range(256, len(tb)) if len(tb[t]) <= 40]
+    for fam in FAMS:
+        tok = tt.Tokenizer(merges, fam)
+        data, offs = textgen.to_batch([" ".join(words[i:i + 7]) for i in range(0, len(words), 7)])
+        _say("random merges", seed, fam, data.size)
+        gi, go = tok.encode(data.tobytes(), offs)
+        ei, eo = oracle.encode_batch(fam, merges, data, offs)
+        compare_ids(ei, eo, gi, go)
