@@ -42,7 +42,7 @@ LATENCY = ("c1_ec4k", "c2_at100k", "c3_mix1m", "c5_adv4m4")
 
 # input bytes each kernel launch processes (the unit of the algorithmic-bytes figure)
 UNITS = {
-    "classify": "all", "pieces": "all", "bins": "all", "tokscan": "all", "gather": "all", "docoff": "all",
+    "init": "all", "summary": "all", "pieces": "all", "bins": "all", "emit": "all", "gather_long": "binned",
     "bpe_lane": "lane", "bpe_wave": "wave", "bpe_block": "block", "bpe_giant": "giant",
 }
 
@@ -207,8 +207,9 @@ def main():
     # input bytes per length bin (from the GPU split)
     starts = tok.pretokenize(data.tobytes(), offs)
     plen = np.diff(starts.astype(np.int64))
-    bins = {"all": int(n), "lane": int(plen[plen <= 16].sum()), "wave": int(plen[(plen > 16) & (plen <= 1024)].sum()),
-            "block": int(plen[(plen > 1024) & (plen <= 4096)].sum()), "giant": int(plen[plen > 4096].sum())}
+    bins = {"all": int(n), "lane": int(plen[plen <= 64].sum()), "wave": int(plen[(plen > 64) & (plen <= 1024)].sum()),
+            "block": int(plen[(plen > 1024) & (plen <= 4096)].sum()), "giant": int(plen[plen > 4096].sum()),
+            "binned": int(plen[plen > 64].sum())}
     alg_per_byte = (n + 4 * n_tokens + 16 * (D + 1)) / n
     units = bins[UNITS[dominant]]
     alg_bytes = alg_per_byte * units

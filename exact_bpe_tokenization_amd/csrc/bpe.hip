@@ -7,12 +7,13 @@
 // that pair equals iterated single merges (for rank-consistent merge lists, which the loader
 // enforces); only pairs next to a completed merge need a new lookup.
 //
-//   k_bpe_lookup every piece of <= 32 bytes: one probe of a whole-piece table resolves the pieces
-//                that encode to a single token; the rest are listed for
-//   k_bpe_lane   one lane per listed piece (two register-array sizes: <= 16, 17..32 bytes);
-//                sequence and ranks in registers; the textbook
-//                loop (leftmost lowest rank, merge, re-probe the two neighbours)
-//   k_bpe_block  one wavefront (pieces of 33..1024 bytes) or one 256-lane workgroup (up to 4096
+//   k_bpe_lookup every piece of <= 64 bytes: one probe of a whole-piece table resolves the pieces
+//                that encode to a single token; the rest are listed by length for
+//   k_bpe_lane   (<= 16 bytes) one lane per listed piece, sequence and ranks in registers; the
+//                textbook loop (leftmost lowest rank, merge, re-probe the two neighbours)
+//   k_bpe_seg    (17..32 and 33..64 bytes) 32 or 64 lanes per piece, one element per lane; rounds
+//                on ballot masks (see the kernel)
+//   k_bpe_block  one wavefront (pieces of 65..1024 bytes) or one 256-lane workgroup (up to 4096
 //                bytes) per piece; sequence in LDS; rounds: block-min of ranks, selection of the
 //                leftmost non-overlapping occurrences, prefix-sum compaction, neighbour re-probes
 //   k_bpe_giant  one 1024-lane workgroup per piece longer than that; the same rounds over device
@@ -54,7 +55,7 @@ __device__ __forceinline__ bool whole_piece(const DevVocab &v, const uint8_t *__
     if (!v.wb) return false;
     uint64_t k4[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (uint32_t k = 0; k < (uint32_t)LANE_MAX; ++k)
+    for (uint32_t k = 0; k < (uint32_t)TABLE_MAX; ++k)
         if (k < len) k4[k >> 3] |= (uint64_t)src[k] << (8 * (k & 7));
     uint32_t h = (uint32_t)wb_hash(k4[0], k4[1], k4[2], k4[3], len, v.wb_shift);
     for (;;) {
@@ -72,47 +73,62 @@ __device__ __forceinline__ bool whole_piece(const DevVocab &v, const uint8_t *__
     }
 }
 
-// every piece of <= 32 bytes: single bytes and whole-piece hits are written directly; the rest go
-// to the two miss lists (<= 16 bytes, 17..32 bytes) for the lane kernels
-__global__ __launch_bounds__(256) void k_bpe_lookup(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
-                                                    Layout L)
+// Every piece of <= 64 bytes: single bytes and whole-piece hits are written directly; the rest are
+// queued in LDS by length (<= 16, 17..32, 33..64 bytes) and flushed to the three miss lists with one
+// reservation atomic per list per flush.  Each workgroup owns a contiguous range of pieces.
+constexpr int LK_THREADS = 256;
+constexpr int LK_Q = 2048;
+
+__global__ __launch_bounds__(LK_THREADS) void k_bpe_lookup(DevVocab v, const uint8_t *__restrict__ bytes,
+                                                           uint8_t *ws, Layout L)
 {
-    __shared__ uint32_t scnt[2], sbase[2];
+    __shared__ uint32_t q[3][LK_Q];
+    __shared__ uint32_t scnt[3], sbase[3];
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *ntok = (uint32_t *)(ws + L.ntok);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
-    uint32_t *lists[2] = {(uint32_t *)(ws + L.miss16), (uint32_t *)(ws + L.miss32)};
+    uint32_t *lists[3] = {(uint32_t *)(ws + L.miss16), (uint32_t *)(ws + L.miss32), (uint32_t *)(ws + L.miss64)};
     const uint32_t np = ctrl->n_pieces;
     const uint32_t tid = threadIdx.x;
-    for (uint32_t p0 = blockIdx.x * blockDim.x; p0 < np; p0 += gridDim.x * blockDim.x) {
-        if (tid < 2) scnt[tid] = 0;
+    const uint32_t chunk = (np + gridDim.x - 1) / gridDim.x;
+    const uint32_t start = blockIdx.x * chunk, end = min(np, start + chunk);
+    if (tid < 3) scnt[tid] = 0;
+    __syncthreads();
+    auto flush = [&](int l) {
+        // uniform: every thread calls this with the same l
+        if (tid == 0) sbase[l] = atomicAdd(&ctrl->miss_count[l], scnt[l]);
         __syncthreads();
+        const uint32_t c = scnt[l], b = sbase[l];
+        for (uint32_t i = tid; i < c; i += LK_THREADS) lists[l][b + i] = q[l][i];
+        __syncthreads();
+        if (tid == 0) scnt[l] = 0;
+        __syncthreads();
+    };
+    for (uint32_t p0 = start; p0 < end; p0 += LK_THREADS) {
         const uint32_t p = p0 + tid;
-        int miss = -1;
-        if (p < np) {
+        if (p < end) {
             const uint32_t b0 = pstart[p];
             const uint32_t len = pstart[p + 1] - b0;
             uint32_t id;
+            int miss = -1;
             if (len == 1) {
                 scratch[b0] = bytes[b0];
                 ntok[p] = 1;
+            } else if (len <= (uint32_t)TABLE_MAX && whole_piece(v, bytes + b0, len, &id)) {
+                scratch[b0] = id;
+                ntok[p] = 1;
             } else if (len <= (uint32_t)LANE_MAX) {
-                if (whole_piece(v, bytes + b0, len, &id)) {
-                    scratch[b0] = id;
-                    ntok[p] = 1;
-                } else {
-                    miss = len <= 16 ? 0 : 1;
-                }
+                miss = len <= 16 ? 0 : (len <= 32 ? 1 : 2);
             }
+            if (miss >= 0) q[miss][atomicAdd(&scnt[miss], 1u)] = p;
         }
-        const uint32_t local = miss >= 0 ? atomicAdd(&scnt[miss], 1u) : 0u;
         __syncthreads();
-        if (tid < 2 && scnt[tid]) sbase[tid] = atomicAdd(&ctrl->miss_count[tid], scnt[tid]);
-        __syncthreads();
-        if (miss >= 0) lists[miss][sbase[miss] + local] = p;
-        __syncthreads();
+        for (int l = 0; l < 3; ++l)
+            if (scnt[l] > (uint32_t)(LK_Q - LK_THREADS)) flush(l);
     }
+    for (int l = 0; l < 3; ++l)
+        if (scnt[l]) flush(l);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -126,7 +142,7 @@ __global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__r
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *ntok = (uint32_t *)(ws + L.ntok);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
-    const uint32_t *list = (const uint32_t *)(ws + (which ? L.miss32 : L.miss16));
+    const uint32_t *list = (const uint32_t *)(ws + (which == 0 ? L.miss16 : (which == 1 ? L.miss32 : L.miss64)));
     const uint32_t count = ctrl->miss_count[which];
     for (uint32_t q = blockIdx.x * blockDim.x + threadIdx.x; q < count; q += gridDim.x * blockDim.x) {
         const uint32_t p = list[q];
@@ -173,6 +189,83 @@ __global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__r
         for (int k = 0; k < MAXL; ++k)
             if ((uint32_t)k < n) scratch[b0 + k] = id[k];
         ntok[p] = n;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// G lanes per piece (G = 16, 32 or 64; 64 / G pieces per wavefront), element k of a piece in lane
+// k of its segment.  One round per distinct minimum rank, everything in registers:
+//   segment minimum of the pair ranks (xor butterfly inside the segment),
+//   H = ballot of the pairs holding it,
+//   leftmost non-overlapping selection in closed form on H: a chain of consecutive hits (only a
+//   pair (x, x) makes one) keeps the hits at an even distance from its first hit,
+//   keep mask K = valid lanes that are not the right half of a selected pair, new position =
+//   popcount of K below the lane inside its segment (a permutation of the segment: dropped lanes
+//   go after the kept ones), moved with ds_permute,
+//   re-probe of the pairs whose left or right element was merged.
+// A segment never spills into the next one: its last element has no pair, so chains and
+// selections stay inside it.
+
+__device__ __forceinline__ uint32_t lane_push(uint32_t dst_lane, uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_ds_permute((int)(dst_lane << 2), (int)x);
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void k_bpe_seg(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
+                                                 Layout L, int which)
+{
+    static_assert(G == 16 || G == 32 || G == 64, "segment width");
+    constexpr uint32_t SEGS = 64 / G;
+    constexpr uint64_t EVEN = 0x5555555555555555ull, ODD = ~EVEN;
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    uint32_t *ntok = (uint32_t *)(ws + L.ntok);
+    uint32_t *scratch = (uint32_t *)(ws + L.scratch);
+    const uint32_t *list = (const uint32_t *)(ws + (which == 0 ? L.miss16 : (which == 1 ? L.miss32 : L.miss64)));
+    const uint32_t count = ctrl->miss_count[which];
+    const uint32_t lane = threadIdx.x & 63u, seg = lane / G, k = lane % G, sbase = seg * G;
+    const uint64_t segmask = G == 64 ? ~0ull : (((1ull << (G % 64)) - 1ull) << sbase);
+    const uint64_t below = (1ull << lane) - 1ull;
+    const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const uint32_t nwaves = (gridDim.x * blockDim.x) >> 6;
+
+    for (uint32_t q0 = wave * SEGS; q0 < count; q0 += nwaves * SEGS) {
+        const uint32_t q = q0 + seg;
+        uint32_t p = 0, b0 = 0, n = 0;
+        if (q < count) {
+            p = list[q];
+            b0 = pstart[p];
+            n = pstart[p + 1] - b0;   // 2..G bytes
+        }
+        uint32_t id = k < n ? (uint32_t)bytes[b0 + k] : 0u;
+        uint32_t nx = __shfl_down(id, 1, 64);
+        uint32_t rk = k + 1 < n ? __ldg(v.r2 + ((id << 8) | nx)) : NO_RANK;
+        for (;;) {
+            uint32_t m = rk;
+#pragma unroll
+            for (int d = G / 2; d >= 1; d >>= 1) m = min(m, (uint32_t)__shfl_xor(m, d, 64));
+            const uint64_t H = __ballot(rk == m && m != NO_RANK);
+            if (H == 0) break;
+            const uint64_t rsE = H & ~(H << 1) & EVEN;          // chains starting at an even lane
+            const uint64_t runsE = H & ~(H + rsE);              // the hits of those chains
+            const uint64_t sel = (runsE & EVEN) | (H & ~runsE & ODD);
+            const uint64_t K = __ballot(k < n) & ~(sel << 1);
+            const bool me_sel = (sel >> lane) & 1u;
+            const bool nx_sel = lane < 63 && ((sel >> (lane + 1)) & 1u);
+            const uint32_t kept_seg = (uint32_t)__popcll(K & segmask);
+            const uint32_t dst = ((K >> lane) & 1u)
+                                     ? sbase + (uint32_t)__popcll(K & segmask & below)
+                                     : sbase + kept_seg + (uint32_t)__popcll(~K & segmask & below);
+            id = lane_push(dst, me_sel ? 256u + m : id);
+            rk = lane_push(dst, (me_sel || nx_sel) ? PENDING : rk);
+            n = kept_seg;
+            nx = __shfl_down(id, 1, 64);
+            if (k >= n) rk = NO_RANK;
+            else if (rk == PENDING) rk = k + 1 < n ? pair_rank(v, id, nx) : NO_RANK;
+        }
+        if (k < n) scratch[b0 + k] = id;
+        if (k == 0 && q < count) ntok[p] = n;
     }
 }
 
@@ -496,11 +589,14 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     uint32_t g = (uint32_t)((b.n + 255) / 256);
     {
         LaunchScope k(ev, 4, s);
-        hipLaunchKernelGGL(k_bpe_lookup, dim3(g > 4096 ? 4096 : g), dim3(256), 0, s, v, b.bytes, b.ws, L);
+        hipLaunchKernelGGL(k_bpe_lookup, dim3(g > 1024 ? 1024 : g), dim3(LK_THREADS), 0, s, v, b.bytes, b.ws, L);
         hipLaunchKernelGGL((k_bpe_lane<16>), dim3(g > 2048 ? 2048 : g), dim3(256), 0, s, v, b.bytes, b.ws, L, 0);
-        uint32_t g32 = (uint32_t)((b.n / 17 + 256) / 256);
-        hipLaunchKernelGGL((k_bpe_lane<LANE_MAX>), dim3(g32 > 1024 ? 1024 : g32), dim3(256), 0, s, v, b.bytes, b.ws,
-                           L, 1);
+        // at most n / 17 pieces of 17..32 bytes (8 per workgroup), n / 33 of 33..64 (4 per workgroup)
+        const uint64_t g32 = b.n / 17 / 8 + 1, g64 = b.n / 33 / 4 + 1;
+        hipLaunchKernelGGL((k_bpe_seg<32>), dim3(g32 > 2048 ? 2048 : (uint32_t)g32), dim3(256), 0, s, v, b.bytes,
+                           b.ws, L, 1);
+        hipLaunchKernelGGL((k_bpe_seg<64>), dim3(g64 > 1024 ? 1024 : (uint32_t)g64), dim3(256), 0, s, v, b.bytes,
+                           b.ws, L, 2);
     }
     {
         LaunchScope k(ev, 5, s);

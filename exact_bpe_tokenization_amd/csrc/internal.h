@@ -6,19 +6,21 @@
 namespace tt {
 
 // ---------------------------------------------------------------------------------------------
-// stage-1 geometry: one workgroup per 4 KiB tile, 16 input bytes per thread
-constexpr int PRE_THREADS = 256;
+// stage-1 geometry: one workgroup per 8 KiB tile, 16 input bytes per thread
+constexpr int PRE_THREADS = 512;
 constexpr int PRE_CHUNK = 16;
-constexpr int TILE = PRE_THREADS * PRE_CHUNK;  // 4096
-constexpr int HALO = 16;                       // look-ahead bytes past a tile
+constexpr int TILE = PRE_THREADS * PRE_CHUNK;  // 8192
+constexpr int HALO = 16;                       // character codes computed past a tile
+constexpr int RAW_LEAD = 4, RAW_TAIL = 24;     // raw bytes kept before / after a tile
 
 // token-offset scan: one workgroup per 4096 pieces
 constexpr int SCAN_THREADS = 256;
-constexpr int SCAN_PER_THREAD = 32;
+constexpr int SCAN_PER_THREAD = 16;
 constexpr int SCAN_TILE = SCAN_THREADS * SCAN_PER_THREAD;
 
 // BPE length bins (piece bytes): lane <= LANE_MAX < wave <= WAVE_MAX < block <= BLOCK_MAX < giant
-constexpr int LANE_MAX = 32;      // lane kernels: <= 16 and 17..32 bytes
+constexpr int LANE_MAX = 64;      // lane kernels: <= 16, 17..32 and 33..64 bytes
+constexpr int TABLE_MAX = 32;     // whole-piece tables hold pieces of 2..32 bytes
 constexpr int WAVE_MAX = 1024;
 constexpr int BLOCK_MAX = 4096;
 constexpr int BLOCK_THREADS = 256;
@@ -122,6 +124,42 @@ __device__ __forceinline__ uint64_t lookback_sum(const uint64_t *flags, uint32_t
     }
 }
 
+// First index i in [0, n) whose entry satisfies pred (n if none), for a predicate that is false
+// then true along the sorted array.  Called by a whole wavefront: each step probes 64 evenly spaced
+// entries, so a search costs about log64(n) + 1 dependent loads.
+template <typename Pred>
+__device__ __forceinline__ uint32_t wave_partition_point(const uint64_t *a, uint32_t n, Pred pred)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    uint32_t lo = 0, hi = n;   // the answer lies in [lo, hi]
+    while (hi - lo > 64) {
+        const uint32_t step = (hi - lo + 63) / 64;
+        const uint32_t idx = lo + lane * step;
+        const uint64_t t = __ballot(idx >= hi || pred(a[idx]));
+        if (t == 0) {          // every probe is before the answer
+            lo = lo + 63 * step + 1;
+            continue;
+        }
+        const uint32_t k = (uint32_t)__ffsll((unsigned long long)t) - 1u;
+        const uint32_t nlo = k == 0 ? lo : lo + (k - 1) * step + 1;
+        hi = min(hi, lo + k * step);
+        lo = nlo;
+    }
+    const uint32_t idx = lo + lane;
+    const uint64_t t = __ballot(idx >= hi || pred(a[idx]));
+    return t ? lo + (uint32_t)__ffsll((unsigned long long)t) - 1u : hi;
+}
+
+__device__ __forceinline__ uint32_t wave_lower_bound(const uint64_t *a, uint32_t n, uint64_t x)
+{
+    return wave_partition_point(a, n, [x](uint64_t v) { return v >= x; });
+}
+
+__device__ __forceinline__ uint32_t wave_upper_bound(const uint64_t *a, uint32_t n, uint64_t x)
+{
+    return wave_partition_point(a, n, [x](uint64_t v) { return v > x; });
+}
+
 __device__ __forceinline__ uint32_t pair_rank(const DevVocab &v, uint32_t a, uint32_t b)
 {
     if ((a | b) < 256u) return __ldg(v.r2 + ((a << 8) | b));
@@ -146,8 +184,8 @@ struct Ctrl {
     uint32_t n_pieces;
     uint32_t n_tokens;
     uint32_t bin_count[3];     // wave, block, giant bins
-    uint32_t miss_count[2];    // pieces the whole-piece tables did not resolve: <= 16, 17..32 bytes
-    uint32_t pad[54];
+    uint32_t miss_count[3];    // pieces left for lane BPE: <= 16, 17..32, 33..64 bytes
+    uint32_t pad[53];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
@@ -155,7 +193,7 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // workspace layout for n input bytes
 struct Layout {
     uint64_t ctrl, cc, tbwd, tflag_state, tflag_cnt, pstart, ntok, tokoff, scratch, bin_wave,
-        bin_block, bin_giant, miss16, miss32, g_ids, g_rank_a, g_rank_b, sflag, total;
+        bin_block, bin_giant, miss16, miss32, miss64, g_ids, g_rank_a, g_rank_b, sflag, total;
     uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant;
 };
 
@@ -171,7 +209,7 @@ inline Layout make_layout(uint64_t n)
     L.cap_giant = (uint32_t)(n / (BLOCK_MAX + 1) + 1);
     uint64_t o = 0;
     L.ctrl = o;        o += align256(sizeof(Ctrl));
-    L.cc = o;          o += align256((uint64_t)L.n_tiles * TILE + HALO);  // tiles are whole
+    L.cc = o;
     L.tbwd = o;        o += align256((uint64_t)L.n_tiles + 1);
     L.tflag_state = o; o += align256(8ull * L.n_tiles);
     L.tflag_cnt = o;   o += align256(8ull * L.n_tiles);
@@ -185,6 +223,7 @@ inline Layout make_layout(uint64_t n)
     L.bin_giant = o;   o += align256(4ull * L.cap_giant);
     L.miss16 = o;      o += align256(4ull * (n + 1));
     L.miss32 = o;      o += align256(4ull * (n / 17 + 1));
+    L.miss64 = o;      o += align256(4ull * (n / 33 + 1));
     L.g_ids = o;       o += align256(4ull * (n + 1));
     L.g_rank_a = o;    o += align256(4ull * (n + 1));
     L.g_rank_b = o;    o += align256(4ull * (n + 1));

@@ -10,15 +10,16 @@
 // parallel scan of maps: within a thread, across the workgroup, and across tiles through a
 // decoupled look-back.  The two facts that need the future -- "no CR/LF later in this whitespace
 // run" (where `\s*[\r\n]+` stops) and "only uppercase letters left in this letter run" (where the
-// o200k case rule backtracks) -- come from a backward pass whose per-tile summaries the classify
-// kernel leaves behind.
+// o200k case rule backtracks) -- are carried right to left; each tile's carry comes from a summary
+// of the tiles after it.
 //
-// Kernels:  k_init      clear the control block and the look-back flags
-//           k_classify  UTF-8 decode + validation, category lookup, per-byte code, backward
-//                       per-tile summaries                                (1 read, 1 write of n)
-//           k_pieces    backward flags, automaton scan, piece-start bits, piece numbering scan,
-//                       piece start offsets                              (1 read of n, 4 B/piece)
-//           k_bins      piece lengths -> wave / block / giant lists (lane-sized pieces need none)
+// Kernels:  k_init     clear the control block and the look-back flags
+//           k_summary  per tile: the leftmost character that decides each backward flag (an
+//                      early-exit scan of the tile's first bytes; one wavefront per tile)
+//           k_pieces   per 8 KiB tile: UTF-8 decode + validation, categories, backward flags,
+//                      automaton scan, piece starts, piece numbering (one read of the input,
+//                      4 bytes written per piece)
+//           k_bins     piece lengths -> wave / block / giant lists
 #include "internal.h"
 
 #define TT_UCAT_QUAL static __device__ const
@@ -140,6 +141,62 @@ __device__ uint32_t lookback_state(const uint64_t *flags, uint32_t tile)
     }
 }
 
+// Per-byte code of position p (index j into the LDS byte window, `docbit` over the same window).
+// Continuation bytes get CAT_CONT; `bad` is set when p breaks UTF-8 (only when check is true).
+template <typename DocBit>
+__device__ __forceinline__ uint32_t byte_code(const uint8_t *sraw, DocBit docbit, int j, uint64_t p, uint64_t n,
+                                              int family, bool check, bool &bad)
+{
+    const uint32_t c = sraw[j];
+    const bool isdoc = docbit(j);
+    if ((c & 0xC0u) == 0x80u) {
+        if (check) {
+            // a continuation byte must be covered by a lead byte 1..3 bytes back in the same doc
+            bool ok = false;
+            if (!isdoc) {
+                for (int back = 1; back <= 3; ++back) {
+                    if ((int64_t)p - back < 0) break;
+                    uint32_t lead = sraw[j - back];
+                    if ((lead & 0xC0u) != 0x80u) { ok = utf8_len(lead) > (uint32_t)back; break; }
+                }
+            }
+            bad |= !ok;
+        }
+        return CAT_CONT;
+    }
+    uint32_t len = utf8_len(c), cp = c;
+    bool ok = len != 0 && p + len <= n;
+    if (ok && len > 1) {
+        cp = c & (0x7Fu >> len);
+        for (uint32_t t = 1; t < len; ++t) {
+            uint32_t cb = sraw[j + t];
+            ok &= ((cb & 0xC0u) == 0x80u) && !docbit(j + (int)t);
+            cp = (cp << 6) | (cb & 0x3Fu);
+        }
+        ok &= !(len == 3 && cp < 0x800u) && !(len == 4 && (cp < 0x10000u || cp > 0x10FFFFu)) &&
+              !(cp >= 0xD800u && cp <= 0xDFFFu);
+    }
+    if (check) bad |= !ok;
+    if (!ok) cp = 0xFFFDu;
+    uint32_t code = ucat(cp) | (isdoc ? CC_DOC : 0u);
+    if (c == '\r' || c == '\n') code |= CC_CRLF;
+    if (c == ' ') code |= CC_SP;
+    if (c == '\'') {
+        // 's 't 're 've 'm 'll 'd (ASCII; case-insensitive except for the GPT-2 family)
+        auto letter = [&](uint32_t t) -> uint32_t {
+            if (p + t >= n || docbit(j + (int)t)) return 0;
+            uint32_t x = sraw[j + t];
+            if (family != 1 && x >= 'A' && x <= 'Z') x += 32;
+            return x;
+        };
+        uint32_t x1 = letter(1), x2 = letter(2), lc = 0;
+        if (x1 == 's' || x1 == 't' || x1 == 'm' || x1 == 'd') lc = 1;
+        else if ((x1 == 'r' && x2 == 'e') || (x1 == 'v' && x2 == 'e') || (x1 == 'l' && x2 == 'l')) lc = 2;
+        code |= lc << CC_CONTR_SHIFT;
+    }
+    return code;
+}
+
 // ---------------------------------------------------------------------------------------------
 // k_init
 
@@ -152,151 +209,63 @@ __global__ void k_init(uint8_t *ws, Layout L)
              *c = (uint64_t *)(ws + L.sflag);
     for (uint32_t k = i; k < L.n_tiles; k += stride) { a[k] = 0; b[k] = 0; }
     for (uint32_t k = i; k < L.n_scan_tiles; k += stride) c[k] = 0;
-    uint8_t *cc = ws + L.cc + (uint64_t)L.n_tiles * TILE;
-    for (uint32_t k = i; k < HALO; k += stride) cc[k] = CC_EOF;
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_classify: one workgroup per tile (blockIdx.x), 16 bytes per thread
+// k_summary: one wavefront per tile.  The tile's summary of a backward flag is the map of its
+// leftmost character whose map is not "pass through" (for NA: the first character that is not
+// whitespace-other-than-CR/LF, or the last of its document; for AU: the first that is not an
+// uppercase letter, or the last of its document).  Usually found in the first 64 bytes.
 
-__global__ __launch_bounds__(PRE_THREADS) void k_classify(const uint8_t *__restrict__ bytes,
-                                                          const uint64_t *__restrict__ offsets,
-                                                          uint32_t n_docs, uint64_t n, int family,
-                                                          uint8_t *ws, Layout L)
+__global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ bytes,
+                                                const uint64_t *__restrict__ offsets, uint32_t n_docs,
+                                                uint64_t n, uint8_t *ws, Layout L)
 {
-    // bytes [lo-4, lo+TILE+8) and their document-start bits
-    constexpr int SPAN = TILE + 12;
-    __shared__ uint8_t sb[SPAN];
-    __shared__ uint32_t sdoc[(SPAN + 31) / 32];
-    __shared__ uint32_t sagg[PRE_THREADS];
-    __shared__ uint32_t s_d0, s_d1;
-
-    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
-    uint8_t *cc = ws + L.cc;
-    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = threadIdx.x;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
-    const int64_t base = (int64_t)lo - 4;
-
-    for (int j = tid; j < SPAN; j += PRE_THREADS) {
-        int64_t p = base + j;
-        sb[j] = (p >= 0 && (uint64_t)p < n) ? bytes[p] : 0;
-    }
-    for (int j = tid; j < (SPAN + 31) / 32; j += PRE_THREADS) sdoc[j] = 0;
-    if (tid == 0) {
-        // first document start >= base, and first >= base + SPAN (offsets are sorted)
-        uint64_t lo_p = base < 0 ? 0 : (uint64_t)base, hi_p = (uint64_t)(base + SPAN);
-        uint32_t a = 0, b = n_docs + 1;
-        while (a < b) { uint32_t m = (a + b) >> 1; if (offsets[m] < lo_p) a = m + 1; else b = m; }
-        uint32_t d0 = a;
-        b = n_docs + 1;
-        while (a < b) { uint32_t m = (a + b) >> 1; if (offsets[m] < hi_p) a = m + 1; else b = m; }
-        s_d0 = d0;
-        s_d1 = a;
-    }
-    // document offsets must start at 0, never decrease and end at n
-    bool bad_offs = false;
-    for (uint64_t d = (uint64_t)blockIdx.x * PRE_THREADS + tid; d < n_docs;
-         d += (uint64_t)gridDim.x * PRE_THREADS)
-        if (offsets[d] > offsets[d + 1]) bad_offs = true;
-    if (blockIdx.x == 0 && tid == 0 && (offsets[0] != 0 || offsets[n_docs] != n)) bad_offs = true;
-    if (bad_offs) atomicOr(&ctrl->status, ST_BAD_OFFSETS);
-    __syncthreads();
-    for (uint32_t d = s_d0 + tid; d < s_d1; d += PRE_THREADS) {
-        int64_t j = (int64_t)offsets[d] - base;
-        if (j >= 0 && j < SPAN) atomicOr(&sdoc[j >> 5], 1u << (j & 31));
-    }
-    __syncthreads();
-
-    auto docbit = [&](int j) -> bool { return (sdoc[j >> 5] >> (j & 31)) & 1u; };
-
-    bool bad = false;
-    uint32_t na_agg = BK_KEEP, au_agg = BK_KEEP;
-    uint32_t outw[PRE_CHUNK / 4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int k = 0; k < PRE_CHUNK; ++k) {
-        const int j = 4 + tid * PRE_CHUNK + k;       // index into sb / sdoc
-        const uint64_t p = lo + tid * PRE_CHUNK + k;
-        uint32_t code;
-        if (p >= n) {
-            code = CC_EOF;
-        } else {
-            const uint32_t c = sb[j];
-            const bool isdoc = docbit(j);
-            if ((c & 0xC0u) == 0x80u) {
-                // continuation: it must be covered by a lead byte 1..3 bytes back in the same doc
-                bool ok = false;
-                if (!isdoc) {
-                    for (int back = 1; back <= 3; ++back) {
-                        if ((int64_t)p - back < 0) break;
-                        uint32_t lead = sb[j - back];
-                        if ((lead & 0xC0u) != 0x80u) { ok = utf8_len(lead) > (uint32_t)back; break; }
-                    }
-                }
-                bad |= !ok;
-                code = CAT_CONT;
-            } else {
+    const uint64_t hi = min(lo + TILE, n);
+    uint32_t na = BK_KEEP, au = BK_KEEP;
+    for (uint64_t w = lo; w < hi && (na == BK_KEEP || au == BK_KEEP); w += 64) {
+        const uint64_t p = w + lane;
+        // document starts in [w, w + 68): indices [dw, de) of offsets (empty documents repeat one)
+        const uint32_t dw = wave_lower_bound(offsets, n_docs + 1, w);
+        const uint32_t de = wave_lower_bound(offsets, n_docs + 1, w + 68);
+        uint32_t mna = BK_KEEP, mau = BK_KEEP;
+        if (p < hi) {
+            const uint32_t c = bytes[p];
+            if ((c & 0xC0u) != 0x80u) {
                 uint32_t len = utf8_len(c), cp = c;
                 bool ok = len != 0 && p + len <= n;
                 if (ok && len > 1) {
                     cp = c & (0x7Fu >> len);
-                    for (uint32_t t = 1; t < len; ++t) {
-                        uint32_t cb = sb[j + t];
-                        ok &= ((cb & 0xC0u) == 0x80u) && !docbit(j + t);
-                        cp = (cp << 6) | (cb & 0x3Fu);
-                    }
-                    ok &= !(len == 3 && cp < 0x800u) && !(len == 4 && (cp < 0x10000u || cp > 0x10FFFFu)) &&
-                          !(cp >= 0xD800u && cp <= 0xDFFFu);
+                    for (uint32_t t = 1; t < len; ++t) cp = (cp << 6) | (bytes[p + t] & 0x3Fu);
                 }
-                bad |= !ok;
                 if (!ok) { len = 1; cp = 0xFFFDu; }
-                uint32_t cat = ucat(cp);
-                code = cat | (isdoc ? CC_DOC : 0u);
-                if (c == '\r' || c == '\n') code |= CC_CRLF;
-                if (c == ' ') code |= CC_SP;
-                if (c == '\'') {
-                    // 's 't 're 've 'm 'll 'd (ASCII; case-insensitive except for the GPT-2 family)
-                    auto letter = [&](uint32_t t) -> uint32_t {
-                        if (p + t >= n || docbit(j + t)) return 0;
-                        uint32_t x = sb[j + t];
-                        if (family != 1 && x >= 'A' && x <= 'Z') x += 32;
-                        return x;
-                    };
-                    uint32_t x1 = letter(1), x2 = letter(2), lc = 0;
-                    if (x1 == 's' || x1 == 't' || x1 == 'm' || x1 == 'd') lc = 1;
-                    else if ((x1 == 'r' && x2 == 'e') || (x1 == 'v' && x2 == 'e') || (x1 == 'l' && x2 == 'l'))
-                        lc = 2;
-                    code |= lc << CC_CONTR_SHIFT;
-                }
+                uint32_t code = ucat(cp) | ((c == '\r' || c == '\n') ? CC_CRLF : 0u);
                 const uint64_t pn = p + len;
-                const bool eof_next = pn >= n || docbit(j + (int)len);
-                uint32_t na, au;
-                backward_maps(code, eof_next, na, au);
-                if (na_agg == BK_KEEP) na_agg = na;
-                if (au_agg == BK_KEEP) au_agg = au;
+                bool eof_next = pn >= n;
+                if (!eof_next) {
+                    uint32_t a = dw, b = de;   // lower bound of pn; pn < w + 68
+                    while (a < b) {
+                        const uint32_t m = (a + b) >> 1;
+                        if (offsets[m] < pn) a = m + 1; else b = m;
+                    }
+                    eof_next = a < de && offsets[a] == pn;
+                }
+                backward_maps(code, eof_next, mna, mau);
             }
         }
-        outw[k >> 2] |= code << (8 * (k & 3));
+        const uint64_t bna = __ballot(mna != BK_KEEP), bau = __ballot(mau != BK_KEEP);
+        const uint32_t xna = __shfl(mna, bna ? __ffsll((unsigned long long)bna) - 1 : 0, 64);
+        const uint32_t xau = __shfl(mau, bau ? __ffsll((unsigned long long)bau) - 1 : 0, 64);
+        if (na == BK_KEEP && bna) na = xna;
+        if (au == BK_KEEP && bau) au = xau;
     }
-    if (bad) atomicOr(&ctrl->status, ST_BAD_UTF8);
-    *(uint4 *)(cc + lo + tid * PRE_CHUNK) = make_uint4(outw[0], outw[1], outw[2], outw[3]);
-
-    // tile summary: the leftmost non-pass-through map of each flag
-    sagg[tid] = na_agg | (au_agg << 2);
-    __syncthreads();
-    if (tid < 64) {
-        uint32_t na = BK_KEEP, au = BK_KEEP;
-        for (int g = 0; g < PRE_THREADS / 64; ++g) {
-            uint32_t x = sagg[g * 64 + tid];
-            uint64_t mna = __ballot((x & 3u) != 0), mau = __ballot((x >> 2) != 0);
-            if (na == BK_KEEP && mna) na = sagg[g * 64 + __ffsll((unsigned long long)mna) - 1] & 3u;
-            if (au == BK_KEEP && mau) au = sagg[g * 64 + __ffsll((unsigned long long)mau) - 1] >> 2;
-        }
-        if (tid == 0) (ws + L.tbwd)[blockIdx.x] = (uint8_t)(na | (au << 2));
-    }
+    if (lane == 0) (ws + L.tbwd)[blockIdx.x] = (uint8_t)(na | (au << 2));
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_pieces: dynamic tile ids; per-char automaton context, scans, look-backs, piece starts
+// k_pieces: dynamic tile ids; decode, automaton context, scans, look-backs, piece starts
 
 // self code of a character (13 values) from its byte code and its NA flag
 __device__ __forceinline__ uint32_t self_code(uint32_t code, bool na)
@@ -331,19 +300,24 @@ __device__ __forceinline__ uint32_t next_code(uint32_t code)
     }
 }
 
-__global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, uint8_t *ws, Layout L)
+__global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes,
+                                                        const uint64_t *__restrict__ offsets, uint32_t n_docs,
+                                                        uint64_t n, uint8_t *ws, Layout L)
 {
+    constexpr int NW = PRE_THREADS / 64;
+    constexpr int SPAN = RAW_LEAD + TILE + RAW_TAIL;
+    __shared__ __align__(16) uint8_t sraw[SPAN];
+    __shared__ uint32_t sdoc[(SPAN + 31) / 32];
     __shared__ __align__(16) uint8_t scc[TILE + HALO];
-    __shared__ uint16_t sctx[TILE];
+    __shared__ uint16_t spiece[TILE];
     __shared__ uint64_t smap[NCTX];
     __shared__ uint32_t sstart[NCTX];
     __shared__ uint32_t sbk[PRE_THREADS];
-    __shared__ uint64_t swmap[PRE_THREADS / 64];
-    __shared__ uint32_t swcnt[PRE_THREADS / 64];
-    __shared__ uint32_t s_tile, s_carry, s_entry, s_base;
+    __shared__ uint64_t swmap[NW];
+    __shared__ uint32_t swcnt[NW];
+    __shared__ uint32_t s_tile, s_carry, s_entry, s_base, s_d0, s_d1;
 
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
-    const uint8_t *cc = ws + L.cc;
     const uint8_t *tbwd = ws + L.tbwd;
     uint64_t *tfs = (uint64_t *)(ws + L.tflag_state);
     uint64_t *tfc = (uint64_t *)(ws + L.tflag_cnt);
@@ -352,12 +326,62 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, 
 
     if (tid == 0) s_tile = atomicAdd(&ctrl->tile_ctr_pre, 1u);
     for (int i = tid; i < NCTX; i += PRE_THREADS) { smap[i] = v.fmap[i]; sstart[i] = v.fstart[i]; }
+    for (int j = tid; j < (SPAN + 31) / 32; j += PRE_THREADS) sdoc[j] = 0;
     __syncthreads();
     const uint32_t tile = s_tile;
     const uint64_t lo = (uint64_t)tile * TILE;
-    // the code bytes of the tile and its halo (past the batch end they read CC_EOF)
-    *(uint4 *)(scc + tid * PRE_CHUNK) = *(const uint4 *)(cc + lo + tid * PRE_CHUNK);
-    if (tid < HALO / 4) ((uint32_t *)(scc + TILE))[tid] = ((const uint32_t *)(cc + lo + TILE))[tid];
+    const int64_t base = (int64_t)lo - RAW_LEAD;
+
+    // raw bytes [lo - 4, lo + TILE + 24), as 32-bit words
+    for (int j = tid; j < SPAN / 4; j += PRE_THREADS) {
+        const int64_t p = base + 4 * j;
+        uint32_t w = 0;
+        for (int t = 0; t < 4; ++t)
+            if (p + t >= 0 && (uint64_t)(p + t) < n) w |= (uint32_t)bytes[p + t] << (8 * t);
+        ((uint32_t *)sraw)[j] = w;
+    }
+    if (wid == 0) {
+        const uint64_t lo_p = base < 0 ? 0 : (uint64_t)base, hi_p = (uint64_t)(base + SPAN);
+        const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, lo_p);
+        const uint32_t d1 = wave_lower_bound(offsets, n_docs + 1, hi_p);
+        if (lane == 0) { s_d0 = d0; s_d1 = d1; }
+    }
+    // document offsets must start at 0, never decrease and end at n
+    bool bad_offs = false;
+    for (uint64_t d = (uint64_t)tile * PRE_THREADS + tid; d < n_docs; d += (uint64_t)gridDim.x * PRE_THREADS)
+        if (offsets[d] > offsets[d + 1]) bad_offs = true;
+    if (tile == 0 && tid == 0 && (offsets[0] != 0 || offsets[n_docs] != n)) bad_offs = true;
+    if (bad_offs) atomicOr(&ctrl->status, ST_BAD_OFFSETS);
+    __syncthreads();
+    for (uint32_t d = s_d0 + tid; d < s_d1; d += PRE_THREADS) {
+        int64_t j = (int64_t)offsets[d] - base;
+        if (j >= 0 && j < SPAN) atomicOr(&sdoc[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    auto docbit = [&](int j) -> bool { return (sdoc[j >> 5] >> (j & 31)) & 1u; };
+
+    // per-byte codes of the tile (validated) and of the halo after it
+    const int c0 = tid * PRE_CHUNK;
+    {
+        bool bad = false;
+        uint32_t w[PRE_CHUNK / 4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < PRE_CHUNK; ++k) {
+            const uint64_t p = lo + c0 + k;
+            const uint32_t code = p < n ? byte_code(sraw, docbit, RAW_LEAD + c0 + k, p, n, v.family, true, bad)
+                                        : (uint32_t)CC_EOF;
+            w[k >> 2] |= code << (8 * (k & 3));
+        }
+        *(uint4 *)(scc + c0) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (tid < HALO) {
+            const uint64_t p = lo + TILE + tid;
+            bool ignore = false;
+            scc[TILE + tid] = p < n ? (uint8_t)byte_code(sraw, docbit, RAW_LEAD + TILE + tid, p, n, v.family, false,
+                                                         ignore)
+                                    : CC_EOF;
+        }
+        if (bad) atomicOr(&ctrl->status, ST_BAD_UTF8);
+    }
 
     // backward carry into this tile: first non-pass-through summary of a later tile
     if (wid == 0) {
@@ -366,8 +390,8 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, 
             uint32_t t = t0 + lane;
             uint32_t x = t < L.n_tiles ? (uint32_t)tbwd[t] : (BK_T | (BK_T << 2));
             uint64_t mna = __ballot((x & 3u) != 0), mau = __ballot((x >> 2) != 0);
-            uint32_t xna = __shfl(x, __ffsll((unsigned long long)mna) - 1, 64);
-            uint32_t xau = __shfl(x, __ffsll((unsigned long long)mau) - 1, 64);
+            uint32_t xna = __shfl(x, mna ? __ffsll((unsigned long long)mna) - 1 : 0, 64);
+            uint32_t xau = __shfl(x, mau ? __ffsll((unsigned long long)mau) - 1 : 0, 64);
             if (na == BK_KEEP && mna) na = xna & 3u;
             if (au == BK_KEEP && mau) au = xau >> 2;
         }
@@ -376,10 +400,14 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, 
     __syncthreads();
 
     // per character: backward maps of this thread's chunk
-    const int c0 = tid * PRE_CHUNK;
     uint32_t code[PRE_CHUNK + 4];
+    {
+        const uint4 a = *(const uint4 *)(scc + c0);
+        const uint32_t tail = *(const uint32_t *)(scc + c0 + PRE_CHUNK);
+        const uint32_t wv[5] = {a.x, a.y, a.z, a.w, tail};
 #pragma unroll
-    for (int k = 0; k < PRE_CHUNK + 4; ++k) code[k] = scc[c0 + k];
+        for (int k = 0; k < PRE_CHUNK + 4; ++k) code[k] = (wv[k >> 2] >> (8 * (k & 3))) & 255u;
+    }
     uint32_t eofn = 0, nxt_code[PRE_CHUNK];
     uint32_t bna[PRE_CHUNK], bau[PRE_CHUNK];
     uint32_t agg = BK_KEEP | (BK_KEEP << 2);
@@ -451,7 +479,7 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, 
     if (lane == 0) excl = MAP_IDENTITY;
     __syncthreads();
     uint64_t pre = MAP_IDENTITY, tile_map = MAP_IDENTITY;
-    for (uint32_t w = 0; w < PRE_THREADS / 64; ++w) {
+    for (uint32_t w = 0; w < (uint32_t)NW; ++w) {
         if (w < wid) pre = compose(pre, swmap[w]);
         tile_map = compose(tile_map, swmap[w]);
     }
@@ -487,9 +515,18 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, 
     if (lane == 63) swcnt[wid] = icnt;
     __syncthreads();
     uint32_t before = icnt - cnt, total = 0;
-    for (uint32_t w = 0; w < PRE_THREADS / 64; ++w) {
+    for (uint32_t w = 0; w < (uint32_t)NW; ++w) {
         if (w < wid) before += swcnt[w];
         total += swcnt[w];
+    }
+    // stage this tile's starts in LDS for a coalesced write
+    {
+        uint32_t o = before, m = mask;
+        while (m) {
+            int k = __ffs(m) - 1;
+            m &= m - 1;
+            spiece[o++] = (uint16_t)(c0 + k);
+        }
     }
 
     // look-back #2: number of pieces before this tile
@@ -506,12 +543,8 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, uint64_t n, 
         }
     }
     __syncthreads();
-    uint32_t o = s_base + before;
-    while (mask) {
-        int k = __ffs(mask) - 1;
-        mask &= mask - 1;
-        pstart[o++] = (uint32_t)(lo + c0 + k);
-    }
+    const uint32_t gbase = s_base;
+    for (uint32_t i = tid; i < total; i += PRE_THREADS) pstart[gbase + i] = (uint32_t)(lo + spiece[i]);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -556,12 +589,12 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
     if (L.n_tiles == 0) return hipGetLastError();
     {
         LaunchScope k(ev, 1, s);
-        hipLaunchKernelGGL(k_classify, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, b.bytes, b.offsets, b.n_docs,
-                           b.n, v.family, b.ws, L);
+        hipLaunchKernelGGL(k_summary, dim3(L.n_tiles), dim3(64), 0, s, b.bytes, b.offsets, b.n_docs, b.n, b.ws, L);
     }
     {
         LaunchScope k(ev, 2, s);
-        hipLaunchKernelGGL(k_pieces, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.n, b.ws, L);
+        hipLaunchKernelGGL(k_pieces, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs,
+                           b.n, b.ws, L);
     }
     return launch_bins(b, s, ev);
 }

@@ -208,7 +208,7 @@ int build_whole_piece_tables(toktier_vocab *v, const uint32_t *merges, uint32_t 
     std::vector<uint32_t> cand, starts;
     std::vector<uint8_t> batch;
     for (uint32_t t = 256; t < ntok_all; ++t) {
-        if (len[t] < 2 || len[t] > (uint32_t)LANE_MAX) continue;
+        if (len[t] < 2 || len[t] > (uint32_t)TABLE_MAX) continue;
         cand.push_back(t);
         starts.push_back((uint32_t)batch.size());
         batch.insert(batch.end(), tb.begin() + off[t], tb.begin() + off[t] + len[t]);

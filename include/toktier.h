@@ -141,19 +141,19 @@ int toktier_pretokenize_batch(const toktier_vocab *v, const uint8_t *bytes, cons
  */
 int toktier_last_status(void *workspace, void *stream, uint64_t *out_n_tokens);
 
-/* Kernel launches of one toktier_encode_batch call, in stream order (indices for the timed form). */
+/* Kernel launches of one toktier_encode_batch call, in stream order (indices for the timed form).
+ * An index may cover several launches of one step. */
 enum {
-    TOKTIER_K_INIT = 0,       /* clear the control block and look-back flags                  */
-    TOKTIER_K_CLASSIFY,       /* UTF-8 decode, validation, categories, backward summaries     */
-    TOKTIER_K_PIECES,         /* automaton scan, piece starts, piece numbering                */
-    TOKTIER_K_BINS,           /* length bins for pieces longer than a lane's limit            */
-    TOKTIER_K_BPE_LANE,       /* BPE, one lane per piece of <= 16 bytes                       */
-    TOKTIER_K_BPE_WAVE,       /* BPE, one wavefront per piece of 17..1024 bytes               */
-    TOKTIER_K_BPE_BLOCK,      /* BPE, one workgroup per piece of 1025..4096 bytes             */
+    TOKTIER_K_INIT = 0,       /* clear the control block and look-back flags                    */
+    TOKTIER_K_SUMMARY,        /* per tile: the characters that decide the backward flags        */
+    TOKTIER_K_PIECES,         /* UTF-8 decode + validation, automaton scan, piece starts        */
+    TOKTIER_K_BINS,           /* length bins for pieces longer than a lane's limit              */
+    TOKTIER_K_BPE_LANE,       /* whole-piece lookup, then BPE with one lane per piece <= 64 B   */
+    TOKTIER_K_BPE_WAVE,       /* BPE, one wavefront per piece of 65..1024 bytes                 */
+    TOKTIER_K_BPE_BLOCK,      /* BPE, one workgroup per piece of 1025..4096 bytes               */
     TOKTIER_K_BPE_GIANT,      /* BPE, one workgroup per longer piece, sequence in device memory */
-    TOKTIER_K_TOKSCAN,        /* exclusive scan of per-piece token counts                     */
-    TOKTIER_K_GATHER,         /* per-piece IDs -> contiguous out_ids                          */
-    TOKTIER_K_DOCOFF,         /* per-document token offsets                                   */
+    TOKTIER_K_EMIT,           /* token-offset scan, ID gather, per-document token offsets       */
+    TOKTIER_K_GATHER_LONG,    /* ID gather of the binned (long) pieces                          */
     TOKTIER_K_COUNT
 };
 
