@@ -41,9 +41,11 @@ MAIN = "c4_batch64"
 LATENCY = ("c1_ec4k", "c2_at100k", "c3_mix1m", "c5_adv4m4")
 
 # input bytes each kernel launch processes (the unit of the algorithmic-bytes figure)
+# (bytes of the pieces in the length range the launch serves)
 UNITS = {
     "init": "all", "summary": "all", "pieces": "all", "bins": "all", "emit": "all", "gather_long": "binned",
-    "bpe_lane": "lane", "bpe_wave": "wave", "bpe_block": "block", "bpe_giant": "giant",
+    "bpe_lookup": "lane", "bpe_lane": "le16", "bpe_seg32": "17to32", "bpe_seg64": "33to64",
+    "bpe_wave": "wave", "bpe_block": "block", "bpe_giant": "giant",
 }
 
 
@@ -123,7 +125,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--latency-reps", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-latency", action="store_true",
+                    help="skip the single-request latency leg (so that a profiler sees only batch launches)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (for HBM counter calibration)")
     args = ap.parse_args()
@@ -134,7 +138,7 @@ def main():
 
     t_start = time.time()
     _log("generating workloads")
-    work = {name: textgen.workload(name) for name in (MAIN,) + LATENCY}
+    work = {name: textgen.workload(name) for name in (MAIN,) + (() if args.no_latency else LATENCY)}
     fam, voc, data, offs = work[MAIN]
 
     cpu = None
@@ -144,12 +148,13 @@ def main():
         _log(f"cpu baseline: oracle on {workers} workers")
         cpu, oracle_ref[MAIN] = cpu_baseline(fam, voc, data, offs, args.cpu_seconds, workers)
         import oracle
-        for name in LATENCY:
+        for name in (() if args.no_latency else LATENCY):
             f2, v2, d2, o2 = work[name]
             merges, _ = textgen.load_vocab(v2)
             oracle_ref[name] = oracle.encode_batch(f2, merges, d2, o2)
-        f3, v3, d3, o3 = work["c3_mix1m"]
-        cpu["p50_ms_1m_char_request_single_core"] = round(oracle_latency(f3, v3, d3, o3), 3)
+        if not args.no_latency:
+            f3, v3, d3, o3 = work["c3_mix1m"]
+            cpu["p50_ms_1m_char_request_single_core"] = round(oracle_latency(f3, v3, d3, o3), 3)
 
     import torch
     import exact_bpe_tokenization_amd as tt
@@ -207,7 +212,9 @@ def main():
     # input bytes per length bin (from the GPU split)
     starts = tok.pretokenize(data.tobytes(), offs)
     plen = np.diff(starts.astype(np.int64))
-    bins = {"all": int(n), "lane": int(plen[plen <= 64].sum()), "wave": int(plen[(plen > 64) & (plen <= 1024)].sum()),
+    bins = {"all": int(n), "lane": int(plen[plen <= 64].sum()), "le16": int(plen[plen <= 16].sum()),
+            "17to32": int(plen[(plen > 16) & (plen <= 32)].sum()), "33to64": int(plen[(plen > 32) & (plen <= 64)].sum()),
+            "wave": int(plen[(plen > 64) & (plen <= 1024)].sum()),
             "block": int(plen[(plen > 1024) & (plen <= 4096)].sum()), "giant": int(plen[plen > 4096].sum()),
             "binned": int(plen[plen > 64].sum())}
     alg_per_byte = (n + 4 * n_tokens + 16 * (D + 1)) / n
@@ -232,7 +239,7 @@ def main():
     exact = {}
     if oracle_ref:
         exact[MAIN] = bool(np.array_equal(gpu_ids, oracle_ref[MAIN][0]) and np.array_equal(gpu_oo, oracle_ref[MAIN][1]))
-    for name in LATENCY:
+    for name in (() if args.no_latency else LATENCY):
         f2, v2, d2, o2 = work[name]
         m2, ff = textgen.load_vocab(v2)
         t2 = tok if v2 == voc else tt.Tokenizer(m2, ff, device="cuda:0")
@@ -271,7 +278,7 @@ def main():
                                f"{n} bytes, cl100k-style rules, 131,072-merge vocabulary",
                    "bytes": int(n), "docs": int(D), "tokens": int(n_tokens), "family": fam,
                    "input_sha256": textgen.sha256(data.tobytes())},
-        "p50_ms_per_1m_char_request": latency["c3_mix1m"]["p50"],
+        "p50_ms_per_1m_char_request": latency["c3_mix1m"]["p50"] if latency else None,
         "latency_ms": latency,
         "path_alg_gbs": round(path_alg, 3),
         "path_alg_frac_of_hbm": round(path_alg / HBM_PEAK_GBS, 6),

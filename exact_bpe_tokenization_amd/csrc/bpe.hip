@@ -144,10 +144,15 @@ __global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__r
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
     const uint32_t *list = (const uint32_t *)(ws + (which == 0 ? L.miss16 : (which == 1 ? L.miss32 : L.miss64)));
     const uint32_t count = ctrl->miss_count[which];
-    for (uint32_t q = blockIdx.x * blockDim.x + threadIdx.x; q < count; q += gridDim.x * blockDim.x) {
-        const uint32_t p = list[q];
-        const uint32_t b0 = pstart[p];
-        const uint32_t len = pstart[p + 1] - b0;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t stride = gridDim.x * blockDim.x;
+    // wavefront-uniform loop (the token-count update below is a wavefront operation)
+    for (uint32_t q0 = blockIdx.x * blockDim.x + (threadIdx.x & ~63u); q0 < count; q0 += stride) {
+        const uint32_t q = q0 + lane;
+        const bool active = q < count;
+        const uint32_t p = active ? list[q] : 0u;
+        const uint32_t b0 = active ? pstart[p] : 0u;
+        const uint32_t len = active ? pstart[p + 1] - b0 : 0u;   // 0: nothing to merge or write
         uint32_t id[MAXL], rk[MAXL];
 #pragma unroll
         for (int k = 0; k < MAXL; ++k) id[k] = (uint32_t)k < len ? (uint32_t)bytes[b0 + k] : 0u;
@@ -188,7 +193,8 @@ __global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__r
 #pragma unroll
         for (int k = 0; k < MAXL; ++k)
             if ((uint32_t)k < n) scratch[b0 + k] = id[k];
-        ntok[p] = n;
+        if (active) ntok[p] = n;
+        add_excess_wave(ws, L, p, active ? n - 1 : 0u);
     }
 }
 
@@ -265,7 +271,9 @@ __global__ __launch_bounds__(256) void k_bpe_seg(DevVocab v, const uint8_t *__re
             else if (rk == PENDING) rk = k + 1 < n ? pair_rank(v, id, nx) : NO_RANK;
         }
         if (k < n) scratch[b0 + k] = id;
-        if (k == 0 && q < count) ntok[p] = n;
+        const bool head = k == 0 && q < count;
+        if (head) ntok[p] = n;
+        add_excess_wave(ws, L, p, head ? n - 1 : 0u);
     }
 }
 
@@ -444,7 +452,7 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
             n = nnew;
         }
         for (uint32_t k = tid; k < n; k += NT) scratch[b0 + k] = sid[k];
-        if (tid == 0) ntok[p] = n;
+        if (tid == 0) put_ntok(ws, L, p, n);
         __syncthreads();
     }
 }
@@ -575,7 +583,7 @@ __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const u
         uint32_t *dst = (uint32_t *)(ws + L.scratch) + b0;
         if (idA != dst)
             for (uint32_t k = tid; k < n; k += NT) dst[k] = idA[k];
-        if (tid == 0) ntok[p] = n;
+        if (tid == 0) put_ntok(ws, L, p, n);
         __syncthreads();
     }
 }
@@ -590,27 +598,36 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     {
         LaunchScope k(ev, 4, s);
         hipLaunchKernelGGL(k_bpe_lookup, dim3(g > 1024 ? 1024 : g), dim3(LK_THREADS), 0, s, v, b.bytes, b.ws, L);
+    }
+    {
+        LaunchScope k(ev, 5, s);
         hipLaunchKernelGGL((k_bpe_lane<16>), dim3(g > 2048 ? 2048 : g), dim3(256), 0, s, v, b.bytes, b.ws, L, 0);
-        // at most n / 17 pieces of 17..32 bytes (8 per workgroup), n / 33 of 33..64 (4 per workgroup)
-        const uint64_t g32 = b.n / 17 / 8 + 1, g64 = b.n / 33 / 4 + 1;
+    }
+    // at most n / 17 pieces of 17..32 bytes (8 per workgroup), n / 33 of 33..64 (4 per workgroup)
+    const uint64_t g32 = b.n / 17 / 8 + 1, g64 = b.n / 33 / 4 + 1;
+    {
+        LaunchScope k(ev, 6, s);
         hipLaunchKernelGGL((k_bpe_seg<32>), dim3(g32 > 2048 ? 2048 : (uint32_t)g32), dim3(256), 0, s, v, b.bytes,
                            b.ws, L, 1);
+    }
+    {
+        LaunchScope k(ev, 7, s);
         hipLaunchKernelGGL((k_bpe_seg<64>), dim3(g64 > 1024 ? 1024 : (uint32_t)g64), dim3(256), 0, s, v, b.bytes,
                            b.ws, L, 2);
     }
     {
-        LaunchScope k(ev, 5, s);
+        LaunchScope k(ev, 8, s);
         uint32_t gw = L.cap_wave < 4096 ? L.cap_wave : 4096;
         hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
     }
     {
-        LaunchScope k(ev, 6, s);
+        LaunchScope k(ev, 9, s);
         uint32_t gb = L.cap_block < 1024 ? L.cap_block : 1024;
         hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v,
                            b.bytes, b.ws, L, 1);
     }
     {
-        LaunchScope k(ev, 7, s);
+        LaunchScope k(ev, 10, s);
         uint32_t gg = L.cap_giant < 256 ? L.cap_giant : 256;
         hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
     }

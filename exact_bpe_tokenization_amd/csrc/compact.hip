@@ -3,9 +3,10 @@
 // TokTier (arXiv 2607.29678), GPU full-tokenization paragraph: the complete path ends with output
 // compaction, and piece counts and output length stay in device memory (no host round trip between
 // kernels).  k_emit does it in one pass per tile of 4096 pieces: coalesced loads of the per-piece
-// token counts and starts, a workgroup scan plus a decoupled look-back for the tile's first token
-// offset, the gather of each piece's IDs into out_ids (consecutive pieces write consecutive IDs),
-// and the token offsets of the documents whose first piece lies in the tile.  Pieces longer than a
+// token counts and starts, a workgroup scan, the tile's first token offset from the per-tile excess
+// counters the BPE kernels maintain (no look-back between tiles, no tile tickets), the gather of each
+// piece's IDs into out_ids (consecutive pieces write consecutive IDs), and the token offsets of the
+// documents whose first piece lies in the tile.  Pieces longer than a
 // lane's limit (a few, with many IDs each) are copied by k_gather_long, one workgroup per piece.
 #include "internal.h"
 
@@ -16,100 +17,102 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
                                                       uint64_t *__restrict__ out_offsets)
 {
     constexpr int NW = SCAN_THREADS / 64;
-    __shared__ uint32_t soff[SCAN_TILE + 1];     // token counts, then token offsets
-    __shared__ uint32_t sps[SCAN_TILE + 1];      // piece starts of the tile and the next one
-    __shared__ uint32_t swsum[NW];
-    __shared__ uint32_t s_tile, s_base, s_prev, s_dA, s_dB;
+    constexpr int IT = SCAN_TILE / SCAN_THREADS;   // iterations of 64 pieces per wavefront
+    __shared__ uint32_t soff[SCAN_TILE + 1];       // token offset of each piece of the tile
+    __shared__ uint32_t swsum[NW], sxs[NW];
+    __shared__ uint32_t s_dA, s_dB;
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
-    const uint32_t *ntok = (const uint32_t *)(ws + L.ntok);
-    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    const uint32_t *scratch = (const uint32_t *)(ws + L.scratch);
-    uint32_t *tokoff = (uint32_t *)(ws + L.tokoff);
-    uint64_t *flags = (uint64_t *)(ws + L.sflag);
+    const uint32_t *__restrict__ ntok = (const uint32_t *)(ws + L.ntok);
+    const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t *__restrict__ scratch = (const uint32_t *)(ws + L.scratch);
+    const uint32_t *__restrict__ tilex = (const uint32_t *)(ws + L.tilex);
+    uint32_t *__restrict__ tokoff = (uint32_t *)(ws + L.tokoff);
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
-    if (tid == 0) s_tile = atomicAdd(&ctrl->tile_ctr_scan, 1u);
-    __syncthreads();
-    const uint32_t tile = s_tile;
+    const uint32_t tile = blockIdx.x;
     const uint32_t np = ctrl->n_pieces;
     const uint64_t first64 = (uint64_t)tile * SCAN_TILE;
     if (first64 > np) return;                          // nothing at or below P in this tile
     const uint32_t first = (uint32_t)first64;
-    const uint32_t cnt_t = min((uint32_t)SCAN_TILE, np - first);
-    const bool last = first + cnt_t == np;
-    for (uint32_t i = tid; i < cnt_t; i += SCAN_THREADS) {
-        soff[i] = ntok[first + i];
-        sps[i] = pstart[first + i];
-    }
-    if (tid == 0) {
-        sps[cnt_t] = np ? pstart[first + cnt_t] : (uint32_t)n;   // pstart[np] == n
-        s_prev = first ? pstart[first - 1] : 0u;
-    }
-    __syncthreads();
-    const uint32_t i0 = tid * SCAN_PER_THREAD;
-    uint32_t x[SCAN_PER_THREAD], sum = 0;
+    const uint32_t end = min(first + (uint32_t)SCAN_TILE, np);
+    const bool last = end == np;
+
+    // wavefront wid owns pieces [wb, wb + 64 * IT) of the tile, 64 consecutive pieces per iteration
+    // (lane-consecutive: coalesced loads and stores)
+    const uint32_t wb = first + wid * (64u * IT);
+    uint32_t c[IT], st[IT], ex[IT];
 #pragma unroll
-    for (int k = 0; k < SCAN_PER_THREAD; ++k) {
-        x[k] = i0 + k < cnt_t ? soff[i0 + k] : 0u;
-        sum += x[k];
+    for (int it = 0; it < IT; ++it) {
+        const uint32_t i = wb + it * 64u + lane;
+        c[it] = i < end ? ntok[i] : 0u;
+        st[it] = i <= np ? pstart[i] : 0u;            // pstart[np] == n
     }
-    uint32_t inc = sum;
+    // tokens before this tile: one per piece plus the excess counted by the BPE kernels
+    uint32_t xs = 0;
+    for (uint32_t t = tid; t < tile; t += SCAN_THREADS) xs += tilex[t];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(inc, d, 64);
-        if (lane >= (uint32_t)d) inc += y;
-    }
-    if (lane == 63) swsum[wid] = inc;
-    __syncthreads();
-    uint32_t before = inc - sum, total = 0;
-    for (uint32_t w = 0; w < (uint32_t)NW; ++w) {
-        if (w < wid) before += swsum[w];
-        total += swsum[w];
-    }
-    if (wid == 0) {
-        if (lane == 0 && tile > 0) st_flag(flags + tile, (1ull << 62) | total);
-        const uint64_t basev = tile == 0 ? 0 : lookback_sum(flags, tile);
-        if (lane == 0) {
-            st_flag(flags + tile, (2ull << 62) | (basev + total));
-            s_base = (uint32_t)basev;
-            if (last) ctrl->n_tokens = (uint32_t)(basev + total);
+    for (int d = 32; d >= 1; d >>= 1) xs += __shfl_xor(xs, d, 64);
+    uint32_t run = 0;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        uint32_t inc = c[it];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t y = __shfl_up(inc, d, 64);
+            if (lane >= (uint32_t)d) inc += y;
         }
+        ex[it] = run + inc - c[it];
+        run += __shfl(inc, 63, 64);
     }
+    if (lane == 0) { swsum[wid] = run; sxs[wid] = xs; }
     __syncthreads();
-    const uint32_t base = s_base, tile_end = base + total;
-    uint32_t run = base + before;
+    uint32_t before = 0, total = 0, tbase = first;
 #pragma unroll
-    for (int k = 0; k < SCAN_PER_THREAD; ++k) {
-        if (i0 + k < cnt_t) soff[i0 + k] = run;
-        run += x[k];
+    for (int w = 0; w < NW; ++w) {
+        if (w < (int)wid) before += swsum[w];
+        total += swsum[w];
+        tbase += sxs[w];
     }
-    if (tid == 0) soff[cnt_t] = tile_end;
-    __syncthreads();
-    // gather: piece i of the tile owns IDs [soff[i], soff[i+1]) at scratch[its start byte ...]
-    for (uint32_t i = tid; i < cnt_t; i += SCAN_THREADS) {
-        const uint32_t o = soff[i], c = soff[i + 1] - o, b0 = sps[i];
-        if (sps[i + 1] - b0 > (uint32_t)LANE_MAX) {
-            tokoff[first + i] = o;                      // binned piece: k_gather_long copies it
+    if (last && tid == 0) ctrl->n_tokens = tbase + total;
+    const uint32_t obase = tbase + before;
+
+    // gather: piece i owns IDs [o, o + c) at scratch[its start byte ...]; first all loads, then all stores
+    uint32_t len[IT], v0[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const uint32_t i = wb + it * 64u + lane;
+        uint32_t nx = __shfl_down(st[it], 1, 64);
+        const uint32_t nx0 = __shfl(st[(it + 1) % IT], 0, 64);   // first start of the next iteration
+        if (lane == 63) nx = it + 1 < IT ? nx0 : (i + 1 <= np ? pstart[i + 1] : 0u);
+        len[it] = nx - st[it];
+        v0[it] = (i < end && len[it] <= (uint32_t)LANE_MAX) ? scratch[st[it]] : 0u;
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const uint32_t i = wb + it * 64u + lane;
+        if (i >= end) continue;
+        const uint32_t o = obase + ex[it];
+        soff[i - first] = o;
+        if (len[it] > (uint32_t)LANE_MAX) {
+            tokoff[i] = o;                              // binned piece: k_gather_long copies it
             continue;
         }
-        const uint32_t *src = scratch + b0;
-        for (uint32_t j = 0; j < c; ++j) out_ids[o + j] = src[j];
+        out_ids[o] = v0[it];
+        for (uint32_t j = 1; j < c[it]; ++j) out_ids[o + j] = scratch[st[it] + j];
     }
+    if (tid == 0) soff[end - first] = tbase + total;
+
     // documents whose first piece is in this tile: offsets in (start of the piece before the
     // tile, start of the tile's last piece]; the last tile also takes everything after it
     if (wid == 0) {
-        const uint32_t dA = first ? wave_upper_bound(offsets, n_docs + 1, (uint64_t)s_prev) : 0u;
-        const uint32_t dB = last ? n_docs + 1 : wave_upper_bound(offsets, n_docs + 1, (uint64_t)sps[cnt_t - 1]);
+        const uint32_t dA = first ? wave_upper_bound(offsets, n_docs + 1, (uint64_t)pstart[first - 1]) : 0u;
+        const uint32_t dB = last ? n_docs + 1 : wave_upper_bound(offsets, n_docs + 1, (uint64_t)pstart[end - 1]);
         if (lane == 0) { s_dA = dA; s_dB = dB; }
     }
     __syncthreads();
-    for (uint32_t d = s_dA + tid; d < s_dB; d += SCAN_THREADS) {
-        const uint64_t off = offsets[d];
-        uint32_t a = 0, b = cnt_t;
-        while (a < b) {
-            uint32_t m = (a + b) >> 1;
-            if ((uint64_t)sps[m] < off) a = m + 1; else b = m;
-        }
-        out_offsets[d] = soff[a];
+    for (uint32_t d = s_dA + wid; d < s_dB; d += NW) {
+        // the first piece of the tile starting at or after the document's offset
+        const uint32_t a = wave_lower_bound(pstart + first, end - first, (uint32_t)offsets[d]);
+        if (lane == 0) out_offsets[d] = soff[a];
     }
 }
 
@@ -147,12 +150,12 @@ hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offse
 {
     const Layout &L = b.L;
     {
-        LaunchScope k(ev, 8, s);
+        LaunchScope k(ev, 11, s);
         hipLaunchKernelGGL(k_emit, dim3(L.n_scan_tiles), dim3(SCAN_THREADS), 0, s, b.ws, L, b.offsets, b.n_docs,
                            b.n, out_ids, out_offsets);
     }
     if (b.n) {
-        LaunchScope k(ev, 9, s);
+        LaunchScope k(ev, 12, s);
         uint32_t gl = L.cap_wave < 2048 ? L.cap_wave : 2048;
         hipLaunchKernelGGL(k_gather_long, dim3(gl), dim3(256), 0, s, b.ws, L, out_ids);
     }

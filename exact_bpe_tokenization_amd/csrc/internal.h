@@ -127,8 +127,8 @@ __device__ __forceinline__ uint64_t lookback_sum(const uint64_t *flags, uint32_t
 // First index i in [0, n) whose entry satisfies pred (n if none), for a predicate that is false
 // then true along the sorted array.  Called by a whole wavefront: each step probes 64 evenly spaced
 // entries, so a search costs about log64(n) + 1 dependent loads.
-template <typename Pred>
-__device__ __forceinline__ uint32_t wave_partition_point(const uint64_t *a, uint32_t n, Pred pred)
+template <typename T, typename Pred>
+__device__ __forceinline__ uint32_t wave_partition_point(const T *a, uint32_t n, Pred pred)
 {
     const uint32_t lane = threadIdx.x & 63u;
     uint32_t lo = 0, hi = n;   // the answer lies in [lo, hi]
@@ -150,14 +150,16 @@ __device__ __forceinline__ uint32_t wave_partition_point(const uint64_t *a, uint
     return t ? lo + (uint32_t)__ffsll((unsigned long long)t) - 1u : hi;
 }
 
-__device__ __forceinline__ uint32_t wave_lower_bound(const uint64_t *a, uint32_t n, uint64_t x)
+template <typename T>
+__device__ __forceinline__ uint32_t wave_lower_bound(const T *a, uint32_t n, T x)
 {
-    return wave_partition_point(a, n, [x](uint64_t v) { return v >= x; });
+    return wave_partition_point(a, n, [x](T v) { return v >= x; });
 }
 
-__device__ __forceinline__ uint32_t wave_upper_bound(const uint64_t *a, uint32_t n, uint64_t x)
+template <typename T>
+__device__ __forceinline__ uint32_t wave_upper_bound(const T *a, uint32_t n, T x)
 {
-    return wave_partition_point(a, n, [x](uint64_t v) { return v > x; });
+    return wave_partition_point(a, n, [x](T v) { return v > x; });
 }
 
 __device__ __forceinline__ uint32_t pair_rank(const DevVocab &v, uint32_t a, uint32_t b)
@@ -180,12 +182,11 @@ enum : uint32_t { ST_BAD_UTF8 = 1, ST_BAD_OFFSETS = 2 };
 struct Ctrl {
     uint32_t status;
     uint32_t tile_ctr_pre;     // dynamic tile ids for the piece kernel
-    uint32_t tile_ctr_scan;    // dynamic tile ids for the token-offset scan
     uint32_t n_pieces;
     uint32_t n_tokens;
     uint32_t bin_count[3];     // wave, block, giant bins
     uint32_t miss_count[3];    // pieces left for lane BPE: <= 16, 17..32, 33..64 bytes
-    uint32_t pad[53];
+    uint32_t pad[54];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
@@ -193,7 +194,7 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // workspace layout for n input bytes
 struct Layout {
     uint64_t ctrl, cc, tbwd, tflag_state, tflag_cnt, pstart, ntok, tokoff, scratch, bin_wave,
-        bin_block, bin_giant, miss16, miss32, miss64, g_ids, g_rank_a, g_rank_b, sflag, total;
+        bin_block, bin_giant, miss16, miss32, miss64, g_ids, g_rank_a, g_rank_b, tilex, total;
     uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant;
 };
 
@@ -213,7 +214,7 @@ inline Layout make_layout(uint64_t n)
     L.tbwd = o;        o += align256((uint64_t)L.n_tiles + 1);
     L.tflag_state = o; o += align256(8ull * L.n_tiles);
     L.tflag_cnt = o;   o += align256(8ull * L.n_tiles);
-    L.sflag = o;       o += align256(8ull * L.n_scan_tiles);
+    L.tilex = o;       o += align256(4ull * L.n_scan_tiles);
     L.pstart = o;      o += align256(4ull * (n + 2));
     L.ntok = o;        o += align256(4ull * (n + 1));
     L.tokoff = o;      o += align256(4ull * (n + 2));
@@ -229,6 +230,36 @@ inline Layout make_layout(uint64_t n)
     L.g_rank_b = o;    o += align256(4ull * (n + 1));
     L.total = o;
     return L;
+}
+
+// Token count n >= 1 of piece p.  The excess over one token is added to the counter of the piece's
+// output tile (SCAN_TILE consecutive pieces); the compaction kernel derives each tile's first output
+// position from those counters instead of a look-back across tiles.
+__device__ __forceinline__ void put_ntok(uint8_t *ws, const Layout &L, uint32_t p, uint32_t n)
+{
+    ((uint32_t *)(ws + L.ntok))[p] = n;
+    if (n > 1) atomicAdd((uint32_t *)(ws + L.tilex) + p / SCAN_TILE, n - 1);
+}
+
+// Wavefront form of the same counter update, called by all 64 lanes: lane i contributes the
+// excess x (0 when it has none) of piece p; lanes are combined over runs of equal output tiles in
+// lane order (pieces taken from a list in ascending order mostly share a tile) and each run's last
+// lane issues one atomic.
+__device__ __forceinline__ void add_excess_wave(uint8_t *ws, const Layout &L, uint32_t p, uint32_t x)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t key = x ? p / SCAN_TILE : 0xFFFFFFFFu;
+    const uint32_t prev = __shfl_up(key, 1, 64);
+    const uint64_t heads = __ballot(lane == 0 || prev != key);
+    const uint32_t hpos = 63u - (uint32_t)__clzll((unsigned long long)(heads & ((2ull << lane) - 1ull)));
+    uint32_t v = x;
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(v, d, 64);
+        if (lane >= hpos + d) v += y;
+    }
+    const bool tail = lane == 63 || ((heads >> (lane + 1)) & 1ull);
+    if (tail && key != 0xFFFFFFFFu && v) atomicAdd((uint32_t *)(ws + L.tilex) + key, v);
 }
 
 // kernel launchers (each in its own translation unit); all enqueue on `s` and return the launch

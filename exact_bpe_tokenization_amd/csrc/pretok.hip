@@ -13,7 +13,7 @@
 // o200k case rule backtracks) -- are carried right to left; each tile's carry comes from a summary
 // of the tiles after it.
 //
-// Kernels:  k_init     clear the control block and the look-back flags
+// Kernels:  k_init     clear the control block, the look-back flags and the tile token counters
 //           k_summary  per tile: the leftmost character that decides each backward flag (an
 //                      early-exit scan of the tile's first bytes; one wavefront per tile)
 //           k_pieces   per 8 KiB tile: UTF-8 decode + validation, categories, backward flags,
@@ -205,8 +205,8 @@ __global__ void k_init(uint8_t *ws, Layout L)
     uint32_t i = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
     uint32_t *ctrl = (uint32_t *)(ws + L.ctrl);
     for (uint32_t k = i; k < 64; k += stride) ctrl[k] = 0;
-    uint64_t *a = (uint64_t *)(ws + L.tflag_state), *b = (uint64_t *)(ws + L.tflag_cnt),
-             *c = (uint64_t *)(ws + L.sflag);
+    uint64_t *a = (uint64_t *)(ws + L.tflag_state), *b = (uint64_t *)(ws + L.tflag_cnt);
+    uint32_t *c = (uint32_t *)(ws + L.tilex);
     for (uint32_t k = i; k < L.n_tiles; k += stride) { a[k] = 0; b[k] = 0; }
     for (uint32_t k = i; k < L.n_scan_tiles; k += stride) c[k] = 0;
 }

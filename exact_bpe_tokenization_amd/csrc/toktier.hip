@@ -224,6 +224,7 @@ int build_whole_piece_tables(toktier_vocab *v, const uint32_t *merges, uint32_t 
     std::vector<uint32_t> ntok(npc), first(N);
     if (e == hipSuccess) e = hipMemcpy(dbytes, batch.data(), N, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(dws + L.ctrl, 0, sizeof(Ctrl));
+    if (e == hipSuccess) e = hipMemset(dws + L.tilex, 0, 4ull * L.n_scan_tiles);
     if (e == hipSuccess) e = hipMemcpy(dws + L.ctrl + offsetof(Ctrl, n_pieces), &npc, 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(dws + L.pstart, starts.data(), 4ull * starts.size(), hipMemcpyHostToDevice);
