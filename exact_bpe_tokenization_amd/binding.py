@@ -11,7 +11,8 @@ import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtoktier.so")
+# TOKTIER_LIBRARY may name another build of the same library (same exports), e.g. an instrumented one
+LIB_PATH = os.environ.get("TOKTIER_LIBRARY") or os.path.join(HERE, "libtoktier.so")
 
 TOKTIER_GPT2, TOKTIER_CL100K, TOKTIER_O200K = 1, 2, 3
 FAMILIES = {"gpt2": TOKTIER_GPT2, "cl100k": TOKTIER_CL100K, "o200k": TOKTIER_O200K}

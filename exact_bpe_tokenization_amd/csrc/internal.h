@@ -55,8 +55,8 @@ struct DevVocab {
     const uint32_t *r2;       // 65536 byte-pair ranks
     const uint64_t *slots;    // pair hash, 2^k slots, linear probing
     const uint32_t *merges;   // 2 * n_merges (left, right)
-    const uint64_t *fmap;     // NCTX transition maps
-    const uint32_t *fstart;   // NCTX start masks (bit s: a piece starts here when in state s)
+    const uint4 *fmap16;      // NCTX transition maps, one byte per state s (bytes 0..14):
+                              //   bits 0-3 the next state, bit 4 set when a piece starts here in s
     // whole-piece tables: pieces whose BPE result is one token (NULL while they are being built)
     const uint4 *wa;          // 2..7 bytes: {key lo, key hi, id, 0}, key = bytes | len << 56
     const uint4 *wb;          // 8..32 bytes: 3 x uint4 = {k0, k1}, {k2, k3}, {len, id, 0, 0}

@@ -60,13 +60,10 @@ enum : uint32_t { BK_KEEP = 0, BK_F = 2, BK_T = 3 };
 // AU  = "only uppercase letters from here to the end of this letter run" (true outside letters)
 __device__ __forceinline__ void backward_maps(uint32_t code, bool eof_next, uint32_t &na, uint32_t &au)
 {
-    uint32_t cat = code & 7u;
-    if (cat != CAT_W) na = BK_T;
-    else if (code & CC_CRLF) na = BK_F;
-    else na = eof_next ? BK_T : BK_KEEP;
-    if (cat == CAT_LU) au = eof_next ? BK_T : BK_KEEP;
-    else if (cat == CAT_LL || cat == CAT_LO || cat == CAT_M) au = BK_F;
-    else au = BK_T;
+    const uint32_t cat = code & 7u;
+    na = cat != CAT_W ? BK_T : ((code & CC_CRLF) ? BK_F : (eof_next ? BK_T : BK_KEEP));
+    const bool lower = cat == CAT_LL || cat == CAT_LO || cat == CAT_M;
+    au = cat == CAT_LU ? (eof_next ? BK_T : BK_KEEP) : (lower ? BK_F : BK_T);
 }
 
 __device__ __forceinline__ bool is_const_map(uint64_t m)
@@ -109,6 +106,57 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t x, int src)
 {
     uint32_t lo = __shfl((uint32_t)x, src, 64), hi = __shfl((uint32_t)(x >> 32), src, 64);
     return ((uint64_t)hi << 32) | lo;
+}
+
+// 16-byte transition maps: byte s (s < 15) is the image of state s in bits 0-3 (bit 4 is the
+// piece-start flag, ignored when composing); byte 15 is never selected.  Composition is a byte
+// gather done with v_perm: two 8-byte halves selected by the low 3 bits, then one of the two by bit 3.
+struct M16 {
+    uint32_t w[4];
+};
+
+__device__ __forceinline__ M16 m16_identity() { return M16{{0x03020100u, 0x07060504u, 0x0B0A0908u, 0x0F0E0D0Cu}}; }
+
+__device__ __forceinline__ uint32_t gather16(const M16 &b, uint32_t sel)
+{
+    const uint32_t s7 = sel & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(b.w[1], b.w[0], s7);
+    const uint32_t hi = __builtin_amdgcn_perm(b.w[3], b.w[2], s7);
+    return __builtin_amdgcn_perm(hi, lo, ((sel >> 1) & 0x04040404u) | 0x03020100u);
+}
+
+// apply a first, then b
+__device__ __forceinline__ M16 compose16(const M16 &a, const M16 &b)
+{
+    return M16{{gather16(b, a.w[0]), gather16(b, a.w[1]), gather16(b, a.w[2]), gather16(b, a.w[3])}};
+}
+
+__device__ __forceinline__ uint32_t byte16(const M16 &m, uint32_t s)
+{
+    const uint32_t q = s >> 2;
+    const uint32_t w = q == 0 ? m.w[0] : (q == 1 ? m.w[1] : (q == 2 ? m.w[2] : m.w[3]));
+    return (w >> (8u * (s & 3u))) & 255u;
+}
+
+__device__ __forceinline__ M16 shfl_up16(const M16 &m, int d)
+{
+    return M16{{(uint32_t)__shfl_up(m.w[0], d, 64), (uint32_t)__shfl_up(m.w[1], d, 64),
+                (uint32_t)__shfl_up(m.w[2], d, 64), (uint32_t)__shfl_up(m.w[3], d, 64)}};
+}
+
+__device__ __forceinline__ M16 shfl16(const M16 &m, int src)
+{
+    return M16{{(uint32_t)__shfl(m.w[0], src, 64), (uint32_t)__shfl(m.w[1], src, 64),
+                (uint32_t)__shfl(m.w[2], src, 64), (uint32_t)__shfl(m.w[3], src, 64)}};
+}
+
+// the 60-bit nibble form used by the tile look-back flags
+__device__ __forceinline__ uint64_t pack60(const M16 &m)
+{
+    uint64_t r = 0;
+#pragma unroll
+    for (int st = 0; st < NSTATES; ++st) r |= (uint64_t)(byte16(m, (uint32_t)st) & 15u) << (4 * st);
+    return r;
 }
 
 // Automaton state entering `tile`.  flags[t] = (1 << 60 | map of tile t) or (2 << 60 | state after
@@ -264,40 +312,108 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
     if (lane == 0) (ws + L.tbwd)[blockIdx.x] = (uint8_t)(na | (au << 2));
 }
 
+// The same per-byte code from registers: rw holds 24 bytes (4 before the thread's chunk, its 16, 4
+// after), dm bit i says a document starts at window byte i, and window byte i is position
+// p0 + i.  i is a compile-time index in the unrolled callers, so everything stays in registers.
+__device__ __forceinline__ uint32_t wbyte(const uint32_t (&rw)[6], int i)
+{
+    return (rw[i >> 2] >> (8 * (i & 3))) & 255u;
+}
+
+__device__ __forceinline__ uint32_t reg_byte_code(const uint32_t (&rw)[6], uint32_t dm, int i, uint64_t p, uint64_t n,
+                                                  int family, bool &bad)
+{
+    const uint32_t c = wbyte(rw, i);
+    const bool isdoc = (dm >> i) & 1u;
+    if ((c & 0xC0u) == 0x80u) {
+        // a continuation byte must be covered by a lead byte 1..3 bytes back in the same doc
+        bool ok = false, found = false;
+#pragma unroll
+        for (int back = 1; back <= 3; ++back) {
+            if (found || (int64_t)p - back < 0) { found = true; continue; }
+            const uint32_t lead = wbyte(rw, i - back);
+            if ((lead & 0xC0u) != 0x80u) {
+                ok = utf8_len(lead) > (uint32_t)back;
+                found = true;
+            }
+        }
+        bad |= !ok || isdoc;
+        return CAT_CONT;
+    }
+    const uint32_t len = utf8_len(c);
+    uint32_t cp = c;
+    bool ok = len != 0 && p + len <= n;
+    if (len > 1) {
+        cp = c & (0x7Fu >> len);
+#pragma unroll
+        for (int t = 1; t < 4; ++t) {
+            if ((uint32_t)t < len) {
+                const uint32_t cb = wbyte(rw, i + t);
+                ok &= ((cb & 0xC0u) == 0x80u) && !((dm >> (i + t)) & 1u);
+                cp = (cp << 6) | (cb & 0x3Fu);
+            }
+        }
+        ok &= !(len == 3 && cp < 0x800u) && !(len == 4 && (cp < 0x10000u || cp > 0x10FFFFu)) &&
+              !(cp >= 0xD800u && cp <= 0xDFFFu);
+    }
+    bad |= !ok;
+    if (!ok) cp = 0xFFFDu;
+    uint32_t code = ucat(cp) | (isdoc ? CC_DOC : 0u);
+    if (c == '\r' || c == '\n') code |= CC_CRLF;
+    if (c == ' ') code |= CC_SP;
+    if (c == '\'') {
+        auto letter = [&](int t) -> uint32_t {
+            if (p + t >= n || ((dm >> (i + t)) & 1u)) return 0;
+            uint32_t x = wbyte(rw, i + t);
+            if (family != 1 && x >= 'A' && x <= 'Z') x += 32;
+            return x;
+        };
+        const uint32_t x1 = letter(1), x2 = letter(2);
+        uint32_t lc = 0;
+        if (x1 == 's' || x1 == 't' || x1 == 'm' || x1 == 'd') lc = 1;
+        else if ((x1 == 'r' && x2 == 'e') || (x1 == 'v' && x2 == 'e') || (x1 == 'l' && x2 == 'l')) lc = 2;
+        code |= lc << CC_CONTR_SHIFT;
+    }
+    return code;
+}
+
 // ---------------------------------------------------------------------------------------------
 // k_pieces: dynamic tile ids; decode, automaton context, scans, look-backs, piece starts
 
-// self code of a character (13 values) from its byte code and its NA flag
+// self code of a character (13 values) from its byte code and its NA flag, without branches:
+// LU 0, LL 1, LO 2, N 3, M 4, other 5 (6, 7 with a one- or two-letter contraction after an
+// apostrophe), whitespace 8 + 2 (space) + 1 (NA), CR/LF 12
 __device__ __forceinline__ uint32_t self_code(uint32_t code, bool na)
 {
-    uint32_t cat = code & 7u;
-    switch (cat) {
-    case CAT_LU: return 0;
-    case CAT_LL: return 1;
-    case CAT_LO: return 2;
-    case CAT_N: return 3;
-    case CAT_M: return 4;
-    case CAT_O: {
-        uint32_t lc = (code >> CC_CONTR_SHIFT) & 3u;
-        return lc == 0 ? 5u : (lc == 1 ? 6u : 7u);
-    }
-    default:   // whitespace
-        if (code & CC_CRLF) return 12;
-        if (code & CC_SP) return na ? 11u : 10u;
-        return na ? 9u : 8u;
-    }
+    const uint32_t cat = code & 7u;
+    const uint32_t base = (0x05483210u >> (4u * cat)) & 15u;
+    const uint32_t other = base + ((code >> CC_CONTR_SHIFT) & 3u);
+    const uint32_t ws = (code & CC_CRLF) ? 12u : 8u + ((code & CC_SP) ? 2u : 0u) + (na ? 1u : 0u);
+    return cat == CAT_W ? ws : (cat == CAT_O ? other : base);
 }
 
+// next-character code: letter 0, N 1, W 2, M 3, other 4, end of document or batch 5
 __device__ __forceinline__ uint32_t next_code(uint32_t code)
 {
-    if (code == CC_EOF || (code & CC_DOC)) return 5;
-    switch (code & 7u) {
-    case CAT_LU: case CAT_LL: case CAT_LO: return 0;
-    case CAT_N: return 1;
-    case CAT_W: return 2;
-    case CAT_M: return 3;
-    default: return 4;
-    }
+    return (code & CC_DOC) ? 5u : (0x44321000u >> (4u * (code & 7u))) & 15u;   // CC_EOF has CC_DOC set
+}
+
+// contraction length code of an apostrophe at window index j of sraw (position p): 1 for 's 't 'm
+// 'd, 2 for 're 've 'll (ASCII; case-insensitive except for the GPT-2 family), else 0
+template <typename DocBit>
+__device__ __forceinline__ uint32_t contraction_code(const uint8_t *sraw, DocBit docbit, int j, uint64_t p, uint64_t n,
+                                                     int family)
+{
+    auto letter = [&](int t) -> uint32_t {
+        if (p + t >= n || docbit(j + t)) return 0;
+        uint32_t x = sraw[j + t];
+        if (family != 1 && x >= 'A' && x <= 'Z') x += 32;
+        return x;
+    };
+    const uint32_t x1 = letter(1), x2 = letter(2);
+    if (x1 == 's' || x1 == 't' || x1 == 'm' || x1 == 'd') return 1;
+    if ((x1 == 'r' && x2 == 'e') || (x1 == 'v' && x2 == 'e') || (x1 == 'l' && x2 == 'l')) return 2;
+    return 0;
 }
 
 __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes,
@@ -310,12 +426,12 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     __shared__ uint32_t sdoc[(SPAN + 31) / 32];
     __shared__ __align__(16) uint8_t scc[TILE + HALO];
     __shared__ uint16_t spiece[TILE];
-    __shared__ uint64_t smap[NCTX];
-    __shared__ uint32_t sstart[NCTX];
-    __shared__ uint32_t sbk[PRE_THREADS];
-    __shared__ uint64_t swmap[NW];
-    __shared__ uint32_t swcnt[NW];
-    __shared__ uint32_t s_tile, s_carry, s_entry, s_base, s_d0, s_d1;
+    __shared__ uint4 smap16[NCTX + 1];          // [NCTX]: identity (continuation bytes)
+    __shared__ uint8_t sasc[128];               // byte code of each ASCII character (no doc bit)
+    __shared__ uint32_t sbkw[NW];
+    __shared__ uint4 swmap[NW];
+    __shared__ uint32_t swcnt[NW], swstate[NW];
+    __shared__ uint32_t s_tile, s_carry, s_base, s_d0, s_d1;
 
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint8_t *tbwd = ws + L.tbwd;
@@ -325,7 +441,10 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
 
     if (tid == 0) s_tile = atomicAdd(&ctrl->tile_ctr_pre, 1u);
-    for (int i = tid; i < NCTX; i += PRE_THREADS) { smap[i] = v.fmap[i]; sstart[i] = v.fstart[i]; }
+    for (int i = tid; i < NCTX; i += PRE_THREADS) smap16[i] = v.fmap16[i];
+    if (tid == 0) smap16[NCTX] = make_uint4(0x03020100u, 0x07060504u, 0x0B0A0908u, 0x0F0E0D0Cu);
+    if (tid < 128)
+        sasc[tid] = (uint8_t)(ucat(tid) | ((tid == '\r' || tid == '\n') ? CC_CRLF : 0u) | (tid == ' ' ? CC_SP : 0u));
     for (int j = tid; j < (SPAN + 31) / 32; j += PRE_THREADS) sdoc[j] = 0;
     __syncthreads();
     const uint32_t tile = s_tile;
@@ -364,13 +483,45 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     const int c0 = tid * PRE_CHUNK;
     {
         bool bad = false;
+        // window: sraw[c0 .. c0 + 24) = positions lo + c0 - 4 ...; 16-byte aligned LDS reads
+        static_assert(RAW_LEAD == 4 && PRE_CHUNK == 16, "window layout");
+        const uint4 r0 = *(const uint4 *)(sraw + c0);
+        const uint2 r1 = *(const uint2 *)(sraw + c0 + 16);
+        const uint32_t rw[6] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y};
+        const uint32_t dw = (uint32_t)c0 >> 5;
+        const uint32_t dm = (uint32_t)((((uint64_t)sdoc[dw + 1] << 32) | sdoc[dw]) >> (c0 & 31));
         uint32_t w[PRE_CHUNK / 4] = {0, 0, 0, 0};
+        const uint32_t hibits = (rw[0] | rw[1] | rw[2] | rw[3] | rw[4] | rw[5]) & 0x80808080u;
+        if (__ballot(hibits != 0) == 0) {
+            // every byte the wavefront looks at is ASCII: a table lookup per byte, apostrophes apart
+            uint32_t apos = 0;
 #pragma unroll
-        for (int k = 0; k < PRE_CHUNK; ++k) {
-            const uint64_t p = lo + c0 + k;
-            const uint32_t code = p < n ? byte_code(sraw, docbit, RAW_LEAD + c0 + k, p, n, v.family, true, bad)
-                                        : (uint32_t)CC_EOF;
-            w[k >> 2] |= code << (8 * (k & 3));
+            for (int k = 0; k < PRE_CHUNK; ++k) {
+                const uint64_t p = lo + c0 + k;
+                const uint32_t c = wbyte(rw, k + RAW_LEAD);
+                const uint32_t code = (uint32_t)sasc[c] | (((dm >> (k + RAW_LEAD)) & 1u) ? CC_DOC : 0u);
+                apos |= (c == '\'' && p < n ? 1u : 0u) << k;
+                w[k >> 2] |= (p < n ? code : (uint32_t)CC_EOF) << (8 * (k & 3));
+            }
+            while (apos) {
+                const int k = __ffs(apos) - 1;
+                apos &= apos - 1;
+                const uint32_t lc = contraction_code(sraw, docbit, RAW_LEAD + c0 + k, lo + c0 + k, n, v.family);
+                const uint32_t add = lc << (CC_CONTR_SHIFT + 8 * (k & 3));
+                const int q = k >> 2;
+                w[0] |= q == 0 ? add : 0u;
+                w[1] |= q == 1 ? add : 0u;
+                w[2] |= q == 2 ? add : 0u;
+                w[3] |= q == 3 ? add : 0u;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < PRE_CHUNK; ++k) {
+                const uint64_t p = lo + c0 + k;
+                const uint32_t code =
+                    p < n ? reg_byte_code(rw, dm, k + RAW_LEAD, p, n, v.family, bad) : (uint32_t)CC_EOF;
+                w[k >> 2] |= code << (8 * (k & 3));
+            }
         }
         *(uint4 *)(scc + c0) = make_uint4(w[0], w[1], w[2], w[3]);
         if (tid < HALO) {
@@ -399,112 +550,124 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     }
     __syncthreads();
 
-    // per character: backward maps of this thread's chunk
-    uint32_t code[PRE_CHUNK + 4];
+    // per character, left to right: next-character class and backward maps (packed: 2 bits per
+    // character for each backward map, 4 bits for the next-character code)
+    uint32_t cw[5];
     {
         const uint4 a = *(const uint4 *)(scc + c0);
-        const uint32_t tail = *(const uint32_t *)(scc + c0 + PRE_CHUNK);
-        const uint32_t wv[5] = {a.x, a.y, a.z, a.w, tail};
-#pragma unroll
-        for (int k = 0; k < PRE_CHUNK + 4; ++k) code[k] = (wv[k >> 2] >> (8 * (k & 3))) & 255u;
+        cw[0] = a.x; cw[1] = a.y; cw[2] = a.z; cw[3] = a.w;
+        cw[4] = *(const uint32_t *)(scc + c0 + PRE_CHUNK);
     }
-    uint32_t eofn = 0, nxt_code[PRE_CHUNK];
-    uint32_t bna[PRE_CHUNK], bau[PRE_CHUNK];
+    auto code_at = [&](int k) -> uint32_t { return (cw[k >> 2] >> (8 * (k & 3))) & 255u; };
+    uint32_t pk_bna = 0, pk_bau = 0, pk_nx[2] = {0, 0};
     uint32_t agg = BK_KEEP | (BK_KEEP << 2);
 #pragma unroll
     for (int k = 0; k < PRE_CHUNK; ++k) {
         // next char: first non-continuation byte after k (within 4 bytes for valid UTF-8)
-        uint32_t nc = code[k + 1];
-        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code[k + 2];
-        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code[k + 3];
-        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code[k + 4];
-        nxt_code[k] = nc;
-        bool isch = code[k] != CC_EOF && (code[k] & 7u) != CAT_CONT;
-        bool en = nc == CC_EOF || (nc & CC_DOC) || (nc & 7u) == CAT_CONT;
-        uint32_t na = BK_KEEP, au = BK_KEEP;
-        if (isch) backward_maps(code[k], en, na, au);
-        bna[k] = na;
-        bau[k] = au;
-        eofn |= (en ? 1u : 0u) << k;
+        uint32_t nc = code_at(k + 1);
+        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code_at(k + 2);
+        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code_at(k + 3);
+        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code_at(k + 4);
+        const uint32_t ck = code_at(k);
+        const bool isch = ck != CC_EOF && (ck & 7u) != CAT_CONT;
+        const bool en = nc == CC_EOF || (nc & CC_DOC) || (nc & 7u) == CAT_CONT;
+        uint32_t na, au;
+        backward_maps(ck, en, na, au);
+        na = isch ? na : (uint32_t)BK_KEEP;   // continuation bytes pass the flags through
+        au = isch ? au : (uint32_t)BK_KEEP;
+        pk_bna |= na << (2 * k);
+        pk_bau |= au << (2 * k);
+        pk_nx[k >> 3] |= (en ? 5u : next_code(nc)) << (4 * (k & 7));
         if ((agg & 3u) == BK_KEEP) agg = (agg & ~3u) | na;
         if ((agg >> 2) == BK_KEEP) agg = (agg & 3u) | (au << 2);
     }
-    // suffix scan over threads: value entering each chunk from its right
-    sbk[tid] = agg;
-    __syncthreads();
-    for (int d = 1; d < PRE_THREADS; d <<= 1) {
-        uint32_t mine = sbk[tid], right = (tid + d < PRE_THREADS) ? sbk[tid + d] : (BK_KEEP | (BK_KEEP << 2));
-        __syncthreads();
-        uint32_t r = mine;
-        if ((r & 3u) == BK_KEEP) r = (r & ~3u) | (right & 3u);
-        if ((r >> 2) == BK_KEEP) r = (r & 3u) | (right & ~3u);
-        sbk[tid] = r;
-        __syncthreads();
+    // value entering each chunk from its right: the first chunk to the right whose flag is decided
+    // (suffix scan over the wavefront, then the wavefronts to the right, then the tile carry)
+    auto bk_comb = [](uint32_t x, uint32_t r) -> uint32_t {
+        if ((x & 3u) == BK_KEEP) x = (x & ~3u) | (r & 3u);
+        if ((x >> 2) == BK_KEEP) x = (x & 3u) | (r & ~3u);
+        return x;
+    };
+    uint32_t suf = agg;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_down(suf, d, 64);
+        if (lane + d < 64) suf = bk_comb(suf, y);
     }
-    uint32_t right = tid + 1 < PRE_THREADS ? sbk[tid + 1] : (BK_KEEP | (BK_KEEP << 2));
+    if (lane == 0) sbkw[wid] = suf;
+    const uint32_t suf1 = __shfl_down(suf, 1, 64);
+    __syncthreads();
+    uint32_t right = lane < 63 ? suf1 : (BK_KEEP | (BK_KEEP << 2));
+    for (uint32_t w = wid + 1; w < (uint32_t)NW; ++w) right = bk_comb(right, sbkw[w]);
     uint32_t na_val = ((right & 3u) == BK_KEEP) ? (s_carry & 1u) : (right & 1u);
     uint32_t au_val = ((right >> 2) == BK_KEEP) ? ((s_carry >> 1) & 1u) : ((right >> 2) & 1u);
 
-    // right to left: NA of each char, AU of the char after it; then the automaton context
-    uint64_t m_acc = MAP_IDENTITY;
-    uint32_t ctxs[PRE_CHUNK];
+    // right to left: NA of each char, AU of the char after it, the automaton context (packed 16 bits
+    // per character) and the chunk's map, composed from the right
+    uint32_t pk_ctx[PRE_CHUNK / 2] = {0, 0, 0, 0, 0, 0, 0, 0};
+    M16 acc = m16_identity();
 #pragma unroll
     for (int k = PRE_CHUNK - 1; k >= 0; --k) {
-        uint32_t au_next = au_val;                  // AU of the next character
-        if (bna[k] != BK_KEEP) na_val = bna[k] & 1u;
-        if (bau[k] != BK_KEEP) au_val = bau[k] & 1u;
-        bool isch = code[k] != CC_EOF && (code[k] & 7u) != CAT_CONT;
-        uint32_t ctx = 0xFFFFu;
-        if (isch) {
-            uint32_t self = self_code(code[k], na_val != 0);
-            uint32_t doc = (code[k] & CC_DOC) ? 1u : 0u;
-            uint32_t nx = ((eofn >> k) & 1u) ? 5u : next_code(nxt_code[k]);
-            ctx = ((self * 2u + doc) * NNEXT + nx) * 2u + au_next;
-        }
-        ctxs[k] = ctx;
+        const uint32_t au_next = au_val;            // AU of the next character
+        const uint32_t bn = (pk_bna >> (2 * k)) & 3u, bu = (pk_bau >> (2 * k)) & 3u;
+        if (bn != BK_KEEP) na_val = bn & 1u;
+        if (bu != BK_KEEP) au_val = bu & 1u;
+        const uint32_t ck = code_at(k);
+        const bool isch = ck != CC_EOF && (ck & 7u) != CAT_CONT;
+        const uint32_t self = self_code(ck, na_val != 0);
+        const uint32_t doc = (ck & CC_DOC) ? 1u : 0u;
+        const uint32_t nx = (pk_nx[k >> 3] >> (4 * (k & 7))) & 15u;
+        // identity map (NCTX) for continuation bytes and positions past the end
+        const uint32_t ctx = isch ? ((self * 2u + doc) * NNEXT + nx) * 2u + au_next : (uint32_t)NCTX;
+        pk_ctx[k >> 1] |= ctx << (16 * (k & 1));
+        const uint4 m = smap16[ctx];
+        acc = compose16(M16{{m.x, m.y, m.z, m.w}}, acc);
+        __builtin_amdgcn_sched_barrier(0);   // one map load in flight: keeps register use low
     }
-#pragma unroll
-    for (int k = 0; k < PRE_CHUNK; ++k)
-        if (ctxs[k] != 0xFFFFu) m_acc = compose(m_acc, smap[ctxs[k]]);
 
-    // workgroup scan of maps (exclusive per thread) and the tile's map
-    uint64_t incl = m_acc;
+    // wavefront scan of the chunk maps; the wavefronts' maps are scanned by wave 0, which also
+    // takes the state entering the tile from the look-back
+    M16 incl = acc;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        uint64_t y = shfl_up64(incl, d);
-        if (lane >= (uint32_t)d) incl = compose(y, incl);
+        const M16 y = shfl_up16(incl, d);
+        if (lane >= (uint32_t)d) incl = compose16(y, incl);
     }
-    if (lane == 63) swmap[wid] = incl;
-    uint64_t excl = shfl_up64(incl, 1);
-    if (lane == 0) excl = MAP_IDENTITY;
+    M16 excl = shfl_up16(incl, 1);
+    if (lane == 0) excl = m16_identity();
+    if (lane == 63) swmap[wid] = make_uint4(incl.w[0], incl.w[1], incl.w[2], incl.w[3]);
     __syncthreads();
-    uint64_t pre = MAP_IDENTITY, tile_map = MAP_IDENTITY;
-    for (uint32_t w = 0; w < (uint32_t)NW; ++w) {
-        if (w < wid) pre = compose(pre, swmap[w]);
-        tile_map = compose(tile_map, swmap[w]);
-    }
-    excl = compose(pre, excl);
-
-    // look-back #1: automaton state entering this tile
     if (wid == 0) {
-        if (lane == 0 && tile > 0) st_flag(tfs + tile, (1ull << 60) | tile_map);
-        const uint32_t entry = tile == 0 ? (uint32_t)S_ST : lookback_state(tfs, tile);
-        if (lane == 0) {
-            st_flag(tfs + tile, (2ull << 60) | apply_map(tile_map, entry));
-            s_entry = entry;
+        M16 wm = m16_identity();
+        if (lane < (uint32_t)NW) {
+            const uint4 t = swmap[lane];
+            wm = M16{{t.x, t.y, t.z, t.w}};
         }
+#pragma unroll
+        for (int d = 1; d < NW; d <<= 1) {
+            const M16 y = shfl_up16(wm, d);
+            if (lane >= (uint32_t)d) wm = compose16(y, wm);
+        }
+        M16 wex = shfl_up16(wm, 1);
+        if (lane == 0) wex = m16_identity();
+        const M16 tile_map = shfl16(wm, NW - 1);
+        // look-back #1: automaton state entering this tile
+        if (lane == 0 && tile > 0) st_flag(tfs + tile, (1ull << 60) | pack60(tile_map));
+        const uint32_t entry = tile == 0 ? (uint32_t)S_ST : lookback_state(tfs, tile);
+        if (lane == 0) st_flag(tfs + tile, (2ull << 60) | (byte16(tile_map, entry) & 15u));
+        if (lane < (uint32_t)NW) swstate[lane] = byte16(wex, entry) & 15u;
     }
     __syncthreads();
 
     // piece starts of this chunk
-    uint32_t s = apply_map(excl, s_entry), mask = 0;
+    uint32_t s = byte16(excl, swstate[wid]) & 15u, mask = 0;
+    const uint8_t *smb = (const uint8_t *)smap16;
 #pragma unroll
     for (int k = 0; k < PRE_CHUNK; ++k) {
-        uint32_t ctx = ctxs[k];
-        if (ctx != 0xFFFFu) {
-            mask |= ((sstart[ctx] >> s) & 1u) << k;
-            s = apply_map(smap[ctx], s);
-        }
+        const uint32_t ctx = (pk_ctx[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+        const uint32_t b = smb[ctx * 16u + s];
+        mask |= ((b >> 4) & 1u) << k;
+        s = b & 15u;
     }
     uint32_t cnt = __popc(mask), icnt = cnt;
 #pragma unroll

@@ -354,12 +354,16 @@ extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int
     uint64_t fmap[NCTX];
     uint32_t fstart[NCTX];
     build_tables(family, fmap, fstart);
+    uint8_t fmap16[NCTX][16];
+    for (int c = 0; c < NCTX; ++c) {
+        for (int st = 0; st < 16; ++st)
+            fmap16[c][st] = st < NSTATES ? (uint8_t)(((fmap[c] >> (4 * st)) & 15u) | (((fstart[c] >> st) & 1u) << 4)) : 0;
+    }
 
-    // one device allocation: r2 | slots | merges | fmap | fstart
+    // one device allocation: r2 | slots | merges | byte transition maps
     const uint64_t o_r2 = 0, o_slots = align256(65536 * 4), o_merges = o_slots + align256(cap * 8);
     const uint64_t o_fmap = o_merges + align256(8ull * n_merges + 8);
-    const uint64_t o_fstart = o_fmap + align256(8 * NCTX);
-    const uint64_t total = o_fstart + align256(4 * NCTX);
+    const uint64_t total = o_fmap + align256(sizeof(fmap16));
 
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
@@ -374,9 +378,8 @@ extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int
     hipError_t c2 = hipMemcpy(base + o_slots, slots.data(), cap * 8, hipMemcpyHostToDevice);
     hipError_t c3 = n_merges ? hipMemcpy(base + o_merges, merges, 8ull * n_merges, hipMemcpyHostToDevice)
                              : hipSuccess;
-    hipError_t c4 = hipMemcpy(base + o_fmap, fmap, sizeof(fmap), hipMemcpyHostToDevice);
-    hipError_t c5 = hipMemcpy(base + o_fstart, fstart, sizeof(fstart), hipMemcpyHostToDevice);
-    for (hipError_t ci : {c1, c2, c3, c4, c5})
+    hipError_t c4 = hipMemcpy(base + o_fmap, fmap16, sizeof(fmap16), hipMemcpyHostToDevice);
+    for (hipError_t ci : {c1, c2, c3, c4})
         if (ci != hipSuccess) {
             (void)hipFree(d);
             return hip_fail(ci);
@@ -393,8 +396,7 @@ extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int
     v->dv.r2 = (const uint32_t *)(base + o_r2);
     v->dv.slots = (const uint64_t *)(base + o_slots);
     v->dv.merges = (const uint32_t *)(base + o_merges);
-    v->dv.fmap = (const uint64_t *)(base + o_fmap);
-    v->dv.fstart = (const uint32_t *)(base + o_fstart);
+    v->dv.fmap16 = (const uint4 *)(base + o_fmap);
     v->dv.mask = (uint32_t)(cap - 1);
     v->dv.shift = shift;
     v->dv.n_merges = n_merges;
