@@ -34,7 +34,7 @@ extern "C" {
 typedef struct toktier_vocab toktier_vocab;   /* opaque; immutable after load */
 
 /* Pre-tokenizer rule families (paper: the GPT-2, cl100k and o200k pattern lineages; the exact
- * alternatives are listed in the library's design notes and implemented by the oracle). */
+ * alternatives are implemented by the oracle and summarized below). */
 enum {
     TOKTIER_GPT2 = 1,     /* contractions ('s 't 're 've 'm 'll 'd, lowercase), ' ?' + letters,
                              ' ?' + numbers, ' ?' + other, whitespace with lookahead */
