@@ -43,8 +43,8 @@ LATENCY = ("c1_ec4k", "c2_at100k", "c3_mix1m", "c5_adv4m4")
 # input bytes each kernel launch processes (the unit of the algorithmic-bytes figure)
 # (bytes of the pieces in the length range the launch serves)
 UNITS = {
-    "init": "all", "summary": "all", "pieces": "all", "bins": "all", "emit": "all", "gather_long": "binned",
-    "bpe_lookup": "lane", "bpe_lane": "le16", "bpe_seg32": "17to32", "bpe_seg64": "33to64",
+    "init": "all", "summary": "all", "pieces": "all", "route": "all", "emit": "all", "gather_long": "binned",
+    "bpe_lane": "le16", "bpe_seg32": "17to32", "bpe_seg64": "33to64",
     "bpe_wave": "wave", "bpe_block": "block", "bpe_giant": "giant",
 }
 

@@ -7,8 +7,8 @@
 // that pair equals iterated single merges (for rank-consistent merge lists, which the loader
 // enforces); only pairs next to a completed merge need a new lookup.
 //
-//   k_bpe_lookup every piece of <= 64 bytes: one probe of a whole-piece table resolves the pieces
-//                that encode to a single token; the rest are listed by length for
+//   (single-byte pieces and whole-piece table hits are resolved while pieces are formed; k_route does
+//   the same for pieces whose end the forming tile could not see; the rest arrive here as lists)
 //   k_bpe_lane   (<= 16 bytes) one lane per listed piece, sequence and ranks in registers; the
 //                textbook loop (leftmost lowest rank, merge, re-probe the two neighbours)
 //   k_bpe_seg    (17..32 and 33..64 bytes) 32 or 64 lanes per piece, one element per lane; rounds
@@ -18,8 +18,8 @@
 //                leftmost non-overlapping occurrences, prefix-sum compaction, neighbour re-probes
 //   k_bpe_giant  one 1024-lane workgroup per piece longer than that; the same rounds over device
 //                memory (double-buffered)
-// Every kernel writes the piece's IDs at scratch[piece start byte ...] (a piece never has more IDs
-// than bytes) and its ID count to ntok[piece].
+// Every kernel writes the piece's result word (a single ID, or the count of IDs it stored at
+// scratch[piece start byte ...]; a piece never has more IDs than bytes).
 #include "internal.h"
 
 namespace tt {
@@ -29,110 +29,76 @@ constexpr uint32_t PENDING = 0xFFFFFFFEu;
 // ---------------------------------------------------------------------------------------------
 // lane per piece
 
-// ---------------------------------------------------------------------------------------------
-// whole-piece lookup: a piece whose BPE result is a single token is found with one probe.  The
-// tables hold exactly the tokens t whose own byte string encodes to [t] (established at load time
-// by these same kernels), so a hit is the exact BPE result.
+// k_route: every piece.  Single bytes and whole-piece table hits get their result word here; the
+// others are listed for BPE by length.  Each workgroup owns a contiguous range of pieces and keeps
+// two pieces per thread in flight (their loads and table probes overlap).  List entries are queued
+// in LDS and flushed with one reservation atomic per list at the end (a full queue spills straight
+// to the global list).
+constexpr int RT_THREADS = 512;
+constexpr uint32_t RTQ[6] = {2048, 512, 256, 128, 64, 64};
+constexpr uint32_t RTQ_OFF[7] = {0, 2048, 2560, 2816, 2944, 3008, 3072};
 
-__device__ __forceinline__ bool whole_piece(const DevVocab &v, const uint8_t *__restrict__ src, uint32_t len,
-                                            uint32_t *id)
+__global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
+                                                      Layout L)
 {
-    if (len <= WA_MAX) {
-        if (!v.wa) return false;
-        uint64_t key = (uint64_t)len << 56;
-#pragma unroll
-        for (uint32_t k = 0; k < WA_MAX; ++k)
-            if (k < len) key |= (uint64_t)src[k] << (8 * k);
-        uint32_t h = (uint32_t)wa_hash(key, v.wa_shift);
-        for (;;) {
-            const uint4 sl = v.wa[h];
-            const uint64_t sk = (uint64_t)sl.x | ((uint64_t)sl.y << 32);
-            if (sk == key) { *id = sl.z; return true; }
-            if (sk == 0) return false;
-            h = (h + 1) & v.wa_mask;
-        }
-    }
-    if (!v.wb) return false;
-    uint64_t k4[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (uint32_t k = 0; k < (uint32_t)TABLE_MAX; ++k)
-        if (k < len) k4[k >> 3] |= (uint64_t)src[k] << (8 * (k & 7));
-    uint32_t h = (uint32_t)wb_hash(k4[0], k4[1], k4[2], k4[3], len, v.wb_shift);
-    for (;;) {
-        const uint4 c = v.wb[3 * h + 2];
-        if (c.x == 0) return false;
-        if (c.x == len) {
-            const uint4 a = v.wb[3 * h], b = v.wb[3 * h + 1];
-            if (((uint64_t)a.x | ((uint64_t)a.y << 32)) == k4[0] && ((uint64_t)a.z | ((uint64_t)a.w << 32)) == k4[1] &&
-                ((uint64_t)b.x | ((uint64_t)b.y << 32)) == k4[2] && ((uint64_t)b.z | ((uint64_t)b.w << 32)) == k4[3]) {
-                *id = c.y;
-                return true;
-            }
-        }
-        h = (h + 1) & v.wb_mask;
-    }
-}
-
-// Every piece of <= 64 bytes: single bytes and whole-piece hits are written directly; the rest are
-// queued in LDS by length (<= 16, 17..32, 33..64 bytes) and flushed to the three miss lists with one
-// reservation atomic per list per flush.  Each workgroup owns a contiguous range of pieces.
-constexpr int LK_THREADS = 256;
-constexpr int LK_Q = 2048;
-
-__global__ __launch_bounds__(LK_THREADS) void k_bpe_lookup(DevVocab v, const uint8_t *__restrict__ bytes,
-                                                           uint8_t *ws, Layout L)
-{
-    __shared__ uint32_t q[3][LK_Q];
-    __shared__ uint32_t scnt[3], sbase[3];
+    __shared__ uint32_t q[RTQ_OFF[6]];
+    __shared__ uint32_t qn[6], qbase[6];
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
-    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    uint32_t *ntok = (uint32_t *)(ws + L.ntok);
-    uint32_t *scratch = (uint32_t *)(ws + L.scratch);
-    uint32_t *lists[3] = {(uint32_t *)(ws + L.miss16), (uint32_t *)(ws + L.miss32), (uint32_t *)(ws + L.miss64)};
+    const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
+    uint32_t *__restrict__ pval = (uint32_t *)(ws + L.pval);
     const uint32_t np = ctrl->n_pieces;
     const uint32_t tid = threadIdx.x;
     const uint32_t chunk = (np + gridDim.x - 1) / gridDim.x;
-    const uint32_t start = blockIdx.x * chunk, end = min(np, start + chunk);
-    if (tid < 3) scnt[tid] = 0;
+    const uint64_t start64 = (uint64_t)blockIdx.x * chunk;
+    const uint32_t start = start64 < np ? (uint32_t)start64 : np;
+    const uint32_t end = min(np, start + chunk);
+    if (tid < 6) qn[tid] = 0;
     __syncthreads();
-    auto flush = [&](int l) {
-        // uniform: every thread calls this with the same l
-        if (tid == 0) sbase[l] = atomicAdd(&ctrl->miss_count[l], scnt[l]);
-        __syncthreads();
-        const uint32_t c = scnt[l], b = sbase[l];
-        for (uint32_t i = tid; i < c; i += LK_THREADS) lists[l][b + i] = q[l][i];
-        __syncthreads();
-        if (tid == 0) scnt[l] = 0;
-        __syncthreads();
+    auto list_piece = [&](uint32_t p, uint32_t len) {
+        const uint32_t r = route_of(len);
+        const uint32_t slot = atomicAdd(&qn[r], 1u);
+        if (slot < RTQ[r]) q[RTQ_OFF[r] + slot] = p;
+        else route_list(ws, L, r)[atomicAdd(route_count(ctrl, r), 1u)] = p;
     };
-    for (uint32_t p0 = start; p0 < end; p0 += LK_THREADS) {
-        const uint32_t p = p0 + tid;
-        if (p < end) {
-            const uint32_t b0 = pstart[p];
-            const uint32_t len = pstart[p + 1] - b0;
-            uint32_t id;
-            int miss = -1;
-            if (len == 1) {
-                scratch[b0] = bytes[b0];
-                ntok[p] = 1;
-            } else if (len <= (uint32_t)TABLE_MAX && whole_piece(v, bytes + b0, len, &id)) {
-                scratch[b0] = id;
-                ntok[p] = 1;
-            } else if (len <= (uint32_t)LANE_MAX) {
-                miss = len <= 16 ? 0 : (len <= 32 ? 1 : 2);
-            }
-            if (miss >= 0) q[miss][atomicAdd(&scnt[miss], 1u)] = p;
+    for (uint32_t p0 = start; p0 < end; p0 += 2 * RT_THREADS) {
+        const uint32_t pa = p0 + tid, pb = p0 + RT_THREADS + tid;
+        const bool va = pa < end, vb = pb < end;
+        const uint32_t a0 = va ? pstart[pa] : 0u, a1 = va ? pstart[pa + 1] : 0u;
+        const uint32_t b0 = vb ? pstart[pb] : 0u, b1 = vb ? pstart[pb + 1] : 0u;
+        const uint32_t la = a1 - a0, lb = b1 - b0;
+        WPQ qa = wp_make(v, bytes + a0, la), qb = wp_make(v, bytes + b0, lb);
+        uint32_t ida = va && la == 1 ? (uint32_t)bytes[a0] : 0u, idb = vb && lb == 1 ? (uint32_t)bytes[b0] : 0u;
+        uint32_t sa = qa.kind ? WP_MORE : (la == 1 ? WP_HIT : WP_MISS);
+        uint32_t sb = qb.kind ? WP_MORE : (lb == 1 ? WP_HIT : WP_MISS);
+        while (sa == WP_MORE || sb == WP_MORE) {
+            if (sa == WP_MORE) sa = wp_step(v, qa, &ida);
+            if (sb == WP_MORE) sb = wp_step(v, qb, &idb);
         }
-        __syncthreads();
-        for (int l = 0; l < 3; ++l)
-            if (scnt[l] > (uint32_t)(LK_Q - LK_THREADS)) flush(l);
+        if (va) {
+            if (sa == WP_HIT) pval[pa] = ida;
+            else list_piece(pa, la);
+        }
+        if (vb) {
+            if (sb == WP_HIT) pval[pb] = idb;
+            else list_piece(pb, lb);
+        }
     }
-    for (int l = 0; l < 3; ++l)
-        if (scnt[l]) flush(l);
+    __syncthreads();
+    if (tid < 6) {
+        const uint32_t c = min(qn[tid], RTQ[tid]);
+        qn[tid] = c;
+        if (c) qbase[tid] = atomicAdd(route_count(ctrl, tid), c);
+    }
+    __syncthreads();
+#pragma unroll
+    for (uint32_t r = 0; r < 6; ++r) {
+        uint32_t *dst = route_list(ws, L, r) + qbase[r];
+        for (uint32_t i = tid; i < qn[r]; i += RT_THREADS) dst[i] = q[RTQ_OFF[r] + i];
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
-// lane per piece (pieces the lookup did not resolve)
+// lane per piece (unresolved pieces of <= 16 bytes)
 
 template <int MAXL>
 __global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
@@ -140,7 +106,7 @@ __global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__r
 {
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    uint32_t *ntok = (uint32_t *)(ws + L.ntok);
+    uint32_t *pval = (uint32_t *)(ws + L.pval);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
     const uint32_t *list = (const uint32_t *)(ws + (which == 0 ? L.miss16 : (which == 1 ? L.miss32 : L.miss64)));
     const uint32_t count = ctrl->miss_count[which];
@@ -190,10 +156,12 @@ __global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__r
                 if ((uint32_t)j == pos) rk[j] = rr;
             }
         }
+        if (n > 1) {
 #pragma unroll
-        for (int k = 0; k < MAXL; ++k)
-            if ((uint32_t)k < n) scratch[b0 + k] = id[k];
-        if (active) ntok[p] = n;
+            for (int k = 0; k < MAXL; ++k)
+                if ((uint32_t)k < n) scratch[b0 + k] = id[k];
+        }
+        if (active) pval[p] = n == 1 ? id[0] : (PV_MULTI | n);
         add_excess_wave(ws, L, p, active ? n - 1 : 0u);
     }
 }
@@ -226,7 +194,7 @@ __global__ __launch_bounds__(256) void k_bpe_seg(DevVocab v, const uint8_t *__re
     constexpr uint64_t EVEN = 0x5555555555555555ull, ODD = ~EVEN;
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    uint32_t *ntok = (uint32_t *)(ws + L.ntok);
+    uint32_t *pval = (uint32_t *)(ws + L.pval);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
     const uint32_t *list = (const uint32_t *)(ws + (which == 0 ? L.miss16 : (which == 1 ? L.miss32 : L.miss64)));
     const uint32_t count = ctrl->miss_count[which];
@@ -270,9 +238,9 @@ __global__ __launch_bounds__(256) void k_bpe_seg(DevVocab v, const uint8_t *__re
             if (k >= n) rk = NO_RANK;
             else if (rk == PENDING) rk = k + 1 < n ? pair_rank(v, id, nx) : NO_RANK;
         }
-        if (k < n) scratch[b0 + k] = id;
+        if (k < n && n > 1) scratch[b0 + k] = id;
         const bool head = k == 0 && q < count;
-        if (head) ntok[p] = n;
+        if (head) pval[p] = n == 1 ? id : (PV_MULTI | n);
         add_excess_wave(ws, L, p, head ? n - 1 : 0u);
     }
 }
@@ -366,7 +334,7 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
 
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    uint32_t *ntok = (uint32_t *)(ws + L.ntok);
+    uint32_t *pval = (uint32_t *)(ws + L.pval);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
     const uint32_t *list = (const uint32_t *)(ws + (bin == 0 ? L.bin_wave : L.bin_block));
     const uint32_t count = ctrl->bin_count[bin];
@@ -452,7 +420,7 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
             n = nnew;
         }
         for (uint32_t k = tid; k < n; k += NT) scratch[b0 + k] = sid[k];
-        if (tid == 0) put_ntok(ws, L, p, n);
+        if (tid == 0) put_piece(ws, L, p, n, 0u, true);
         __syncthreads();
     }
 }
@@ -477,7 +445,7 @@ __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const u
     __shared__ int32_t s_last_cs;
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    uint32_t *ntok = (uint32_t *)(ws + L.ntok);
+    uint32_t *pval = (uint32_t *)(ws + L.pval);
     const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
     const uint32_t count = ctrl->bin_count[2];
     const uint32_t tid = threadIdx.x;
@@ -583,12 +551,21 @@ __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const u
         uint32_t *dst = (uint32_t *)(ws + L.scratch) + b0;
         if (idA != dst)
             for (uint32_t k = tid; k < n; k += NT) dst[k] = idA[k];
-        if (tid == 0) put_ntok(ws, L, p, n);
+        if (tid == 0) put_piece(ws, L, p, n, 0u, true);
         __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------------------------------------
+
+hipError_t launch_route(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev)
+{
+    if (b.n == 0) return hipGetLastError();
+    const uint64_t g = (b.n + 4095) / 4096;   // about 4 KiB of input (1-2K pieces) per workgroup, at most 1024
+    LaunchScope k(ev, 3, s);
+    hipLaunchKernelGGL(k_route, dim3(g > 1024 ? 1024u : (uint32_t)g), dim3(RT_THREADS), 0, s, v, b.bytes, b.ws, b.L);
+    return hipGetLastError();
+}
 
 hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev)
 {
@@ -597,37 +574,33 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     uint32_t g = (uint32_t)((b.n + 255) / 256);
     {
         LaunchScope k(ev, 4, s);
-        hipLaunchKernelGGL(k_bpe_lookup, dim3(g > 1024 ? 1024 : g), dim3(LK_THREADS), 0, s, v, b.bytes, b.ws, L);
-    }
-    {
-        LaunchScope k(ev, 5, s);
         hipLaunchKernelGGL((k_bpe_lane<16>), dim3(g > 2048 ? 2048 : g), dim3(256), 0, s, v, b.bytes, b.ws, L, 0);
     }
     // at most n / 17 pieces of 17..32 bytes (8 per workgroup), n / 33 of 33..64 (4 per workgroup)
     const uint64_t g32 = b.n / 17 / 8 + 1, g64 = b.n / 33 / 4 + 1;
     {
-        LaunchScope k(ev, 6, s);
+        LaunchScope k(ev, 5, s);
         hipLaunchKernelGGL((k_bpe_seg<32>), dim3(g32 > 2048 ? 2048 : (uint32_t)g32), dim3(256), 0, s, v, b.bytes,
                            b.ws, L, 1);
     }
     {
-        LaunchScope k(ev, 7, s);
+        LaunchScope k(ev, 6, s);
         hipLaunchKernelGGL((k_bpe_seg<64>), dim3(g64 > 1024 ? 1024 : (uint32_t)g64), dim3(256), 0, s, v, b.bytes,
                            b.ws, L, 2);
     }
     {
-        LaunchScope k(ev, 8, s);
+        LaunchScope k(ev, 7, s);
         uint32_t gw = L.cap_wave < 4096 ? L.cap_wave : 4096;
         hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
     }
     {
-        LaunchScope k(ev, 9, s);
+        LaunchScope k(ev, 8, s);
         uint32_t gb = L.cap_block < 1024 ? L.cap_block : 1024;
         hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v,
                            b.bytes, b.ws, L, 1);
     }
     {
-        LaunchScope k(ev, 10, s);
+        LaunchScope k(ev, 9, s);
         uint32_t gg = L.cap_giant < 256 ? L.cap_giant : 256;
         hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
     }

@@ -3,7 +3,7 @@
 // TokTier (arXiv 2607.29678), GPU full-tokenization paragraph: the complete path ends with output
 // compaction, and piece counts and output length stay in device memory (no host round trip between
 // kernels).  k_emit does it in one pass per tile of 4096 pieces: coalesced loads of the per-piece
-// token counts and starts, a workgroup scan, the tile's first token offset from the per-tile excess
+// result words, a workgroup scan, the tile's first token offset from the per-tile excess
 // counters the BPE kernels maintain (no look-back between tiles, no tile tickets), the gather of each
 // piece's IDs into out_ids (consecutive pieces write consecutive IDs), and the token offsets of the
 // documents whose first piece lies in the tile.  Pieces longer than a
@@ -22,7 +22,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
     __shared__ uint32_t swsum[NW], sxs[NW];
     __shared__ uint32_t s_dA, s_dB;
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
-    const uint32_t *__restrict__ ntok = (const uint32_t *)(ws + L.ntok);
+    const uint32_t *__restrict__ pval = (const uint32_t *)(ws + L.pval);
     const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *__restrict__ scratch = (const uint32_t *)(ws + L.scratch);
     const uint32_t *__restrict__ tilex = (const uint32_t *)(ws + L.tilex);
@@ -39,12 +39,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
     // wavefront wid owns pieces [wb, wb + 64 * IT) of the tile, 64 consecutive pieces per iteration
     // (lane-consecutive: coalesced loads and stores)
     const uint32_t wb = first + wid * (64u * IT);
-    uint32_t c[IT], st[IT], ex[IT];
+    uint32_t c[IT], pv[IT], ex[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const uint32_t i = wb + it * 64u + lane;
-        c[it] = i < end ? ntok[i] : 0u;
-        st[it] = i <= np ? pstart[i] : 0u;            // pstart[np] == n
+        pv[it] = i < end ? pval[i] : 0u;
+        c[it] = i >= end ? 0u : (pv[it] & PV_MULTI) ? (pv[it] & PV_COUNT) : 1u;
     }
     // tokens before this tile: one per piece plus the excess counted by the BPE kernels
     uint32_t xs = 0;
@@ -75,29 +75,22 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
     if (last && tid == 0) ctrl->n_tokens = tbase + total;
     const uint32_t obase = tbase + before;
 
-    // gather: piece i owns IDs [o, o + c) at scratch[its start byte ...]; first all loads, then all stores
-    uint32_t len[IT], v0[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const uint32_t i = wb + it * 64u + lane;
-        uint32_t nx = __shfl_down(st[it], 1, 64);
-        const uint32_t nx0 = __shfl(st[(it + 1) % IT], 0, 64);   // first start of the next iteration
-        if (lane == 63) nx = it + 1 < IT ? nx0 : (i + 1 <= np ? pstart[i + 1] : 0u);
-        len[it] = nx - st[it];
-        v0[it] = (i < end && len[it] <= (uint32_t)LANE_MAX) ? scratch[st[it]] : 0u;
-    }
+    // IDs: a single-token piece's ID is its result word (coalesced); a short multi-token piece's IDs
+    // are at scratch[its start byte ...]; a long piece gets its output offset for k_gather_long
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const uint32_t i = wb + it * 64u + lane;
         if (i >= end) continue;
-        const uint32_t o = obase + ex[it];
+        const uint32_t o = obase + ex[it], v = pv[it];
         soff[i - first] = o;
-        if (len[it] > (uint32_t)LANE_MAX) {
-            tokoff[i] = o;                              // binned piece: k_gather_long copies it
-            continue;
+        if (!(v & PV_MULTI)) {
+            out_ids[o] = v;
+        } else if (v & PV_LONG) {
+            tokoff[i] = o;
+        } else {
+            const uint32_t *src = scratch + pstart[i];
+            for (uint32_t j = 0; j < c[it]; ++j) out_ids[o + j] = src[j];
         }
-        out_ids[o] = v0[it];
-        for (uint32_t j = 1; j < c[it]; ++j) out_ids[o + j] = scratch[st[it] + j];
     }
     if (tid == 0) soff[end - first] = tbase + total;
 
@@ -121,7 +114,7 @@ __global__ __launch_bounds__(256) void k_gather_long(uint8_t *ws, Layout L, uint
 {
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    const uint32_t *ntok = (const uint32_t *)(ws + L.ntok);
+    const uint32_t *pval = (const uint32_t *)(ws + L.pval);
     const uint32_t *tokoff = (const uint32_t *)(ws + L.tokoff);
     const uint32_t *scratch = (const uint32_t *)(ws + L.scratch);
     const uint32_t c0 = ctrl->bin_count[0], c1 = ctrl->bin_count[1], c2 = ctrl->bin_count[2];
@@ -131,7 +124,7 @@ __global__ __launch_bounds__(256) void k_gather_long(uint8_t *ws, Layout L, uint
         const uint32_t p = q < c0 ? l0[q] : (q < c0 + c1 ? l1[q - c0] : l2[q - c0 - c1]);
         const uint32_t *src = scratch + pstart[p];
         uint32_t *dst = out_ids + tokoff[p];
-        const uint32_t c = ntok[p];
+        const uint32_t c = pval[p] & PV_COUNT;
         for (uint32_t j = threadIdx.x; j < c; j += blockDim.x) dst[j] = src[j];
     }
 }
@@ -150,12 +143,12 @@ hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offse
 {
     const Layout &L = b.L;
     {
-        LaunchScope k(ev, 11, s);
+        LaunchScope k(ev, 10, s);
         hipLaunchKernelGGL(k_emit, dim3(L.n_scan_tiles), dim3(SCAN_THREADS), 0, s, b.ws, L, b.offsets, b.n_docs,
                            b.n, out_ids, out_offsets);
     }
     if (b.n) {
-        LaunchScope k(ev, 12, s);
+        LaunchScope k(ev, 11, s);
         uint32_t gl = L.cap_wave < 2048 ? L.cap_wave : 2048;
         hipLaunchKernelGGL(k_gather_long, dim3(gl), dim3(256), 0, s, b.ws, L, out_ids);
     }

@@ -193,7 +193,7 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // ---------------------------------------------------------------------------------------------
 // workspace layout for n input bytes
 struct Layout {
-    uint64_t ctrl, cc, tbwd, tflag_state, tflag_cnt, pstart, ntok, tokoff, scratch, bin_wave,
+    uint64_t ctrl, cc, tbwd, tflag_state, tflag_cnt, pstart, pval, tokoff, scratch, bin_wave,
         bin_block, bin_giant, miss16, miss32, miss64, g_ids, g_rank_a, g_rank_b, tilex, total;
     uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant;
 };
@@ -216,7 +216,7 @@ inline Layout make_layout(uint64_t n)
     L.tflag_cnt = o;   o += align256(8ull * L.n_tiles);
     L.tilex = o;       o += align256(4ull * L.n_scan_tiles);
     L.pstart = o;      o += align256(4ull * (n + 2));
-    L.ntok = o;        o += align256(4ull * (n + 1));
+    L.pval = o;        o += align256(4ull * (n + 1));
     L.tokoff = o;      o += align256(4ull * (n + 2));
     L.scratch = o;     o += align256(4ull * (n + 1));
     L.bin_wave = o;    o += align256(4ull * L.cap_wave);
@@ -232,13 +232,144 @@ inline Layout make_layout(uint64_t n)
     return L;
 }
 
-// Token count n >= 1 of piece p.  The excess over one token is added to the counter of the piece's
-// output tile (SCAN_TILE consecutive pieces); the compaction kernel derives each tile's first output
-// position from those counters instead of a look-back across tiles.
-__device__ __forceinline__ void put_ntok(uint8_t *ws, const Layout &L, uint32_t p, uint32_t n)
+// whole-piece lookup: a piece whose BPE result is a single token is found with one probe.  The
+// tables hold exactly the tokens t whose own byte string encodes to [t] (established at load time
+// by these same kernels), so a hit is the exact BPE result.
+
+__device__ __forceinline__ bool whole_piece(const DevVocab &v, const uint8_t *__restrict__ src, uint32_t len,
+                                            uint32_t *id)
 {
-    ((uint32_t *)(ws + L.ntok))[p] = n;
+    if (len <= WA_MAX) {
+        if (!v.wa) return false;
+        uint64_t key = (uint64_t)len << 56;
+#pragma unroll
+        for (uint32_t k = 0; k < WA_MAX; ++k)
+            if (k < len) key |= (uint64_t)src[k] << (8 * k);
+        uint32_t h = (uint32_t)wa_hash(key, v.wa_shift);
+        for (;;) {
+            const uint4 sl = v.wa[h];
+            const uint64_t sk = (uint64_t)sl.x | ((uint64_t)sl.y << 32);
+            if (sk == key) { *id = sl.z; return true; }
+            if (sk == 0) return false;
+            h = (h + 1) & v.wa_mask;
+        }
+    }
+    if (!v.wb) return false;
+    uint64_t k4[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (uint32_t k = 0; k < (uint32_t)TABLE_MAX; ++k)
+        if (k < len) k4[k >> 3] |= (uint64_t)src[k] << (8 * (k & 7));
+    uint32_t h = (uint32_t)wb_hash(k4[0], k4[1], k4[2], k4[3], len, v.wb_shift);
+    for (;;) {
+        const uint4 c = v.wb[3 * h + 2];
+        if (c.x == 0) return false;
+        if (c.x == len) {
+            const uint4 a = v.wb[3 * h], b = v.wb[3 * h + 1];
+            if (((uint64_t)a.x | ((uint64_t)a.y << 32)) == k4[0] && ((uint64_t)a.z | ((uint64_t)a.w << 32)) == k4[1] &&
+                ((uint64_t)b.x | ((uint64_t)b.y << 32)) == k4[2] && ((uint64_t)b.z | ((uint64_t)b.w << 32)) == k4[3]) {
+                *id = c.y;
+                return true;
+            }
+        }
+        h = (h + 1) & v.wb_mask;
+    }
+}
+
+// The same lookup split into steps, so that a thread can keep the probes of two pieces in flight:
+// wp_make reads the piece's bytes and hashes them; each wp_step loads one slot and answers
+// WP_HIT (id set), WP_MISS, or WP_MORE (the next slot must be probed).
+enum : uint32_t { WP_MORE = 0, WP_HIT = 1, WP_MISS = 2 };
+struct WPQ {
+    uint64_t k0, k1, k2, k3;
+    uint32_t len, h, kind;   // kind 0: no table applies, 1: short table, 2: long table
+};
+
+__device__ __forceinline__ WPQ wp_make(const DevVocab &v, const uint8_t *__restrict__ src, uint32_t len)
+{
+    WPQ q{0, 0, 0, 0, len, 0, 0};
+    if (len < 2 || len > (uint32_t)TABLE_MAX) return q;
+    if (len <= WA_MAX) {
+        if (!v.wa) return q;
+        uint64_t key = (uint64_t)len << 56;
+#pragma unroll
+        for (uint32_t k = 0; k < WA_MAX; ++k)
+            if (k < len) key |= (uint64_t)src[k] << (8 * k);
+        q.k0 = key;
+        q.h = (uint32_t)wa_hash(key, v.wa_shift);
+        q.kind = 1;
+        return q;
+    }
+    if (!v.wb) return q;
+    uint64_t k4[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (uint32_t k = 0; k < (uint32_t)TABLE_MAX; ++k)
+        if (k < len) k4[k >> 3] |= (uint64_t)src[k] << (8 * (k & 7));
+    q.k0 = k4[0]; q.k1 = k4[1]; q.k2 = k4[2]; q.k3 = k4[3];
+    q.h = (uint32_t)wb_hash(k4[0], k4[1], k4[2], k4[3], len, v.wb_shift);
+    q.kind = 2;
+    return q;
+}
+
+__device__ __forceinline__ uint32_t wp_step(const DevVocab &v, WPQ &q, uint32_t *id)
+{
+    if (q.kind == 1) {
+        const uint4 sl = v.wa[q.h];
+        const uint64_t sk = (uint64_t)sl.x | ((uint64_t)sl.y << 32);
+        if (sk == q.k0) { *id = sl.z; return WP_HIT; }
+        if (sk == 0) return WP_MISS;
+        q.h = (q.h + 1) & v.wa_mask;
+        return WP_MORE;
+    }
+    if (q.kind == 2) {
+        const uint4 a = v.wb[3 * q.h], b = v.wb[3 * q.h + 1], c = v.wb[3 * q.h + 2];
+        if (c.x == 0) return WP_MISS;
+        if (c.x == q.len && ((uint64_t)a.x | ((uint64_t)a.y << 32)) == q.k0 &&
+            ((uint64_t)a.z | ((uint64_t)a.w << 32)) == q.k1 && ((uint64_t)b.x | ((uint64_t)b.y << 32)) == q.k2 &&
+            ((uint64_t)b.z | ((uint64_t)b.w << 32)) == q.k3) {
+            *id = c.y;
+            return WP_HIT;
+        }
+        q.h = (q.h + 1) & v.wb_mask;
+        return WP_MORE;
+    }
+    return WP_MISS;
+}
+
+// Per-piece result word (pval).  Bit 31 clear: the piece is one token and the word is its ID.  Bit 31
+// set: the piece has (word & PV_COUNT) tokens stored at scratch[piece start byte ...]; bit 30 also set
+// for pieces longer than 64 bytes, whose IDs are copied by a separate gather.
+constexpr uint32_t PV_MULTI = 1u << 31, PV_LONG = 1u << 30, PV_COUNT = PV_LONG - 1u;
+constexpr uint32_t NO_PIECE = 0xFFFFFFFFu;
+
+// Result of piece p: n >= 1 tokens, first ID id0 (the others already in scratch when n > 1).  The
+// excess over one token is added to the counter of the piece's output tile (SCAN_TILE consecutive
+// pieces); the compaction kernel derives each tile's first output position from those counters
+// instead of a look-back across tiles.
+__device__ __forceinline__ void put_piece(uint8_t *ws, const Layout &L, uint32_t p, uint32_t n, uint32_t id0,
+                                          bool is_long)
+{
+    ((uint32_t *)(ws + L.pval))[p] = (n == 1 && !is_long) ? id0 : (PV_MULTI | (is_long ? PV_LONG : 0u) | n);
     if (n > 1) atomicAdd((uint32_t *)(ws + L.tilex) + p / SCAN_TILE, n - 1);
+}
+
+// List a piece belongs to when it is not resolved directly: 0..2 BPE miss lists (<= 16, 17..32,
+// 33..64 bytes), 3..5 length bins (65..WAVE_MAX, ..BLOCK_MAX, longer).
+__device__ __forceinline__ uint32_t route_of(uint32_t len)
+{
+    return len <= 16u ? 0u : len <= 32u ? 1u : len <= (uint32_t)LANE_MAX ? 2u :
+           len <= (uint32_t)WAVE_MAX ? 3u : len <= (uint32_t)BLOCK_MAX ? 4u : 5u;
+}
+
+__device__ __forceinline__ uint32_t *route_list(uint8_t *ws, const Layout &L, uint32_t r)
+{
+    const uint64_t o = r == 0 ? L.miss16 : r == 1 ? L.miss32 : r == 2 ? L.miss64 :
+                       r == 3 ? L.bin_wave : r == 4 ? L.bin_block : L.bin_giant;
+    return (uint32_t *)(ws + o);
+}
+
+__device__ __forceinline__ uint32_t *route_count(Ctrl *ctrl, uint32_t r)
+{
+    return r < 3 ? &ctrl->miss_count[r] : &ctrl->bin_count[r - 3];
 }
 
 // Wavefront form of the same counter update, called by all 64 lanes: lane i contributes the
@@ -298,6 +429,6 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
 hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offsets, hipStream_t s,
                           const Events *ev);
 hipError_t launch_export_starts(const Batch &b, uint32_t *out_starts, hipStream_t s);
-hipError_t launch_bins(const Batch &b, hipStream_t s, const Events *ev);
+hipError_t launch_route(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
 
 }  // namespace tt

@@ -19,7 +19,6 @@
 //           k_pieces   per 8 KiB tile: UTF-8 decode + validation, categories, backward flags,
 //                      automaton scan, piece starts, piece numbering (one read of the input,
 //                      4 bytes written per piece)
-//           k_bins     piece lengths -> wave / block / giant lists
 #include "internal.h"
 
 #define TT_UCAT_QUAL static __device__ const
@@ -708,36 +707,7 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     __syncthreads();
     const uint32_t gbase = s_base;
     for (uint32_t i = tid; i < total; i += PRE_THREADS) pstart[gbase + i] = (uint32_t)(lo + spiece[i]);
-}
 
-// ---------------------------------------------------------------------------------------------
-// k_bins: pieces longer than a lane's limit go to the wave / block / giant lists
-
-__global__ __launch_bounds__(256) void k_bins(uint8_t *ws, Layout L)
-{
-    __shared__ uint32_t scnt[3], sbase[3];
-    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
-    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    uint32_t *lists[3] = {(uint32_t *)(ws + L.bin_wave), (uint32_t *)(ws + L.bin_block),
-                          (uint32_t *)(ws + L.bin_giant)};
-    const uint32_t np = ctrl->n_pieces;
-    const uint32_t tid = threadIdx.x;
-    for (uint32_t p0 = blockIdx.x * blockDim.x; p0 < np; p0 += gridDim.x * blockDim.x) {
-        if (tid < 3) scnt[tid] = 0;
-        __syncthreads();
-        const uint32_t p = p0 + tid;
-        int bin = -1;
-        if (p < np) {
-            uint32_t len = pstart[p + 1] - pstart[p];
-            bin = len <= LANE_MAX ? -1 : (len <= WAVE_MAX ? 0 : (len <= BLOCK_MAX ? 1 : 2));
-        }
-        const uint32_t local = bin >= 0 ? atomicAdd(&scnt[bin], 1u) : 0u;
-        __syncthreads();
-        if (tid < 3 && scnt[tid]) sbase[tid] = atomicAdd(&ctrl->bin_count[tid], scnt[tid]);
-        __syncthreads();
-        if (bin >= 0) lists[bin][sbase[bin] + local] = p;
-        __syncthreads();
-    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -759,16 +729,6 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
         hipLaunchKernelGGL(k_pieces, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs,
                            b.n, b.ws, L);
     }
-    return launch_bins(b, s, ev);
-}
-
-hipError_t launch_bins(const Batch &b, hipStream_t s, const Events *ev)
-{
-    uint32_t g = (uint32_t)((b.n + 255) / 256);
-    if (g > 2048) g = 2048;
-    if (g == 0) return hipGetLastError();
-    LaunchScope k(ev, 3, s);
-    hipLaunchKernelGGL(k_bins, dim3(g), dim3(256), 0, s, b.ws, b.L);
     return hipGetLastError();
 }
 

@@ -221,7 +221,7 @@ int build_whole_piece_tables(toktier_vocab *v, const uint32_t *merges, uint32_t 
     uint8_t *dbytes = nullptr, *dws = nullptr;
     hipError_t e = hipMalloc((void **)&dbytes, N);
     if (e == hipSuccess) e = hipMalloc((void **)&dws, L.total);
-    std::vector<uint32_t> ntok(npc), first(N);
+    std::vector<uint32_t> pv(npc);
     if (e == hipSuccess) e = hipMemcpy(dbytes, batch.data(), N, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(dws + L.ctrl, 0, sizeof(Ctrl));
     if (e == hipSuccess) e = hipMemset(dws + L.tilex, 0, 4ull * L.n_scan_tiles);
@@ -230,19 +230,18 @@ int build_whole_piece_tables(toktier_vocab *v, const uint32_t *merges, uint32_t 
         e = hipMemcpy(dws + L.pstart, starts.data(), 4ull * starts.size(), hipMemcpyHostToDevice);
     if (e == hipSuccess) {
         Batch b{dbytes, nullptr, 1, N, dws, L};
-        e = launch_bins(b, 0, nullptr);
+        e = launch_route(v->dv, b, 0, nullptr);
         if (e == hipSuccess) e = launch_bpe(v->dv, b, 0, nullptr);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(0);
-    if (e == hipSuccess) e = hipMemcpy(ntok.data(), dws + L.ntok, 4ull * npc, hipMemcpyDeviceToHost);
-    if (e == hipSuccess) e = hipMemcpy(first.data(), dws + L.scratch, 4ull * N, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(pv.data(), dws + L.pval, 4ull * npc, hipMemcpyDeviceToHost);
     if (dbytes) (void)hipFree(dbytes);
     if (dws) (void)hipFree(dws);
     if (e != hipSuccess) return hip_fail(e);
 
     std::vector<uint32_t> short_t, long_t;
     for (uint32_t i = 0; i < npc; ++i) {
-        if (ntok[i] != 1 || first[starts[i]] != cand[i]) continue;   // not self-reachable
+        if (pv[i] != cand[i]) continue;   // not self-reachable: BPE of its bytes is not [token]
         (len[cand[i]] <= WA_MAX ? short_t : long_t).push_back(cand[i]);
     }
     uint32_t la = 10, lb = 10;
@@ -500,6 +499,7 @@ int encode_impl(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *of
     if (ids_capacity < total_bytes) return TOKTIER_E_CAPACITY;
     hipStream_t s = (hipStream_t)stream;
     HIP_TRY(launch_pretokenize(v->dv, b, s, ev));
+    HIP_TRY(launch_route(v->dv, b, s, ev));
     HIP_TRY(launch_bpe(v->dv, b, s, ev));
     HIP_TRY(launch_compact(b, out_ids, out_offsets, s, ev));
     if (!out_n_tokens) return TOKTIER_OK;

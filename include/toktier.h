@@ -147,8 +147,7 @@ enum {
     TOKTIER_K_INIT = 0,       /* clear the control block and look-back flags                    */
     TOKTIER_K_SUMMARY,        /* per tile: the characters that decide the backward flags        */
     TOKTIER_K_PIECES,         /* UTF-8 decode + validation, automaton scan, piece starts        */
-    TOKTIER_K_BINS,           /* length bins for pieces longer than 64 bytes                    */
-    TOKTIER_K_BPE_LOOKUP,     /* whole-piece table probe of every piece of <= 64 bytes          */
+    TOKTIER_K_ROUTE,          /* every piece: single byte or whole-piece table hit, else BPE list */
     TOKTIER_K_BPE_LANE,       /* BPE, one lane per unresolved piece of <= 16 bytes              */
     TOKTIER_K_BPE_SEG32,      /* BPE, 32 lanes per unresolved piece of 17..32 bytes             */
     TOKTIER_K_BPE_SEG64,      /* BPE, one wavefront per unresolved piece of 33..64 bytes        */
