@@ -590,18 +590,18 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     }
     {
         LaunchScope k(ev, 7, s);
-        uint32_t gw = L.cap_wave < 4096 ? L.cap_wave : 4096;
+        uint32_t gw = L.cap_wave < 1024 ? L.cap_wave : 1024;
         hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
     }
     {
         LaunchScope k(ev, 8, s);
-        uint32_t gb = L.cap_block < 1024 ? L.cap_block : 1024;
+        uint32_t gb = L.cap_block < 256 ? L.cap_block : 256;
         hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v,
                            b.bytes, b.ws, L, 1);
     }
     {
         LaunchScope k(ev, 9, s);
-        uint32_t gg = L.cap_giant < 256 ? L.cap_giant : 256;
+        uint32_t gg = L.cap_giant < 64 ? L.cap_giant : 64;
         hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
     }
     return hipGetLastError();

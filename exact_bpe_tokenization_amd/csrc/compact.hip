@@ -76,21 +76,33 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
     const uint32_t obase = tbase + before;
 
     // IDs: a single-token piece's ID is its result word (coalesced); a short multi-token piece's IDs
-    // are at scratch[its start byte ...]; a long piece gets its output offset for k_gather_long
+    // are at scratch[its start byte ...]; a long piece gets its output offset for k_gather_long.
+    // The loads of every iteration are issued before any store.
+    uint32_t st[IT], f0[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const uint32_t i = wb + it * 64u + lane;
+        const bool multi = i < end && (pv[it] & (PV_MULTI | PV_LONG)) == PV_MULTI;
+        st[it] = multi ? pstart[i] : 0u;
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const uint32_t i = wb + it * 64u + lane;
+        const bool multi = i < end && (pv[it] & (PV_MULTI | PV_LONG)) == PV_MULTI;
+        f0[it] = multi ? scratch[st[it]] : pv[it];
+    }
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const uint32_t i = wb + it * 64u + lane;
         if (i >= end) continue;
         const uint32_t o = obase + ex[it], v = pv[it];
         soff[i - first] = o;
-        if (!(v & PV_MULTI)) {
-            out_ids[o] = v;
-        } else if (v & PV_LONG) {
+        if ((v & (PV_MULTI | PV_LONG)) == (PV_MULTI | PV_LONG)) {
             tokoff[i] = o;
-        } else {
-            const uint32_t *src = scratch + pstart[i];
-            for (uint32_t j = 0; j < c[it]; ++j) out_ids[o + j] = src[j];
+            continue;
         }
+        out_ids[o] = f0[it];
+        for (uint32_t j = 1; j < c[it]; ++j) out_ids[o + j] = scratch[st[it] + j];
     }
     if (tid == 0) soff[end - first] = tbase + total;
 
@@ -149,7 +161,7 @@ hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offse
     }
     if (b.n) {
         LaunchScope k(ev, 11, s);
-        uint32_t gl = L.cap_wave < 2048 ? L.cap_wave : 2048;
+        uint32_t gl = L.cap_wave < 512 ? L.cap_wave : 512;
         hipLaunchKernelGGL(k_gather_long, dim3(gl), dim3(256), 0, s, b.ws, L, out_ids);
     }
     return hipGetLastError();

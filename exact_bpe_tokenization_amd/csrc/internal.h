@@ -50,10 +50,11 @@ constexpr uint64_t NIBBLE_ONES = 0x0111111111111111ull;
 // merge tables.  Pair hash slot: bits 63..21 = (left << 21 | right), bits 20..0 = rank.
 constexpr uint32_t NO_RANK = 0xFFFFFFFFu;
 constexpr uint64_t EMPTY_SLOT = ~0ull;
+constexpr uint32_t PAIR_BUCKET_LOG2 = 3, PAIR_BUCKET = 1u << PAIR_BUCKET_LOG2;   // 8 slots = 64 bytes
 
 struct DevVocab {
     const uint32_t *r2;       // 65536 byte-pair ranks
-    const uint64_t *slots;    // pair hash, 2^k slots, linear probing
+    const uint64_t *slots;    // pair hash: buckets of 8 slots, a full bucket continues in the next
     const uint32_t *merges;   // 2 * n_merges (left, right)
     const uint4 *fmap16;      // NCTX transition maps, one byte per state s (bytes 0..14):
                               //   bits 0-3 the next state, bit 4 set when a piece starts here in s
@@ -162,16 +163,31 @@ __device__ __forceinline__ uint32_t wave_upper_bound(const T *a, uint32_t n, T x
     return wave_partition_point(a, n, [x](T v) { return v > x; });
 }
 
+// Rank of the pair (a, b), NO_RANK if it is not a merge.  Byte pairs come from the dense table;
+// other pairs from the bucketed hash: one 64-byte bucket per probe (four independent 16-byte
+// loads), usually a single round trip whether the pair is present or not.
 __device__ __forceinline__ uint32_t pair_rank(const DevVocab &v, uint32_t a, uint32_t b)
 {
     if ((a | b) < 256u) return __ldg(v.r2 + ((a << 8) | b));
-    uint64_t key = ((uint64_t)a << 21) | b;
-    uint32_t h = (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> v.shift);
+    const uint64_t key = ((uint64_t)a << 21) | b;
+    uint32_t bk = (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> v.shift);
     for (;;) {
-        uint64_t s = __ldg(v.slots + h);
-        if (s == EMPTY_SLOT) return NO_RANK;
-        if ((s >> 21) == key) return (uint32_t)(s & 0x1FFFFFu);
-        h = (h + 1) & v.mask;
+        const uint4 *q = (const uint4 *)(v.slots + (uint64_t)bk * PAIR_BUCKET);
+        const uint4 w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
+        const uint64_t sl[PAIR_BUCKET] = {
+            (uint64_t)w0.x | ((uint64_t)w0.y << 32), (uint64_t)w0.z | ((uint64_t)w0.w << 32),
+            (uint64_t)w1.x | ((uint64_t)w1.y << 32), (uint64_t)w1.z | ((uint64_t)w1.w << 32),
+            (uint64_t)w2.x | ((uint64_t)w2.y << 32), (uint64_t)w2.z | ((uint64_t)w2.w << 32),
+            (uint64_t)w3.x | ((uint64_t)w3.y << 32), (uint64_t)w3.z | ((uint64_t)w3.w << 32)};
+        uint32_t r = NO_RANK;
+        bool open = false;
+#pragma unroll
+        for (int j = 0; j < PAIR_BUCKET; ++j) {
+            if ((sl[j] >> 21) == key) r = (uint32_t)(sl[j] & 0x1FFFFFu);
+            open |= sl[j] == EMPTY_SLOT;
+        }
+        if (r != NO_RANK || open) return r;
+        bk = (bk + 1) & v.mask;
     }
 }
 

@@ -334,20 +334,24 @@ extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int
             ++n_general;
         }
     }
+    // pair hash: buckets of PAIR_BUCKET slots (one 64-byte line), filled in slot order; a full
+    // bucket continues in the next one.  At most half the slots are used.
     uint32_t log2cap = 10;
     while ((1ull << log2cap) < 2ull * n_general) ++log2cap;
-    const uint64_t cap = 1ull << log2cap;
+    const uint64_t cap = 1ull << log2cap, nbuckets = cap / PAIR_BUCKET;
     std::vector<uint64_t> slots(cap, EMPTY_SLOT);
-    const uint32_t shift = 64 - log2cap;
+    const uint32_t shift = 64 - (log2cap - PAIR_BUCKET_LOG2);
     for (uint32_t r = 0; r < n_merges; ++r) {
         uint32_t a = merges[2 * r], b = merges[2 * r + 1];
         if ((a | b) < 256u) continue;
         uint64_t key = ((uint64_t)a << 21) | b;
-        uint64_t h = (key * 0x9E3779B97F4A7C15ull) >> shift;
-        for (;;) {
-            if (slots[h] == EMPTY_SLOT) { slots[h] = (key << 21) | r; break; }
-            if ((slots[h] >> 21) == key) return TOKTIER_E_BAD_MERGES;      // duplicate pair
-            h = (h + 1) & (cap - 1);
+        uint64_t bk = (key * 0x9E3779B97F4A7C15ull) >> shift;
+        for (bool placed = false; !placed; bk = (bk + 1) & (nbuckets - 1)) {
+            for (uint32_t j = 0; j < PAIR_BUCKET; ++j) {
+                uint64_t &sl = slots[bk * PAIR_BUCKET + j];
+                if (sl == EMPTY_SLOT) { sl = (key << 21) | r; placed = true; break; }
+                if ((sl >> 21) == key) return TOKTIER_E_BAD_MERGES;      // duplicate pair
+            }
         }
     }
     uint64_t fmap[NCTX];
@@ -396,7 +400,7 @@ extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int
     v->dv.slots = (const uint64_t *)(base + o_slots);
     v->dv.merges = (const uint32_t *)(base + o_merges);
     v->dv.fmap16 = (const uint4 *)(base + o_fmap);
-    v->dv.mask = (uint32_t)(cap - 1);
+    v->dv.mask = (uint32_t)(nbuckets - 1);
     v->dv.shift = shift;
     v->dv.n_merges = n_merges;
     v->dv.family = family;
