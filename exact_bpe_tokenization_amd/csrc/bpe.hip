@@ -338,13 +338,25 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
     const uint32_t *list = (const uint32_t *)(ws + (bin == 0 ? L.bin_wave : L.bin_block));
     const uint32_t count = ctrl->bin_count[bin];
+    // the block bin also takes the chunks of giant pieces that fit (their results go to ccount)
+    const uint32_t n_chunks = bin == 1 ? ctrl->n_chunks : 0u;
+    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
+    uint32_t *ccount = (uint32_t *)(ws + L.ccount);
     const uint32_t tid = threadIdx.x;
     const uint32_t k0 = tid * E;
 
-    for (uint32_t q = blockIdx.x; q < count; q += gridDim.x) {
-        const uint32_t p = list[q];
-        const uint32_t b0 = pstart[p];
-        uint32_t n = pstart[p + 1] - b0;
+    for (uint32_t q = blockIdx.x; q < count + n_chunks; q += gridDim.x) {
+        const bool is_chunk = q >= count;
+        uint32_t p = 0, b0, n;
+        if (!is_chunk) {
+            p = list[q];
+            b0 = pstart[p];
+            n = pstart[p + 1] - b0;
+        } else {
+            b0 = cstart[q - count];
+            n = clen[q - count];
+            if (n == 0 || n > (uint32_t)MAXN) continue;   // unused slot, or a chunk for the giant kernel
+        }
         for (uint32_t k = tid; k < n; k += NT) sid[k] = bytes[b0 + k];
         __syncthreads();
         for (uint32_t k = tid; k < n; k += NT)
@@ -420,7 +432,164 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
             n = nnew;
         }
         for (uint32_t k = tid; k < n; k += NT) scratch[b0 + k] = sid[k];
-        if (tid == 0) put_piece(ws, L, p, n, 0u, true);
+        if (tid == 0) {
+            if (is_chunk) ccount[q - count] = n;
+            else put_piece(ws, L, p, n, 0u, true);
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// giant pieces: seams no merge can cross.  A merge that would join bytes on both sides of position
+// j joins a token x ending at j with a token y starting at j, so if no pair (x, y) of such tokens
+// has a rank, BPE never merges across j and the piece's IDs are those of its two sides encoded on
+// their own, concatenated (merges on one side never change the tokens on the other).  Every token
+// whose byte string is a suffix (prefix) of the text before (after) j is found through the token
+// string hash, duplicates included; a candidate with more than SEAM_MAXT of either is rejected.
+
+constexpr int SEAM_MAXT = 8;
+
+// calls f(id) for every token whose byte string equals s[0, len); the table key was computed by the
+// caller as str_key(H(s), len)
+template <typename F>
+__device__ __forceinline__ void str_find(const DevVocab &v, const uint8_t *s, uint32_t len, uint64_t key, F f)
+{
+    uint32_t i = (uint32_t)str_slot(key, v.str_shift);
+    for (;;) {
+        const uint4 e = v.str[i];
+        if (e.w == 0) return;
+        if (e.w == len && ((uint64_t)e.x | ((uint64_t)e.y << 32)) == key) {
+            const uint8_t *t = v.tok_bytes + v.tok_off[e.z];
+            bool eq = true;
+            for (uint32_t k = 0; k < len && eq; ++k) eq = t[k] == s[k];
+            if (eq) f(e.z);
+        }
+        i = (i + 1) & v.str_mask;
+    }
+}
+
+// may the piece s[0, n) be cut before byte j (0 < j < n)?
+__device__ bool seam_safe(const DevVocab &v, const uint8_t *s, uint32_t n, uint32_t j)
+{
+    uint32_t xs[SEAM_MAXT], ys[SEAM_MAXT];
+    uint32_t nx = 0, ny = 0;
+    bool over = false;
+    uint64_t h = 0, pw = 1;
+    const uint32_t lx = min(v.lmax, j), ly = min(v.lmax, n - j);
+    for (uint32_t l = 1; l <= lx && !over; ++l) {
+        h += (uint64_t)s[j - l] * pw;
+        pw *= STR_P;
+        str_find(v, s + j - l, l, str_key(h, l), [&](uint32_t id) {
+            if (nx < (uint32_t)SEAM_MAXT) xs[nx++] = id;
+            else over = true;
+        });
+    }
+    h = 0;
+    for (uint32_t l = 1; l <= ly && !over; ++l) {
+        h = h * STR_P + s[j + l - 1];
+        str_find(v, s + j, l, str_key(h, l), [&](uint32_t id) {
+            if (ny < (uint32_t)SEAM_MAXT) ys[ny++] = id;
+            else over = true;
+        });
+    }
+    if (over) return false;
+    for (uint32_t a = 0; a < nx; ++a)
+        for (uint32_t b = 0; b < ny; ++b)
+            if (pair_rank(v, xs[a], ys[b]) != NO_RANK) return false;
+    return true;
+}
+
+// k_gseam: one workgroup per giant piece.  Candidate seams lie in windows [k GCH, k GCH + GW) of the
+// piece; each window contributes its first safe position.  The piece's chunks get consecutive slots
+// of the chunk table (start, length); slots reserved but not used keep length 0.
+__global__ __launch_bounds__(1024) void k_gseam(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws, Layout L)
+{
+    constexpr uint32_t NWB = 1024 / GW;   // windows per pass
+    __shared__ uint32_t sfirst[NWB];
+    __shared__ uint32_t s_c0, s_nc;
+    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
+    uint32_t *cstart = (uint32_t *)(ws + L.cstart), *clen = (uint32_t *)(ws + L.clen);
+    uint32_t *gc0 = (uint32_t *)(ws + L.gc0), *gnc = (uint32_t *)(ws + L.gnc);
+    const uint32_t count = ctrl->bin_count[2];
+    const uint32_t tid = threadIdx.x;
+    for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
+        const uint32_t p = list[g];
+        const uint32_t b0 = pstart[p], n = pstart[p + 1] - b0;
+        const uint32_t nwin = (v.str && n > 2 * GCH) ? (n - GCH) / GCH : 0u;
+        if (tid == 0) {
+            s_c0 = atomicAdd(&ctrl->n_chunks, nwin + 1);
+            cstart[s_c0] = b0;
+            s_nc = 1;
+        }
+        __syncthreads();
+        const uint32_t c0 = s_c0;
+        for (uint32_t w0 = 0; w0 < nwin; w0 += NWB) {
+            if (tid < NWB) sfirst[tid] = GW;
+            __syncthreads();
+            const uint32_t w = w0 + tid / GW, d = tid % GW;
+            if (w < nwin && seam_safe(v, bytes + b0, n, (w + 1) * GCH + d)) atomicMin(&sfirst[tid / GW], d);
+            __syncthreads();
+            if (tid == 0) {
+                uint32_t nc = s_nc;
+                for (uint32_t k = 0; k < NWB && w0 + k < nwin; ++k)
+                    if (sfirst[k] < GW) cstart[c0 + nc++] = b0 + (w0 + k + 1) * GCH + sfirst[k];
+                s_nc = nc;
+            }
+            __syncthreads();
+        }
+        const uint32_t nc = s_nc;
+        for (uint32_t i = tid; i <= nwin; i += blockDim.x)
+            clen[c0 + i] = i < nc ? (i + 1 < nc ? cstart[c0 + i + 1] : b0 + n) - cstart[c0 + i] : 0u;
+        if (tid == 0) {
+            gc0[g] = c0;
+            gnc[g] = nc;
+        }
+        __syncthreads();
+    }
+}
+
+// k_gassemble: one workgroup per giant piece; moves the chunks' IDs next to each other at the piece's
+// start (each chunk moves left or stays; a segment is read completely before it is written) and
+// records the piece's token count
+__global__ __launch_bounds__(1024) void k_gassemble(uint8_t *ws, Layout L)
+{
+    constexpr uint32_t NT = 1024, PER = 4;
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
+    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *ccount = (const uint32_t *)(ws + L.ccount);
+    const uint32_t *gc0 = (const uint32_t *)(ws + L.gc0), *gnc = (const uint32_t *)(ws + L.gnc);
+    uint32_t *scratch = (uint32_t *)(ws + L.scratch);
+    const uint32_t count = ctrl->bin_count[2];
+    const uint32_t tid = threadIdx.x;
+    for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
+        const uint32_t p = list[g], b0 = pstart[p], c0 = gc0[g], nc = gnc[g];
+        uint32_t acc = 0;
+        for (uint32_t i = 0; i < nc; ++i) {
+            const uint32_t cs = cstart[c0 + i], cnt = ccount[c0 + i];
+            if (cs != b0 + acc) {
+                for (uint32_t s0 = 0; s0 < cnt; s0 += NT * PER) {
+                    uint32_t x[PER];
+#pragma unroll
+                    for (uint32_t k = 0; k < PER; ++k) {
+                        const uint32_t j = s0 + k * NT + tid;
+                        x[k] = j < cnt ? scratch[cs + j] : 0u;
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (uint32_t k = 0; k < PER; ++k) {
+                        const uint32_t j = s0 + k * NT + tid;
+                        if (j < cnt) scratch[b0 + acc + j] = x[k];
+                    }
+                    __syncthreads();
+                }
+            }
+            acc += cnt;
+        }
+        if (tid == 0) put_piece(ws, L, p, acc, 0u, true);
         __syncthreads();
     }
 }
@@ -446,15 +615,16 @@ __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const u
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *pval = (uint32_t *)(ws + L.pval);
-    const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
-    const uint32_t count = ctrl->bin_count[2];
+    const uint32_t count = ctrl->n_chunks;
+    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
+    uint32_t *ccount = (uint32_t *)(ws + L.ccount);
     const uint32_t tid = threadIdx.x;
     const uint32_t i0 = tid * GE;
 
     for (uint32_t q = blockIdx.x; q < count; q += gridDim.x) {
-        const uint32_t p = list[q];
-        const uint32_t b0 = pstart[p];
-        uint32_t n = pstart[p + 1] - b0;
+        const uint32_t b0 = cstart[q];
+        uint32_t n = clen[q];
+        if (n <= (uint32_t)BLOCK_MAX) continue;   // unused slot, or a chunk for the workgroup kernel
         uint32_t *idA = (uint32_t *)(ws + L.scratch) + b0, *idB = (uint32_t *)(ws + L.g_ids) + b0;
         uint32_t *rkA = (uint32_t *)(ws + L.g_rank_a) + b0, *rkB = (uint32_t *)(ws + L.g_rank_b) + b0;
         for (uint32_t k = tid; k < n; k += NT) idA[k] = bytes[b0 + k];
@@ -551,7 +721,7 @@ __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const u
         uint32_t *dst = (uint32_t *)(ws + L.scratch) + b0;
         if (idA != dst)
             for (uint32_t k = tid; k < n; k += NT) dst[k] = idA[k];
-        if (tid == 0) put_piece(ws, L, p, n, 0u, true);
+        if (tid == 0) ccount[q] = n;
         __syncthreads();
     }
 }
@@ -593,16 +763,24 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
         uint32_t gw = L.cap_wave < 1024 ? L.cap_wave : 1024;
         hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
     }
+    const uint32_t gg = L.cap_giant < 64 ? L.cap_giant : 64;
     {
         LaunchScope k(ev, 8, s);
-        uint32_t gb = L.cap_block < 256 ? L.cap_block : 256;
+        hipLaunchKernelGGL(k_gseam, dim3(gg), dim3(1024), 0, s, v, b.bytes, b.ws, L);
+    }
+    {
+        LaunchScope k(ev, 9, s);
+        uint32_t gb = L.cap_block + L.cap_chunks < 256 ? L.cap_block + L.cap_chunks : 256;
         hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v,
                            b.bytes, b.ws, L, 1);
     }
     {
-        LaunchScope k(ev, 9, s);
-        uint32_t gg = L.cap_giant < 64 ? L.cap_giant : 64;
+        LaunchScope k(ev, 10, s);
         hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
+    }
+    {
+        LaunchScope k(ev, 11, s);
+        hipLaunchKernelGGL(k_gassemble, dim3(gg), dim3(1024), 0, s, b.ws, L);
     }
     return hipGetLastError();
 }

@@ -18,6 +18,10 @@ constexpr int SCAN_THREADS = 256;
 constexpr int SCAN_PER_THREAD = 16;
 constexpr int SCAN_TILE = SCAN_THREADS * SCAN_PER_THREAD;
 
+// giant pieces are cut into chunks of about GCH bytes at seams that no merge can cross, searched
+// in a window of GW positions after each multiple of GCH
+constexpr uint32_t GCH = 2048, GW = 64;
+
 // BPE length bins (piece bytes): lane <= LANE_MAX < wave <= WAVE_MAX < block <= BLOCK_MAX < giant
 constexpr int LANE_MAX = 64;      // lane kernels: <= 16, 17..32 and 33..64 bytes
 constexpr int TABLE_MAX = 32;     // whole-piece tables hold pieces of 2..32 bytes
@@ -61,12 +65,31 @@ struct DevVocab {
     // whole-piece tables: pieces whose BPE result is one token (NULL while they are being built)
     const uint4 *wa;          // 2..7 bytes: {key lo, key hi, id, 0}, key = bytes | len << 56
     const uint4 *wb;          // 8..32 bytes: 3 x uint4 = {k0, k1}, {k2, k3}, {len, id, 0, 0}
+    // every token's byte string: bytes, offsets, and a hash from (string) to token ID, used to find
+    // seams no merge can cross in giant pieces (NULL when the longest token exceeds STR_LMAX bytes)
+    const uint8_t *tok_bytes;
+    const uint32_t *tok_off;  // 256 + n_merges + 1 offsets into tok_bytes
+    const uint4 *str;         // {key lo, key hi, id, len}; len 0 = empty slot
     uint32_t mask;
     uint32_t shift;
     uint32_t wa_mask, wa_shift, wb_mask, wb_shift;
+    uint32_t str_mask, str_shift, lmax;
     uint32_t n_merges;
     int family;
 };
+
+// token string hash: H(s) = sum s_i P^(len-1-i) mod 2^64, so H(s c) = H(s) P + c and
+// H(c s) = c P^len + H(s); the key mixes in the length
+constexpr uint64_t STR_P = 0x100000001B3ull;
+constexpr uint32_t STR_LMAX = 256;
+__host__ __device__ __forceinline__ uint64_t str_key(uint64_t h, uint32_t len)
+{
+    return h ^ ((uint64_t)len * 0x9E3779B97F4A7C15ull);
+}
+__host__ __device__ __forceinline__ uint64_t str_slot(uint64_t key, uint32_t shift)
+{
+    return (key * 0xD6E8FEB86659FD93ull) >> shift;
+}
 
 // whole-piece keys
 constexpr uint32_t WA_MAX = 7;
@@ -202,7 +225,8 @@ struct Ctrl {
     uint32_t n_tokens;
     uint32_t bin_count[3];     // wave, block, giant bins
     uint32_t miss_count[3];    // pieces left for lane BPE: <= 16, 17..32, 33..64 bytes
-    uint32_t pad[54];
+    uint32_t n_chunks;         // chunk slots reserved for giant pieces
+    uint32_t pad[53];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
@@ -210,8 +234,9 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // workspace layout for n input bytes
 struct Layout {
     uint64_t ctrl, cc, tbwd, tflag_state, tflag_cnt, pstart, pval, tokoff, scratch, bin_wave,
-        bin_block, bin_giant, miss16, miss32, miss64, g_ids, g_rank_a, g_rank_b, tilex, total;
-    uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant;
+        bin_block, bin_giant, miss16, miss32, miss64, g_ids, g_rank_a, g_rank_b, tilex, cstart, clen, ccount,
+        gc0, gnc, total;
+    uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant, cap_chunks;
 };
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
@@ -224,6 +249,7 @@ inline Layout make_layout(uint64_t n)
     L.cap_wave = (uint32_t)(n / (LANE_MAX + 1) + 1);
     L.cap_block = (uint32_t)(n / (WAVE_MAX + 1) + 1);
     L.cap_giant = (uint32_t)(n / (BLOCK_MAX + 1) + 1);
+    L.cap_chunks = (uint32_t)(n / (GCH - GW) + 2ull * L.cap_giant + 2);
     uint64_t o = 0;
     L.ctrl = o;        o += align256(sizeof(Ctrl));
     L.cc = o;
@@ -244,6 +270,11 @@ inline Layout make_layout(uint64_t n)
     L.g_ids = o;       o += align256(4ull * (n + 1));
     L.g_rank_a = o;    o += align256(4ull * (n + 1));
     L.g_rank_b = o;    o += align256(4ull * (n + 1));
+    L.cstart = o;      o += align256(4ull * L.cap_chunks);
+    L.clen = o;        o += align256(4ull * L.cap_chunks);
+    L.ccount = o;      o += align256(4ull * L.cap_chunks);
+    L.gc0 = o;         o += align256(4ull * L.cap_giant);
+    L.gnc = o;         o += align256(4ull * L.cap_giant);
     L.total = o;
     return L;
 }

@@ -7,6 +7,7 @@
 
 #include <string>
 #include <vector>
+#include <algorithm>
 
 #include "../../include/toktier.h"
 #include "internal.h"
@@ -20,6 +21,7 @@ struct toktier_vocab {
     uint32_t n_merges;
     void *dmem;     // pair tables, merges, automaton tables
     void *dwords;   // whole-piece tables (may be NULL)
+    void *dstr;     // token strings and their hash (may be NULL)
     DevVocab dv;
 };
 
@@ -186,25 +188,89 @@ void build_tables(int fam, uint64_t *fmap, uint32_t *fstart)
 
 namespace {
 
-int build_whole_piece_tables(toktier_vocab *v, const uint32_t *merges, uint32_t n_merges)
+// byte string of every token: len[t], off[t] into tb
+struct TokenStrings {
+    std::vector<uint32_t> len, off;
+    std::vector<uint8_t> tb;
+};
+
+int token_strings(const uint32_t *merges, uint32_t n_merges, TokenStrings &ts)
 {
     const uint32_t ntok_all = 256 + n_merges;
-    std::vector<uint32_t> len(ntok_all), off(ntok_all + 1);
+    ts.len.resize(ntok_all);
+    ts.off.resize(ntok_all + 1);
     uint64_t total = 0;
     for (uint32_t t = 0; t < ntok_all; ++t) {
-        len[t] = t < 256 ? 1u : len[merges[2 * (t - 256)]] + len[merges[2 * (t - 256) + 1]];
-        off[t] = (uint32_t)total;
-        total += len[t];
+        ts.len[t] = t < 256 ? 1u : ts.len[merges[2 * (t - 256)]] + ts.len[merges[2 * (t - 256) + 1]];
+        ts.off[t] = (uint32_t)total;
+        total += ts.len[t];
         if (total > 0xFFFFFFF0ull) return TOKTIER_E_BAD_MERGES;
     }
-    off[ntok_all] = (uint32_t)total;
-    std::vector<uint8_t> tb(total);
+    ts.off[ntok_all] = (uint32_t)total;
+    ts.tb.resize(total);
     for (uint32_t t = 0; t < ntok_all; ++t) {
-        if (t < 256) { tb[off[t]] = (uint8_t)t; continue; }
+        if (t < 256) { ts.tb[ts.off[t]] = (uint8_t)t; continue; }
         uint32_t a = merges[2 * (t - 256)], b = merges[2 * (t - 256) + 1];
-        memcpy(&tb[off[t]], &tb[off[a]], len[a]);
-        memcpy(&tb[off[t] + len[a]], &tb[off[b]], len[b]);
+        memcpy(&ts.tb[ts.off[t]], &ts.tb[ts.off[a]], ts.len[a]);
+        memcpy(&ts.tb[ts.off[t] + ts.len[a]], &ts.tb[ts.off[b]], ts.len[b]);
     }
+    return TOKTIER_OK;
+}
+
+// The token-string hash (every token, duplicates of one string included) and the strings, on the
+// device.  Skipped (pointers stay NULL) when some token is longer than STR_LMAX bytes.
+int build_string_table(toktier_vocab *v, const TokenStrings &ts)
+{
+    const uint32_t ntok_all = (uint32_t)ts.len.size();
+    uint32_t lmax = 0;
+    for (uint32_t t = 0; t < ntok_all; ++t) lmax = std::max(lmax, ts.len[t]);
+    if (lmax > STR_LMAX) return TOKTIER_OK;
+    uint32_t lc = 10;
+    while ((1ull << lc) < 2ull * ntok_all) ++lc;
+    const uint64_t cap = 1ull << lc;
+    std::vector<uint32_t> tab(4 * cap, 0);
+    for (uint32_t t = 0; t < ntok_all; ++t) {
+        uint64_t h = 0;
+        for (uint32_t k = 0; k < ts.len[t]; ++k) h = h * STR_P + ts.tb[ts.off[t] + k];
+        const uint64_t key = str_key(h, ts.len[t]);
+        uint64_t i = str_slot(key, 64 - lc);
+        while (tab[4 * i + 3]) i = (i + 1) & (cap - 1);
+        tab[4 * i] = (uint32_t)key;
+        tab[4 * i + 1] = (uint32_t)(key >> 32);
+        tab[4 * i + 2] = t;
+        tab[4 * i + 3] = ts.len[t];
+    }
+    const uint64_t o_tab = 0, o_off = align256(16 * cap), o_bytes = o_off + align256(4ull * (ntok_all + 1));
+    const uint64_t total = o_bytes + align256(ts.tb.size());
+    void *d = nullptr;
+    hipError_t e = hipMalloc(&d, total);
+    if (e != hipSuccess) {
+        hip_fail(e);
+        return TOKTIER_E_OOM;
+    }
+    uint8_t *base = (uint8_t *)d;
+    e = hipMemcpy(base + o_tab, tab.data(), 16 * cap, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(base + o_off, ts.off.data(), 4ull * (ntok_all + 1), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(base + o_bytes, ts.tb.data(), ts.tb.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return hip_fail(e);
+    }
+    v->dstr = d;
+    v->dv.str = (const uint4 *)(base + o_tab);
+    v->dv.tok_off = (const uint32_t *)(base + o_off);
+    v->dv.tok_bytes = base + o_bytes;
+    v->dv.str_mask = (uint32_t)(cap - 1);
+    v->dv.str_shift = 64 - lc;
+    v->dv.lmax = lmax;
+    return TOKTIER_OK;
+}
+
+int build_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts)
+{
+    const uint32_t ntok_all = (uint32_t)ts.len.size();
+    const std::vector<uint32_t> &len = ts.len, &off = ts.off;
+    const std::vector<uint8_t> &tb = ts.tb;
     std::vector<uint32_t> cand, starts;
     std::vector<uint8_t> batch;
     for (uint32_t t = 256; t < ntok_all; ++t) {
@@ -406,8 +472,16 @@ extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int
     v->dv.family = family;
     v->dv.wa = nullptr;
     v->dv.wb = nullptr;
-    int rc = build_whole_piece_tables(v, merges, n_merges);
+    v->dv.str = nullptr;
+    v->dv.tok_off = nullptr;
+    v->dv.tok_bytes = nullptr;
+    TokenStrings ts;
+    int rc = token_strings(merges, n_merges, ts);
+    if (rc == TOKTIER_OK) rc = build_string_table(v, ts);
+    if (rc == TOKTIER_OK) rc = build_whole_piece_tables(v, ts);
     if (rc != TOKTIER_OK) {
+        if (v->dwords) (void)hipFree(v->dwords);
+        if (v->dstr) (void)hipFree(v->dstr);
         (void)hipFree(v->dmem);
         free(v);
         return rc;
@@ -421,8 +495,9 @@ extern "C" int toktier_free_vocab(toktier_vocab *v)
     if (!v) return TOKTIER_OK;
     hipError_t e = hipDeviceSynchronize();
     hipError_t f = hipFree(v->dmem);
-    if (v->dwords) {
-        hipError_t g = hipFree(v->dwords);
+    for (void *extra : {v->dwords, v->dstr}) {
+        if (!extra) continue;
+        hipError_t g = hipFree(extra);
         if (f == hipSuccess) f = g;
     }
     free(v);

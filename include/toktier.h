@@ -152,8 +152,10 @@ enum {
     TOKTIER_K_BPE_SEG32,      /* BPE, 32 lanes per unresolved piece of 17..32 bytes             */
     TOKTIER_K_BPE_SEG64,      /* BPE, one wavefront per unresolved piece of 33..64 bytes        */
     TOKTIER_K_BPE_WAVE,       /* BPE, one wavefront per piece of 65..1024 bytes                 */
-    TOKTIER_K_BPE_BLOCK,      /* BPE, one workgroup per piece of 1025..4096 bytes               */
-    TOKTIER_K_BPE_GIANT,      /* BPE, one workgroup per longer piece, sequence in device memory */
+    TOKTIER_K_GIANT_SEAMS,    /* cut pieces > 4096 bytes into chunks at seams no merge crosses  */
+    TOKTIER_K_BPE_BLOCK,      /* BPE, one workgroup per piece of 1025..4096 bytes or chunk      */
+    TOKTIER_K_BPE_GIANT,      /* BPE, one workgroup per longer chunk, sequence in device memory */
+    TOKTIER_K_GIANT_JOIN,     /* concatenate each giant piece's chunk IDs                       */
     TOKTIER_K_EMIT,           /* token-offset scan, ID gather, per-document token offsets       */
     TOKTIER_K_GATHER_LONG,    /* ID gather of the binned (long) pieces                          */
     TOKTIER_K_COUNT

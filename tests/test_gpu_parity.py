@@ -142,6 +142,27 @@ def test_giant_pieces(tt):
     compare_ids(eids, eoo, ids, oo)
 
 
+@pytest.mark.parametrize("vocab", ["v1", "v3", "v4"])
+def test_giant_pieces_chunked(tt, vocab):
+    """Pieces longer than 4096 bytes are cut at seams no merge crosses and their chunks encoded in
+    parallel: random letter runs (many seams), a repeated letter run glued to random letters (the
+    run has none), random whitespace, and digits mixed with letters."""
+    tok, merges, fam = tokenizer(tt, vocab)
+    rng = np.random.default_rng({"v1": 21, "v3": 22, "v4": 23}[vocab])
+    az = "abcdefghijklmnopqrstuvwxyz"
+    strings = []
+    for n in (4097, 6000, 9001, 20000, 65537):
+        strings.append("".join(az[int(i)] for i in rng.integers(0, 26, n)))
+    strings.append("a" * 12000 + "".join(az[int(i)] for i in rng.integers(0, 26, 15000)))
+    strings.append("".join(" \t\r\n"[int(i)] for i in rng.integers(0, 4, 20000)) + "z")
+    strings.append("".join("Ab"[int(i)] for i in rng.integers(0, 2, 10000)))
+    data, offs = _batch(strings)
+    _say("giant chunked", vocab, data.size)
+    ids, oo = tok.encode(data.tobytes(), offs)
+    eids, eoo = oracle.encode_batch(fam, merges, data, offs)
+    compare_ids(eids, eoo, ids, oo)
+
+
 def test_history_independence(tt):
     tok, merges, fam = tokenizer(tt, "v4")
     x = textgen.agent_transcript(301, 20000).encode()

@@ -221,3 +221,39 @@ def test_trainer_deterministic_and_consistent():
     assert len({tuple(x) for x in a.tolist()}) == a.shape[0]
     tb = oracle.Merges(a).token_bytes()
     assert max(len(t) for t in tb) <= 128
+
+
+def _seam_safe(rank, tb_index, text, j, lmax):
+    """No pair (x, y) of tokens with x's bytes ending at j and y's bytes starting at j has a rank."""
+    xs = [t for l in range(1, min(lmax, j) + 1) for t in tb_index.get(text[j - l:j], [])]
+    ys = [t for l in range(1, min(lmax, len(text) - j) + 1) for t in tb_index.get(text[j:j + l], [])]
+    return not any((x, y) in rank for x in xs for y in ys)
+
+
+def test_seam_criterion_splits_exactly():
+    """The criterion used to cut giant pieces: where no token ending at j and token starting at j form
+    a merge pair, BPE of the whole string is BPE of its two sides concatenated.  Checked on random
+    strings with dense random merge lists; the unsafe positions must include real counterexamples,
+    so the check is not vacuous."""
+    rng = np.random.default_rng(77)
+    safe_seen = unsafe_broken = 0
+    for trial in range(30):
+        alpha = [ord(c) for c in "abcd"[: 2 + trial % 3]]
+        merges = random_consistent_merges(rng, 60, alpha)
+        m = oracle.Merges(merges)
+        tb = m.token_bytes()
+        index = collections.defaultdict(list)
+        for t, b in enumerate(tb):
+            index[b].append(t)
+        rank = {(int(a), int(b)): r for r, (a, b) in enumerate(merges)}
+        lmax = max(len(b) for b in tb)
+        text = bytes(int(c) for c in rng.choice(alpha, 120))
+        whole = oracle.textbook_bpe(merges, text)
+        for j in range(1, len(text)):
+            split = oracle.textbook_bpe(merges, text[:j]) + oracle.textbook_bpe(merges, text[j:])
+            if _seam_safe(rank, index, text, j, lmax):
+                safe_seen += 1
+                assert split == whole, (trial, j)
+            elif split != whole:
+                unsafe_broken += 1
+    assert safe_seen > 50 and unsafe_broken > 50
