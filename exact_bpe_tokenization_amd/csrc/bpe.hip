@@ -110,15 +110,19 @@ __global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__r
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
     const uint32_t *list = (const uint32_t *)(ws + (which == 0 ? L.miss16 : (which == 1 ? L.miss32 : L.miss64)));
     const uint32_t count = ctrl->miss_count[which];
+    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
+    uint32_t *ccount = (uint32_t *)(ws + L.ccount);
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t stride = gridDim.x * blockDim.x;
     // wavefront-uniform loop (the token-count update below is a wavefront operation)
     for (uint32_t q0 = blockIdx.x * blockDim.x + (threadIdx.x & ~63u); q0 < count; q0 += stride) {
         const uint32_t q = q0 + lane;
         const bool active = q < count;
-        const uint32_t p = active ? list[q] : 0u;
-        const uint32_t b0 = active ? pstart[p] : 0u;
-        const uint32_t len = active ? pstart[p + 1] - b0 : 0u;   // 0: nothing to merge or write
+        const uint32_t e = active ? list[q] : 0u;
+        const bool chunk = (e & CHUNK_ITEM) != 0;
+        const uint32_t p = e & ~CHUNK_ITEM;
+        const uint32_t b0 = !active ? 0u : chunk ? cstart[p] : pstart[p];
+        const uint32_t len = !active ? 0u : chunk ? clen[p] : pstart[p + 1] - b0;   // 0: nothing to do
         uint32_t id[MAXL], rk[MAXL];
 #pragma unroll
         for (int k = 0; k < MAXL; ++k) id[k] = (uint32_t)k < len ? (uint32_t)bytes[b0 + k] : 0u;
@@ -156,13 +160,14 @@ __global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__r
                 if ((uint32_t)j == pos) rk[j] = rr;
             }
         }
-        if (n > 1) {
+        if (n > 1 || chunk) {
 #pragma unroll
             for (int k = 0; k < MAXL; ++k)
                 if ((uint32_t)k < n) scratch[b0 + k] = id[k];
         }
-        if (active) pval[p] = n == 1 ? id[0] : (PV_MULTI | n);
-        add_excess_wave(ws, L, p, active ? n - 1 : 0u);
+        if (active && chunk) ccount[p] = n;
+        else if (active) pval[p] = n == 1 ? id[0] : (PV_MULTI | n);
+        add_excess_wave(ws, L, p, active && !chunk ? n - 1 : 0u);
     }
 }
 
@@ -204,13 +209,18 @@ __global__ __launch_bounds__(256) void k_bpe_seg(DevVocab v, const uint8_t *__re
     const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const uint32_t nwaves = (gridDim.x * blockDim.x) >> 6;
 
+    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
+    uint32_t *ccount = (uint32_t *)(ws + L.ccount);
     for (uint32_t q0 = wave * SEGS; q0 < count; q0 += nwaves * SEGS) {
         const uint32_t q = q0 + seg;
         uint32_t p = 0, b0 = 0, n = 0;
+        bool chunk = false;
         if (q < count) {
-            p = list[q];
-            b0 = pstart[p];
-            n = pstart[p + 1] - b0;   // 2..G bytes
+            const uint32_t e = list[q];
+            chunk = (e & CHUNK_ITEM) != 0;
+            p = e & ~CHUNK_ITEM;
+            b0 = chunk ? cstart[p] : pstart[p];
+            n = chunk ? clen[p] : pstart[p + 1] - b0;   // up to G bytes
         }
         uint32_t id = k < n ? (uint32_t)bytes[b0 + k] : 0u;
         uint32_t nx = __shfl_down(id, 1, 64);
@@ -238,10 +248,11 @@ __global__ __launch_bounds__(256) void k_bpe_seg(DevVocab v, const uint8_t *__re
             if (k >= n) rk = NO_RANK;
             else if (rk == PENDING) rk = k + 1 < n ? pair_rank(v, id, nx) : NO_RANK;
         }
-        if (k < n && n > 1) scratch[b0 + k] = id;
+        if (k < n && (n > 1 || chunk)) scratch[b0 + k] = id;
         const bool head = k == 0 && q < count;
-        if (head) pval[p] = n == 1 ? id : (PV_MULTI | n);
-        add_excess_wave(ws, L, p, head ? n - 1 : 0u);
+        if (head && chunk) ccount[p] = n;
+        else if (head) pval[p] = n == 1 ? id : (PV_MULTI | n);
+        add_excess_wave(ws, L, p, head && !chunk ? n - 1 : 0u);
     }
 }
 
@@ -338,8 +349,10 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
     const uint32_t *list = (const uint32_t *)(ws + (bin == 0 ? L.bin_wave : L.bin_block));
     const uint32_t count = ctrl->bin_count[bin];
-    // the block bin also takes the chunks of giant pieces that fit (their results go to ccount)
-    const uint32_t n_chunks = bin == 1 ? ctrl->n_chunks : 0u;
+    // chunks of giant pieces of this kernel's size range come after the bin's pieces (their results
+    // go to ccount): up to WAVE_MAX bytes for the wavefront kernel, up to BLOCK_MAX for the other
+    const uint32_t n_chunks = ctrl->n_chunks;
+    const uint32_t cmin = bin == 0 ? (uint32_t)LANE_MAX + 1u : (uint32_t)WAVE_MAX + 1u;
     const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
     uint32_t *ccount = (uint32_t *)(ws + L.ccount);
     const uint32_t tid = threadIdx.x;
@@ -355,7 +368,7 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
         } else {
             b0 = cstart[q - count];
             n = clen[q - count];
-            if (n == 0 || n > (uint32_t)MAXN) continue;   // unused slot, or a chunk for the giant kernel
+            if (n < cmin || n > (uint32_t)MAXN) continue;   // unused slot, or a chunk for another kernel
         }
         for (uint32_t k = tid; k < n; k += NT) sid[k] = bytes[b0 + k];
         __syncthreads();
@@ -469,11 +482,12 @@ __device__ __forceinline__ void str_find(const DevVocab &v, const uint8_t *s, ui
     }
 }
 
-// may the piece s[0, n) be cut before byte j (0 < j < n)?
+// may the piece s[0, n) be cut before byte j (0 < j < n)?  Tokens ending at j are collected first;
+// each token starting at j is checked against them as soon as it is found.
 __device__ bool seam_safe(const DevVocab &v, const uint8_t *s, uint32_t n, uint32_t j)
 {
-    uint32_t xs[SEAM_MAXT], ys[SEAM_MAXT];
-    uint32_t nx = 0, ny = 0;
+    uint32_t xs[SEAM_MAXT];
+    uint32_t nx = 0;
     bool over = false;
     uint64_t h = 0, pw = 1;
     const uint32_t lx = min(v.lmax, j), ly = min(v.lmax, n - j);
@@ -485,64 +499,152 @@ __device__ bool seam_safe(const DevVocab &v, const uint8_t *s, uint32_t n, uint3
             else over = true;
         });
     }
+    if (over) return false;
+    bool ranked = false;
     h = 0;
-    for (uint32_t l = 1; l <= ly && !over; ++l) {
+    for (uint32_t l = 1; l <= ly && !ranked; ++l) {
         h = h * STR_P + s[j + l - 1];
         str_find(v, s + j, l, str_key(h, l), [&](uint32_t id) {
-            if (ny < (uint32_t)SEAM_MAXT) ys[ny++] = id;
-            else over = true;
+            for (uint32_t a = 0; a < nx && !ranked; ++a) ranked = pair_rank(v, xs[a], id) != NO_RANK;
         });
     }
-    if (over) return false;
-    for (uint32_t a = 0; a < nx; ++a)
-        for (uint32_t b = 0; b < ny; ++b)
-            if (pair_rank(v, xs[a], ys[b]) != NO_RANK) return false;
-    return true;
+    return !ranked;
 }
 
-// k_gseam: one workgroup per giant piece.  Candidate seams lie in windows [k GCH, k GCH + GW) of the
-// piece; each window contributes its first safe position.  The piece's chunks get consecutive slots
-// of the chunk table (start, length); slots reserved but not used keep length 0.
-__global__ __launch_bounds__(1024) void k_gseam(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws, Layout L)
+// Safe-seam bitmap of the giant pieces: bit (a % 32) of word a / 32 + b0 / 4096 says the piece
+// starting at byte b0 may be cut before byte a (b0 < a < b0 + n).  The b0 / 4096 term keeps the
+// words of two giant pieces (each longer than 4096 bytes) apart.
+__device__ __forceinline__ uint32_t safe_word(uint32_t a, uint32_t b0)
 {
-    constexpr uint32_t NWB = 1024 / GW;   // windows per pass
-    __shared__ uint32_t sfirst[NWB];
+    return a / 32 + b0 / 4096;
+}
+
+// k_gsafe: every position of every giant piece is tested; workgroups share out 1024-position
+// blocks (aligned to absolute positions) of each piece in turn
+__global__ __launch_bounds__(1024) void k_gsafe(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws, Layout L)
+{
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
+    uint32_t *bm = (uint32_t *)(ws + L.gsafe);
+    const uint32_t count = ctrl->bin_count[2];
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    if (!v.str) return;
+    for (uint32_t g = 0; g < count; ++g) {
+        const uint32_t p = list[g];
+        const uint32_t b0 = pstart[p], n = pstart[p + 1] - b0;
+        const uint32_t first = b0 / 1024, last = (b0 + n - 1) / 1024;
+        for (uint32_t blk = first + blockIdx.x; blk <= last; blk += gridDim.x) {
+            const uint32_t a = blk * 1024 + tid;
+            const bool ok = a > b0 && a < b0 + n && seam_safe(v, bytes + b0, n, a - b0);
+            const uint64_t m = __ballot(ok);
+            const uint32_t a0 = a - lane;   // multiple of 64
+            // a word is written by the piece whose positions (b0, b0 + n) it covers
+            if (lane == 0 && a0 + 31 > b0 && a0 < b0 + n) bm[safe_word(a0, b0)] = (uint32_t)m;
+            if (lane == 32 && a0 + 63 > b0 && a0 + 32 < b0 + n) bm[safe_word(a0 + 32, b0)] = (uint32_t)(m >> 32);
+        }
+    }
+}
+
+// first and last safe position of window [lo, hi) of the piece at b0 (NO_PIECE if none); lo > b0
+__device__ __forceinline__ void window_safe(const uint32_t *bm, uint32_t b0, uint32_t lo, uint32_t hi, uint32_t &f,
+                                            uint32_t &l)
+{
+    f = l = NO_PIECE;
+    for (uint32_t w = lo / 32; w * 32 < hi; ++w) {
+        uint32_t bits = bm[safe_word(w * 32, b0)];
+        if (w == lo / 32) bits &= ~0u << (lo % 32);
+        if (w == hi / 32) bits &= (hi % 32) ? ((1u << (hi % 32)) - 1u) : 0u;
+        if (!bits) continue;
+        if (f == NO_PIECE) f = w * 32 + (uint32_t)__ffs(bits) - 1u;
+        l = w * 32 + 31u - (uint32_t)__clz(bits);
+    }
+}
+
+// k_gcut: one workgroup per giant piece turns the bitmap into chunks.  The piece is divided into
+// windows of GCH positions; every window with a safe position is cut at its first one (chunks of
+// about GCH bytes where seams are common), and a window followed by one without any safe position
+// is also cut at its last one, so that a stretch without seams (typically a repeated character,
+// which needs few merge rounds) is a chunk of its own.  Cuts come out sorted; a workgroup scan
+// places them.  Chunks take consecutive slots of the chunk table (unused reserved slots: length 0);
+// chunks of up to LANE_MAX bytes are also listed for the lane and segment kernels.
+__global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, Layout L)
+{
+    constexpr uint32_t NT = 1024, NW = NT / 64;
+    __shared__ uint32_t swsum[NW];
     __shared__ uint32_t s_c0, s_nc;
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
+    const uint32_t *bm = (const uint32_t *)(ws + L.gsafe);
     uint32_t *cstart = (uint32_t *)(ws + L.cstart), *clen = (uint32_t *)(ws + L.clen);
     uint32_t *gc0 = (uint32_t *)(ws + L.gc0), *gnc = (uint32_t *)(ws + L.gnc);
     const uint32_t count = ctrl->bin_count[2];
-    const uint32_t tid = threadIdx.x;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
     for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
         const uint32_t p = list[g];
-        const uint32_t b0 = pstart[p], n = pstart[p + 1] - b0;
-        const uint32_t nwin = (v.str && n > 2 * GCH) ? (n - GCH) / GCH : 0u;
+        const uint32_t b0 = pstart[p], n = pstart[p + 1] - b0, end = b0 + n;
+        const uint32_t nwin = v.str ? (n + GCH - 1) / GCH : 0u;
+        const uint32_t reserve = 2 * nwin + 2;
         if (tid == 0) {
-            s_c0 = atomicAdd(&ctrl->n_chunks, nwin + 1);
+            s_c0 = atomicAdd(&ctrl->n_chunks, reserve);
             cstart[s_c0] = b0;
             s_nc = 1;
         }
         __syncthreads();
         const uint32_t c0 = s_c0;
-        for (uint32_t w0 = 0; w0 < nwin; w0 += NWB) {
-            if (tid < NWB) sfirst[tid] = GW;
-            __syncthreads();
-            const uint32_t w = w0 + tid / GW, d = tid % GW;
-            if (w < nwin && seam_safe(v, bytes + b0, n, (w + 1) * GCH + d)) atomicMin(&sfirst[tid / GW], d);
-            __syncthreads();
-            if (tid == 0) {
-                uint32_t nc = s_nc;
-                for (uint32_t k = 0; k < NWB && w0 + k < nwin; ++k)
-                    if (sfirst[k] < GW) cstart[c0 + nc++] = b0 + (w0 + k + 1) * GCH + sfirst[k];
-                s_nc = nc;
+        for (uint32_t k0 = 0; k0 < nwin; k0 += NT) {
+            const uint32_t k = k0 + tid;
+            uint32_t f = NO_PIECE, l = NO_PIECE, fn = NO_PIECE, ln;
+            if (k < nwin) {
+                window_safe(bm, b0, max(b0 + 1, b0 + k * GCH), min(end, b0 + (k + 1) * GCH), f, l);
+                if (k + 1 < nwin) window_safe(bm, b0, b0 + (k + 1) * GCH, min(end, b0 + (k + 2) * GCH), fn, ln);
             }
+            const bool cf = k >= 1 && f != NO_PIECE;
+            const bool cl = l != NO_PIECE && k + 1 < nwin && fn == NO_PIECE && !(cf && l == f);
+            const uint32_t e = (cf ? 1u : 0u) + (cl ? 1u : 0u);
+            uint32_t inc = e;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t y = __shfl_up(inc, d, 64);
+                if (lane >= (uint32_t)d) inc += y;
+            }
+            if (lane == 63) swsum[wid] = inc;
+            __syncthreads();
+            uint32_t before = s_nc, tot = 0;
+            for (uint32_t w = 0; w < NW; ++w) {
+                if (w < wid) before += swsum[w];
+                tot += swsum[w];
+            }
+            uint32_t o = before + inc - e;
+            if (cf) cstart[c0 + o++] = f;
+            if (cl) cstart[c0 + o] = l;
+            __syncthreads();
+            if (tid == 0) s_nc += tot;
             __syncthreads();
         }
+        __threadfence();   // chunk starts are read by other threads below
+        __syncthreads();
         const uint32_t nc = s_nc;
-        for (uint32_t i = tid; i <= nwin; i += blockDim.x)
-            clen[c0 + i] = i < nc ? (i + 1 < nc ? cstart[c0 + i + 1] : b0 + n) - cstart[c0 + i] : 0u;
+        // lengths; chunks of up to LANE_MAX bytes also go to the BPE lists (one atomic per list and
+        // wavefront step), longer ones are found in the table by the workgroup kernels
+        for (uint32_t i0 = wid * 64; i0 < reserve; i0 += NT) {
+            const uint32_t i = i0 + lane;
+            const uint32_t len = i < nc ? (i + 1 < nc ? cstart[c0 + i + 1] : end) - cstart[c0 + i] : 0u;
+            if (i < reserve) clen[c0 + i] = len;
+            const uint32_t r = len >= 1 && len <= (uint32_t)LANE_MAX ? route_of(len) : 3u;
+#pragma unroll
+            for (uint32_t rl = 0; rl < 3; ++rl) {
+                const uint64_t m = __ballot(r == rl);
+                if (!m) continue;
+                const uint32_t leader = (uint32_t)__ffsll((unsigned long long)m) - 1u;
+                uint32_t base = 0;
+                if (lane == leader) base = atomicAdd(&ctrl->miss_count[rl], (uint32_t)__popcll(m));
+                base = __shfl(base, (int)leader, 64);
+                if (r == rl)
+                    route_list(ws, L, rl)[base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull))] = CHUNK_ITEM | (c0 + i);
+            }
+        }
         if (tid == 0) {
             gc0[g] = c0;
             gnc[g] = nc;
@@ -551,45 +653,62 @@ __global__ __launch_bounds__(1024) void k_gseam(DevVocab v, const uint8_t *__res
     }
 }
 
-// k_gassemble: one workgroup per giant piece; moves the chunks' IDs next to each other at the piece's
-// start (each chunk moves left or stays; a segment is read completely before it is written) and
-// records the piece's token count
+// k_gassemble: one workgroup per giant piece.  A scan of the chunks' token counts gives each chunk's
+// place in the piece's output; the wavefronts copy the chunks there in a second buffer (chunks in
+// parallel), then the whole piece is copied back to its start in scratch, and the piece's token
+// count is recorded.
 __global__ __launch_bounds__(1024) void k_gassemble(uint8_t *ws, Layout L)
 {
-    constexpr uint32_t NT = 1024, PER = 4;
+    constexpr uint32_t NT = 1024, NW = NT / 64;
+    __shared__ uint32_t swsum[NW];
+    __shared__ uint32_t s_acc;
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
     const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *ccount = (const uint32_t *)(ws + L.ccount);
+    uint32_t *cdest = (uint32_t *)(ws + L.clen);   // chunk lengths are no longer needed
     const uint32_t *gc0 = (const uint32_t *)(ws + L.gc0), *gnc = (const uint32_t *)(ws + L.gnc);
-    uint32_t *scratch = (uint32_t *)(ws + L.scratch);
+    uint32_t *scratch = (uint32_t *)(ws + L.scratch), *tmp = (uint32_t *)(ws + L.g_ids);
     const uint32_t count = ctrl->bin_count[2];
-    const uint32_t tid = threadIdx.x;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
     for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
         const uint32_t p = list[g], b0 = pstart[p], c0 = gc0[g], nc = gnc[g];
-        uint32_t acc = 0;
-        for (uint32_t i = 0; i < nc; ++i) {
-            const uint32_t cs = cstart[c0 + i], cnt = ccount[c0 + i];
-            if (cs != b0 + acc) {
-                for (uint32_t s0 = 0; s0 < cnt; s0 += NT * PER) {
-                    uint32_t x[PER];
+        if (tid == 0) s_acc = 0;
+        __syncthreads();
+        for (uint32_t i0 = 0; i0 < nc; i0 += NT) {
+            const uint32_t i = i0 + tid;
+            const uint32_t x = i < nc ? ccount[c0 + i] : 0u;
+            uint32_t inc = x;
 #pragma unroll
-                    for (uint32_t k = 0; k < PER; ++k) {
-                        const uint32_t j = s0 + k * NT + tid;
-                        x[k] = j < cnt ? scratch[cs + j] : 0u;
-                    }
-                    __syncthreads();
-#pragma unroll
-                    for (uint32_t k = 0; k < PER; ++k) {
-                        const uint32_t j = s0 + k * NT + tid;
-                        if (j < cnt) scratch[b0 + acc + j] = x[k];
-                    }
-                    __syncthreads();
-                }
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t y = __shfl_up(inc, d, 64);
+                if (lane >= (uint32_t)d) inc += y;
             }
-            acc += cnt;
+            if (lane == 63) swsum[wid] = inc;
+            __syncthreads();
+            uint32_t before = s_acc, tot = 0;
+            for (uint32_t w = 0; w < NW; ++w) {
+                if (w < wid) before += swsum[w];
+                tot += swsum[w];
+            }
+            if (i < nc) cdest[c0 + i] = before + inc - x;
+            __syncthreads();
+            if (tid == 0) s_acc += tot;
+            __syncthreads();
         }
-        if (tid == 0) put_piece(ws, L, p, acc, 0u, true);
+        const uint32_t total = s_acc;
+        __threadfence();
+        __syncthreads();
+        for (uint32_t i = wid; i < nc; i += NW) {
+            const uint32_t *src = scratch + cstart[c0 + i];
+            uint32_t *dst = tmp + b0 + cdest[c0 + i];
+            const uint32_t c = ccount[c0 + i];
+            for (uint32_t j = lane; j < c; j += 64) dst[j] = src[j];
+        }
+        __threadfence();
+        __syncthreads();
+        for (uint32_t j = tid; j < total; j += NT) scratch[b0 + j] = tmp[b0 + j];
+        if (tid == 0) put_piece(ws, L, p, total, 0u, true);
         __syncthreads();
     }
 }
@@ -743,6 +862,15 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     if (b.n == 0) return hipGetLastError();
     uint32_t g = (uint32_t)((b.n + 255) / 256);
     {
+        // giant pieces: safe-seam bitmap, then chunks (before the other BPE kernels, which also
+        // encode the chunks)
+        LaunchScope k(ev, 8, s);
+        const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
+        hipLaunchKernelGGL(k_gsafe, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
+        const uint32_t gc = L.cap_giant < 64 ? L.cap_giant : 64;
+        hipLaunchKernelGGL(k_gcut, dim3(gc), dim3(1024), 0, s, v, b.ws, L);
+    }
+    {
         LaunchScope k(ev, 4, s);
         hipLaunchKernelGGL((k_bpe_lane<16>), dim3(g > 2048 ? 2048 : g), dim3(256), 0, s, v, b.bytes, b.ws, L, 0);
     }
@@ -760,14 +888,10 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     }
     {
         LaunchScope k(ev, 7, s);
-        uint32_t gw = L.cap_wave < 1024 ? L.cap_wave : 1024;
+        uint32_t gw = L.cap_wave + L.cap_chunks < 1024 ? L.cap_wave + L.cap_chunks : 1024;
         hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
     }
     const uint32_t gg = L.cap_giant < 64 ? L.cap_giant : 64;
-    {
-        LaunchScope k(ev, 8, s);
-        hipLaunchKernelGGL(k_gseam, dim3(gg), dim3(1024), 0, s, v, b.bytes, b.ws, L);
-    }
     {
         LaunchScope k(ev, 9, s);
         uint32_t gb = L.cap_block + L.cap_chunks < 256 ? L.cap_block + L.cap_chunks : 256;

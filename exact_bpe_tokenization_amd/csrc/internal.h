@@ -18,9 +18,11 @@ constexpr int SCAN_THREADS = 256;
 constexpr int SCAN_PER_THREAD = 16;
 constexpr int SCAN_TILE = SCAN_THREADS * SCAN_PER_THREAD;
 
-// giant pieces are cut into chunks of about GCH bytes at seams that no merge can cross, searched
-// in a window of GW positions after each multiple of GCH
-constexpr uint32_t GCH = 2048, GW = 64;
+// giant pieces are cut at seams that no merge can cross: about every GCH bytes where such seams are
+// common, and at both ends of stretches longer than GCH without one
+constexpr uint32_t GCH = 48;
+// BPE list entries: a piece index, or CHUNK_ITEM | index into the chunk table
+constexpr uint32_t CHUNK_ITEM = 1u << 31;
 
 // BPE length bins (piece bytes): lane <= LANE_MAX < wave <= WAVE_MAX < block <= BLOCK_MAX < giant
 constexpr int LANE_MAX = 64;      // lane kernels: <= 16, 17..32 and 33..64 bytes
@@ -235,8 +237,8 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 struct Layout {
     uint64_t ctrl, cc, tbwd, tflag_state, tflag_cnt, pstart, pval, tokoff, scratch, bin_wave,
         bin_block, bin_giant, miss16, miss32, miss64, g_ids, g_rank_a, g_rank_b, tilex, cstart, clen, ccount,
-        gc0, gnc, total;
-    uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant, cap_chunks;
+        gc0, gnc, gsafe, total;
+    uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
 };
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
@@ -249,7 +251,8 @@ inline Layout make_layout(uint64_t n)
     L.cap_wave = (uint32_t)(n / (LANE_MAX + 1) + 1);
     L.cap_block = (uint32_t)(n / (WAVE_MAX + 1) + 1);
     L.cap_giant = (uint32_t)(n / (BLOCK_MAX + 1) + 1);
-    L.cap_chunks = (uint32_t)(n / (GCH - GW) + 2ull * L.cap_giant + 2);
+    L.cap_chunks = (uint32_t)(2 * (n / GCH) + 2ull * L.cap_giant + 2);
+    L.n_safe_words = (uint32_t)(n / 32 + n / 4096 + 4);
     uint64_t o = 0;
     L.ctrl = o;        o += align256(sizeof(Ctrl));
     L.cc = o;
@@ -275,6 +278,7 @@ inline Layout make_layout(uint64_t n)
     L.ccount = o;      o += align256(4ull * L.cap_chunks);
     L.gc0 = o;         o += align256(4ull * L.cap_giant);
     L.gnc = o;         o += align256(4ull * L.cap_giant);
+    L.gsafe = o;       o += align256(4ull * L.n_safe_words);
     L.total = o;
     return L;
 }
