@@ -631,7 +631,10 @@ __global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, La
         for (uint32_t i0 = wid * 64; i0 < reserve; i0 += NT) {
             const uint32_t i = i0 + lane;
             const uint32_t len = i < nc ? (i + 1 < nc ? cstart[c0 + i + 1] : end) - cstart[c0 + i] : 0u;
-            if (i < reserve) clen[c0 + i] = len;
+            if (i < reserve) {
+                clen[c0 + i] = len;
+                ((uint32_t *)(ws + L.cpiece))[c0 + i] = i < nc ? p : NO_PIECE;
+            }
             const uint32_t r = len >= 1 && len <= (uint32_t)LANE_MAX ? route_of(len) : 3u;
 #pragma unroll
             for (uint32_t rl = 0; rl < 3; ++rl) {
@@ -654,25 +657,22 @@ __global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, La
 }
 
 // k_gassemble: one workgroup per giant piece.  A scan of the chunks' token counts gives each chunk's
-// place in the piece's output; the wavefronts copy the chunks there in a second buffer (chunks in
-// parallel), then the whole piece is copied back to its start in scratch, and the piece's token
-// count is recorded.
+// place in the piece's output (cdest, in the chunk-length array, no longer needed); the piece's
+// token count is recorded, and the output gather copies each chunk from scratch.
 __global__ __launch_bounds__(1024) void k_gassemble(uint8_t *ws, Layout L)
 {
     constexpr uint32_t NT = 1024, NW = NT / 64;
     __shared__ uint32_t swsum[NW];
     __shared__ uint32_t s_acc;
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
-    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
-    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *ccount = (const uint32_t *)(ws + L.ccount);
-    uint32_t *cdest = (uint32_t *)(ws + L.clen);   // chunk lengths are no longer needed
+    const uint32_t *ccount = (const uint32_t *)(ws + L.ccount);
+    uint32_t *cdest = (uint32_t *)(ws + L.clen);
     const uint32_t *gc0 = (const uint32_t *)(ws + L.gc0), *gnc = (const uint32_t *)(ws + L.gnc);
-    uint32_t *scratch = (uint32_t *)(ws + L.scratch), *tmp = (uint32_t *)(ws + L.g_ids);
     const uint32_t count = ctrl->bin_count[2];
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
     for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
-        const uint32_t p = list[g], b0 = pstart[p], c0 = gc0[g], nc = gnc[g];
+        const uint32_t p = list[g], c0 = gc0[g], nc = gnc[g];
         if (tid == 0) s_acc = 0;
         __syncthreads();
         for (uint32_t i0 = 0; i0 < nc; i0 += NT) {
@@ -696,19 +696,7 @@ __global__ __launch_bounds__(1024) void k_gassemble(uint8_t *ws, Layout L)
             if (tid == 0) s_acc += tot;
             __syncthreads();
         }
-        const uint32_t total = s_acc;
-        __threadfence();
-        __syncthreads();
-        for (uint32_t i = wid; i < nc; i += NW) {
-            const uint32_t *src = scratch + cstart[c0 + i];
-            uint32_t *dst = tmp + b0 + cdest[c0 + i];
-            const uint32_t c = ccount[c0 + i];
-            for (uint32_t j = lane; j < c; j += 64) dst[j] = src[j];
-        }
-        __threadfence();
-        __syncthreads();
-        for (uint32_t j = tid; j < total; j += NT) scratch[b0 + j] = tmp[b0 + j];
-        if (tid == 0) put_piece(ws, L, p, total, 0u, true);
+        if (tid == 0) put_piece(ws, L, p, s_acc, 0u, true);
         __syncthreads();
     }
 }

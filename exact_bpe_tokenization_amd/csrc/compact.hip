@@ -121,7 +121,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
     }
 }
 
-// one workgroup per binned (longer than a lane's limit) piece
+// IDs of the pieces longer than 64 bytes: one workgroup per piece of the wave and block bins, and
+// one per chunk of a giant piece (a chunk's IDs go to its place in the piece's output)
 __global__ __launch_bounds__(256) void k_gather_long(uint8_t *ws, Layout L, uint32_t *__restrict__ out_ids)
 {
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
@@ -129,14 +130,26 @@ __global__ __launch_bounds__(256) void k_gather_long(uint8_t *ws, Layout L, uint
     const uint32_t *pval = (const uint32_t *)(ws + L.pval);
     const uint32_t *tokoff = (const uint32_t *)(ws + L.tokoff);
     const uint32_t *scratch = (const uint32_t *)(ws + L.scratch);
-    const uint32_t c0 = ctrl->bin_count[0], c1 = ctrl->bin_count[1], c2 = ctrl->bin_count[2];
-    const uint32_t *l0 = (const uint32_t *)(ws + L.bin_wave), *l1 = (const uint32_t *)(ws + L.bin_block),
-                   *l2 = (const uint32_t *)(ws + L.bin_giant);
-    for (uint32_t q = blockIdx.x; q < c0 + c1 + c2; q += gridDim.x) {
-        const uint32_t p = q < c0 ? l0[q] : (q < c0 + c1 ? l1[q - c0] : l2[q - c0 - c1]);
-        const uint32_t *src = scratch + pstart[p];
-        uint32_t *dst = out_ids + tokoff[p];
-        const uint32_t c = pval[p] & PV_COUNT;
+    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *cdest = (const uint32_t *)(ws + L.clen);
+    const uint32_t *ccount = (const uint32_t *)(ws + L.ccount), *cpiece = (const uint32_t *)(ws + L.cpiece);
+    const uint32_t c0 = ctrl->bin_count[0], c1 = ctrl->bin_count[1], nch = ctrl->n_chunks;
+    const uint32_t *l0 = (const uint32_t *)(ws + L.bin_wave), *l1 = (const uint32_t *)(ws + L.bin_block);
+    for (uint32_t q = blockIdx.x; q < c0 + c1 + nch; q += gridDim.x) {
+        const uint32_t *src;
+        uint32_t *dst;
+        uint32_t c;
+        if (q < c0 + c1) {
+            const uint32_t p = q < c0 ? l0[q] : l1[q - c0];
+            src = scratch + pstart[p];
+            dst = out_ids + tokoff[p];
+            c = pval[p] & PV_COUNT;
+        } else {
+            const uint32_t k = q - c0 - c1, p = cpiece[k];
+            if (p == NO_PIECE) continue;   // reserved chunk slot not used
+            src = scratch + cstart[k];
+            dst = out_ids + tokoff[p] + cdest[k];
+            c = ccount[k];
+        }
         for (uint32_t j = threadIdx.x; j < c; j += blockDim.x) dst[j] = src[j];
     }
 }
@@ -161,7 +174,7 @@ hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offse
     }
     if (b.n) {
         LaunchScope k(ev, 13, s);
-        uint32_t gl = L.cap_wave < 512 ? L.cap_wave : 512;
+        uint32_t gl = L.cap_wave + L.cap_chunks < 1024 ? L.cap_wave + L.cap_chunks : 1024;
         hipLaunchKernelGGL(k_gather_long, dim3(gl), dim3(256), 0, s, b.ws, L, out_ids);
     }
     return hipGetLastError();

@@ -237,7 +237,7 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 struct Layout {
     uint64_t ctrl, cc, tbwd, tflag_state, tflag_cnt, pstart, pval, tokoff, scratch, bin_wave,
         bin_block, bin_giant, miss16, miss32, miss64, g_ids, g_rank_a, g_rank_b, tilex, cstart, clen, ccount,
-        gc0, gnc, gsafe, total;
+        gc0, gnc, gsafe, cpiece, total;
     uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
 };
 
@@ -279,6 +279,7 @@ inline Layout make_layout(uint64_t n)
     L.gc0 = o;         o += align256(4ull * L.cap_giant);
     L.gnc = o;         o += align256(4ull * L.cap_giant);
     L.gsafe = o;       o += align256(4ull * L.n_safe_words);
+    L.cpiece = o;      o += align256(4ull * L.cap_chunks);
     L.total = o;
     return L;
 }

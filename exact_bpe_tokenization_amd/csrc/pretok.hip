@@ -262,7 +262,7 @@ __global__ void k_init(uint8_t *ws, Layout L)
 // k_summary: one wavefront per tile.  The tile's summary of a backward flag is the map of its
 // leftmost character whose map is not "pass through" (for NA: the first character that is not
 // whitespace-other-than-CR/LF, or the last of its document; for AU: the first that is not an
-// uppercase letter, or the last of its document).  Usually found in the first 64 bytes.
+// uppercase letter, or the last of its document).  Usually found in the first 256 bytes.
 
 __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ bytes,
                                                 const uint64_t *__restrict__ offsets, uint32_t n_docs,
@@ -271,36 +271,41 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
     const uint32_t lane = threadIdx.x;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
     const uint64_t hi = min(lo + TILE, n);
+    // document starts in [lo, hi + 4): indices [d0, d1) of offsets (empty documents repeat one)
+    const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, lo);
+    const uint32_t d1 = wave_lower_bound(offsets, n_docs + 1, hi + 4);
     uint32_t na = BK_KEEP, au = BK_KEEP;
-    for (uint64_t w = lo; w < hi && (na == BK_KEEP || au == BK_KEEP); w += 64) {
-        const uint64_t p = w + lane;
-        // document starts in [w, w + 68): indices [dw, de) of offsets (empty documents repeat one)
-        const uint32_t dw = wave_lower_bound(offsets, n_docs + 1, w);
-        const uint32_t de = wave_lower_bound(offsets, n_docs + 1, w + 68);
+    // 256 bytes per step, 4 per lane
+    for (uint64_t w = lo; w < hi && (na == BK_KEEP || au == BK_KEEP); w += 256) {
         uint32_t mna = BK_KEEP, mau = BK_KEEP;
-        if (p < hi) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint64_t p = w + 4 * lane + t;
+            if (p >= hi) continue;
             const uint32_t c = bytes[p];
-            if ((c & 0xC0u) != 0x80u) {
-                uint32_t len = utf8_len(c), cp = c;
-                bool ok = len != 0 && p + len <= n;
-                if (ok && len > 1) {
-                    cp = c & (0x7Fu >> len);
-                    for (uint32_t t = 1; t < len; ++t) cp = (cp << 6) | (bytes[p + t] & 0x3Fu);
-                }
-                if (!ok) { len = 1; cp = 0xFFFDu; }
-                uint32_t code = ucat(cp) | ((c == '\r' || c == '\n') ? CC_CRLF : 0u);
-                const uint64_t pn = p + len;
-                bool eof_next = pn >= n;
-                if (!eof_next) {
-                    uint32_t a = dw, b = de;   // lower bound of pn; pn < w + 68
-                    while (a < b) {
-                        const uint32_t m = (a + b) >> 1;
-                        if (offsets[m] < pn) a = m + 1; else b = m;
-                    }
-                    eof_next = a < de && offsets[a] == pn;
-                }
-                backward_maps(code, eof_next, mna, mau);
+            if ((c & 0xC0u) == 0x80u) continue;
+            uint32_t len = utf8_len(c), cp = c;
+            const bool ok = len != 0 && p + len <= n;
+            if (ok && len > 1) {
+                cp = c & (0x7Fu >> len);
+                for (uint32_t u = 1; u < len; ++u) cp = (cp << 6) | (bytes[p + u] & 0x3Fu);
             }
+            if (!ok) { len = 1; cp = 0xFFFDu; }
+            const uint32_t code = ucat(cp) | ((c == '\r' || c == '\n') ? CC_CRLF : 0u);
+            const uint64_t pn = p + len;
+            bool eof_next = pn >= n;
+            if (!eof_next) {
+                uint32_t a = d0, b = d1;   // lower bound of pn among the tile's document starts
+                while (a < b) {
+                    const uint32_t m = (a + b) >> 1;
+                    if (offsets[m] < pn) a = m + 1; else b = m;
+                }
+                eof_next = a < d1 && offsets[a] == pn;
+            }
+            uint32_t xna, xau;
+            backward_maps(code, eof_next, xna, xau);
+            if (mna == BK_KEEP) mna = xna;
+            if (mau == BK_KEEP) mau = xau;
         }
         const uint64_t bna = __ballot(mna != BK_KEEP), bau = __ballot(mau != BK_KEEP);
         const uint32_t xna = __shfl(mna, bna ? __ffsll((unsigned long long)bna) - 1 : 0, 64);
