@@ -35,14 +35,14 @@ constexpr uint32_t PENDING = 0xFFFFFFFEu;
 // in LDS and flushed with one reservation atomic per list at the end (a full queue spills straight
 // to the global list).
 constexpr int RT_THREADS = 512;
-constexpr uint32_t RTQ[6] = {2048, 512, 256, 128, 64, 64};
-constexpr uint32_t RTQ_OFF[7] = {0, 2048, 2560, 2816, 2944, 3008, 3072};
+constexpr uint32_t RTQ[NROUTES] = {2048, 512, 256, 128, 64, 64, 64};
+constexpr uint32_t RTQ_OFF[NROUTES + 1] = {0, 2048, 2560, 2816, 2944, 3008, 3072, 3136};
 
 __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
                                                       Layout L)
 {
-    __shared__ uint32_t q[RTQ_OFF[6]];
-    __shared__ uint32_t qn[6], qbase[6];
+    __shared__ uint32_t q[RTQ_OFF[NROUTES]];
+    __shared__ uint32_t qn[NROUTES], qbase[NROUTES];
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *__restrict__ pval = (uint32_t *)(ws + L.pval);
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t 
     const uint64_t start64 = (uint64_t)blockIdx.x * chunk;
     const uint32_t start = start64 < np ? (uint32_t)start64 : np;
     const uint32_t end = min(np, start + chunk);
-    if (tid < 6) qn[tid] = 0;
+    if (tid < NROUTES) qn[tid] = 0;
     __syncthreads();
     auto list_piece = [&](uint32_t p, uint32_t len) {
         const uint32_t r = route_of(len);
@@ -84,14 +84,14 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t 
         }
     }
     __syncthreads();
-    if (tid < 6) {
+    if (tid < NROUTES) {
         const uint32_t c = min(qn[tid], RTQ[tid]);
         qn[tid] = c;
         if (c) qbase[tid] = atomicAdd(route_count(ctrl, tid), c);
     }
     __syncthreads();
 #pragma unroll
-    for (uint32_t r = 0; r < 6; ++r) {
+    for (uint32_t r = 0; r < NROUTES; ++r) {
         uint32_t *dst = route_list(ws, L, r) + qbase[r];
         for (uint32_t i = tid; i < qn[r]; i += RT_THREADS) dst[i] = q[RTQ_OFF[r] + i];
     }
@@ -256,6 +256,104 @@ __global__ __launch_bounds__(256) void k_bpe_seg(DevVocab v, const uint8_t *__re
     }
 }
 
+// One wavefront per piece of 65..SEG2_MAX bytes, two elements per lane (element e in lane e % 64 of
+// row e / 64): the rounds of k_bpe_seg on 128-bit masks (two ballots; shifts and the addition carry
+// between the words), compaction through a 128-entry LDS row per wavefront (a wavefront's LDS
+// accesses are performed in order, so no barrier is needed).
+
+__device__ __forceinline__ void shl128(uint64_t lo, uint64_t hi, uint64_t &rlo, uint64_t &rhi)
+{
+    rhi = (hi << 1) | (lo >> 63);
+    rlo = lo << 1;
+}
+
+__global__ __launch_bounds__(256) void k_bpe_seg2(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
+                                                  Layout L)
+{
+    constexpr uint64_t EVEN = 0x5555555555555555ull, ODD = ~EVEN;
+    __shared__ uint32_t sid[4][2 * 64], srk[4][2 * 64];
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    uint32_t *pval = (uint32_t *)(ws + L.pval);
+    uint32_t *scratch = (uint32_t *)(ws + L.scratch);
+    const uint32_t *list = (const uint32_t *)(ws + L.miss128);
+    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
+    uint32_t *ccount = (uint32_t *)(ws + L.ccount);
+    const uint32_t count = ctrl->miss_count[3];
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
+    const uint64_t below = (1ull << lane) - 1ull;
+    const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const uint32_t nwaves = (gridDim.x * blockDim.x) >> 6;
+    for (uint32_t q = wave; q < count; q += nwaves) {
+        const uint32_t e = list[q];
+        const bool chunk = (e & CHUNK_ITEM) != 0;
+        const uint32_t p = e & ~CHUNK_ITEM;
+        const uint32_t b0 = chunk ? cstart[p] : pstart[p];
+        uint32_t n = chunk ? clen[p] : pstart[p + 1] - b0;   // up to 128 bytes
+        uint32_t id0 = lane < n ? (uint32_t)bytes[b0 + lane] : 0u;
+        uint32_t id1 = 64 + lane < n ? (uint32_t)bytes[b0 + 64 + lane] : 0u;
+        uint32_t nx0 = __shfl_down(id0, 1, 64), nx1 = __shfl_down(id1, 1, 64);
+        const uint32_t f1 = __shfl(id1, 0, 64);
+        if (lane == 63) nx0 = f1;
+        uint32_t rk0 = lane + 1 < n ? __ldg(v.r2 + ((id0 << 8) | nx0)) : NO_RANK;
+        uint32_t rk1 = 65 + lane < n ? __ldg(v.r2 + ((id1 << 8) | nx1)) : NO_RANK;
+        for (;;) {
+            uint32_t m = min(rk0, rk1);
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) m = min(m, (uint32_t)__shfl_xor(m, d, 64));
+            if (m == NO_RANK) break;
+            const uint64_t H0 = __ballot(rk0 == m), H1 = __ballot(rk1 == m);
+            uint64_t s0, s1;
+            shl128(H0, H1, s0, s1);
+            const uint64_t rsE0 = H0 & ~s0 & EVEN, rsE1 = H1 & ~s1 & EVEN;
+            const uint64_t a0 = H0 + rsE0;
+            const uint64_t a1 = H1 + rsE1 + (a0 < H0 ? 1ull : 0ull);
+            const uint64_t runsE0 = H0 & ~a0, runsE1 = H1 & ~a1;
+            const uint64_t sel0 = (runsE0 & EVEN) | (H0 & ~runsE0 & ODD);
+            const uint64_t sel1 = (runsE1 & EVEN) | (H1 & ~runsE1 & ODD);
+            uint64_t l0, l1;
+            shl128(sel0, sel1, l0, l1);
+            const uint64_t K0 = __ballot(lane < n) & ~l0, K1 = __ballot(64 + lane < n) & ~l1;
+            const bool ms0 = (sel0 >> lane) & 1u, ms1 = (sel1 >> lane) & 1u;
+            const bool ns0 = lane < 63 ? ((sel0 >> (lane + 1)) & 1u) : (sel1 & 1u);
+            const bool ns1 = lane < 63 && ((sel1 >> (lane + 1)) & 1u);
+            const uint32_t k0 = (uint32_t)__popcll(K0);
+            if ((K0 >> lane) & 1u) {
+                const uint32_t o = (uint32_t)__popcll(K0 & below);
+                sid[w][o] = ms0 ? 256u + m : id0;
+                srk[w][o] = (ms0 || ns0) ? PENDING : rk0;
+            }
+            if ((K1 >> lane) & 1u) {
+                const uint32_t o = k0 + (uint32_t)__popcll(K1 & below);
+                sid[w][o] = ms1 ? 256u + m : id1;
+                srk[w][o] = (ms1 || ns1) ? PENDING : rk1;
+            }
+            n = k0 + (uint32_t)__popcll(K1);
+            id0 = sid[w][lane];
+            rk0 = srk[w][lane];
+            id1 = sid[w][64 + lane];
+            rk1 = srk[w][64 + lane];
+            nx0 = __shfl_down(id0, 1, 64);
+            nx1 = __shfl_down(id1, 1, 64);
+            const uint32_t g1 = __shfl(id1, 0, 64);
+            if (lane == 63) nx0 = g1;
+            if (lane >= n) rk0 = NO_RANK;
+            else if (rk0 == PENDING) rk0 = lane + 1 < n ? pair_rank(v, id0, nx0) : NO_RANK;
+            if (64 + lane >= n) rk1 = NO_RANK;
+            else if (rk1 == PENDING) rk1 = 65 + lane < n ? pair_rank(v, id1, nx1) : NO_RANK;
+        }
+        if (n > 1 || chunk) {
+            if (lane < n) scratch[b0 + lane] = id0;
+            if (64 + lane < n) scratch[b0 + 64 + lane] = id1;
+        }
+        if (lane == 0) {
+            if (chunk) ccount[p] = n;
+            else pval[p] = n == 1 ? id0 : (PV_MULTI | n);
+        }
+        add_excess_wave(ws, L, p, lane == 0 && !chunk ? n - 1 : 0u);
+    }
+}
+
 // ---------------------------------------------------------------------------------------------
 // workgroup primitives (NT threads, NT a multiple of 64)
 
@@ -352,7 +450,7 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
     // chunks of giant pieces of this kernel's size range come after the bin's pieces (their results
     // go to ccount): up to WAVE_MAX bytes for the wavefront kernel, up to BLOCK_MAX for the other
     const uint32_t n_chunks = ctrl->n_chunks;
-    const uint32_t cmin = bin == 0 ? (uint32_t)LANE_MAX + 1u : (uint32_t)WAVE_MAX + 1u;
+    const uint32_t cmin = bin == 0 ? (uint32_t)SEG2_MAX + 1u : (uint32_t)WAVE_MAX + 1u;
     const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
     uint32_t *ccount = (uint32_t *)(ws + L.ccount);
     const uint32_t tid = threadIdx.x;
@@ -567,7 +665,7 @@ __device__ __forceinline__ void window_safe(const uint32_t *bm, uint32_t b0, uin
 // is also cut at its last one, so that a stretch without seams (typically a repeated character,
 // which needs few merge rounds) is a chunk of its own.  Cuts come out sorted; a workgroup scan
 // places them.  Chunks take consecutive slots of the chunk table (unused reserved slots: length 0);
-// chunks of up to LANE_MAX bytes are also listed for the lane and segment kernels.
+// chunks of up to SEG2_MAX bytes are also listed for the lane and segment kernels.
 __global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, Layout L)
 {
     constexpr uint32_t NT = 1024, NW = NT / 64;
@@ -626,7 +724,7 @@ __global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, La
         __threadfence();   // chunk starts are read by other threads below
         __syncthreads();
         const uint32_t nc = s_nc;
-        // lengths; chunks of up to LANE_MAX bytes also go to the BPE lists (one atomic per list and
+        // lengths; chunks of up to SEG2_MAX bytes also go to the BPE lists (one atomic per list and
         // wavefront step), longer ones are found in the table by the workgroup kernels
         for (uint32_t i0 = wid * 64; i0 < reserve; i0 += NT) {
             const uint32_t i = i0 + lane;
@@ -635,9 +733,9 @@ __global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, La
                 clen[c0 + i] = len;
                 ((uint32_t *)(ws + L.cpiece))[c0 + i] = i < nc ? p : NO_PIECE;
             }
-            const uint32_t r = len >= 1 && len <= (uint32_t)LANE_MAX ? route_of(len) : 3u;
+            const uint32_t r = len >= 1 && len <= (uint32_t)SEG2_MAX ? route_of(len) : 4u;
 #pragma unroll
-            for (uint32_t rl = 0; rl < 3; ++rl) {
+            for (uint32_t rl = 0; rl < 4; ++rl) {
                 const uint64_t m = __ballot(r == rl);
                 if (!m) continue;
                 const uint32_t leader = (uint32_t)__ffsll((unsigned long long)m) - 1u;
@@ -852,7 +950,7 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     {
         // giant pieces: safe-seam bitmap, then chunks (before the other BPE kernels, which also
         // encode the chunks)
-        LaunchScope k(ev, 8, s);
+        LaunchScope k(ev, 9, s);
         const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
         hipLaunchKernelGGL(k_gsafe, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
         const uint32_t gc = L.cap_giant < 64 ? L.cap_giant : 64;
@@ -876,22 +974,28 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     }
     {
         LaunchScope k(ev, 7, s);
+        const uint64_t g128 = b.n / 65 / 4 + 1;
+        hipLaunchKernelGGL(k_bpe_seg2, dim3(g128 > 1024 ? 1024 : (uint32_t)g128), dim3(256), 0, s, v, b.bytes, b.ws,
+                           L);
+    }
+    {
+        LaunchScope k(ev, 8, s);
         uint32_t gw = L.cap_wave + L.cap_chunks < 1024 ? L.cap_wave + L.cap_chunks : 1024;
         hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
     }
     const uint32_t gg = L.cap_giant < 64 ? L.cap_giant : 64;
     {
-        LaunchScope k(ev, 9, s);
+        LaunchScope k(ev, 10, s);
         uint32_t gb = L.cap_block + L.cap_chunks < 256 ? L.cap_block + L.cap_chunks : 256;
         hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v,
                            b.bytes, b.ws, L, 1);
     }
     {
-        LaunchScope k(ev, 10, s);
+        LaunchScope k(ev, 11, s);
         hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
     }
     {
-        LaunchScope k(ev, 11, s);
+        LaunchScope k(ev, 12, s);
         hipLaunchKernelGGL(k_gassemble, dim3(gg), dim3(1024), 0, s, b.ws, L);
     }
     return hipGetLastError();

@@ -26,6 +26,7 @@ constexpr uint32_t CHUNK_ITEM = 1u << 31;
 
 // BPE length bins (piece bytes): lane <= LANE_MAX < wave <= WAVE_MAX < block <= BLOCK_MAX < giant
 constexpr int LANE_MAX = 64;      // lane kernels: <= 16, 17..32 and 33..64 bytes
+constexpr int SEG2_MAX = 128;     // one wavefront, two elements per lane: 65..128 bytes
 constexpr int TABLE_MAX = 32;     // whole-piece tables hold pieces of 2..32 bytes
 constexpr int WAVE_MAX = 1024;
 constexpr int BLOCK_MAX = 4096;
@@ -226,9 +227,9 @@ struct Ctrl {
     uint32_t n_pieces;
     uint32_t n_tokens;
     uint32_t bin_count[3];     // wave, block, giant bins
-    uint32_t miss_count[3];    // pieces left for lane BPE: <= 16, 17..32, 33..64 bytes
+    uint32_t miss_count[4];    // pieces left for BPE: <= 16, 17..32, 33..64, 65..128 bytes
     uint32_t n_chunks;         // chunk slots reserved for giant pieces
-    uint32_t pad[53];
+    uint32_t pad[52];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
@@ -236,7 +237,7 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // workspace layout for n input bytes
 struct Layout {
     uint64_t ctrl, cc, tbwd, tflag_state, tflag_cnt, pstart, pval, tokoff, scratch, bin_wave,
-        bin_block, bin_giant, miss16, miss32, miss64, g_ids, g_rank_a, g_rank_b, tilex, cstart, clen, ccount,
+        bin_block, bin_giant, miss16, miss32, miss64, miss128, g_ids, g_rank_a, g_rank_b, tilex, cstart, clen, ccount,
         gc0, gnc, gsafe, cpiece, total;
     uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
 };
@@ -270,6 +271,7 @@ inline Layout make_layout(uint64_t n)
     L.miss16 = o;      o += align256(4ull * (n + 1));
     L.miss32 = o;      o += align256(4ull * (n / 17 + 1));
     L.miss64 = o;      o += align256(4ull * (n / 33 + 1));
+    L.miss128 = o;     o += align256(4ull * (n / 65 + 1));
     L.g_ids = o;       o += align256(4ull * (n + 1));
     L.g_rank_a = o;    o += align256(4ull * (n + 1));
     L.g_rank_b = o;    o += align256(4ull * (n + 1));
@@ -404,24 +406,25 @@ __device__ __forceinline__ void put_piece(uint8_t *ws, const Layout &L, uint32_t
     if (n > 1) atomicAdd((uint32_t *)(ws + L.tilex) + p / SCAN_TILE, n - 1);
 }
 
-// List a piece belongs to when it is not resolved directly: 0..2 BPE miss lists (<= 16, 17..32,
-// 33..64 bytes), 3..5 length bins (65..WAVE_MAX, ..BLOCK_MAX, longer).
+// List a piece belongs to when it is not resolved directly: 0..3 BPE miss lists (<= 16, 17..32,
+// 33..64, 65..SEG2_MAX bytes), 4..6 length bins (..WAVE_MAX, ..BLOCK_MAX, longer).
+constexpr uint32_t NROUTES = 7;
 __device__ __forceinline__ uint32_t route_of(uint32_t len)
 {
-    return len <= 16u ? 0u : len <= 32u ? 1u : len <= (uint32_t)LANE_MAX ? 2u :
-           len <= (uint32_t)WAVE_MAX ? 3u : len <= (uint32_t)BLOCK_MAX ? 4u : 5u;
+    return len <= 16u ? 0u : len <= 32u ? 1u : len <= (uint32_t)LANE_MAX ? 2u : len <= (uint32_t)SEG2_MAX ? 3u :
+           len <= (uint32_t)WAVE_MAX ? 4u : len <= (uint32_t)BLOCK_MAX ? 5u : 6u;
 }
 
 __device__ __forceinline__ uint32_t *route_list(uint8_t *ws, const Layout &L, uint32_t r)
 {
-    const uint64_t o = r == 0 ? L.miss16 : r == 1 ? L.miss32 : r == 2 ? L.miss64 :
-                       r == 3 ? L.bin_wave : r == 4 ? L.bin_block : L.bin_giant;
+    const uint64_t o = r == 0 ? L.miss16 : r == 1 ? L.miss32 : r == 2 ? L.miss64 : r == 3 ? L.miss128 :
+                       r == 4 ? L.bin_wave : r == 5 ? L.bin_block : L.bin_giant;
     return (uint32_t *)(ws + o);
 }
 
 __device__ __forceinline__ uint32_t *route_count(Ctrl *ctrl, uint32_t r)
 {
-    return r < 3 ? &ctrl->miss_count[r] : &ctrl->bin_count[r - 3];
+    return r < 4 ? &ctrl->miss_count[r] : &ctrl->bin_count[r - 4];
 }
 
 // Wavefront form of the same counter update, called by all 64 lanes: lane i contributes the

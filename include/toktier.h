@@ -151,7 +151,8 @@ enum {
     TOKTIER_K_BPE_LANE,       /* BPE, one lane per unresolved piece of <= 16 bytes              */
     TOKTIER_K_BPE_SEG32,      /* BPE, 32 lanes per unresolved piece of 17..32 bytes             */
     TOKTIER_K_BPE_SEG64,      /* BPE, one wavefront per unresolved piece of 33..64 bytes        */
-    TOKTIER_K_BPE_WAVE,       /* BPE, one wavefront per piece of 65..1024 bytes                 */
+    TOKTIER_K_BPE_SEG128,     /* BPE, one wavefront (two elements per lane), 65..128 bytes      */
+    TOKTIER_K_BPE_WAVE,       /* BPE, one wavefront per piece of 129..1024 bytes                */
     TOKTIER_K_GIANT_SEAMS,    /* cut pieces > 4096 bytes into chunks at seams no merge crosses  */
     TOKTIER_K_BPE_BLOCK,      /* BPE, one workgroup per piece of 1025..4096 bytes or chunk      */
     TOKTIER_K_BPE_GIANT,      /* BPE, one workgroup per longer chunk, sequence in device memory */

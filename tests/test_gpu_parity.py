@@ -286,8 +286,8 @@ def test_random_merge_lists(tt, seed):
         ids.append(255 + len(merges))
     merges = np.array(merges, dtype=np.uint32)
     tb = oracle.Merges(merges).token_bytes()
-    words = ["".join(chr(int(c)) for c in rng.choice(alpha, int(rng.integers(1, 70)))) for _ in range(3000)]
-    words += [tb[t].decode() for t in range(256, len(tb)) if len(tb[t]) <= 70]
+    words = ["".join(chr(int(c)) for c in rng.choice(alpha, int(rng.integers(1, 140)))) for _ in range(3000)]
+    words += [tb[t].decode() for t in range(256, len(tb)) if len(tb[t]) <= 140]
     for fam in FAMS:
         tok = tt.Tokenizer(merges, fam)
         data, offs = textgen.to_batch([" ".join(words[i:i + 7]) for i in range(0, len(words), 7)])
