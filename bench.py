@@ -44,7 +44,7 @@ LATENCY = ("c1_ec4k", "c2_at100k", "c3_mix1m", "c5_adv4m4")
 # (bytes of the pieces in the length range the launch serves)
 UNITS = {
     "init": "all", "summary": "all", "pieces": "all", "route": "all", "emit": "all", "gather_long": "binned",
-    "bpe_lane": "le16", "bpe_seg32": "17to32", "bpe_seg64": "33to64", "bpe_seg128": "65to128",
+    "bpe_small": "le128",
     "bpe_wave": "wave", "giant_seams": "giant", "bpe_block": "block", "bpe_giant": "giant", "giant_join": "giant",
 }
 
@@ -214,7 +214,7 @@ def main():
     plen = np.diff(starts.astype(np.int64))
     bins = {"all": int(n), "lane": int(plen[plen <= 64].sum()), "le16": int(plen[plen <= 16].sum()),
             "17to32": int(plen[(plen > 16) & (plen <= 32)].sum()), "33to64": int(plen[(plen > 32) & (plen <= 64)].sum()),
-            "65to128": int(plen[(plen > 64) & (plen <= 128)].sum()),
+            "65to128": int(plen[(plen > 64) & (plen <= 128)].sum()), "le128": int(plen[plen <= 128].sum()),
             "wave": int(plen[(plen > 128) & (plen <= 1024)].sum()),
             "block": int(plen[(plen > 1024) & (plen <= 4096)].sum()), "giant": int(plen[plen > 4096].sum()),
             "binned": int(plen[plen > 64].sum())}

@@ -101,8 +101,8 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t 
 // lane per piece (unresolved pieces of <= 16 bytes)
 
 template <int MAXL>
-__global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
-                                                  Layout L, int which)
+__device__ void bpe_lane(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
+                         int which, uint32_t blk, uint32_t nblk)
 {
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
@@ -113,9 +113,9 @@ __global__ __launch_bounds__(256) void k_bpe_lane(DevVocab v, const uint8_t *__r
     const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
     uint32_t *ccount = (uint32_t *)(ws + L.ccount);
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t stride = gridDim.x * blockDim.x;
+    const uint32_t stride = nblk * blockDim.x;
     // wavefront-uniform loop (the token-count update below is a wavefront operation)
-    for (uint32_t q0 = blockIdx.x * blockDim.x + (threadIdx.x & ~63u); q0 < count; q0 += stride) {
+    for (uint32_t q0 = blk * blockDim.x + (threadIdx.x & ~63u); q0 < count; q0 += stride) {
         const uint32_t q = q0 + lane;
         const bool active = q < count;
         const uint32_t e = active ? list[q] : 0u;
@@ -191,8 +191,8 @@ __device__ __forceinline__ uint32_t lane_push(uint32_t dst_lane, uint32_t x)
 }
 
 template <int G>
-__global__ __launch_bounds__(256) void k_bpe_seg(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
-                                                 Layout L, int which)
+__device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L, int which,
+                        uint32_t blk, uint32_t nblk)
 {
     static_assert(G == 16 || G == 32 || G == 64, "segment width");
     constexpr uint32_t SEGS = 64 / G;
@@ -206,8 +206,8 @@ __global__ __launch_bounds__(256) void k_bpe_seg(DevVocab v, const uint8_t *__re
     const uint32_t lane = threadIdx.x & 63u, seg = lane / G, k = lane % G, sbase = seg * G;
     const uint64_t segmask = G == 64 ? ~0ull : (((1ull << (G % 64)) - 1ull) << sbase);
     const uint64_t below = (1ull << lane) - 1ull;
-    const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const uint32_t nwaves = (gridDim.x * blockDim.x) >> 6;
+    const uint32_t wave = (blk * blockDim.x + threadIdx.x) >> 6;
+    const uint32_t nwaves = (nblk * blockDim.x) >> 6;
 
     const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
     uint32_t *ccount = (uint32_t *)(ws + L.ccount);
@@ -267,8 +267,8 @@ __device__ __forceinline__ void shl128(uint64_t lo, uint64_t hi, uint64_t &rlo, 
     rlo = lo << 1;
 }
 
-__global__ __launch_bounds__(256) void k_bpe_seg2(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
-                                                  Layout L)
+__device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
+                         uint32_t blk, uint32_t nblk)
 {
     constexpr uint64_t EVEN = 0x5555555555555555ull, ODD = ~EVEN;
     __shared__ uint32_t sid[4][2 * 64], srk[4][2 * 64];
@@ -282,8 +282,8 @@ __global__ __launch_bounds__(256) void k_bpe_seg2(DevVocab v, const uint8_t *__r
     const uint32_t count = ctrl->miss_count[3];
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
     const uint64_t below = (1ull << lane) - 1ull;
-    const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    const uint32_t nwaves = (gridDim.x * blockDim.x) >> 6;
+    const uint32_t wave = (blk * blockDim.x + threadIdx.x) >> 6;
+    const uint32_t nwaves = (nblk * blockDim.x) >> 6;
     for (uint32_t q = wave; q < count; q += nwaves) {
         const uint32_t e = list[q];
         const bool chunk = (e & CHUNK_ITEM) != 0;
@@ -352,6 +352,31 @@ __global__ __launch_bounds__(256) void k_bpe_seg2(DevVocab v, const uint8_t *__r
         }
         add_excess_wave(ws, L, p, lane == 0 && !chunk ? n - 1 : 0u);
     }
+}
+
+// The lists of short unresolved pieces are independent and each kernel above is bound by its
+// dependent table probes, so they run as one launch: the workgroups are split into four ranges, one
+// per list, and all four progress at the same time.
+__global__ __launch_bounds__(256) void k_bpe_small(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
+                                                   Layout L, uint32_t g16, uint32_t g32, uint32_t g64, uint32_t g128)
+{
+    uint32_t b = blockIdx.x;
+    if (b < g16) {
+        bpe_lane<16>(v, bytes, ws, L, 0, b, g16);
+        return;
+    }
+    b -= g16;
+    if (b < g32) {
+        bpe_seg<32>(v, bytes, ws, L, 1, b, g32);
+        return;
+    }
+    b -= g32;
+    if (b < g64) {
+        bpe_seg<64>(v, bytes, ws, L, 2, b, g64);
+        return;
+    }
+    b -= g64;
+    if (b < g128) bpe_seg2(v, bytes, ws, L, b, g128);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -946,56 +971,43 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
 {
     const Layout &L = b.L;
     if (b.n == 0) return hipGetLastError();
-    uint32_t g = (uint32_t)((b.n + 255) / 256);
     {
         // giant pieces: safe-seam bitmap, then chunks (before the other BPE kernels, which also
         // encode the chunks)
-        LaunchScope k(ev, 9, s);
+        LaunchScope k(ev, 4, s);
         const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
         hipLaunchKernelGGL(k_gsafe, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
         const uint32_t gc = L.cap_giant < 64 ? L.cap_giant : 64;
         hipLaunchKernelGGL(k_gcut, dim3(gc), dim3(1024), 0, s, v, b.ws, L);
     }
     {
-        LaunchScope k(ev, 4, s);
-        hipLaunchKernelGGL((k_bpe_lane<16>), dim3(g > 2048 ? 2048 : g), dim3(256), 0, s, v, b.bytes, b.ws, L, 0);
-    }
-    // at most n / 17 pieces of 17..32 bytes (8 per workgroup), n / 33 of 33..64 (4 per workgroup)
-    const uint64_t g32 = b.n / 17 / 8 + 1, g64 = b.n / 33 / 4 + 1;
-    {
+        // lists of <= 16, 17..32, 33..64 and 65..128 bytes: at most n / 1, n / 17, n / 33, n / 65 items;
+        // 256 lane items, 8, 4 and 4 pieces per workgroup
+        const uint64_t b16 = b.n / 256 + 1, b32 = b.n / 17 / 8 + 1, b64 = b.n / 33 / 4 + 1, b128 = b.n / 65 / 4 + 1;
+        const uint32_t g16 = b16 > 2048 ? 2048u : (uint32_t)b16, g32 = b32 > 2048 ? 2048u : (uint32_t)b32;
+        const uint32_t g64 = b64 > 1024 ? 1024u : (uint32_t)b64, g128 = b128 > 1024 ? 1024u : (uint32_t)b128;
         LaunchScope k(ev, 5, s);
-        hipLaunchKernelGGL((k_bpe_seg<32>), dim3(g32 > 2048 ? 2048 : (uint32_t)g32), dim3(256), 0, s, v, b.bytes,
-                           b.ws, L, 1);
+        hipLaunchKernelGGL(k_bpe_small, dim3(g16 + g32 + g64 + g128), dim3(256), 0, s, v, b.bytes, b.ws, L, g16, g32,
+                           g64, g128);
     }
     {
         LaunchScope k(ev, 6, s);
-        hipLaunchKernelGGL((k_bpe_seg<64>), dim3(g64 > 1024 ? 1024 : (uint32_t)g64), dim3(256), 0, s, v, b.bytes,
-                           b.ws, L, 2);
-    }
-    {
-        LaunchScope k(ev, 7, s);
-        const uint64_t g128 = b.n / 65 / 4 + 1;
-        hipLaunchKernelGGL(k_bpe_seg2, dim3(g128 > 1024 ? 1024 : (uint32_t)g128), dim3(256), 0, s, v, b.bytes, b.ws,
-                           L);
-    }
-    {
-        LaunchScope k(ev, 8, s);
         uint32_t gw = L.cap_wave + L.cap_chunks < 1024 ? L.cap_wave + L.cap_chunks : 1024;
         hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
     }
     const uint32_t gg = L.cap_giant < 64 ? L.cap_giant : 64;
     {
-        LaunchScope k(ev, 10, s);
+        LaunchScope k(ev, 7, s);
         uint32_t gb = L.cap_block + L.cap_chunks < 256 ? L.cap_block + L.cap_chunks : 256;
         hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v,
                            b.bytes, b.ws, L, 1);
     }
     {
-        LaunchScope k(ev, 11, s);
+        LaunchScope k(ev, 8, s);
         hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
     }
     {
-        LaunchScope k(ev, 12, s);
+        LaunchScope k(ev, 9, s);
         hipLaunchKernelGGL(k_gassemble, dim3(gg), dim3(1024), 0, s, b.ws, L);
     }
     return hipGetLastError();
