@@ -67,7 +67,7 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t 
         const uint32_t b0 = vb ? pstart[pb] : 0u, b1 = vb ? pstart[pb + 1] : 0u;
         const uint32_t la = a1 - a0, lb = b1 - b0;
         WPQ qa = wp_make(v, bytes + a0, la), qb = wp_make(v, bytes + b0, lb);
-        uint32_t ida = va && la == 1 ? (uint32_t)bytes[a0] : 0u, idb = vb && lb == 1 ? (uint32_t)bytes[b0] : 0u;
+        uint32_t ida = (uint32_t)qa.k0 & 0xFFu, idb = (uint32_t)qb.k0 & 0xFFu;   // single bytes
         uint32_t sa = qa.kind ? WP_MORE : (la == 1 ? WP_HIT : WP_MISS);
         uint32_t sb = qb.kind ? WP_MORE : (lb == 1 ? WP_HIT : WP_MISS);
         while (sa == WP_MORE || sb == WP_MORE) {
@@ -124,8 +124,10 @@ __device__ void bpe_lane(const DevVocab &v, const uint8_t *__restrict__ bytes, u
         const uint32_t b0 = !active ? 0u : chunk ? cstart[p] : pstart[p];
         const uint32_t len = !active ? 0u : chunk ? clen[p] : pstart[p + 1] - b0;   // 0: nothing to do
         uint32_t id[MAXL], rk[MAXL];
+        uint64_t w[(MAXL + 7) / 8];
+        load_words<(MAXL + 7) / 8>(bytes + b0, len, w);
 #pragma unroll
-        for (int k = 0; k < MAXL; ++k) id[k] = (uint32_t)k < len ? (uint32_t)bytes[b0 + k] : 0u;
+        for (int k = 0; k < MAXL; ++k) id[k] = (uint32_t)(w[k >> 3] >> (8 * (k & 7))) & 0xFFu;
 #pragma unroll
         for (int k = 0; k < MAXL; ++k)
             rk[k] = (uint32_t)(k + 1) < len ? __ldg(v.r2 + ((id[k] << 8) | id[(k + 1) % MAXL])) : NO_RANK;

@@ -290,42 +290,24 @@ inline Layout make_layout(uint64_t n)
 // tables hold exactly the tokens t whose own byte string encodes to [t] (established at load time
 // by these same kernels), so a hit is the exact BPE result.
 
-__device__ __forceinline__ bool whole_piece(const DevVocab &v, const uint8_t *__restrict__ src, uint32_t len,
-                                            uint32_t *id)
+// Bytes src[0, len) as little-endian 64-bit words k[0..NW), zero past len (len <= 8 * NW).  The
+// words are assembled from aligned 8-byte loads: NW + 1 load instructions per wavefront instead of
+// one byte gather per byte.  Only aligned words that hold at least one byte of src[0, len) are read,
+// and such a word never leaves the page of that byte; the neighbouring bytes it brings are masked.
+template <int NW>
+__device__ __forceinline__ void load_words(const uint8_t *src, uint32_t len, uint64_t (&k)[NW])
 {
-    if (len <= WA_MAX) {
-        if (!v.wa) return false;
-        uint64_t key = (uint64_t)len << 56;
+    const uintptr_t p = (uintptr_t)src;
+    const uint64_t *al = (const uint64_t *)(p & ~(uintptr_t)7);
+    const uint32_t off = (uint32_t)(p & 7u), sh = 8u * off;
+    uint64_t w[NW + 1];
 #pragma unroll
-        for (uint32_t k = 0; k < WA_MAX; ++k)
-            if (k < len) key |= (uint64_t)src[k] << (8 * k);
-        uint32_t h = (uint32_t)wa_hash(key, v.wa_shift);
-        for (;;) {
-            const uint4 sl = v.wa[h];
-            const uint64_t sk = (uint64_t)sl.x | ((uint64_t)sl.y << 32);
-            if (sk == key) { *id = sl.z; return true; }
-            if (sk == 0) return false;
-            h = (h + 1) & v.wa_mask;
-        }
-    }
-    if (!v.wb) return false;
-    uint64_t k4[4] = {0, 0, 0, 0};
+    for (int i = 0; i <= NW; ++i) w[i] = 8u * i < off + len ? al[i] : 0ull;
 #pragma unroll
-    for (uint32_t k = 0; k < (uint32_t)TABLE_MAX; ++k)
-        if (k < len) k4[k >> 3] |= (uint64_t)src[k] << (8 * (k & 7));
-    uint32_t h = (uint32_t)wb_hash(k4[0], k4[1], k4[2], k4[3], len, v.wb_shift);
-    for (;;) {
-        const uint4 c = v.wb[3 * h + 2];
-        if (c.x == 0) return false;
-        if (c.x == len) {
-            const uint4 a = v.wb[3 * h], b = v.wb[3 * h + 1];
-            if (((uint64_t)a.x | ((uint64_t)a.y << 32)) == k4[0] && ((uint64_t)a.z | ((uint64_t)a.w << 32)) == k4[1] &&
-                ((uint64_t)b.x | ((uint64_t)b.y << 32)) == k4[2] && ((uint64_t)b.z | ((uint64_t)b.w << 32)) == k4[3]) {
-                *id = c.y;
-                return true;
-            }
-        }
-        h = (h + 1) & v.wb_mask;
+    for (int i = 0; i < NW; ++i) {
+        const uint64_t x = sh ? (w[i] >> sh) | (w[i + 1] << (64u - sh)) : w[i];
+        const uint32_t rem = len > 8u * i ? len - 8u * i : 0u;
+        k[i] = rem >= 8u ? x : (x & ((1ull << (8u * rem)) - 1ull));
     }
 }
 
@@ -338,26 +320,24 @@ struct WPQ {
     uint32_t len, h, kind;   // kind 0: no table applies, 1: short table, 2: long table
 };
 
+// (for len 1, q.k0 is the piece's byte, which is its token ID)
 __device__ __forceinline__ WPQ wp_make(const DevVocab &v, const uint8_t *__restrict__ src, uint32_t len)
 {
     WPQ q{0, 0, 0, 0, len, 0, 0};
-    if (len < 2 || len > (uint32_t)TABLE_MAX) return q;
+    if (len == 0 || len > (uint32_t)TABLE_MAX) return q;
     if (len <= WA_MAX) {
-        if (!v.wa) return q;
-        uint64_t key = (uint64_t)len << 56;
-#pragma unroll
-        for (uint32_t k = 0; k < WA_MAX; ++k)
-            if (k < len) key |= (uint64_t)src[k] << (8 * k);
-        q.k0 = key;
-        q.h = (uint32_t)wa_hash(key, v.wa_shift);
+        uint64_t k[1];
+        load_words<1>(src, len, k);
+        q.k0 = k[0];
+        if (len == 1 || !v.wa) return q;
+        q.k0 |= (uint64_t)len << 56;
+        q.h = (uint32_t)wa_hash(q.k0, v.wa_shift);
         q.kind = 1;
         return q;
     }
     if (!v.wb) return q;
-    uint64_t k4[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (uint32_t k = 0; k < (uint32_t)TABLE_MAX; ++k)
-        if (k < len) k4[k >> 3] |= (uint64_t)src[k] << (8 * (k & 7));
+    uint64_t k4[4];
+    load_words<4>(src, len, k4);
     q.k0 = k4[0]; q.k1 = k4[1]; q.k2 = k4[2]; q.k3 = k4[3];
     q.h = (uint32_t)wb_hash(k4[0], k4[1], k4[2], k4[3], len, v.wb_shift);
     q.kind = 2;
