@@ -31,10 +31,11 @@ constexpr uint32_t PENDING = 0xFFFFFFFEu;
 
 // k_route: every piece.  Single bytes and whole-piece table hits get their result word here; the
 // others are listed for BPE by length.  Each workgroup owns a contiguous range of pieces and keeps
-// two pieces per thread in flight (their loads and table probes overlap).  List entries are queued
+// RT_PPT pieces per thread in flight (their loads and table probes overlap).  List entries are queued
 // in LDS and flushed with one reservation atomic per list at the end (a full queue spills straight
 // to the global list).
 constexpr int RT_THREADS = 512;
+constexpr int RT_PPT = 2;   // pieces per thread in flight (more costs occupancy: slower)
 constexpr uint32_t RTQ[NROUTES] = {2048, 512, 256, 128, 64, 64, 64};
 constexpr uint32_t RTQ_OFF[NROUTES + 1] = {0, 2048, 2560, 2816, 2944, 3008, 3072, 3136};
 
@@ -60,27 +61,36 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t 
         if (slot < RTQ[r]) q[RTQ_OFF[r] + slot] = p;
         else route_list(ws, L, r)[atomicAdd(route_count(ctrl, r), 1u)] = p;
     };
-    for (uint32_t p0 = start; p0 < end; p0 += 2 * RT_THREADS) {
-        const uint32_t pa = p0 + tid, pb = p0 + RT_THREADS + tid;
-        const bool va = pa < end, vb = pb < end;
-        const uint32_t a0 = va ? pstart[pa] : 0u, a1 = va ? pstart[pa + 1] : 0u;
-        const uint32_t b0 = vb ? pstart[pb] : 0u, b1 = vb ? pstart[pb + 1] : 0u;
-        const uint32_t la = a1 - a0, lb = b1 - b0;
-        WPQ qa = wp_make(v, bytes + a0, la), qb = wp_make(v, bytes + b0, lb);
-        uint32_t ida = (uint32_t)qa.k0 & 0xFFu, idb = (uint32_t)qb.k0 & 0xFFu;   // single bytes
-        uint32_t sa = qa.kind ? WP_MORE : (la == 1 ? WP_HIT : WP_MISS);
-        uint32_t sb = qb.kind ? WP_MORE : (lb == 1 ? WP_HIT : WP_MISS);
-        while (sa == WP_MORE || sb == WP_MORE) {
-            if (sa == WP_MORE) sa = wp_step(v, qa, &ida);
-            if (sb == WP_MORE) sb = wp_step(v, qb, &idb);
+    for (uint32_t p0 = start; p0 < end; p0 += RT_PPT * RT_THREADS) {
+        uint32_t pp[RT_PPT], a0[RT_PPT], len[RT_PPT], id[RT_PPT], st[RT_PPT];
+        WPQ q[RT_PPT];
+#pragma unroll
+        for (int u = 0; u < RT_PPT; ++u) {
+            pp[u] = p0 + u * RT_THREADS + tid;
+            const bool ok = pp[u] < end;
+            a0[u] = ok ? pstart[pp[u]] : 0u;
+            len[u] = ok ? pstart[pp[u] + 1] - a0[u] : 0u;
         }
-        if (va) {
-            if (sa == WP_HIT) pval[pa] = ida;
-            else list_piece(pa, la);
+#pragma unroll
+        for (int u = 0; u < RT_PPT; ++u) {
+            q[u] = wp_make(v, bytes + a0[u], len[u]);
+            id[u] = (uint32_t)q[u].k0 & 0xFFu;   // single bytes
+            st[u] = q[u].kind ? WP_MORE : (len[u] == 1 ? WP_HIT : WP_MISS);
         }
-        if (vb) {
-            if (sb == WP_HIT) pval[pb] = idb;
-            else list_piece(pb, lb);
+        for (;;) {
+            bool more = false;
+#pragma unroll
+            for (int u = 0; u < RT_PPT; ++u) {
+                if (st[u] == WP_MORE) st[u] = wp_step(v, q[u], &id[u]);
+                more |= st[u] == WP_MORE;
+            }
+            if (!more) break;
+        }
+#pragma unroll
+        for (int u = 0; u < RT_PPT; ++u) {
+            if (pp[u] >= end) continue;
+            if (st[u] == WP_HIT) pval[pp[u]] = id[u];
+            else list_piece(pp[u], len[u]);
         }
     }
     __syncthreads();

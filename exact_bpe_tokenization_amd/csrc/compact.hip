@@ -37,30 +37,40 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
     const bool last = end == np;
 
     // wavefront wid owns pieces [wb, wb + 64 * IT) of the tile, 64 consecutive pieces per iteration
-    // (lane-consecutive: coalesced loads and stores)
+    // (lane-consecutive: coalesced loads and stores).  Only the result words stay in registers; the
+    // token offsets go through LDS (few registers, so every tile of a large batch is resident at once).
     const uint32_t wb = first + wid * (64u * IT);
-    uint32_t c[IT], pv[IT], ex[IT];
+    uint32_t pv[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const uint32_t i = wb + it * 64u + lane;
         pv[it] = i < end ? pval[i] : 0u;
-        c[it] = i >= end ? 0u : (pv[it] & PV_MULTI) ? (pv[it] & PV_COUNT) : 1u;
     }
-    // tokens before this tile: one per piece plus the excess counted by the BPE kernels
+    // tokens before this tile: one per piece plus the excess counted by the BPE kernels (16-byte reads)
     uint32_t xs = 0;
-    for (uint32_t t = tid; t < tile; t += SCAN_THREADS) xs += tilex[t];
+    {
+        const uint32_t nq = tile / 4u;
+        const uint4 *tx4 = (const uint4 *)tilex;
+        for (uint32_t t = tid; t < nq; t += SCAN_THREADS) {
+            const uint4 x = tx4[t];
+            xs += x.x + x.y + x.z + x.w;
+        }
+        if (tid < tile - 4u * nq) xs += tilex[4u * nq + tid];
+    }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) xs += __shfl_xor(xs, d, 64);
     uint32_t run = 0;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        uint32_t inc = c[it];
+        const uint32_t i = wb + it * 64u + lane;
+        const uint32_t c = i >= end ? 0u : (pv[it] & PV_MULTI) ? (pv[it] & PV_COUNT) : 1u;
+        uint32_t inc = c;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const uint32_t y = __shfl_up(inc, d, 64);
             if (lane >= (uint32_t)d) inc += y;
         }
-        ex[it] = run + inc - c[it];
+        soff[wid * (64u * IT) + it * 64u + lane] = run + inc - c;   // offset inside the wavefront's run
         run += __shfl(inc, 63, 64);
     }
     if (lane == 0) { swsum[wid] = run; sxs[wid] = xs; }
@@ -77,32 +87,41 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
 
     // IDs: a single-token piece's ID is its result word (coalesced); a short multi-token piece's IDs
     // are at scratch[its start byte ...]; a long piece gets its output offset for k_gather_long.
-    // The loads of every iteration are issued before any store.
-    uint32_t st[IT], f0[IT];
+    // Two halves of IT / 2 iterations; in each, all loads are issued before any store.
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const uint32_t i = wb + it * 64u + lane;
-        const bool multi = i < end && (pv[it] & (PV_MULTI | PV_LONG)) == PV_MULTI;
-        st[it] = multi ? pstart[i] : 0u;
-    }
+    for (int h = 0; h < 2; ++h) {
+        constexpr int HI = IT / 2;
+        uint32_t st[HI], f0[HI];
 #pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const uint32_t i = wb + it * 64u + lane;
-        const bool multi = i < end && (pv[it] & (PV_MULTI | PV_LONG)) == PV_MULTI;
-        f0[it] = multi ? scratch[st[it]] : pv[it];
-    }
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const uint32_t i = wb + it * 64u + lane;
-        if (i >= end) continue;
-        const uint32_t o = obase + ex[it], v = pv[it];
-        soff[i - first] = o;
-        if ((v & (PV_MULTI | PV_LONG)) == (PV_MULTI | PV_LONG)) {
-            tokoff[i] = o;
-            continue;
+        for (int u = 0; u < HI; ++u) {
+            const int it = h * HI + u;
+            const uint32_t i = wb + it * 64u + lane;
+            const bool multi = i < end && (pv[it] & (PV_MULTI | PV_LONG)) == PV_MULTI;
+            st[u] = multi ? pstart[i] : 0u;
         }
-        out_ids[o] = f0[it];
-        for (uint32_t j = 1; j < c[it]; ++j) out_ids[o + j] = scratch[st[it] + j];
+#pragma unroll
+        for (int u = 0; u < HI; ++u) {
+            const int it = h * HI + u;
+            const uint32_t i = wb + it * 64u + lane;
+            const bool multi = i < end && (pv[it] & (PV_MULTI | PV_LONG)) == PV_MULTI;
+            f0[u] = multi ? scratch[st[u]] : pv[it];
+        }
+#pragma unroll
+        for (int u = 0; u < HI; ++u) {
+            const int it = h * HI + u;
+            const uint32_t i = wb + it * 64u + lane;
+            if (i >= end) continue;
+            const uint32_t li = wid * (64u * IT) + it * 64u + lane;
+            const uint32_t o = obase + soff[li], v = pv[it];
+            soff[li] = o;
+            if ((v & (PV_MULTI | PV_LONG)) == (PV_MULTI | PV_LONG)) {
+                tokoff[i] = o;
+                continue;
+            }
+            out_ids[o] = f0[u];
+            const uint32_t c = (v & PV_MULTI) ? (v & PV_COUNT) : 1u;
+            for (uint32_t j = 1; j < c; ++j) out_ids[o + j] = scratch[st[u] + j];
+        }
     }
     if (tid == 0) soff[end - first] = tbase + total;
 
