@@ -368,8 +368,10 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
 
 // The lists of short unresolved pieces are independent and each kernel above is bound by its
 // dependent table probes, so they run as one launch: the workgroups are split into four ranges, one
-// per list, and all four progress at the same time.
-__global__ __launch_bounds__(256) void k_bpe_small(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
+// per list, and all four progress at the same time.  Register use is capped at six wavefronts per
+// SIMD (no spills): more resident workgroups hide more probe latency than the lane role's longer
+// register lifetimes cost.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_bpe_small(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
                                                    Layout L, uint32_t g16, uint32_t g32, uint32_t g64, uint32_t g128)
 {
     uint32_t b = blockIdx.x;
