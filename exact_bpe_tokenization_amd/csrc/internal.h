@@ -59,6 +59,8 @@ constexpr uint32_t NO_RANK = 0xFFFFFFFFu;
 constexpr uint64_t EMPTY_SLOT = ~0ull;
 constexpr uint32_t PAIR_BUCKET_LOG2 = 3, PAIR_BUCKET = 1u << PAIR_BUCKET_LOG2;   // 8 slots = 64 bytes
 
+constexpr int FAMILY_GPT2 = 1, FAMILY_O200K = 3;   // the family codes of the public header
+
 struct DevVocab {
     const uint32_t *r2;       // 65536 byte-pair ranks
     const uint64_t *slots;    // pair hash: buckets of 8 slots, a full bucket continues in the next

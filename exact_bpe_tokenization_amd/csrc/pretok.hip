@@ -384,6 +384,25 @@ __device__ __forceinline__ uint32_t reg_byte_code(const uint32_t (&rw)[6], uint3
 // ---------------------------------------------------------------------------------------------
 // k_pieces: dynamic tile ids; decode, automaton context, scans, look-backs, piece starts
 
+// A backward flag of all 16 characters of a chunk at once.  Bit k of D: character k decides the
+// flag (bit k of T: its value); other positions pass on the value of the position after them, and
+// position 16 holds `carry`.  The result's bit k is the value of the first deciding position j >= k.
+// On the bit-reversed masks the value moves upward through each run of pass-through positions; an
+// addition carries it across the run.
+__device__ __forceinline__ uint32_t fill_down16(uint32_t T, uint32_t D, uint32_t carry)
+{
+    const uint32_t Pr = __builtin_bitreverse32(~D & 0xFFFFu) >> 16, Tr = __builtin_bitreverse32(T) >> 16;
+    const uint32_t s = ((Tr << 1) | carry) & Pr;
+    const uint32_t filled = ((Pr + s) ^ Pr) & Pr;
+    return __builtin_bitreverse32(Tr | filled) >> 16;
+}
+
+// first deciding value of a chunk from the left (the chunk's summary for the right-to-left scan)
+__device__ __forceinline__ uint32_t first_decided(uint32_t T, uint32_t D)
+{
+    return D ? (((T >> (__ffs(D) - 1)) & 1u) ? (uint32_t)BK_T : (uint32_t)BK_F) : (uint32_t)BK_KEEP;
+}
+
 // self code of a character (13 values) from its byte code and its NA flag, without branches:
 // LU 0, LL 1, LO 2, N 3, M 4, other 5 (6, 7 with a one- or two-letter contraction after an
 // apostrophe), whitespace 8 + 2 (space) + 1 (NA), CR/LF 12
@@ -420,6 +439,9 @@ __device__ __forceinline__ uint32_t contraction_code(const uint8_t *sraw, DocBit
     return 0;
 }
 
+// CASE: the family has the case-boundary letter rule (the only one that reads the AU flag; for the
+// others the flag changes no transition between reachable states and is left at zero).
+template <bool CASE>
 __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes,
                                                         const uint64_t *__restrict__ offsets, uint32_t n_docs,
                                                         uint64_t n, uint8_t *ws, Layout L)
@@ -431,7 +453,9 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     __shared__ __align__(16) uint8_t scc[TILE + HALO];
     __shared__ uint16_t spiece[TILE];
     __shared__ uint4 smap16[NCTX + 1];          // [NCTX]: identity (continuation bytes)
-    __shared__ uint8_t sasc[128];               // byte code of each ASCII character (no doc bit)
+    __shared__ uint16_t sasc[128];              // ASCII character: byte code (no doc bit) | W, LU, LL bits 8-10
+    __shared__ uint16_t sctxa[256];             // byte code -> its part of the context (0xFFFF: not a character)
+    __shared__ uint8_t sctxb[256];              // next character's byte code -> its part of the context
     __shared__ uint32_t sbkw[NW];
     __shared__ uint4 swmap[NW];
     __shared__ uint32_t swcnt[NW], swstate[NW];
@@ -447,8 +471,20 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     if (tid == 0) s_tile = atomicAdd(&ctrl->tile_ctr_pre, 1u);
     for (int i = tid; i < NCTX; i += PRE_THREADS) smap16[i] = v.fmap16[i];
     if (tid == 0) smap16[NCTX] = make_uint4(0x03020100u, 0x07060504u, 0x0B0A0908u, 0x0F0E0D0Cu);
-    if (tid < 128)
-        sasc[tid] = (uint8_t)(ucat(tid) | ((tid == '\r' || tid == '\n') ? CC_CRLF : 0u) | (tid == ' ' ? CC_SP : 0u));
+    if (tid < 128) {
+        const uint32_t cat = ucat(tid);
+        sasc[tid] = (uint16_t)(cat | ((tid == '\r' || tid == '\n') ? CC_CRLF : 0u) | (tid == ' ' ? CC_SP : 0u) |
+                               (cat == CAT_W ? 0x100u : 0u) | (cat == CAT_LU ? 0x200u : 0u) |
+                               (cat == CAT_LL ? 0x400u : 0u));
+    }
+    if (tid < 256) {
+        // context = ((self * 2 + doc) * NNEXT + next) * 2 + au: the self / doc part (self code with
+        // NA clear) and the next-character part (end of document or batch: 5)
+        sctxa[tid] = (tid & 7u) == CAT_CONT ? (uint16_t)0xFFFFu
+                                             : (uint16_t)(self_code(tid, false) * (4u * NNEXT) +
+                                                          ((tid & CC_DOC) ? 2u * NNEXT : 0u));
+        sctxb[tid] = (uint8_t)(2u * next_code(tid));
+    }
     for (int j = tid; j < (SPAN + 31) / 32; j += PRE_THREADS) sdoc[j] = 0;
     __syncthreads();
     const uint32_t tile = s_tile;
@@ -456,11 +492,21 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     const int64_t base = (int64_t)lo - RAW_LEAD;
 
     // raw bytes [lo - 4, lo + TILE + 24), as 32-bit words
+    // (interior words from two aligned 4-byte loads, which never leave the pages of the bytes they
+    // hold; the words at the batch edges byte by byte)
     for (int j = tid; j < SPAN / 4; j += PRE_THREADS) {
         const int64_t p = base + 4 * j;
         uint32_t w = 0;
-        for (int t = 0; t < 4; ++t)
-            if (p + t >= 0 && (uint64_t)(p + t) < n) w |= (uint32_t)bytes[p + t] << (8 * t);
+        if (p >= 0 && (uint64_t)p + 4 <= n) {
+            const uintptr_t a = (uintptr_t)(bytes + p);
+            const uint32_t *al = (const uint32_t *)(a & ~(uintptr_t)3);
+            const uint32_t sh = 8u * (uint32_t)(a & 3u);
+            const uint32_t w0 = al[0];
+            w = sh ? __builtin_amdgcn_alignbyte(al[1], w0, sh >> 3) : w0;
+        } else {
+            for (int t = 0; t < 4; ++t)
+                if (p + t >= 0 && (uint64_t)(p + t) < n) w |= (uint32_t)bytes[p + t] << (8 * t);
+        }
         ((uint32_t *)sraw)[j] = w;
     }
     if (wid == 0) {
@@ -483,8 +529,15 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     __syncthreads();
     auto docbit = [&](int j) -> bool { return (sdoc[j >> 5] >> (j & 31)) & 1u; };
 
-    // per-byte codes of the tile (validated) and of the halo after it
+    // per-byte codes of the tile (validated) and of the halo after it.  A wavefront whose bytes are
+    // all ASCII also records per-chunk masks (bit k: byte k of the chunk) for the fast path below.
     const int c0 = tid * PRE_CHUNK;
+    const uint64_t pos0 = lo + (uint64_t)c0;
+    // bytes 0..16 of the chunk at or past the end of the batch
+    const uint32_t rem = pos0 >= n ? 0u : (n - pos0 > 17u ? 17u : (uint32_t)(n - pos0));
+    const uint32_t xeof = (0x1FFFFu << rem) & 0x1FFFFu;
+    uint32_t dm = 0, mW = 0, mC = 0, mU = 0, mL = 0;
+    bool ascii = false;
     {
         bool bad = false;
         // window: sraw[c0 .. c0 + 24) = positions lo + c0 - 4 ...; 16-byte aligned LDS reads
@@ -493,19 +546,27 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
         const uint2 r1 = *(const uint2 *)(sraw + c0 + 16);
         const uint32_t rw[6] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y};
         const uint32_t dw = (uint32_t)c0 >> 5;
-        const uint32_t dm = (uint32_t)((((uint64_t)sdoc[dw + 1] << 32) | sdoc[dw]) >> (c0 & 31));
+        dm = (uint32_t)((((uint64_t)sdoc[dw + 1] << 32) | sdoc[dw]) >> (c0 & 31));
         uint32_t w[PRE_CHUNK / 4] = {0, 0, 0, 0};
         const uint32_t hibits = (rw[0] | rw[1] | rw[2] | rw[3] | rw[4] | rw[5]) & 0x80808080u;
-        if (__ballot(hibits != 0) == 0) {
+        ascii = __ballot(hibits != 0) == 0;
+        if (ascii) {
             // every byte the wavefront looks at is ASCII: a table lookup per byte, apostrophes apart
             uint32_t apos = 0;
 #pragma unroll
             for (int k = 0; k < PRE_CHUNK; ++k) {
-                const uint64_t p = lo + c0 + k;
                 const uint32_t c = wbyte(rw, k + RAW_LEAD);
-                const uint32_t code = (uint32_t)sasc[c] | (((dm >> (k + RAW_LEAD)) & 1u) ? CC_DOC : 0u);
-                apos |= (c == '\'' && p < n ? 1u : 0u) << k;
-                w[k >> 2] |= (p < n ? code : (uint32_t)CC_EOF) << (8 * (k & 3));
+                const uint32_t f = sasc[c];
+                const uint32_t code = (f & 0xFFu) | (((dm >> (k + RAW_LEAD)) & 1u) ? CC_DOC : 0u);
+                const bool eof = (xeof >> k) & 1u;
+                apos |= (c == '\'' && !eof ? 1u : 0u) << k;
+                w[k >> 2] |= (eof ? (uint32_t)CC_EOF : code) << (8 * (k & 3));
+                mW |= ((f >> 8) & 1u) << k;
+                mC |= ((f >> 3) & 1u) << k;
+                if (CASE) {
+                    mU |= ((f >> 9) & 1u) << k;
+                    mL |= ((f >> 10) & 1u) << k;
+                }
             }
             while (apos) {
                 const int k = __ffs(apos) - 1;
@@ -565,6 +626,24 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     auto code_at = [&](int k) -> uint32_t { return (cw[k >> 2] >> (8 * (k & 3))) & 255u; };
     uint32_t pk_bna = 0, pk_bau = 0, pk_nx[2] = {0, 0};
     uint32_t agg = BK_KEEP | (BK_KEEP << 2);
+    // ASCII fast path: every byte is a character and the next character is the next byte.  NA is
+    // decided by a non-whitespace character (true), a CR/LF (false) or whitespace followed by the
+    // end of its document (true); AU by a non-letter (true), a lowercase letter (false) or an
+    // uppercase letter followed by the end of its document (true).  Other positions pass the value on.
+    uint32_t tna = 0, dna = 0, tau = 0, dau = 0;
+    if (ascii) {
+        const uint32_t isch = ~xeof & 0xFFFFu;
+        const uint32_t en = ((dm >> (RAW_LEAD + 1)) | (xeof >> 1)) & 0xFFFFu;   // next char starts a document / ends the batch
+        const uint32_t ws_ = mW & isch, crlf = mC & isch;
+        tna = (isch & ~ws_) | (ws_ & ~crlf & en);
+        dna = tna | crlf;
+        if (CASE) {
+            const uint32_t up = mU & isch, low = mL & isch;
+            tau = (isch & ~(up | low)) | (up & en);
+            dau = tau | low;
+        }
+        agg = first_decided(tna, dna) | (first_decided(tau, dau) << 2);
+    } else {
 #pragma unroll
     for (int k = 0; k < PRE_CHUNK; ++k) {
         // next char: first non-continuation byte after k (within 4 bytes for valid UTF-8)
@@ -578,12 +657,13 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
         uint32_t na, au;
         backward_maps(ck, en, na, au);
         na = isch ? na : (uint32_t)BK_KEEP;   // continuation bytes pass the flags through
-        au = isch ? au : (uint32_t)BK_KEEP;
+        au = isch && CASE ? au : (uint32_t)BK_KEEP;
         pk_bna |= na << (2 * k);
         pk_bau |= au << (2 * k);
         pk_nx[k >> 3] |= (en ? 5u : next_code(nc)) << (4 * (k & 7));
         if ((agg & 3u) == BK_KEEP) agg = (agg & ~3u) | na;
         if ((agg >> 2) == BK_KEEP) agg = (agg & 3u) | (au << 2);
+    }
     }
     // value entering each chunk from its right: the first chunk to the right whose flag is decided
     // (suffix scan over the wavefront, then the wavefronts to the right, then the tile carry)
@@ -610,9 +690,26 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     // per character) and the chunk's map, composed from the right
     uint32_t pk_ctx[PRE_CHUNK / 2] = {0, 0, 0, 0, 0, 0, 0, 0};
     M16 acc = m16_identity();
+    if (ascii) {
+        // the context from two table entries (this byte's code, the next byte's code) plus the two
+        // flags; past the end of the batch the table entry saturates it to the identity map
+        const uint32_t naw = fill_down16(tna, dna, na_val) & mW & ~mC;   // whitespace (not CR/LF) with NA set
+        uint32_t aun = 0;
+        if (CASE) aun = (fill_down16(tau, dau, au_val) >> 1) | (au_val << 15);   // AU of the next character
+#pragma unroll
+        for (int k = PRE_CHUNK - 1; k >= 0; --k) {
+            uint32_t ctx = (uint32_t)sctxa[code_at(k)] + (uint32_t)sctxb[code_at(k + 1)] + 4u * NNEXT * ((naw >> k) & 1u);
+            if (CASE) ctx += (aun >> k) & 1u;
+            ctx = min(ctx, (uint32_t)NCTX);
+            pk_ctx[k >> 1] |= ctx << (16 * (k & 1));
+            const uint4 m = smap16[ctx];
+            acc = compose16(M16{{m.x, m.y, m.z, m.w}}, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
 #pragma unroll
     for (int k = PRE_CHUNK - 1; k >= 0; --k) {
-        const uint32_t au_next = au_val;            // AU of the next character
+        const uint32_t au_next = CASE ? au_val : 0u;   // AU of the next character
         const uint32_t bn = (pk_bna >> (2 * k)) & 3u, bu = (pk_bau >> (2 * k)) & 3u;
         if (bn != BK_KEEP) na_val = bn & 1u;
         if (bu != BK_KEEP) au_val = bu & 1u;
@@ -627,6 +724,7 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
         const uint4 m = smap16[ctx];
         acc = compose16(M16{{m.x, m.y, m.z, m.w}}, acc);
         __builtin_amdgcn_sched_barrier(0);   // one map load in flight: keeps register use low
+    }
     }
 
     // wavefront scan of the chunk maps; the wavefronts' maps are scanned by wave 0, which also
@@ -731,8 +829,12 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
     }
     {
         LaunchScope k(ev, 2, s);
-        hipLaunchKernelGGL(k_pieces, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs,
-                           b.n, b.ws, L);
+        if (v.family == FAMILY_O200K)
+            hipLaunchKernelGGL(k_pieces<true>, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets,
+                               b.n_docs, b.n, b.ws, L);
+        else
+            hipLaunchKernelGGL(k_pieces<false>, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets,
+                               b.n_docs, b.n, b.ws, L);
     }
     return hipGetLastError();
 }

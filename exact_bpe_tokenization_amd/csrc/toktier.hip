@@ -11,6 +11,8 @@
 
 #include "../../include/toktier.h"
 #include "internal.h"
+
+static_assert(tt::FAMILY_GPT2 == TOKTIER_GPT2 && tt::FAMILY_O200K == TOKTIER_O200K, "family codes");
 #include "unicode_table.inc"
 
 using namespace tt;
