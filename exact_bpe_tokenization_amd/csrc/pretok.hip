@@ -483,7 +483,7 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
         sctxa[tid] = (tid & 7u) == CAT_CONT ? (uint16_t)0xFFFFu
                                              : (uint16_t)(self_code(tid, false) * (4u * NNEXT) +
                                                           ((tid & CC_DOC) ? 2u * NNEXT : 0u));
-        sctxb[tid] = (uint8_t)(2u * next_code(tid));
+        sctxb[tid] = (uint8_t)((tid & 7u) == CAT_CONT ? 2u * 5u : 2u * next_code(tid));
     }
     for (int j = tid; j < (SPAN + 31) / 32; j += PRE_THREADS) sdoc[j] = 0;
     __syncthreads();
@@ -529,14 +529,15 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     __syncthreads();
     auto docbit = [&](int j) -> bool { return (sdoc[j >> 5] >> (j & 31)) & 1u; };
 
-    // per-byte codes of the tile (validated) and of the halo after it.  A wavefront whose bytes are
-    // all ASCII also records per-chunk masks (bit k: byte k of the chunk) for the fast path below.
+    // per-byte codes of the tile (validated) and of the halo after it, and per-chunk masks of the
+    // characters (bit k: byte k of the chunk).  A wavefront whose bytes are all ASCII takes its codes
+    // and masks from a table; the others decode UTF-8.
     const int c0 = tid * PRE_CHUNK;
     const uint64_t pos0 = lo + (uint64_t)c0;
     // bytes 0..16 of the chunk at or past the end of the batch
     const uint32_t rem = pos0 >= n ? 0u : (n - pos0 > 17u ? 17u : (uint32_t)(n - pos0));
     const uint32_t xeof = (0x1FFFFu << rem) & 0x1FFFFu;
-    uint32_t dm = 0, mW = 0, mC = 0, mU = 0, mL = 0;
+    uint32_t dm = 0, mW = 0, mC = 0, mU = 0, mL = 0, mX = xeof & 0xFFFFu;
     bool ascii = false;
     {
         bool bad = false;
@@ -582,10 +583,17 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
         } else {
 #pragma unroll
             for (int k = 0; k < PRE_CHUNK; ++k) {
-                const uint64_t p = lo + c0 + k;
-                const uint32_t code =
-                    p < n ? reg_byte_code(rw, dm, k + RAW_LEAD, p, n, v.family, bad) : (uint32_t)CC_EOF;
+                const uint32_t code = ((xeof >> k) & 1u) ? (uint32_t)CC_EOF
+                                                         : reg_byte_code(rw, dm, k + RAW_LEAD, pos0 + k, n, v.family, bad);
                 w[k >> 2] |= code << (8 * (k & 3));
+                const uint32_t cat = code & 7u;
+                mW |= ((0x10u >> cat) & 1u) << k;                   // whitespace
+                mC |= ((code >> 3) & (0x10u >> cat) & 1u) << k;     // CR/LF
+                mX |= ((0x80u >> cat) & 1u) << k;                   // continuation byte or past the end
+                if (CASE) {
+                    mU |= ((0x01u >> cat) & 1u) << k;               // uppercase letter
+                    mL |= ((0x26u >> cat) & 1u) << k;               // lowercase or other letter, mark
+                }
             }
         }
         *(uint4 *)(scc + c0) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -615,8 +623,7 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     }
     __syncthreads();
 
-    // per character, left to right: next-character class and backward maps (packed: 2 bits per
-    // character for each backward map, 4 bits for the next-character code)
+    // codes of the chunk's 16 bytes and the 4 after it
     uint32_t cw[5];
     {
         const uint4 a = *(const uint4 *)(scc + c0);
@@ -624,16 +631,37 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
         cw[4] = *(const uint32_t *)(scc + c0 + PRE_CHUNK);
     }
     auto code_at = [&](int k) -> uint32_t { return (cw[k >> 2] >> (8 * (k & 3))) & 255u; };
-    uint32_t pk_bna = 0, pk_bau = 0, pk_nx[2] = {0, 0};
-    uint32_t agg = BK_KEEP | (BK_KEEP << 2);
-    // ASCII fast path: every byte is a character and the next character is the next byte.  NA is
-    // decided by a non-whitespace character (true), a CR/LF (false) or whitespace followed by the
-    // end of its document (true); AU by a non-letter (true), a lowercase letter (false) or an
-    // uppercase letter followed by the end of its document (true).  Other positions pass the value on.
-    uint32_t tna = 0, dna = 0, tau = 0, dau = 0;
+    // code of the character after each byte (packed like cw) and the mask of bytes whose next
+    // character starts a document or lies past the end of the batch
+    uint32_t ncw[PRE_CHUNK / 4], en;
     if (ascii) {
-        const uint32_t isch = ~xeof & 0xFFFFu;
-        const uint32_t en = ((dm >> (RAW_LEAD + 1)) | (xeof >> 1)) & 0xFFFFu;   // next char starts a document / ends the batch
+#pragma unroll
+        for (int j = 0; j < PRE_CHUNK / 4; ++j) ncw[j] = __builtin_amdgcn_alignbyte(cw[j + 1], cw[j], 1);
+        en = ((dm >> (RAW_LEAD + 1)) | (xeof >> 1)) & 0xFFFFu;
+    } else {
+        // right to left: the first byte after j that is not a continuation byte (byte 19 at the latest)
+        uint32_t nxt = code_at(PRE_CHUNK + 3);
+        ncw[0] = ncw[1] = ncw[2] = ncw[3] = 0;
+        en = 0;
+#pragma unroll
+        for (int j = PRE_CHUNK + 2; j >= 0; --j) {
+            if (j < PRE_CHUNK) {
+                ncw[j >> 2] |= nxt << (8 * (j & 3));
+                en |= ((nxt >> 7) | ((0x80u >> (nxt & 7u)) & 1u)) << j;
+            }
+            const uint32_t cj = code_at(j);
+            nxt = ((cj & 7u) == CAT_CONT && cj != CC_EOF) ? nxt : cj;
+        }
+    }
+
+    // The two backward flags of the chunk's characters.  NA is decided by a character that is not
+    // whitespace (true), a CR/LF (false) or whitespace whose next character starts a document (true);
+    // AU by a character that is not a letter or mark (true), a lowercase or other letter or a mark
+    // (false) or an uppercase letter whose next character starts a document (true).  Continuation
+    // bytes and the other characters pass on the value of the position after them.
+    const uint32_t isch = ~mX & 0xFFFFu;
+    uint32_t tna, dna, tau = 0, dau = 0;
+    {
         const uint32_t ws_ = mW & isch, crlf = mC & isch;
         tna = (isch & ~ws_) | (ws_ & ~crlf & en);
         dna = tna | crlf;
@@ -642,31 +670,10 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
             tau = (isch & ~(up | low)) | (up & en);
             dau = tau | low;
         }
-        agg = first_decided(tna, dna) | (first_decided(tau, dau) << 2);
-    } else {
-#pragma unroll
-    for (int k = 0; k < PRE_CHUNK; ++k) {
-        // next char: first non-continuation byte after k (within 4 bytes for valid UTF-8)
-        uint32_t nc = code_at(k + 1);
-        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code_at(k + 2);
-        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code_at(k + 3);
-        if ((nc & 7u) == CAT_CONT && nc != CC_EOF) nc = code_at(k + 4);
-        const uint32_t ck = code_at(k);
-        const bool isch = ck != CC_EOF && (ck & 7u) != CAT_CONT;
-        const bool en = nc == CC_EOF || (nc & CC_DOC) || (nc & 7u) == CAT_CONT;
-        uint32_t na, au;
-        backward_maps(ck, en, na, au);
-        na = isch ? na : (uint32_t)BK_KEEP;   // continuation bytes pass the flags through
-        au = isch && CASE ? au : (uint32_t)BK_KEEP;
-        pk_bna |= na << (2 * k);
-        pk_bau |= au << (2 * k);
-        pk_nx[k >> 3] |= (en ? 5u : next_code(nc)) << (4 * (k & 7));
-        if ((agg & 3u) == BK_KEEP) agg = (agg & ~3u) | na;
-        if ((agg >> 2) == BK_KEEP) agg = (agg & 3u) | (au << 2);
-    }
     }
     // value entering each chunk from its right: the first chunk to the right whose flag is decided
     // (suffix scan over the wavefront, then the wavefronts to the right, then the tile carry)
+    const uint32_t agg = first_decided(tna, dna) | (first_decided(tau, dau) << 2);
     auto bk_comb = [](uint32_t x, uint32_t r) -> uint32_t {
         if ((x & 3u) == BK_KEEP) x = (x & ~3u) | (r & 3u);
         if ((x >> 2) == BK_KEEP) x = (x & 3u) | (r & ~3u);
@@ -683,48 +690,30 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
     __syncthreads();
     uint32_t right = lane < 63 ? suf1 : (BK_KEEP | (BK_KEEP << 2));
     for (uint32_t w = wid + 1; w < (uint32_t)NW; ++w) right = bk_comb(right, sbkw[w]);
-    uint32_t na_val = ((right & 3u) == BK_KEEP) ? (s_carry & 1u) : (right & 1u);
-    uint32_t au_val = ((right >> 2) == BK_KEEP) ? ((s_carry >> 1) & 1u) : ((right >> 2) & 1u);
+    const uint32_t na_in = ((right & 3u) == BK_KEEP) ? (s_carry & 1u) : (right & 1u);
+    const uint32_t au_in = ((right >> 2) == BK_KEEP) ? ((s_carry >> 1) & 1u) : ((right >> 2) & 1u);
 
-    // right to left: NA of each char, AU of the char after it, the automaton context (packed 16 bits
-    // per character) and the chunk's map, composed from the right
+    // right to left: each character's automaton context (packed 16 bits per character) and the
+    // chunk's map, composed from the right.  The context is the sum of two table entries (the
+    // character's code, the next character's code) and the two flags; continuation bytes and
+    // positions past the end saturate to the identity map.
     uint32_t pk_ctx[PRE_CHUNK / 2] = {0, 0, 0, 0, 0, 0, 0, 0};
     M16 acc = m16_identity();
-    if (ascii) {
-        // the context from two table entries (this byte's code, the next byte's code) plus the two
-        // flags; past the end of the batch the table entry saturates it to the identity map
-        const uint32_t naw = fill_down16(tna, dna, na_val) & mW & ~mC;   // whitespace (not CR/LF) with NA set
+    {
+        const uint32_t naw = fill_down16(tna, dna, na_in) & mW & ~mC;   // whitespace (not CR/LF) with NA set
         uint32_t aun = 0;
-        if (CASE) aun = (fill_down16(tau, dau, au_val) >> 1) | (au_val << 15);   // AU of the next character
+        if (CASE) aun = (fill_down16(tau, dau, au_in) >> 1) | (au_in << 15);   // AU of the next character
 #pragma unroll
         for (int k = PRE_CHUNK - 1; k >= 0; --k) {
-            uint32_t ctx = (uint32_t)sctxa[code_at(k)] + (uint32_t)sctxb[code_at(k + 1)] + 4u * NNEXT * ((naw >> k) & 1u);
+            const uint32_t nc = (ncw[k >> 2] >> (8 * (k & 3))) & 255u;
+            uint32_t ctx = (uint32_t)sctxa[code_at(k)] + (uint32_t)sctxb[nc] + 4u * NNEXT * ((naw >> k) & 1u);
             if (CASE) ctx += (aun >> k) & 1u;
             ctx = min(ctx, (uint32_t)NCTX);
             pk_ctx[k >> 1] |= ctx << (16 * (k & 1));
             const uint4 m = smap16[ctx];
             acc = compose16(M16{{m.x, m.y, m.z, m.w}}, acc);
-            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);   // one map load in flight: keeps register use low
         }
-    } else {
-#pragma unroll
-    for (int k = PRE_CHUNK - 1; k >= 0; --k) {
-        const uint32_t au_next = CASE ? au_val : 0u;   // AU of the next character
-        const uint32_t bn = (pk_bna >> (2 * k)) & 3u, bu = (pk_bau >> (2 * k)) & 3u;
-        if (bn != BK_KEEP) na_val = bn & 1u;
-        if (bu != BK_KEEP) au_val = bu & 1u;
-        const uint32_t ck = code_at(k);
-        const bool isch = ck != CC_EOF && (ck & 7u) != CAT_CONT;
-        const uint32_t self = self_code(ck, na_val != 0);
-        const uint32_t doc = (ck & CC_DOC) ? 1u : 0u;
-        const uint32_t nx = (pk_nx[k >> 3] >> (4 * (k & 7))) & 15u;
-        // identity map (NCTX) for continuation bytes and positions past the end
-        const uint32_t ctx = isch ? ((self * 2u + doc) * NNEXT + nx) * 2u + au_next : (uint32_t)NCTX;
-        pk_ctx[k >> 1] |= ctx << (16 * (k & 1));
-        const uint4 m = smap16[ctx];
-        acc = compose16(M16{{m.x, m.y, m.z, m.w}}, acc);
-        __builtin_amdgcn_sched_barrier(0);   // one map load in flight: keeps register use low
-    }
     }
 
     // wavefront scan of the chunk maps; the wavefronts' maps are scanned by wave 0, which also
