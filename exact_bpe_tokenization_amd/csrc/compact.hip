@@ -87,24 +87,25 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
 
     // IDs: a single-token piece's ID is its result word (coalesced); a short multi-token piece's IDs
     // are at scratch[its start byte ...]; a long piece gets its output offset for k_gather_long.
-    // Two halves of IT / 2 iterations; in each, all loads are issued before any store.
+    // All start loads are issued first; the first IDs in two halves (fewer registers); the further
+    // IDs of a piece four independent loads at a time.
+    uint32_t st[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const uint32_t i = wb + it * 64u + lane;
+        const bool multi = i < end && (pv[it] & (PV_MULTI | PV_LONG)) == PV_MULTI;
+        st[it] = multi ? pstart[i] : 0u;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         constexpr int HI = IT / 2;
-        uint32_t st[HI], f0[HI];
+        uint32_t f0[HI];
 #pragma unroll
         for (int u = 0; u < HI; ++u) {
             const int it = h * HI + u;
             const uint32_t i = wb + it * 64u + lane;
             const bool multi = i < end && (pv[it] & (PV_MULTI | PV_LONG)) == PV_MULTI;
-            st[u] = multi ? pstart[i] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < HI; ++u) {
-            const int it = h * HI + u;
-            const uint32_t i = wb + it * 64u + lane;
-            const bool multi = i < end && (pv[it] & (PV_MULTI | PV_LONG)) == PV_MULTI;
-            f0[u] = multi ? scratch[st[u]] : pv[it];
+            f0[u] = multi ? scratch[st[it]] : pv[it];
         }
 #pragma unroll
         for (int u = 0; u < HI; ++u) {
@@ -120,7 +121,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
             }
             out_ids[o] = f0[u];
             const uint32_t c = (v & PV_MULTI) ? (v & PV_COUNT) : 1u;
-            for (uint32_t j = 1; j < c; ++j) out_ids[o + j] = scratch[st[u] + j];
+            for (uint32_t j = 1; j < c; j += 4) {
+                uint32_t x[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[t] = j + t < c ? scratch[st[it] + j + t] : 0u;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (j + t < c) out_ids[o + j + t] = x[t];
+            }
         }
     }
     if (tid == 0) soff[end - first] = tbase + total;
