@@ -43,7 +43,7 @@ LATENCY = ("c1_ec4k", "c2_at100k", "c3_mix1m", "c5_adv4m4")
 # input bytes each kernel launch processes (the unit of the algorithmic-bytes figure)
 # (bytes of the pieces in the length range the launch serves)
 UNITS = {
-    "init": "all", "summary": "all", "pieces": "all", "route": "all", "emit": "all", "gather_long": "binned",
+    "summary": "all", "pieces": "all", "route": "all", "emit": "all", "gather_long": "binned",
     "bpe_small": "le128",
     "bpe_wave": "wave", "giant_seams": "giant", "bpe_block": "block", "bpe_giant": "giant", "giant_join": "giant",
 }

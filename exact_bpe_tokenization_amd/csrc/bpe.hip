@@ -110,76 +110,121 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t 
 // ---------------------------------------------------------------------------------------------
 // lane per piece (unresolved pieces of <= 16 bytes)
 
+// One item per lane, sequence and pair ranks in registers (MAXL elements): the textbook loop --
+// merge the leftmost pair of lowest rank, shift the tail left, re-probe the two neighbours.  Called
+// by all 64 lanes of a wavefront (the token-count update is a wavefront operation); len 0 = idle.
 template <int MAXL>
-__device__ void bpe_lane(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
-                         int which, uint32_t blk, uint32_t nblk)
+__device__ __forceinline__ void lane_bpe(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws,
+                                         const Layout &L, uint32_t e, uint32_t b0, uint32_t len)
 {
-    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
-    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *pval = (uint32_t *)(ws + L.pval);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
-    const uint32_t *list = (const uint32_t *)(ws + (which == 0 ? L.miss16 : (which == 1 ? L.miss32 : L.miss64)));
-    const uint32_t count = ctrl->miss_count[which];
-    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
     uint32_t *ccount = (uint32_t *)(ws + L.ccount);
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t stride = nblk * blockDim.x;
-    // wavefront-uniform loop (the token-count update below is a wavefront operation)
-    for (uint32_t q0 = blk * blockDim.x + (threadIdx.x & ~63u); q0 < count; q0 += stride) {
-        const uint32_t q = q0 + lane;
-        const bool active = q < count;
-        const uint32_t e = active ? list[q] : 0u;
-        const bool chunk = (e & CHUNK_ITEM) != 0;
-        const uint32_t p = e & ~CHUNK_ITEM;
-        const uint32_t b0 = !active ? 0u : chunk ? cstart[p] : pstart[p];
-        const uint32_t len = !active ? 0u : chunk ? clen[p] : pstart[p + 1] - b0;   // 0: nothing to do
-        uint32_t id[MAXL], rk[MAXL];
-        uint64_t w[(MAXL + 7) / 8];
-        load_words<(MAXL + 7) / 8>(bytes + b0, len, w);
+    const bool active = len != 0;
+    const bool chunk = (e & CHUNK_ITEM) != 0;
+    const uint32_t p = e & ~CHUNK_ITEM;
+    uint32_t id[MAXL], rk[MAXL];
+    uint64_t w[(MAXL + 7) / 8];
+    load_words<(MAXL + 7) / 8>(bytes + b0, len, w);
 #pragma unroll
-        for (int k = 0; k < MAXL; ++k) id[k] = (uint32_t)(w[k >> 3] >> (8 * (k & 7))) & 0xFFu;
+    for (int k = 0; k < MAXL; ++k) id[k] = (uint32_t)(w[k >> 3] >> (8 * (k & 7))) & 0xFFu;
+#pragma unroll
+    for (int k = 0; k < MAXL; ++k)
+        rk[k] = (uint32_t)(k + 1) < len ? __ldg(v.r2 + ((id[k] << 8) | id[(k + 1) % MAXL])) : NO_RANK;
+    uint32_t n = len;
+    for (;;) {
+        uint32_t best = NO_RANK, pos = 0;
+#pragma unroll
+        for (int k = 0; k < MAXL - 1; ++k)
+            if (rk[k] < best) { best = rk[k]; pos = k; }
+        if (best == NO_RANK) break;
+        const uint32_t nid = 256u + best;
+        // id[pos] <- nid, drop id[pos+1], shift the tail left
+#pragma unroll
+        for (int j = 0; j < MAXL; ++j) {
+            uint32_t nx_id = j + 1 < MAXL ? id[(j + 1) % MAXL] : 0u;
+            uint32_t nx_rk = j + 1 < MAXL ? rk[(j + 1) % MAXL] : NO_RANK;
+            id[j] = (uint32_t)j < pos ? id[j] : ((uint32_t)j == pos ? nid : nx_id);
+            rk[j] = (uint32_t)j < pos ? rk[j] : nx_rk;
+        }
+        --n;
+        uint32_t left = 0, right = 0;
+#pragma unroll
+        for (int j = 0; j < MAXL; ++j) {
+            if ((uint32_t)j + 1 == pos) left = id[j];
+            if ((uint32_t)j == pos + 1) right = id[j];
+        }
+        const uint32_t rl = pos > 0 ? pair_rank(v, left, nid) : NO_RANK;
+        const uint32_t rr = pos + 1 < n ? pair_rank(v, nid, right) : NO_RANK;
+#pragma unroll
+        for (int j = 0; j < MAXL; ++j) {
+            if ((uint32_t)j + 1 == pos) rk[j] = rl;
+            if ((uint32_t)j == pos) rk[j] = rr;
+        }
+    }
+    if (n > 1 || chunk) {
 #pragma unroll
         for (int k = 0; k < MAXL; ++k)
-            rk[k] = (uint32_t)(k + 1) < len ? __ldg(v.r2 + ((id[k] << 8) | id[(k + 1) % MAXL])) : NO_RANK;
-        uint32_t n = len;
-        for (;;) {
-            uint32_t best = NO_RANK, pos = 0;
-#pragma unroll
-            for (int k = 0; k < MAXL - 1; ++k)
-                if (rk[k] < best) { best = rk[k]; pos = k; }
-            if (best == NO_RANK) break;
-            const uint32_t nid = 256u + best;
-            // id[pos] <- nid, drop id[pos+1], shift the tail left
-#pragma unroll
-            for (int j = 0; j < MAXL; ++j) {
-                uint32_t nx_id = j + 1 < MAXL ? id[(j + 1) % MAXL] : 0u;
-                uint32_t nx_rk = j + 1 < MAXL ? rk[(j + 1) % MAXL] : NO_RANK;
-                id[j] = (uint32_t)j < pos ? id[j] : ((uint32_t)j == pos ? nid : nx_id);
-                rk[j] = (uint32_t)j < pos ? rk[j] : nx_rk;
-            }
-            --n;
-            uint32_t left = 0, right = 0;
-#pragma unroll
-            for (int j = 0; j < MAXL; ++j) {
-                if ((uint32_t)j + 1 == pos) left = id[j];
-                if ((uint32_t)j == pos + 1) right = id[j];
-            }
-            const uint32_t rl = pos > 0 ? pair_rank(v, left, nid) : NO_RANK;
-            const uint32_t rr = pos + 1 < n ? pair_rank(v, nid, right) : NO_RANK;
-#pragma unroll
-            for (int j = 0; j < MAXL; ++j) {
-                if ((uint32_t)j + 1 == pos) rk[j] = rl;
-                if ((uint32_t)j == pos) rk[j] = rr;
-            }
+            if ((uint32_t)k < n) scratch[b0 + k] = id[k];
+    }
+    if (active && chunk) ccount[p] = n;
+    else if (active) pval[p] = n == 1 ? id[0] : (PV_MULTI | n);
+    add_excess_wave(ws, L, p, active && !chunk ? n - 1 : 0u);
+}
+
+// The <= 16-byte list, 256 items per workgroup step.  The items are sorted by length in LDS first
+// (counting sort), so each wavefront holds items of similar length: its loop runs about as many
+// rounds as its items need merges, on arrays sized for its longest item (8, 12 or 16 elements).
+__device__ void bpe_lane(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
+                         uint32_t blk, uint32_t nblk)
+{
+    constexpr uint32_t NT = 256, NB = 17;   // lengths 0 (idle) .. 16
+    __shared__ uint32_t s_cnt[NB], s_e[NT], s_b0[NT], s_len[NT];
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t *list = (const uint32_t *)(ws + L.miss16);
+    const uint32_t count = ctrl->miss_count[0];
+    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    for (uint32_t q0 = blk * NT; q0 < count; q0 += nblk * NT) {   // workgroup-uniform
+        const uint32_t q = q0 + tid;
+        uint32_t e = 0, b0 = 0, len = 0;
+        if (q < count) {
+            e = list[q];
+            const uint32_t p = e & ~CHUNK_ITEM;
+            if (e & CHUNK_ITEM) { b0 = cstart[p]; len = clen[p]; }
+            else { b0 = pstart[p]; len = pstart[p + 1] - b0; }
         }
-        if (n > 1 || chunk) {
+        if (tid < NB) s_cnt[tid] = 0;
+        __syncthreads();
+        const uint32_t r = atomicAdd(&s_cnt[len], 1u);
+        __syncthreads();
+        if (tid < 64) {   // exclusive scan of the length histogram
+            const uint32_t c = tid < NB ? s_cnt[tid] : 0u;
+            uint32_t x = c;
 #pragma unroll
-            for (int k = 0; k < MAXL; ++k)
-                if ((uint32_t)k < n) scratch[b0 + k] = id[k];
+            for (int d = 1; d < 32; d <<= 1) {
+                const uint32_t y = __shfl_up(x, d, 64);
+                if (lane >= (uint32_t)d) x += y;
+            }
+            if (tid < NB) s_cnt[tid] = x - c;
         }
-        if (active && chunk) ccount[p] = n;
-        else if (active) pval[p] = n == 1 ? id[0] : (PV_MULTI | n);
-        add_excess_wave(ws, L, p, active && !chunk ? n - 1 : 0u);
+        __syncthreads();
+        const uint32_t at = s_cnt[len] + r;
+        s_e[at] = e;
+        s_b0[at] = b0;
+        s_len[at] = len;
+        __syncthreads();
+        e = s_e[tid];
+        b0 = s_b0[tid];
+        len = s_len[tid];
+        uint32_t wmax = len;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) wmax = max(wmax, (uint32_t)__shfl_xor(wmax, d, 64));
+        if (wmax <= 8u) lane_bpe<8>(v, bytes, ws, L, e, b0, len);
+        else if (wmax <= 12u) lane_bpe<12>(v, bytes, ws, L, e, b0, len);
+        else lane_bpe<16>(v, bytes, ws, L, e, b0, len);
+        __syncthreads();   // the LDS arrays are reused by the next step
     }
 }
 
@@ -376,7 +421,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
 {
     uint32_t b = blockIdx.x;
     if (b < g16) {
-        bpe_lane<16>(v, bytes, ws, L, 0, b, g16);
+        bpe_lane(v, bytes, ws, L, b, g16);
         return;
     }
     b -= g16;
@@ -976,7 +1021,7 @@ hipError_t launch_route(const DevVocab &v, const Batch &b, hipStream_t s, const 
 {
     if (b.n == 0) return hipGetLastError();
     const uint64_t g = (b.n + 4095) / 4096;   // about 4 KiB of input (1-2K pieces) per workgroup, at most 1024
-    LaunchScope k(ev, 3, s);
+    LaunchScope k(ev, 2, s);
     hipLaunchKernelGGL(k_route, dim3(g > 1024 ? 1024u : (uint32_t)g), dim3(RT_THREADS), 0, s, v, b.bytes, b.ws, b.L);
     return hipGetLastError();
 }
@@ -988,7 +1033,7 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     {
         // giant pieces: safe-seam bitmap, then chunks (before the other BPE kernels, which also
         // encode the chunks)
-        LaunchScope k(ev, 4, s);
+        LaunchScope k(ev, 3, s);
         const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
         hipLaunchKernelGGL(k_gsafe, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
         const uint32_t gc = L.cap_giant < 64 ? L.cap_giant : 64;
@@ -1000,28 +1045,28 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
         const uint64_t b16 = b.n / 256 + 1, b32 = b.n / 17 / 8 + 1, b64 = b.n / 33 / 4 + 1, b128 = b.n / 65 / 4 + 1;
         const uint32_t g16 = b16 > 2048 ? 2048u : (uint32_t)b16, g32 = b32 > 2048 ? 2048u : (uint32_t)b32;
         const uint32_t g64 = b64 > 1024 ? 1024u : (uint32_t)b64, g128 = b128 > 1024 ? 1024u : (uint32_t)b128;
-        LaunchScope k(ev, 5, s);
+        LaunchScope k(ev, 4, s);
         hipLaunchKernelGGL(k_bpe_small, dim3(g16 + g32 + g64 + g128), dim3(256), 0, s, v, b.bytes, b.ws, L, g16, g32,
                            g64, g128);
     }
     {
-        LaunchScope k(ev, 6, s);
+        LaunchScope k(ev, 5, s);
         uint32_t gw = L.cap_wave + L.cap_chunks < 1024 ? L.cap_wave + L.cap_chunks : 1024;
         hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
     }
     const uint32_t gg = L.cap_giant < 64 ? L.cap_giant : 64;
     {
-        LaunchScope k(ev, 7, s);
+        LaunchScope k(ev, 6, s);
         uint32_t gb = L.cap_block + L.cap_chunks < 256 ? L.cap_block + L.cap_chunks : 256;
         hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v,
                            b.bytes, b.ws, L, 1);
     }
     {
-        LaunchScope k(ev, 8, s);
+        LaunchScope k(ev, 7, s);
         hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
     }
     {
-        LaunchScope k(ev, 9, s);
+        LaunchScope k(ev, 8, s);
         hipLaunchKernelGGL(k_gassemble, dim3(gg), dim3(1024), 0, s, b.ws, L);
     }
     return hipGetLastError();

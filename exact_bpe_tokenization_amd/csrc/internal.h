@@ -46,12 +46,10 @@ constexpr uint8_t CC_EOF = 0xFF;   // placed past the end of the batch
 // pre-tokenizer automaton: the state before a character says what the running match expects
 enum : int { S_ST = 0, S_LRUN, S_NALL, S_N1, S_N2, S_ORUN, S_ORNL, S_ONL, S_WNL, S_WNS, S_C1,
              S_C2, S_LA, S_LB, S_LEND, NSTATES };
-static_assert(NSTATES == 15, "a transition map packs 15 states into 60 bits");
+static_assert(NSTATES == 15, "a transition map holds one byte per state in 16 bytes, byte 15 free");
 
 // character context: self code (13) x first-of-document (2) x next-char code (6) x flag (2)
 constexpr int NSELF = 13, NNEXT = 6, NCTX = NSELF * 2 * NNEXT * 2;
-constexpr uint64_t MAP_IDENTITY = 0x0EDCBA9876543210ull;
-constexpr uint64_t NIBBLE_ONES = 0x0111111111111111ull;
 
 // ---------------------------------------------------------------------------------------------
 // merge tables.  Pair hash slot: bits 63..21 = (left << 21 | right), bits 20..0 = rank.
@@ -260,7 +258,7 @@ inline Layout make_layout(uint64_t n)
     L.ctrl = o;        o += align256(sizeof(Ctrl));
     L.cc = o;
     L.tbwd = o;        o += align256((uint64_t)L.n_tiles + 1);
-    L.tflag_state = o; o += align256(8ull * L.n_tiles);
+    L.tflag_state = o; o += align256(16ull * L.n_tiles);
     L.tflag_cnt = o;   o += align256(8ull * L.n_tiles);
     L.tilex = o;       o += align256(4ull * L.n_scan_tiles);
     L.pstart = o;      o += align256(4ull * (n + 2));

@@ -5,17 +5,17 @@
 // whether a character starts a piece depends only on its offset in the run, a few characters of
 // look-back and per-run aggregates -- so classification is parallel and run summaries come from
 // prefix scans.  Here the per-character rule is a 15-state automaton (the state says what the
-// running leftmost-first match expects next).  Each character's transition function is a 60-bit
-// map (15 nibbles), maps compose associatively, so the state before every character comes from a
-// parallel scan of maps: within a thread, across the workgroup, and across tiles through a
-// decoupled look-back.  The two facts that need the future -- "no CR/LF later in this whitespace
-// run" (where `\s*[\r\n]+` stops) and "only uppercase letters left in this letter run" (where the
-// o200k case rule backtracks) -- are carried right to left; each tile's carry comes from a summary
-// of the tiles after it.
+// running leftmost-first match expects next).  Each character's transition function is a 16-byte
+// map (one byte per state), maps compose associatively with byte permutes, so the state before
+// every character comes from a parallel scan of maps: within a thread, across the workgroup, and
+// across tiles through a decoupled look-back.  The two facts that need the future -- "no CR/LF
+// later in this whitespace run" (where `\s*[\r\n]+` stops) and "only uppercase letters left in this
+// letter run" (where the o200k case rule backtracks) -- are carried right to left; each tile's
+// carry comes from a summary of the tiles after it.
 //
-// Kernels:  k_init     clear the control block, the look-back flags and the tile token counters
-//           k_summary  per tile: the leftmost character that decides each backward flag (an
-//                      early-exit scan of the tile's first bytes; one wavefront per tile)
+// Kernels:  k_summary  per tile: the leftmost character that decides each backward flag (an
+//                      early-exit scan of the tile's first bytes; one wavefront per tile); also
+//                      clears the control block, the look-back flags and the tile token counters
 //           k_pieces   per 8 KiB tile: UTF-8 decode + validation, categories, backward flags,
 //                      automaton scan, piece starts, piece numbering (one read of the input,
 //                      4 bytes written per piece)
@@ -65,48 +65,6 @@ __device__ __forceinline__ void backward_maps(uint32_t code, bool eof_next, uint
     au = cat == CAT_LU ? (eof_next ? BK_T : BK_KEEP) : (lower ? BK_F : BK_T);
 }
 
-__device__ __forceinline__ bool is_const_map(uint64_t m)
-{
-    return m == (m & 15u) * NIBBLE_ONES;
-}
-
-// apply a first, then b
-__device__ __forceinline__ uint64_t compose(uint64_t a, uint64_t b)
-{
-    uint32_t a0 = (uint32_t)(a & 15u);
-    if (a == a0 * NIBBLE_ONES) return ((b >> (4u * a0)) & 15u) * NIBBLE_ONES;
-    uint64_t r = 0;
-#pragma unroll
-    for (int s = 0; s < NSTATES; ++s) {
-        uint32_t x = (uint32_t)(a >> (4 * s)) & 15u;
-        r |= ((b >> (4u * x)) & 15ull) << (4 * s);
-    }
-    return r;
-}
-
-__device__ __forceinline__ uint32_t apply_map(uint64_t m, uint32_t s)
-{
-    return (uint32_t)(m >> (4u * s)) & 15u;
-}
-
-__device__ __forceinline__ uint64_t shfl_up64(uint64_t x, int d)
-{
-    uint32_t lo = __shfl_up((uint32_t)x, d, 64), hi = __shfl_up((uint32_t)(x >> 32), d, 64);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t shfl_down64(uint64_t x, int d)
-{
-    uint32_t lo = __shfl_down((uint32_t)x, d, 64), hi = __shfl_down((uint32_t)(x >> 32), d, 64);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t shfl64(uint64_t x, int src)
-{
-    uint32_t lo = __shfl((uint32_t)x, src, 64), hi = __shfl((uint32_t)(x >> 32), src, 64);
-    return ((uint64_t)hi << 32) | lo;
-}
-
 // 16-byte transition maps: byte s (s < 15) is the image of state s in bits 0-3 (bit 4 is the
 // piece-start flag, ignored when composing); byte 15 is never selected.  Composition is a byte
 // gather done with v_perm: two 8-byte halves selected by the low 3 bits, then one of the two by bit 3.
@@ -149,41 +107,70 @@ __device__ __forceinline__ M16 shfl16(const M16 &m, int src)
                 (uint32_t)__shfl(m.w[2], src, 64), (uint32_t)__shfl(m.w[3], src, 64)}};
 }
 
-// the 60-bit nibble form used by the tile look-back flags
-__device__ __forceinline__ uint64_t pack60(const M16 &m)
+__device__ __forceinline__ M16 shfl_down16(const M16 &m, int d)
 {
-    uint64_t r = 0;
-#pragma unroll
-    for (int st = 0; st < NSTATES; ++st) r |= (uint64_t)(byte16(m, (uint32_t)st) & 15u) << (4 * st);
-    return r;
+    return M16{{(uint32_t)__shfl_down(m.w[0], d, 64), (uint32_t)__shfl_down(m.w[1], d, 64),
+                (uint32_t)__shfl_down(m.w[2], d, 64), (uint32_t)__shfl_down(m.w[3], d, 64)}};
 }
 
-// Automaton state entering `tile`.  flags[t] = (1 << 60 | map of tile t) or (2 << 60 | state after
-// tile t); the batch starts in S_ST.  Wave 0 reads 64 predecessors per step and composes their maps
-// (farthest first); a prefix state or any constant composition ends the walk.
-__device__ uint32_t lookback_state(const uint64_t *flags, uint32_t tile)
+__device__ __forceinline__ M16 m16_const(uint32_t st) { const uint32_t c = st * 0x01010101u; return M16{{c, c, c, c}}; }
+
+// every state maps to the same state (only the state nibbles of bytes 0..14 count)
+__device__ __forceinline__ bool is_const16(const M16 &m)
+{
+    const uint32_t c = (m.w[0] & 15u) * 0x01010101u;
+    return (m.w[0] & 0x0F0F0F0Fu) == c && (m.w[1] & 0x0F0F0F0Fu) == c && (m.w[2] & 0x0F0F0F0Fu) == c &&
+           (m.w[3] & 0x000F0F0Fu) == (c & 0x000F0F0Fu);
+}
+
+// Tile look-back flags of the automaton state: one map per tile, 4 words, each word carrying the
+// flag kind in its top two bits (bytes 3, 7, 11 and 15 of a map use only bits 0-4): 1 = the tile's
+// map, 2 = the constant map of the state after the tile, 0 = nothing published yet.  Words are
+// stored and loaded one by one, each atomically; a reader accepts a flag only when its four words
+// carry the same kind, so it never combines words of the two stores.
+constexpr uint32_t FLAG_AGG = 1, FLAG_PREFIX = 2;
+
+__device__ __forceinline__ void st_flag16(uint32_t *p, const M16 &m, uint32_t kind)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(p + i, (m.w[i] & 0x3FFFFFFFu) | (kind << 30), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Automaton state entering `tile`.  Wave 0 reads the flags of 64 predecessors per step and composes
+// their maps (farthest first) with byte permutes; a prefix or a constant composition ends the walk.
+// The batch starts in S_ST.
+__device__ uint32_t lookback_state(const uint32_t *flags, uint32_t tile)
 {
     const uint32_t lane = threadIdx.x & 63u;
-    uint64_t acc = MAP_IDENTITY;
+    M16 acc = m16_identity();
     int64_t top = (int64_t)tile - 1;
     for (;;) {
         const int64_t pos = top - (int64_t)lane;
-        const uint64_t f = pos >= 0 ? ld_flag(flags + pos) : ((2ull << 60) | S_ST);
-        const uint32_t flag = (uint32_t)(f >> 60);
-        const uint64_t pre = __ballot(flag == 2), nr = __ballot(flag == 0);
+        uint32_t f[4];
+        if (pos >= 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                f[i] = __hip_atomic_load(flags + 4 * pos + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[i] = (uint32_t)S_ST * 0x01010101u | (FLAG_PREFIX << 30);
+        }
+        const uint32_t k0 = f[0] >> 30;
+        const uint32_t kind = ((f[1] >> 30) == k0 && (f[2] >> 30) == k0 && (f[3] >> 30) == k0) ? k0 : 0u;
+        const uint64_t pre = __ballot(kind == FLAG_PREFIX), nr = __ballot(kind == 0);
         const uint32_t kp = pre ? (uint32_t)__ffsll((unsigned long long)pre) - 1u : 64u;
         const uint64_t need = kp >= 63 ? ~0ull : ((2ull << kp) - 1);
         if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
-        uint64_t x = MAP_IDENTITY;
-        if (lane < kp) x = f & ((1ull << 60) - 1);
-        else if (lane == kp) x = (f & 15u) * NIBBLE_ONES;
+        M16 x = m16_identity();
+        if (lane <= kp) x = M16{{f[0] & 0x0F0F0F0Fu, f[1] & 0x0F0F0F0Fu, f[2] & 0x0F0F0F0Fu, f[3] & 0x0F0F0F0Fu}};
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
-            uint64_t y = shfl_down64(x, d);
-            if ((lane & (2u * d - 1u)) == 0) x = compose(y, x);
+            const M16 y = shfl_down16(x, d);
+            if ((lane & (2u * d - 1u)) == 0) x = compose16(y, x);
         }
-        acc = compose(shfl64(x, 0), acc);
-        if (kp < 64 || is_const_map(acc)) return (uint32_t)(acc & 15u);
+        acc = compose16(shfl16(x, 0), acc);
+        if (kp < 64 || is_const16(acc)) return byte16(acc, 0) & 15u;
         top -= 64;
     }
 }
@@ -245,30 +232,25 @@ __device__ __forceinline__ uint32_t byte_code(const uint8_t *sraw, DocBit docbit
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_init
-
-__global__ void k_init(uint8_t *ws, Layout L)
-{
-    uint32_t i = blockIdx.x * blockDim.x + threadIdx.x, stride = gridDim.x * blockDim.x;
-    uint32_t *ctrl = (uint32_t *)(ws + L.ctrl);
-    for (uint32_t k = i; k < 64; k += stride) ctrl[k] = 0;
-    uint64_t *a = (uint64_t *)(ws + L.tflag_state), *b = (uint64_t *)(ws + L.tflag_cnt);
-    uint32_t *c = (uint32_t *)(ws + L.tilex);
-    for (uint32_t k = i; k < L.n_tiles; k += stride) { a[k] = 0; b[k] = 0; }
-    for (uint32_t k = i; k < L.n_scan_tiles; k += stride) c[k] = 0;
-}
-
-// ---------------------------------------------------------------------------------------------
-// k_summary: one wavefront per tile.  The tile's summary of a backward flag is the map of its
-// leftmost character whose map is not "pass through" (for NA: the first character that is not
-// whitespace-other-than-CR/LF, or the last of its document; for AU: the first that is not an
-// uppercase letter, or the last of its document).  Usually found in the first 256 bytes.
+// k_summary: one wavefront per tile (one workgroup when the batch is empty).  It also clears what
+// the later kernels count on: the control block, the tile's look-back flags and the per-tile token
+// counters.  The tile's summary of a backward flag is the map of its leftmost character whose map
+// is not "pass through" (for NA: the first character that is not whitespace-other-than-CR/LF, or
+// the last of its document; for AU: the first that is not an uppercase letter, or the last of its
+// document).  Usually found in the first 256 bytes.
 
 __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ bytes,
                                                 const uint64_t *__restrict__ offsets, uint32_t n_docs,
                                                 uint64_t n, uint8_t *ws, Layout L)
 {
     const uint32_t lane = threadIdx.x;
+    if (blockIdx.x == 0) ((uint32_t *)(ws + L.ctrl))[lane] = 0;   // 64 words
+    if (blockIdx.x < L.n_tiles && lane == 0) {
+        ((uint4 *)(ws + L.tflag_state))[blockIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+        ((uint64_t *)(ws + L.tflag_cnt))[blockIdx.x] = 0;
+    }
+    for (uint32_t k = blockIdx.x * 64u + lane; k < L.n_scan_tiles; k += gridDim.x * 64u) ((uint32_t *)(ws + L.tilex))[k] = 0;
+    if (blockIdx.x >= L.n_tiles) return;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
     const uint64_t hi = min(lo + TILE, n);
     // document starts in [lo, hi + 4): indices [d0, d1) of offsets (empty documents repeat one)
@@ -441,10 +423,12 @@ __device__ __forceinline__ uint32_t contraction_code(const uint8_t *sraw, DocBit
 
 // CASE: the family has the case-boundary letter rule (the only one that reads the AU flag; for the
 // others the flag changes no transition between reachable states and is left at zero).
+// Eight wavefronts per SIMD (at most 64 VGPRs): four tiles per CU, whose LDS (40 KB each) fits too;
+// the tiles spend much of their time waiting on look-backs, which the fourth tile helps to hide.
 template <bool CASE>
-__global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes,
-                                                        const uint64_t *__restrict__ offsets, uint32_t n_docs,
-                                                        uint64_t n, uint8_t *ws, Layout L)
+__global__ __launch_bounds__(PRE_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__restrict__ offsets, uint32_t n_docs,
+              uint64_t n, uint8_t *ws, Layout L)
 {
     constexpr int NW = PRE_THREADS / 64;
     constexpr int SPAN = RAW_LEAD + TILE + RAW_TAIL;
@@ -463,7 +447,7 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
 
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint8_t *tbwd = ws + L.tbwd;
-    uint64_t *tfs = (uint64_t *)(ws + L.tflag_state);
+    uint32_t *tfs = (uint32_t *)(ws + L.tflag_state);
     uint64_t *tfc = (uint64_t *)(ws + L.tflag_cnt);
     uint32_t *pstart = (uint32_t *)(ws + L.pstart);
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
@@ -743,9 +727,9 @@ __global__ __launch_bounds__(PRE_THREADS) void k_pieces(DevVocab v, const uint8_
         if (lane == 0) wex = m16_identity();
         const M16 tile_map = shfl16(wm, NW - 1);
         // look-back #1: automaton state entering this tile
-        if (lane == 0 && tile > 0) st_flag(tfs + tile, (1ull << 60) | pack60(tile_map));
+        if (lane == 0 && tile > 0) st_flag16(tfs + 4 * tile, tile_map, FLAG_AGG);
         const uint32_t entry = tile == 0 ? (uint32_t)S_ST : lookback_state(tfs, tile);
-        if (lane == 0) st_flag(tfs + tile, (2ull << 60) | (byte16(tile_map, entry) & 15u));
+        if (lane == 0) st_flag16(tfs + 4 * tile, m16_const(byte16(tile_map, entry) & 15u), FLAG_PREFIX);
         if (lane < (uint32_t)NW) swstate[lane] = byte16(wex, entry) & 15u;
     }
     __syncthreads();
@@ -809,15 +793,12 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
     const Layout &L = b.L;
     {
         LaunchScope k(ev, 0, s);
-        hipLaunchKernelGGL(k_init, dim3(64), dim3(256), 0, s, b.ws, L);
+        hipLaunchKernelGGL(k_summary, dim3(L.n_tiles ? L.n_tiles : 1u), dim3(64), 0, s, b.bytes, b.offsets, b.n_docs,
+                           b.n, b.ws, L);
     }
     if (L.n_tiles == 0) return hipGetLastError();
     {
         LaunchScope k(ev, 1, s);
-        hipLaunchKernelGGL(k_summary, dim3(L.n_tiles), dim3(64), 0, s, b.bytes, b.offsets, b.n_docs, b.n, b.ws, L);
-    }
-    {
-        LaunchScope k(ev, 2, s);
         if (v.family == FAMILY_O200K)
             hipLaunchKernelGGL(k_pieces<true>, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets,
                                b.n_docs, b.n, b.ws, L);

@@ -144,8 +144,8 @@ int toktier_last_status(void *workspace, void *stream, uint64_t *out_n_tokens);
 /* Kernel launches of one toktier_encode_batch call, in stream order (indices for the timed form).
  * An index may cover several launches of one step. */
 enum {
-    TOKTIER_K_INIT = 0,       /* clear the control block and look-back flags                    */
-    TOKTIER_K_SUMMARY,        /* per tile: the characters that decide the backward flags        */
+    TOKTIER_K_SUMMARY = 0,    /* clear the control block, look-back flags and token counters;   */
+                              /* per tile: the characters that decide the backward flags        */
     TOKTIER_K_PIECES,         /* UTF-8 decode + validation, automaton scan, piece starts        */
     TOKTIER_K_ROUTE,          /* every piece: single byte or whole-piece table hit, else BPE list */
     TOKTIER_K_GIANT_SEAMS,    /* pieces > 4096 bytes: seams no merge crosses, then chunks       */
@@ -166,7 +166,7 @@ enum {
  * (hipEvent_t passed as void*) on the stream immediately before and after each kernel launch:
  * events_before[k] / events_after[k] for launch k in the enum above.  Either array, and any entry,
  * may be NULL (not recorded).  Launches that a batch does not need (e.g. every kernel after
- * TOKTIER_K_INIT when total_bytes == 0) record nothing.  Errors as in toktier_encode_batch.
+ * TOKTIER_K_SUMMARY when total_bytes == 0) record nothing.  Errors as in toktier_encode_batch.
  */
 int toktier_encode_batch_timed(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
                                uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
