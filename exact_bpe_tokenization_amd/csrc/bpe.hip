@@ -7,13 +7,15 @@
 // that pair equals iterated single merges (for rank-consistent merge lists, which the loader
 // enforces); only pairs next to a completed merge need a new lookup.
 //
-//   (single-byte pieces and whole-piece table hits are resolved while pieces are formed; k_route does
-//   the same for pieces whose end the forming tile could not see; the rest arrive here as lists)
-//   k_bpe_lane   (<= 16 bytes) one lane per listed piece, sequence and ranks in registers; the
-//                textbook loop (leftmost lowest rank, merge, re-probe the two neighbours)
-//   k_bpe_seg    (17..32 and 33..64 bytes) 32 or 64 lanes per piece, one element per lane; rounds
-//                on ballot masks (see the kernel)
-//   k_bpe_block  one wavefront (pieces of 65..1024 bytes) or one 256-lane workgroup (up to 4096
+//   k_route      every piece: a single byte is its ID, a whole-piece table hit is its result; the
+//                others are listed by length
+//   k_bpe_small  the lists of pieces up to 128 bytes, one launch with a workgroup range per list:
+//                <= 16 bytes, one lane per piece (sorted by length per workgroup), the textbook loop
+//                in registers (leftmost lowest rank, merge, re-probe the two neighbours);
+//                17..32 bytes, 16 lanes x 2 rows per piece, four pieces per wavefront; 33..64 bytes,
+//                64 lanes per piece; 65..128 bytes, a wavefront with two elements per lane: rounds
+//                on ballot masks (see the kernels)
+//   k_bpe_block  one wavefront (pieces of 129..1024 bytes) or one 256-lane workgroup (up to 4096
 //                bytes) per piece; sequence in LDS; rounds: block-min of ranks, selection of the
 //                leftmost non-overlapping occurrences, prefix-sum compaction, neighbour re-probes
 //   k_bpe_giant  one 1024-lane workgroup per piece longer than that; the same rounds over device
@@ -313,6 +315,126 @@ __device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, ui
     }
 }
 
+// Pieces of 17..32 bytes: 16 lanes per piece and two elements per lane (element e of segment s in
+// lane 16 s + e % 16, row e / 16), four pieces per wavefront.  The rounds of k_bpe_seg on each piece's
+// 32-bit masks, two pieces packed in a 64-bit word (a piece's last element never holds a hit, so
+// neither shifts nor the carry of the addition cross from one piece into the next); compaction
+// through 32-entry LDS rows; the pairs to re-probe are gathered across the wavefront so that one
+// hash probe per lane serves all four pieces.
+
+// 64-bit row masks (bit 16 s + k: element k, resp. 16 + k, of piece s) -> piece masks, pieces 0 and 1
+// in the first word, 2 and 3 in the second (bits 32 t .. 32 t + 31: piece t, element order)
+__device__ __forceinline__ uint64_t zip_rows(uint64_t r0, uint64_t r1, int half)
+{
+    const uint64_t a = (r0 >> (32 * half)) & 0xFFFFFFFFull, b = (r1 >> (32 * half)) & 0xFFFFFFFFull;
+    return (a & 0xFFFFull) | ((b & 0xFFFFull) << 16) | ((a & 0xFFFF0000ull) << 16) | ((b & 0xFFFF0000ull) << 32);
+}
+
+__device__ void bpe_seg16x2(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
+                            uint32_t blk, uint32_t nblk)
+{
+    constexpr uint64_t EVEN = 0x5555555555555555ull, ODD = ~EVEN;
+    constexpr int NW = 4;   // wavefronts per workgroup
+    __shared__ uint32_t sid[NW][4][33], srk[NW][4][33], sra[NW][64], srb[NW][64], sres[NW][64];
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    uint32_t *pval = (uint32_t *)(ws + L.pval);
+    uint32_t *scratch = (uint32_t *)(ws + L.scratch);
+    const uint32_t *list = (const uint32_t *)(ws + L.miss32);
+    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
+    uint32_t *ccount = (uint32_t *)(ws + L.ccount);
+    const uint32_t count = ctrl->miss_count[1];
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6, sg = lane >> 4, k = lane & 15u;
+    const uint64_t below = (1ull << lane) - 1ull;
+    const uint32_t wave = (blk * blockDim.x + threadIdx.x) >> 6;
+    const uint32_t nwaves = (nblk * blockDim.x) >> 6;
+    for (uint32_t q0 = wave * 4u; q0 < count; q0 += nwaves * 4u) {
+        const uint32_t q = q0 + sg;
+        uint32_t p = 0, b0 = 0, n = 0;
+        bool chunk = false;
+        if (q < count) {
+            const uint32_t e = list[q];
+            chunk = (e & CHUNK_ITEM) != 0;
+            p = e & ~CHUNK_ITEM;
+            b0 = chunk ? cstart[p] : pstart[p];
+            n = chunk ? clen[p] : pstart[p + 1] - b0;   // up to 32 bytes
+        }
+        uint32_t id0 = k < n ? (uint32_t)bytes[b0 + k] : 0u;
+        uint32_t id1 = 16u + k < n ? (uint32_t)bytes[b0 + 16u + k] : 0u;
+        uint32_t rk0, rk1;
+        {
+            // the element after: the next lane of the row, or (last lane of row 0) row 1 of the first lane
+            const uint32_t d0 = __shfl_down(id0, 1, 64), f1 = __shfl(id1, lane & ~15u, 64);
+            const uint32_t nx0 = k == 15u ? f1 : d0, nx1 = __shfl_down(id1, 1, 64);
+            rk0 = k + 1u < n ? __ldg(v.r2 + ((id0 << 8) | nx0)) : NO_RANK;
+            rk1 = 17u + k < n ? __ldg(v.r2 + ((id1 << 8) | nx1)) : NO_RANK;
+        }
+        for (;;) {
+            uint32_t m = min(rk0, rk1);
+#pragma unroll
+            for (int d = 1; d < 16; d <<= 1) m = min(m, (uint32_t)__shfl_xor(m, d, 64));
+            const uint64_t H0 = __ballot(rk0 == m && m != NO_RANK), H1 = __ballot(rk1 == m && m != NO_RANK);
+            if ((H0 | H1) == 0) break;
+            const uint64_t V0 = __ballot(k < n), V1 = __ballot(16u + k < n);
+            uint64_t S[2], K[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint64_t W = zip_rows(H0, H1, h);
+                const uint64_t rsE = W & ~(W << 1) & EVEN;   // chains starting at an even element
+                const uint64_t runsE = W & ~(W + rsE);       // the hits of those chains
+                S[h] = (runsE & EVEN) | (W & ~runsE & ODD);
+                K[h] = zip_rows(V0, V1, h) & ~(S[h] << 1);
+            }
+            const uint32_t sh = 32u * (sg & 1u);
+            const uint32_t Ss = (uint32_t)((sg >> 1 ? S[1] : S[0]) >> sh);
+            const uint32_t Ks = (uint32_t)((sg >> 1 ? K[1] : K[0]) >> sh);
+            const uint32_t ms0 = (Ss >> k) & 1u, ms1 = (Ss >> (16u + k)) & 1u;
+            const uint32_t ns0 = (Ss >> (k + 1u)) & 1u, ns1 = k < 15u ? (Ss >> (17u + k)) & 1u : 0u;
+            if ((Ks >> k) & 1u) {
+                const uint32_t o = (uint32_t)__popc(Ks & ((1u << k) - 1u));
+                sid[w][sg][o] = ms0 ? 256u + m : id0;
+                srk[w][sg][o] = (ms0 || ns0) ? PENDING : rk0;
+            }
+            if ((Ks >> (16u + k)) & 1u) {
+                const uint32_t o = (uint32_t)__popc(Ks & ((1u << (16u + k)) - 1u));
+                sid[w][sg][o] = ms1 ? 256u + m : id1;
+                srk[w][sg][o] = (ms1 || ns1) ? PENDING : rk1;
+            }
+            n = (uint32_t)__popc(Ks);
+            id0 = sid[w][sg][k];
+            id1 = sid[w][sg][16u + k];
+            rk0 = k < n ? srk[w][sg][k] : NO_RANK;
+            rk1 = 16u + k < n ? srk[w][sg][16u + k] : NO_RANK;
+            const uint32_t nx0 = sid[w][sg][k + 1u], nx1 = sid[w][sg][17u + k];
+            // the last element of a piece has no pair
+            if (rk0 == PENDING && k + 1u >= n) rk0 = NO_RANK;
+            if (rk1 == PENDING && 17u + k >= n) rk1 = NO_RANK;
+            // gather the pairs to probe, one per lane, probe, scatter the ranks back
+            const bool pd0 = rk0 == PENDING, pd1 = rk1 == PENDING;
+            const uint64_t P0 = __ballot(pd0), P1 = __ballot(pd1);
+            const uint32_t c0 = (uint32_t)__popcll(P0), total = c0 + (uint32_t)__popcll(P1);
+            const uint32_t i0 = (uint32_t)__popcll(P0 & below), i1 = c0 + (uint32_t)__popcll(P1 & below);
+            for (uint32_t base = 0; base < total; base += 64u) {
+                if (pd0 && i0 - base < 64u) { sra[w][i0 - base] = id0; srb[w][i0 - base] = nx0; }
+                if (pd1 && i1 - base < 64u) { sra[w][i1 - base] = id1; srb[w][i1 - base] = nx1; }
+                uint32_t r = NO_RANK;
+                if (lane < total - base) r = pair_rank(v, sra[w][lane], srb[w][lane]);
+                sres[w][lane] = r;
+                if (pd0 && i0 - base < 64u) rk0 = sres[w][i0 - base];
+                if (pd1 && i1 - base < 64u) rk1 = sres[w][i1 - base];
+            }
+        }
+        if (n > 1 || chunk) {
+            if (k < n) scratch[b0 + k] = id0;
+            if (16u + k < n) scratch[b0 + 16u + k] = id1;
+        }
+        const bool head = k == 0 && q < count;
+        if (head && chunk) ccount[p] = n;
+        else if (head) pval[p] = n == 1 ? id0 : (PV_MULTI | n);
+        add_excess_wave(ws, L, p, head && !chunk ? n - 1 : 0u);
+    }
+}
+
 // One wavefront per piece of 65..SEG2_MAX bytes, two elements per lane (element e in lane e % 64 of
 // row e / 64): the rounds of k_bpe_seg on 128-bit masks (two ballots; shifts and the addition carry
 // between the words), compaction through a 128-entry LDS row per wavefront (a wavefront's LDS
@@ -419,23 +541,25 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_bpe_small(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
                                                    Layout L, uint32_t g16, uint32_t g32, uint32_t g64, uint32_t g128)
 {
+    // workgroup ranges in order of the units' round counts (longest first): workgroups are dispatched
+    // in order, so the long chains start at once and the many short ones fill in around them
     uint32_t b = blockIdx.x;
-    if (b < g16) {
-        bpe_lane(v, bytes, ws, L, b, g16);
+    if (b < g128) {
+        bpe_seg2(v, bytes, ws, L, b, g128);
         return;
     }
-    b -= g16;
-    if (b < g32) {
-        bpe_seg<32>(v, bytes, ws, L, 1, b, g32);
-        return;
-    }
-    b -= g32;
+    b -= g128;
     if (b < g64) {
         bpe_seg<64>(v, bytes, ws, L, 2, b, g64);
         return;
     }
     b -= g64;
-    if (b < g128) bpe_seg2(v, bytes, ws, L, b, g128);
+    if (b < g32) {
+        bpe_seg16x2(v, bytes, ws, L, b, g32);
+        return;
+    }
+    b -= g32;
+    if (b < g16) bpe_lane(v, bytes, ws, L, b, g16);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1041,10 +1165,10 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     }
     {
         // lists of <= 16, 17..32, 33..64 and 65..128 bytes: at most n / 1, n / 17, n / 33, n / 65 items;
-        // 256 lane items, 8, 4 and 4 pieces per workgroup
-        const uint64_t b16 = b.n / 256 + 1, b32 = b.n / 17 / 8 + 1, b64 = b.n / 33 / 4 + 1, b128 = b.n / 65 / 4 + 1;
+        // 256 lane items, 16, 4 and 4 pieces per workgroup
+        const uint64_t b16 = b.n / 256 + 1, b32 = b.n / 17 / 16 + 1, b64 = b.n / 33 / 4 + 1, b128 = b.n / 65 / 4 + 1;
         const uint32_t g16 = b16 > 2048 ? 2048u : (uint32_t)b16, g32 = b32 > 2048 ? 2048u : (uint32_t)b32;
-        const uint32_t g64 = b64 > 1024 ? 1024u : (uint32_t)b64, g128 = b128 > 1024 ? 1024u : (uint32_t)b128;
+        const uint32_t g64 = b64 > 256 ? 256u : (uint32_t)b64, g128 = b128 > 256 ? 256u : (uint32_t)b128;
         LaunchScope k(ev, 4, s);
         hipLaunchKernelGGL(k_bpe_small, dim3(g16 + g32 + g64 + g128), dim3(256), 0, s, v, b.bytes, b.ws, L, g16, g32,
                            g64, g128);

@@ -236,7 +236,7 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // ---------------------------------------------------------------------------------------------
 // workspace layout for n input bytes
 struct Layout {
-    uint64_t ctrl, cc, tbwd, tflag_state, tflag_cnt, pstart, pval, tokoff, scratch, bin_wave,
+    uint64_t ctrl, cc, tbwd, tdoc, tflag_state, tflag_cnt, pstart, pval, tokoff, scratch, bin_wave,
         bin_block, bin_giant, miss16, miss32, miss64, miss128, g_ids, g_rank_a, g_rank_b, tilex, cstart, clen, ccount,
         gc0, gnc, gsafe, cpiece, total;
     uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
@@ -258,6 +258,7 @@ inline Layout make_layout(uint64_t n)
     L.ctrl = o;        o += align256(sizeof(Ctrl));
     L.cc = o;
     L.tbwd = o;        o += align256((uint64_t)L.n_tiles + 1);
+    L.tdoc = o;        o += align256(8ull * L.n_tiles);
     L.tflag_state = o; o += align256(16ull * L.n_tiles);
     L.tflag_cnt = o;   o += align256(8ull * L.n_tiles);
     L.tilex = o;       o += align256(4ull * L.n_scan_tiles);

@@ -253,9 +253,13 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
     if (blockIdx.x >= L.n_tiles) return;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
     const uint64_t hi = min(lo + TILE, n);
-    // document starts in [lo, hi + 4): indices [d0, d1) of offsets (empty documents repeat one)
-    const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, lo);
-    const uint32_t d1 = wave_lower_bound(offsets, n_docs + 1, hi + 4);
+    // document starts in the pieces kernel's byte window of this tile, [lo - RAW_LEAD, lo + TILE +
+    // RAW_TAIL): indices [d0, d1) of offsets (empty documents repeat one), kept for that kernel; the
+    // window holds [lo, hi + 4), which the search below needs
+    const uint64_t lo_w = lo >= (uint64_t)RAW_LEAD ? lo - RAW_LEAD : 0;
+    const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, lo_w);
+    const uint32_t d1 = wave_lower_bound(offsets, n_docs + 1, lo + TILE + RAW_TAIL);
+    if (lane == 0) ((uint2 *)(ws + L.tdoc))[blockIdx.x] = make_uint2(d0, d1);
     uint32_t na = BK_KEEP, au = BK_KEEP;
     // 256 bytes per step, 4 per lane
     for (uint64_t w = lo; w < hi && (na == BK_KEEP || au == BK_KEEP); w += 256) {
@@ -493,11 +497,10 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         }
         ((uint32_t *)sraw)[j] = w;
     }
-    if (wid == 0) {
-        const uint64_t lo_p = base < 0 ? 0 : (uint64_t)base, hi_p = (uint64_t)(base + SPAN);
-        const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, lo_p);
-        const uint32_t d1 = wave_lower_bound(offsets, n_docs + 1, hi_p);
-        if (lane == 0) { s_d0 = d0; s_d1 = d1; }
+    if (tid == 0) {   // documents starting in [base, base + SPAN), found by k_summary
+        const uint2 dd = ((const uint2 *)(ws + L.tdoc))[tile];
+        s_d0 = dd.x;
+        s_d1 = dd.y;
     }
     // document offsets must start at 0, never decrease and end at n
     bool bad_offs = false;
