@@ -137,9 +137,11 @@ __device__ __forceinline__ void st_flag16(uint32_t *p, const M16 &m, uint32_t ki
         __hip_atomic_store(p + i, (m.w[i] & 0x3FFFFFFFu) | (kind << 30), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Automaton state entering `tile`.  Wave 0 reads the flags of 64 predecessors per step and composes
-// their maps (farthest first) with byte permutes; a prefix or a constant composition ends the walk.
-// The batch starts in S_ST.
+// Automaton state entering `tile`.  Wave 0 reads the flags of 64 predecessors per step.  The walk
+// ends at the nearest predecessor whose flag fixes the state: a prefix, or a map that sends every
+// state to one state (an 8 KiB tile of text nearly always has one); only the predecessors up to it
+// must have published, and their maps are composed (farthest first) with byte permutes.  The batch
+// starts in S_ST.
 __device__ uint32_t lookback_state(const uint32_t *flags, uint32_t tile)
 {
     const uint32_t lane = threadIdx.x & 63u;
@@ -158,12 +160,14 @@ __device__ uint32_t lookback_state(const uint32_t *flags, uint32_t tile)
         }
         const uint32_t k0 = f[0] >> 30;
         const uint32_t kind = ((f[1] >> 30) == k0 && (f[2] >> 30) == k0 && (f[3] >> 30) == k0) ? k0 : 0u;
-        const uint64_t pre = __ballot(kind == FLAG_PREFIX), nr = __ballot(kind == 0);
-        const uint32_t kp = pre ? (uint32_t)__ffsll((unsigned long long)pre) - 1u : 64u;
+        M16 x = M16{{f[0] & 0x0F0F0F0Fu, f[1] & 0x0F0F0F0Fu, f[2] & 0x0F0F0F0Fu, f[3] & 0x0F0F0F0Fu}};
+        const bool fixes = kind == FLAG_PREFIX || (kind == FLAG_AGG && is_const16(x));
+        const uint64_t st = __ballot(fixes), nr = __ballot(kind == 0);
+        const uint32_t kp = st ? (uint32_t)__ffsll((unsigned long long)st) - 1u : 64u;
         const uint64_t need = kp >= 63 ? ~0ull : ((2ull << kp) - 1);
         if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
-        M16 x = m16_identity();
-        if (lane <= kp) x = M16{{f[0] & 0x0F0F0F0Fu, f[1] & 0x0F0F0F0Fu, f[2] & 0x0F0F0F0Fu, f[3] & 0x0F0F0F0Fu}};
+        if (kp == 0) return byte16(acc, byte16(shfl16(x, 0), 0) & 15u) & 15u;
+        if (lane > kp) x = m16_identity();
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const M16 y = shfl_down16(x, d);
