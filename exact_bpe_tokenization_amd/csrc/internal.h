@@ -139,12 +139,10 @@ __device__ __forceinline__ uint64_t lookback_sum(const uint64_t *flags, uint32_t
         const uint32_t kp = pre ? (uint32_t)__ffsll((unsigned long long)pre) - 1u : 64u;
         const uint64_t need = kp >= 63 ? ~0ull : ((2ull << kp) - 1);
         if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
-        uint64_t v = lane <= kp ? (f & ((1ull << 62) - 1)) : 0;
+        // (the counts are piece counts: every partial sum is below 2^32)
+        uint32_t v = lane <= kp ? (uint32_t)f : 0u;
 #pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) {
-            uint32_t lo = __shfl_xor((uint32_t)v, d, 64), hi = __shfl_xor((uint32_t)(v >> 32), d, 64);
-            v += ((uint64_t)hi << 32) | lo;
-        }
+        for (int d = 32; d >= 1; d >>= 1) v += (uint32_t)__shfl_xor(v, d, 64);
         sum += v;
         if (kp < 64) return sum;
         top -= 64;
@@ -258,7 +256,7 @@ inline Layout make_layout(uint64_t n)
     L.ctrl = o;        o += align256(sizeof(Ctrl));
     L.cc = o;
     L.tbwd = o;        o += align256((uint64_t)L.n_tiles + 1);
-    L.tdoc = o;        o += align256(8ull * L.n_tiles);
+    L.tdoc = o;        o += align256(16ull * L.n_tiles);
     L.tflag_state = o; o += align256(16ull * L.n_tiles);
     L.tflag_cnt = o;   o += align256(8ull * L.n_tiles);
     L.tilex = o;       o += align256(4ull * L.n_scan_tiles);

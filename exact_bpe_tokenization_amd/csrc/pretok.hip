@@ -263,7 +263,10 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
     const uint64_t lo_w = lo >= (uint64_t)RAW_LEAD ? lo - RAW_LEAD : 0;
     const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, lo_w);
     const uint32_t d1 = wave_lower_bound(offsets, n_docs + 1, lo + TILE + RAW_TAIL);
-    if (lane == 0) ((uint2 *)(ws + L.tdoc))[blockIdx.x] = make_uint2(d0, d1);
+    if (lane == 0) {   // and the first two of those starts, so that the pieces kernel seldom reads offsets
+        const uint32_t o0 = d0 < d1 ? (uint32_t)offsets[d0] : 0u, o1 = d0 + 1 < d1 ? (uint32_t)offsets[d0 + 1] : 0u;
+        ((uint4 *)(ws + L.tdoc))[blockIdx.x] = make_uint4(d0, d1, o0, o1);
+    }
     uint32_t na = BK_KEEP, au = BK_KEEP;
     // 256 bytes per step, 4 per lane
     for (uint64_t w = lo; w < hi && (na == BK_KEEP || au == BK_KEEP); w += 256) {
@@ -451,7 +454,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     __shared__ uint32_t sbkw[NW];
     __shared__ uint4 swmap[NW];
     __shared__ uint32_t swcnt[NW], swstate[NW];
-    __shared__ uint32_t s_tile, s_carry, s_base, s_d0, s_d1;
+    __shared__ uint32_t s_tile, s_carry, s_base, s_d0, s_d1, s_o0, s_o1;
 
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint8_t *tbwd = ws + L.tbwd;
@@ -482,6 +485,10 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     const uint32_t tile = s_tile;
     const uint64_t lo = (uint64_t)tile * TILE;
     const int64_t base = (int64_t)lo - RAW_LEAD;
+    // summaries of the next 64 tiles for the backward carry (wave 0), loaded now so that the load
+    // overlaps the decode
+    uint32_t bk_first = BK_T | (BK_T << 2);
+    if (wid == 0 && tile + 1 + lane < L.n_tiles) bk_first = (ws + L.tbwd)[tile + 1 + lane];
 
     // raw bytes [lo - 4, lo + TILE + 24), as 32-bit words
     // (interior words from two aligned 4-byte loads, which never leave the pages of the bytes they
@@ -502,19 +509,22 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         ((uint32_t *)sraw)[j] = w;
     }
     if (tid == 0) {   // documents starting in [base, base + SPAN), found by k_summary
-        const uint2 dd = ((const uint2 *)(ws + L.tdoc))[tile];
+        const uint4 dd = ((const uint4 *)(ws + L.tdoc))[tile];
         s_d0 = dd.x;
         s_d1 = dd.y;
+        s_o0 = dd.z;
+        s_o1 = dd.w;
     }
     // document offsets must start at 0, never decrease and end at n
     bool bad_offs = false;
-    for (uint64_t d = (uint64_t)tile * PRE_THREADS + tid; d < n_docs; d += (uint64_t)gridDim.x * PRE_THREADS)
+    for (uint64_t d = (uint64_t)tile * PRE_THREADS + tid; d < n_docs; d += (uint64_t)L.n_tiles * PRE_THREADS)
         if (offsets[d] > offsets[d + 1]) bad_offs = true;
     if (tile == 0 && tid == 0 && (offsets[0] != 0 || offsets[n_docs] != n)) bad_offs = true;
     if (bad_offs) atomicOr(&ctrl->status, ST_BAD_OFFSETS);
     __syncthreads();
     for (uint32_t d = s_d0 + tid; d < s_d1; d += PRE_THREADS) {
-        int64_t j = (int64_t)offsets[d] - base;
+        const uint64_t od = d == s_d0 ? s_o0 : d == s_d0 + 1 ? s_o1 : offsets[d];
+        int64_t j = (int64_t)od - base;
         if (j >= 0 && j < SPAN) atomicOr(&sdoc[j >> 5], 1u << (j & 31));
     }
     __syncthreads();
@@ -603,7 +613,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         uint32_t na = BK_KEEP, au = BK_KEEP;
         for (uint32_t t0 = tile + 1; na == BK_KEEP || au == BK_KEEP; t0 += 64) {
             uint32_t t = t0 + lane;
-            uint32_t x = t < L.n_tiles ? (uint32_t)tbwd[t] : (BK_T | (BK_T << 2));
+            uint32_t x = t0 == tile + 1 ? bk_first : t < L.n_tiles ? (uint32_t)tbwd[t] : (BK_T | (BK_T << 2));
             uint64_t mna = __ballot((x & 3u) != 0), mau = __ballot((x >> 2) != 0);
             uint32_t xna = __shfl(x, mna ? __ffsll((unsigned long long)mna) - 1 : 0, 64);
             uint32_t xau = __shfl(x, mau ? __ffsll((unsigned long long)mau) - 1 : 0, 64);
@@ -806,12 +816,13 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
     if (L.n_tiles == 0) return hipGetLastError();
     {
         LaunchScope k(ev, 1, s);
+        const dim3 grid(L.n_tiles);
         if (v.family == FAMILY_O200K)
-            hipLaunchKernelGGL(k_pieces<true>, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets,
-                               b.n_docs, b.n, b.ws, L);
+            hipLaunchKernelGGL(k_pieces<true>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs, b.n,
+                               b.ws, L);
         else
-            hipLaunchKernelGGL(k_pieces<false>, dim3(L.n_tiles), dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets,
-                               b.n_docs, b.n, b.ws, L);
+            hipLaunchKernelGGL(k_pieces<false>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs, b.n,
+                               b.ws, L);
     }
     return hipGetLastError();
 }
