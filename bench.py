@@ -45,7 +45,7 @@ LATENCY = ("c1_ec4k", "c2_at100k", "c3_mix1m", "c5_adv4m4")
 UNITS = {
     "summary": "all", "pieces": "all", "route": "all", "emit": "all", "gather_long": "binned",
     "bpe_small": "le128",
-    "bpe_wave": "wave", "giant_seams": "giant", "bpe_block": "block", "bpe_giant": "giant", "giant_join": "giant",
+    "bpe_wave": "wave", "giant_seams": "giant", "bpe_block": "block", "bpe_giant": "giant",
 }
 
 

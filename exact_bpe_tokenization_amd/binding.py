@@ -26,8 +26,8 @@ EXPORTS = ("toktier_load_vocab", "toktier_free_vocab", "toktier_vocab_info", "to
            "toktier_unicode_table_sha256")
 
 # kernel launches of one encode call, in stream order (TOKTIER_K_* in toktier.h)
-KERNELS = ("summary", "pieces", "route", "giant_seams", "bpe_small", "bpe_wave", "bpe_block", "bpe_giant",
-           "giant_join", "emit", "gather_long")
+KERNELS = ("summary", "pieces", "route", "giant_seams", "bpe_small", "bpe_wave", "bpe_block", "bpe_giant", "emit",
+           "gather_long")
 
 
 class ToktierError(RuntimeError):

@@ -827,6 +827,8 @@ __device__ __forceinline__ uint32_t safe_word(uint32_t a, uint32_t b0)
 
 // k_gsafe: every position of every giant piece is tested; workgroups share out 1024-position
 // blocks (aligned to absolute positions) of each piece in turn
+__device__ void giant_cut(const DevVocab &v, uint8_t *ws, const Layout &L);
+
 __global__ __launch_bounds__(1024) void k_gsafe(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws, Layout L)
 {
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
@@ -835,8 +837,8 @@ __global__ __launch_bounds__(1024) void k_gsafe(DevVocab v, const uint8_t *__res
     uint32_t *bm = (uint32_t *)(ws + L.gsafe);
     const uint32_t count = ctrl->bin_count[2];
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
-    if (!v.str) return;
-    for (uint32_t g = 0; g < count; ++g) {
+    if (count == 0) return;
+    for (uint32_t g = 0; v.str && g < count; ++g) {
         const uint32_t p = list[g];
         const uint32_t b0 = pstart[p], n = pstart[p + 1] - b0;
         const uint32_t first = b0 / 1024, last = (b0 + n - 1) / 1024;
@@ -850,6 +852,7 @@ __global__ __launch_bounds__(1024) void k_gsafe(DevVocab v, const uint8_t *__res
             if (lane == 32 && a0 + 63 > b0 && a0 + 32 < b0 + n) bm[safe_word(a0 + 32, b0)] = (uint32_t)(m >> 32);
         }
     }
+    if (last_workgroup(&((Ctrl *)(ws + L.ctrl))->done_seams)) giant_cut(v, ws, L);
 }
 
 // first and last safe position of window [lo, hi) of the piece at b0 (NO_PIECE if none); lo > b0
@@ -867,14 +870,14 @@ __device__ __forceinline__ void window_safe(const uint32_t *bm, uint32_t b0, uin
     }
 }
 
-// k_gcut: one workgroup per giant piece turns the bitmap into chunks.  The piece is divided into
+// giant_cut: the last workgroup of k_gsafe turns the bitmap into chunks, piece by piece.  The piece is divided into
 // windows of GCH positions; every window with a safe position is cut at its first one (chunks of
 // about GCH bytes where seams are common), and a window followed by one without any safe position
 // is also cut at its last one, so that a stretch without seams (typically a repeated character,
 // which needs few merge rounds) is a chunk of its own.  Cuts come out sorted; a workgroup scan
 // places them.  Chunks take consecutive slots of the chunk table (unused reserved slots: length 0);
 // chunks of up to SEG2_MAX bytes are also listed for the lane and segment kernels.
-__global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, Layout L)
+__device__ void giant_cut(const DevVocab &v, uint8_t *ws, const Layout &L)
 {
     constexpr uint32_t NT = 1024, NW = NT / 64;
     __shared__ uint32_t swsum[NW];
@@ -887,7 +890,7 @@ __global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, La
     uint32_t *gc0 = (uint32_t *)(ws + L.gc0), *gnc = (uint32_t *)(ws + L.gnc);
     const uint32_t count = ctrl->bin_count[2];
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
-    for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
+    for (uint32_t g = 0; g < count; ++g) {
         const uint32_t p = list[g];
         const uint32_t b0 = pstart[p], n = pstart[p + 1] - b0, end = b0 + n;
         const uint32_t nwin = v.str ? (n + GCH - 1) / GCH : 0u;
@@ -962,10 +965,10 @@ __global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, La
     }
 }
 
-// k_gassemble: one workgroup per giant piece.  A scan of the chunks' token counts gives each chunk's
-// place in the piece's output (cdest, in the chunk-length array, no longer needed); the piece's
-// token count is recorded, and the output gather copies each chunk from scratch.
-__global__ __launch_bounds__(1024) void k_gassemble(uint8_t *ws, Layout L)
+// giant_join: the last workgroup of k_bpe_giant, piece by piece.  A scan of the chunks' token counts
+// gives each chunk's place in the piece's output (cdest, in the chunk-length array, no longer
+// needed); the piece's token count is recorded, and the output gather copies each chunk from scratch.
+__device__ void giant_join(uint8_t *ws, const Layout &L)
 {
     constexpr uint32_t NT = 1024, NW = NT / 64;
     __shared__ uint32_t swsum[NW];
@@ -977,7 +980,7 @@ __global__ __launch_bounds__(1024) void k_gassemble(uint8_t *ws, Layout L)
     const uint32_t *gc0 = (const uint32_t *)(ws + L.gc0), *gnc = (const uint32_t *)(ws + L.gnc);
     const uint32_t count = ctrl->bin_count[2];
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
-    for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
+    for (uint32_t g = 0; g < count; ++g) {
         const uint32_t p = list[g], c0 = gc0[g], nc = gnc[g];
         if (tid == 0) s_acc = 0;
         __syncthreads();
@@ -1025,9 +1028,10 @@ __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const u
     __shared__ uint32_t red[NT / 64 + 1];
     __shared__ int32_t redi[NT / 64 + 1];
     __shared__ int32_t s_last_cs;
-    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *pval = (uint32_t *)(ws + L.pval);
+    if (ctrl->bin_count[2] == 0) return;   // no giant pieces: no chunks to encode or join
     const uint32_t count = ctrl->n_chunks;
     const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
     uint32_t *ccount = (uint32_t *)(ws + L.ccount);
@@ -1137,6 +1141,7 @@ __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const u
         if (tid == 0) ccount[q] = n;
         __syncthreads();
     }
+    if (last_workgroup(&ctrl->done_giant)) giant_join(ws, L);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1160,8 +1165,6 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
         LaunchScope k(ev, 3, s);
         const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
         hipLaunchKernelGGL(k_gsafe, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
-        const uint32_t gc = L.cap_giant < 64 ? L.cap_giant : 64;
-        hipLaunchKernelGGL(k_gcut, dim3(gc), dim3(1024), 0, s, v, b.ws, L);
     }
     {
         // lists of <= 16, 17..32, 33..64 and 65..128 bytes: at most n / 1, n / 17, n / 33, n / 65 items;
@@ -1188,10 +1191,6 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     {
         LaunchScope k(ev, 7, s);
         hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
-    }
-    {
-        LaunchScope k(ev, 8, s);
-        hipLaunchKernelGGL(k_gassemble, dim3(gg), dim3(1024), 0, s, b.ws, L);
     }
     return hipGetLastError();
 }

@@ -195,12 +195,12 @@ hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offse
 {
     const Layout &L = b.L;
     {
-        LaunchScope k(ev, 9, s);
+        LaunchScope k(ev, 8, s);
         hipLaunchKernelGGL(k_emit, dim3(L.n_scan_tiles), dim3(SCAN_THREADS), 0, s, b.ws, L, b.offsets, b.n_docs,
                            b.n, out_ids, out_offsets);
     }
     if (b.n) {
-        LaunchScope k(ev, 10, s);
+        LaunchScope k(ev, 9, s);
         uint32_t gl = L.cap_wave + L.cap_chunks < 1024 ? L.cap_wave + L.cap_chunks : 1024;
         hipLaunchKernelGGL(k_gather_long, dim3(gl), dim3(256), 0, s, b.ws, L, out_ids);
     }

@@ -227,7 +227,9 @@ struct Ctrl {
     uint32_t bin_count[3];     // wave, block, giant bins
     uint32_t miss_count[4];    // pieces left for BPE: <= 16, 17..32, 33..64, 65..128 bytes
     uint32_t n_chunks;         // chunk slots reserved for giant pieces
-    uint32_t pad[52];
+    uint32_t done_seams;       // workgroups of k_gsafe done (the last one cuts the giant pieces)
+    uint32_t done_giant;       // workgroups of k_bpe_giant done (the last one joins the chunks)
+    uint32_t pad[50];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
@@ -404,6 +406,22 @@ __device__ __forceinline__ uint32_t *route_list(uint8_t *ws, const Layout &L, ui
 __device__ __forceinline__ uint32_t *route_count(Ctrl *ctrl, uint32_t r)
 {
     return r < 4 ? &ctrl->miss_count[r] : &ctrl->bin_count[r - 4];
+}
+
+// Called by every thread of a workgroup when it has written its results: true in the workgroup that
+// finishes last, which then sees every other workgroup's writes (each thread's writes are fenced at
+// agent scope before the count; the last workgroup's threads fence again before their loads).
+__device__ __forceinline__ bool last_workgroup(uint32_t *done)
+{
+    __shared__ uint32_t s_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+    __syncthreads();
+    const bool last = s_last != 0;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return last;
 }
 
 // Wavefront form of the same counter update, called by all 64 lanes: lane i contributes the

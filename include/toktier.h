@@ -148,14 +148,16 @@ enum {
                               /* per tile: the characters that decide the backward flags        */
     TOKTIER_K_PIECES,         /* UTF-8 decode + validation, automaton scan, piece starts        */
     TOKTIER_K_ROUTE,          /* every piece: single byte or whole-piece table hit, else BPE list */
-    TOKTIER_K_GIANT_SEAMS,    /* pieces > 4096 bytes: seams no merge crosses, then chunks       */
+    TOKTIER_K_GIANT_SEAMS,    /* pieces > 4096 bytes: seams no merge crosses, then (last       */
+                              /* workgroup) the chunks                                          */
     TOKTIER_K_BPE_SMALL,      /* BPE of unresolved pieces and chunks of <= 128 bytes: lane per  */
                               /* piece (<= 16), 32-lane segments (<= 32), a wavefront (<= 64),  */
                               /* a wavefront with two elements per lane (<= 128), one launch    */
     TOKTIER_K_BPE_WAVE,       /* BPE, one wavefront per piece of 129..1024 bytes                */
     TOKTIER_K_BPE_BLOCK,      /* BPE, one workgroup per piece of 1025..4096 bytes or chunk      */
-    TOKTIER_K_BPE_GIANT,      /* BPE, one workgroup per longer chunk, sequence in device memory */
-    TOKTIER_K_GIANT_JOIN,     /* each giant piece's token count and its chunks' output places   */
+    TOKTIER_K_BPE_GIANT,      /* BPE, one workgroup per longer chunk, sequence in device memory; */
+                              /* then (last workgroup) each giant piece's token count and its    */
+                              /* chunks' output places                                           */
     TOKTIER_K_EMIT,           /* token-offset scan, ID gather, per-document token offsets       */
     TOKTIER_K_GATHER_LONG,    /* ID gather of the pieces longer than 128 bytes                  */
     TOKTIER_K_COUNT
