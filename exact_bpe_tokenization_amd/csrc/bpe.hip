@@ -286,8 +286,12 @@ __device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, ui
         uint32_t rk = k + 1 < n ? __ldg(v.r2 + ((id << 8) | nx)) : NO_RANK;
         for (;;) {
             uint32_t m = rk;
+            if (G == 64) m = wave_min(m);
+            else if (G == 16) m = row_min16(m);
+            else {
 #pragma unroll
-            for (int d = G / 2; d >= 1; d >>= 1) m = min(m, (uint32_t)__shfl_xor(m, d, 64));
+                for (int d = G / 2; d >= 1; d >>= 1) m = min(m, (uint32_t)__shfl_xor(m, d, 64));
+            }
             const uint64_t H = __ballot(rk == m && m != NO_RANK);
             if (H == 0) break;
             const uint64_t rsE = H & ~(H << 1) & EVEN;          // chains starting at an even lane
@@ -371,8 +375,7 @@ __device__ void bpe_seg16x2(const DevVocab &v, const uint8_t *__restrict__ bytes
         }
         for (;;) {
             uint32_t m = min(rk0, rk1);
-#pragma unroll
-            for (int d = 1; d < 16; d <<= 1) m = min(m, (uint32_t)__shfl_xor(m, d, 64));
+            m = row_min16(m);   // a segment is a DPP row
             const uint64_t H0 = __ballot(rk0 == m && m != NO_RANK), H1 = __ballot(rk1 == m && m != NO_RANK);
             if ((H0 | H1) == 0) break;
             const uint64_t V0 = __ballot(k < n), V1 = __ballot(16u + k < n);
@@ -478,8 +481,7 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
         uint32_t rk1 = 65 + lane < n ? __ldg(v.r2 + ((id1 << 8) | nx1)) : NO_RANK;
         for (;;) {
             uint32_t m = min(rk0, rk1);
-#pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) m = min(m, (uint32_t)__shfl_xor(m, d, 64));
+            m = wave_min(m);
             if (m == NO_RANK) break;
             const uint64_t H0 = __ballot(rk0 == m), H1 = __ballot(rk1 == m);
             uint64_t s0, s1;
@@ -568,8 +570,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
 template <int NT>
 __device__ __forceinline__ uint32_t block_min(uint32_t x, uint32_t *red)
 {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x = min(x, (uint32_t)__shfl_xor(x, d, 64));
+    x = wave_min(x);
     if (NT == 64) return x;
     const uint32_t lane = threadIdx.x & 63u, wid = threadIdx.x >> 6;
     if (lane == 0) red[wid] = x;

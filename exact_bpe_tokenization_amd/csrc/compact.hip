@@ -64,14 +64,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
     for (int it = 0; it < IT; ++it) {
         const uint32_t i = wb + it * 64u + lane;
         const uint32_t c = i >= end ? 0u : (pv[it] & PV_MULTI) ? (pv[it] & PV_COUNT) : 1u;
-        uint32_t inc = c;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t y = __shfl_up(inc, d, 64);
-            if (lane >= (uint32_t)d) inc += y;
-        }
+        const uint32_t inc = wave_incl_sum(c);
         soff[wid * (64u * IT) + it * 64u + lane] = run + inc - c;   // offset inside the wavefront's run
-        run += __shfl(inc, 63, 64);
+        run += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
     }
     if (lane == 0) { swsum[wid] = run; sxs[wid] = xs; }
     __syncthreads();

@@ -720,10 +720,21 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     // wavefront scan of the chunk maps; the wavefronts' maps are scanned by wave 0, which also
     // takes the state entering the tile from the look-back
     M16 incl = acc;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const M16 y = shfl_up16(incl, d);
-        if (lane >= (uint32_t)d) incl = compose16(y, incl);
+    {
+        // inside each row of 16 lanes (DPP row shifts), then across rows (row broadcasts of lanes 15
+        // and 31), composing the farther map first
+        const uint32_t r = lane & 15u, row = lane >> 4;
+#define TT_DPP4(ctrl, rmask) M16{{(uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl.w[0], ctrl, rmask, 0xF, false), \
+                                  (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl.w[1], ctrl, rmask, 0xF, false), \
+                                  (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl.w[2], ctrl, rmask, 0xF, false), \
+                                  (uint32_t)__builtin_amdgcn_update_dpp(0, (int)incl.w[3], ctrl, rmask, 0xF, false)}}
+        { const M16 y = TT_DPP4(0x111, 0xF); if (r >= 1) incl = compose16(y, incl); }
+        { const M16 y = TT_DPP4(0x112, 0xF); if (r >= 2) incl = compose16(y, incl); }
+        { const M16 y = TT_DPP4(0x114, 0xF); if (r >= 4) incl = compose16(y, incl); }
+        { const M16 y = TT_DPP4(0x118, 0xF); if (r >= 8) incl = compose16(y, incl); }
+        { const M16 y = TT_DPP4(0x142, 0xA); if (row & 1u) incl = compose16(y, incl); }   // row_bcast:15
+        { const M16 y = TT_DPP4(0x143, 0xC); if (row >= 2) incl = compose16(y, incl); }   // row_bcast:31
+#undef TT_DPP4
     }
     M16 excl = shfl_up16(incl, 1);
     if (lane == 0) excl = m16_identity();
@@ -761,12 +772,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         mask |= ((b >> 4) & 1u) << k;
         s = b & 15u;
     }
-    uint32_t cnt = __popc(mask), icnt = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(icnt, d, 64);
-        if (lane >= (uint32_t)d) icnt += y;
-    }
+    const uint32_t cnt = __popc(mask), icnt = wave_incl_sum(cnt);
     if (lane == 63) swcnt[wid] = icnt;
     __syncthreads();
     uint32_t before = icnt - cnt, total = 0;
