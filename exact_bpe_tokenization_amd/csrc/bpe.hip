@@ -221,8 +221,7 @@ __device__ void bpe_lane(const DevVocab &v, const uint8_t *__restrict__ bytes, u
         b0 = s_b0[tid];
         len = s_len[tid];
         uint32_t wmax = len;
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) wmax = max(wmax, (uint32_t)__shfl_xor(wmax, d, 64));
+        wmax = wave_max(wmax);
         if (wmax <= 8u) lane_bpe<8>(v, bytes, ws, L, e, b0, len);
         else if (wmax <= 12u) lane_bpe<12>(v, bytes, ws, L, e, b0, len);
         else lane_bpe<16>(v, bytes, ws, L, e, b0, len);
@@ -282,7 +281,7 @@ __device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, ui
             n = chunk ? clen[p] : pstart[p + 1] - b0;   // up to G bytes
         }
         uint32_t id = k < n ? (uint32_t)bytes[b0 + k] : 0u;
-        uint32_t nx = __shfl_down(id, 1, 64);
+        uint32_t nx = wave_next(id);
         uint32_t rk = k + 1 < n ? __ldg(v.r2 + ((id << 8) | nx)) : NO_RANK;
         for (;;) {
             uint32_t m = rk;
@@ -307,7 +306,7 @@ __device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, ui
             id = lane_push(dst, me_sel ? 256u + m : id);
             rk = lane_push(dst, (me_sel || nx_sel) ? PENDING : rk);
             n = kept_seg;
-            nx = __shfl_down(id, 1, 64);
+            nx = wave_next(id);
             if (k >= n) rk = NO_RANK;
             else if (rk == PENDING) rk = k + 1 < n ? pair_rank(v, id, nx) : NO_RANK;
         }
@@ -474,9 +473,8 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
         uint32_t n = chunk ? clen[p] : pstart[p + 1] - b0;   // up to 128 bytes
         uint32_t id0 = lane < n ? (uint32_t)bytes[b0 + lane] : 0u;
         uint32_t id1 = 64 + lane < n ? (uint32_t)bytes[b0 + 64 + lane] : 0u;
-        uint32_t nx0 = __shfl_down(id0, 1, 64), nx1 = __shfl_down(id1, 1, 64);
-        const uint32_t f1 = __shfl(id1, 0, 64);
-        if (lane == 63) nx0 = f1;
+        uint32_t nx0 = wave_next(id0), nx1 = wave_next(id1);
+        if (lane == 63) nx0 = (uint32_t)__builtin_amdgcn_readlane((int)id1, 0);
         uint32_t rk0 = lane + 1 < n ? __ldg(v.r2 + ((id0 << 8) | nx0)) : NO_RANK;
         uint32_t rk1 = 65 + lane < n ? __ldg(v.r2 + ((id1 << 8) | nx1)) : NO_RANK;
         for (;;) {
@@ -514,10 +512,9 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
             rk0 = srk[w][lane];
             id1 = sid[w][64 + lane];
             rk1 = srk[w][64 + lane];
-            nx0 = __shfl_down(id0, 1, 64);
-            nx1 = __shfl_down(id1, 1, 64);
-            const uint32_t g1 = __shfl(id1, 0, 64);
-            if (lane == 63) nx0 = g1;
+            nx0 = wave_next(id0);
+            nx1 = wave_next(id1);
+            if (lane == 63) nx0 = (uint32_t)__builtin_amdgcn_readlane((int)id1, 0);
             if (lane >= n) rk0 = NO_RANK;
             else if (rk0 == PENDING) rk0 = lane + 1 < n ? pair_rank(v, id0, nx0) : NO_RANK;
             if (64 + lane >= n) rk1 = NO_RANK;

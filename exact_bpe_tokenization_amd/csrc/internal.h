@@ -112,6 +112,60 @@ __host__ __device__ __forceinline__ uint64_t wb_hash(uint64_t k0, uint64_t k1, u
 }
 
 // ---------------------------------------------------------------------------------------------
+// wavefront primitives on DPP moves
+
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves (no LDS round trips): a
+// Hillis-Steele scan inside each row of 16 lanes (row_shr 1, 2, 4, 8), then row 0's total added to
+// row 1 and row 2's to row 3 (row_bcast:15), then rows 0-1's total to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x)
+{
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
+// The value of the next lane (lane 63: 0), by a DPP wavefront shift.
+__device__ __forceinline__ uint32_t wave_next(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x130, 0xF, 0xF, true);   // wave_shl:1
+}
+
+// Maximum over the wavefront (wavefront-uniform result).
+__device__ __forceinline__ uint32_t wave_max(uint32_t x)
+{
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false));   // row_ror:1
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false));   // row_ror:2
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false));   // row_ror:4
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false));   // row_ror:8
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// Minimum over each row of 16 lanes, in every lane of the row (DPP row rotations 1, 2, 4, 8).
+__device__ __forceinline__ uint32_t row_min16(uint32_t x)
+{
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false));   // row_ror:1
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false));   // row_ror:2
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false));   // row_ror:4
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false));   // row_ror:8
+    return x;
+}
+
+// Minimum over the wavefront (wavefront-uniform result): row minima, then the four rows' lanes 0.
+__device__ __forceinline__ uint32_t wave_min(uint32_t x)
+{
+    x = row_min16(x);
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return min(min(a, b), min(c, d));
+}
+
+// ---------------------------------------------------------------------------------------------
 // decoupled look-back helpers (one wavefront reads a window of 64 predecessor flags at once)
 
 __device__ __forceinline__ uint64_t ld_flag(const uint64_t *p)
@@ -140,10 +194,8 @@ __device__ __forceinline__ uint64_t lookback_sum(const uint64_t *flags, uint32_t
         const uint64_t need = kp >= 63 ? ~0ull : ((2ull << kp) - 1);
         if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
         // (the counts are piece counts: every partial sum is below 2^32)
-        uint32_t v = lane <= kp ? (uint32_t)f : 0u;
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) v += (uint32_t)__shfl_xor(v, d, 64);
-        sum += v;
+        const uint32_t v = lane <= kp ? (uint32_t)f : 0u;
+        sum += (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(v), 63);
         if (kp < 64) return sum;
         top -= 64;
     }
@@ -185,39 +237,6 @@ template <typename T>
 __device__ __forceinline__ uint32_t wave_upper_bound(const T *a, uint32_t n, T x)
 {
     return wave_partition_point(a, n, [x](T v) { return v > x; });
-}
-
-// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves (no LDS round trips): a
-// Hillis-Steele scan inside each row of 16 lanes (row_shr 1, 2, 4, 8), then row 0's total added to
-// row 1 and row 2's to row 3 (row_bcast:15), then rows 0-1's total to rows 2 and 3 (row_bcast:31).
-__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x)
-{
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
-    return x;
-}
-
-// Minimum over each row of 16 lanes, in every lane of the row (DPP row rotations 1, 2, 4, 8).
-__device__ __forceinline__ uint32_t row_min16(uint32_t x)
-{
-    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false));   // row_ror:1
-    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false));   // row_ror:2
-    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false));   // row_ror:4
-    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false));   // row_ror:8
-    return x;
-}
-
-// Minimum over the wavefront (wavefront-uniform result): row minima, then the four rows' lanes 0.
-__device__ __forceinline__ uint32_t wave_min(uint32_t x)
-{
-    x = row_min16(x);
-    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
-    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
-    return min(min(a, b), min(c, d));
 }
 
 // Rank of the pair (a, b), NO_RANK if it is not a merge.  Byte pairs come from the dense table;

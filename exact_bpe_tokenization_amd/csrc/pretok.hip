@@ -301,8 +301,8 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
             if (mau == BK_KEEP) mau = xau;
         }
         const uint64_t bna = __ballot(mna != BK_KEEP), bau = __ballot(mau != BK_KEEP);
-        const uint32_t xna = __shfl(mna, bna ? __ffsll((unsigned long long)bna) - 1 : 0, 64);
-        const uint32_t xau = __shfl(mau, bau ? __ffsll((unsigned long long)bau) - 1 : 0, 64);
+        const uint32_t xna = (uint32_t)__builtin_amdgcn_readlane((int)mna, bna ? __ffsll((unsigned long long)bna) - 1 : 0);
+        const uint32_t xau = (uint32_t)__builtin_amdgcn_readlane((int)mau, bau ? __ffsll((unsigned long long)bau) - 1 : 0);
         if (na == BK_KEEP && bna) na = xna;
         if (au == BK_KEEP && bau) au = xau;
     }
@@ -615,8 +615,8 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
             uint32_t t = t0 + lane;
             uint32_t x = t0 == tile + 1 ? bk_first : t < L.n_tiles ? (uint32_t)tbwd[t] : (BK_T | (BK_T << 2));
             uint64_t mna = __ballot((x & 3u) != 0), mau = __ballot((x >> 2) != 0);
-            uint32_t xna = __shfl(x, mna ? __ffsll((unsigned long long)mna) - 1 : 0, 64);
-            uint32_t xau = __shfl(x, mau ? __ffsll((unsigned long long)mau) - 1 : 0, 64);
+            uint32_t xna = (uint32_t)__builtin_amdgcn_readlane((int)x, mna ? __ffsll((unsigned long long)mna) - 1 : 0);
+            uint32_t xau = (uint32_t)__builtin_amdgcn_readlane((int)x, mau ? __ffsll((unsigned long long)mau) - 1 : 0);
             if (na == BK_KEEP && mna) na = xna & 3u;
             if (au == BK_KEEP && mau) au = xau >> 2;
         }
