@@ -825,8 +825,6 @@ __device__ __forceinline__ uint32_t safe_word(uint32_t a, uint32_t b0)
 
 // k_gsafe: every position of every giant piece is tested; workgroups share out 1024-position
 // blocks (aligned to absolute positions) of each piece in turn
-__device__ void giant_cut(const DevVocab &v, uint8_t *ws, const Layout &L);
-
 __global__ __launch_bounds__(1024) void k_gsafe(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws, Layout L)
 {
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
@@ -850,7 +848,6 @@ __global__ __launch_bounds__(1024) void k_gsafe(DevVocab v, const uint8_t *__res
             if (lane == 32 && a0 + 63 > b0 && a0 + 32 < b0 + n) bm[safe_word(a0 + 32, b0)] = (uint32_t)(m >> 32);
         }
     }
-    if (last_workgroup(&((Ctrl *)(ws + L.ctrl))->done_seams)) giant_cut(v, ws, L);
 }
 
 // first and last safe position of window [lo, hi) of the piece at b0 (NO_PIECE if none); lo > b0
@@ -868,14 +865,14 @@ __device__ __forceinline__ void window_safe(const uint32_t *bm, uint32_t b0, uin
     }
 }
 
-// giant_cut: the last workgroup of k_gsafe turns the bitmap into chunks, piece by piece.  The piece is divided into
+// k_gcut: one workgroup per giant piece turns the bitmap into chunks.  The piece is divided into
 // windows of GCH positions; every window with a safe position is cut at its first one (chunks of
 // about GCH bytes where seams are common), and a window followed by one without any safe position
 // is also cut at its last one, so that a stretch without seams (typically a repeated character,
 // which needs few merge rounds) is a chunk of its own.  Cuts come out sorted; a workgroup scan
 // places them.  Chunks take consecutive slots of the chunk table (unused reserved slots: length 0);
 // chunks of up to SEG2_MAX bytes are also listed for the lane and segment kernels.
-__device__ void giant_cut(const DevVocab &v, uint8_t *ws, const Layout &L)
+__global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, Layout L)
 {
     constexpr uint32_t NT = 1024, NW = NT / 64;
     __shared__ uint32_t swsum[NW];
@@ -888,7 +885,7 @@ __device__ void giant_cut(const DevVocab &v, uint8_t *ws, const Layout &L)
     uint32_t *gc0 = (uint32_t *)(ws + L.gc0), *gnc = (uint32_t *)(ws + L.gnc);
     const uint32_t count = ctrl->bin_count[2];
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
-    for (uint32_t g = 0; g < count; ++g) {
+    for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
         const uint32_t p = list[g];
         const uint32_t b0 = pstart[p], n = pstart[p + 1] - b0, end = b0 + n;
         const uint32_t nwin = v.str ? (n + GCH - 1) / GCH : 0u;
@@ -1163,6 +1160,8 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
         LaunchScope k(ev, 3, s);
         const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
         hipLaunchKernelGGL(k_gsafe, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
+        const uint32_t gc = L.cap_giant < 64 ? L.cap_giant : 64;
+        hipLaunchKernelGGL(k_gcut, dim3(gc), dim3(1024), 0, s, v, b.ws, L);
     }
     {
         // lists of <= 16, 17..32, 33..64 and 65..128 bytes: at most n / 1, n / 17, n / 33, n / 65 items;

@@ -279,9 +279,8 @@ struct Ctrl {
     uint32_t bin_count[3];     // wave, block, giant bins
     uint32_t miss_count[4];    // pieces left for BPE: <= 16, 17..32, 33..64, 65..128 bytes
     uint32_t n_chunks;         // chunk slots reserved for giant pieces
-    uint32_t done_seams;       // workgroups of k_gsafe done (the last one cuts the giant pieces)
     uint32_t done_giant;       // workgroups of k_bpe_giant done (the last one joins the chunks)
-    uint32_t pad[50];
+    uint32_t pad[51];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 

@@ -148,8 +148,7 @@ enum {
                               /* per tile: the characters that decide the backward flags        */
     TOKTIER_K_PIECES,         /* UTF-8 decode + validation, automaton scan, piece starts        */
     TOKTIER_K_ROUTE,          /* every piece: single byte or whole-piece table hit, else BPE list */
-    TOKTIER_K_GIANT_SEAMS,    /* pieces > 4096 bytes: seams no merge crosses, then (last       */
-                              /* workgroup) the chunks                                          */
+    TOKTIER_K_GIANT_SEAMS,    /* pieces > 4096 bytes: seams no merge crosses, then chunks       */
     TOKTIER_K_BPE_SMALL,      /* BPE of unresolved pieces and chunks of <= 128 bytes: lane per  */
                               /* piece (<= 16), 32-lane segments (<= 32), a wavefront (<= 64),  */
                               /* a wavefront with two elements per lane (<= 128), one launch    */
