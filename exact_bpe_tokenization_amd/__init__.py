@@ -2,12 +2,14 @@
 
 The public entry points mirror include/toktier.h; see ``binding`` for the argument conventions.
 """
-from .binding import (EXPORTS, FAMILIES, KERNELS, HipEvents, toktier_encode_batch_timed, TOKTIER_CL100K, TOKTIER_GPT2, TOKTIER_O200K, Tokenizer, ToktierError,
-                      Vocab, lib, toktier_encode_batch, toktier_free_vocab, toktier_last_status,
-                      toktier_load_vocab, toktier_pretokenize_batch, toktier_unicode_table_sha256,
-                      toktier_vocab_info, toktier_workspace_bytes)
+from .binding import (EXPORTS, FAMILIES, KERNELS, TOKTIER_CL100K, TOKTIER_GPT2, TOKTIER_O200K, HipEvents, Tokenizer,
+                      ToktierError, Vocab, lib, toktier_encode_batch, toktier_encode_batch_spans,
+                      toktier_encode_batch_timed, toktier_free_vocab, toktier_last_status, toktier_load_vocab,
+                      toktier_pretokenize_batch, toktier_unicode_table_sha256, toktier_vocab_info,
+                      toktier_workspace_bytes)
 
-__all__ = ["EXPORTS", "FAMILIES", "KERNELS", "HipEvents", "toktier_encode_batch_timed", "TOKTIER_CL100K", "TOKTIER_GPT2", "TOKTIER_O200K", "Tokenizer", "ToktierError",
-           "Vocab", "lib", "toktier_encode_batch", "toktier_free_vocab", "toktier_last_status", "toktier_load_vocab",
+__all__ = ["EXPORTS", "FAMILIES", "KERNELS", "TOKTIER_CL100K", "TOKTIER_GPT2", "TOKTIER_O200K", "HipEvents",
+           "Tokenizer", "ToktierError", "Vocab", "lib", "toktier_encode_batch", "toktier_encode_batch_spans",
+           "toktier_encode_batch_timed", "toktier_free_vocab", "toktier_last_status", "toktier_load_vocab",
            "toktier_pretokenize_batch", "toktier_unicode_table_sha256", "toktier_vocab_info",
            "toktier_workspace_bytes"]

@@ -21,7 +21,8 @@ STATUS = {0: "TOKTIER_OK", 1: "TOKTIER_E_INVALID_ARG", 2: "TOKTIER_E_BAD_FAMILY"
 
 # every symbol declared in include/toktier.h
 EXPORTS = ("toktier_load_vocab", "toktier_free_vocab", "toktier_vocab_info", "toktier_workspace_bytes",
-           "toktier_encode_batch", "toktier_encode_batch_timed", "toktier_pretokenize_batch",
+           "toktier_encode_batch", "toktier_encode_batch_spans", "toktier_encode_batch_timed",
+           "toktier_pretokenize_batch",
            "toktier_last_status", "toktier_status_string", "toktier_last_hip_error",
            "toktier_unicode_table_sha256")
 
@@ -60,6 +61,7 @@ def lib():
     L.toktier_vocab_info.argtypes = [vp, ctypes.POINTER(u32), ctypes.POINTER(i32)]
     L.toktier_workspace_bytes.argtypes = [u64, u32, u64p]
     L.toktier_encode_batch.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, u64, vp, u64p]
+    L.toktier_encode_batch_spans.argtypes = [vp, vp, vp, u32, u64, vp, vp, u64, vp, vp, u64, vp, u64p]
     L.toktier_encode_batch_timed.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, u64, vp, u64p, vp, vp]
     L.toktier_pretokenize_batch.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, u64, vp, u64p]
     L.toktier_last_status.argtypes = [vp, vp, u64p]
@@ -158,6 +160,19 @@ def toktier_encode_batch(vocab, data, offsets, out_ids, out_offsets, workspace, 
     return n_tok.value if sync else None
 
 
+def toktier_encode_batch_spans(vocab, data, offsets, out_ids, out_spans, out_offsets, workspace, stream=None,
+                               sync=True):
+    """toktier_encode_batch that also writes each token's source byte offset to out_spans (int32
+    device tensor, read as uint32, >= len(data) elements)."""
+    n_tok = ctypes.c_uint64()
+    rc = lib().toktier_encode_batch_spans(vocab.handle, _ptr(data), _ptr(offsets), offsets.numel() - 1,
+                                          data.numel(), _ptr(out_ids), _ptr(out_spans), out_ids.numel(),
+                                          _ptr(out_offsets), _ptr(workspace), workspace.numel(), _stream(stream),
+                                          ctypes.byref(n_tok) if sync else None)
+    _check(rc, "toktier_encode_batch_spans")
+    return n_tok.value if sync else None
+
+
 def toktier_encode_batch_timed(vocab, data, offsets, out_ids, out_offsets, workspace, events_before,
                                events_after, stream=None, sync=True):
     """toktier_encode_batch plus HIP events recorded around each kernel launch.  events_before /
@@ -253,14 +268,25 @@ class Tokenizer:
                                   self.out_offsets[: d + 1], ws, stream=stream, sync=sync)
         return self.out_ids, self.out_offsets[: d + 1], nt
 
-    def encode(self, data: bytes, offsets=None):
-        """Host bytes in, host numpy arrays out: (ids uint32[T], out_offsets uint64[D+1])."""
+    def encode(self, data: bytes, offsets=None, spans=False):
+        """Host bytes in, host numpy arrays out: (ids uint32[T], out_offsets uint64[D+1]), plus the
+        tokens' source byte offsets (uint32[T]) as a third array when spans is True."""
         arr = np.frombuffer(bytes(data), dtype=np.uint8) if len(data) else np.zeros(0, np.uint8)
         offs = np.asarray([0, arr.size] if offsets is None else offsets, dtype=np.int64)
         dd = torch.from_numpy(arr.copy()).to(self.device)
         do = torch.from_numpy(offs).to(self.device)
-        ids, oo, nt = self.encode_device(dd, do)
-        return (ids[:nt].cpu().numpy().view(np.uint32).copy(), oo.cpu().numpy().astype(np.uint64))
+        if not spans:
+            ids, oo, nt = self.encode_device(dd, do)
+            return (ids[:nt].cpu().numpy().view(np.uint32).copy(), oo.cpu().numpy().astype(np.uint64))
+        n, d = arr.size, offs.size - 1
+        self._buffers(n, d)
+        ws = self.workspace[: toktier_workspace_bytes(n, d)]
+        out_spans = torch.empty(max(n, 1), dtype=torch.int32, device=self.device)
+        nt = toktier_encode_batch_spans(self.vocab, dd, do, self.out_ids[: max(n, 1)], out_spans,
+                                        self.out_offsets[: d + 1], ws)
+        return (self.out_ids[:nt].cpu().numpy().view(np.uint32).copy(),
+                self.out_offsets[: d + 1].cpu().numpy().astype(np.uint64),
+                out_spans[:nt].cpu().numpy().view(np.uint32).copy())
 
     def pretokenize(self, data: bytes, offsets=None):
         arr = np.frombuffer(bytes(data), dtype=np.uint8) if len(data) else np.zeros(0, np.uint8)

@@ -12,9 +12,14 @@
 
 namespace tt {
 
+// SPANS: also write each token's source byte offset (a separate instantiation, so that the plain form
+// keeps its few registers)
+template <bool SPANS>
 __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, const uint64_t *__restrict__ offsets,
                                                       uint32_t n_docs, uint64_t n, uint32_t *__restrict__ out_ids,
-                                                      uint64_t *__restrict__ out_offsets)
+                                                      uint64_t *__restrict__ out_offsets,
+                                                      uint32_t *__restrict__ out_spans,
+                                                      const uint32_t *__restrict__ tok_len)
 {
     constexpr int NW = SCAN_THREADS / 64;
     constexpr int IT = SCAN_TILE / SCAN_THREADS;   // iterations of 64 pieces per wavefront
@@ -83,13 +88,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
     // IDs: a single-token piece's ID is its result word (coalesced); a short multi-token piece's IDs
     // are at scratch[its start byte ...]; a long piece gets its output offset for k_gather_long.
     // All start loads are issued first; the first IDs in two halves (fewer registers); the further
-    // IDs of a piece four independent loads at a time.
+    // IDs of a piece four independent loads at a time.  With spans, every piece's start is loaded (it
+    // is its first token's span) and each further token's span adds the length of the token before.
     uint32_t st[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const uint32_t i = wb + it * 64u + lane;
         const bool multi = i < end && (pv[it] & (PV_MULTI | PV_LONG)) == PV_MULTI;
-        st[it] = multi ? pstart[i] : 0u;
+        st[it] = multi || (SPANS && i < end) ? pstart[i] : 0u;
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -115,7 +121,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
                 continue;
             }
             out_ids[o] = f0[u];
+            if (SPANS) out_spans[o] = st[it];
             const uint32_t c = (v & PV_MULTI) ? (v & PV_COUNT) : 1u;
+            uint32_t sp = st[it], prev = f0[u];   // span and ID of the token before token j
             for (uint32_t j = 1; j < c; j += 4) {
                 uint32_t x[4];
 #pragma unroll
@@ -123,6 +131,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
                     if (j + t < c) out_ids[o + j + t] = x[t];
+                if (SPANS) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        if (j + t >= c) break;
+                        sp += tok_len[prev];
+                        out_spans[o + j + t] = sp;
+                        prev = x[t];
+                    }
+                }
             }
         }
     }
@@ -143,10 +160,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void k_emit(uint8_t *ws, Layout L, co
     }
 }
 
-// IDs of the pieces longer than 64 bytes: one workgroup per piece of the wave and block bins, and
-// one per chunk of a giant piece (a chunk's IDs go to its place in the piece's output)
-__global__ __launch_bounds__(256) void k_gather_long(uint8_t *ws, Layout L, uint32_t *__restrict__ out_ids)
+// IDs of the pieces longer than 128 bytes: one workgroup per piece of the wave and block bins, and
+// one per chunk of a giant piece (a chunk's IDs go to its place in the piece's output).  With spans,
+// a workgroup scan of the token lengths gives each token's span from the piece's or chunk's start.
+__global__ __launch_bounds__(256) void k_gather_long(uint8_t *ws, Layout L, uint32_t *__restrict__ out_ids,
+                                                     uint32_t *__restrict__ out_spans,
+                                                     const uint32_t *__restrict__ tok_len)
 {
+    __shared__ uint32_t swsum[4];
+    __shared__ uint32_t s_carry;
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *pval = (const uint32_t *)(ws + L.pval);
@@ -172,7 +194,34 @@ __global__ __launch_bounds__(256) void k_gather_long(uint8_t *ws, Layout L, uint
             dst = out_ids + tokoff[p] + cdest[k];
             c = ccount[k];
         }
-        for (uint32_t j = threadIdx.x; j < c; j += blockDim.x) dst[j] = src[j];
+        if (!out_spans) {
+            for (uint32_t j = threadIdx.x; j < c; j += blockDim.x) dst[j] = src[j];
+            continue;
+        }
+        uint32_t *sdst = out_spans + (dst - out_ids);
+        const uint32_t lane = threadIdx.x & 63u, wid = threadIdx.x >> 6;
+        if (threadIdx.x == 0) s_carry = q < c0 + c1 ? pstart[q < c0 ? l0[q] : l1[q - c0]] : cstart[q - c0 - c1];
+        __syncthreads();
+        for (uint32_t j0 = 0; j0 < c; j0 += blockDim.x) {
+            const uint32_t j = j0 + threadIdx.x;
+            const uint32_t id = j < c ? src[j] : 0u;
+            const uint32_t len = j < c ? tok_len[id] : 0u;
+            const uint32_t inc = wave_incl_sum(len);
+            if (lane == 63) swsum[wid] = inc;
+            __syncthreads();
+            uint32_t before = s_carry, tot = 0;
+            for (uint32_t w = 0; w < 4; ++w) {
+                if (w < wid) before += swsum[w];
+                tot += swsum[w];
+            }
+            if (j < c) {
+                dst[j] = id;
+                sdst[j] = before + inc - len;
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) s_carry += tot;
+        }
+        __syncthreads();
     }
 }
 
@@ -185,19 +234,23 @@ __global__ __launch_bounds__(256) void k_export_starts(uint8_t *ws, Layout L, ui
         out[i] = i == np ? (uint32_t)n : pstart[i];
 }
 
-hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offsets, hipStream_t s,
-                          const Events *ev)
+hipError_t launch_compact(const DevVocab &v, const Batch &b, uint32_t *out_ids, uint64_t *out_offsets,
+                          uint32_t *out_spans, hipStream_t s, const Events *ev)
 {
     const Layout &L = b.L;
     {
         LaunchScope k(ev, 8, s);
-        hipLaunchKernelGGL(k_emit, dim3(L.n_scan_tiles), dim3(SCAN_THREADS), 0, s, b.ws, L, b.offsets, b.n_docs,
-                           b.n, out_ids, out_offsets);
+        if (out_spans)
+            hipLaunchKernelGGL(k_emit<true>, dim3(L.n_scan_tiles), dim3(SCAN_THREADS), 0, s, b.ws, L, b.offsets,
+                               b.n_docs, b.n, out_ids, out_offsets, out_spans, v.tok_len);
+        else
+            hipLaunchKernelGGL(k_emit<false>, dim3(L.n_scan_tiles), dim3(SCAN_THREADS), 0, s, b.ws, L, b.offsets,
+                               b.n_docs, b.n, out_ids, out_offsets, out_spans, v.tok_len);
     }
     if (b.n) {
         LaunchScope k(ev, 9, s);
         uint32_t gl = L.cap_wave + L.cap_chunks < 1024 ? L.cap_wave + L.cap_chunks : 1024;
-        hipLaunchKernelGGL(k_gather_long, dim3(gl), dim3(256), 0, s, b.ws, L, out_ids);
+        hipLaunchKernelGGL(k_gather_long, dim3(gl), dim3(256), 0, s, b.ws, L, out_ids, out_spans, v.tok_len);
     }
     return hipGetLastError();
 }

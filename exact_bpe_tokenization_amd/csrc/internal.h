@@ -72,6 +72,7 @@ struct DevVocab {
     // seams no merge can cross in giant pieces (NULL when the longest token exceeds STR_LMAX bytes)
     const uint8_t *tok_bytes;
     const uint32_t *tok_off;  // 256 + n_merges + 1 offsets into tok_bytes
+    const uint32_t *tok_len;  // byte length of every token (for token spans; always present)
     const uint4 *str;         // {key lo, key hi, id, len}; len 0 = empty slot
     uint32_t mask;
     uint32_t shift;
@@ -529,8 +530,8 @@ struct LaunchScope {   // records before[k] on construction and after[k] on dest
 
 hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
 hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
-hipError_t launch_compact(const Batch &b, uint32_t *out_ids, uint64_t *out_offsets, hipStream_t s,
-                          const Events *ev);
+hipError_t launch_compact(const DevVocab &v, const Batch &b, uint32_t *out_ids, uint64_t *out_offsets,
+                          uint32_t *out_spans, hipStream_t s, const Events *ev);
 hipError_t launch_export_starts(const Batch &b, uint32_t *out_starts, hipStream_t s);
 hipError_t launch_route(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
 

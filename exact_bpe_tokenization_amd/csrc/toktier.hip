@@ -24,6 +24,7 @@ struct toktier_vocab {
     void *dmem;     // pair tables, merges, automaton tables
     void *dwords;   // whole-piece tables (may be NULL)
     void *dstr;     // token strings and their hash (may be NULL)
+    void *dlen;     // byte length of every token
     DevVocab dv;
 };
 
@@ -479,11 +480,18 @@ extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int
     v->dv.tok_bytes = nullptr;
     TokenStrings ts;
     int rc = token_strings(merges, n_merges, ts);
+    if (rc == TOKTIER_OK) {
+        hipError_t el = hipMalloc(&v->dlen, 4ull * ts.len.size());
+        if (el == hipSuccess) el = hipMemcpy(v->dlen, ts.len.data(), 4ull * ts.len.size(), hipMemcpyHostToDevice);
+        if (el != hipSuccess) rc = hip_fail(el);
+        v->dv.tok_len = (const uint32_t *)v->dlen;
+    }
     if (rc == TOKTIER_OK) rc = build_string_table(v, ts);
     if (rc == TOKTIER_OK) rc = build_whole_piece_tables(v, ts);
     if (rc != TOKTIER_OK) {
         if (v->dwords) (void)hipFree(v->dwords);
         if (v->dstr) (void)hipFree(v->dstr);
+        if (v->dlen) (void)hipFree(v->dlen);
         (void)hipFree(v->dmem);
         free(v);
         return rc;
@@ -497,7 +505,7 @@ extern "C" int toktier_free_vocab(toktier_vocab *v)
     if (!v) return TOKTIER_OK;
     hipError_t e = hipDeviceSynchronize();
     hipError_t f = hipFree(v->dmem);
-    for (void *extra : {v->dwords, v->dstr}) {
+    for (void *extra : {v->dwords, v->dstr, v->dlen}) {
         if (!extra) continue;
         hipError_t g = hipFree(extra);
         if (f == hipSuccess) f = g;
@@ -571,7 +579,8 @@ namespace {
 
 int encode_impl(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets, uint32_t n_docs,
                 uint64_t total_bytes, uint32_t *out_ids, uint64_t ids_capacity, uint64_t *out_offsets,
-                void *workspace, uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens, const Events *ev)
+                uint32_t *out_spans, void *workspace, uint64_t workspace_bytes, void *stream,
+                uint64_t *out_n_tokens, const Events *ev)
 {
     Batch b;
     int rc = check_batch(v, bytes, offsets, n_docs, total_bytes, workspace, workspace_bytes, &b);
@@ -582,7 +591,7 @@ int encode_impl(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *of
     HIP_TRY(launch_pretokenize(v->dv, b, s, ev));
     HIP_TRY(launch_route(v->dv, b, s, ev));
     HIP_TRY(launch_bpe(v->dv, b, s, ev));
-    HIP_TRY(launch_compact(b, out_ids, out_offsets, s, ev));
+    HIP_TRY(launch_compact(v->dv, b, out_ids, out_offsets, out_spans, s, ev));
     if (!out_n_tokens) return TOKTIER_OK;
     Ctrl c;
     rc = read_ctrl(workspace, s, &c);
@@ -598,8 +607,19 @@ extern "C" int toktier_encode_batch(const toktier_vocab *v, const uint8_t *bytes
                                     uint64_t ids_capacity, uint64_t *out_offsets, void *workspace,
                                     uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens)
 {
-    return encode_impl(v, bytes, offsets, n_docs, total_bytes, out_ids, ids_capacity, out_offsets, workspace,
-                       workspace_bytes, stream, out_n_tokens, nullptr);
+    return encode_impl(v, bytes, offsets, n_docs, total_bytes, out_ids, ids_capacity, out_offsets, nullptr,
+                       workspace, workspace_bytes, stream, out_n_tokens, nullptr);
+}
+
+extern "C" int toktier_encode_batch_spans(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                                          uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
+                                          uint32_t *out_spans, uint64_t ids_capacity, uint64_t *out_offsets,
+                                          void *workspace, uint64_t workspace_bytes, void *stream,
+                                          uint64_t *out_n_tokens)
+{
+    if (total_bytes && !out_spans) return TOKTIER_E_INVALID_ARG;
+    return encode_impl(v, bytes, offsets, n_docs, total_bytes, out_ids, ids_capacity, out_offsets, out_spans,
+                       workspace, workspace_bytes, stream, out_n_tokens, nullptr);
 }
 
 extern "C" int toktier_encode_batch_timed(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
@@ -609,8 +629,8 @@ extern "C" int toktier_encode_batch_timed(const toktier_vocab *v, const uint8_t 
                                           void *const *events_before, void *const *events_after)
 {
     Events ev{events_before, events_after};
-    return encode_impl(v, bytes, offsets, n_docs, total_bytes, out_ids, ids_capacity, out_offsets, workspace,
-                       workspace_bytes, stream, out_n_tokens, &ev);
+    return encode_impl(v, bytes, offsets, n_docs, total_bytes, out_ids, ids_capacity, out_offsets, nullptr,
+                       workspace, workspace_bytes, stream, out_n_tokens, &ev);
 }
 
 extern "C" int toktier_pretokenize_batch(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,

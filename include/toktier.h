@@ -17,7 +17,7 @@
  *     was loaded; "host" pointers are ordinary process memory.
  *   - All device buffers passed in (input bytes, offsets, outputs, workspace) are owned by the
  *     caller.  The library owns only the vocabulary handle and the device tables behind it.
- *   - toktier_encode_batch and toktier_pretokenize_batch allocate nothing: every scratch byte lives
+ *   - The encode and pretokenize calls allocate nothing: every scratch byte lives
  *     in the caller's workspace, and all their work is enqueued on the caller's stream.
  *   - Calls on different streams are independent when they use different workspaces; a workspace
  *     must not be shared by two calls in flight.  Results never depend on earlier calls.
@@ -118,6 +118,24 @@ int toktier_encode_batch(const toktier_vocab *v, const uint8_t *bytes, const uin
                          uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
                          uint64_t ids_capacity, uint64_t *out_offsets, void *workspace,
                          uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens);
+
+/*
+ * toktier_encode_batch plus source byte spans of the tokens (paper: the session store keeps token
+ * IDs with their source byte spans, session-state paragraph and Figure 14a; the GPU path it
+ * describes returns IDs only, and its closing follow-ups list GPU span export).  A span is stored as
+ * its start; the end is the next token's start.  Same kernels, same IDs and out_offsets; in addition
+ *   out_spans    device, uint32[ids_capacity]: out_spans[i] is the batch byte offset of the first
+ *                byte of token i.  Token i covers bytes [out_spans[i], out_spans[i + 1]), the last
+ *                token of document d ending at offsets[d + 1]: the tokens of a document tile it, and
+ *                each token's bytes are its vocabulary string.
+ * Other arguments, ownership and errors as in toktier_encode_batch; out_spans may be NULL only when
+ * total_bytes == 0 (E_INVALID_ARG otherwise).
+ */
+int toktier_encode_batch_spans(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                               uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
+                               uint32_t *out_spans, uint64_t ids_capacity, uint64_t *out_offsets,
+                               void *workspace, uint64_t workspace_bytes, void *stream,
+                               uint64_t *out_n_tokens);
 
 /*
  * Stage 1 alone, for split-level checks (paper, exactness section: boundaries are compared apart

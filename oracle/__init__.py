@@ -6,6 +6,7 @@ F = E* o G -- a leftmost-first pre-tokenizer G, then byte-level BPE E on every p
 * ``pretokenize``  -- G, a hand-written leftmost-first matcher per regex alternative (oracle.c)
 * ``bpe_encode``   -- E, priority-queue BPE over a linked list (oracle.c)
 * ``encode_batch`` -- F over a batch of documents, with per-document ID offsets
+* ``token_spans``  -- the source byte offset of every token of such a batch
 * ``train``        -- the byte-level BPE trainer that produces the merge lists used as inputs
 * ``textbook_bpe`` -- the exhaustive textbook merge loop in pure Python, for pinning E on tiny inputs
 
@@ -230,6 +231,30 @@ def textbook_bpe(merges, piece: bytes):
             return seq
         r, i = best
         seq[i:i + 2] = [256 + r]
+
+
+def token_lengths(merges):
+    """Byte length of every token ID: 1 for the 256 byte tokens, len(left) + len(right) for the token
+    that merge r creates (ID 256 + r)."""
+    m = np.asarray(merges, dtype=np.int64).reshape(-1, 2)
+    ln = np.ones(256 + m.shape[0], dtype=np.int64)
+    for r, (a, b) in enumerate(m.tolist()):
+        ln[256 + r] = ln[a] + ln[b]
+    return ln
+
+
+def token_spans(merges, ids, out_offsets, offsets):
+    """Source byte offset of every token.  Document d's tokens, ids[out_offsets[d]:out_offsets[d+1]],
+    spell its bytes [offsets[d], offsets[d+1]) in order (F = E* o G only regroups the text), so token
+    i starts where the tokens before it in its document end.  (TokTier's session store keeps these
+    byte spans beside the IDs; its GPU path does not produce them.)"""
+    ln = token_lengths(merges)[np.asarray(ids, dtype=np.int64)]
+    out = np.zeros(len(ids), dtype=np.uint64)
+    for d in range(len(offsets) - 1):
+        a, b = int(out_offsets[d]), int(out_offsets[d + 1])
+        if a < b:
+            out[a:b] = int(offsets[d]) + np.concatenate([[0], np.cumsum(ln[a:b - 1])])
+    return out
 
 
 def decode(merges, ids):

@@ -295,3 +295,44 @@ def test_random_merge_lists(tt, seed):
         gi, go = tok.encode(data.tobytes(), offs)
         ei, eo = oracle.encode_batch(fam, merges, data, offs)
         compare_ids(ei, eo, gi, go)
+
+
+def _check_spans(tok, merges, fam, data, offs, label):
+    _say("spans", label, data.size)
+    ids, oo, sp = tok.encode(data.tobytes(), offs, spans=True)
+    eids, eoo = oracle.encode_batch(fam, merges, data, offs)
+    compare_ids(eids, eoo, ids, oo)
+    esp = oracle.token_spans(merges, eids, eoo, offs)
+    bad = np.flatnonzero(esp.astype(np.uint64) != sp.astype(np.uint64))
+    assert bad.size == 0, f"{bad.size} spans differ, first at token {bad[0]}: {sp[bad[0]]} vs {esp[bad[0]]}"
+
+
+@pytest.mark.parametrize("name", list(textgen.WORKLOADS))
+@pytest.mark.parametrize("scale", [0.01, 1.0])
+def test_spans_workloads(tt, name, scale):
+    fam, voc, data, offs = textgen.workload(name, scale)
+    tok, merges, _ = tokenizer(tt, voc)
+    _check_spans(tok, merges, fam, data, offs, f"{name} {scale}")
+
+
+def test_spans_edge_and_giant(tt):
+    """Spans of empty, ragged and tile-straddling documents and of pieces long enough to be chunked
+    (the long-piece gather writes their spans)."""
+    tok, merges, fam = tokenizer(tt, "v2")
+    rng = np.random.default_rng(31)
+    az = "abcdefghijklmnopqrstuvwxyz"
+    for strings in ([""], ["", "a", "", "bc", ""], ["x" * 4095, "y"], ["q" * 4097], ["中", "\U0010FFFF"],
+                    ["a" * 20000, "".join(az[int(i)] for i in rng.integers(0, 26, 30000)), " " * 20000 + "x",
+                     "ab" * 7000, textgen.agent_transcript(5, 40000)]):
+        data, offs = _batch(strings)
+        _check_spans(tok, merges, fam, data, offs, [s[:8] for s in strings])
+
+
+def test_spans_leave_ids_unchanged(tt):
+    """The span-writing entry point returns the same IDs and offsets as the plain one."""
+    tok, _, _ = tokenizer(tt, "v4")
+    data, offs = textgen.workload("c4_batch64", 0.05)[2:]
+    _say("spans vs plain", data.size)
+    a, ao = tok.encode(data.tobytes(), offs)
+    b, bo, _ = tok.encode(data.tobytes(), offs, spans=True)
+    assert np.array_equal(a, b) and np.array_equal(ao, bo)
