@@ -7,6 +7,8 @@ F = E* o G -- a leftmost-first pre-tokenizer G, then byte-level BPE E on every p
 * ``bpe_encode``   -- E, priority-queue BPE over a linked list (oracle.c)
 * ``encode_batch`` -- F over a batch of documents, with per-document ID offsets
 * ``token_spans``  -- the source byte offset of every token of such a batch
+* ``added_matches`` / ``encode_batch_ex`` -- the leftmost-longest added-token pass in front of F,
+  and the ignore_merges whole-piece rule
 * ``train``        -- the byte-level BPE trainer that produces the merge lists used as inputs
 * ``textbook_bpe`` -- the exhaustive textbook merge loop in pure Python, for pinning E on tiny inputs
 
@@ -255,6 +257,106 @@ def token_spans(merges, ids, out_offsets, offsets):
         if a < b:
             out[a:b] = int(offsets[d]) + np.concatenate([[0], np.cumsum(ln[a:b - 1])])
     return out
+
+
+def added_matches(data, offsets, literals):
+    """The added-token pass: literals (special and added tokens) that the model reserves as single
+    IDs are taken out of the text before the family's pre-tokenizer runs (paper, implementation
+    paragraph on added and special tokens: a leftmost-longest literal pass).  Within each document,
+    scanning left to right: where some literal starts and ends inside the document, the longest
+    such literal is taken and the scan resumes after it; elsewhere the scan moves one byte on.
+    Returns a list of (start byte, literal index) in text order."""
+    raw = bytes(_as_u8(data))
+    offs = [int(x) for x in _offsets(len(raw), offsets)]
+    lits = [bytes(l) for l in literals]
+    if any(len(l) == 0 for l in lits):
+        raise ValueError("empty literal")
+    starts = {}                                  # position -> indices of the literals found there
+    for k, l in enumerate(lits):
+        i = raw.find(l)
+        while i >= 0:
+            starts.setdefault(i, []).append(k)
+            i = raw.find(l, i + 1)
+    out, d, resume = [], 0, 0
+    for p in sorted(starts):
+        if p < resume:
+            continue
+        while offs[d + 1] <= p:                  # the document holding byte p
+            d += 1
+        fit = [k for k in starts[p] if p + len(lits[k]) <= offs[d + 1]]
+        if not fit:
+            continue
+        k = max(fit, key=lambda k: (len(lits[k]), -k))
+        out.append((p, k))
+        resume = p + len(lits[k])
+    return out
+
+
+def encode_batch_ex(family, merges, data, offsets=None, added=(), ignore_merges=False):
+    """F with the added-token pass in front of it and, optionally, the ignore_merges rule in E.
+
+    added: (literal bytes, ID) pairs; every literal taken by ``added_matches`` becomes its one ID, and
+    the text between literals (and between a literal and its document's ends) is tokenized as a
+    document of its own.  ignore_merges (paper, GPU BPE paragraph: the Llama 3 / gpt-oss encoder
+    emits one ID when the whole piece is a vocabulary entry): a piece whose bytes are some token's
+    bytes becomes that token -- the smallest such ID when several tokens share the bytes -- and
+    only the other pieces go through the merge loop.  Returns (ids uint32[T], out_offsets
+    uint64[D+1])."""
+    m = merges if isinstance(merges, Merges) else Merges(merges)
+    raw = bytes(_as_u8(data))
+    offs = [int(x) for x in _offsets(len(raw), offsets)]
+    lits = [bytes(b) for b, _ in added]
+    lid = [int(i) for _, i in added]
+    found = added_matches(raw, offs, lits) if lits else []
+    # documents cut at the literals: items are ("seg", a, b) or ("lit", k), per document in order
+    items, fi = [], 0
+    for d in range(len(offs) - 1):
+        doc, cur = [], offs[d]
+        while fi < len(found) and found[fi][0] < offs[d + 1]:
+            p, k = found[fi]
+            doc.append(("seg", cur, p))
+            doc.append(("lit", k))
+            cur = p + len(lits[k])
+            fi += 1
+        doc.append(("seg", cur, offs[d + 1]))
+        items.append(doc)
+    segs = [(it[1], it[2]) for doc in items for it in doc if it[0] == "seg"]
+    seg_offs = np.array([0] + [b for _, b in segs], dtype=np.uint64) if segs else np.zeros(1, np.uint64)
+    # G on the text segments (segment i spans [segs[i][0], segs[i][1]) of raw, cut out and
+    # concatenated; each is a document of its own)
+    text = b"".join(raw[a:b] for a, b in segs)
+    cut = np.concatenate([[0], np.cumsum([b - a for a, b in segs])]).astype(np.uint64)
+    starts = pretokenize(family, text, cut)
+    pieces = [text[int(starts[k]):int(starts[k + 1])] for k in range(len(starts) - 1)]
+    whole = {}
+    if ignore_merges:
+        for t, b in enumerate(m.token_bytes()):
+            whole.setdefault(b, t)
+    # E on every piece that the whole-piece rule does not settle
+    todo = [i for i, pc in enumerate(pieces) if pc not in whole]
+    ids_of = [[whole[pc]] if pc in whole else None for pc in pieces]
+    if todo:
+        buf = b"".join(pieces[i] for i in todo)
+        ps = np.concatenate([[0], np.cumsum([len(pieces[i]) for i in todo])]).astype(np.uint64)
+        e, nt = bpe_encode(m, buf, ps)
+        pos = 0
+        for i, c in zip(todo, nt.tolist()):
+            ids_of[i] = e[pos:pos + c].tolist()
+            pos += c
+    piece_seg = np.searchsorted(cut, starts[:-1], side="right") - 1
+    seg_ids = [[] for _ in segs]
+    for i, sidx in enumerate(piece_seg.tolist()):
+        seg_ids[sidx].extend(ids_of[i])
+    out, oo, si = [], [0], 0
+    for doc in items:
+        for it in doc:
+            if it[0] == "lit":
+                out.append(lid[it[1]])
+            else:
+                out.extend(seg_ids[si])
+                si += 1
+        oo.append(len(out))
+    return np.array(out, dtype=np.uint32), np.array(oo, dtype=np.uint64)
 
 
 def decode(merges, ids):
