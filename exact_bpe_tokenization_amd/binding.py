@@ -15,12 +15,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("TOKTIER_LIBRARY") or os.path.join(HERE, "libtoktier.so")
 
 TOKTIER_GPT2, TOKTIER_CL100K, TOKTIER_O200K = 1, 2, 3
+TOKTIER_IGNORE_MERGES = 1
 FAMILIES = {"gpt2": TOKTIER_GPT2, "cl100k": TOKTIER_CL100K, "o200k": TOKTIER_O200K}
 STATUS = {0: "TOKTIER_OK", 1: "TOKTIER_E_INVALID_ARG", 2: "TOKTIER_E_BAD_FAMILY", 3: "TOKTIER_E_BAD_MERGES",
           4: "TOKTIER_E_INVALID_UTF8", 5: "TOKTIER_E_CAPACITY", 6: "TOKTIER_E_HIP", 7: "TOKTIER_E_OOM"}
 
 # every symbol declared in include/toktier.h
-EXPORTS = ("toktier_load_vocab", "toktier_free_vocab", "toktier_vocab_info", "toktier_workspace_bytes",
+EXPORTS = ("toktier_load_vocab", "toktier_load_vocab_ex", "toktier_free_vocab", "toktier_vocab_info",
+           "toktier_workspace_bytes", "toktier_workspace_bytes_ex",
            "toktier_encode_batch", "toktier_encode_batch_spans", "toktier_encode_batch_timed",
            "toktier_pretokenize_batch",
            "toktier_last_status", "toktier_status_string", "toktier_last_hip_error",
@@ -57,6 +59,8 @@ def lib():
     vp, u32, u64, i32 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int
     u64p = ctypes.POINTER(ctypes.c_uint64)
     L.toktier_load_vocab.argtypes = [vp, u32, i32, ctypes.POINTER(vp)]
+    L.toktier_load_vocab_ex.argtypes = [vp, u32, i32, u32, vp, vp, vp, u32, ctypes.POINTER(vp)]
+    L.toktier_workspace_bytes_ex.argtypes = [vp, u64, u32, u64p]
     L.toktier_free_vocab.argtypes = [vp]
     L.toktier_vocab_info.argtypes = [vp, ctypes.POINTER(u32), ctypes.POINTER(i32)]
     L.toktier_workspace_bytes.argtypes = [u64, u32, u64p]
@@ -130,6 +134,25 @@ def toktier_load_vocab(merges, family):
     return Vocab(h, m.shape[0], fam)
 
 
+def toktier_load_vocab_ex(merges, family, flags=0, added=()):
+    """toktier_load_vocab with vocabulary flags (TOKTIER_IGNORE_MERGES) and added tokens: `added` is a
+    sequence of (literal bytes, ID) pairs."""
+    m = np.ascontiguousarray(np.asarray(merges, dtype=np.uint32).reshape(-1, 2))
+    fam = FAMILIES.get(family, family) if isinstance(family, str) else int(family)
+    lits = [bytes(b) for b, _ in added]
+    blob = np.frombuffer(b"".join(lits) or b"\0", dtype=np.uint8).copy()
+    offs = np.zeros(len(lits) + 1, dtype=np.uint32)
+    offs[1:] = np.cumsum([len(b) for b in lits]) if lits else []
+    ids = np.asarray([int(i) for _, i in added] or [0], dtype=np.uint32)
+    h = ctypes.c_void_p()
+    rc = lib().toktier_load_vocab_ex(m.ctypes.data_as(ctypes.c_void_p) if m.size else None, m.shape[0], fam,
+                                     int(flags), blob.ctypes.data_as(ctypes.c_void_p),
+                                     offs.ctypes.data_as(ctypes.c_void_p), ids.ctypes.data_as(ctypes.c_void_p),
+                                     len(lits), ctypes.byref(h))
+    _check(rc, "toktier_load_vocab_ex")
+    return Vocab(h, m.shape[0], fam)
+
+
 def toktier_free_vocab(vocab):
     vocab.close()
 
@@ -144,6 +167,13 @@ def toktier_workspace_bytes(total_bytes, n_docs):
     out = ctypes.c_uint64()
     _check(lib().toktier_workspace_bytes(int(total_bytes), int(n_docs), ctypes.byref(out)),
            "toktier_workspace_bytes")
+    return out.value
+
+
+def toktier_workspace_bytes_ex(vocab, total_bytes, n_docs):
+    out = ctypes.c_uint64()
+    _check(lib().toktier_workspace_bytes_ex(vocab.handle, int(total_bytes), int(n_docs), ctypes.byref(out)),
+           "toktier_workspace_bytes_ex")
     return out.value
 
 
@@ -243,17 +273,21 @@ def toktier_unicode_table_sha256():
 class Tokenizer:
     """Convenience wrapper: a vocabulary plus device buffers sized for the largest batch seen."""
 
-    def __init__(self, merges, family, device="cuda:0"):
+    def __init__(self, merges, family, device="cuda:0", added=(), ignore_merges=False):
         self.device = torch.device(device)
         with torch.cuda.device(self.device):
-            self.vocab = toktier_load_vocab(merges, family)
+            if added or ignore_merges:
+                self.vocab = toktier_load_vocab_ex(merges, family, TOKTIER_IGNORE_MERGES if ignore_merges else 0,
+                                                   added)
+            else:
+                self.vocab = toktier_load_vocab(merges, family)
         self._cap = -1
         self._docs = -1
 
     def _buffers(self, n, d):
         if n > self._cap or d > self._docs:
             self._cap, self._docs = max(n, self._cap), max(d, self._docs)
-            ws = toktier_workspace_bytes(self._cap, self._docs)
+            ws = toktier_workspace_bytes_ex(self.vocab, self._cap, self._docs)
             self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.device)
             self.out_ids = torch.empty(max(self._cap, 1), dtype=torch.int32, device=self.device)
             self.out_offsets = torch.empty(self._docs + 1, dtype=torch.int64, device=self.device)
@@ -263,7 +297,7 @@ class Tokenizer:
         """data/offsets already on the device.  Returns (ids view, offsets view, n_tokens)."""
         n, d = data.numel(), offsets.numel() - 1
         self._buffers(n, d)
-        ws = self.workspace[: toktier_workspace_bytes(n, d)]
+        ws = self.workspace[: toktier_workspace_bytes_ex(self.vocab, n, d)]
         nt = toktier_encode_batch(self.vocab, data, offsets, self.out_ids[: max(n, 1)],
                                   self.out_offsets[: d + 1], ws, stream=stream, sync=sync)
         return self.out_ids, self.out_offsets[: d + 1], nt
@@ -280,7 +314,7 @@ class Tokenizer:
             return (ids[:nt].cpu().numpy().view(np.uint32).copy(), oo.cpu().numpy().astype(np.uint64))
         n, d = arr.size, offs.size - 1
         self._buffers(n, d)
-        ws = self.workspace[: toktier_workspace_bytes(n, d)]
+        ws = self.workspace[: toktier_workspace_bytes_ex(self.vocab, n, d)]
         out_spans = torch.empty(max(n, 1), dtype=torch.int32, device=self.device)
         nt = toktier_encode_batch_spans(self.vocab, dd, do, self.out_ids[: max(n, 1)], out_spans,
                                         self.out_offsets[: d + 1], ws)
@@ -295,6 +329,6 @@ class Tokenizer:
         self._buffers(n, d)
         dd = torch.from_numpy(arr.copy()).to(self.device)
         do = torch.from_numpy(offs).to(self.device)
-        ws = self.workspace[: toktier_workspace_bytes(n, d)]
+        ws = self.workspace[: toktier_workspace_bytes_ex(self.vocab, n, d)]
         np_ = toktier_pretokenize_batch(self.vocab, dd, do, self.out_starts[: n + 1], ws)
         return self.out_starts[: np_ + 1].cpu().numpy().view(np.uint32).astype(np.uint64)

@@ -31,6 +31,36 @@ constexpr uint32_t PENDING = 0xFFFFFFFEu;
 // ---------------------------------------------------------------------------------------------
 // lane per piece
 
+// calls f(id) for every token whose byte string equals s[0, len); the table key was computed by the
+// caller as str_key(H(s), len)
+template <typename F>
+__device__ __forceinline__ void str_find(const DevVocab &v, const uint8_t *s, uint32_t len, uint64_t key, F f)
+{
+    uint32_t i = (uint32_t)str_slot(key, v.str_shift);
+    for (;;) {
+        const uint4 e = v.str[i];
+        if (e.w == 0) return;
+        if (e.w == len && ((uint64_t)e.x | ((uint64_t)e.y << 32)) == key) {
+            const uint8_t *t = v.tok_bytes + v.tok_off[e.z];
+            bool eq = true;
+            for (uint32_t k = 0; k < len && eq; ++k) eq = t[k] == s[k];
+            if (eq) f(e.z);
+        }
+        i = (i + 1) & v.str_mask;
+    }
+}
+
+// ignore_merges: the smallest ID of a token whose bytes are s[0, len) (len up to the longest token),
+// NO_PIECE if there is none
+__device__ uint32_t whole_token(const DevVocab &v, const uint8_t *s, uint32_t len)
+{
+    uint64_t h = 0;
+    for (uint32_t k = 0; k < len; ++k) h = h * STR_P + s[k];
+    uint32_t best = NO_PIECE;
+    str_find(v, s, len, str_key(h, len), [&](uint32_t id) { best = min(best, id); });
+    return best;
+}
+
 // k_route: every piece.  Single bytes and whole-piece table hits get their result word here; the
 // others are listed for BPE by length.  Each workgroup owns a contiguous range of pieces and keeps
 // RT_PPT pieces per thread in flight (their loads and table probes overlap).  List entries are queued
@@ -91,6 +121,10 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t 
 #pragma unroll
         for (int u = 0; u < RT_PPT; ++u) {
             if (pp[u] >= end) continue;
+            if (st[u] != WP_HIT && (v.flags & VF_IGNORE_MERGES) && len[u] > (uint32_t)TABLE_MAX && len[u] <= v.lmax) {
+                id[u] = whole_token(v, bytes + a0[u], len[u]);
+                if (id[u] != NO_PIECE) st[u] = WP_HIT;
+            }
             if (st[u] == WP_HIT) pval[pp[u]] = id[u];
             else list_piece(pp[u], len[u]);
         }
@@ -766,25 +800,6 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
 // string hash, duplicates included; a candidate with more than SEAM_MAXT of either is rejected.
 
 constexpr int SEAM_MAXT = 8;
-
-// calls f(id) for every token whose byte string equals s[0, len); the table key was computed by the
-// caller as str_key(H(s), len)
-template <typename F>
-__device__ __forceinline__ void str_find(const DevVocab &v, const uint8_t *s, uint32_t len, uint64_t key, F f)
-{
-    uint32_t i = (uint32_t)str_slot(key, v.str_shift);
-    for (;;) {
-        const uint4 e = v.str[i];
-        if (e.w == 0) return;
-        if (e.w == len && ((uint64_t)e.x | ((uint64_t)e.y << 32)) == key) {
-            const uint8_t *t = v.tok_bytes + v.tok_off[e.z];
-            bool eq = true;
-            for (uint32_t k = 0; k < len && eq; ++k) eq = t[k] == s[k];
-            if (eq) f(e.z);
-        }
-        i = (i + 1) & v.str_mask;
-    }
-}
 
 // may the piece s[0, n) be cut before byte j (0 < j < n)?  Tokens ending at j are collected first;
 // each token starting at j is checked against them as soon as it is found.

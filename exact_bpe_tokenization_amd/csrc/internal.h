@@ -80,7 +80,12 @@ struct DevVocab {
     uint32_t str_mask, str_shift, lmax;
     uint32_t n_merges;
     int family;
+    uint32_t flags;           // VF_* below
 };
+
+// vocabulary flags: VF_IGNORE_MERGES -- the whole-piece tables hold every token's byte string (the
+// smallest ID of each), and pieces longer than TABLE_MAX are looked up in the token string hash
+constexpr uint32_t VF_IGNORE_MERGES = 1u;
 
 // token string hash: H(s) = sum s_i P^(len-1-i) mod 2^64, so H(s c) = H(s) P + c and
 // H(c s) = c P^len + H(s); the key mixes in the length
@@ -527,6 +532,71 @@ struct LaunchScope {   // records before[k] on construction and after[k] on dest
         if (ev && ev->after && ev->after[k]) (void)hipEventRecord((hipEvent_t)ev->after[k], s);
     }
 };
+
+// ---------------------------------------------------------------------------------------------
+// added tokens: literals taken out leftmost-longest before the pre-tokenizer
+
+struct DevAdded {
+    const uint8_t *bytes;     // the literals' bytes, concatenated
+    const uint32_t *off;      // n + 1 offsets into bytes
+    const uint32_t *id;       // n output IDs
+    const uint32_t *pmap;     // 65536-bit map of the first two bytes (b0 | b1 << 8) of literals >= 2 bytes
+    const uint32_t *pre;      // 65537 offsets into list: the literals >= 2 bytes with those first two
+    const uint32_t *list;     //   bytes, longest first
+    const uint32_t *one;      // 256: the index of the one-byte literal of each byte, or NO_LIT
+    uint32_t n, lmin, lmax;
+};
+constexpr uint32_t NO_LIT = 0xFFFFFFFFu;
+constexpr uint32_t LIT_TILE = 4096;          // bytes per workgroup of the literal search
+constexpr uint32_t LIT_TAKEN = 1u << 31;     // candidate flag: taken by the leftmost-longest scan
+
+// control words of the literal pass (its own block: the pipeline clears its control block)
+struct LitCtrl {
+    uint32_t status;      // ST_BAD_OFFSETS
+    uint32_t n_cand;      // candidates (a literal starts and ends inside the document)
+    uint32_t n_lit;       // literals taken
+    uint32_t pad[61];
+};
+
+// Workspace of an encode with added tokens: the pipeline's layout first (its control block stays at
+// offset 0), then these regions.  K_cap = n / lmin literals at most; S_cap = n_docs + 2 K_cap
+// documents after cutting.
+struct AddLayout {
+    uint64_t lctrl, tcount, tbase, cand, lits, lstart, lcnt, lpref, offs2, oo2, ids2, spans2, total;
+    uint32_t n_ltiles;
+    uint64_t k_cap, s_cap;
+};
+
+inline AddLayout make_add_layout(uint64_t base, uint64_t n, uint32_t n_docs, uint32_t lmin)
+{
+    AddLayout A;
+    A.n_ltiles = (uint32_t)((n + LIT_TILE - 1) / LIT_TILE);
+    A.k_cap = n / (lmin ? lmin : 1) + 1;
+    A.s_cap = (uint64_t)n_docs + 2 * A.k_cap + 1;
+    uint64_t o = base;
+    A.lctrl = o;  o += align256(sizeof(LitCtrl));
+    A.tcount = o; o += align256(4ull * (A.n_ltiles + 1));
+    A.tbase = o;  o += align256(4ull * (A.n_ltiles + 1));
+    A.cand = o;   o += align256(8ull * (n + 1));
+    A.lits = o;   o += align256(16ull * A.k_cap);
+    A.lstart = o; o += align256(4ull * (A.k_cap + 1));
+    A.lcnt = o;   o += align256(4ull * (A.k_cap + 1));
+    A.lpref = o;  o += align256(4ull * (A.k_cap + 1));
+    A.offs2 = o;  o += align256(8ull * A.s_cap);
+    A.oo2 = o;    o += align256(8ull * A.s_cap);
+    A.ids2 = o;   o += align256(4ull * (n + 1));
+    A.spans2 = o; o += align256(4ull * (n + 1));
+    A.total = o;
+    return A;
+}
+
+// the literal search and leftmost-longest scan; the count of taken literals is left in LitCtrl
+hipError_t launch_literals(const DevAdded &a, const Batch &b, const AddLayout &A, hipStream_t s);
+// the documents cut at the n_lit taken literals (offsets for the pipeline), before it runs
+hipError_t launch_literal_docs(const Batch &b, const AddLayout &A, uint32_t n_lit, hipStream_t s);
+// after the pipeline encoded the cut documents: final IDs, spans and document offsets
+hipError_t launch_literal_merge(const DevAdded &a, const Batch &b, const AddLayout &A, uint32_t n_lit,
+                                uint32_t *out_ids, uint64_t *out_offsets, uint32_t *out_spans, hipStream_t s);
 
 hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
 hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);

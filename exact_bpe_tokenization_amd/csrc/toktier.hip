@@ -25,7 +25,9 @@ struct toktier_vocab {
     void *dwords;   // whole-piece tables (may be NULL)
     void *dstr;     // token strings and their hash (may be NULL)
     void *dlen;     // byte length of every token
+    void *dadded;   // added-token tables (NULL without added tokens)
     DevVocab dv;
+    DevAdded da;    // da.n == 0: no added tokens
 };
 
 static thread_local std::string g_hip_err;
@@ -181,6 +183,92 @@ void build_tables(int fam, uint64_t *fmap, uint32_t *fstart)
                 }
 }
 
+// valid UTF-8 in the sense the pre-tokenizer checks: no overlong forms, surrogates or code points
+// above U+10FFFF, no truncated or stray sequences
+bool valid_utf8(const uint8_t *s, uint32_t n)
+{
+    for (uint32_t i = 0; i < n;) {
+        const uint32_t c = s[i];
+        uint32_t len = c < 0x80 ? 1 : (c >> 5) == 6 ? 2 : (c >> 4) == 14 ? 3 : (c >> 3) == 30 ? 4 : 0;
+        if (!len || i + len > n) return false;
+        uint32_t cp = len == 1 ? c : c & (0x7Fu >> len);
+        for (uint32_t k = 1; k < len; ++k) {
+            if ((s[i + k] & 0xC0) != 0x80) return false;
+            cp = (cp << 6) | (s[i + k] & 0x3Fu);
+        }
+        static const uint32_t min_cp[5] = {0, 0, 0x80, 0x800, 0x10000};
+        if (cp < min_cp[len] || cp > 0x10FFFF || (cp >= 0xD800 && cp <= 0xDFFF)) return false;
+        i += len;
+    }
+    return true;
+}
+
+// the added-token tables: literals, IDs, the first-two-bytes map and lists (longest first), the
+// one-byte literals
+int build_added_tables(toktier_vocab *v, const uint8_t *bytes, const uint32_t *offs, const uint32_t *ids,
+                       uint32_t n)
+{
+    const uint32_t total = offs[n];
+    std::vector<uint32_t> pmap(2048, 0), pre(65537, 0), list, one(256, NO_LIT);
+    std::vector<std::vector<uint32_t>> by2(65536);
+    uint32_t lmin = ~0u, lmax = 0;
+    for (uint32_t k = 0; k < n; ++k) {
+        const uint32_t len = offs[k + 1] - offs[k];
+        lmin = std::min(lmin, len);
+        lmax = std::max(lmax, len);
+        const uint8_t *s = bytes + offs[k];
+        if (len == 1) { one[s[0]] = k; continue; }
+        const uint32_t x = s[0] | ((uint32_t)s[1] << 8);
+        by2[x].push_back(k);
+        pmap[x >> 5] |= 1u << (x & 31);
+    }
+    for (uint32_t x = 0; x < 65536; ++x) {
+        std::vector<uint32_t> &l = by2[x];
+        std::sort(l.begin(), l.end(), [&](uint32_t a, uint32_t b) {
+            const uint32_t la = offs[a + 1] - offs[a], lb = offs[b + 1] - offs[b];
+            return la != lb ? la > lb : a < b;
+        });
+        pre[x] = (uint32_t)list.size();
+        list.insert(list.end(), l.begin(), l.end());
+    }
+    pre[65536] = (uint32_t)list.size();
+    const uint64_t o_bytes = 0, o_off = align256(total + 1), o_id = o_off + align256(4ull * (n + 1));
+    const uint64_t o_pmap = o_id + align256(4ull * n), o_pre = o_pmap + align256(4ull * pmap.size());
+    const uint64_t o_list = o_pre + align256(4ull * pre.size()), o_one = o_list + align256(4ull * list.size() + 4);
+    const uint64_t size = o_one + align256(4ull * 256);
+    void *d = nullptr;
+    hipError_t e = hipMalloc(&d, size);
+    if (e != hipSuccess) {
+        hip_fail(e);
+        return TOKTIER_E_OOM;
+    }
+    uint8_t *base = (uint8_t *)d;
+    e = hipMemcpy(base + o_bytes, bytes, total, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(base + o_off, offs, 4ull * (n + 1), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(base + o_id, ids, 4ull * n, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(base + o_pmap, pmap.data(), 4ull * pmap.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(base + o_pre, pre.data(), 4ull * pre.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !list.empty())
+        e = hipMemcpy(base + o_list, list.data(), 4ull * list.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(base + o_one, one.data(), 4ull * 256, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(d);
+        return hip_fail(e);
+    }
+    v->dadded = d;
+    v->da.bytes = base + o_bytes;
+    v->da.off = (const uint32_t *)(base + o_off);
+    v->da.id = (const uint32_t *)(base + o_id);
+    v->da.pmap = (const uint32_t *)(base + o_pmap);
+    v->da.pre = (const uint32_t *)(base + o_pre);
+    v->da.list = (const uint32_t *)(base + o_list);
+    v->da.one = (const uint32_t *)(base + o_one);
+    v->da.n = n;
+    v->da.lmin = lmin;
+    v->da.lmax = lmax;
+    return TOKTIER_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------
@@ -269,6 +357,9 @@ int build_string_table(toktier_vocab *v, const TokenStrings &ts)
     return TOKTIER_OK;
 }
 
+int fill_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts, const std::vector<uint32_t> &cand,
+                            const std::vector<uint32_t> &pv);
+
 int build_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts)
 {
     const uint32_t ntok_all = (uint32_t)ts.len.size();
@@ -284,13 +375,26 @@ int build_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts)
     }
     if (cand.empty()) return TOKTIER_OK;
     const uint32_t npc = (uint32_t)cand.size();
+    std::vector<uint32_t> pv(npc);
+    if (v->dv.flags & VF_IGNORE_MERGES) {
+        // every token string is its own piece's result: the smallest ID of each string
+        std::vector<std::pair<std::string, uint32_t>> keyed;
+        keyed.reserve(npc);
+        for (uint32_t i = 0; i < npc; ++i)
+            keyed.emplace_back(std::string((const char *)&tb[off[cand[i]]], len[cand[i]]), cand[i]);
+        std::sort(keyed.begin(), keyed.end());
+        std::vector<uint32_t> first(ntok_all, 0);
+        for (size_t i = 0; i < keyed.size(); ++i)
+            if (i == 0 || keyed[i].first != keyed[i - 1].first) first[keyed[i].second] = 1;
+        for (uint32_t i = 0; i < npc; ++i) pv[i] = first[cand[i]] ? cand[i] : NO_PIECE;
+        return fill_whole_piece_tables(v, ts, cand, pv);
+    }
     starts.push_back((uint32_t)batch.size());
     const uint64_t N = batch.size();
     const Layout L = make_layout(N);
     uint8_t *dbytes = nullptr, *dws = nullptr;
     hipError_t e = hipMalloc((void **)&dbytes, N);
     if (e == hipSuccess) e = hipMalloc((void **)&dws, L.total);
-    std::vector<uint32_t> pv(npc);
     if (e == hipSuccess) e = hipMemcpy(dbytes, batch.data(), N, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(dws + L.ctrl, 0, sizeof(Ctrl));
     if (e == hipSuccess) e = hipMemset(dws + L.tilex, 0, 4ull * L.n_scan_tiles);
@@ -307,7 +411,16 @@ int build_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts)
     if (dbytes) (void)hipFree(dbytes);
     if (dws) (void)hipFree(dws);
     if (e != hipSuccess) return hip_fail(e);
+    return fill_whole_piece_tables(v, ts, cand, pv);
+}
 
+// the tables from the candidates whose result word pv[i] is the candidate itself
+int fill_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts, const std::vector<uint32_t> &cand,
+                            const std::vector<uint32_t> &pv)
+{
+    const std::vector<uint32_t> &len = ts.len, &off = ts.off;
+    const std::vector<uint8_t> &tb = ts.tb;
+    const uint32_t npc = (uint32_t)cand.size();
     std::vector<uint32_t> short_t, long_t;
     for (uint32_t i = 0; i < npc; ++i) {
         if (pv[i] != cand[i]) continue;   // not self-reachable: BPE of its bytes is not [token]
@@ -341,7 +454,7 @@ int build_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts)
     }
     void *d = nullptr;
     const uint64_t bytes_a = 16 * ca, bytes_b = 48 * cb;
-    e = hipMalloc(&d, bytes_a + bytes_b);
+    hipError_t e = hipMalloc(&d, bytes_a + bytes_b);
     if (e != hipSuccess) {
         hip_fail(e);
         return TOKTIER_E_OOM;
@@ -387,7 +500,28 @@ extern "C" const char *toktier_unicode_table_sha256(void) { return TT_UNICODE_TA
 
 extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int family, toktier_vocab **out)
 {
+    return toktier_load_vocab_ex(merges, n_merges, family, 0, nullptr, nullptr, nullptr, 0, out);
+}
+
+extern "C" int toktier_load_vocab_ex(const uint32_t *merges, uint32_t n_merges, int family, uint32_t flags,
+                                     const uint8_t *added_bytes, const uint32_t *added_offsets,
+                                     const uint32_t *added_ids, uint32_t n_added, toktier_vocab **out)
+{
     if (!out || (n_merges && !merges)) return TOKTIER_E_INVALID_ARG;
+    if ((flags & ~(uint32_t)TOKTIER_IGNORE_MERGES) || n_added > TOKTIER_MAX_ADDED) return TOKTIER_E_INVALID_ARG;
+    if (n_added) {
+        if (!added_bytes || !added_offsets || !added_ids || added_offsets[0] != 0) return TOKTIER_E_INVALID_ARG;
+        std::vector<std::string> seen;
+        for (uint32_t k = 0; k < n_added; ++k) {
+            if (added_offsets[k + 1] <= added_offsets[k]) return TOKTIER_E_INVALID_ARG;
+            const uint32_t len = added_offsets[k + 1] - added_offsets[k];
+            if (len > TOKTIER_MAX_ADDED_BYTES || !valid_utf8(added_bytes + added_offsets[k], len))
+                return TOKTIER_E_INVALID_ARG;
+            seen.emplace_back((const char *)added_bytes + added_offsets[k], len);
+        }
+        std::sort(seen.begin(), seen.end());
+        if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return TOKTIER_E_INVALID_ARG;
+    }
     if (family != TOKTIER_GPT2 && family != TOKTIER_CL100K && family != TOKTIER_O200K) return TOKTIER_E_BAD_FAMILY;
     if (n_merges > TOKTIER_MAX_MERGES) return TOKTIER_E_BAD_MERGES;
 
@@ -473,6 +607,7 @@ extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int
     v->dv.shift = shift;
     v->dv.n_merges = n_merges;
     v->dv.family = family;
+    v->dv.flags = (flags & TOKTIER_IGNORE_MERGES) ? VF_IGNORE_MERGES : 0u;
     v->dv.wa = nullptr;
     v->dv.wb = nullptr;
     v->dv.str = nullptr;
@@ -487,8 +622,12 @@ extern "C" int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int
         v->dv.tok_len = (const uint32_t *)v->dlen;
     }
     if (rc == TOKTIER_OK) rc = build_string_table(v, ts);
+    // ignore_merges looks long pieces up in the token string hash, which needs tokens <= STR_LMAX bytes
+    if (rc == TOKTIER_OK && (v->dv.flags & VF_IGNORE_MERGES) && !v->dv.str) rc = TOKTIER_E_INVALID_ARG;
     if (rc == TOKTIER_OK) rc = build_whole_piece_tables(v, ts);
+    if (rc == TOKTIER_OK && n_added) rc = build_added_tables(v, added_bytes, added_offsets, added_ids, n_added);
     if (rc != TOKTIER_OK) {
+        if (v->dadded) (void)hipFree(v->dadded);
         if (v->dwords) (void)hipFree(v->dwords);
         if (v->dstr) (void)hipFree(v->dstr);
         if (v->dlen) (void)hipFree(v->dlen);
@@ -505,7 +644,7 @@ extern "C" int toktier_free_vocab(toktier_vocab *v)
     if (!v) return TOKTIER_OK;
     hipError_t e = hipDeviceSynchronize();
     hipError_t f = hipFree(v->dmem);
-    for (void *extra : {v->dwords, v->dstr, v->dlen}) {
+    for (void *extra : {v->dwords, v->dstr, v->dlen, v->dadded}) {
         if (!extra) continue;
         hipError_t g = hipFree(extra);
         if (f == hipSuccess) f = g;
@@ -528,6 +667,16 @@ extern "C" int toktier_workspace_bytes(uint64_t total_bytes, uint32_t n_docs, ui
 {
     if (!out_bytes || total_bytes >= 0xFFFFFFFFull || n_docs == 0xFFFFFFFFu) return TOKTIER_E_INVALID_ARG;
     *out_bytes = make_layout(total_bytes).total;
+    return TOKTIER_OK;
+}
+
+extern "C" int toktier_workspace_bytes_ex(const toktier_vocab *v, uint64_t total_bytes, uint32_t n_docs,
+                                          uint64_t *out_bytes)
+{
+    if (!v) return TOKTIER_E_INVALID_ARG;
+    int rc = toktier_workspace_bytes(total_bytes, n_docs, out_bytes);
+    if (rc || !v->da.n) return rc;
+    *out_bytes = make_add_layout(*out_bytes, total_bytes, n_docs, v->da.lmin).total;
     return TOKTIER_OK;
 }
 
@@ -588,6 +737,36 @@ int encode_impl(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *of
     if (!out_offsets || (total_bytes && !out_ids)) return TOKTIER_E_INVALID_ARG;
     if (ids_capacity < total_bytes) return TOKTIER_E_CAPACITY;
     hipStream_t s = (hipStream_t)stream;
+    if (v->da.n && total_bytes) {
+        // added tokens: literal pass, one read of the literal count, then the pipeline on the
+        // documents cut at the literals and the final merge
+        const AddLayout A = make_add_layout(b.L.total, total_bytes, n_docs, v->da.lmin);
+        if (workspace_bytes < A.total) return TOKTIER_E_CAPACITY;
+        HIP_TRY(launch_literals(v->da, b, A, s));
+        LitCtrl lc;
+        HIP_TRY(hipMemcpyAsync(&lc, b.ws + A.lctrl, sizeof(LitCtrl), hipMemcpyDeviceToHost, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        if (lc.status & ST_BAD_OFFSETS) return TOKTIER_E_INVALID_ARG;
+        if (lc.n_lit) {
+            if ((uint64_t)n_docs + 2ull * lc.n_lit >= 0xFFFFFFFFull || lc.n_lit > A.k_cap) return TOKTIER_E_CAPACITY;
+            HIP_TRY(launch_literal_docs(b, A, lc.n_lit, s));
+            Batch b2 = b;
+            b2.offsets = (const uint64_t *)(b.ws + A.offs2);
+            b2.n_docs = n_docs + 2 * lc.n_lit;
+            HIP_TRY(launch_pretokenize(v->dv, b2, s, ev));
+            HIP_TRY(launch_route(v->dv, b2, s, ev));
+            HIP_TRY(launch_bpe(v->dv, b2, s, ev));
+            HIP_TRY(launch_compact(v->dv, b2, (uint32_t *)(b.ws + A.ids2), (uint64_t *)(b.ws + A.oo2),
+                                   out_spans ? (uint32_t *)(b.ws + A.spans2) : nullptr, s, ev));
+            HIP_TRY(launch_literal_merge(v->da, b, A, lc.n_lit, out_ids, out_offsets, out_spans, s));
+            if (!out_n_tokens) return TOKTIER_OK;
+            Ctrl c;
+            rc = read_ctrl(workspace, s, &c);
+            if (rc) return rc;
+            *out_n_tokens = c.n_tokens;
+            return TOKTIER_OK;
+        }
+    }
     HIP_TRY(launch_pretokenize(v->dv, b, s, ev));
     HIP_TRY(launch_route(v->dv, b, s, ev));
     HIP_TRY(launch_bpe(v->dv, b, s, ev));

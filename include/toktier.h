@@ -74,6 +74,44 @@ enum {
  */
 int toktier_load_vocab(const uint32_t *merges, uint32_t n_merges, int family, toktier_vocab **out);
 
+/* Vocabulary flags of toktier_load_vocab_ex. */
+enum {
+    /* A piece whose bytes are some token's bytes becomes that token (the smallest such ID), without
+     * the merge loop; other pieces merge as usual (paper, GPU BPE paragraph: the encoders configured
+     * with ignore_merges, Llama 3 and gpt-oss, emit one ID for a piece that is a vocabulary entry). */
+    TOKTIER_IGNORE_MERGES = 1
+};
+
+/* Limits on added tokens. */
+#define TOKTIER_MAX_ADDED 65536u
+#define TOKTIER_MAX_ADDED_BYTES 256u
+
+/*
+ * toktier_load_vocab with vocabulary flags and added tokens.
+ *   flags          0 or TOKTIER_IGNORE_MERGES.  TOKTIER_IGNORE_MERGES needs every token to be at
+ *                  most 256 bytes long (else E_INVALID_ARG).
+ *   added_bytes    host, the added tokens' byte strings concatenated (may be NULL when n_added = 0).
+ *   added_offsets  host, uint32[n_added + 1]: token k is added_bytes[added_offsets[k] ..
+ *                  added_offsets[k+1]); added_offsets[0] = 0.
+ *   added_ids      host, uint32[n_added]: the ID that token k is encoded as (any value; typically
+ *                  256 + n_merges + k, or a model's reserved ID).
+ *   n_added        0 .. TOKTIER_MAX_ADDED.
+ * Added tokens (special tokens such as <|endoftext|>) are literals that the model reserves as single
+ * IDs.  Before the family's pre-tokenizer runs, each document is scanned left to right for them,
+ * leftmost-longest: where one or more literals start and end inside the document, the longest is
+ * taken and the scan resumes after it (paper, implementation paragraph on added and special
+ * tokens).  Each taken literal becomes its one ID; the text between literals is tokenized as if it
+ * were a document of its own.  Every literal must be 1 .. TOKTIER_MAX_ADDED_BYTES bytes of valid
+ * UTF-8, and no two may be equal (else E_INVALID_ARG).
+ * Encoding with added tokens costs one host read of the literal count inside the encode call (that
+ * call then synchronizes its stream even when out_n_tokens is NULL) and a larger workspace
+ * (toktier_workspace_bytes_ex).  toktier_pretokenize_batch ignores added tokens.
+ * Errors: as toktier_load_vocab.  Synchronous.
+ */
+int toktier_load_vocab_ex(const uint32_t *merges, uint32_t n_merges, int family, uint32_t flags,
+                          const uint8_t *added_bytes, const uint32_t *added_offsets, const uint32_t *added_ids,
+                          uint32_t n_added, toktier_vocab **out);
+
 /* Release a handle and its device tables (synchronizes the device).  NULL is accepted. */
 int toktier_free_vocab(toktier_vocab *v);
 
@@ -86,6 +124,16 @@ int toktier_vocab_info(const toktier_vocab *v, uint32_t *n_merges, int *family);
  * Errors: E_INVALID_ARG (total_bytes >= 2^32 - 1 or n_docs == 0xFFFFFFFF).
  */
 int toktier_workspace_bytes(uint64_t total_bytes, uint32_t n_docs, uint64_t *out_bytes);
+
+/*
+ * Workspace size for encoding with vocabulary v: equal to toktier_workspace_bytes for a vocabulary
+ * without added tokens; with added tokens it also holds the literal matches and the intermediate
+ * output of the documents cut at the literals (up to about 80 bytes per input byte more when the
+ * shortest literal is one byte long, less for longer ones).  Pure host arithmetic.
+ * Errors: E_INVALID_ARG.
+ */
+int toktier_workspace_bytes_ex(const toktier_vocab *v, uint64_t total_bytes, uint32_t n_docs,
+                               uint64_t *out_bytes);
 
 /*
  * Tokenize a batch of documents (paper: multi-document batches are concatenated and runs are cut
@@ -103,7 +151,8 @@ int toktier_workspace_bytes(uint64_t total_bytes, uint32_t n_docs, uint64_t *out
  *                suffices); otherwise TOKTIER_E_CAPACITY before any device work.
  *   out_offsets  device, uint64[n_docs + 1]: out_offsets[d] is the index in out_ids of document
  *                d's first token; out_offsets[n_docs] is the total token count.
- *   workspace    device scratch of at least toktier_workspace_bytes(total_bytes, n_docs) bytes,
+ *   workspace    device scratch of at least toktier_workspace_bytes_ex(v, total_bytes, n_docs) bytes
+ *                (= toktier_workspace_bytes(total_bytes, n_docs) for a vocabulary without added tokens),
  *                256-byte aligned; contents on entry do not matter.
  *   stream       hipStream_t (passed as void*); NULL means the default stream.
  *   out_n_tokens host; if non-NULL the call waits for the stream and stores the token count

@@ -326,6 +326,10 @@ def encode_batch_ex(family, merges, data, offsets=None, added=(), ignore_merges=
     # concatenated; each is a document of its own)
     text = b"".join(raw[a:b] for a, b in segs)
     cut = np.concatenate([[0], np.cumsum([b - a for a, b in segs])]).astype(np.uint64)
+    if not ignore_merges:   # F on the segments as documents
+        e, eo = encode_batch(family, m, text, cut)
+        seg_ids = [e[int(eo[i]):int(eo[i + 1])].tolist() for i in range(len(segs))]
+        return _join_items(items, seg_ids, lid)
     starts = pretokenize(family, text, cut)
     pieces = [text[int(starts[k]):int(starts[k + 1])] for k in range(len(starts) - 1)]
     whole = {}
@@ -347,6 +351,11 @@ def encode_batch_ex(family, merges, data, offsets=None, added=(), ignore_merges=
     seg_ids = [[] for _ in segs]
     for i, sidx in enumerate(piece_seg.tolist()):
         seg_ids[sidx].extend(ids_of[i])
+    return _join_items(items, seg_ids, lid)
+
+
+def _join_items(items, seg_ids, lid):
+    """Per document, the text segments' IDs with the literals' IDs between them."""
     out, oo, si = [], [0], 0
     for doc in items:
         for it in doc:
