@@ -71,6 +71,9 @@ constexpr int RT_PPT = 2;   // pieces per thread in flight (more costs occupancy
 constexpr uint32_t RTQ[NROUTES] = {2048, 512, 256, 128, 64, 64, 64};
 constexpr uint32_t RTQ_OFF[NROUTES + 1] = {0, 2048, 2560, 2816, 2944, 3008, 3072, 3136};
 
+// IGN: the vocabulary ignores merges (pieces longer than the whole-piece tables are looked up in the
+// token string hash); a template flag so that the usual instantiation carries none of that code
+template <bool IGN>
 __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
                                                       Layout L)
 {
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t 
 #pragma unroll
         for (int u = 0; u < RT_PPT; ++u) {
             if (pp[u] >= end) continue;
-            if (st[u] != WP_HIT && (v.flags & VF_IGNORE_MERGES) && len[u] > (uint32_t)TABLE_MAX && len[u] <= v.lmax) {
+            if (IGN && st[u] != WP_HIT && len[u] > (uint32_t)TABLE_MAX && len[u] <= v.lmax) {
                 id[u] = whole_token(v, bytes + a0[u], len[u]);
                 if (id[u] != NO_PIECE) st[u] = WP_HIT;
             }
@@ -1161,7 +1164,10 @@ hipError_t launch_route(const DevVocab &v, const Batch &b, hipStream_t s, const 
     if (b.n == 0) return hipGetLastError();
     const uint64_t g = (b.n + 4095) / 4096;   // about 4 KiB of input (1-2K pieces) per workgroup, at most 1024
     LaunchScope k(ev, 2, s);
-    hipLaunchKernelGGL(k_route, dim3(g > 1024 ? 1024u : (uint32_t)g), dim3(RT_THREADS), 0, s, v, b.bytes, b.ws, b.L);
+    if (v.flags & VF_IGNORE_MERGES)
+        hipLaunchKernelGGL(k_route<true>, dim3(g > 1024 ? 1024u : (uint32_t)g), dim3(RT_THREADS), 0, s, v, b.bytes, b.ws, b.L);
+    else
+        hipLaunchKernelGGL(k_route<false>, dim3(g > 1024 ? 1024u : (uint32_t)g), dim3(RT_THREADS), 0, s, v, b.bytes, b.ws, b.L);
     return hipGetLastError();
 }
 
