@@ -23,7 +23,7 @@ import numpy as np
 
 from . import unicode_classes
 
-FAMILIES = {"gpt2": 1, "cl100k": 2, "o200k": 3}
+FAMILIES = {"gpt2": 1, "cl100k": 2, "o200k": 3, "deepseek": 4}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _BUILD = os.path.join(_HERE, "_build")

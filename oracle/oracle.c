@@ -20,8 +20,9 @@
  *  T  The BPE trainer that produces the merge lists used as inputs (most frequent pair, ties to the
  *     smallest (left, right); merges creating a token longer than max_token_bytes are skipped).
  *
- * The three rule families are this project's own wording of the GPT-2-, cl100k- and o200k-style
- * patterns the paper evaluates (paper, derivation paragraph: "cl100k lineage", "o200k lineage").
+ * The rule families are this project's own wording of the GPT-2-, cl100k-, o200k- and
+ * DeepSeek-style patterns the paper evaluates (paper, derivation paragraph: the cl100k and o200k
+ * lineages, and the DeepSeek family's three splitters applied in sequence).
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -30,7 +31,7 @@
 /* ------------------------------------------------------------------------------------------ */
 /* character classes (table probed out of the `regex` engine by unicode_classes.py)            */
 
-enum { C_LU = 1, C_LL = 2, C_LO = 3, C_N = 4, C_W = 5, C_M = 6, C_O = 7 };
+enum { C_LU = 1, C_LL = 2, C_LO = 3, C_N = 4, C_W = 5, C_M = 6, C_O = 7, C_PS = 8 };   /* PS: \p{P} or \p{S} */
 static uint8_t *g_cls = NULL;
 
 int orc_set_classes(const uint8_t *table, uint64_t n)
@@ -54,6 +55,20 @@ static inline int is_X(uint32_t c) { return !is_crlf(c) && !is_L(c) && !is_N(c);
 /* o200k-style letter sets: A = [\p{Lu}\p{Lt}\p{Lm}\p{Lo}\p{M}], B = [\p{Ll}\p{Lm}\p{Lo}\p{M}] */
 static inline int is_A(uint32_t c) { int k = klass(c); return k == C_LU || k == C_LO || k == C_M; }
 static inline int is_B(uint32_t c) { int k = klass(c); return k == C_LL || k == C_LO || k == C_M; }
+
+/* DeepSeek-style sets */
+static inline int is_PS(uint32_t c) { return klass(c) == C_PS; }
+static inline int is_LM(uint32_t c) { return is_L(c) || klass(c) == C_M; }
+static inline int is_ascii_alpha(uint32_t c) { return (c >= 'a' && c <= 'z') || (c >= 'A' && c <= 'Z'); }
+/* the 32 ASCII punctuation and symbol characters: ! through /, : through @, [ through `, { through ~ */
+static inline int is_ascii_punct(uint32_t c)
+{
+    return (c >= 0x21 && c <= 0x2F) || (c >= 0x3A && c <= 0x40) || (c >= 0x5B && c <= 0x60) || (c >= 0x7B && c <= 0x7E);
+}
+/* CJK unified ideographs U+4E00..U+9FA5, hiragana and katakana blocks U+3040..U+30FF */
+static inline int is_cjk(uint32_t c) { return (c >= 0x4E00 && c <= 0x9FA5) || (c >= 0x3040 && c <= 0x30FF); }
+/* [^\r\n\p{L}\p{P}\p{S}] */
+static inline int is_ds_prefix(uint32_t c) { return !is_crlf(c) && !is_L(c) && !is_PS(c); }
 
 /* ------------------------------------------------------------------------------------------ */
 /* UTF-8 decode with validation (RFC 3629: no overlongs, no surrogates, nothing above U+10FFFF)  */
@@ -231,7 +246,85 @@ static int64_t ok_word_upper(const Doc *d, int64_t p)       /* X? A+ B* C? */
     return -1;
 }
 
+/* ---- DeepSeek style: three splitters applied one after the other ----
+ * Stage 1 isolates digit groups (\p{N}{1,3}), stage 2 isolates runs of CJK ideographs and kana,
+ * stage 3 splits with the body alternatives below.  Each stage re-splits every piece of the stage
+ * before it on its own (the piece's ends are the text's ends for the stage's matcher), and the
+ * characters between two matches of a stage form a piece too (paper, derivation paragraph on the
+ * DeepSeek family: the splitters' composition is one per-character predicate provided every
+ * splitter re-splits each earlier piece and unmatched spans survive as pieces). */
+
+/* stage 2: [\u4E00-\u9FA5\u3040-\u30FF]+ */
+static int64_t ds_cjk_run(const Doc *d, int64_t p) { return is_cjk(d->c[p]) ? run_end(d, p, is_cjk) : -1; }
+
+/* stage 3, alternative 1: one ASCII punctuation or symbol character, then ASCII letters */
+static int64_t ds_punct_word(const Doc *d, int64_t p)
+{
+    if (!is_ascii_punct(d->c[p]) || p + 1 >= d->n || !is_ascii_alpha(d->c[p + 1])) return -1;
+    return run_end(d, p + 1, is_ascii_alpha);
+}
+
+/* alternative 2: [^\r\n\p{L}\p{P}\p{S}]?[\p{L}\p{M}]+ (the optional prefix is tried first) */
+static int64_t ds_word(const Doc *d, int64_t p)
+{
+    if (is_ds_prefix(d->c[p]) && p + 1 < d->n && is_LM(d->c[p + 1])) return run_end(d, p + 1, is_LM);
+    return is_LM(d->c[p]) ? run_end(d, p, is_LM) : -1;
+}
+
+/* alternative 3: ' ?[\p{P}\p{S}]+[\r\n]*' */
+static int64_t ds_punct(const Doc *d, int64_t p)
+{
+    int64_t q = sp_opt_run(d, p, is_PS);
+    if (q < 0) return -1;
+    while (q < d->n && is_crlf(d->c[q])) q++;
+    return q;
+}
+
 typedef int64_t (*alt_fn)(const Doc *, int64_t);
+
+static const alt_fn DS_STAGE1[] = { num_upto3, NULL };
+static const alt_fn DS_STAGE2[] = { ds_cjk_run, NULL };
+static const alt_fn DS_STAGE3[] = { ds_punct_word, ds_word, ds_punct, ws_to_last_newline, ws_not_before_nonws,
+                                    ws_all, NULL };
+
+/* One splitter on chars [a, b) of doc: leftmost-first matching, each match starting where the last
+ * one ended; a position where no alternative matches is passed over, and the passed-over characters
+ * between two matches form one piece.  Appends the piece starts (document char indices) to out. */
+static int64_t split_isolated(const uint32_t *cp, int64_t a, int64_t b, const alt_fn *alts, int64_t *out)
+{
+    Doc sub = { cp + a, b - a };
+    int64_t np = 0, p = 0;
+    int in_gap = 0;
+    while (p < sub.n) {
+        int64_t e = -1;
+        for (int k = 0; alts[k]; k++) {
+            e = alts[k](&sub, p);
+            if (e > p) break;
+        }
+        if (e > p) {
+            out[np++] = a + p;
+            in_gap = 0;
+            p = e;
+        } else {
+            if (!in_gap) out[np++] = a + p;
+            in_gap = 1;
+            p++;
+        }
+    }
+    return np;
+}
+
+/* The three stages over one document of nc chars: returns the number of pieces, their starts (char
+ * indices) in s3.  s1, s2, s3 hold nc + 1 entries each. */
+static int64_t ds_split_doc(const uint32_t *cp, int64_t nc, int64_t *s1, int64_t *s2, int64_t *s3)
+{
+    int64_t n1 = split_isolated(cp, 0, nc, DS_STAGE1, s1), n2 = 0, n3 = 0;
+    s1[n1] = nc;
+    for (int64_t k = 0; k < n1; k++) n2 += split_isolated(cp, s1[k], s1[k + 1], DS_STAGE2, s2 + n2);
+    s2[n2] = nc;
+    for (int64_t k = 0; k < n2; k++) n3 += split_isolated(cp, s2[k], s2[k + 1], DS_STAGE3, s3 + n3);
+    return n3;
+}
 
 static const alt_fn FAM_G2[] = { g2_contraction, g2_letters, g2_numbers, g2_other,
                                  ws_not_before_nonws, ws_all, NULL };
@@ -246,6 +339,7 @@ static const alt_fn *family_alts(int family)
     case 1: return FAM_G2;
     case 2: return FAM_CL;
     case 3: return FAM_OK;
+    case 4: return DS_STAGE3;   /* the DeepSeek style runs all three stages (ds_split_doc) */
     default: return NULL;
     }
 }
@@ -268,13 +362,21 @@ int64_t orc_pretokenize(int family, const uint8_t *text, uint64_t n, const uint6
     }
     uint32_t *cp = (uint32_t *)malloc((maxdoc + 1) * sizeof(uint32_t));
     uint64_t *pos = (uint64_t *)malloc((maxdoc + 1) * sizeof(uint64_t));
-    if (!cp || !pos) { free(cp); free(pos); return -5; }
+    int64_t *ds = family == 4 ? (int64_t *)malloc(3 * (maxdoc + 1) * sizeof(int64_t)) : NULL;
+    if (!cp || !pos || (family == 4 && !ds)) { free(cp); free(pos); free(ds); return -5; }
     uint64_t np = 0;
     int64_t rc = 0;
     for (uint32_t d = 0; d < n_docs && rc == 0; d++) {
         uint64_t b0 = offsets[d];
         int64_t nc = utf8_decode(text + b0, offsets[d + 1] - b0, cp, pos);
         if (nc < 0) { rc = -1; break; }
+        if (family == 4) {
+            int64_t *s3 = ds + 2 * (maxdoc + 1);
+            int64_t n3 = ds_split_doc(cp, nc, ds, ds + (maxdoc + 1), s3);
+            if (np + (uint64_t)n3 > cap) { rc = -2; break; }
+            for (int64_t k = 0; k < n3; k++) piece_starts[np++] = b0 + pos[s3[k]];
+            continue;
+        }
         Doc doc = { cp, nc };
         int64_t p = 0;
         while (p < nc) {
@@ -291,6 +393,7 @@ int64_t orc_pretokenize(int family, const uint8_t *text, uint64_t n, const uint6
     }
     free(cp);
     free(pos);
+    free(ds);
     return rc ? rc : (int64_t)np;
 }
 

@@ -12,7 +12,8 @@ Codes (one byte per code point, index = code point):
     4 N   number                          (\\p{N})
     5 W   whitespace                      (what `\\s` matches)
     6 M   mark                            (\\p{M}; "other" in the 4-class split, a letter for o200k)
-    7 O   everything else
+    7 O   everything else: controls, format characters, private use, unassigned, surrogates
+    8 PS  punctuation or symbol           (\\p{P} | \\p{S}; "other" in the 4-class split)
 
 This module is only imported by tests, by the smoke check and by the benchmark's CPU-baseline leg.
 """
@@ -21,7 +22,7 @@ import hashlib
 import numpy as np
 
 MAXCP = 0x110000
-LU, LL, LO, N, W, M, O = 1, 2, 3, 4, 5, 6, 7
+LU, LL, LO, N, W, M, O, PS = 1, 2, 3, 4, 5, 6, 7, 8
 
 _PROBES = (
     (LU, r"[\p{Lu}\p{Lt}]"),
@@ -30,6 +31,7 @@ _PROBES = (
     (N, r"\p{N}"),
     (W, r"\s"),
     (M, r"\p{M}"),
+    (PS, r"[\p{P}\p{S}]"),
 )
 
 _cache = None

@@ -327,6 +327,43 @@ def multilingual(seed, n_chars):
     return _cut(" ".join(words), n_chars)
 
 
+def kana_mix(seed, n_chars):
+    """Multilingual text (above) with, by code-point count, ~6% kana runs (hiragana U+3041-U+3096,
+    katakana U+30A1-U+30FA, with the prolonged sound mark U+30FC and the middle dot U+30FB inside),
+    ~2% CJK punctuation (U+3001, U+3002, U+300C, U+300D, U+FF08, U+FF09), ~1% digits glued to the
+    ends of words, and a few kana-block characters that are marks, symbols, dashes or unassigned
+    (U+3099, U+309B, U+30A0, U+3040).  Exactly n_chars code points."""
+    rng = np.random.default_rng(seed)
+    words = multilingual(seed + 2_000_003, int(n_chars * 0.92) + 64).split(" ")
+    nw = len(words)
+    hira = [chr(c) for c in range(0x3041, 0x3097)]
+    kata = [chr(c) for c in range(0x30A1, 0x30FB)]
+    punct = ["\u3001", "\u3002", "\u300c", "\u300d", "\uff08", "\uff09"]
+    odd = ["\u3099", "\u309b", "\u30a0", "\u3040"]
+    got = 0
+    while got < int(0.06 * n_chars):
+        k = int(rng.integers(2, 10))
+        src = hira if rng.random() < 0.5 else kata
+        run = [src[int(j)] for j in rng.integers(0, len(src), k)]
+        if rng.random() < 0.3:
+            run[int(rng.integers(0, k))] = "\u30fc" if rng.random() < 0.6 else "\u30fb"
+        i = int(rng.integers(0, nw))
+        words[i] = "".join(run) + words[i] if rng.random() < 0.5 else words[i] + "".join(run)
+        got += k
+    for _ in range(int(0.02 * n_chars)):
+        i = int(rng.integers(0, nw))
+        c = punct[int(rng.integers(0, len(punct)))]
+        words[i] = words[i] + c if rng.random() < 0.7 else c + words[i]
+    for _ in range(int(0.01 * n_chars / 2)):
+        i = int(rng.integers(0, nw))
+        d = str(int(rng.integers(0, 10 ** int(rng.integers(1, 5)))))
+        words[i] = words[i] + d if rng.random() < 0.5 else d + words[i]
+    for _ in range(max(1, n_chars // 2000)):
+        i = int(rng.integers(0, nw))
+        words[i] = words[i] + odd[int(rng.integers(0, len(odd)))]
+    return _cut(" ".join(words), n_chars)
+
+
 def _alternating(rng, n):
     letters = "abcdefghijklmnopqrstuvwxyzABCDEFGHIJKLMNOPQRSTUVWXYZé中"
     digits = "0123456789٣"
