@@ -14,9 +14,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # TOKTIER_LIBRARY may name another build of the same library (same exports), e.g. an instrumented one
 LIB_PATH = os.environ.get("TOKTIER_LIBRARY") or os.path.join(HERE, "libtoktier.so")
 
-TOKTIER_GPT2, TOKTIER_CL100K, TOKTIER_O200K = 1, 2, 3
+TOKTIER_GPT2, TOKTIER_CL100K, TOKTIER_O200K, TOKTIER_DEEPSEEK = 1, 2, 3, 4
 TOKTIER_IGNORE_MERGES = 1
-FAMILIES = {"gpt2": TOKTIER_GPT2, "cl100k": TOKTIER_CL100K, "o200k": TOKTIER_O200K}
+FAMILIES = {"gpt2": TOKTIER_GPT2, "cl100k": TOKTIER_CL100K, "o200k": TOKTIER_O200K,
+            "deepseek": TOKTIER_DEEPSEEK}
 STATUS = {0: "TOKTIER_OK", 1: "TOKTIER_E_INVALID_ARG", 2: "TOKTIER_E_BAD_FAMILY", 3: "TOKTIER_E_BAD_MERGES",
           4: "TOKTIER_E_INVALID_UTF8", 5: "TOKTIER_E_CAPACITY", 6: "TOKTIER_E_HIP", 7: "TOKTIER_E_OOM"}
 

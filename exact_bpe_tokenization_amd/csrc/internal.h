@@ -35,11 +35,15 @@ constexpr int GIANT_THREADS = 1024;
 
 // ---------------------------------------------------------------------------------------------
 // per-byte character code written by the classify kernel
-//   bits 0-2 category; bit 3 CR or LF; bit 4 U+0020; bits 5-6 contraction length code at an
-//   apostrophe (0 none, 1 two chars "'x", 2 three chars "'xy"); bit 7 first char of a document
+//   bits 0-2 category; bit 3 CR or LF; bit 4 U+0020 (whitespace) or punctuation / symbol (other
+//   characters); bits 5-6 contraction length code at an apostrophe (0 none, 1 two chars "'x", 2
+//   three chars "'xy"), in the DeepSeek-style family instead bit 5 ASCII letter or ASCII
+//   punctuation / symbol and bit 6 a code point of the CJK ranges of its second splitter; bit 7
+//   first char of a document
 enum : uint8_t { CAT_LU = 0, CAT_LL = 1, CAT_LO = 2, CAT_N = 3, CAT_W = 4, CAT_M = 5, CAT_O = 6,
                  CAT_CONT = 7 };
-constexpr uint8_t CC_CRLF = 8, CC_SP = 16, CC_CONTR_SHIFT = 5, CC_DOC = 128;
+constexpr uint8_t CC_CRLF = 8, CC_SP = 16, CC_PS = 16, CC_CONTR_SHIFT = 5, CC_DOC = 128;
+constexpr uint8_t CC_DS_ASCII = 32, CC_DS_CJK = 64;
 constexpr uint8_t CC_EOF = 0xFF;   // placed past the end of the batch
 
 // ---------------------------------------------------------------------------------------------
@@ -48,8 +52,11 @@ enum : int { S_ST = 0, S_LRUN, S_NALL, S_N1, S_N2, S_ORUN, S_ORNL, S_ONL, S_WNL,
              S_C2, S_LA, S_LB, S_LEND, NSTATES };
 static_assert(NSTATES == 15, "a transition map holds one byte per state in 16 bytes, byte 15 free");
 
-// character context: self code (13) x first-of-document (2) x next-char code (6) x flag (2)
+// character context: self code (13) x first-of-document (2) x next-char code (6) x flag (2);
+// DeepSeek style: self code (16) x first-of-document (2) x next-char code (10), no flag
 constexpr int NSELF = 13, NNEXT = 6, NCTX = NSELF * 2 * NNEXT * 2;
+constexpr int DS_NSELF = 16, DS_NNEXT = 10, DS_NCTX = DS_NSELF * 2 * DS_NNEXT;
+constexpr int NCTX_MAX = NCTX > DS_NCTX ? NCTX : DS_NCTX;
 
 // ---------------------------------------------------------------------------------------------
 // merge tables.  Pair hash slot: bits 63..21 = (left << 21 | right), bits 20..0 = rank.
@@ -57,13 +64,13 @@ constexpr uint32_t NO_RANK = 0xFFFFFFFFu;
 constexpr uint64_t EMPTY_SLOT = ~0ull;
 constexpr uint32_t PAIR_BUCKET_LOG2 = 3, PAIR_BUCKET = 1u << PAIR_BUCKET_LOG2;   // 8 slots = 64 bytes
 
-constexpr int FAMILY_GPT2 = 1, FAMILY_O200K = 3;   // the family codes of the public header
+constexpr int FAMILY_GPT2 = 1, FAMILY_O200K = 3, FAMILY_DEEPSEEK = 4;   // the family codes of the public header
 
 struct DevVocab {
     const uint32_t *r2;       // 65536 byte-pair ranks
     const uint64_t *slots;    // pair hash: buckets of 8 slots, a full bucket continues in the next
     const uint32_t *merges;   // 2 * n_merges (left, right)
-    const uint4 *fmap16;      // NCTX transition maps, one byte per state s (bytes 0..14):
+    const uint4 *fmap16;      // NCTX (DeepSeek style: DS_NCTX) transition maps, one byte per state s (bytes 0..14):
                               //   bits 0-3 the next state, bit 4 set when a piece starts here in s
     // whole-piece tables: pieces whose BPE result is one token (NULL while they are being built)
     const uint4 *wa;          // 2..7 bytes: {key lo, key hi, id, 0}, key = bytes | len << 56

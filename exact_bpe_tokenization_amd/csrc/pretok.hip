@@ -46,9 +46,21 @@ __device__ __forceinline__ uint32_t ucat(uint32_t cp)
         if (lc >= 'a' && lc <= 'z') return cp >= 'a' ? CAT_LL : CAT_LU;
         if (cp >= '0' && cp <= '9') return CAT_N;
         if (cp == ' ' || (cp >= 9u && cp <= 13u)) return CAT_W;
-        return CAT_O;
+        return (cp >= 0x21u && cp <= 0x7Eu) ? (uint32_t)(CAT_O | CC_PS) : (uint32_t)CAT_O;   // punctuation, symbols
     }
     return tt_ucat_stage2[((uint32_t)tt_ucat_stage1[cp >> 8] << 8) | (cp & 255u)];
+}
+
+// DeepSeek-style bits of a character's code (code = its category bits, with CC_PS): ASCII letter or
+// ASCII punctuation / symbol (the first character of that family's punctuation-word alternative),
+// and a code point of its second splitter's CJK ranges (ideographs U+4E00..U+9FA5, hiragana and
+// katakana U+3040..U+30FF)
+__device__ __forceinline__ uint32_t ds_bits(uint32_t cp, uint32_t code)
+{
+    const uint32_t cat = code & 7u;
+    const bool ascii = cp < 0x80u && (cat <= CAT_LO || (cat == CAT_O && (code & CC_PS)));
+    const bool cjk = cp - 0x4E00u <= 0x9FA5u - 0x4E00u || cp - 0x3040u <= 0x30FFu - 0x3040u;
+    return (ascii ? CC_DS_ASCII : 0u) | (cjk ? CC_DS_CJK : 0u);
 }
 
 // backward map of one character for a boolean carried right-to-left:
@@ -219,7 +231,9 @@ __device__ __forceinline__ uint32_t byte_code(const uint8_t *sraw, DocBit docbit
     uint32_t code = ucat(cp) | (isdoc ? CC_DOC : 0u);
     if (c == '\r' || c == '\n') code |= CC_CRLF;
     if (c == ' ') code |= CC_SP;
-    if (c == '\'') {
+    if (family == FAMILY_DEEPSEEK) {
+        code |= ds_bits(cp, code);
+    } else if (c == '\'') {
         // 's 't 're 've 'm 'll 'd (ASCII; case-insensitive except for the GPT-2 family)
         auto letter = [&](uint32_t t) -> uint32_t {
             if (p + t >= n || docbit(j + (int)t)) return 0;
@@ -358,7 +372,9 @@ __device__ __forceinline__ uint32_t reg_byte_code(const uint32_t (&rw)[6], uint3
     uint32_t code = ucat(cp) | (isdoc ? CC_DOC : 0u);
     if (c == '\r' || c == '\n') code |= CC_CRLF;
     if (c == ' ') code |= CC_SP;
-    if (c == '\'') {
+    if (family == FAMILY_DEEPSEEK) {
+        code |= ds_bits(cp, code);
+    } else if (c == '\'') {
         auto letter = [&](int t) -> uint32_t {
             if (p + t >= n || ((dm >> (i + t)) & 1u)) return 0;
             uint32_t x = wbyte(rw, i + t);
@@ -414,6 +430,33 @@ __device__ __forceinline__ uint32_t next_code(uint32_t code)
     return (code & CC_DOC) ? 5u : (0x44321000u >> (4u * (code & 7u))) & 15u;   // CC_EOF has CC_DOC set
 }
 
+// DeepSeek style (16 self codes): ASCII letter 0, other letter 1, CJK-range letter 2, mark 3,
+// CJK-range mark 4, ASCII punctuation / symbol 5, other punctuation / symbol 6, CJK-range one 7,
+// other character 8, CJK-range other 9, number 10, whitespace 11 + 2 (space) + 1 (NA), CR/LF 15
+__device__ __forceinline__ uint32_t self_code_ds(uint32_t code)
+{
+    const uint32_t cat = code & 7u;
+    const bool cjk = code & CC_DS_CJK, asc = code & CC_DS_ASCII, ps = code & CC_PS;
+    if (cat <= CAT_LO) return asc ? 0u : (cjk ? 2u : 1u);
+    if (cat == CAT_M) return cjk ? 4u : 3u;
+    if (cat == CAT_O) return ps ? (asc ? 5u : (cjk ? 7u : 6u)) : (cjk ? 9u : 8u);
+    if (cat == CAT_N) return 10u;
+    return (code & CC_CRLF) ? 15u : ((code & CC_SP) ? 13u : 11u);
+}
+
+// DeepSeek style next-character code: ASCII letter 0, letter or mark 1, CJK-range letter or mark 2,
+// punctuation / symbol 3, CJK-range one 4, whitespace 5, other 6, CJK-range other 7, number 8, end
+// of document or batch 9
+__device__ __forceinline__ uint32_t next_code_ds(uint32_t code)
+{
+    const uint32_t cat = code & 7u;
+    const bool cjk = code & CC_DS_CJK;
+    if ((code & CC_DOC) || cat == CAT_CONT) return 9u;
+    if (cat <= CAT_LO || cat == CAT_M) return (code & CC_DS_ASCII) ? 0u : (cjk ? 2u : 1u);
+    if (cat == CAT_O) return (code & CC_PS) ? (cjk ? 4u : 3u) : (cjk ? 7u : 6u);
+    return cat == CAT_W ? 5u : 8u;
+}
+
 // contraction length code of an apostrophe at window index j of sraw (position p): 1 for 's 't 'm
 // 'd, 2 for 're 've 'll (ASCII; case-insensitive except for the GPT-2 family), else 0
 template <typename DocBit>
@@ -432,22 +475,29 @@ __device__ __forceinline__ uint32_t contraction_code(const uint8_t *sraw, DocBit
     return 0;
 }
 
-// CASE: the family has the case-boundary letter rule (the only one that reads the AU flag; for the
-// others the flag changes no transition between reachable states and is left at zero).
+// VAR_CASE: the family has the case-boundary letter rule (the only one that reads the AU flag; for
+// the others the flag changes no transition between reachable states and is left at zero).
+// VAR_DS: the DeepSeek-style family (its own character bits and contexts, no contractions).
 // Eight wavefronts per SIMD (at most 64 VGPRs): four tiles per CU, whose LDS (40 KB each) fits too;
 // the tiles spend much of their time waiting on look-backs, which the fourth tile helps to hide.
-template <bool CASE>
+enum : int { VAR_PLAIN = 0, VAR_CASE = 1, VAR_DS = 2 };
+
+template <int VAR>
 __global__ __launch_bounds__(PRE_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__restrict__ offsets, uint32_t n_docs,
               uint64_t n, uint8_t *ws, Layout L)
 {
+    constexpr bool CASE = VAR == VAR_CASE, DS = VAR == VAR_DS;
+    // context = ((self * 2 + doc) * NX + next) * AUM + au
+    constexpr uint32_t NX = DS ? DS_NNEXT : NNEXT, AUM = DS ? 1u : 2u, NCTXV = DS ? DS_NCTX : NCTX;
+    constexpr uint32_t NA_STEP = 2u * NX * AUM;   // NA set: the next self code (W0 -> W1, SP0 -> SP1)
     constexpr int NW = PRE_THREADS / 64;
     constexpr int SPAN = RAW_LEAD + TILE + RAW_TAIL;
     __shared__ __align__(16) uint8_t sraw[SPAN];
     __shared__ uint32_t sdoc[(SPAN + 31) / 32];
     __shared__ __align__(16) uint8_t scc[TILE + HALO];
     __shared__ uint16_t spiece[TILE];
-    __shared__ uint4 smap16[NCTX + 1];          // [NCTX]: identity (continuation bytes)
+    __shared__ uint4 smap16[NCTX_MAX + 1];      // [NCTXV]: identity (continuation bytes)
     __shared__ uint16_t sasc[128];              // ASCII character: byte code (no doc bit) | W, LU, LL bits 8-10
     __shared__ uint16_t sctxa[256];             // byte code -> its part of the context (0xFFFF: not a character)
     __shared__ uint8_t sctxb[256];              // next character's byte code -> its part of the context
@@ -464,21 +514,22 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
 
     if (tid == 0) s_tile = atomicAdd(&ctrl->tile_ctr_pre, 1u);
-    for (int i = tid; i < NCTX; i += PRE_THREADS) smap16[i] = v.fmap16[i];
-    if (tid == 0) smap16[NCTX] = make_uint4(0x03020100u, 0x07060504u, 0x0B0A0908u, 0x0F0E0D0Cu);
+    for (int i = tid; i < (int)NCTXV; i += PRE_THREADS) smap16[i] = v.fmap16[i];
+    if (tid == 0) smap16[NCTXV] = make_uint4(0x03020100u, 0x07060504u, 0x0B0A0908u, 0x0F0E0D0Cu);
     if (tid < 128) {
-        const uint32_t cat = ucat(tid);
-        sasc[tid] = (uint16_t)(cat | ((tid == '\r' || tid == '\n') ? CC_CRLF : 0u) | (tid == ' ' ? CC_SP : 0u) |
+        const uint32_t u = ucat(tid), cat = u & 7u;
+        sasc[tid] = (uint16_t)(u | ((tid == '\r' || tid == '\n') ? CC_CRLF : 0u) | (tid == ' ' ? CC_SP : 0u) |
+                               (DS ? ds_bits(tid, u) : 0u) |
                                (cat == CAT_W ? 0x100u : 0u) | (cat == CAT_LU ? 0x200u : 0u) |
                                (cat == CAT_LL ? 0x400u : 0u));
     }
     if (tid < 256) {
-        // context = ((self * 2 + doc) * NNEXT + next) * 2 + au: the self / doc part (self code with
-        // NA clear) and the next-character part (end of document or batch: 5)
+        // the self / doc part of the context (self code with NA clear) and the next-character part
+        const uint32_t selfc = DS ? self_code_ds(tid) : self_code(tid, false);
+        const uint32_t nextc = DS ? next_code_ds(tid) : ((tid & 7u) == CAT_CONT ? 5u : next_code(tid));
         sctxa[tid] = (tid & 7u) == CAT_CONT ? (uint16_t)0xFFFFu
-                                             : (uint16_t)(self_code(tid, false) * (4u * NNEXT) +
-                                                          ((tid & CC_DOC) ? 2u * NNEXT : 0u));
-        sctxb[tid] = (uint8_t)((tid & 7u) == CAT_CONT ? 2u * 5u : 2u * next_code(tid));
+                                             : (uint16_t)((selfc * 2u + ((tid & CC_DOC) ? 1u : 0u)) * NX * AUM);
+        sctxb[tid] = (uint8_t)(nextc * AUM);
     }
     for (int j = tid; j < (SPAN + 31) / 32; j += PRE_THREADS) sdoc[j] = 0;
     __syncthreads();
@@ -561,7 +612,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
                 const uint32_t f = sasc[c];
                 const uint32_t code = (f & 0xFFu) | (((dm >> (k + RAW_LEAD)) & 1u) ? CC_DOC : 0u);
                 const bool eof = (xeof >> k) & 1u;
-                apos |= (c == '\'' && !eof ? 1u : 0u) << k;
+                if (!DS) apos |= (c == '\'' && !eof ? 1u : 0u) << k;
                 w[k >> 2] |= (eof ? (uint32_t)CC_EOF : code) << (8 * (k & 3));
                 mW |= ((f >> 8) & 1u) << k;
                 mC |= ((f >> 3) & 1u) << k;
@@ -707,9 +758,9 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
 #pragma unroll
         for (int k = PRE_CHUNK - 1; k >= 0; --k) {
             const uint32_t nc = (ncw[k >> 2] >> (8 * (k & 3))) & 255u;
-            uint32_t ctx = (uint32_t)sctxa[code_at(k)] + (uint32_t)sctxb[nc] + 4u * NNEXT * ((naw >> k) & 1u);
+            uint32_t ctx = (uint32_t)sctxa[code_at(k)] + (uint32_t)sctxb[nc] + NA_STEP * ((naw >> k) & 1u);
             if (CASE) ctx += (aun >> k) & 1u;
-            ctx = min(ctx, (uint32_t)NCTX);
+            ctx = min(ctx, NCTXV);
             pk_ctx[k >> 1] |= ctx << (16 * (k & 1));
             const uint4 m = smap16[ctx];
             acc = compose16(M16{{m.x, m.y, m.z, m.w}}, acc);
@@ -824,11 +875,14 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
         LaunchScope k(ev, 1, s);
         const dim3 grid(L.n_tiles);
         if (v.family == FAMILY_O200K)
-            hipLaunchKernelGGL(k_pieces<true>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs, b.n,
-                               b.ws, L);
+            hipLaunchKernelGGL(k_pieces<VAR_CASE>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs,
+                               b.n, b.ws, L);
+        else if (v.family == FAMILY_DEEPSEEK)
+            hipLaunchKernelGGL(k_pieces<VAR_DS>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs,
+                               b.n, b.ws, L);
         else
-            hipLaunchKernelGGL(k_pieces<false>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs, b.n,
-                               b.ws, L);
+            hipLaunchKernelGGL(k_pieces<VAR_PLAIN>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs,
+                               b.n, b.ws, L);
     }
     return hipGetLastError();
 }

@@ -12,7 +12,8 @@
 #include "../../include/toktier.h"
 #include "internal.h"
 
-static_assert(tt::FAMILY_GPT2 == TOKTIER_GPT2 && tt::FAMILY_O200K == TOKTIER_O200K, "family codes");
+static_assert(tt::FAMILY_GPT2 == TOKTIER_GPT2 && tt::FAMILY_O200K == TOKTIER_O200K &&
+              tt::FAMILY_DEEPSEEK == TOKTIER_DEEPSEEK, "family codes");
 #include "unicode_table.inc"
 
 using namespace tt;
@@ -162,8 +163,112 @@ int cont(int fam, int st, const Ctx &c)
     return STOP;
 }
 
+// ---- DeepSeek style: three splitters in sequence (paper, derivation paragraph on the DeepSeek
+// family: the composition is one per-character rule when every splitter re-splits each earlier
+// piece and the unmatched stretches stay pieces).  Splitter 1 isolates digit groups of 1-3,
+// splitter 2 runs of CJK ideographs and kana, splitter 3 applies the body alternatives
+//   A  one ASCII punctuation / symbol character, then ASCII letters
+//   B  one optional character that is not CR/LF, a letter, punctuation or a symbol, then letters
+//      and marks
+//   C  an optional space, punctuation / symbols, then any CR/LF
+//   D-F  the whitespace alternatives of cl100k
+// to each piece left by the first two, whose ends are the ends of the text for it.  Between
+// characters i and i+1 the first two splitters cut where the document ends, where a digit meets a
+// non-digit, and (between non-digits) where the CJK ranges begin or end: the character before such
+// a cut sees "end of text" next, and its transition ends every match (state DS_ST).  Digit groups
+// count in states DS_N1 and DS_N2.  Characters that no body alternative can start are passed over
+// by the splitter and form a piece of their own (state DS_GAP), which ends where a match can start.
+
+enum DsState { DS_ST = 0, DS_N1, DS_N2, DS_AL, DS_LM, DS_PSR, DS_PNL, DS_WNL, DS_WNS, DS_GAP, DS_NSTATES };
+static_assert(DS_NSTATES <= NSTATES, "DeepSeek-style states fit the maps");
+
+// self codes 0..15 and next codes 0..9 as defined by the pieces kernel (self_code_ds, next_code_ds)
+struct DsCtx {
+    int self, nx;   // nx: the next character as the body splitter sees it (9 = end of text)
+    bool cut;       // the first two splitters cut after this character
+    bool N() const { return self == 10; }
+    bool LA() const { return self == 0; }
+    bool LM() const { return self <= 4; }
+    bool PSa() const { return self == 5; }
+    bool PS() const { return self >= 5 && self <= 7; }
+    bool X() const { return self == 8 || self == 9; }
+    bool W() const { return self >= 11; }
+    bool SP() const { return self == 13 || self == 14; }
+    bool CRLF() const { return self == 15; }
+    bool NA() const { return self == 12 || self == 14; }   // no CR/LF ahead in this whitespace run
+    bool nxLA() const { return nx == 0; }
+    bool nxLM() const { return nx <= 2; }
+    bool nxPS() const { return nx == 3 || nx == 4; }
+    bool nxW_or_eof() const { return nx == 5 || nx == 9; }
+};
+
+DsCtx ds_ctx(int self, int next)
+{
+    auto self_cjk = [](int x) { return x == 2 || x == 4 || x == 7 || x == 9; };
+    auto next_cjk = [](int x) { return x == 2 || x == 4 || x == 7; };
+    const bool sn = self == 10, nn = next == 8;
+    const bool cut = next == 9 || sn != nn || (!sn && !nn && self_cjk(self) != next_cjk(next));
+    return DsCtx{self, cut ? 9 : next, cut};
+}
+
+int ds_dispatch(const DsCtx &c)
+{
+    if (c.N()) return DS_N1;
+    if (c.PSa() && c.nxLA()) return DS_AL;
+    if (c.LM()) return DS_LM;
+    if (((c.W() && !c.CRLF()) || c.X()) && c.nxLM()) return DS_LM;
+    if (c.SP() && c.nxPS()) return DS_PSR;
+    if (c.PS()) return DS_PSR;
+    if (c.W()) {
+        if (!c.NA()) return DS_WNL;
+        return c.nxW_or_eof() ? DS_WNS : DS_ST;
+    }
+    return DS_GAP;
+}
+
+int ds_cont(int st, const DsCtx &c)
+{
+    switch (st) {
+    case DS_N1: return c.N() ? DS_N2 : STOP;
+    case DS_N2: return c.N() ? DS_ST : STOP;
+    case DS_AL: return c.LA() ? DS_AL : STOP;
+    case DS_LM: return c.LM() ? DS_LM : STOP;
+    case DS_PSR: return c.PS() ? DS_PSR : (c.CRLF() ? DS_PNL : STOP);
+    case DS_PNL: return c.CRLF() ? DS_PNL : STOP;
+    case DS_WNL: return (c.W() && !c.NA()) ? DS_WNL : STOP;
+    case DS_WNS: return (c.W() && c.nxW_or_eof()) ? DS_WNS : STOP;
+    case DS_GAP: return ds_dispatch(c) == DS_GAP ? DS_GAP : STOP;
+    default: return STOP;   // DS_ST and the unused states
+    }
+}
+
+void build_tables_ds(uint64_t *fmap, uint32_t *fstart)
+{
+    for (int self = 0; self < DS_NSELF; ++self)
+        for (int doc = 0; doc < 2; ++doc)
+            for (int nx = 0; nx < DS_NNEXT; ++nx) {
+                const DsCtx c = ds_ctx(self, nx);
+                const int idx = (self * 2 + doc) * DS_NNEXT + nx;
+                const int d = ds_dispatch(c);
+                uint64_t m = 0;
+                uint32_t st = 0;
+                for (int s = 0; s < NSTATES; ++s) {
+                    int r = doc ? STOP : ds_cont(s, c);
+                    if (r == STOP) { r = d; st |= 1u << s; }
+                    if (c.cut) r = DS_ST;
+                    m |= (uint64_t)r << (4 * s);
+                }
+                fmap[idx] = m;
+                fstart[idx] = st;
+            }
+}
+
 void build_tables(int fam, uint64_t *fmap, uint32_t *fstart)
 {
+    if (fam == TOKTIER_DEEPSEEK) {
+        build_tables_ds(fmap, fstart);
+        return;
+    }
     for (int self = 0; self < NSELF; ++self)
         for (int doc = 0; doc < 2; ++doc)
             for (int nx = 0; nx < NNEXT; ++nx)
@@ -522,7 +627,8 @@ extern "C" int toktier_load_vocab_ex(const uint32_t *merges, uint32_t n_merges, 
         std::sort(seen.begin(), seen.end());
         if (std::adjacent_find(seen.begin(), seen.end()) != seen.end()) return TOKTIER_E_INVALID_ARG;
     }
-    if (family != TOKTIER_GPT2 && family != TOKTIER_CL100K && family != TOKTIER_O200K) return TOKTIER_E_BAD_FAMILY;
+    if (family != TOKTIER_GPT2 && family != TOKTIER_CL100K && family != TOKTIER_O200K && family != TOKTIER_DEEPSEEK)
+        return TOKTIER_E_BAD_FAMILY;
     if (n_merges > TOKTIER_MAX_MERGES) return TOKTIER_E_BAD_MERGES;
 
     std::vector<uint32_t> r2(65536, NO_RANK);
@@ -557,11 +663,11 @@ extern "C" int toktier_load_vocab_ex(const uint32_t *merges, uint32_t n_merges, 
             }
         }
     }
-    uint64_t fmap[NCTX];
-    uint32_t fstart[NCTX];
+    uint64_t fmap[NCTX_MAX] = {};
+    uint32_t fstart[NCTX_MAX] = {};
     build_tables(family, fmap, fstart);
-    uint8_t fmap16[NCTX][16];
-    for (int c = 0; c < NCTX; ++c) {
+    uint8_t fmap16[NCTX_MAX][16];
+    for (int c = 0; c < NCTX_MAX; ++c) {
         for (int st = 0; st < 16; ++st)
             fmap16[c][st] = st < NSTATES ? (uint8_t)(((fmap[c] >> (4 * st)) & 15u) | (((fstart[c] >> st) & 1u) << 4)) : 0;
     }

@@ -33,15 +33,22 @@ extern "C" {
 
 typedef struct toktier_vocab toktier_vocab;   /* opaque; immutable after load */
 
-/* Pre-tokenizer rule families (paper: the GPT-2, cl100k and o200k pattern lineages; the exact
- * alternatives are implemented by the oracle and summarized below). */
+/* Pre-tokenizer rule families (paper: the GPT-2, cl100k and o200k pattern lineages and the DeepSeek
+ * family's three splitters in sequence; the exact alternatives are implemented by the oracle and
+ * summarized below). */
 enum {
     TOKTIER_GPT2 = 1,     /* contractions ('s 't 're 've 'm 'll 'd, lowercase), ' ?' + letters,
                              ' ?' + numbers, ' ?' + other, whitespace with lookahead */
     TOKTIER_CL100K = 2,   /* case-insensitive contractions, one non-letter prefix + letters, digits
                              grouped 1-3, other + trailing CR/LF, whitespace up to the last CR/LF */
-    TOKTIER_O200K = 3     /* cl100k plus a case-boundary letter rule (upper* lower+ | upper+ lower*),
+    TOKTIER_O200K = 3,    /* cl100k plus a case-boundary letter rule (upper* lower+ | upper+ lower*),
                              marks inside words, contractions as word suffixes */
+    TOKTIER_DEEPSEEK = 4  /* three splitters, each re-splitting every piece of the one before and
+                             keeping unmatched stretches as pieces: digit groups of 1-3; runs of CJK
+                             ideographs U+4E00-U+9FA5 and kana U+3040-U+30FF; then ASCII punctuation
+                             + ASCII letters, an optional non-letter/punctuation/symbol/CR/LF
+                             character + letters and marks, ' ?' + punctuation/symbols + trailing
+                             CR/LF, and the cl100k whitespace rules */
 };
 
 enum {
@@ -64,7 +71,7 @@ enum {
  *             joined by merge rank r, which creates token ID 256 + r (byte-level BPE: IDs 0..255
  *             are the byte values).  Ranks are the list order; lower rank merges first.
  *   n_merges  0 .. TOKTIER_MAX_MERGES.
- *   family    TOKTIER_GPT2 / TOKTIER_CL100K / TOKTIER_O200K.
+ *   family    TOKTIER_GPT2 / TOKTIER_CL100K / TOKTIER_O200K / TOKTIER_DEEPSEEK.
  *   out       receives the handle; unchanged on failure.
  * The list must be rank-consistent: left, right < 256 + r for every rank r, and no (left, right)
  * pair may appear twice.  The GPU merges every leftmost non-overlapping occurrence of the minimum

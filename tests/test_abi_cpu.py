@@ -76,6 +76,6 @@ def test_unicode_table_frozen_and_independent():
     from oracle import unicode_classes as uc
     orc = uc.class_table()
     cats = np.frombuffer(gen.categories(), dtype=np.uint8)
-    mapping = {0: uc.LU, 1: uc.LL, 2: uc.LO, 3: uc.N, 4: uc.W, 5: uc.M, 6: uc.O}
+    mapping = {0: uc.LU, 1: uc.LL, 2: uc.LO, 3: uc.N, 4: uc.W, 5: uc.M, 6: uc.O, 6 | 16: uc.PS}
     mapped = np.vectorize(mapping.get, otypes=[np.uint8])(cats)
-    assert np.array_equal(mapped, np.where(orc == uc.PS, uc.O, orc))
+    assert np.array_equal(mapped, orc)
