@@ -25,13 +25,19 @@ STATUS = {0: "TOKTIER_OK", 1: "TOKTIER_E_INVALID_ARG", 2: "TOKTIER_E_BAD_FAMILY"
 EXPORTS = ("toktier_load_vocab", "toktier_load_vocab_ex", "toktier_free_vocab", "toktier_vocab_info",
            "toktier_workspace_bytes", "toktier_workspace_bytes_ex",
            "toktier_encode_batch", "toktier_encode_batch_spans", "toktier_encode_batch_timed",
-           "toktier_pretokenize_batch",
+           "toktier_pretokenize_batch", "toktier_repair_scratch_bytes", "toktier_repair_append",
            "toktier_last_status", "toktier_status_string", "toktier_last_hip_error",
            "toktier_unicode_table_sha256")
 
 # kernel launches of one encode call, in stream order (TOKTIER_K_* in toktier.h)
 KERNELS = ("summary", "pieces", "route", "giant_seams", "bpe_small", "bpe_wave", "bpe_block", "bpe_giant", "emit",
            "gather_long")
+
+
+class RepairInfo(ctypes.Structure):
+    """toktier_repair_info"""
+    _fields_ = [("attempts", ctypes.c_uint32), ("window_chars", ctypes.c_uint32), ("spliced", ctypes.c_uint32),
+                ("pad", ctypes.c_uint32), ("splice_byte", ctypes.c_uint64), ("fresh_tokens", ctypes.c_uint64)]
 
 
 class ToktierError(RuntimeError):
@@ -70,6 +76,9 @@ def lib():
     L.toktier_encode_batch_timed.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, u64, vp, u64p, vp, vp]
     L.toktier_pretokenize_batch.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, u64, vp, u64p]
     L.toktier_last_status.argtypes = [vp, vp, u64p]
+    L.toktier_repair_scratch_bytes.argtypes = [vp, u64, u64p]
+    L.toktier_repair_append.argtypes = [vp, vp, u64, u64, vp, vp, u64, vp, vp, u64, u64p, vp, u64, vp,
+                                        ctypes.POINTER(RepairInfo)]
     for f in ("toktier_status_string",):
         getattr(L, f).argtypes = [i32]
         getattr(L, f).restype = ctypes.c_char_p
@@ -261,6 +270,36 @@ def toktier_pretokenize_batch(vocab, data, offsets, out_starts, workspace, strea
     return n.value
 
 
+def toktier_repair_scratch_bytes(vocab, total_bytes):
+    n = ctypes.c_uint64()
+    _check(lib().toktier_repair_scratch_bytes(vocab.handle, total_bytes, ctypes.byref(n)),
+           "toktier_repair_scratch_bytes")
+    return n.value
+
+
+def toktier_repair_append(vocab, text, len_a, cached_ids, cached_spans, scratch, stream=None):
+    """Incremental repair of an append: text = A || B (host bytes), len_a = bytes of A, cached records
+    of A (uint32 arrays).  Returns (ids uint32[T], spans uint32[T], info dict) for A || B."""
+    raw = bytes(text)
+    ci = np.ascontiguousarray(cached_ids, dtype=np.uint32)
+    cs = np.ascontiguousarray(cached_spans, dtype=np.uint32)
+    cap = max(len(raw), 1)
+    out_ids = np.zeros(cap, dtype=np.uint32)
+    out_spans = np.zeros(cap, dtype=np.uint32)
+    n = ctypes.c_uint64()
+    info = RepairInfo()
+    tb = (ctypes.c_uint8 * max(len(raw), 1)).from_buffer_copy(raw if raw else b"\0")
+    rc = lib().toktier_repair_append(vocab.handle, ctypes.cast(tb, ctypes.c_void_p), len_a, len(raw),
+                                     ci.ctypes.data_as(ctypes.c_void_p), cs.ctypes.data_as(ctypes.c_void_p), ci.size,
+                                     out_ids.ctypes.data_as(ctypes.c_void_p),
+                                     out_spans.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n),
+                                     _ptr(scratch), scratch.numel(), _stream(stream), ctypes.byref(info))
+    _check(rc, "toktier_repair_append")
+    k = n.value
+    return (out_ids[:k].copy(), out_spans[:k].copy(),
+            {f: getattr(info, f) for f, _ in RepairInfo._fields_ if f != "pad"})
+
+
 def toktier_last_status(workspace, stream=None):
     n = ctypes.c_uint64()
     _check(lib().toktier_last_status(_ptr(workspace), _stream(stream), ctypes.byref(n)), "toktier_last_status")
@@ -322,6 +361,14 @@ class Tokenizer:
         return (self.out_ids[:nt].cpu().numpy().view(np.uint32).copy(),
                 self.out_offsets[: d + 1].cpu().numpy().astype(np.uint64),
                 out_spans[:nt].cpu().numpy().view(np.uint32).copy())
+
+    def repair_append(self, text: bytes, len_a, cached_ids, cached_spans):
+        """Records of text = A || B from the cached records of A (toktier_repair_append)."""
+        with torch.cuda.device(self.device):
+            need = toktier_repair_scratch_bytes(self.vocab, len(text))
+            if getattr(self, "_repair_scratch", None) is None or self._repair_scratch.numel() < need:
+                self._repair_scratch = torch.empty(need, dtype=torch.uint8, device=self.device)
+            return toktier_repair_append(self.vocab, text, len_a, cached_ids, cached_spans, self._repair_scratch)
 
     def pretokenize(self, data: bytes, offsets=None):
         arr = np.frombuffer(bytes(data), dtype=np.uint8) if len(data) else np.zeros(0, np.uint8)

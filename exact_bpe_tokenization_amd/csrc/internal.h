@@ -47,6 +47,66 @@ constexpr uint8_t CC_DS_ASCII = 32, CC_DS_CJK = 64;
 constexpr uint8_t CC_EOF = 0xFF;   // placed past the end of the batch
 
 // ---------------------------------------------------------------------------------------------
+// character codes -> automaton context parts (the pieces kernel and the host-side repair check)
+
+// DeepSeek-style bits of a character's code (code = its category bits, with CC_PS): ASCII letter or
+// ASCII punctuation / symbol (the first character of that family's punctuation-word alternative),
+// and a code point of its second splitter's CJK ranges (ideographs U+4E00..U+9FA5, hiragana and
+// katakana U+3040..U+30FF)
+__host__ __device__ __forceinline__ uint32_t ds_bits(uint32_t cp, uint32_t code)
+{
+    const uint32_t cat = code & 7u;
+    const bool ascii = cp < 0x80u && (cat <= CAT_LO || (cat == CAT_O && (code & CC_PS)));
+    const bool cjk = cp - 0x4E00u <= 0x9FA5u - 0x4E00u || cp - 0x3040u <= 0x30FFu - 0x3040u;
+    return (ascii ? CC_DS_ASCII : 0u) | (cjk ? CC_DS_CJK : 0u);
+}
+
+// self code of a character (13 values) from its byte code and its NA flag, without branches:
+// LU 0, LL 1, LO 2, N 3, M 4, other 5 (6, 7 with a one- or two-letter contraction after an
+// apostrophe), whitespace 8 + 2 (space) + 1 (NA), CR/LF 12
+__host__ __device__ __forceinline__ uint32_t self_code(uint32_t code, bool na)
+{
+    const uint32_t cat = code & 7u;
+    const uint32_t base = (0x05483210u >> (4u * cat)) & 15u;
+    const uint32_t other = base + ((code >> CC_CONTR_SHIFT) & 3u);
+    const uint32_t ws = (code & CC_CRLF) ? 12u : 8u + ((code & CC_SP) ? 2u : 0u) + (na ? 1u : 0u);
+    return cat == CAT_W ? ws : (cat == CAT_O ? other : base);
+}
+
+// next-character code: letter 0, N 1, W 2, M 3, other 4, end of document or batch 5
+__host__ __device__ __forceinline__ uint32_t next_code(uint32_t code)
+{
+    return (code & CC_DOC) ? 5u : (0x44321000u >> (4u * (code & 7u))) & 15u;   // CC_EOF has CC_DOC set
+}
+
+// DeepSeek style (16 self codes): ASCII letter 0, other letter 1, CJK-range letter 2, mark 3,
+// CJK-range mark 4, ASCII punctuation / symbol 5, other punctuation / symbol 6, CJK-range one 7,
+// other character 8, CJK-range other 9, number 10, whitespace 11 + 2 (space) + 1 (NA), CR/LF 15
+__host__ __device__ __forceinline__ uint32_t self_code_ds(uint32_t code)
+{
+    const uint32_t cat = code & 7u;
+    const bool cjk = code & CC_DS_CJK, asc = code & CC_DS_ASCII, ps = code & CC_PS;
+    if (cat <= CAT_LO) return asc ? 0u : (cjk ? 2u : 1u);
+    if (cat == CAT_M) return cjk ? 4u : 3u;
+    if (cat == CAT_O) return ps ? (asc ? 5u : (cjk ? 7u : 6u)) : (cjk ? 9u : 8u);
+    if (cat == CAT_N) return 10u;
+    return (code & CC_CRLF) ? 15u : ((code & CC_SP) ? 13u : 11u);
+}
+
+// DeepSeek style next-character code: ASCII letter 0, letter or mark 1, CJK-range letter or mark 2,
+// punctuation / symbol 3, CJK-range one 4, whitespace 5, other 6, CJK-range other 7, number 8, end
+// of document or batch 9
+__host__ __device__ __forceinline__ uint32_t next_code_ds(uint32_t code)
+{
+    const uint32_t cat = code & 7u;
+    const bool cjk = code & CC_DS_CJK;
+    if ((code & CC_DOC) || cat == CAT_CONT) return 9u;
+    if (cat <= CAT_LO || cat == CAT_M) return (code & CC_DS_ASCII) ? 0u : (cjk ? 2u : 1u);
+    if (cat == CAT_O) return (code & CC_PS) ? (cjk ? 4u : 3u) : (cjk ? 7u : 6u);
+    return cat == CAT_W ? 5u : 8u;
+}
+
+// ---------------------------------------------------------------------------------------------
 // pre-tokenizer automaton: the state before a character says what the running match expects
 enum : int { S_ST = 0, S_LRUN, S_NALL, S_N1, S_N2, S_ORUN, S_ORNL, S_ONL, S_WNL, S_WNS, S_C1,
              S_C2, S_LA, S_LB, S_LEND, NSTATES };

@@ -15,21 +15,10 @@
 static_assert(tt::FAMILY_GPT2 == TOKTIER_GPT2 && tt::FAMILY_O200K == TOKTIER_O200K &&
               tt::FAMILY_DEEPSEEK == TOKTIER_DEEPSEEK, "family codes");
 #include "unicode_table.inc"
+#include "vocab.h"
 
 using namespace tt;
 
-struct toktier_vocab {
-    int device;
-    int family;
-    uint32_t n_merges;
-    void *dmem;     // pair tables, merges, automaton tables
-    void *dwords;   // whole-piece tables (may be NULL)
-    void *dstr;     // token strings and their hash (may be NULL)
-    void *dlen;     // byte length of every token
-    void *dadded;   // added-token tables (NULL without added tokens)
-    DevVocab dv;
-    DevAdded da;    // da.n == 0: no added tokens
-};
 
 static thread_local std::string g_hip_err;
 
@@ -703,6 +692,7 @@ extern "C" int toktier_load_vocab_ex(const uint32_t *merges, uint32_t n_merges, 
     }
     v->device = dev;
     v->family = family;
+    memcpy(v->hmap, fmap16, sizeof(fmap16));
     v->n_merges = n_merges;
     v->dmem = d;
     v->dv.r2 = (const uint32_t *)(base + o_r2);

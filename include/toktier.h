@@ -249,6 +249,49 @@ int toktier_encode_batch_timed(const toktier_vocab *v, const uint8_t *bytes, con
                                uint64_t workspace_bytes, void *stream, uint64_t *out_n_tokens,
                                void *const *events_before, void *const *events_after);
 
+/*
+ * Incremental repair of an append (paper, incremental repair section and Figure 5).  A session
+ * holds the records of its text A -- the token IDs of A and each token's source byte offset, as
+ * toktier_encode_batch_spans returns them for A as one document -- and the next request is A || B.
+ * The last w characters of A (w = 512, doubled at most five times) and B are encoded on the GPU as
+ * a window; in the longest run of records where the cached and the window's records agree in
+ * position and ID (at least two tokens, more bytes than the longest token) a splice point is
+ * accepted when the pre-tokenizer automaton is synchronized before it inside the window (the
+ * composition of its characters' transition maps sends every state to one state), the contexts up
+ * to it are the same for A alone and for A || B, and a piece starts there.  The output is then A's
+ * records before the splice point followed by the window's records from it; if every window
+ * misses, the whole text is encoded.  Either way the output equals the encoding of A || B as one
+ * document, records in the same form as the cached ones.
+ *   v             vocabulary handle without added tokens (E_INVALID_ARG otherwise).
+ *   text          host, uint8[len_total]: A || B, valid UTF-8; A ends on a character boundary.
+ *   len_a         bytes of A (<= len_total < 2^32 - 1).
+ *   cached_ids, cached_spans   host, uint32[n_cached]: the records of A (spans start at 0, strictly
+ *                 increasing, below len_a; n_cached = 0 only when len_a = 0).  Not checked to be
+ *                 the encoding of A: the caller keeps them from an earlier encode.
+ *   out_ids, out_spans   host, uint32[capacity]: the records of A || B; capacity >= len_total.
+ *   out_n         host: number of records written.
+ *   scratch       device, toktier_repair_scratch_bytes(v, len_total) bytes (text staging, records
+ *                 and the encoder's workspace), 256-byte aligned.
+ *   stream        hipStream_t (void*), NULL = default; the call synchronizes it.
+ *   info          host, may be NULL: windows tried, last window size, whether it spliced and where.
+ * Errors: E_INVALID_ARG, E_CAPACITY, E_INVALID_UTF8, E_HIP, and the encoder's errors.
+ */
+typedef struct {
+    uint32_t attempts;       /* windows encoded (0: A is no longer than the first window) */
+    uint32_t window_chars;   /* characters of A in the last window encoded */
+    uint32_t spliced;        /* 1: cached records up to splice_byte + window records; 0: full encode */
+    uint32_t pad;
+    uint64_t splice_byte;    /* byte offset of the splice point when spliced */
+    uint64_t fresh_tokens;   /* records taken from the GPU encode (window or full text) */
+} toktier_repair_info;
+
+int toktier_repair_scratch_bytes(const toktier_vocab *v, uint64_t total_bytes, uint64_t *out_bytes);
+
+int toktier_repair_append(const toktier_vocab *v, const uint8_t *text, uint64_t len_a, uint64_t len_total,
+                          const uint32_t *cached_ids, const uint32_t *cached_spans, uint64_t n_cached,
+                          uint32_t *out_ids, uint32_t *out_spans, uint64_t capacity, uint64_t *out_n,
+                          void *scratch, uint64_t scratch_bytes, void *stream, toktier_repair_info *info);
+
 /* Static English text for a status code. */
 const char *toktier_status_string(int status);
 
