@@ -12,7 +12,8 @@ Prints ONE JSON line:
   value        scanned GB/s of the batch = input bytes x K / wall time of K back-to-back steps
   latency_ms   p50 / p90 wall-clock latency of single requests, device-resident input, including the
                final device-to-host read of the token count (configs 1, 2, 3, 5); the 1M-character
-               multilingual request is the "p50 ms per 1M-char request"
+               multilingual request is the "p50 ms per 1M-char request"; graph_p50 / graph_p90: the
+               same request replayed through a captured HIP graph of the kernel chain (toktier_plan)
   roofline     the dominant kernel: algorithmic bytes per launch / its average duration measured with
                HIP events recorded around that launch inside the timed steps, against 8 TB/s
   cpu_baseline the CPU oracle (serial pre-tokenizer + priority-queue BPE, one document per worker
@@ -263,6 +264,27 @@ def main():
         latency[name] = {"p50": round(statistics.median(ts), 4), "p90": round(ts[int(0.9 * (len(ts) - 1))], 4),
                          "bytes": int(d2.size), "chars": chars, "reps": reps,
                          "scanned_gbs_p50": round(d2.size / (statistics.median(ts) * 1e-3) / 1e9, 3)}
+        # the same request replayed through a captured HIP graph of the kernel chain (a plan bound to
+        # these buffers; every replay recomputes everything from the input buffer)
+        nd2 = o2.size - 1
+        plan = tt.Plan(t2.vocab, dd, do, t2.out_ids[:max(d2.size, 1)], t2.out_offsets[:nd2 + 1],
+                       t2.workspace[: tt.toktier_workspace_bytes(d2.size, nd2)])
+        for _ in range(3):
+            nt = plan.launch()
+        if name in oracle_ref:
+            exact[name + "_graph"] = bool(
+                np.array_equal(t2.out_ids[:nt].cpu().numpy().view(np.uint32), oracle_ref[name][0]) and
+                np.array_equal(t2.out_offsets[:nd2 + 1].cpu().numpy().astype(np.uint64), oracle_ref[name][1]))
+        gs = []
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            plan.launch()
+            gs.append((time.perf_counter() - t0) * 1e3)
+        del plan
+        gs.sort()
+        latency[name]["graph_p50"] = round(statistics.median(gs), 4)
+        latency[name]["graph_p90"] = round(gs[int(0.9 * (len(gs) - 1))], 4)
 
     if args.calibrate_copy_mib:
         src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -280,6 +302,7 @@ def main():
                    "bytes": int(n), "docs": int(D), "tokens": int(n_tokens), "family": fam,
                    "input_sha256": textgen.sha256(data.tobytes())},
         "p50_ms_per_1m_char_request": latency["c3_mix1m"]["p50"] if latency else None,
+        "p50_ms_per_1m_char_request_graph": latency["c3_mix1m"]["graph_p50"] if latency else None,
         "latency_ms": latency,
         "path_alg_gbs": round(path_alg, 3),
         "path_alg_frac_of_hbm": round(path_alg / HBM_PEAK_GBS, 6),

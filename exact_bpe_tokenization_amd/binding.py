@@ -26,6 +26,7 @@ EXPORTS = ("toktier_load_vocab", "toktier_load_vocab_ex", "toktier_free_vocab", 
            "toktier_workspace_bytes", "toktier_workspace_bytes_ex",
            "toktier_encode_batch", "toktier_encode_batch_spans", "toktier_encode_batch_timed",
            "toktier_pretokenize_batch", "toktier_repair_scratch_bytes", "toktier_repair_append",
+           "toktier_plan_create", "toktier_plan_launch", "toktier_plan_free",
            "toktier_last_status", "toktier_status_string", "toktier_last_hip_error",
            "toktier_unicode_table_sha256")
 
@@ -76,6 +77,9 @@ def lib():
     L.toktier_encode_batch_timed.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, u64, vp, u64p, vp, vp]
     L.toktier_pretokenize_batch.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, u64, vp, u64p]
     L.toktier_last_status.argtypes = [vp, vp, u64p]
+    L.toktier_plan_create.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, vp, u64, vp, ctypes.POINTER(vp)]
+    L.toktier_plan_launch.argtypes = [vp, vp, u64p]
+    L.toktier_plan_free.argtypes = [vp]
     L.toktier_repair_scratch_bytes.argtypes = [vp, u64, u64p]
     L.toktier_repair_append.argtypes = [vp, vp, u64, u64, vp, vp, u64, vp, vp, u64, u64p, vp, u64, vp,
                                         ctypes.POINTER(RepairInfo)]
@@ -268,6 +272,32 @@ def toktier_pretokenize_batch(vocab, data, offsets, out_starts, workspace, strea
                                          workspace.numel(), _stream(stream), ctypes.byref(n))
     _check(rc, "toktier_pretokenize_batch")
     return n.value
+
+
+class Plan:
+    """A captured encode (toktier_plan_create) bound to fixed device buffers; launch() replays it."""
+
+    def __init__(self, vocab, data, offsets, out_ids, out_offsets, workspace, out_spans=None, stream=None):
+        self.vocab = vocab
+        self._keep = (data, offsets, out_ids, out_offsets, workspace, out_spans)
+        h = ctypes.c_void_p()
+        rc = lib().toktier_plan_create(vocab.handle, _ptr(data), _ptr(offsets), offsets.numel() - 1, data.numel(),
+                                       _ptr(out_ids), out_ids.numel(), _ptr(out_offsets), _ptr(out_spans),
+                                       _ptr(workspace), workspace.numel(), _stream(stream), ctypes.byref(h))
+        _check(rc, "toktier_plan_create")
+        self.handle = h
+
+    def launch(self, stream=None, sync=True):
+        """Replay; returns the token count when sync is True (else None)."""
+        n = ctypes.c_uint64()
+        _check(lib().toktier_plan_launch(self.handle, _stream(stream), ctypes.byref(n) if sync else None),
+               "toktier_plan_launch")
+        return n.value if sync else None
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.toktier_plan_free(self.handle)
+            self.handle = None
 
 
 def toktier_repair_scratch_bytes(vocab, total_bytes):

@@ -877,6 +877,91 @@ int encode_impl(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *of
 
 }  // namespace
 
+// ---------------------------------------------------------------------------------------------
+// plans: the kernel chain of one encode captured once as a HIP graph for fixed buffers and sizes
+// (paper, latency paragraph: device-resident counts and a CUDA graph take the host out of the
+// chain).  The chain holds kernels only -- every counter and flag is cleared by its first kernel --
+// so a replay recomputes everything from the input buffer's current contents.
+
+struct toktier_plan {
+    const toktier_vocab *v;
+    void *workspace;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+extern "C" int toktier_plan_create(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                                   uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids, uint64_t ids_capacity,
+                                   uint64_t *out_offsets, uint32_t *out_spans, void *workspace,
+                                   uint64_t workspace_bytes, void *stream, toktier_plan **out)
+{
+    if (!out) return TOKTIER_E_INVALID_ARG;
+    *out = nullptr;
+    Batch b;
+    int rc = check_batch(v, bytes, offsets, n_docs, total_bytes, workspace, workspace_bytes, &b);
+    if (rc) return rc;
+    if (v->da.n) return TOKTIER_E_INVALID_ARG;   // the literal pass reads a count on the host
+    if (!out_offsets || (total_bytes && !out_ids)) return TOKTIER_E_INVALID_ARG;
+    if (ids_capacity < total_bytes) return TOKTIER_E_CAPACITY;
+    hipStream_t s = (hipStream_t)stream;
+    hipStream_t cap = nullptr;
+    HIP_TRY(hipStreamCreateWithFlags(&cap, hipStreamNonBlocking));
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
+    if (e == hipSuccess) {
+        hipError_t e1 = launch_pretokenize(v->dv, b, cap, nullptr);
+        if (e1 == hipSuccess) e1 = launch_route(v->dv, b, cap, nullptr);
+        if (e1 == hipSuccess) e1 = launch_bpe(v->dv, b, cap, nullptr);
+        if (e1 == hipSuccess) e1 = launch_compact(v->dv, b, out_ids, out_offsets, out_spans, cap, nullptr);
+        e = hipStreamEndCapture(cap, &g);
+        if (e == hipSuccess) e = e1;
+    }
+    hipGraphExec_t x = nullptr;
+    if (e == hipSuccess) e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+    if (e == hipSuccess) e = hipGraphUpload(x, s);
+    (void)hipStreamDestroy(cap);
+    if (e != hipSuccess) {
+        if (x) (void)hipGraphExecDestroy(x);
+        if (g) (void)hipGraphDestroy(g);
+        return hip_fail(e);
+    }
+    toktier_plan *p = (toktier_plan *)calloc(1, sizeof(toktier_plan));
+    if (!p) {
+        (void)hipGraphExecDestroy(x);
+        (void)hipGraphDestroy(g);
+        return TOKTIER_E_OOM;
+    }
+    p->v = v;
+    p->workspace = workspace;
+    p->graph = g;
+    p->exec = x;
+    *out = p;
+    return TOKTIER_OK;
+}
+
+extern "C" int toktier_plan_launch(toktier_plan *p, void *stream, uint64_t *out_n_tokens)
+{
+    if (!p) return TOKTIER_E_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    HIP_TRY(hipGraphLaunch(p->exec, s));
+    if (!out_n_tokens) return TOKTIER_OK;
+    Ctrl c;
+    int rc = read_ctrl(p->workspace, s, &c);
+    if (rc) return rc;
+    *out_n_tokens = c.n_tokens;
+    return TOKTIER_OK;
+}
+
+extern "C" int toktier_plan_free(toktier_plan *p)
+{
+    if (!p) return TOKTIER_OK;
+    hipError_t e1 = hipGraphExecDestroy(p->exec), e2 = hipGraphDestroy(p->graph);
+    free(p);
+    if (e1 != hipSuccess) return hip_fail(e1);
+    if (e2 != hipSuccess) return hip_fail(e2);
+    return TOKTIER_OK;
+}
+
 extern "C" int toktier_encode_batch(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
                                     uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
                                     uint64_t ids_capacity, uint64_t *out_offsets, void *workspace,

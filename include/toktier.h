@@ -292,6 +292,29 @@ int toktier_repair_append(const toktier_vocab *v, const uint8_t *text, uint64_t 
                           uint32_t *out_ids, uint32_t *out_spans, uint64_t capacity, uint64_t *out_n,
                           void *scratch, uint64_t scratch_bytes, void *stream, toktier_repair_info *info);
 
+/*
+ * Plans: the kernel chain of toktier_encode_batch (or of the span form when out_spans is non-NULL)
+ * captured once as a HIP graph for fixed device buffers and sizes, then replayed (paper, latency
+ * paragraph: counts stay on the device and a CUDA graph removes the host from the chain).  A replay
+ * encodes whatever the bytes and offsets buffers hold at that time (same total_bytes and n_docs);
+ * nothing is cached between replays.  Arguments as in toktier_encode_batch(_spans); the buffers must
+ * outlive the plan.  Vocabularies with added tokens are rejected (E_INVALID_ARG): their literal pass
+ * reads a count on the host.  Plans sharing a workspace must not run at the same time.
+ *   toktier_plan_create  captures and uploads the graph (on `stream`; no kernel runs).
+ *   toktier_plan_launch  replays it on `stream`; out_n_tokens as in toktier_encode_batch (NULL: no
+ *                        wait; the count and device-detected errors then come from
+ *                        toktier_last_status on the workspace).
+ *   toktier_plan_free    releases the graph (NULL is a no-op).
+ * Errors: those of toktier_encode_batch, E_HIP for graph failures, E_OOM.
+ */
+typedef struct toktier_plan toktier_plan;
+int toktier_plan_create(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets, uint32_t n_docs,
+                        uint64_t total_bytes, uint32_t *out_ids, uint64_t ids_capacity, uint64_t *out_offsets,
+                        uint32_t *out_spans, void *workspace, uint64_t workspace_bytes, void *stream,
+                        toktier_plan **out);
+int toktier_plan_launch(toktier_plan *p, void *stream, uint64_t *out_n_tokens);
+int toktier_plan_free(toktier_plan *p);
+
 /* Static English text for a status code. */
 const char *toktier_status_string(int status);
 
