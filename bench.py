@@ -14,6 +14,8 @@ Prints ONE JSON line:
                final device-to-host read of the token count (configs 1, 2, 3, 5); the 1M-character
                multilingual request is the "p50 ms per 1M-char request"; graph_p50 / graph_p90: the
                same request replayed through a captured HIP graph of the kernel chain (toktier_plan)
+  value_two_in_flight  the same steps alternating between two streams (two batches in flight, each
+               with its own workspace and outputs)
   roofline     the dominant kernel: algorithmic bytes per launch / its average duration measured with
                HIP events recorded around that launch inside the timed steps, against 8 TB/s
   cpu_baseline the CPU oracle (serial pre-tokenizer + priority-queue BPE, one document per worker
@@ -194,6 +196,25 @@ def main():
     gbs = n / (wall / args.steps) / 1e9
     n_tokens = tt.toktier_last_status(ws)
 
+    # ---- the same steps with two batches in flight: alternate steps on two streams, each with its
+    # own workspace and outputs (every step still encodes the whole batch) ----
+    s2 = [torch.cuda.Stream(device=dev) for _ in range(2)]
+    bufs2 = [(ws, out_ids, out_offs), (torch.empty_like(ws), torch.empty_like(out_ids), torch.empty_like(out_offs))]
+    for _ in range(max(1, args.warmup)):   # warm the second set of buffers too
+        for k in range(2):
+            tt.toktier_encode_batch(tok.vocab, d_data, d_offs, bufs2[k][1], bufs2[k][2], bufs2[k][0], stream=s2[k],
+                                    sync=False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        w2, i2, o2 = bufs2[i % 2]
+        tt.toktier_encode_batch(tok.vocab, d_data, d_offs, i2, o2, w2, stream=s2[i % 2], sync=False)
+    torch.cuda.synchronize()
+    wall2 = time.perf_counter() - t0
+    gbs_two = n / (wall2 / args.steps) / 1e9
+    two_exact = all(np.array_equal(b[1][:n_tok].cpu().numpy().view(np.uint32), gpu_ids) for b in bufs2)
+    del bufs2
+
     # ---- per-kernel durations from HIP events around each launch, same steps ----
     _log("timed steps with per-kernel events")
     nk = len(tt.KERNELS)
@@ -239,6 +260,7 @@ def main():
     # ---- single-request latency ----
     latency = {}
     exact = {}
+    exact[MAIN + "_two_in_flight_same_ids"] = bool(two_exact)
     if oracle_ref:
         exact[MAIN] = bool(np.array_equal(gpu_ids, oracle_ref[MAIN][0]) and np.array_equal(gpu_oo, oracle_ref[MAIN][1]))
     for name in (() if args.no_latency else LATENCY):
@@ -301,6 +323,7 @@ def main():
                                f"{n} bytes, cl100k-style rules, 131,072-merge vocabulary",
                    "bytes": int(n), "docs": int(D), "tokens": int(n_tokens), "family": fam,
                    "input_sha256": textgen.sha256(data.tobytes())},
+        "value_two_in_flight": round(gbs_two, 4),
         "p50_ms_per_1m_char_request": latency["c3_mix1m"]["p50"] if latency else None,
         "p50_ms_per_1m_char_request_graph": latency["c3_mix1m"]["graph_p50"] if latency else None,
         "latency_ms": latency,
