@@ -122,13 +122,12 @@ constexpr int NCTX_MAX = NCTX > DS_NCTX ? NCTX : DS_NCTX;
 // merge tables.  Pair hash slot: bits 63..21 = (left << 21 | right), bits 20..0 = rank.
 constexpr uint32_t NO_RANK = 0xFFFFFFFFu;
 constexpr uint64_t EMPTY_SLOT = ~0ull;
-constexpr uint32_t PAIR_BUCKET_LOG2 = 3, PAIR_BUCKET = 1u << PAIR_BUCKET_LOG2;   // 8 slots = 64 bytes
 
 constexpr int FAMILY_GPT2 = 1, FAMILY_O200K = 3, FAMILY_DEEPSEEK = 4;   // the family codes of the public header
 
 struct DevVocab {
     const uint32_t *r2;       // 65536 byte-pair ranks
-    const uint64_t *slots;    // pair hash: buckets of 8 slots, a full bucket continues in the next
+    const uint64_t *slots;    // pair hash: 8-byte slots, linear probing, at most one in 32 used
     const uint32_t *merges;   // 2 * n_merges (left, right)
     const uint4 *fmap16;      // NCTX (DeepSeek style: DS_NCTX) transition maps, one byte per state s (bytes 0..14):
                               //   bits 0-3 the next state, bit 4 set when a piece starts here in s
@@ -315,28 +314,18 @@ __device__ __forceinline__ uint32_t wave_upper_bound(const T *a, uint32_t n, T x
 // Rank of the pair (a, b), NO_RANK if it is not a merge.  Byte pairs come from the dense table;
 // other pairs from the bucketed hash: one 64-byte bucket per probe (four independent 16-byte
 // loads), usually a single round trip whether the pair is present or not.
+// Rank of the pair (a, b), NO_RANK if no merge joins them: byte pairs from the dense table, the others
+// by linear probing of single slots (a sparse table keeps a wavefront's longest probe chain short)
 __device__ __forceinline__ uint32_t pair_rank(const DevVocab &v, uint32_t a, uint32_t b)
 {
     if ((a | b) < 256u) return __ldg(v.r2 + ((a << 8) | b));
     const uint64_t key = ((uint64_t)a << 21) | b;
-    uint32_t bk = (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> v.shift);
+    uint32_t h = (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> v.shift);
     for (;;) {
-        const uint4 *q = (const uint4 *)(v.slots + (uint64_t)bk * PAIR_BUCKET);
-        const uint4 w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
-        const uint64_t sl[PAIR_BUCKET] = {
-            (uint64_t)w0.x | ((uint64_t)w0.y << 32), (uint64_t)w0.z | ((uint64_t)w0.w << 32),
-            (uint64_t)w1.x | ((uint64_t)w1.y << 32), (uint64_t)w1.z | ((uint64_t)w1.w << 32),
-            (uint64_t)w2.x | ((uint64_t)w2.y << 32), (uint64_t)w2.z | ((uint64_t)w2.w << 32),
-            (uint64_t)w3.x | ((uint64_t)w3.y << 32), (uint64_t)w3.z | ((uint64_t)w3.w << 32)};
-        uint32_t r = NO_RANK;
-        bool open = false;
-#pragma unroll
-        for (int j = 0; j < PAIR_BUCKET; ++j) {
-            if ((sl[j] >> 21) == key) r = (uint32_t)(sl[j] & 0x1FFFFFu);
-            open |= sl[j] == EMPTY_SLOT;
-        }
-        if (r != NO_RANK || open) return r;
-        bk = (bk + 1) & v.mask;
+        const uint64_t sl = v.slots[h];
+        if ((sl >> 21) == key) return (uint32_t)(sl & 0x1FFFFFu);
+        if (sl == EMPTY_SLOT) return NO_RANK;
+        h = (h + 1) & v.mask;
     }
 }
 
