@@ -439,10 +439,12 @@ __device__ __forceinline__ WPQ wp_make(const DevVocab &v, const uint8_t *__restr
 {
     WPQ q{0, 0, 0, 0, len, 0, 0};
     if (len == 0 || len > (uint32_t)TABLE_MAX) return q;
+    // one round of loads for every length (the words past the piece are not read), so that a
+    // wavefront holding short and long pieces waits once
+    uint64_t k4[4];
+    load_words<4>(src, len, k4);
+    q.k0 = k4[0]; q.k1 = k4[1]; q.k2 = k4[2]; q.k3 = k4[3];
     if (len <= WA_MAX) {
-        uint64_t k[1];
-        load_words<1>(src, len, k);
-        q.k0 = k[0];
         if (len == 1 || !v.wa) return q;
         q.k0 |= (uint64_t)len << 56;
         q.h = (uint32_t)wa_hash(q.k0, v.wa_shift);
@@ -450,9 +452,6 @@ __device__ __forceinline__ WPQ wp_make(const DevVocab &v, const uint8_t *__restr
         return q;
     }
     if (!v.wb) return q;
-    uint64_t k4[4];
-    load_words<4>(src, len, k4);
-    q.k0 = k4[0]; q.k1 = k4[1]; q.k2 = k4[2]; q.k3 = k4[3];
     q.h = (uint32_t)wb_hash(k4[0], k4[1], k4[2], k4[3], len, v.wb_shift);
     q.kind = 2;
     return q;
@@ -460,16 +459,24 @@ __device__ __forceinline__ WPQ wp_make(const DevVocab &v, const uint8_t *__restr
 
 __device__ __forceinline__ uint32_t wp_step(const DevVocab &v, WPQ &q, uint32_t *id)
 {
+    if (q.kind == 0) return WP_MISS;
+    // the slot reads of both tables issued together (a wavefront holding pieces of both kinds waits
+    // for one round trip, not two)
+    const uint4 *e = q.kind == 1 ? v.wa + q.h : v.wb + 3ull * q.h;
+    const uint4 a = e[0];
+    uint4 b = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
+    if (q.kind == 2) {
+        b = e[1];
+        c = e[2];
+    }
     if (q.kind == 1) {
-        const uint4 sl = v.wa[q.h];
-        const uint64_t sk = (uint64_t)sl.x | ((uint64_t)sl.y << 32);
-        if (sk == q.k0) { *id = sl.z; return WP_HIT; }
+        const uint64_t sk = (uint64_t)a.x | ((uint64_t)a.y << 32);
+        if (sk == q.k0) { *id = a.z; return WP_HIT; }
         if (sk == 0) return WP_MISS;
         q.h = (q.h + 1) & v.wa_mask;
         return WP_MORE;
     }
-    if (q.kind == 2) {
-        const uint4 a = v.wb[3 * q.h], b = v.wb[3 * q.h + 1], c = v.wb[3 * q.h + 2];
+    {
         if (c.x == 0) return WP_MISS;
         if (c.x == q.len && ((uint64_t)a.x | ((uint64_t)a.y << 32)) == q.k0 &&
             ((uint64_t)a.z | ((uint64_t)a.w << 32)) == q.k1 && ((uint64_t)b.x | ((uint64_t)b.y << 32)) == q.k2 &&
