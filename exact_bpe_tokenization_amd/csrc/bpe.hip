@@ -193,8 +193,10 @@ __device__ __forceinline__ void lane_bpe(const DevVocab &v, const uint8_t *__res
             if ((uint32_t)j + 1 == pos) left = id[j];
             if ((uint32_t)j == pos + 1) right = id[j];
         }
-        const uint32_t rl = pos > 0 ? pair_rank(v, left, nid) : NO_RANK;
-        const uint32_t rr = pos + 1 < n ? pair_rank(v, nid, right) : NO_RANK;
+        uint32_t rl, rr;   // both neighbours' probes in one round trip (nid >= 256: no byte pair)
+        pair_rank2_general(v, left, nid, nid, right, rl, rr);
+        if (pos == 0) rl = NO_RANK;
+        if (pos + 1 >= n) rr = NO_RANK;
 #pragma unroll
         for (int j = 0; j < MAXL; ++j) {
             if ((uint32_t)j + 1 == pos) rk[j] = rl;
@@ -552,10 +554,16 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
             nx0 = wave_next(id0);
             nx1 = wave_next(id1);
             if (lane == 63) nx0 = (uint32_t)__builtin_amdgcn_readlane((int)id1, 0);
-            if (lane >= n) rk0 = NO_RANK;
-            else if (rk0 == PENDING) rk0 = lane + 1 < n ? pair_rank(v, id0, nx0) : NO_RANK;
-            if (64 + lane >= n) rk1 = NO_RANK;
-            else if (rk1 == PENDING) rk1 = 65 + lane < n ? pair_rank(v, id1, nx1) : NO_RANK;
+            if (rk0 == PENDING || rk1 == PENDING) {
+                // both rows' probes in one round trip; a pending pair holds a merged token (>= 256),
+                // the other row's result is dropped when it is not pending
+                uint32_t q0, q1;
+                pair_rank2_general(v, id0, nx0, id1, nx1, q0, q1);
+                if (rk0 == PENDING) rk0 = q0;
+                if (rk1 == PENDING) rk1 = q1;
+            }
+            if (lane + 1 >= n) rk0 = NO_RANK;
+            if (65 + lane >= n) rk1 = NO_RANK;
         }
         if (n > 1 || chunk) {
             if (lane < n) scratch[b0 + lane] = id0;

@@ -314,6 +314,27 @@ __device__ __forceinline__ uint32_t wave_upper_bound(const T *a, uint32_t n, T x
 // Rank of the pair (a, b), NO_RANK if it is not a merge.  Byte pairs come from the dense table;
 // other pairs from the bucketed hash: one 64-byte bucket per probe (four independent 16-byte
 // loads), usually a single round trip whether the pair is present or not.
+// Ranks of two pairs, each with an operand >= 256 (not byte pairs), with both first slot reads in
+// flight at once: a merge step that needs both waits for one round trip, not two
+__device__ __forceinline__ void pair_rank2_general(const DevVocab &v, uint32_t a0, uint32_t b0, uint32_t a1,
+                                                   uint32_t b1, uint32_t &r0, uint32_t &r1)
+{
+    const uint64_t k0 = ((uint64_t)a0 << 21) | b0, k1 = ((uint64_t)a1 << 21) | b1;
+    uint32_t h0 = (uint32_t)((k0 * 0x9E3779B97F4A7C15ull) >> v.shift);
+    uint32_t h1 = (uint32_t)((k1 * 0x9E3779B97F4A7C15ull) >> v.shift);
+    uint64_t s0 = v.slots[h0], s1 = v.slots[h1];
+    while ((s0 >> 21) != k0 && s0 != EMPTY_SLOT) {
+        h0 = (h0 + 1) & v.mask;
+        s0 = v.slots[h0];
+    }
+    while ((s1 >> 21) != k1 && s1 != EMPTY_SLOT) {
+        h1 = (h1 + 1) & v.mask;
+        s1 = v.slots[h1];
+    }
+    r0 = s0 == EMPTY_SLOT ? NO_RANK : (uint32_t)(s0 & 0x1FFFFFu);
+    r1 = s1 == EMPTY_SLOT ? NO_RANK : (uint32_t)(s1 & 0x1FFFFFu);
+}
+
 // Rank of the pair (a, b), NO_RANK if no merge joins them: byte pairs from the dense table, the others
 // by linear probing of single slots (a sparse table keeps a wavefront's longest probe chain short)
 __device__ __forceinline__ uint32_t pair_rank(const DevVocab &v, uint32_t a, uint32_t b)
