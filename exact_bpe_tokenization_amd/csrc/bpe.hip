@@ -579,10 +579,11 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
 
 // The lists of short unresolved pieces are independent and each kernel above is bound by its
 // dependent table probes, so they run as one launch: the workgroups are split into four ranges, one
-// per list, and all four progress at the same time.  Register use is capped at six wavefronts per
-// SIMD (no spills): more resident workgroups hide more probe latency than the lane role's longer
-// register lifetimes cost.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6, 8))) void k_bpe_small(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
+// per list, and all four progress at the same time.  Register use is capped for seven wavefronts per
+// SIMD (72 VGPRs; the lane role spills a little): more resident workgroups hide more probe latency
+// than the spills cost (measured on the 18.4 MB batch: six wavefronts 61 us, seven 57 us, eight
+// with 64 VGPRs 143 us).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 8))) void k_bpe_small(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
                                                    Layout L, uint32_t g16, uint32_t g32, uint32_t g64, uint32_t g128)
 {
     // workgroup ranges in order of the units' round counts (longest first): workgroups are dispatched
