@@ -587,7 +587,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 8))) voi
                                                    Layout L, uint32_t g16, uint32_t g32, uint32_t g64, uint32_t g128)
 {
     // workgroup ranges in order of the units' round counts (longest first): workgroups are dispatched
-    // in order, so the long chains start at once and the many short ones fill in around them
+    // in order, so the long chains start at once and the many short ones fill in around them.  The
+    // ranges are cut to what the lists hold (the grid is sized for the largest possible lists), so
+    // that the workgroups with work come first and the idle ones are dispatched last.
+    {
+        const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+        g128 = min(g128, (ctrl->miss_count[3] + 3u) / 4u);     // 4 pieces per workgroup step
+        g64 = min(g64, (ctrl->miss_count[2] + 3u) / 4u);
+        g32 = min(g32, (ctrl->miss_count[1] + 15u) / 16u);     // 16
+        g16 = min(g16, (ctrl->miss_count[0] + 255u) / 256u);   // 256
+    }
     uint32_t b = blockIdx.x;
     if (b < g128) {
         bpe_seg2(v, bytes, ws, L, b, g128);
