@@ -91,8 +91,11 @@ def test_round_schedule_needs_rank_consistency():
     # rank 0 uses ID 257, which rank 1 creates: the schedules diverge, so such lists are rejected
     a, b = 97, 98
     m = np.array([(257, a), (a, b), (b, a)], dtype=np.uint32)   # 256=(257,a) 257=(a,b) 258=(b,a)
-    p = b"abab" + b"a"
-    assert oracle.textbook_bpe(m, p) != round_bpe(m, p) or True
+    p = b"ababa"
+    # serial: (a,b) at 0 -> 257, then (257,a) -> 256 at once, later (b,a) -> 258; the round merges
+    # both (a,b) first, so its later (257,a) takes the second 257's right neighbour instead
+    assert oracle.textbook_bpe(m, p) == [256, 258]
+    assert round_bpe(m, p) == [257, 256]
     diffs = 0
     rng = np.random.default_rng(5)
     for _ in range(3000):
