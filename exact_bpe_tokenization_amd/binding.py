@@ -25,6 +25,7 @@ STATUS = {0: "TOKTIER_OK", 1: "TOKTIER_E_INVALID_ARG", 2: "TOKTIER_E_BAD_FAMILY"
 EXPORTS = ("toktier_load_vocab", "toktier_load_vocab_ex", "toktier_free_vocab", "toktier_vocab_info",
            "toktier_workspace_bytes", "toktier_workspace_bytes_ex",
            "toktier_encode_batch", "toktier_encode_batch_spans", "toktier_encode_batch_timed",
+           "toktier_encode_batch_static",
            "toktier_pretokenize_batch", "toktier_repair_scratch_bytes", "toktier_repair_append",
            "toktier_plan_create", "toktier_plan_launch", "toktier_plan_free",
            "toktier_last_status", "toktier_status_string", "toktier_last_hip_error",
@@ -75,6 +76,7 @@ def lib():
     L.toktier_encode_batch.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, u64, vp, u64p]
     L.toktier_encode_batch_spans.argtypes = [vp, vp, vp, u32, u64, vp, vp, u64, vp, vp, u64, vp, u64p]
     L.toktier_encode_batch_timed.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, u64, vp, u64p, vp, vp]
+    L.toktier_encode_batch_static.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, u64p]
     L.toktier_pretokenize_batch.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, u64, vp, u64p]
     L.toktier_last_status.argtypes = [vp, vp, u64p]
     L.toktier_plan_create.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, vp, u64, vp, ctypes.POINTER(vp)]
@@ -201,6 +203,17 @@ def toktier_encode_batch(vocab, data, offsets, out_ids, out_offsets, workspace, 
                                     _ptr(out_ids), out_ids.numel(), _ptr(out_offsets), _ptr(workspace),
                                     workspace.numel(), _stream(stream), ctypes.byref(n_tok) if sync else None)
     _check(rc, "toktier_encode_batch")
+    return n_tok.value if sync else None
+
+
+def toktier_encode_batch_static(vocab, data, offsets, out_ids, out_offsets, stream=None, sync=True):
+    """toktier_encode_batch on the library-owned scratch of the device (no workspace argument, no
+    allocation in the call).  Returns the token count when sync is True, else None."""
+    n_tok = ctypes.c_uint64()
+    rc = lib().toktier_encode_batch_static(vocab.handle, _ptr(data), _ptr(offsets), offsets.numel() - 1,
+                                           data.numel(), _ptr(out_ids), out_ids.numel(), _ptr(out_offsets),
+                                           _stream(stream), ctypes.byref(n_tok) if sync else None)
+    _check(rc, "toktier_encode_batch_static")
     return n_tok.value if sync else None
 
 

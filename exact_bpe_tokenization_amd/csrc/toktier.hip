@@ -8,6 +8,7 @@
 #include <string>
 #include <vector>
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/toktier.h"
 #include "internal.h"
@@ -34,6 +35,41 @@ static int hip_fail(hipError_t e)
         hipError_t e_ = (x);                       \
         if (e_ != hipSuccess) return hip_fail(e_); \
     } while (0)
+
+// ---------------------------------------------------------------------------------------------
+// Library-owned scratch of toktier_encode_batch_static: one fixed array per device, used in place of
+// a caller workspace by callers that cannot allocate.  In host code `scratch` is only a handle for
+// the runtime; its device address on each device comes from hipGetSymbolAddress (taken once per
+// device, with that device current, when the first vocabulary is loaded there) and only that
+// address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[TOKTIER_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];   // device address of `scratch` per device; NULL until set up
+
+// Called with device `dev` current.  Idempotent.
+int setup_static_scratch(int dev)
+{
+    if (dev < 0 || dev >= MAX_DEVICES) return TOKTIER_E_INVALID_ARG;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (g_scratch_ptr[dev]) return TOKTIER_OK;
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!ptr || ((uintptr_t)ptr & 255u)) return TOKTIER_E_HIP;
+    g_scratch_ptr[dev] = ptr;
+    return TOKTIER_OK;
+}
+
+void *static_scratch(int dev)
+{
+    if (dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    return g_scratch_ptr[dev];
+}
+}  // namespace
 
 // ---------------------------------------------------------------------------------------------
 // pre-tokenizer automaton tables.
@@ -671,6 +707,10 @@ extern "C" int toktier_load_vocab_ex(const uint32_t *merges, uint32_t n_merges, 
 
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
+    {
+        const int rs = setup_static_scratch(dev);
+        if (rs != TOKTIER_OK) return rs;
+    }
     void *d = nullptr;
     hipError_t e = hipMalloc(&d, total);
     if (e != hipSuccess) {
@@ -972,6 +1012,40 @@ extern "C" int toktier_encode_batch(const toktier_vocab *v, const uint8_t *bytes
 {
     return encode_impl(v, bytes, offsets, n_docs, total_bytes, out_ids, ids_capacity, out_offsets, nullptr,
                        workspace, workspace_bytes, stream, out_n_tokens, nullptr);
+}
+
+// The encode chain on the library-owned scratch of the current device (for callers that cannot
+// allocate): no allocation of any kind, the same kernels as toktier_encode_batch.
+extern "C" int toktier_encode_batch_static(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                                           uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids,
+                                           uint64_t ids_capacity, uint64_t *out_offsets, void *stream,
+                                           uint64_t *out_n_tokens)
+{
+    if (!v || v->da.n) return TOKTIER_E_INVALID_ARG;   // added tokens read a count on the host
+    uint64_t need = 0;
+    int rc = toktier_workspace_bytes(total_bytes, n_docs, &need);
+    if (rc) return rc;
+    if (need > (uint64_t)TOKTIER_STATIC_SCRATCH_BYTES) return TOKTIER_E_CAPACITY;
+    void *ws = static_scratch(v->device);
+    if (!ws) return TOKTIER_E_HIP;   // set up when the vocabulary was loaded on its device
+    Batch b;
+    rc = check_batch(v, bytes, offsets, n_docs, total_bytes, ws, TOKTIER_STATIC_SCRATCH_BYTES, &b);
+    if (rc) return rc;
+    if (!out_offsets || (total_bytes && !out_ids)) return TOKTIER_E_INVALID_ARG;
+    if (ids_capacity < total_bytes) return TOKTIER_E_CAPACITY;
+    hipStream_t s = (hipStream_t)stream;
+    HIP_TRY(launch_pretokenize(v->dv, b, s, nullptr));
+    HIP_TRY(launch_route(v->dv, b, s, nullptr));
+    HIP_TRY(launch_bpe(v->dv, b, s, nullptr));
+    HIP_TRY(launch_compact(v->dv, b, out_ids, out_offsets, nullptr, s, nullptr));
+    if (!out_n_tokens) return TOKTIER_OK;
+    Ctrl c;   // one blocking copy of the control block into this frame
+    HIP_TRY(hipMemcpyAsync(&c, ws, sizeof(Ctrl), hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    if (c.status & ST_BAD_OFFSETS) return TOKTIER_E_INVALID_ARG;
+    if (c.status & ST_BAD_UTF8) return TOKTIER_E_INVALID_UTF8;
+    *out_n_tokens = c.n_tokens;
+    return TOKTIER_OK;
 }
 
 extern "C" int toktier_encode_batch_spans(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,

@@ -193,6 +193,32 @@ int toktier_encode_batch_spans(const toktier_vocab *v, const uint8_t *bytes, con
                                void *workspace, uint64_t workspace_bytes, void *stream,
                                uint64_t *out_n_tokens);
 
+/* Size of the library-owned scratch that toktier_encode_batch_static uses on each device. */
+#define TOKTIER_STATIC_SCRATCH_BYTES (128ull << 20)
+
+/*
+ * toktier_encode_batch for callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no workspace: the same
+ * kernels run on a scratch array of TOKTIER_STATIC_SCRATCH_BYTES bytes that the library holds on
+ * each device from the moment a vocabulary is first loaded there until the process ends.  The call
+ * itself allocates nothing (no hipMalloc, hipFree, pinned host memory or other allocating routine).
+ *   Arguments v, bytes, offsets, n_docs, total_bytes, out_ids, ids_capacity, out_offsets and
+ *   stream as in toktier_encode_batch; the caller still owns the input and output buffers.
+ *   out_n_tokens  host, may be NULL: if non-NULL, one blocking device-to-host copy of the control
+ *                 block, then the token count is stored there and device-detected errors
+ *                 (E_INVALID_UTF8, bad offsets) are returned; if NULL, the call only enqueues and the
+ *                 count is out_offsets[n_docs].
+ * Limits: toktier_workspace_bytes(total_bytes, n_docs) must not exceed TOKTIER_STATIC_SCRATCH_BYTES
+ * (else E_CAPACITY before any device work; about 4 MB of input); vocabularies with added tokens are
+ * rejected (E_INVALID_ARG).  Every call on one device shares that device's scratch, and each call
+ * clears what it needs at its start: calls that overlap on one device (other streams, other host
+ * threads) race and must be serialized by the caller.
+ * Errors: E_INVALID_ARG, E_CAPACITY, E_HIP, and (with out_n_tokens) E_INVALID_UTF8.
+ */
+int toktier_encode_batch_static(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                                uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids, uint64_t ids_capacity,
+                                uint64_t *out_offsets, void *stream, uint64_t *out_n_tokens);
+
 /*
  * Stage 1 alone, for split-level checks (paper, exactness section: boundaries are compared apart
  * from IDs because an ID comparison can hide a wrong split).  Runs exactly the pre-tokenization
