@@ -31,36 +31,6 @@ constexpr uint32_t PENDING = 0xFFFFFFFEu;
 // ---------------------------------------------------------------------------------------------
 // lane per piece
 
-// calls f(id) for every token whose byte string equals s[0, len); the table key was computed by the
-// caller as str_key(H(s), len)
-template <typename F>
-__device__ __forceinline__ void str_find(const DevVocab &v, const uint8_t *s, uint32_t len, uint64_t key, F f)
-{
-    uint32_t i = (uint32_t)str_slot(key, v.str_shift);
-    for (;;) {
-        const uint4 e = v.str[i];
-        if (e.w == 0) return;
-        if (e.w == len && ((uint64_t)e.x | ((uint64_t)e.y << 32)) == key) {
-            const uint8_t *t = v.tok_bytes + v.tok_off[e.z];
-            bool eq = true;
-            for (uint32_t k = 0; k < len && eq; ++k) eq = t[k] == s[k];
-            if (eq) f(e.z);
-        }
-        i = (i + 1) & v.str_mask;
-    }
-}
-
-// ignore_merges: the smallest ID of a token whose bytes are s[0, len) (len up to the longest token),
-// NO_PIECE if there is none
-__device__ uint32_t whole_token(const DevVocab &v, const uint8_t *s, uint32_t len)
-{
-    uint64_t h = 0;
-    for (uint32_t k = 0; k < len; ++k) h = h * STR_P + s[k];
-    uint32_t best = NO_PIECE;
-    str_find(v, s, len, str_key(h, len), [&](uint32_t id) { best = min(best, id); });
-    return best;
-}
-
 // k_route: every piece.  Single bytes and whole-piece table hits get their result word here; the
 // others are listed for BPE by length.  Each workgroup owns a contiguous range of pieces and keeps
 // RT_PPT pieces per thread in flight (their loads and table probes overlap).  List entries are queued
@@ -210,7 +180,6 @@ __device__ __forceinline__ void lane_bpe(const DevVocab &v, const uint8_t *__res
     }
     if (active && chunk) ccount[p] = n;
     else if (active) pval[p] = n == 1 ? id[0] : (PV_MULTI | n);
-    add_excess_wave(ws, L, p, active && !chunk ? n - 1 : 0u);
 }
 
 // The <= 16-byte list, 256 items per workgroup step.  The items are sorted by length in LDS first
@@ -353,7 +322,6 @@ __device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, ui
         const bool head = k == 0 && q < count;
         if (head && chunk) ccount[p] = n;
         else if (head) pval[p] = n == 1 ? id : (PV_MULTI | n);
-        add_excess_wave(ws, L, p, head && !chunk ? n - 1 : 0u);
     }
 }
 
@@ -472,7 +440,6 @@ __device__ void bpe_seg16x2(const DevVocab &v, const uint8_t *__restrict__ bytes
         const bool head = k == 0 && q < count;
         if (head && chunk) ccount[p] = n;
         else if (head) pval[p] = n == 1 ? id0 : (PV_MULTI | n);
-        add_excess_wave(ws, L, p, head && !chunk ? n - 1 : 0u);
     }
 }
 
@@ -573,7 +540,6 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
             if (chunk) ccount[p] = n;
             else pval[p] = n == 1 ? id0 : (PV_MULTI | n);
         }
-        add_excess_wave(ws, L, p, lane == 0 && !chunk ? n - 1 : 0u);
     }
 }
 
@@ -592,10 +558,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 8))) voi
     // that the workgroups with work come first and the idle ones are dispatched last.
     {
         const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
-        g128 = min(g128, (ctrl->miss_count[3] + 3u) / 4u);     // 4 pieces per workgroup step
-        g64 = min(g64, (ctrl->miss_count[2] + 3u) / 4u);
-        g32 = min(g32, (ctrl->miss_count[1] + 15u) / 16u);     // 16
-        g16 = min(g16, (ctrl->miss_count[0] + 255u) / 256u);   // 256
+        const uint32_t *cnt = ctrl->miss_count;
+        g128 = min(g128, (cnt[3] + 3u) / 4u);     // 4 pieces per workgroup step
+        g64 = min(g64, (cnt[2] + 3u) / 4u);
+        g32 = min(g32, (cnt[1] + 15u) / 16u);     // 16
+        g16 = min(g16, (cnt[0] + 255u) / 256u);   // 256
     }
     uint32_t b = blockIdx.x;
     if (b < g128) {
@@ -728,6 +695,20 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
             b0 = cstart[q - count];
             n = clen[q - count];
             if (n < cmin || n > (uint32_t)MAXN) continue;   // unused slot, or a chunk for another kernel
+        }
+        if ((v.flags & VF_IGNORE_MERGES) && !is_chunk && n <= v.lmax) {
+            // ignore_merges: a piece that is a token's byte string is that token
+            if (tid == 0) red[0] = whole_token(v, bytes + b0, n);
+            __syncthreads();
+            const uint32_t w = red[0];
+            __syncthreads();
+            if (w != NO_PIECE) {
+                if (tid == 0) {
+                    scratch[b0] = w;
+                    put_piece(ws, L, p, 1u, 0u, true);
+                }
+                continue;
+            }
         }
         for (uint32_t k = tid; k < n; k += NT) sid[k] = bytes[b0 + k];
         __syncthreads();
@@ -1181,7 +1162,7 @@ hipError_t launch_route(const DevVocab &v, const Batch &b, hipStream_t s, const 
 {
     if (b.n == 0) return hipGetLastError();
     const uint64_t g = (b.n + 4095) / 4096;   // about 4 KiB of input (1-2K pieces) per workgroup, at most 1024
-    LaunchScope k(ev, 2, s);
+    LaunchScope k(nullptr, 0, s);   // (not part of the encode chain)
     if (v.flags & VF_IGNORE_MERGES)
         hipLaunchKernelGGL(k_route<true>, dim3(g > 1024 ? 1024u : (uint32_t)g), dim3(RT_THREADS), 0, s, v, b.bytes, b.ws, b.L);
     else
@@ -1196,7 +1177,7 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     {
         // giant pieces: safe-seam bitmap, then chunks (before the other BPE kernels, which also
         // encode the chunks)
-        LaunchScope k(ev, 3, s);
+        LaunchScope k(ev, TK_GIANT_SEAMS, s);
         const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
         hipLaunchKernelGGL(k_gsafe, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
         const uint32_t gc = L.cap_giant < 64 ? L.cap_giant : 64;
@@ -1208,24 +1189,24 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
         const uint64_t b16 = b.n / 256 + 1, b32 = b.n / 17 / 16 + 1, b64 = b.n / 33 / 4 + 1, b128 = b.n / 65 / 4 + 1;
         const uint32_t g16 = b16 > 2048 ? 2048u : (uint32_t)b16, g32 = b32 > 2048 ? 2048u : (uint32_t)b32;
         const uint32_t g64 = b64 > 256 ? 256u : (uint32_t)b64, g128 = b128 > 256 ? 256u : (uint32_t)b128;
-        LaunchScope k(ev, 4, s);
+        LaunchScope k(ev, TK_BPE_CHUNKS, s);
         hipLaunchKernelGGL(k_bpe_small, dim3(g16 + g32 + g64 + g128), dim3(256), 0, s, v, b.bytes, b.ws, L, g16, g32,
                            g64, g128);
     }
     {
-        LaunchScope k(ev, 5, s);
+        LaunchScope k(ev, TK_BPE_WAVE, s);
         uint32_t gw = L.cap_wave + L.cap_chunks < 1024 ? L.cap_wave + L.cap_chunks : 1024;
         hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
     }
     const uint32_t gg = L.cap_giant < 64 ? L.cap_giant : 64;
     {
-        LaunchScope k(ev, 6, s);
+        LaunchScope k(ev, TK_BPE_BLOCK, s);
         uint32_t gb = L.cap_block + L.cap_chunks < 256 ? L.cap_block + L.cap_chunks : 256;
         hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v,
                            b.bytes, b.ws, L, 1);
     }
     {
-        LaunchScope k(ev, 7, s);
+        LaunchScope k(ev, TK_BPE_GIANT, s);
         hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
     }
     return hipGetLastError();

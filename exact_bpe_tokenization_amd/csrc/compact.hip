@@ -239,7 +239,7 @@ hipError_t launch_compact(const DevVocab &v, const Batch &b, uint32_t *out_ids, 
 {
     const Layout &L = b.L;
     {
-        LaunchScope k(ev, 8, s);
+        LaunchScope k(nullptr, 0, s);
         if (out_spans)
             hipLaunchKernelGGL(k_emit<true>, dim3(L.n_scan_tiles), dim3(SCAN_THREADS), 0, s, b.ws, L, b.offsets,
                                b.n_docs, b.n, out_ids, out_offsets, out_spans, v.tok_len);
@@ -248,7 +248,7 @@ hipError_t launch_compact(const DevVocab &v, const Batch &b, uint32_t *out_ids, 
                                b.n_docs, b.n, out_ids, out_offsets, out_spans, v.tok_len);
     }
     if (b.n) {
-        LaunchScope k(ev, 9, s);
+        LaunchScope k(nullptr, 0, s);
         uint32_t gl = L.cap_wave + L.cap_chunks < 1024 ? L.cap_wave + L.cap_chunks : 1024;
         hipLaunchKernelGGL(k_gather_long, dim3(gl), dim3(256), 0, s, b.ws, L, out_ids, out_spans, v.tok_len);
     }

@@ -31,6 +31,9 @@ constexpr int TABLE_MAX = 32;     // whole-piece tables hold pieces of 2..32 byt
 constexpr int WAVE_MAX = 1024;
 constexpr int BLOCK_MAX = 4096;
 constexpr int BLOCK_THREADS = 256;
+// pieces of up to SHORT_MAX bytes are encoded by the tile encoder (their bytes lie in its window);
+// longer ones are listed by the pieces kernel and encoded before it
+constexpr int SHORT_MAX = SEG2_MAX;
 constexpr int GIANT_THREADS = 1024;
 
 // ---------------------------------------------------------------------------------------------
@@ -121,6 +124,7 @@ constexpr int NCTX_MAX = NCTX > DS_NCTX ? NCTX : DS_NCTX;
 // ---------------------------------------------------------------------------------------------
 // merge tables.  Pair hash slot: bits 63..21 = (left << 21 | right), bits 20..0 = rank.
 constexpr uint32_t NO_RANK = 0xFFFFFFFFu;
+constexpr uint32_t NO_PIECE = 0xFFFFFFFFu;
 constexpr uint64_t EMPTY_SLOT = ~0ull;
 
 constexpr int FAMILY_GPT2 = 1, FAMILY_O200K = 3, FAMILY_DEEPSEEK = 4;   // the family codes of the public header
@@ -350,6 +354,36 @@ __device__ __forceinline__ uint32_t pair_rank(const DevVocab &v, uint32_t a, uin
     }
 }
 
+// calls f(id) for every token whose byte string equals s[0, len); the table key was computed by the
+// caller as str_key(H(s), len)
+template <typename F>
+__device__ __forceinline__ void str_find(const DevVocab &v, const uint8_t *s, uint32_t len, uint64_t key, F f)
+{
+    uint32_t i = (uint32_t)str_slot(key, v.str_shift);
+    for (;;) {
+        const uint4 e = v.str[i];
+        if (e.w == 0) return;
+        if (e.w == len && ((uint64_t)e.x | ((uint64_t)e.y << 32)) == key) {
+            const uint8_t *t = v.tok_bytes + v.tok_off[e.z];
+            bool eq = true;
+            for (uint32_t k = 0; k < len && eq; ++k) eq = t[k] == s[k];
+            if (eq) f(e.z);
+        }
+        i = (i + 1) & v.str_mask;
+    }
+}
+
+// ignore_merges: the smallest ID of a token whose bytes are s[0, len) (len up to the longest token),
+// NO_PIECE if there is none
+__device__ __forceinline__ uint32_t whole_token(const DevVocab &v, const uint8_t *s, uint32_t len)
+{
+    uint64_t h = 0;
+    for (uint32_t k = 0; k < len; ++k) h = h * STR_P + s[k];
+    uint32_t best = NO_PIECE;
+    str_find(v, s, len, str_key(h, len), [&](uint32_t id) { best = min(best, id); });
+    return best;
+}
+
 // ---------------------------------------------------------------------------------------------
 // device control block at the start of the workspace (cleared by the init kernel)
 enum : uint32_t { ST_BAD_UTF8 = 1, ST_BAD_OFFSETS = 2 };
@@ -370,9 +404,10 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // ---------------------------------------------------------------------------------------------
 // workspace layout for n input bytes
 struct Layout {
-    uint64_t ctrl, cc, tbwd, tdoc, tflag_state, tflag_cnt, pstart, pval, tokoff, scratch, bin_wave,
-        bin_block, bin_giant, miss16, miss32, miss64, miss128, g_ids, g_rank_a, g_rank_b, tilex, cstart, clen, ccount,
-        gc0, gnc, gsafe, cpiece, total;
+    uint64_t ctrl, cc, tbwd, tdoc, tflag_state, tflag_cnt, tcount, tsb, tmiss, tbase, tlast, pstart, pval, tokoff,
+        mlist, scratch,
+        bin_wave, bin_block, bin_giant, miss16, miss32, miss64, miss128, g_ids, g_rank_a, g_rank_b, tilex, cstart,
+        clen, ccount, gc0, gnc, gsafe, cpiece, total;
     uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
 };
 
@@ -395,10 +430,16 @@ inline Layout make_layout(uint64_t n)
     L.tdoc = o;        o += align256(16ull * L.n_tiles);
     L.tflag_state = o; o += align256(16ull * L.n_tiles);
     L.tflag_cnt = o;   o += align256(8ull * L.n_tiles);
+    L.tcount = o;      o += align256(4ull * (L.n_tiles + 1));   // tokens of the pieces starting in each tile
+    L.tsb = o;         o += align256(4ull * (L.n_tiles / 64 + 1));  // the same summed over 64 tiles
+    L.tmiss = o;       o += align256(4ull * (L.n_tiles + 1));   // pieces of each tile left for BPE
+    L.tbase = o;       o += align256(4ull * (L.n_tiles + 1));
+    L.tlast = o;       o += align256(4ull * L.n_tiles);
     L.tilex = o;       o += align256(4ull * L.n_scan_tiles);
     L.pstart = o;      o += align256(4ull * (n + 2));
     L.pval = o;        o += align256(4ull * (n + 1));
     L.tokoff = o;      o += align256(4ull * (n + 2));
+    L.mlist = o;       o += align256(4ull * (n + 1));   // those pieces, at the tile's first piece index
     L.scratch = o;     o += align256(4ull * (n + 1));
     L.bin_wave = o;    o += align256(4ull * L.cap_wave);
     L.bin_block = o;   o += align256(4ull * L.cap_block);
@@ -515,7 +556,6 @@ __device__ __forceinline__ uint32_t wp_step(const DevVocab &v, WPQ &q, uint32_t 
 // set: the piece has (word & PV_COUNT) tokens stored at scratch[piece start byte ...]; bit 30 also set
 // for pieces longer than 64 bytes, whose IDs are copied by a separate gather.
 constexpr uint32_t PV_MULTI = 1u << 31, PV_LONG = 1u << 30, PV_COUNT = PV_LONG - 1u;
-constexpr uint32_t NO_PIECE = 0xFFFFFFFFu;
 
 // Result of piece p: n >= 1 tokens, first ID id0 (the others already in scratch when n > 1).  The
 // excess over one token is added to the counter of the piece's output tile (SCAN_TILE consecutive
@@ -586,6 +626,30 @@ __device__ __forceinline__ void add_excess_wave(uint8_t *ws, const Layout &L, ui
     if (tail && key != 0xFFFFFFFFu && v) atomicAdd((uint32_t *)(ws + L.tilex) + key, v);
 }
 
+// Wavefront form of the per-tile token counters of the tile encoder's pieces, called by all 64 lanes:
+// lane i adds x tokens (0: none) of the piece starting at byte b0 to the counter of b0's input tile
+// and of its group of 64 tiles; lanes are combined over runs of equal tiles in lane order and each
+// run's last lane issues the atomics.
+__device__ __forceinline__ void add_tile_tokens(uint8_t *ws, const Layout &L, uint32_t b0, uint32_t x)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t key = x ? b0 / (uint32_t)TILE : 0xFFFFFFFFu;
+    const uint32_t prev = __shfl_up(key, 1, 64);
+    const uint64_t heads = __ballot(lane == 0 || prev != key);
+    const uint32_t hpos = 63u - (uint32_t)__clzll((unsigned long long)(heads & ((2ull << lane) - 1ull)));
+    uint32_t v = x;
+#pragma unroll
+    for (uint32_t d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(v, d, 64);
+        if (lane >= hpos + d) v += y;
+    }
+    const bool tail = lane == 63 || ((heads >> (lane + 1)) & 1ull);
+    if (tail && key != 0xFFFFFFFFu && v) {
+        atomicAdd((uint32_t *)(ws + L.tcount) + key, v);
+        atomicAdd((uint32_t *)(ws + L.tsb) + key / 64u, v);
+    }
+}
+
 // kernel launchers (each in its own translation unit); all enqueue on `s` and return the launch
 // status from hipGetLastError
 struct Batch {
@@ -596,6 +660,11 @@ struct Batch {
     uint8_t *ws;
     Layout L;
 };
+
+// launch indices of the encode chain (TOKTIER_K_* in toktier.h)
+enum : int { TK_SUMMARY = 0, TK_PIECES = 1, TK_GIANT_SEAMS = 2, TK_BPE_CHUNKS = 3, TK_BPE_WAVE = 4, TK_BPE_BLOCK = 5,
+             TK_BPE_GIANT = 6, TK_TILES = 7, TK_BPE_TILES = 8,
+             TK_EMIT = 9, TK_COUNT = 10 };
 
 // optional events recorded around each kernel launch (indices: TOKTIER_K_* in toktier.h)
 struct Events {
@@ -688,5 +757,9 @@ hipError_t launch_compact(const DevVocab &v, const Batch &b, uint32_t *out_ids, 
                           uint32_t *out_spans, hipStream_t s, const Events *ev);
 hipError_t launch_export_starts(const Batch &b, uint32_t *out_starts, hipStream_t s);
 hipError_t launch_route(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
+hipError_t launch_bpe_tiles(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
+hipError_t launch_tiles(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
+hipError_t launch_emit(const DevVocab &v, const Batch &b, uint32_t *out_ids, uint64_t *out_offsets,
+                       uint32_t *out_spans, hipStream_t s, const Events *ev);
 
 }  // namespace tt

@@ -259,8 +259,10 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
     if (blockIdx.x < L.n_tiles && lane == 0) {
         ((uint4 *)(ws + L.tflag_state))[blockIdx.x] = make_uint4(0u, 0u, 0u, 0u);
         ((uint64_t *)(ws + L.tflag_cnt))[blockIdx.x] = 0;
+        ((uint32_t *)(ws + L.tlast))[blockIdx.x] = 0;
     }
     for (uint32_t k = blockIdx.x * 64u + lane; k < L.n_scan_tiles; k += gridDim.x * 64u) ((uint32_t *)(ws + L.tilex))[k] = 0;
+    for (uint32_t k = blockIdx.x * 64u + lane; k <= L.n_tiles / 64u; k += gridDim.x * 64u) ((uint32_t *)(ws + L.tsb))[k] = 0;
     if (blockIdx.x >= L.n_tiles) return;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
     const uint64_t hi = min(lo + TILE, n);
@@ -391,6 +393,33 @@ __device__ __forceinline__ uint32_t reg_byte_code(const uint32_t (&rw)[6], uint3
 
 // ---------------------------------------------------------------------------------------------
 // k_pieces: dynamic tile ids; decode, automaton context, scans, look-backs, piece starts
+
+// Position of the last piece start before `tile`.  Every tile publishes its last start in tlast
+// (0: not yet, 1: the tile has none, else position + 2) as soon as its starts are known; tile 0
+// always has one (at byte 0).  Wave 0 reads 64 predecessors per step; uniform result.
+__device__ uint32_t last_start_before(const uint32_t *tlast, uint32_t tile)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    int64_t top = (int64_t)tile - 1;
+    for (;;) {
+        const int64_t pos = top - (int64_t)lane;
+        const uint32_t w = pos >= 0 ? __hip_atomic_load(tlast + pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 2u;
+        const uint64_t has = __ballot(w >= 2u), nr = __ballot(w == 0u);
+        const uint32_t k = has ? (uint32_t)__ffsll((unsigned long long)has) - 1u : 64u;
+        const uint64_t need = k >= 63 ? ~0ull : ((2ull << k) - 1);
+        if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
+        if (k < 64) return (uint32_t)__builtin_amdgcn_readlane((int)w, k) - 2u;
+        top -= 64;
+    }
+}
+
+// a piece longer than SHORT_MAX bytes goes on the list of its length bin (encoded before the tile
+// encoder, which only collects its result)
+__device__ __forceinline__ void list_long(uint8_t *ws, const Layout &L, Ctrl *ctrl, uint32_t p, uint32_t len)
+{
+    const uint32_t r = route_of(len);
+    route_list(ws, L, r)[atomicAdd(route_count(ctrl, r), 1u)] = p;
+}
 
 // A backward flag of all 16 characters of a chunk at once.  Bit k of D: character k decides the
 // flag (bit k of T: its value); other positions pass on the value of the position after them, and
@@ -795,22 +824,48 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         }
     }
 
-    // look-back #2: number of pieces before this tile
+    __syncthreads();
+    uint32_t *tlast = (uint32_t *)(ws + L.tlast);
+    uint32_t *tbase = (uint32_t *)(ws + L.tbase);
+    if (tid == 0)
+        __hip_atomic_store(tlast + tile, total ? (uint32_t)(lo + spiece[total - 1]) + 2u : 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+
+    // look-back #2: number of pieces before this tile; then the piece that ends at this tile's first
+    // start (or, in the last tile, at the end of the batch) is checked for length: it started at the
+    // last start before this tile
     if (wid == 0) {
         if (lane == 0 && tile > 0) st_flag(tfc + tile, (1ull << 62) | total);
         const uint64_t basev = tile == 0 ? 0 : lookback_sum(tfc, tile);
+        const bool last_tile = tile == L.n_tiles - 1;
         if (lane == 0) {
             st_flag(tfc + tile, (2ull << 62) | (basev + total));
             s_base = (uint32_t)basev;
-            if (tile == L.n_tiles - 1) {
+            tbase[tile] = (uint32_t)basev;
+            if (last_tile) {
                 ctrl->n_pieces = (uint32_t)(basev + total);
                 pstart[basev + total] = (uint32_t)n;
+                tbase[L.n_tiles] = (uint32_t)(basev + total);
             }
+        }
+        if (tile > 0 && (total > 0 || last_tile)) {
+            const uint32_t prev = last_start_before(tlast, tile);
+            const uint32_t end = total ? (uint32_t)(lo + spiece[0]) : (uint32_t)n;
+            if (lane == 0 && end - prev > (uint32_t)SHORT_MAX) list_long(ws, L, ctrl, (uint32_t)basev - 1u, end - prev);
+        }
+        if (last_tile && total > 0 && lane == 0) {
+            const uint32_t a = (uint32_t)(lo + spiece[total - 1]);
+            if ((uint32_t)n - a > (uint32_t)SHORT_MAX) list_long(ws, L, ctrl, (uint32_t)basev + total - 1u, (uint32_t)n - a);
         }
     }
     __syncthreads();
     const uint32_t gbase = s_base;
-    for (uint32_t i = tid; i < total; i += PRE_THREADS) pstart[gbase + i] = (uint32_t)(lo + spiece[i]);
+    for (uint32_t i = tid; i < total; i += PRE_THREADS) {
+        const uint32_t a = spiece[i];
+        pstart[gbase + i] = (uint32_t)(lo + a);
+        if (i + 1 < total && (uint32_t)spiece[i + 1] - a > (uint32_t)SHORT_MAX)
+            list_long(ws, L, ctrl, gbase + i, (uint32_t)spiece[i + 1] - a);
+    }
 
 }
 
@@ -820,13 +875,13 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
 {
     const Layout &L = b.L;
     {
-        LaunchScope k(ev, 0, s);
+        LaunchScope k(ev, TK_SUMMARY, s);
         hipLaunchKernelGGL(k_summary, dim3(L.n_tiles ? L.n_tiles : 1u), dim3(64), 0, s, b.bytes, b.offsets, b.n_docs,
                            b.n, b.ws, L);
     }
     if (L.n_tiles == 0) return hipGetLastError();
     {
-        LaunchScope k(ev, 1, s);
+        LaunchScope k(ev, TK_PIECES, s);
         const dim3 grid(L.n_tiles);
         if (v.family == FAMILY_O200K)
             hipLaunchKernelGGL(k_pieces<VAR_CASE>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs,

@@ -865,6 +865,19 @@ int read_ctrl(void *workspace, hipStream_t s, Ctrl *out)
 
 namespace {
 
+// the encode chain: pre-tokenizer (with the long-piece lists), the long pieces, the tile encoder,
+// BPE of the pieces it left, the output writer
+hipError_t launch_chain(const DevVocab &v, const Batch &b, uint32_t *out_ids, uint64_t *out_offsets,
+                        uint32_t *out_spans, hipStream_t s, const Events *ev)
+{
+    hipError_t e = launch_pretokenize(v, b, s, ev);
+    if (e == hipSuccess) e = launch_bpe(v, b, s, ev);
+    if (e == hipSuccess) e = launch_tiles(v, b, s, ev);
+    if (e == hipSuccess) e = launch_bpe_tiles(v, b, s, ev);
+    if (e == hipSuccess) e = launch_emit(v, b, out_ids, out_offsets, out_spans, s, ev);
+    return e;
+}
+
 int encode_impl(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets, uint32_t n_docs,
                 uint64_t total_bytes, uint32_t *out_ids, uint64_t ids_capacity, uint64_t *out_offsets,
                 uint32_t *out_spans, void *workspace, uint64_t workspace_bytes, void *stream,
@@ -892,11 +905,8 @@ int encode_impl(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *of
             Batch b2 = b;
             b2.offsets = (const uint64_t *)(b.ws + A.offs2);
             b2.n_docs = n_docs + 2 * lc.n_lit;
-            HIP_TRY(launch_pretokenize(v->dv, b2, s, ev));
-            HIP_TRY(launch_route(v->dv, b2, s, ev));
-            HIP_TRY(launch_bpe(v->dv, b2, s, ev));
-            HIP_TRY(launch_compact(v->dv, b2, (uint32_t *)(b.ws + A.ids2), (uint64_t *)(b.ws + A.oo2),
-                                   out_spans ? (uint32_t *)(b.ws + A.spans2) : nullptr, s, ev));
+            HIP_TRY(launch_chain(v->dv, b2, (uint32_t *)(b.ws + A.ids2), (uint64_t *)(b.ws + A.oo2),
+                                 out_spans ? (uint32_t *)(b.ws + A.spans2) : nullptr, s, ev));
             HIP_TRY(launch_literal_merge(v->da, b, A, lc.n_lit, out_ids, out_offsets, out_spans, s));
             if (!out_n_tokens) return TOKTIER_OK;
             Ctrl c;
@@ -906,10 +916,7 @@ int encode_impl(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *of
             return TOKTIER_OK;
         }
     }
-    HIP_TRY(launch_pretokenize(v->dv, b, s, ev));
-    HIP_TRY(launch_route(v->dv, b, s, ev));
-    HIP_TRY(launch_bpe(v->dv, b, s, ev));
-    HIP_TRY(launch_compact(v->dv, b, out_ids, out_offsets, out_spans, s, ev));
+    HIP_TRY(launch_chain(v->dv, b, out_ids, out_offsets, out_spans, s, ev));
     if (!out_n_tokens) return TOKTIER_OK;
     Ctrl c;
     rc = read_ctrl(workspace, s, &c);
@@ -952,10 +959,7 @@ extern "C" int toktier_plan_create(const toktier_vocab *v, const uint8_t *bytes,
     hipGraph_t g = nullptr;
     hipError_t e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
-        hipError_t e1 = launch_pretokenize(v->dv, b, cap, nullptr);
-        if (e1 == hipSuccess) e1 = launch_route(v->dv, b, cap, nullptr);
-        if (e1 == hipSuccess) e1 = launch_bpe(v->dv, b, cap, nullptr);
-        if (e1 == hipSuccess) e1 = launch_compact(v->dv, b, out_ids, out_offsets, out_spans, cap, nullptr);
+        hipError_t e1 = launch_chain(v->dv, b, out_ids, out_offsets, out_spans, cap, nullptr);
         e = hipStreamEndCapture(cap, &g);
         if (e == hipSuccess) e = e1;
     }
@@ -1034,10 +1038,7 @@ extern "C" int toktier_encode_batch_static(const toktier_vocab *v, const uint8_t
     if (!out_offsets || (total_bytes && !out_ids)) return TOKTIER_E_INVALID_ARG;
     if (ids_capacity < total_bytes) return TOKTIER_E_CAPACITY;
     hipStream_t s = (hipStream_t)stream;
-    HIP_TRY(launch_pretokenize(v->dv, b, s, nullptr));
-    HIP_TRY(launch_route(v->dv, b, s, nullptr));
-    HIP_TRY(launch_bpe(v->dv, b, s, nullptr));
-    HIP_TRY(launch_compact(v->dv, b, out_ids, out_offsets, nullptr, s, nullptr));
+    HIP_TRY(launch_chain(v->dv, b, out_ids, out_offsets, nullptr, s, nullptr));
     if (!out_n_tokens) return TOKTIER_OK;
     Ctrl c;   // one blocking copy of the control block into this frame
     HIP_TRY(hipMemcpyAsync(&c, ws, sizeof(Ctrl), hipMemcpyDeviceToHost, s));

@@ -244,21 +244,23 @@ int toktier_last_status(void *workspace, void *stream, uint64_t *out_n_tokens);
 /* Kernel launches of one toktier_encode_batch call, in stream order (indices for the timed form).
  * An index may cover several launches of one step. */
 enum {
-    TOKTIER_K_SUMMARY = 0,    /* clear the control block, look-back flags and token counters;   */
-                              /* per tile: the characters that decide the backward flags        */
-    TOKTIER_K_PIECES,         /* UTF-8 decode + validation, automaton scan, piece starts        */
-    TOKTIER_K_ROUTE,          /* every piece: single byte or whole-piece table hit, else BPE list */
-    TOKTIER_K_GIANT_SEAMS,    /* pieces > 4096 bytes: seams no merge crosses, then chunks       */
-    TOKTIER_K_BPE_SMALL,      /* BPE of unresolved pieces and chunks of <= 128 bytes: lane per  */
-                              /* piece (<= 16), 32-lane segments (<= 32), a wavefront (<= 64),  */
-                              /* a wavefront with two elements per lane (<= 128), one launch    */
-    TOKTIER_K_BPE_WAVE,       /* BPE, one wavefront per piece of 129..1024 bytes                */
-    TOKTIER_K_BPE_BLOCK,      /* BPE, one workgroup per piece of 1025..4096 bytes or chunk      */
-    TOKTIER_K_BPE_GIANT,      /* BPE, one workgroup per longer chunk, sequence in device memory; */
-                              /* then (last workgroup) each giant piece's token count and its    */
-                              /* chunks' output places                                           */
-    TOKTIER_K_EMIT,           /* token-offset scan, ID gather, per-document token offsets       */
-    TOKTIER_K_GATHER_LONG,    /* ID gather of the pieces longer than 128 bytes                  */
+    TOKTIER_K_SUMMARY = 0,    /* clear the control block and look-back flags; per tile: the        */
+                              /* characters that decide the backward flags, the documents near it  */
+    TOKTIER_K_PIECES,         /* UTF-8 decode + validation, automaton scan, piece starts; pieces    */
+                              /* longer than 128 bytes listed by length                            */
+    TOKTIER_K_GIANT_SEAMS,    /* pieces > 4096 bytes: seams no merge crosses, then chunks           */
+    TOKTIER_K_BPE_CHUNKS,     /* BPE of the chunks of <= 128 bytes of those pieces                  */
+    TOKTIER_K_BPE_WAVE,       /* BPE, one wavefront per piece of 129..1024 bytes or chunk           */
+    TOKTIER_K_BPE_BLOCK,      /* BPE, one workgroup per piece of 1025..4096 bytes or chunk          */
+    TOKTIER_K_BPE_GIANT,      /* BPE, one workgroup per longer chunk, sequence in device memory;    */
+                              /* then (last workgroup) each giant piece's token count and its       */
+                              /* chunks' output places                                              */
+    TOKTIER_K_TILES,          /* per 8 KiB tile: single bytes and whole-piece table lookups; the    */
+                              /* other pieces of <= 128 bytes listed in the tile's slice            */
+    TOKTIER_K_BPE_TILES,      /* per tile, BPE of those pieces: lane per piece (<= 16), 16 lanes x  */
+                              /* 2 rows (<= 32), a wavefront (<= 64), two elements per lane (<= 128)*/
+    TOKTIER_K_EMIT,           /* per tile: IDs placed by a scan of token counts, document offsets,  */
+                              /* token spans                                                        */
     TOKTIER_K_COUNT
 };
 
