@@ -131,22 +131,23 @@ constexpr int FAMILY_GPT2 = 1, FAMILY_O200K = 3, FAMILY_DEEPSEEK = 4;   // the f
 
 struct DevVocab {
     const uint32_t *r2;       // 65536 byte-pair ranks
-    const uint64_t *slots;    // pair hash: 8-byte slots, linear probing, at most one in 32 used
+    const uint64_t *slots;    // pair table: 8-byte slots (left << 21 | right) << 21 | rank, two-choice cuckoo
     const uint32_t *merges;   // 2 * n_merges (left, right)
     const uint4 *fmap16;      // NCTX (DeepSeek style: DS_NCTX) transition maps, one byte per state s (bytes 0..14):
                               //   bits 0-3 the next state, bit 4 set when a piece starts here in s
     // whole-piece tables: pieces whose BPE result is one token (NULL while they are being built)
-    const uint4 *wa;          // 2..7 bytes: {key lo, key hi, id, 0}, key = bytes | len << 56
-    const uint4 *wb;          // 8..32 bytes: 3 x uint4 = {k0, k1}, {k2, k3}, {len, id, 0, 0}
+    // (two-choice cuckoo tables: every key is in one of its two candidate slots, both read at once)
+    const uint4 *wa;          // 2..7 bytes: {key lo, key hi, id, 0}, key = bytes | len << 56; key 0 = empty
+    const uint4 *wb;          // 8..32 bytes: 3 x uint4 = {k0, k1}, {k2, k3}, {len, id, 0, 0}; len 0 = empty
+    const uint4 *hot;         // HOT_SLOTS entries of the short table, the lowest IDs: 2-way sets, copied to LDS
     // every token's byte string: bytes, offsets, and a hash from (string) to token ID, used to find
     // seams no merge can cross in giant pieces (NULL when the longest token exceeds STR_LMAX bytes)
     const uint8_t *tok_bytes;
     const uint32_t *tok_off;  // 256 + n_merges + 1 offsets into tok_bytes
     const uint32_t *tok_len;  // byte length of every token (for token spans; always present)
     const uint4 *str;         // {key lo, key hi, id, len}; len 0 = empty slot
-    uint32_t mask;
-    uint32_t shift;
-    uint32_t wa_mask, wa_shift, wb_mask, wb_shift;
+    uint64_t pseed, wseed, bseed;   // seeds of the candidate-slot hashes (pairs, wa, wb)
+    uint32_t slot_cap, wa_cap, wb_cap;
     uint32_t str_mask, str_shift, lmax;
     uint32_t n_merges;
     int family;
@@ -172,19 +173,44 @@ __host__ __device__ __forceinline__ uint64_t str_slot(uint64_t key, uint32_t shi
 
 // whole-piece keys
 constexpr uint32_t WA_MAX = 7;
-__host__ __device__ __forceinline__ uint64_t wa_hash(uint64_t key, uint32_t shift)
+
+// The hot part of the short whole-piece table: the 2..7-byte entries with the lowest token IDs (the
+// first merges are the most frequent pairs of the training text, and their tokens dominate real
+// text) in HOT_SLOTS / 2 sets of two, small enough for every tile workgroup to keep in LDS.
+constexpr uint32_t HOT_SLOTS = 1024;
+__host__ __device__ __forceinline__ uint32_t hot_set(uint64_t key)
 {
-    return (key * 0x9E3779B97F4A7C15ull) >> shift;
+    return (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> 55);   // HOT_SLOTS / 2 = 512 sets
 }
-__host__ __device__ __forceinline__ uint64_t wb_hash(uint64_t k0, uint64_t k1, uint64_t k2, uint64_t k3,
-                                                    uint32_t len, uint32_t shift)
+
+// Two-choice cuckoo hashing: a 64-bit digest of the key, mixed with the table's seed, gives two
+// candidate slots in [0, cap) (its two 32-bit halves scaled to cap).  A lookup reads both slots at
+// once, so it always costs one round trip, and the tables stay small (under half full).
+__host__ __device__ __forceinline__ uint64_t ck_mix(uint64_t x)
+{
+    x ^= x >> 33;
+    x *= 0xFF51AFD7ED558CCDull;
+    x ^= x >> 33;
+    x *= 0xC4CEB9FE1A85EC53ull;
+    x ^= x >> 33;
+    return x;
+}
+__host__ __device__ __forceinline__ void ck_slots(uint64_t digest, uint64_t seed, uint32_t cap, uint32_t &i1,
+                                                  uint32_t &i2)
+{
+    const uint64_t h = ck_mix(digest ^ seed);
+    i1 = (uint32_t)(((h & 0xFFFFFFFFull) * cap) >> 32);
+    i2 = (uint32_t)(((h >> 32) * cap) >> 32);
+}
+// digest of an 8..32-byte key (its four words and length)
+__host__ __device__ __forceinline__ uint64_t wb_digest(uint64_t k0, uint64_t k1, uint64_t k2, uint64_t k3,
+                                                      uint32_t len)
 {
     uint64_t h = k0 * 0x9E3779B97F4A7C15ull;
     h ^= (k1 + 0x632BE59BD9B4E019ull) * 0xC2B2AE3D27D4EB4Full;
     h ^= (k2 + 0x85EBCA77C2B2AE63ull) * 0x165667B19E3779F9ull;
     h ^= (k3 + len) * 0x27D4EB2F165667C5ull;
-    h ^= h >> 29;
-    return (h * 0x9E3779B97F4A7C15ull) >> shift;
+    return h;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -315,43 +341,36 @@ __device__ __forceinline__ uint32_t wave_upper_bound(const T *a, uint32_t n, T x
     return wave_partition_point(a, n, [x](T v) { return v > x; });
 }
 
-// Rank of the pair (a, b), NO_RANK if it is not a merge.  Byte pairs come from the dense table;
-// other pairs from the bucketed hash: one 64-byte bucket per probe (four independent 16-byte
-// loads), usually a single round trip whether the pair is present or not.
-// Ranks of two pairs, each with an operand >= 256 (not byte pairs), with both first slot reads in
-// flight at once: a merge step that needs both waits for one round trip, not two
+// rank held by a pair-table slot for key, NO_RANK if neither candidate holds it (an empty slot is
+// all ones: its key field exceeds every (left << 21 | right))
+__device__ __forceinline__ uint32_t slot_rank(uint64_t s0, uint64_t s1, uint64_t key)
+{
+    return (s0 >> 21) == key ? (uint32_t)(s0 & 0x1FFFFFu) : ((s1 >> 21) == key ? (uint32_t)(s1 & 0x1FFFFFu) : NO_RANK);
+}
+
+// Ranks of two pairs, each with an operand >= 256 (not byte pairs): all four candidate slots read at
+// once, so a merge step that needs both waits for one round trip
 __device__ __forceinline__ void pair_rank2_general(const DevVocab &v, uint32_t a0, uint32_t b0, uint32_t a1,
                                                    uint32_t b1, uint32_t &r0, uint32_t &r1)
 {
     const uint64_t k0 = ((uint64_t)a0 << 21) | b0, k1 = ((uint64_t)a1 << 21) | b1;
-    uint32_t h0 = (uint32_t)((k0 * 0x9E3779B97F4A7C15ull) >> v.shift);
-    uint32_t h1 = (uint32_t)((k1 * 0x9E3779B97F4A7C15ull) >> v.shift);
-    uint64_t s0 = v.slots[h0], s1 = v.slots[h1];
-    while ((s0 >> 21) != k0 && s0 != EMPTY_SLOT) {
-        h0 = (h0 + 1) & v.mask;
-        s0 = v.slots[h0];
-    }
-    while ((s1 >> 21) != k1 && s1 != EMPTY_SLOT) {
-        h1 = (h1 + 1) & v.mask;
-        s1 = v.slots[h1];
-    }
-    r0 = s0 == EMPTY_SLOT ? NO_RANK : (uint32_t)(s0 & 0x1FFFFFu);
-    r1 = s1 == EMPTY_SLOT ? NO_RANK : (uint32_t)(s1 & 0x1FFFFFu);
+    uint32_t i0, j0, i1, j1;
+    ck_slots(k0, v.pseed, v.slot_cap, i0, j0);
+    ck_slots(k1, v.pseed, v.slot_cap, i1, j1);
+    const uint64_t s0 = v.slots[i0], t0 = v.slots[j0], s1 = v.slots[i1], t1 = v.slots[j1];
+    r0 = slot_rank(s0, t0, k0);
+    r1 = slot_rank(s1, t1, k1);
 }
 
 // Rank of the pair (a, b), NO_RANK if no merge joins them: byte pairs from the dense table, the others
-// by linear probing of single slots (a sparse table keeps a wavefront's longest probe chain short)
+// from the pair table (both candidate slots in one round trip)
 __device__ __forceinline__ uint32_t pair_rank(const DevVocab &v, uint32_t a, uint32_t b)
 {
     if ((a | b) < 256u) return __ldg(v.r2 + ((a << 8) | b));
     const uint64_t key = ((uint64_t)a << 21) | b;
-    uint32_t h = (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> v.shift);
-    for (;;) {
-        const uint64_t sl = v.slots[h];
-        if ((sl >> 21) == key) return (uint32_t)(sl & 0x1FFFFFu);
-        if (sl == EMPTY_SLOT) return NO_RANK;
-        h = (h + 1) & v.mask;
-    }
+    uint32_t i, j;
+    ck_slots(key, v.pseed, v.slot_cap, i, j);
+    return slot_rank(v.slots[i], v.slots[j], key);
 }
 
 // calls f(id) for every token whose byte string equals s[0, len); the table key was computed by the
@@ -487,68 +506,57 @@ __device__ __forceinline__ void load_words(const uint8_t *src, uint32_t len, uin
     }
 }
 
-// The same lookup split into steps, so that a thread can keep the probes of two pieces in flight:
-// wp_make reads the piece's bytes and hashes them; each wp_step loads one slot and answers
-// WP_HIT (id set), WP_MISS, or WP_MORE (the next slot must be probed).
+// The whole-piece lookup split into two steps, so that a thread can keep the probes of several pieces
+// in flight: wp_make reads the piece's bytes and hashes them; wp_step reads both candidate slots and
+// answers WP_HIT (id set) or WP_MISS.
 enum : uint32_t { WP_MORE = 0, WP_HIT = 1, WP_MISS = 2 };
 struct WPQ {
     uint64_t k0, k1, k2, k3;
-    uint32_t len, h, kind;   // kind 0: no table applies, 1: short table, 2: long table
+    uint32_t len, i, j, kind;   // kind 0: no table applies, 1: short table, 2: long table; i, j: candidates
 };
 
 // (for len 1, q.k0 is the piece's byte, which is its token ID)
 __device__ __forceinline__ WPQ wp_make(const DevVocab &v, const uint8_t *__restrict__ src, uint32_t len)
 {
-    WPQ q{0, 0, 0, 0, len, 0, 0};
+    WPQ q{0, 0, 0, 0, len, 0, 0, 0};
     if (len == 0 || len > (uint32_t)TABLE_MAX) return q;
-    // one round of loads for every length (the words past the piece are not read), so that a
-    // wavefront holding short and long pieces waits once
     uint64_t k4[4];
     load_words<4>(src, len, k4);
     q.k0 = k4[0]; q.k1 = k4[1]; q.k2 = k4[2]; q.k3 = k4[3];
     if (len <= WA_MAX) {
         if (len == 1 || !v.wa) return q;
         q.k0 |= (uint64_t)len << 56;
-        q.h = (uint32_t)wa_hash(q.k0, v.wa_shift);
+        ck_slots(q.k0, v.wseed, v.wa_cap, q.i, q.j);
         q.kind = 1;
         return q;
     }
     if (!v.wb) return q;
-    q.h = (uint32_t)wb_hash(k4[0], k4[1], k4[2], k4[3], len, v.wb_shift);
+    ck_slots(wb_digest(k4[0], k4[1], k4[2], k4[3], len), v.bseed, v.wb_cap, q.i, q.j);
     q.kind = 2;
     return q;
+}
+
+// an 8..32-byte entry (three 16-byte words) equal to the key?
+__device__ __forceinline__ bool wb_match(uint4 a, uint4 b, uint4 c, uint64_t k0, uint64_t k1, uint64_t k2,
+                                         uint64_t k3, uint32_t len)
+{
+    return c.x == len && ((uint64_t)a.x | ((uint64_t)a.y << 32)) == k0 && ((uint64_t)a.z | ((uint64_t)a.w << 32)) == k1 &&
+           ((uint64_t)b.x | ((uint64_t)b.y << 32)) == k2 && ((uint64_t)b.z | ((uint64_t)b.w << 32)) == k3;
 }
 
 __device__ __forceinline__ uint32_t wp_step(const DevVocab &v, WPQ &q, uint32_t *id)
 {
     if (q.kind == 0) return WP_MISS;
-    // the slot reads of both tables issued together (a wavefront holding pieces of both kinds waits
-    // for one round trip, not two)
-    const uint4 *e = q.kind == 1 ? v.wa + q.h : v.wb + 3ull * q.h;
-    const uint4 a = e[0];
-    uint4 b = make_uint4(0u, 0u, 0u, 0u), c = make_uint4(0u, 0u, 0u, 0u);
-    if (q.kind == 2) {
-        b = e[1];
-        c = e[2];
-    }
     if (q.kind == 1) {
-        const uint64_t sk = (uint64_t)a.x | ((uint64_t)a.y << 32);
-        if (sk == q.k0) { *id = a.z; return WP_HIT; }
-        if (sk == 0) return WP_MISS;
-        q.h = (q.h + 1) & v.wa_mask;
-        return WP_MORE;
+        const uint4 a = v.wa[q.i], b = v.wa[q.j];
+        if (((uint64_t)a.x | ((uint64_t)a.y << 32)) == q.k0) { *id = a.z; return WP_HIT; }
+        if (((uint64_t)b.x | ((uint64_t)b.y << 32)) == q.k0) { *id = b.z; return WP_HIT; }
+        return WP_MISS;
     }
-    {
-        if (c.x == 0) return WP_MISS;
-        if (c.x == q.len && ((uint64_t)a.x | ((uint64_t)a.y << 32)) == q.k0 &&
-            ((uint64_t)a.z | ((uint64_t)a.w << 32)) == q.k1 && ((uint64_t)b.x | ((uint64_t)b.y << 32)) == q.k2 &&
-            ((uint64_t)b.z | ((uint64_t)b.w << 32)) == q.k3) {
-            *id = c.y;
-            return WP_HIT;
-        }
-        q.h = (q.h + 1) & v.wb_mask;
-        return WP_MORE;
-    }
+    const uint4 *e = v.wb + 3ull * q.i, *f = v.wb + 3ull * q.j;
+    const uint4 a0 = e[0], a1 = e[1], a2 = e[2], b0 = f[0], b1 = f[1], b2 = f[2];
+    if (wb_match(a0, a1, a2, q.k0, q.k1, q.k2, q.k3, q.len)) { *id = a2.y; return WP_HIT; }
+    if (wb_match(b0, b1, b2, q.k0, q.k1, q.k2, q.k3, q.len)) { *id = b2.y; return WP_HIT; }
     return WP_MISS;
 }
 

@@ -50,15 +50,14 @@ struct Smem {
 
 struct ResolveSmem {
     uint32_t win[WIN / 4];            // the byte window as words
+    uint4 hot[HOT_SLOTS];             // the hot sets of the short whole-piece table
     uint32_t wsum[NW];
-    uint32_t qn;
+    uint32_t qn, ln;                  // pieces listed for BPE / for the 8..32-byte table
 };
 
 struct EmitSmem {
     uint32_t docbits[TILE / 32];      // document starts in the tile
     uint32_t wsum[NW];
-    uint32_t longp[NT], longo[NT];    // long pieces of a round: piece, first output index
-    uint32_t nlong;
     uint32_t base;
 };
 
@@ -91,19 +90,19 @@ __device__ __forceinline__ void win_words(const S &sm, uint32_t j, uint32_t len,
 template <typename S>
 __device__ __forceinline__ WPQ wp_make_win(const DevVocab &v, const S &sm, uint32_t j, uint32_t len)
 {
-    WPQ q{0, 0, 0, 0, len, 0, 0};
+    WPQ q{0, 0, 0, 0, len, 0, 0, 0};
     uint64_t k4[4];
     win_words<4>(sm, j, len, k4);
     q.k0 = k4[0]; q.k1 = k4[1]; q.k2 = k4[2]; q.k3 = k4[3];
     if (len <= WA_MAX) {
         if (!v.wa) return q;
         q.k0 |= (uint64_t)len << 56;
-        q.h = (uint32_t)wa_hash(q.k0, v.wa_shift);
+        ck_slots(q.k0, v.wseed, v.wa_cap, q.i, q.j);
         q.kind = 1;
         return q;
     }
     if (!v.wb) return q;
-    q.h = (uint32_t)wb_hash(k4[0], k4[1], k4[2], k4[3], len, v.wb_shift);
+    ck_slots(wb_digest(k4[0], k4[1], k4[2], k4[3], len), v.bseed, v.wb_cap, q.i, q.j);
     q.kind = 2;
     return q;
 }
@@ -472,25 +471,55 @@ __device__ void drain(const DevVocab &v, Smem &sm, uint32_t nq, const uint32_t *
     __syncthreads();
 }
 
-// the byte window [lo, lo + WIN), zero past the batch (two aligned loads per word, which never leave
-// the pages of the bytes they hold)
+// the byte window [lo, lo + WIN), zero past the batch.  Every thread issues all of its loads before
+// storing any (a loop that waits for each load pays one memory latency per iteration): interior
+// tiles with 16-byte aligned input read aligned 16-byte words; otherwise 32-bit words from two
+// aligned loads each (never leaving the pages of the bytes they hold), zero past the batch.
 template <typename S>
 __device__ __forceinline__ void load_window(S &sm, const uint8_t *__restrict__ bytes, uint64_t n, uint64_t lo)
 {
-    for (uint32_t w = threadIdx.x; w < (uint32_t)WIN / 4; w += NT) {
+    constexpr int NV = WIN / 16;                    // 16-byte words of the window
+    constexpr int PER = (NV + NT - 1) / NT;
+    static_assert(WIN % 16 == 0, "window of whole 16-byte words");
+    const uint32_t tid = threadIdx.x;
+    if (lo + WIN <= n && ((uintptr_t)(bytes + lo) & 15u) == 0) {
+        const uint4 *src = (const uint4 *)(bytes + lo);
+        uint4 x[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const uint32_t w = tid + k * NT;
+            x[k] = w < (uint32_t)NV ? src[w] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const uint32_t w = tid + k * NT;
+            if (w < (uint32_t)NV) *(uint4 *)&sm.win[4 * w] = x[k];
+        }
+        return;
+    }
+    constexpr int PER4 = (WIN / 4 + NT - 1) / NT;
+    uint32_t x[PER4];
+#pragma unroll
+    for (int k = 0; k < PER4; ++k) {
+        const uint32_t w = tid + k * NT;
         const uint64_t q = lo + 4ull * w;
-        uint32_t x = 0;
-        if (q + 4 <= n) {
+        uint32_t y = 0;
+        if (w < (uint32_t)WIN / 4 && q + 4 <= n) {
             const uintptr_t ad = (uintptr_t)(bytes + q);
             const uint32_t *al = (const uint32_t *)(ad & ~(uintptr_t)3);
             const uint32_t sh = (uint32_t)(ad & 3u);
-            const uint32_t w0 = al[0];
-            x = sh ? __builtin_amdgcn_alignbyte(al[1], w0, sh) : w0;
-        } else {
+            const uint32_t w0 = al[0], w1 = sh ? al[1] : 0u;
+            y = sh ? __builtin_amdgcn_alignbyte(w1, w0, sh) : w0;
+        } else if (w < (uint32_t)WIN / 4) {
             for (uint32_t t = 0; t < 4; ++t)
-                if (q + t < n) x |= (uint32_t)bytes[q + t] << (8 * t);
+                if (q + t < n) y |= (uint32_t)bytes[q + t] << (8 * t);
         }
-        sm.win[w] = x;
+        x[k] = y;
+    }
+#pragma unroll
+    for (int k = 0; k < PER4; ++k) {
+        const uint32_t w = tid + k * NT;
+        if (w < (uint32_t)WIN / 4) sm.win[w] = x[k];
     }
 }
 
@@ -525,13 +554,14 @@ __device__ uint32_t giant_index(const uint8_t *ws, const Layout &L, uint32_t p)
     return NO_PIECE;
 }
 
-// the IDs of a piece encoded before the tile encoder (longer than SHORT_MAX bytes), copied by the
-// whole workgroup from scratch (for a giant piece, chunk by chunk to each chunk's place in the
-// piece's output); with spans, a workgroup scan of the token lengths from the piece's (chunk's) start
+// the IDs of a piece encoded before the tile encoder (longer than SHORT_MAX bytes), copied by one
+// wavefront from scratch (for a giant piece, chunk by chunk to each chunk's place in the piece's
+// output); with spans, a wavefront scan of the token lengths from the piece's (chunk's) start
 template <bool SPANS>
-__device__ void copy_long(EmitSmem &sm, const uint8_t *ws, const Layout &L, uint32_t p, uint32_t a, uint32_t len,
-                          uint32_t o, uint32_t c, uint32_t *out_ids, uint32_t *out_spans, const uint32_t *tok_len)
+__device__ void copy_long(const uint8_t *ws, const Layout &L, uint32_t p, uint32_t a, uint32_t len, uint32_t o,
+                          uint32_t c, uint32_t *out_ids, uint32_t *out_spans, const uint32_t *tok_len)
 {
+    const uint32_t lane = threadIdx.x & 63u;
     const uint32_t *scratch = (const uint32_t *)(ws + L.scratch);
     uint32_t g = NO_PIECE, nc = 1, c0 = 0;
     if (len > (uint32_t)BLOCK_MAX) g = giant_index(ws, L, p);   // (always listed: the pieces kernel lists by length)
@@ -541,42 +571,57 @@ __device__ void copy_long(EmitSmem &sm, const uint8_t *ws, const Layout &L, uint
     }
     for (uint32_t k = 0; k < nc; ++k) {
         const uint32_t *src;
-        uint32_t dst, cnt, sp0;
+        uint32_t dst, cnt, carry;
         if (g == NO_PIECE) {
             src = scratch + a;
             dst = o;
             cnt = c;
-            sp0 = a;
+            carry = a;
         } else {
             const uint32_t ck = c0 + k;
             const uint32_t cs = ((const uint32_t *)(ws + L.cstart))[ck];
             src = scratch + cs;
             dst = o + ((const uint32_t *)(ws + L.clen))[ck];   // the chunk's place in the piece's output
             cnt = ((const uint32_t *)(ws + L.ccount))[ck];
-            sp0 = cs;
+            carry = cs;
         }
-        if (!SPANS) {
-            for (uint32_t t = threadIdx.x; t < cnt; t += NT) out_ids[dst + t] = src[t];
-            continue;
-        }
-        uint32_t carry = sp0;
-        for (uint32_t t0 = 0; t0 < cnt; t0 += NT) {
-            const uint32_t t = t0 + threadIdx.x;
+        for (uint32_t t0 = 0; t0 < cnt; t0 += 64) {
+            const uint32_t t = t0 + lane;
             const uint32_t id = t < cnt ? src[t] : 0u;
-            const uint32_t l = t < cnt ? tok_len[id] : 0u;
-            uint32_t tot;
-            const uint32_t ex = wg_excl_sum(sm, l, &tot);
-            if (t < cnt) {
-                out_ids[dst + t] = id;
-                out_spans[dst + t] = carry + ex;
+            if (t < cnt) out_ids[dst + t] = id;
+            if (SPANS) {
+                const uint32_t l = t < cnt ? tok_len[id] : 0u;
+                const uint32_t inc = wave_incl_sum(l);
+                if (t < cnt) out_spans[dst + t] = carry + inc - l;
+                carry += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
             }
-            carry += tot;
         }
     }
 }
 
 }  // namespace
 
+// key of a 2..7-byte piece at window offset j: its bytes (little-endian) | len << 56
+template <typename S>
+__device__ __forceinline__ uint64_t short_key(const S &sm, uint32_t j, uint32_t len)
+{
+    const uint32_t q0 = j >> 2, sh = j & 3u;
+    const uint32_t x0 = sm.win[q0], x1 = sm.win[q0 + 1], x2 = sm.win[q0 + 2];
+    const uint32_t lo = sh ? __builtin_amdgcn_alignbyte(x1, x0, sh) : x0;
+    const uint32_t hi = sh ? __builtin_amdgcn_alignbyte(x2, x1, sh) : x1;
+    const uint64_t w = (uint64_t)lo | ((uint64_t)hi << 32);
+    return (w & ((1ull << (8u * len)) - 1ull)) | ((uint64_t)len << 56);
+}
+
+// Resolve pass over the tile's pieces.  Each piece, by length:
+//   1 byte          its own ID
+//   2..7 bytes      the hot sets in LDS (the lowest token IDs), else: 2 bytes the byte-pair rank
+//                   table (one merge or none decides it; ignore_merges vocabularies look them up like
+//                   3..7 bytes), 3..7 bytes the short whole-piece table (four pieces per thread with
+//                   their loads in flight)
+//   8..32 bytes     listed in the tile's slice of a second list, probed in a second compact pass
+//   33..128 bytes   (and table misses) listed in the tile's slice of the BPE list
+//   longer          encoded before this kernel: its result word is read
 template <bool IGN>
 __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restrict__ bytes, uint64_t n, uint8_t *ws,
                                               Layout L)
@@ -585,64 +630,150 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
     const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *__restrict__ tbase = (const uint32_t *)(ws + L.tbase);
     uint32_t *pval = (uint32_t *)(ws + L.pval);
+    uint32_t *scratch = (uint32_t *)(ws + L.scratch);
     const uint32_t tid = threadIdx.x;
     const uint32_t tile = blockIdx.x;
     const uint64_t lo = (uint64_t)tile * TILE;
-    const uint32_t p0 = tbase[tile], p1 = tbase[tile + 1];
-
-    load_window(sm, bytes, n, lo);
-    if (tid == 0) sm.qn = 0;
-    __syncthreads();
+    const uint32_t p0 = tbase[tile], p1 = tbase[tile + 1], cnt = p1 - p0;
     uint32_t *mlist = (uint32_t *)(ws + L.mlist) + p0;
+    uint32_t *llist = (uint32_t *)(ws + L.tokoff) + p0;   // the 8..32-byte pieces
 
-    // two pieces per thread in flight; the misses go to the tile's slice of the BPE list
+    // the window and the hot sets (their loads issued together)
+    {
+        constexpr int PH = HOT_SLOTS / NT;
+        uint4 h[PH];
+#pragma unroll
+        for (int k = 0; k < PH; ++k) h[k] = v.hot ? v.hot[tid + k * NT] : make_uint4(0u, 0u, 0u, 0u);
+        load_window(sm, bytes, n, lo);
+#pragma unroll
+        for (int k = 0; k < PH; ++k) sm.hot[tid + k * NT] = h[k];
+    }
+    if (tid == 0) {
+        sm.qn = 0;
+        sm.ln = 0;
+    }
+    __syncthreads();
+    auto list_miss = [&](uint32_t i, uint32_t len) { mlist[atomicAdd(&sm.qn, 1u)] = i | (len << 16); };
+
     uint32_t mytok = 0;
-    for (uint32_t b0 = p0; b0 < p1; b0 += 2 * NT) {
-        uint32_t pp[2], a[2], len[2], id[2], st[2];
-        WPQ q[2];
-        enum : uint32_t { S_DONE = 0, S_HIT = 1, S_MORE = 2, S_MISS = 3, S_LONG = 4 };
+    constexpr int K = 4;
+    for (uint32_t i0 = 0; i0 < cnt; i0 += K * NT) {
+        uint32_t a[K], e[K];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            pp[u] = b0 + u * NT + tid;
-            const bool ok = pp[u] < p1;
-            a[u] = ok ? pstart[pp[u]] : 0u;
-            len[u] = ok ? pstart[pp[u] + 1] - a[u] : 0u;
-            id[u] = 0;
-            q[u] = WPQ{0, 0, 0, 0, 0, 0, 0};
-            if (!ok) st[u] = S_DONE;
-            else if (len[u] > (uint32_t)SHORT_MAX) st[u] = S_LONG;
-            else if (len[u] == 1) { st[u] = S_HIT; id[u] = win_byte(sm, (uint32_t)(a[u] - lo)); }
-            else if (len[u] <= (uint32_t)TABLE_MAX) {
-                q[u] = wp_make_win(v, sm, (uint32_t)(a[u] - lo), len[u]);
-                st[u] = q[u].kind ? S_MORE : S_MISS;
-            } else st[u] = S_MISS;
+        for (int u = 0; u < K; ++u) {
+            const uint32_t i = i0 + u * NT + tid;
+            a[u] = i < cnt ? pstart[p0 + i] : 0u;
+            e[u] = i < cnt ? pstart[p0 + i + 1] : 0u;
         }
-        for (;;) {
-            bool more = false;
+        // kind: 0 nothing to load, 2 byte pair, 3 short table (both candidate slots)
+        uint32_t kind[K], si[K], sj[K];
+        uint64_t key[K];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                if (st[u] == S_MORE) {
-                    const uint32_t r = wp_step(v, q[u], &id[u]);
-                    st[u] = r == WP_HIT ? S_HIT : (r == WP_MISS ? S_MISS : S_MORE);
-                }
-                more |= st[u] == S_MORE;
-            }
-            if (!more) break;
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if (IGN && st[u] == S_MISS && len[u] > (uint32_t)TABLE_MAX && len[u] <= v.lmax) {
-                const uint32_t w = whole_token(v, bytes + a[u], len[u]);
-                if (w != NO_PIECE) { st[u] = S_HIT; id[u] = w; }
-            }
-            if (st[u] == S_HIT) {
-                pval[pp[u]] = id[u];
+        for (int u = 0; u < K; ++u) {
+            const uint32_t i = i0 + u * NT + tid;
+            kind[u] = 0;
+            si[u] = 0;
+            sj[u] = 0;
+            key[u] = 0;
+            if (i >= cnt) continue;
+            const uint32_t j = a[u] - (uint32_t)lo, len = e[u] - a[u];
+            if (len == 1) {
+                pval[p0 + i] = win_byte(sm, j);
                 ++mytok;
-            } else if (st[u] == S_LONG) {
-                mytok += pval[pp[u]] & PV_COUNT;   // written by the long-piece kernels
-            } else if (st[u] == S_MISS) {
-                mlist[atomicAdd(&sm.qn, 1u)] = (pp[u] - p0) | (len[u] << 16);
+            } else if (len <= WA_MAX) {
+                key[u] = short_key(sm, j, len);
+                const uint32_t set = hot_set(key[u]);
+                const uint4 h0 = sm.hot[2 * set], h1 = sm.hot[2 * set + 1];
+                const uint64_t k0 = (uint64_t)h0.x | ((uint64_t)h0.y << 32), k1 = (uint64_t)h1.x | ((uint64_t)h1.y << 32);
+                if (k0 == key[u] || k1 == key[u]) {
+                    pval[p0 + i] = k0 == key[u] ? h0.z : h1.z;
+                    ++mytok;
+                } else if (len == 2 && !IGN) {
+                    kind[u] = 2;
+                    si[u] = (win_byte(sm, j) << 8) | win_byte(sm, j + 1);
+                } else if (v.wa) {
+                    kind[u] = 3;
+                    ck_slots(key[u], v.wseed, v.wa_cap, si[u], sj[u]);
+                } else {
+                    list_miss(i, len);
+                }
+            } else if (len <= (uint32_t)TABLE_MAX) {
+                llist[atomicAdd(&sm.ln, 1u)] = i | (len << 16);
+            } else if (len <= (uint32_t)SHORT_MAX) {
+                uint32_t w = NO_PIECE;
+                if (IGN && len <= v.lmax) w = whole_token(v, bytes + a[u], len);
+                if (w != NO_PIECE) {
+                    pval[p0 + i] = w;
+                    ++mytok;
+                } else {
+                    list_miss(i, len);
+                }
+            } else {
+                mytok += pval[p0 + i] & PV_COUNT;   // written by the long-piece kernels
             }
+        }
+        // the global lookups of the pieces the hot sets did not answer: all loads in flight at once
+        uint4 x[K], y[K];
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            if (kind[u] == 2) {
+                x[u] = make_uint4(__ldg(v.r2 + si[u]), 0u, 0u, 0u);
+                y[u] = make_uint4(0u, 0u, 0u, 0u);
+            } else if (kind[u] == 3) {
+                x[u] = v.wa[si[u]];
+                y[u] = v.wa[sj[u]];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            const uint32_t i = i0 + u * NT + tid;
+            if (kind[u] == 2) {
+                const uint32_t r = x[u].x;
+                if (r != NO_RANK) {
+                    pval[p0 + i] = 256u + r;
+                    ++mytok;
+                } else {   // no merge joins the two bytes: two tokens
+                    pval[p0 + i] = PV_MULTI | 2u;
+                    scratch[a[u]] = si[u] >> 8;
+                    scratch[a[u] + 1] = si[u] & 255u;
+                    mytok += 2;
+                }
+            } else if (kind[u] == 3) {
+                const uint64_t ka = (uint64_t)x[u].x | ((uint64_t)x[u].y << 32);
+                const uint64_t kb = (uint64_t)y[u].x | ((uint64_t)y[u].y << 32);
+                if (ka == key[u] || kb == key[u]) {
+                    pval[p0 + i] = ka == key[u] ? x[u].z : y[u].z;
+                    ++mytok;
+                } else {
+                    list_miss(i, (uint32_t)(key[u] >> 56));
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // 8..32-byte pieces, compacted: the long whole-piece table
+    const uint32_t nl = sm.ln;
+    for (uint32_t k = tid; k < nl; k += NT) {
+        const uint32_t ent = llist[k];
+        const uint32_t i = ent & 0xFFFFu, len = ent >> 16, j = pstart[p0 + i] - (uint32_t)lo;
+        uint64_t k4[4];
+        win_words<4>(sm, j, len, k4);
+        bool hit = false;
+        uint32_t id = 0;
+        if (v.wb) {
+            uint32_t ci, cj;
+            ck_slots(wb_digest(k4[0], k4[1], k4[2], k4[3], len), v.bseed, v.wb_cap, ci, cj);
+            const uint4 *ep = v.wb + 3ull * ci, *fp = v.wb + 3ull * cj;
+            const uint4 a0 = ep[0], a1 = ep[1], a2 = ep[2], b0 = fp[0], b1 = fp[1], b2 = fp[2];
+            if (wb_match(a0, a1, a2, k4[0], k4[1], k4[2], k4[3], len)) { hit = true; id = a2.y; }
+            else if (wb_match(b0, b1, b2, k4[0], k4[1], k4[2], k4[3], len)) { hit = true; id = b2.y; }
+        }
+        if (hit) {
+            pval[p0 + i] = id;
+            ++mytok;
+        } else {
+            list_miss(i, len);
         }
     }
 
@@ -703,15 +834,35 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
     const uint32_t tile = blockIdx.x;
     const uint64_t lo = (uint64_t)tile * TILE;
     const uint64_t hi = min(lo + (uint64_t)TILE, n);
-    const uint32_t p0 = tbase[tile], p1 = tbase[tile + 1];
-    if (tid == 0) sm.nlong = 0;
+    const uint32_t p0 = tbase[tile], p1 = tbase[tile + 1], cnt = p1 - p0;
+    // wavefront wid owns pieces [qb, qe) of the tile (a multiple of 64 each)
+    const uint32_t Q = ((cnt + NW - 1) / NW + 63u) & ~63u;
+    const uint32_t qb = p0 + min(cnt, wid * Q), qe = p0 + min(cnt, (wid + 1) * Q);
+    auto count_of = [](uint32_t pv) -> uint32_t { return (pv & PV_MULTI) ? (pv & PV_COUNT) : 1u; };
+
     for (uint32_t i = tid; i < TILE / 32; i += NT) sm.docbits[i] = 0;
-    // first output index: the groups of 64 tiles before this tile's group, then the tiles before it
-    // in its group (counts are final: every kernel that adds to them has finished)
+    // tokens of this wavefront's pieces (all loads in flight, four per lane per step)
+    {
+        uint32_t x = 0;
+        for (uint32_t r = qb; r < qe; r += 256) {
+            uint32_t pv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t p = r + 64u * u + lane;
+                pv[u] = p < qe ? pval[p] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x += r + 64u * u + lane < qe ? count_of(pv[u]) : 0u;
+        }
+        x = wave_incl_sum(x);
+        if (lane == 63) sm.wsum[wid] = x;
+    }
+    // first output index of the tile: the groups of 64 tiles before its group, then the tiles before
+    // it in its group (counts are final: every kernel that adds to them has finished)
     if (wid == 0) {
         const uint32_t g = tile / 64u;
         uint32_t x = 0;
-        for (uint32_t s = lane; s < g; s += 64) x += tsb[s];
+        for (uint32_t t = lane; t < g; t += 64) x += tsb[t];
         if (64 * g + lane < tile) x += tcount[64 * g + lane];
         x = wave_incl_sum(x);
         if (lane == 63) sm.base = x;
@@ -723,18 +874,33 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
         const uint64_t od = offsets[d];
         if (od >= lo && od < hi) atomicOr(&sm.docbits[(od - lo) >> 5], 1u << ((od - lo) & 31u));
     }
+    uint32_t run = sm.base;
+    for (uint32_t w = 0; w < wid; ++w) run += sm.wsum[w];
     __syncthreads();
 
+    // rounds of 64 pieces per wavefront: a DPP scan of their counts places their IDs (the loads of
+    // four rounds in flight at once)
     const uint32_t *tok_len = v.tok_len;
-    uint32_t run = sm.base;
-    for (uint32_t r0 = p0; r0 < p1; r0 += NT) {
-        const uint32_t p = r0 + tid;
-        const bool ok = p < p1;
-        const uint32_t pv = ok ? pval[p] : 0u;
-        const uint32_t a = ok ? pstart[p] : 0u;
-        const uint32_t c = !ok ? 0u : ((pv & PV_MULTI) ? (pv & PV_COUNT) : 1u);
-        uint32_t rtot;
-        const uint32_t o = run + wg_excl_sum(sm, c, &rtot);
+    for (uint32_t r4 = qb; r4 < qe; r4 += 256) {
+      uint32_t pv4[4], a4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+          const uint32_t p = r4 + 64u * u + lane;
+          pv4[u] = p < qe ? pval[p] : 0u;
+          a4[u] = p < qe ? pstart[p] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t r = r4 + 64u * u;
+        if (r >= qe) break;
+        const uint32_t p = r + lane;
+        const bool ok = p < qe;
+        const uint32_t pv = pv4[u];
+        const uint32_t a = a4[u];
+        const uint32_t c = ok ? count_of(pv) : 0u;
+        const uint32_t inc = wave_incl_sum(c);
+        const uint32_t o = run + inc - c;
+        run += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
         if (ok) {
             if (!(pv & PV_MULTI)) {
                 out_ids[o] = pv;
@@ -749,10 +915,6 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
                         sp += tok_len[x];
                     }
                 }
-            } else {
-                const uint32_t k = atomicAdd(&sm.nlong, 1u);
-                sm.longp[k] = p;
-                sm.longo[k] = o;
             }
             // documents that start with this piece (every document offset below n is a piece start)
             const uint32_t j = (uint32_t)(a - lo);
@@ -765,20 +927,21 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
                 for (uint32_t d = lo_d; d < dd.y && offsets[d] == a; ++d) out_offsets[d] = o;
             }
         }
-        __syncthreads();
-        const uint32_t nl = sm.nlong;
-        for (uint32_t k = 0; k < nl; ++k) {
-            const uint32_t lp = sm.longp[k];
-            const uint32_t la = pstart[lp];
-            copy_long<SPANS>(sm, ws, L, lp, la, pstart[lp + 1] - la, sm.longo[k], pval[lp] & PV_COUNT, out_ids, out_spans,
-                             tok_len);
+        // long pieces of this round: copied by the whole wavefront, one after the other
+        uint64_t lm = __ballot(ok && (pv & PV_LONG));
+        while (lm) {
+            const int k = __ffsll((unsigned long long)lm) - 1;
+            lm &= lm - 1;
+            const uint32_t lp = (uint32_t)__builtin_amdgcn_readlane((int)p, k);
+            const uint32_t la = (uint32_t)__builtin_amdgcn_readlane((int)a, k);
+            const uint32_t lo_ = (uint32_t)__builtin_amdgcn_readlane((int)o, k);
+            const uint32_t lc = (uint32_t)__builtin_amdgcn_readlane((int)c, k);
+            copy_long<SPANS>(ws, L, lp, la, pstart[lp + 1] - la, lo_, lc, out_ids, out_spans, tok_len);
         }
-        __syncthreads();
-        if (tid == 0) sm.nlong = 0;
-        run += rtot;
+      }
     }
     // the last tile: documents that start at the end of the batch (empty ones), the total
-    if (tile == L.n_tiles - 1 && wid == 0) {
+    if (tile == L.n_tiles - 1 && wid == NW - 1) {
         const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, (uint64_t)n);
         for (uint32_t d = d0 + lane; d <= n_docs; d += 64) out_offsets[d] = run;
         if (lane == 0) ctrl->n_tokens = run;

@@ -9,6 +9,7 @@
 #include <vector>
 #include <algorithm>
 #include <mutex>
+#include <array>
 
 #include "../../include/toktier.h"
 #include "internal.h"
@@ -313,6 +314,47 @@ void build_tables(int fam, uint64_t *fmap, uint32_t *fstart)
                 }
 }
 
+// Two-choice cuckoo placement of n items into `cap` slots (candidate slots from ck_slots with `seed`):
+// an item goes to a free candidate slot, else it takes one and the item there moves to its other
+// candidate, and so on.  where[slot] = item + 1 (0: free).  False when an eviction chain runs too long
+// (the caller retries with another seed, then a larger table).
+template <typename Digest>
+bool cuckoo_place(uint32_t n, uint32_t cap, uint64_t seed, Digest digest, std::vector<uint32_t> &where)
+{
+    where.assign(cap, 0);
+    for (uint32_t it = 0; it < n; ++it) {
+        uint32_t cur = it, i, j;
+        ck_slots(digest(cur), seed, cap, i, j);
+        uint32_t pos = where[i] == 0 ? i : (where[j] == 0 ? j : i);
+        for (int kick = 0;; ++kick) {
+            if (where[pos] == 0) {
+                where[pos] = cur + 1;
+                break;
+            }
+            if (kick >= 1000) return false;
+            const uint32_t out = where[pos] - 1;
+            where[pos] = cur + 1;
+            cur = out;
+            ck_slots(digest(cur), seed, cap, i, j);
+            if (i == j) return false;
+            pos = pos == i ? j : i;
+        }
+    }
+    return true;
+}
+
+// a table of at most about 45 % load for n items, placed; returns its capacity and seed
+template <typename Digest>
+void cuckoo_build(uint32_t n, uint64_t salt, Digest digest, std::vector<uint32_t> &where, uint32_t &cap, uint64_t &seed)
+{
+    cap = (uint32_t)std::max<uint64_t>(64, (uint64_t)n * 20 / 9 + 1);
+    for (uint32_t attempt = 1;; ++attempt) {
+        seed = ck_mix(salt + 0x9E3779B97F4A7C15ull * attempt);
+        if (cuckoo_place(n, cap, seed, digest, where)) return;
+        if (attempt % 4 == 0) cap = (uint32_t)((uint64_t)cap * 9 / 8 + 1);
+    }
+}
+
 // valid UTF-8 in the sense the pre-tokenizer checks: no overlong forms, surrogates or code points
 // above U+10FFFF, no truncated or stray sequences
 bool valid_utf8(const uint8_t *s, uint32_t n)
@@ -556,44 +598,69 @@ int fill_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts, const std:
         if (pv[i] != cand[i]) continue;   // not self-reachable: BPE of its bytes is not [token]
         (len[cand[i]] <= WA_MAX ? short_t : long_t).push_back(cand[i]);
     }
-    // at most an eighth of the slots used: a wavefront's table step waits for the longest probe chain
-    // of its 128 pieces, and sparse tables keep that chain near one read (measured on MI355X, 18.4 MB
-    // batch: twice the entries 64 us, four times 59 us, eight times 56 us; 1.25 times 126 us)
-    uint32_t la = 10, lb = 10;
-    while ((1ull << la) < 8ull * short_t.size()) ++la;
-    while ((1ull << lb) < 8ull * long_t.size()) ++lb;
-    const uint64_t ca = 1ull << la, cb = 1ull << lb;
-    std::vector<uint32_t> wa(4 * ca, 0), wb(12 * cb, 0);
-    for (uint32_t t : short_t) {
+    // two-choice cuckoo tables, under half full (both candidate slots are read in one round trip)
+    std::vector<uint64_t> akeys(short_t.size());
+    for (size_t i = 0; i < short_t.size(); ++i) {
+        const uint32_t t = short_t[i];
         uint64_t key = (uint64_t)len[t] << 56;
         for (uint32_t k = 0; k < len[t]; ++k) key |= (uint64_t)tb[off[t] + k] << (8 * k);
-        uint64_t h = wa_hash(key, 64 - la);
-        while (wa[4 * h] || wa[4 * h + 1]) h = (h + 1) & (ca - 1);
-        wa[4 * h] = (uint32_t)key;
-        wa[4 * h + 1] = (uint32_t)(key >> 32);
-        wa[4 * h + 2] = t;
+        akeys[i] = key;
     }
-    for (uint32_t t : long_t) {
-        uint64_t k4[4] = {0, 0, 0, 0};
+    std::vector<std::array<uint64_t, 4>> bkeys(long_t.size());
+    for (size_t i = 0; i < long_t.size(); ++i) {
+        const uint32_t t = long_t[i];
+        std::array<uint64_t, 4> k4 = {0, 0, 0, 0};
         for (uint32_t k = 0; k < len[t]; ++k) k4[k >> 3] |= (uint64_t)tb[off[t] + k] << (8 * (k & 7));
-        uint64_t h = wb_hash(k4[0], k4[1], k4[2], k4[3], len[t], 64 - lb);
-        while (wb[12 * h + 8]) h = (h + 1) & (cb - 1);
+        bkeys[i] = k4;
+    }
+    std::vector<uint32_t> wa_where, wb_where;
+    uint32_t ca = 0, cb = 0;
+    uint64_t sa = 0, sb = 0;
+    cuckoo_build((uint32_t)short_t.size(), 0x5A17ull, [&](uint32_t i) { return akeys[i]; }, wa_where, ca, sa);
+    cuckoo_build((uint32_t)long_t.size(), 0xB16Bull,
+                 [&](uint32_t i) { return wb_digest(bkeys[i][0], bkeys[i][1], bkeys[i][2], bkeys[i][3], len[long_t[i]]); },
+                 wb_where, cb, sb);
+    std::vector<uint32_t> wa(4ull * ca, 0), wb(12ull * cb, 0);
+    for (uint32_t h = 0; h < ca; ++h) {
+        if (!wa_where[h]) continue;
+        const uint32_t i = wa_where[h] - 1;
+        wa[4 * h] = (uint32_t)akeys[i];
+        wa[4 * h + 1] = (uint32_t)(akeys[i] >> 32);
+        wa[4 * h + 2] = short_t[i];
+    }
+    for (uint32_t h = 0; h < cb; ++h) {
+        if (!wb_where[h]) continue;
+        const uint32_t i = wb_where[h] - 1;
         for (int w = 0; w < 4; ++w) {
-            wb[12 * h + 2 * w] = (uint32_t)k4[w];
-            wb[12 * h + 2 * w + 1] = (uint32_t)(k4[w] >> 32);
+            wb[12ull * h + 2 * w] = (uint32_t)bkeys[i][w];
+            wb[12ull * h + 2 * w + 1] = (uint32_t)(bkeys[i][w] >> 32);
         }
-        wb[12 * h + 8] = len[t];
-        wb[12 * h + 9] = t;
+        wb[12ull * h + 8] = len[long_t[i]];
+        wb[12ull * h + 9] = long_t[i];
+    }
+    // the hot sets: the short entries in ID order, each into a free way of its set
+    std::vector<uint32_t> hot(4ull * HOT_SLOTS, 0);
+    for (size_t i = 0; i < short_t.size(); ++i) {
+        const uint32_t set = hot_set(akeys[i]);
+        for (uint32_t w = 0; w < 2; ++w) {
+            uint32_t *e = &hot[4ull * (2 * set + w)];
+            if (e[0] | e[1]) continue;
+            e[0] = (uint32_t)akeys[i];
+            e[1] = (uint32_t)(akeys[i] >> 32);
+            e[2] = short_t[i];
+            break;
+        }
     }
     void *d = nullptr;
-    const uint64_t bytes_a = 16 * ca, bytes_b = 48 * cb;
-    hipError_t e = hipMalloc(&d, bytes_a + bytes_b);
+    const uint64_t bytes_a = 16ull * ca, bytes_b = 48ull * cb, bytes_h = 16ull * HOT_SLOTS;
+    hipError_t e = hipMalloc(&d, bytes_a + bytes_b + bytes_h);
     if (e != hipSuccess) {
         hip_fail(e);
         return TOKTIER_E_OOM;
     }
     e = hipMemcpy(d, wa.data(), bytes_a, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy((uint8_t *)d + bytes_a, wb.data(), bytes_b, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy((uint8_t *)d + bytes_a + bytes_b, hot.data(), bytes_h, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
         (void)hipFree(d);
         return hip_fail(e);
@@ -601,10 +668,11 @@ int fill_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts, const std:
     v->dwords = d;
     v->dv.wa = (const uint4 *)d;
     v->dv.wb = (const uint4 *)((uint8_t *)d + bytes_a);
-    v->dv.wa_mask = (uint32_t)(ca - 1);
-    v->dv.wa_shift = 64 - la;
-    v->dv.wb_mask = (uint32_t)(cb - 1);
-    v->dv.wb_shift = 64 - lb;
+    v->dv.hot = (const uint4 *)((uint8_t *)d + bytes_a + bytes_b);
+    v->dv.wa_cap = ca;
+    v->dv.wseed = sa;
+    v->dv.wb_cap = cb;
+    v->dv.bseed = sb;
     return TOKTIER_OK;
 }
 
@@ -671,26 +739,27 @@ extern "C" int toktier_load_vocab_ex(const uint32_t *merges, uint32_t n_merges, 
             ++n_general;
         }
     }
-    // pair hash: single 8-byte slots, linear probing, at most one slot in 32 used.  A merge round of a
-    // wavefront waits for the longest probe chain of its lanes; the sparser the table, the shorter
-    // that chain (small-piece BPE launch on the 18.4 MB batch, MI355X: 64-byte buckets of 8 slots at
-    // half load 83 us; single slots, an eighth used 72 us, a sixteenth 67 us, a 32nd 62 us)
-    uint32_t log2cap = 10;
-    while ((1ull << log2cap) < 32ull * n_general) ++log2cap;
-    const uint64_t cap = 1ull << log2cap;
-    std::vector<uint64_t> slots(cap, EMPTY_SLOT);
-    const uint32_t shift = 64 - log2cap;
+    // pair table: two-choice cuckoo, under half full (both candidate slots read in one round trip)
+    std::vector<uint64_t> pkeys;
+    pkeys.reserve(n_general);
     for (uint32_t r = 0; r < n_merges; ++r) {
-        uint32_t a = merges[2 * r], b = merges[2 * r + 1];
-        if ((a | b) < 256u) continue;
-        uint64_t key = ((uint64_t)a << 21) | b;
-        uint64_t h = (key * 0x9E3779B97F4A7C15ull) >> shift;
-        for (;; h = (h + 1) & (cap - 1)) {
-            uint64_t &sl = slots[h];
-            if (sl == EMPTY_SLOT) { sl = (key << 21) | r; break; }
-            if ((sl >> 21) == key) return TOKTIER_E_BAD_MERGES;      // duplicate pair
-        }
+        const uint32_t a = merges[2 * r], b = merges[2 * r + 1];
+        if ((a | b) >= 256u) pkeys.push_back((((uint64_t)a << 21) | b) << 21 | r);
     }
+    {
+        std::vector<uint64_t> ks(pkeys.size());
+        for (size_t i = 0; i < pkeys.size(); ++i) ks[i] = pkeys[i] >> 21;
+        std::sort(ks.begin(), ks.end());
+        if (std::adjacent_find(ks.begin(), ks.end()) != ks.end()) return TOKTIER_E_BAD_MERGES;   // duplicate pair
+    }
+    std::vector<uint32_t> pwhere;
+    uint32_t pcap = 0;
+    uint64_t pseed = 0;
+    cuckoo_build((uint32_t)pkeys.size(), 0x7A1Bull, [&](uint32_t i) { return pkeys[i] >> 21; }, pwhere, pcap, pseed);
+    const uint64_t cap = pcap;
+    std::vector<uint64_t> slots(cap, EMPTY_SLOT);
+    for (uint32_t h = 0; h < pcap; ++h)
+        if (pwhere[h]) slots[h] = pkeys[pwhere[h] - 1];
     uint64_t fmap[NCTX_MAX] = {};
     uint32_t fstart[NCTX_MAX] = {};
     build_tables(family, fmap, fstart);
@@ -742,13 +811,14 @@ extern "C" int toktier_load_vocab_ex(const uint32_t *merges, uint32_t n_merges, 
     v->dv.slots = (const uint64_t *)(base + o_slots);
     v->dv.merges = (const uint32_t *)(base + o_merges);
     v->dv.fmap16 = (const uint4 *)(base + o_fmap);
-    v->dv.mask = (uint32_t)(cap - 1);
-    v->dv.shift = shift;
+    v->dv.slot_cap = pcap;
+    v->dv.pseed = pseed;
     v->dv.n_merges = n_merges;
     v->dv.family = family;
     v->dv.flags = (flags & TOKTIER_IGNORE_MERGES) ? VF_IGNORE_MERGES : 0u;
     v->dv.wa = nullptr;
     v->dv.wb = nullptr;
+    v->dv.hot = nullptr;
     v->dv.str = nullptr;
     v->dv.tok_off = nullptr;
     v->dv.tok_bytes = nullptr;
