@@ -46,7 +46,7 @@ LATENCY = ("c1_ec4k", "c2_at100k", "c3_mix1m", "c5_adv4m4")
 # input bytes each kernel launch processes (the unit of the algorithmic-bytes figure)
 # (bytes of the pieces in the length range the launch serves)
 UNITS = {
-    "summary": "all", "pieces": "all", "tiles": "all", "emit": "all", "bpe_tiles": "le128", "giant_seams": "giant", "bpe_chunks": "giant",
+    "summary": "all", "pieces": "all", "tiles": "all", "emit": "all", "bpe_short": "le128", "giant_seams": "giant",
     "bpe_wave": "wave", "bpe_block": "block", "bpe_giant": "giant",
 }
 

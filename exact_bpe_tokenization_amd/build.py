@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtoktier.so")
-SOURCES = ["pretok.hip", "bpe.hip", "tiles.hip", "compact.hip", "added.hip", "toktier.hip", "repair.hip"]
+SOURCES = ["pretok.hip", "bpe.hip", "tiles.hip", "added.hip", "toktier.hip", "repair.hip"]
 ARCH = "gfx950"
 
 

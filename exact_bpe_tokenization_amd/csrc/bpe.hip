@@ -7,21 +7,23 @@
 // that pair equals iterated single merges (for rank-consistent merge lists, which the loader
 // enforces); only pairs next to a completed merge need a new lookup.
 //
-//   k_route      every piece: a single byte is its ID, a whole-piece table hit is its result; the
-//                others are listed by length
+//   k_route      (vocabulary load) every piece: a single byte is its ID, a whole-piece table hit
+//                is its result; the others are listed by length (the tile encoder does the same for
+//                the encode chain)
 //   k_bpe_small  the lists of pieces up to 128 bytes, one launch with a workgroup range per list:
-//                <= 16 bytes, one lane per piece (sorted by length per workgroup), the textbook loop
-//                in registers (leftmost lowest rank, merge, re-probe the two neighbours);
-//                17..32 bytes, 16 lanes x 2 rows per piece, four pieces per wavefront; 33..64 bytes,
-//                64 lanes per piece; 65..128 bytes, a wavefront with two elements per lane: rounds
-//                on ballot masks (see the kernels)
+//                <= 8, 9..12, 13..16 and 17..32 bytes, one lane per piece and 64 consecutive list
+//                items per wavefront, the textbook loop over an LDS row per lane (leftmost lowest rank,
+//                merge, re-probe the two neighbours); 33..64 bytes, 64 lanes per piece; 65..128
+//                bytes, a wavefront with two elements per lane: rounds on ballot masks (see the
+//                kernels)
 //   k_bpe_block  one wavefront (pieces of 129..1024 bytes) or one 256-lane workgroup (up to 4096
 //                bytes) per piece; sequence in LDS; rounds: block-min of ranks, selection of the
 //                leftmost non-overlapping occurrences, prefix-sum compaction, neighbour re-probes
 //   k_bpe_giant  one 1024-lane workgroup per piece longer than that; the same rounds over device
 //                memory (double-buffered)
 // Every kernel writes the piece's result word (a single ID, or the count of IDs it stored at
-// scratch[piece start byte ...]; a piece never has more IDs than bytes).
+// scratch[piece start byte ...]; a piece never has more IDs than bytes) and adds its token count to
+// the counters of its input tile (tcount) and of that tile's group of 64 tiles (tsb).
 #include "internal.h"
 
 namespace tt {
@@ -38,8 +40,8 @@ constexpr uint32_t PENDING = 0xFFFFFFFEu;
 // to the global list).
 constexpr int RT_THREADS = 512;
 constexpr int RT_PPT = 2;   // pieces per thread in flight (more costs occupancy: slower)
-constexpr uint32_t RTQ[NROUTES] = {2048, 512, 256, 128, 64, 64, 64};
-constexpr uint32_t RTQ_OFF[NROUTES + 1] = {0, 2048, 2560, 2816, 2944, 3008, 3072, 3136};
+constexpr uint32_t RTQ[NROUTES] = {1024, 512, 256, 256, 64, 64, 64, 64, 64};
+constexpr uint32_t RTQ_OFF[NROUTES + 1] = {0, 1024, 1536, 1792, 2048, 2112, 2176, 2240, 2304, 2368};
 
 // IGN: the vocabulary ignores merges (pieces longer than the whole-piece tables are looked up in the
 // token string hash); a template flag so that the usual instantiation carries none of that code
@@ -117,87 +119,112 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t 
 }
 
 // ---------------------------------------------------------------------------------------------
-// lane per piece (unresolved pieces of <= 16 bytes)
+// lane per piece (unresolved pieces of <= 32 bytes)
 
-// One item per lane, sequence and pair ranks in registers (MAXL elements): the textbook loop --
-// merge the leftmost pair of lowest rank, shift the tail left, re-probe the two neighbours.  Called
-// by all 64 lanes of a wavefront (the token-count update is a wavefront operation); len 0 = idle.
+// One item per lane, the textbook loop: merge the leftmost pair of lowest rank, re-probe its two new
+// neighbour pairs.  The lane's sequence lives in its own LDS row at fixed byte positions: ranks in
+// words [0, 32), elements (ID | operand bits) in [32, 64), 4 words of padding so that the 16-byte
+// rank reads of 16 consecutive lanes fall on distinct banks.  A rank word is (rkx << 5) | position
+// (NO_RANK at dead positions and at the last live one), so the minimum over the row is the lowest
+// rank at its leftmost position in one pass; the live positions are a bit mask (a merge at p kills
+// the next live position q; p's neighbours are the live positions around it).  A round is one pass of
+// 16-byte LDS reads, a few bit operations, two element reads, three writes and the probes.  Called by
+// all 64 lanes of a wavefront; len 0 = idle.
+constexpr int LROW = 68;   // words per lane row
+
 template <int MAXL>
-__device__ __forceinline__ void lane_bpe(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws,
-                                         const Layout &L, uint32_t e, uint32_t b0, uint32_t len)
+__device__ __forceinline__ uint32_t lane_bpe(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws,
+                                             const Layout &L, uint32_t *row, uint32_t e, uint32_t b0, uint32_t len)
 {
+    static_assert(MAXL % 4 == 0 && MAXL <= 32, "row layout");
     uint32_t *pval = (uint32_t *)(ws + L.pval);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
     uint32_t *ccount = (uint32_t *)(ws + L.ccount);
     const bool active = len != 0;
     const bool chunk = (e & CHUNK_ITEM) != 0;
     const uint32_t p = e & ~CHUNK_ITEM;
-    uint32_t id[MAXL], rk[MAXL];
-    uint64_t w[(MAXL + 7) / 8];
-    load_words<(MAXL + 7) / 8>(bytes + b0, len, w);
+    uint32_t *el = row + 32;
+    {
+        uint64_t w[MAXL / 8 + (MAXL % 8 ? 1 : 0)];
+        load_words<MAXL / 8 + (MAXL % 8 ? 1 : 0)>(bytes + b0, len, w);
+        uint32_t c[MAXL + 1];
 #pragma unroll
-    for (int k = 0; k < MAXL; ++k) id[k] = (uint32_t)(w[k >> 3] >> (8 * (k & 7))) & 0xFFu;
+        for (int k = 0; k < MAXL; ++k) c[k] = (uint32_t)(w[k >> 3] >> (8 * (k & 7))) & 0xFFu;
+        c[MAXL] = 0;
+        uint32_t r[MAXL];
 #pragma unroll
-    for (int k = 0; k < MAXL; ++k)
-        rk[k] = (uint32_t)(k + 1) < len ? __ldg(v.r2 + ((id[k] << 8) | id[(k + 1) % MAXL])) : NO_RANK;
-    uint32_t n = len;
-    for (;;) {
-        uint32_t best = NO_RANK, pos = 0;
+        for (int k = 0; k < MAXL; ++k) r[k] = (uint32_t)(k + 1) < len ? __ldg(v.r2 + ((c[k] << 8) | c[k + 1])) : NO_RANK;
 #pragma unroll
-        for (int k = 0; k < MAXL - 1; ++k)
-            if (rk[k] < best) { best = rk[k]; pos = k; }
-        if (best == NO_RANK) break;
-        const uint32_t nid = 256u + best;
-        // id[pos] <- nid, drop id[pos+1], shift the tail left
-#pragma unroll
-        for (int j = 0; j < MAXL; ++j) {
-            uint32_t nx_id = j + 1 < MAXL ? id[(j + 1) % MAXL] : 0u;
-            uint32_t nx_rk = j + 1 < MAXL ? rk[(j + 1) % MAXL] : NO_RANK;
-            id[j] = (uint32_t)j < pos ? id[j] : ((uint32_t)j == pos ? nid : nx_id);
-            rk[j] = (uint32_t)j < pos ? rk[j] : nx_rk;
-        }
-        --n;
-        uint32_t left = 0, right = 0;
-#pragma unroll
-        for (int j = 0; j < MAXL; ++j) {
-            if ((uint32_t)j + 1 == pos) left = id[j];
-            if ((uint32_t)j == pos + 1) right = id[j];
-        }
-        uint32_t rl, rr;   // both neighbours' probes in one round trip (nid >= 256: no byte pair)
-        pair_rank2_general(v, left, nid, nid, right, rl, rr);
-        if (pos == 0) rl = NO_RANK;
-        if (pos + 1 >= n) rr = NO_RANK;
-#pragma unroll
-        for (int j = 0; j < MAXL; ++j) {
-            if ((uint32_t)j + 1 == pos) rk[j] = rl;
-            if ((uint32_t)j == pos) rk[j] = rr;
+        for (int k = 0; k < MAXL; k += 4) {
+            uint4 x, y;
+            x.x = r[k] == NO_RANK ? NO_RANK : (r[k] << 5) | k;
+            x.y = r[k + 1] == NO_RANK ? NO_RANK : (r[k + 1] << 5) | (k + 1);
+            x.z = r[k + 2] == NO_RANK ? NO_RANK : (r[k + 2] << 5) | (k + 2);
+            x.w = r[k + 3] == NO_RANK ? NO_RANK : (r[k + 3] << 5) | (k + 3);
+            y = make_uint4(c[k] | EL_BYTE, c[k + 1] | EL_BYTE, c[k + 2] | EL_BYTE, c[k + 3] | EL_BYTE);
+            *(uint4 *)(row + k) = x;
+            *(uint4 *)(el + k) = y;
         }
     }
-    if (n > 1 || chunk) {
+    uint32_t live = len >= 32 ? 0xFFFFFFFFu : (1u << len) - 1u;
+    for (;;) {
+        uint32_t best = NO_RANK;
 #pragma unroll
-        for (int k = 0; k < MAXL; ++k)
-            if ((uint32_t)k < n) scratch[b0 + k] = id[k];
+        for (int k = 0; k < MAXL; k += 4) {
+            const uint4 x = *(const uint4 *)(row + k);
+            best = min(best, min(min(x.x, x.y), min(x.z, x.w)));
+        }
+        if (best == NO_RANK) break;
+        const uint32_t pos = best & 31u, nid = merged_element(best >> 5);
+        const uint32_t above = ~((2u << pos) - 1u);             // positions > pos (none when pos = 31)
+        const uint32_t q = (uint32_t)__ffs(live & above) - 1u;   // the right element of the pair
+        live &= ~(1u << q);
+        const uint32_t lo = live & ((1u << pos) - 1u), hi = live & above;
+        const uint32_t l = lo ? 31u - (uint32_t)__clz(lo) : 0u, r = hi ? (uint32_t)__ffs(hi) - 1u : 0u;
+        const uint32_t idl = lo ? el[l] : 0u, idr = hi ? el[r] : 0u;
+        el[pos] = nid;
+        row[q] = NO_RANK;
+        uint32_t rl, rr;   // both neighbours' probes in one round trip (nid >= 256: no byte pair)
+        pair_rkx2(v, idl & ID_MASK, nid & ID_MASK, lo && may_merge(idl, nid), nid & ID_MASK, idr & ID_MASK,
+                  hi && may_merge(nid, idr), rl, rr);
+        if (lo) row[l] = rl == NO_RANK ? NO_RANK : (rl << 5) | l;
+        row[pos] = rr == NO_RANK ? NO_RANK : (rr << 5) | pos;
+    }
+    const uint32_t n = (uint32_t)__popc(live & (len >= 32 ? 0xFFFFFFFFu : (1u << len) - 1u));
+    if (n > 1 || chunk) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int k = 0; k < MAXL; k += 4) {
+            const uint4 x = *(const uint4 *)(el + k);
+            const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if ((uint32_t)(k + j) < len && ((live >> (k + j)) & 1u)) scratch[b0 + t++] = xs[j] & ID_MASK;
+        }
     }
     if (active && chunk) ccount[p] = n;
-    else if (active) pval[p] = n == 1 ? id[0] : (PV_MULTI | n);
+    else if (active) pval[p] = n == 1 ? el[0] & ID_MASK : (PV_MULTI | n);
+    return active ? n : 0u;
 }
 
-// The <= 16-byte list, 256 items per workgroup step.  The items are sorted by length in LDS first
-// (counting sort), so each wavefront holds items of similar length: its loop runs about as many
-// rounds as its items need merges, on arrays sized for its longest item (8, 12 or 16 elements).
+// A list of <= 32-byte items (r: <= 8, 9..12, 13..16 or 17..32 bytes, MAXL its longest), 64 consecutive
+// items per wavefront.  The tile encoder lists each tile's pieces in one run, so a wavefront's pieces
+// mostly share one or two input tiles and its token counts take that many atomics.
+template <int MAXL>
 __device__ void bpe_lane(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
-                         uint32_t blk, uint32_t nblk)
+                         uint32_t *rows, uint32_t r, uint32_t blk, uint32_t nblk)
 {
-    constexpr uint32_t NT = 256, NB = 17;   // lengths 0 (idle) .. 16
-    __shared__ uint32_t s_cnt[NB], s_e[NT], s_b0[NT], s_len[NT];
+    uint32_t *row = rows + (threadIdx.x) * LROW;
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    const uint32_t *list = (const uint32_t *)(ws + L.miss16);
-    const uint32_t count = ctrl->miss_count[0];
+    const uint32_t *list = route_list(ws, L, r);
+    const uint32_t count = ctrl->miss_count[r];
     const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
-    const uint32_t tid = threadIdx.x, lane = tid & 63u;
-    for (uint32_t q0 = blk * NT; q0 < count; q0 += nblk * NT) {   // workgroup-uniform
-        const uint32_t q = q0 + tid;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = (blk * blockDim.x + threadIdx.x) >> 6;
+    const uint32_t nwaves = (nblk * blockDim.x) >> 6;
+    for (uint32_t q0 = wave * 64u; q0 < count; q0 += nwaves * 64u) {   // wavefront-uniform
+        const uint32_t q = q0 + lane;
         uint32_t e = 0, b0 = 0, len = 0;
         if (q < count) {
             e = list[q];
@@ -205,35 +232,8 @@ __device__ void bpe_lane(const DevVocab &v, const uint8_t *__restrict__ bytes, u
             if (e & CHUNK_ITEM) { b0 = cstart[p]; len = clen[p]; }
             else { b0 = pstart[p]; len = pstart[p + 1] - b0; }
         }
-        if (tid < NB) s_cnt[tid] = 0;
-        __syncthreads();
-        const uint32_t r = atomicAdd(&s_cnt[len], 1u);
-        __syncthreads();
-        if (tid < 64) {   // exclusive scan of the length histogram
-            const uint32_t c = tid < NB ? s_cnt[tid] : 0u;
-            uint32_t x = c;
-#pragma unroll
-            for (int d = 1; d < 32; d <<= 1) {
-                const uint32_t y = __shfl_up(x, d, 64);
-                if (lane >= (uint32_t)d) x += y;
-            }
-            if (tid < NB) s_cnt[tid] = x - c;
-        }
-        __syncthreads();
-        const uint32_t at = s_cnt[len] + r;
-        s_e[at] = e;
-        s_b0[at] = b0;
-        s_len[at] = len;
-        __syncthreads();
-        e = s_e[tid];
-        b0 = s_b0[tid];
-        len = s_len[tid];
-        uint32_t wmax = len;
-        wmax = wave_max(wmax);
-        if (wmax <= 8u) lane_bpe<8>(v, bytes, ws, L, e, b0, len);
-        else if (wmax <= 12u) lane_bpe<12>(v, bytes, ws, L, e, b0, len);
-        else lane_bpe<16>(v, bytes, ws, L, e, b0, len);
-        __syncthreads();   // the LDS arrays are reused by the next step
+        const uint32_t n = lane_bpe<MAXL>(v, bytes, ws, L, row, e, b0, len);
+        add_tile_tokens(ws, L, b0, (e & CHUNK_ITEM) ? 0u : n);
     }
 }
 
@@ -257,7 +257,7 @@ __device__ __forceinline__ uint32_t lane_push(uint32_t dst_lane, uint32_t x)
 }
 
 template <int G>
-__device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L, int which,
+__device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L, uint32_t r,
                         uint32_t blk, uint32_t nblk)
 {
     static_assert(G == 16 || G == 32 || G == 64, "segment width");
@@ -267,8 +267,8 @@ __device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, ui
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *pval = (uint32_t *)(ws + L.pval);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
-    const uint32_t *list = (const uint32_t *)(ws + (which == 0 ? L.miss16 : (which == 1 ? L.miss32 : L.miss64)));
-    const uint32_t count = ctrl->miss_count[which];
+    const uint32_t *list = route_list(ws, L, r);
+    const uint32_t count = ctrl->miss_count[r];
     const uint32_t lane = threadIdx.x & 63u, seg = lane / G, k = lane % G, sbase = seg * G;
     const uint64_t segmask = G == 64 ? ~0ull : (((1ull << (G % 64)) - 1ull) << sbase);
     const uint64_t below = (1ull << lane) - 1ull;
@@ -291,6 +291,7 @@ __device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, ui
         uint32_t id = k < n ? (uint32_t)bytes[b0 + k] : 0u;
         uint32_t nx = wave_next(id);
         uint32_t rk = k + 1 < n ? __ldg(v.r2 + ((id << 8) | nx)) : NO_RANK;
+        id |= EL_BYTE;
         for (;;) {
             uint32_t m = rk;
             if (G == 64) m = wave_min(m);
@@ -311,135 +312,22 @@ __device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, ui
             const uint32_t dst = ((K >> lane) & 1u)
                                      ? sbase + (uint32_t)__popcll(K & segmask & below)
                                      : sbase + kept_seg + (uint32_t)__popcll(~K & segmask & below);
-            id = lane_push(dst, me_sel ? 256u + m : id);
+            id = lane_push(dst, me_sel ? merged_element(m) : id);
             rk = lane_push(dst, (me_sel || nx_sel) ? PENDING : rk);
             n = kept_seg;
             nx = wave_next(id);
             if (k >= n) rk = NO_RANK;
-            else if (rk == PENDING) rk = k + 1 < n ? pair_rank(v, id, nx) : NO_RANK;
+            else if (rk == PENDING) rk = k + 1 < n ? element_rkx(v, id, nx) : NO_RANK;
         }
+        id &= ID_MASK;
         if (k < n && (n > 1 || chunk)) scratch[b0 + k] = id;
         const bool head = k == 0 && q < count;
         if (head && chunk) ccount[p] = n;
         else if (head) pval[p] = n == 1 ? id : (PV_MULTI | n);
-    }
-}
-
-// Pieces of 17..32 bytes: 16 lanes per piece and two elements per lane (element e of segment s in
-// lane 16 s + e % 16, row e / 16), four pieces per wavefront.  The rounds of k_bpe_seg on each piece's
-// 32-bit masks, two pieces packed in a 64-bit word (a piece's last element never holds a hit, so
-// neither shifts nor the carry of the addition cross from one piece into the next); compaction
-// through 32-entry LDS rows; the pairs to re-probe are gathered across the wavefront so that one
-// hash probe per lane serves all four pieces.
-
-// 64-bit row masks (bit 16 s + k: element k, resp. 16 + k, of piece s) -> piece masks, pieces 0 and 1
-// in the first word, 2 and 3 in the second (bits 32 t .. 32 t + 31: piece t, element order)
-__device__ __forceinline__ uint64_t zip_rows(uint64_t r0, uint64_t r1, int half)
-{
-    const uint64_t a = (r0 >> (32 * half)) & 0xFFFFFFFFull, b = (r1 >> (32 * half)) & 0xFFFFFFFFull;
-    return (a & 0xFFFFull) | ((b & 0xFFFFull) << 16) | ((a & 0xFFFF0000ull) << 16) | ((b & 0xFFFF0000ull) << 32);
-}
-
-__device__ void bpe_seg16x2(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
-                            uint32_t blk, uint32_t nblk)
-{
-    constexpr uint64_t EVEN = 0x5555555555555555ull, ODD = ~EVEN;
-    constexpr int NW = 4;   // wavefronts per workgroup
-    __shared__ uint32_t sid[NW][4][33], srk[NW][4][33], sra[NW][64], srb[NW][64], sres[NW][64];
-    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
-    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    uint32_t *pval = (uint32_t *)(ws + L.pval);
-    uint32_t *scratch = (uint32_t *)(ws + L.scratch);
-    const uint32_t *list = (const uint32_t *)(ws + L.miss32);
-    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
-    uint32_t *ccount = (uint32_t *)(ws + L.ccount);
-    const uint32_t count = ctrl->miss_count[1];
-    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6, sg = lane >> 4, k = lane & 15u;
-    const uint64_t below = (1ull << lane) - 1ull;
-    const uint32_t wave = (blk * blockDim.x + threadIdx.x) >> 6;
-    const uint32_t nwaves = (nblk * blockDim.x) >> 6;
-    for (uint32_t q0 = wave * 4u; q0 < count; q0 += nwaves * 4u) {
-        const uint32_t q = q0 + sg;
-        uint32_t p = 0, b0 = 0, n = 0;
-        bool chunk = false;
-        if (q < count) {
-            const uint32_t e = list[q];
-            chunk = (e & CHUNK_ITEM) != 0;
-            p = e & ~CHUNK_ITEM;
-            b0 = chunk ? cstart[p] : pstart[p];
-            n = chunk ? clen[p] : pstart[p + 1] - b0;   // up to 32 bytes
-        }
-        uint32_t id0 = k < n ? (uint32_t)bytes[b0 + k] : 0u;
-        uint32_t id1 = 16u + k < n ? (uint32_t)bytes[b0 + 16u + k] : 0u;
-        uint32_t rk0, rk1;
-        {
-            // the element after: the next lane of the row, or (last lane of row 0) row 1 of the first lane
-            const uint32_t d0 = __shfl_down(id0, 1, 64), f1 = __shfl(id1, lane & ~15u, 64);
-            const uint32_t nx0 = k == 15u ? f1 : d0, nx1 = __shfl_down(id1, 1, 64);
-            rk0 = k + 1u < n ? __ldg(v.r2 + ((id0 << 8) | nx0)) : NO_RANK;
-            rk1 = 17u + k < n ? __ldg(v.r2 + ((id1 << 8) | nx1)) : NO_RANK;
-        }
-        for (;;) {
-            uint32_t m = min(rk0, rk1);
-            m = row_min16(m);   // a segment is a DPP row
-            const uint64_t H0 = __ballot(rk0 == m && m != NO_RANK), H1 = __ballot(rk1 == m && m != NO_RANK);
-            if ((H0 | H1) == 0) break;
-            const uint64_t V0 = __ballot(k < n), V1 = __ballot(16u + k < n);
-            uint64_t S[2], K[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint64_t W = zip_rows(H0, H1, h);
-                const uint64_t rsE = W & ~(W << 1) & EVEN;   // chains starting at an even element
-                const uint64_t runsE = W & ~(W + rsE);       // the hits of those chains
-                S[h] = (runsE & EVEN) | (W & ~runsE & ODD);
-                K[h] = zip_rows(V0, V1, h) & ~(S[h] << 1);
-            }
-            const uint32_t sh = 32u * (sg & 1u);
-            const uint32_t Ss = (uint32_t)((sg >> 1 ? S[1] : S[0]) >> sh);
-            const uint32_t Ks = (uint32_t)((sg >> 1 ? K[1] : K[0]) >> sh);
-            const uint32_t ms0 = (Ss >> k) & 1u, ms1 = (Ss >> (16u + k)) & 1u;
-            const uint32_t ns0 = (Ss >> (k + 1u)) & 1u, ns1 = k < 15u ? (Ss >> (17u + k)) & 1u : 0u;
-            if ((Ks >> k) & 1u) {
-                const uint32_t o = (uint32_t)__popc(Ks & ((1u << k) - 1u));
-                sid[w][sg][o] = ms0 ? 256u + m : id0;
-                srk[w][sg][o] = (ms0 || ns0) ? PENDING : rk0;
-            }
-            if ((Ks >> (16u + k)) & 1u) {
-                const uint32_t o = (uint32_t)__popc(Ks & ((1u << (16u + k)) - 1u));
-                sid[w][sg][o] = ms1 ? 256u + m : id1;
-                srk[w][sg][o] = (ms1 || ns1) ? PENDING : rk1;
-            }
-            n = (uint32_t)__popc(Ks);
-            id0 = sid[w][sg][k];
-            id1 = sid[w][sg][16u + k];
-            rk0 = k < n ? srk[w][sg][k] : NO_RANK;
-            rk1 = 16u + k < n ? srk[w][sg][16u + k] : NO_RANK;
-            const uint32_t nx0 = sid[w][sg][k + 1u], nx1 = sid[w][sg][17u + k];
-            // the last element of a piece has no pair
-            if (rk0 == PENDING && k + 1u >= n) rk0 = NO_RANK;
-            if (rk1 == PENDING && 17u + k >= n) rk1 = NO_RANK;
-            // gather the pairs to probe, one per lane, probe, scatter the ranks back
-            const bool pd0 = rk0 == PENDING, pd1 = rk1 == PENDING;
-            const uint64_t P0 = __ballot(pd0), P1 = __ballot(pd1);
-            const uint32_t c0 = (uint32_t)__popcll(P0), total = c0 + (uint32_t)__popcll(P1);
-            const uint32_t i0 = (uint32_t)__popcll(P0 & below), i1 = c0 + (uint32_t)__popcll(P1 & below);
-            for (uint32_t base = 0; base < total; base += 64u) {
-                if (pd0 && i0 - base < 64u) { sra[w][i0 - base] = id0; srb[w][i0 - base] = nx0; }
-                if (pd1 && i1 - base < 64u) { sra[w][i1 - base] = id1; srb[w][i1 - base] = nx1; }
-                uint32_t r = NO_RANK;
-                if (lane < total - base) r = pair_rank(v, sra[w][lane], srb[w][lane]);
-                sres[w][lane] = r;
-                if (pd0 && i0 - base < 64u) rk0 = sres[w][i0 - base];
-                if (pd1 && i1 - base < 64u) rk1 = sres[w][i1 - base];
-            }
-        }
-        if (n > 1 || chunk) {
-            if (k < n) scratch[b0 + k] = id0;
-            if (16u + k < n) scratch[b0 + 16u + k] = id1;
-        }
-        const bool head = k == 0 && q < count;
-        if (head && chunk) ccount[p] = n;
-        else if (head) pval[p] = n == 1 ? id0 : (PV_MULTI | n);
+        // the segments' counts, moved to lanes 0 .. SEGS - 1 so that equal tiles are adjacent
+        const uint32_t src = (lane % SEGS) * G;
+        const uint32_t x = __shfl((head && !chunk) ? n : 0u, (int)src, 64), xb = __shfl(b0, (int)src, 64);
+        add_tile_tokens(ws, L, xb, lane < SEGS ? x : 0u);
     }
 }
 
@@ -463,10 +351,10 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     uint32_t *pval = (uint32_t *)(ws + L.pval);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
-    const uint32_t *list = (const uint32_t *)(ws + L.miss128);
+    const uint32_t *list = route_list(ws, L, 5);
     const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
     uint32_t *ccount = (uint32_t *)(ws + L.ccount);
-    const uint32_t count = ctrl->miss_count[3];
+    const uint32_t count = ctrl->miss_count[5];
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
     const uint64_t below = (1ull << lane) - 1ull;
     const uint32_t wave = (blk * blockDim.x + threadIdx.x) >> 6;
@@ -483,6 +371,8 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
         if (lane == 63) nx0 = (uint32_t)__builtin_amdgcn_readlane((int)id1, 0);
         uint32_t rk0 = lane + 1 < n ? __ldg(v.r2 + ((id0 << 8) | nx0)) : NO_RANK;
         uint32_t rk1 = 65 + lane < n ? __ldg(v.r2 + ((id1 << 8) | nx1)) : NO_RANK;
+        id0 |= EL_BYTE;
+        id1 |= EL_BYTE;
         for (;;) {
             uint32_t m = min(rk0, rk1);
             m = wave_min(m);
@@ -505,12 +395,12 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
             const uint32_t k0 = (uint32_t)__popcll(K0);
             if ((K0 >> lane) & 1u) {
                 const uint32_t o = (uint32_t)__popcll(K0 & below);
-                sid[w][o] = ms0 ? 256u + m : id0;
+                sid[w][o] = ms0 ? merged_element(m) : id0;
                 srk[w][o] = (ms0 || ns0) ? PENDING : rk0;
             }
             if ((K1 >> lane) & 1u) {
                 const uint32_t o = k0 + (uint32_t)__popcll(K1 & below);
-                sid[w][o] = ms1 ? 256u + m : id1;
+                sid[w][o] = ms1 ? merged_element(m) : id1;
                 srk[w][o] = (ms1 || ns1) ? PENDING : rk1;
             }
             n = k0 + (uint32_t)__popcll(K1);
@@ -522,16 +412,19 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
             nx1 = wave_next(id1);
             if (lane == 63) nx0 = (uint32_t)__builtin_amdgcn_readlane((int)id1, 0);
             if (rk0 == PENDING || rk1 == PENDING) {
-                // both rows' probes in one round trip; a pending pair holds a merged token (>= 256),
-                // the other row's result is dropped when it is not pending
+                // both rows' probes in one round trip; a pending pair holds a merged token (>= 256); a
+                // row is probed only when it is pending and the operand bits allow a merge
                 uint32_t q0, q1;
-                pair_rank2_general(v, id0, nx0, id1, nx1, q0, q1);
+                pair_rkx2(v, id0 & ID_MASK, nx0 & ID_MASK, rk0 == PENDING && may_merge(id0, nx0), id1 & ID_MASK,
+                          nx1 & ID_MASK, rk1 == PENDING && may_merge(id1, nx1), q0, q1);
                 if (rk0 == PENDING) rk0 = q0;
                 if (rk1 == PENDING) rk1 = q1;
             }
             if (lane + 1 >= n) rk0 = NO_RANK;
             if (65 + lane >= n) rk1 = NO_RANK;
         }
+        id0 &= ID_MASK;
+        id1 &= ID_MASK;
         if (n > 1 || chunk) {
             if (lane < n) scratch[b0 + lane] = id0;
             if (64 + lane < n) scratch[b0 + 64 + lane] = id1;
@@ -540,18 +433,18 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
             if (chunk) ccount[p] = n;
             else pval[p] = n == 1 ? id0 : (PV_MULTI | n);
         }
+        add_tile_tokens(ws, L, b0, (lane == 0 && !chunk) ? n : 0u);
     }
 }
 
-// The lists of short unresolved pieces are independent and each kernel above is bound by its
-// dependent table probes, so they run as one launch: the workgroups are split into four ranges, one
-// per list, and all four progress at the same time.  Register use is capped for seven wavefronts per
-// SIMD (72 VGPRs; the lane role spills a little): more resident workgroups hide more probe latency
-// than the spills cost (measured on the 18.4 MB batch: six wavefronts 61 us, seven 57 us, eight
-// with 64 VGPRs 143 us).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 8))) void k_bpe_small(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
-                                                   Layout L, uint32_t g16, uint32_t g32, uint32_t g64, uint32_t g128)
+// The lists of short unresolved pieces are independent and each role above is bound by its
+// dependent table probes, so they run as one launch: the workgroups are split into six ranges, one
+// per list, and all of them progress at the same time.
+__global__ __launch_bounds__(256) void k_bpe_small(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws, Layout L,
+                                                  uint32_t g8, uint32_t g12, uint32_t g16, uint32_t g32, uint32_t g64,
+                                                  uint32_t g128)
 {
+    __shared__ __align__(16) uint32_t rows[256 * LROW];   // the lane units' rows
     // workgroup ranges in order of the units' round counts (longest first): workgroups are dispatched
     // in order, so the long chains start at once and the many short ones fill in around them.  The
     // ranges are cut to what the lists hold (the grid is sized for the largest possible lists), so
@@ -559,28 +452,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 8))) voi
     {
         const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
         const uint32_t *cnt = ctrl->miss_count;
-        g128 = min(g128, (cnt[3] + 3u) / 4u);     // 4 pieces per workgroup step
-        g64 = min(g64, (cnt[2] + 3u) / 4u);
-        g32 = min(g32, (cnt[1] + 15u) / 16u);     // 16
-        g16 = min(g16, (cnt[0] + 255u) / 256u);   // 256
+        g128 = min(g128, (cnt[5] + 3u) / 4u);     // a piece per wavefront
+        g64 = min(g64, (cnt[4] + 3u) / 4u);
+        g32 = min(g32, (cnt[3] + 255u) / 256u);   // a piece per lane
+        g16 = min(g16, (cnt[2] + 255u) / 256u);
+        g12 = min(g12, (cnt[1] + 255u) / 256u);
+        g8 = min(g8, (cnt[0] + 255u) / 256u);
     }
     uint32_t b = blockIdx.x;
     if (b < g128) {
         bpe_seg2(v, bytes, ws, L, b, g128);
-        return;
+    } else if ((b -= g128) < g64) {
+        bpe_seg<64>(v, bytes, ws, L, 4, b, g64);
+    } else if ((b -= g64) < g32) {
+        bpe_lane<32>(v, bytes, ws, L, rows, 3, b, g32);
+    } else if ((b -= g32) < g16) {
+        bpe_lane<16>(v, bytes, ws, L, rows, 2, b, g16);
+    } else if ((b -= g16) < g12) {
+        bpe_lane<12>(v, bytes, ws, L, rows, 1, b, g12);
+    } else if ((b -= g12) < g8) {
+        bpe_lane<8>(v, bytes, ws, L, rows, 0, b, g8);
     }
-    b -= g128;
-    if (b < g64) {
-        bpe_seg<64>(v, bytes, ws, L, 2, b, g64);
-        return;
-    }
-    b -= g64;
-    if (b < g32) {
-        bpe_seg16x2(v, bytes, ws, L, b, g32);
-        return;
-    }
-    b -= g32;
-    if (b < g16) bpe_lane(v, bytes, ws, L, b, g16);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -705,7 +597,7 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
             if (w != NO_PIECE) {
                 if (tid == 0) {
                     scratch[b0] = w;
-                    put_piece(ws, L, p, 1u, 0u, true);
+                    put_piece(ws, L, p, b0, 1u, 0u, true);
                 }
                 continue;
             }
@@ -713,7 +605,7 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
         for (uint32_t k = tid; k < n; k += NT) sid[k] = bytes[b0 + k];
         __syncthreads();
         for (uint32_t k = tid; k < n; k += NT)
-            srk[k] = k + 1 < n ? __ldg(v.r2 + ((sid[k] << 8) | sid[k + 1])) : NO_RANK;
+            srk[k] = k + 1 < n ? rkx_rank(__ldg(v.r2 + ((sid[k] << 8) | sid[k + 1]))) : NO_RANK;
         __syncthreads();
         for (;;) {
             uint32_t lmin = NO_RANK;
@@ -787,7 +679,7 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
         for (uint32_t k = tid; k < n; k += NT) scratch[b0 + k] = sid[k];
         if (tid == 0) {
             if (is_chunk) ccount[q - count] = n;
-            else put_piece(ws, L, p, n, 0u, true);
+            else put_piece(ws, L, p, b0, n, 0u, true);
         }
         __syncthreads();
     }
@@ -956,9 +848,9 @@ __global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, La
                 clen[c0 + i] = len;
                 ((uint32_t *)(ws + L.cpiece))[c0 + i] = i < nc ? p : NO_PIECE;
             }
-            const uint32_t r = len >= 1 && len <= (uint32_t)SEG2_MAX ? route_of(len) : 4u;
+            const uint32_t r = len >= 1 && len <= (uint32_t)SEG2_MAX ? route_of(len) : NMISS;
 #pragma unroll
-            for (uint32_t rl = 0; rl < 4; ++rl) {
+            for (uint32_t rl = 0; rl < NMISS; ++rl) {
                 const uint64_t m = __ballot(r == rl);
                 if (!m) continue;
                 const uint32_t leader = (uint32_t)__ffsll((unsigned long long)m) - 1u;
@@ -1017,7 +909,7 @@ __device__ void giant_join(uint8_t *ws, const Layout &L)
             if (tid == 0) s_acc += tot;
             __syncthreads();
         }
-        if (tid == 0) put_piece(ws, L, p, s_acc, 0u, true);
+        if (tid == 0) put_piece(ws, L, p, ((const uint32_t *)(ws + L.pstart))[p], s_acc, 0u, true);
         __syncthreads();
     }
 }
@@ -1059,7 +951,7 @@ __global__ __launch_bounds__(GIANT_THREADS) void k_bpe_giant(DevVocab v, const u
         for (uint32_t k = tid; k < n; k += NT) idA[k] = bytes[b0 + k];
         uint32_t lmin = NO_RANK;
         for (uint32_t k = tid; k < n; k += NT) {
-            uint32_t r = k + 1 < n ? __ldg(v.r2 + ((uint32_t)bytes[b0 + k] << 8 | bytes[b0 + k + 1])) : NO_RANK;
+            uint32_t r = k + 1 < n ? rkx_rank(__ldg(v.r2 + ((uint32_t)bytes[b0 + k] << 8 | bytes[b0 + k + 1]))) : NO_RANK;
             rkA[k] = r;
             lmin = min(lmin, r);
         }
@@ -1170,28 +1062,33 @@ hipError_t launch_route(const DevVocab &v, const Batch &b, hipStream_t s, const 
     return hipGetLastError();
 }
 
+hipError_t launch_giant_prep(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev)
+{
+    const Layout &L = b.L;
+    if (b.n == 0) return hipGetLastError();
+    // giant pieces: safe-seam bitmap, then chunks (listed with the other BPE items by length)
+    LaunchScope k(ev, TK_GIANT_SEAMS, s);
+    const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
+    hipLaunchKernelGGL(k_gsafe, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
+    const uint32_t gc = L.cap_giant < 64 ? L.cap_giant : 64;
+    hipLaunchKernelGGL(k_gcut, dim3(gc), dim3(1024), 0, s, v, b.ws, L);
+    return hipGetLastError();
+}
+
 hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev)
 {
     const Layout &L = b.L;
     if (b.n == 0) return hipGetLastError();
     {
-        // giant pieces: safe-seam bitmap, then chunks (before the other BPE kernels, which also
-        // encode the chunks)
-        LaunchScope k(ev, TK_GIANT_SEAMS, s);
-        const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
-        hipLaunchKernelGGL(k_gsafe, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
-        const uint32_t gc = L.cap_giant < 64 ? L.cap_giant : 64;
-        hipLaunchKernelGGL(k_gcut, dim3(gc), dim3(1024), 0, s, v, b.ws, L);
-    }
-    {
-        // lists of <= 16, 17..32, 33..64 and 65..128 bytes: at most n / 1, n / 17, n / 33, n / 65 items;
-        // 256 lane items, 16, 4 and 4 pieces per workgroup
-        const uint64_t b16 = b.n / 256 + 1, b32 = b.n / 17 / 16 + 1, b64 = b.n / 33 / 4 + 1, b128 = b.n / 65 / 4 + 1;
-        const uint32_t g16 = b16 > 2048 ? 2048u : (uint32_t)b16, g32 = b32 > 2048 ? 2048u : (uint32_t)b32;
-        const uint32_t g64 = b64 > 256 ? 256u : (uint32_t)b64, g128 = b128 > 256 ? 256u : (uint32_t)b128;
-        LaunchScope k(ev, TK_BPE_CHUNKS, s);
-        hipLaunchKernelGGL(k_bpe_small, dim3(g16 + g32 + g64 + g128), dim3(256), 0, s, v, b.bytes, b.ws, L, g16, g32,
-                           g64, g128);
+        // lists of <= 8, 9..12, 13..16, 17..32, 33..64 and 65..128 bytes: at most n / 2 (plus chunks),
+        // n / 9, n / 13, n / 17, n / 33, n / 65 items; 256 lane items, 4 and 4 pieces per workgroup
+        auto cap = [](uint64_t x, uint32_t c) { return x > c ? c : (uint32_t)x; };
+        const uint32_t g8 = cap((b.n / 2 + L.cap_chunks) / 256 + 1, 2048), g12 = cap(b.n / 9 / 256 + 1, 2048);
+        const uint32_t g16 = cap(b.n / 13 / 256 + 1, 2048), g32 = cap(b.n / 17 / 256 + 1, 2048);
+        const uint32_t g64 = cap(b.n / 33 / 4 + 1, 256), g128 = cap(b.n / 65 / 4 + 1, 256);
+        LaunchScope k(ev, TK_BPE_SHORT, s);
+        hipLaunchKernelGGL(k_bpe_small, dim3(g8 + g12 + g16 + g32 + g64 + g128), dim3(256), 0, s, v, b.bytes, b.ws, L,
+                           g8, g12, g16, g32, g64, g128);
     }
     {
         LaunchScope k(ev, TK_BPE_WAVE, s);

@@ -14,9 +14,6 @@ constexpr int HALO = 16;                       // character codes computed past 
 constexpr int RAW_LEAD = 4, RAW_TAIL = 24;     // raw bytes kept before / after a tile
 
 // token-offset scan: one workgroup per 4096 pieces
-constexpr int SCAN_THREADS = 256;
-constexpr int SCAN_PER_THREAD = 16;
-constexpr int SCAN_TILE = SCAN_THREADS * SCAN_PER_THREAD;
 
 // giant pieces are cut at seams that no merge can cross: about every GCH bytes where such seams are
 // common, and at both ends of stretches longer than GCH without one
@@ -25,7 +22,7 @@ constexpr uint32_t GCH = 48;
 constexpr uint32_t CHUNK_ITEM = 1u << 31;
 
 // BPE length bins (piece bytes): lane <= LANE_MAX < wave <= WAVE_MAX < block <= BLOCK_MAX < giant
-constexpr int LANE_MAX = 64;      // lane kernels: <= 16, 17..32 and 33..64 bytes
+constexpr int LANE_MAX = 64;      // lane kernels: <= 16 (by 8, 12, 16), 17..32 and 33..64 bytes
 constexpr int SEG2_MAX = 128;     // one wavefront, two elements per lane: 65..128 bytes
 constexpr int TABLE_MAX = 32;     // whole-piece tables hold pieces of 2..32 bytes
 constexpr int WAVE_MAX = 1024;
@@ -122,16 +119,28 @@ constexpr int DS_NSELF = 16, DS_NNEXT = 10, DS_NCTX = DS_NSELF * 2 * DS_NNEXT;
 constexpr int NCTX_MAX = NCTX > DS_NCTX ? NCTX : DS_NCTX;
 
 // ---------------------------------------------------------------------------------------------
-// merge tables.  Pair hash slot: bits 63..21 = (left << 21 | right), bits 20..0 = rank.
+// merge tables.  A merge's rank word (rkx) is rank << 2 | L << 1 | R, where L (R) is set when the
+// token the merge creates is the left (right) operand of some merge: a pair (x, y) can only have a
+// rank when x is some merge's left operand and y some merge's right operand, so the BPE kernels skip
+// the lookups of the pairs that fail this test.  Pair hash slot: bits 63..22 = (left << 21 | right),
+// bits 21..0 = rkx.  Ranks stay below 2^20, token IDs below 2^21.
 constexpr uint32_t NO_RANK = 0xFFFFFFFFu;
 constexpr uint32_t NO_PIECE = 0xFFFFFFFFu;
 constexpr uint64_t EMPTY_SLOT = ~0ull;
+constexpr uint32_t RKX_MASK = 0x3FFFFFu;
+__host__ __device__ __forceinline__ uint32_t rkx_rank(uint32_t x) { return x == NO_RANK ? NO_RANK : x >> 2; }
+// a sequence element of the short BPE units: token ID | L << 31 | R << 30 (bytes carry both)
+constexpr uint32_t ID_MASK = 0x3FFFFFFFu, EL_L = 1u << 31, EL_R = 1u << 30, EL_BYTE = EL_L | EL_R;
+// the element a merge of rank word x creates
+__device__ __forceinline__ uint32_t merged_element(uint32_t x) { return (256u + (x >> 2)) | ((x & 3u) << 30); }
+// can the pair of elements (a, b) have a rank?
+__device__ __forceinline__ bool may_merge(uint32_t a, uint32_t b) { return (a & EL_L) && (b & EL_R); }
 
 constexpr int FAMILY_GPT2 = 1, FAMILY_O200K = 3, FAMILY_DEEPSEEK = 4;   // the family codes of the public header
 
 struct DevVocab {
-    const uint32_t *r2;       // 65536 byte-pair ranks
-    const uint64_t *slots;    // pair table: 8-byte slots (left << 21 | right) << 21 | rank, two-choice cuckoo
+    const uint32_t *r2;       // 65536 byte-pair rank words (rkx), NO_RANK for no merge
+    const uint64_t *slots;    // pair table: 8-byte slots (left << 21 | right) << 22 | rkx, two-choice cuckoo
     const uint32_t *merges;   // 2 * n_merges (left, right)
     const uint4 *fmap16;      // NCTX (DeepSeek style: DS_NCTX) transition maps, one byte per state s (bytes 0..14):
                               //   bits 0-3 the next state, bit 4 set when a piece starts here in s
@@ -341,36 +350,55 @@ __device__ __forceinline__ uint32_t wave_upper_bound(const T *a, uint32_t n, T x
     return wave_partition_point(a, n, [x](T v) { return v > x; });
 }
 
-// rank held by a pair-table slot for key, NO_RANK if neither candidate holds it (an empty slot is
+// rank word held by a pair-table slot for key, NO_RANK if neither candidate holds it (an empty slot is
 // all ones: its key field exceeds every (left << 21 | right))
-__device__ __forceinline__ uint32_t slot_rank(uint64_t s0, uint64_t s1, uint64_t key)
+__device__ __forceinline__ uint32_t slot_rkx(uint64_t s0, uint64_t s1, uint64_t key)
 {
-    return (s0 >> 21) == key ? (uint32_t)(s0 & 0x1FFFFFu) : ((s1 >> 21) == key ? (uint32_t)(s1 & 0x1FFFFFu) : NO_RANK);
+    return (s0 >> 22) == key ? (uint32_t)(s0 & RKX_MASK) : ((s1 >> 22) == key ? (uint32_t)(s1 & RKX_MASK) : NO_RANK);
 }
 
-// Ranks of two pairs, each with an operand >= 256 (not byte pairs): all four candidate slots read at
-// once, so a merge step that needs both waits for one round trip
-__device__ __forceinline__ void pair_rank2_general(const DevVocab &v, uint32_t a0, uint32_t b0, uint32_t a1,
-                                                   uint32_t b1, uint32_t &r0, uint32_t &r1)
+// Rank words of two pairs, each with an operand >= 256 (not byte pairs), looked up only where need0 /
+// need1: all candidate slots read at once, so a merge step that needs both waits for one round trip
+__device__ __forceinline__ void pair_rkx2(const DevVocab &v, uint32_t a0, uint32_t b0, bool need0, uint32_t a1,
+                                          uint32_t b1, bool need1, uint32_t &r0, uint32_t &r1)
 {
     const uint64_t k0 = ((uint64_t)a0 << 21) | b0, k1 = ((uint64_t)a1 << 21) | b1;
     uint32_t i0, j0, i1, j1;
     ck_slots(k0, v.pseed, v.slot_cap, i0, j0);
     ck_slots(k1, v.pseed, v.slot_cap, i1, j1);
-    const uint64_t s0 = v.slots[i0], t0 = v.slots[j0], s1 = v.slots[i1], t1 = v.slots[j1];
-    r0 = slot_rank(s0, t0, k0);
-    r1 = slot_rank(s1, t1, k1);
+    uint64_t s0 = EMPTY_SLOT, t0 = EMPTY_SLOT, s1 = EMPTY_SLOT, t1 = EMPTY_SLOT;
+    if (need0) {
+        s0 = v.slots[i0];
+        t0 = v.slots[j0];
+    }
+    if (need1) {
+        s1 = v.slots[i1];
+        t1 = v.slots[j1];
+    }
+    r0 = slot_rkx(s0, t0, k0);
+    r1 = slot_rkx(s1, t1, k1);
 }
 
-// Rank of the pair (a, b), NO_RANK if no merge joins them: byte pairs from the dense table, the others
-// from the pair table (both candidate slots in one round trip)
-__device__ __forceinline__ uint32_t pair_rank(const DevVocab &v, uint32_t a, uint32_t b)
+// Rank word of the pair (a, b), NO_RANK if no merge joins them: byte pairs from the dense table, the
+// others from the pair table (both candidate slots in one round trip)
+__device__ __forceinline__ uint32_t pair_rkx(const DevVocab &v, uint32_t a, uint32_t b)
 {
     if ((a | b) < 256u) return __ldg(v.r2 + ((a << 8) | b));
     const uint64_t key = ((uint64_t)a << 21) | b;
     uint32_t i, j;
     ck_slots(key, v.pseed, v.slot_cap, i, j);
-    return slot_rank(v.slots[i], v.slots[j], key);
+    return slot_rkx(v.slots[i], v.slots[j], key);
+}
+
+__device__ __forceinline__ uint32_t pair_rank(const DevVocab &v, uint32_t a, uint32_t b)
+{
+    return rkx_rank(pair_rkx(v, a, b));
+}
+
+// the same for two elements (ID | L | R bits): NO_RANK without a lookup when the bits rule a merge out
+__device__ __forceinline__ uint32_t element_rkx(const DevVocab &v, uint32_t a, uint32_t b)
+{
+    return may_merge(a, b) ? pair_rkx(v, a & ID_MASK, b & ID_MASK) : NO_RANK;
 }
 
 // calls f(id) for every token whose byte string equals s[0, len); the table key was computed by the
@@ -413,21 +441,20 @@ struct Ctrl {
     uint32_t n_pieces;
     uint32_t n_tokens;
     uint32_t bin_count[3];     // wave, block, giant bins
-    uint32_t miss_count[4];    // pieces left for BPE: <= 16, 17..32, 33..64, 65..128 bytes
+    uint32_t miss_count[6];    // pieces left for BPE: <= 8, 9..12, 13..16, 17..32, 33..64, 65..128 bytes
     uint32_t n_chunks;         // chunk slots reserved for giant pieces
     uint32_t done_giant;       // workgroups of k_bpe_giant done (the last one joins the chunks)
-    uint32_t pad[51];
+    uint32_t pad[49];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
 // ---------------------------------------------------------------------------------------------
 // workspace layout for n input bytes
 struct Layout {
-    uint64_t ctrl, cc, tbwd, tdoc, tflag_state, tflag_cnt, tcount, tsb, tmiss, tbase, tlast, pstart, pval, tokoff,
-        mlist, scratch,
-        bin_wave, bin_block, bin_giant, miss16, miss32, miss64, miss128, g_ids, g_rank_a, g_rank_b, tilex, cstart,
-        clen, ccount, gc0, gnc, gsafe, cpiece, total;
-    uint32_t n_tiles, n_scan_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
+    uint64_t ctrl, cc, tbwd, tdoc, tflag_state, tflag_cnt, tcount, tsb, tbase, tlast, pstart, pval, tokoff, scratch,
+        bin_wave, bin_block, bin_giant, miss[6], g_ids, g_rank_a, g_rank_b, tspill, cstart, clen, ccount, gc0, gnc, gsafe,
+        cpiece, total;
+    uint32_t n_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
 };
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
@@ -436,7 +463,6 @@ inline Layout make_layout(uint64_t n)
 {
     Layout L;
     L.n_tiles = (uint32_t)((n + TILE - 1) / TILE);
-    L.n_scan_tiles = (uint32_t)((n + 1 + SCAN_TILE - 1) / SCAN_TILE);
     L.cap_wave = (uint32_t)(n / (LANE_MAX + 1) + 1);
     L.cap_block = (uint32_t)(n / (WAVE_MAX + 1) + 1);
     L.cap_giant = (uint32_t)(n / (BLOCK_MAX + 1) + 1);
@@ -451,25 +477,30 @@ inline Layout make_layout(uint64_t n)
     L.tflag_cnt = o;   o += align256(8ull * L.n_tiles);
     L.tcount = o;      o += align256(4ull * (L.n_tiles + 1));   // tokens of the pieces starting in each tile
     L.tsb = o;         o += align256(4ull * (L.n_tiles / 64 + 1));  // the same summed over 64 tiles
-    L.tmiss = o;       o += align256(4ull * (L.n_tiles + 1));   // pieces of each tile left for BPE
     L.tbase = o;       o += align256(4ull * (L.n_tiles + 1));
     L.tlast = o;       o += align256(4ull * L.n_tiles);
-    L.tilex = o;       o += align256(4ull * L.n_scan_tiles);
     L.pstart = o;      o += align256(4ull * (n + 2));
     L.pval = o;        o += align256(4ull * (n + 1));
     L.tokoff = o;      o += align256(4ull * (n + 2));
-    L.mlist = o;       o += align256(4ull * (n + 1));   // those pieces, at the tile's first piece index
     L.scratch = o;     o += align256(4ull * (n + 1));
     L.bin_wave = o;    o += align256(4ull * L.cap_wave);
     L.bin_block = o;   o += align256(4ull * L.cap_block);
     L.bin_giant = o;   o += align256(4ull * L.cap_giant);
-    L.miss16 = o;      o += align256(4ull * (n + 1));
-    L.miss32 = o;      o += align256(4ull * (n / 17 + 1));
-    L.miss64 = o;      o += align256(4ull * (n / 33 + 1));
-    L.miss128 = o;     o += align256(4ull * (n / 65 + 1));
+    // BPE lists: their items (pieces and chunks of giant pieces) are disjoint byte ranges, so at most
+    // n / (shortest length) of them; only chunks are a single byte long
+    {
+        const uint64_t shortest[6] = {2, 9, 13, 17, 33, 65};
+        for (int r = 0; r < 6; ++r) {
+            L.miss[r] = o;
+            o += align256(4ull * (n / shortest[r] + 1 + (r == 0 ? L.cap_chunks : 0u)));
+        }
+    }
     L.g_ids = o;       o += align256(4ull * (n + 1));
     L.g_rank_a = o;    o += align256(4ull * (n + 1));
     L.g_rank_b = o;    o += align256(4ull * (n + 1));
+    // the tile encoder's BPE queue beyond its LDS part, at the tile's first piece index: used only
+    // inside k_tiles, so it shares g_rank_b (only k_bpe_giant, later in the chain, uses that)
+    L.tspill = L.g_rank_b;
     L.cstart = o;      o += align256(4ull * L.cap_chunks);
     L.clen = o;        o += align256(4ull * L.cap_chunks);
     L.ccount = o;      o += align256(4ull * L.cap_chunks);
@@ -565,36 +596,35 @@ __device__ __forceinline__ uint32_t wp_step(const DevVocab &v, WPQ &q, uint32_t 
 // for pieces longer than 64 bytes, whose IDs are copied by a separate gather.
 constexpr uint32_t PV_MULTI = 1u << 31, PV_LONG = 1u << 30, PV_COUNT = PV_LONG - 1u;
 
-// Result of piece p: n >= 1 tokens, first ID id0 (the others already in scratch when n > 1).  The
-// excess over one token is added to the counter of the piece's output tile (SCAN_TILE consecutive
-// pieces); the compaction kernel derives each tile's first output position from those counters
-// instead of a look-back across tiles.
-__device__ __forceinline__ void put_piece(uint8_t *ws, const Layout &L, uint32_t p, uint32_t n, uint32_t id0,
-                                          bool is_long)
+// Result of piece p (first byte b0): n >= 1 tokens, first ID id0 (the others already in scratch
+// when n > 1).  The tokens are added to the counters of the input tile of b0 and of its group of 64
+// tiles, from which the compaction kernel derives each tile's first output position.
+__device__ __forceinline__ void put_piece(uint8_t *ws, const Layout &L, uint32_t p, uint32_t b0, uint32_t n,
+                                          uint32_t id0, bool is_long)
 {
     ((uint32_t *)(ws + L.pval))[p] = (n == 1 && !is_long) ? id0 : (PV_MULTI | (is_long ? PV_LONG : 0u) | n);
-    if (n > 1) atomicAdd((uint32_t *)(ws + L.tilex) + p / SCAN_TILE, n - 1);
+    atomicAdd((uint32_t *)(ws + L.tcount) + b0 / (uint32_t)TILE, n);
+    atomicAdd((uint32_t *)(ws + L.tsb) + b0 / (uint32_t)TILE / 64u, n);
 }
 
-// List a piece belongs to when it is not resolved directly: 0..3 BPE miss lists (<= 16, 17..32,
-// 33..64, 65..SEG2_MAX bytes), 4..6 length bins (..WAVE_MAX, ..BLOCK_MAX, longer).
-constexpr uint32_t NROUTES = 7;
+// List a piece belongs to when it is not resolved directly: 0..5 BPE miss lists (<= 8, 9..12, 13..16,
+// 17..32, 33..64, 65..SEG2_MAX bytes), 6..8 length bins (..WAVE_MAX, ..BLOCK_MAX, longer).
+constexpr uint32_t NMISS = 6, NROUTES = 9;
 __device__ __forceinline__ uint32_t route_of(uint32_t len)
 {
-    return len <= 16u ? 0u : len <= 32u ? 1u : len <= (uint32_t)LANE_MAX ? 2u : len <= (uint32_t)SEG2_MAX ? 3u :
-           len <= (uint32_t)WAVE_MAX ? 4u : len <= (uint32_t)BLOCK_MAX ? 5u : 6u;
+    return len <= 8u ? 0u : len <= 12u ? 1u : len <= 16u ? 2u : len <= 32u ? 3u : len <= (uint32_t)LANE_MAX ? 4u :
+           len <= (uint32_t)SEG2_MAX ? 5u : len <= (uint32_t)WAVE_MAX ? 6u : len <= (uint32_t)BLOCK_MAX ? 7u : 8u;
 }
 
 __device__ __forceinline__ uint32_t *route_list(uint8_t *ws, const Layout &L, uint32_t r)
 {
-    const uint64_t o = r == 0 ? L.miss16 : r == 1 ? L.miss32 : r == 2 ? L.miss64 : r == 3 ? L.miss128 :
-                       r == 4 ? L.bin_wave : r == 5 ? L.bin_block : L.bin_giant;
+    const uint64_t o = r < NMISS ? L.miss[r] : r == 6 ? L.bin_wave : r == 7 ? L.bin_block : L.bin_giant;
     return (uint32_t *)(ws + o);
 }
 
 __device__ __forceinline__ uint32_t *route_count(Ctrl *ctrl, uint32_t r)
 {
-    return r < 4 ? &ctrl->miss_count[r] : &ctrl->bin_count[r - 4];
+    return r < NMISS ? &ctrl->miss_count[r] : &ctrl->bin_count[r - NMISS];
 }
 
 // Called by every thread of a workgroup when it has written its results: true in the workgroup that
@@ -611,27 +641,6 @@ __device__ __forceinline__ bool last_workgroup(uint32_t *done)
     const bool last = s_last != 0;
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return last;
-}
-
-// Wavefront form of the same counter update, called by all 64 lanes: lane i contributes the
-// excess x (0 when it has none) of piece p; lanes are combined over runs of equal output tiles in
-// lane order (pieces taken from a list in ascending order mostly share a tile) and each run's last
-// lane issues one atomic.
-__device__ __forceinline__ void add_excess_wave(uint8_t *ws, const Layout &L, uint32_t p, uint32_t x)
-{
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t key = x ? p / SCAN_TILE : 0xFFFFFFFFu;
-    const uint32_t prev = __shfl_up(key, 1, 64);
-    const uint64_t heads = __ballot(lane == 0 || prev != key);
-    const uint32_t hpos = 63u - (uint32_t)__clzll((unsigned long long)(heads & ((2ull << lane) - 1ull)));
-    uint32_t v = x;
-#pragma unroll
-    for (uint32_t d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(v, d, 64);
-        if (lane >= hpos + d) v += y;
-    }
-    const bool tail = lane == 63 || ((heads >> (lane + 1)) & 1ull);
-    if (tail && key != 0xFFFFFFFFu && v) atomicAdd((uint32_t *)(ws + L.tilex) + key, v);
 }
 
 // Wavefront form of the per-tile token counters of the tile encoder's pieces, called by all 64 lanes:
@@ -670,9 +679,8 @@ struct Batch {
 };
 
 // launch indices of the encode chain (TOKTIER_K_* in toktier.h)
-enum : int { TK_SUMMARY = 0, TK_PIECES = 1, TK_GIANT_SEAMS = 2, TK_BPE_CHUNKS = 3, TK_BPE_WAVE = 4, TK_BPE_BLOCK = 5,
-             TK_BPE_GIANT = 6, TK_TILES = 7, TK_BPE_TILES = 8,
-             TK_EMIT = 9, TK_COUNT = 10 };
+enum : int { TK_SUMMARY = 0, TK_PIECES = 1, TK_GIANT_SEAMS = 2, TK_TILES = 3, TK_BPE_SHORT = 4, TK_BPE_WAVE = 5,
+             TK_BPE_BLOCK = 6, TK_BPE_GIANT = 7, TK_EMIT = 8, TK_COUNT = 9 };
 
 // optional events recorded around each kernel launch (indices: TOKTIER_K_* in toktier.h)
 struct Events {
@@ -760,12 +768,13 @@ hipError_t launch_literal_merge(const DevAdded &a, const Batch &b, const AddLayo
                                 uint32_t *out_ids, uint64_t *out_offsets, uint32_t *out_spans, hipStream_t s);
 
 hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
+// pieces longer than BLOCK_MAX: merge-safe seams and chunks (before the tile encoder lists its pieces)
+hipError_t launch_giant_prep(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
+// BPE of every listed piece and chunk, by length: the short lists, then wavefront, workgroup and
+// giant pieces (after the tile encoder)
 hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
-hipError_t launch_compact(const DevVocab &v, const Batch &b, uint32_t *out_ids, uint64_t *out_offsets,
-                          uint32_t *out_spans, hipStream_t s, const Events *ev);
 hipError_t launch_export_starts(const Batch &b, uint32_t *out_starts, hipStream_t s);
 hipError_t launch_route(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
-hipError_t launch_bpe_tiles(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
 hipError_t launch_tiles(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
 hipError_t launch_emit(const DevVocab &v, const Batch &b, uint32_t *out_ids, uint64_t *out_offsets,
                        uint32_t *out_spans, hipStream_t s, const Events *ev);

@@ -261,7 +261,6 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
         ((uint64_t *)(ws + L.tflag_cnt))[blockIdx.x] = 0;
         ((uint32_t *)(ws + L.tlast))[blockIdx.x] = 0;
     }
-    for (uint32_t k = blockIdx.x * 64u + lane; k < L.n_scan_tiles; k += gridDim.x * 64u) ((uint32_t *)(ws + L.tilex))[k] = 0;
     for (uint32_t k = blockIdx.x * 64u + lane; k <= L.n_tiles / 64u; k += gridDim.x * 64u) ((uint32_t *)(ws + L.tsb))[k] = 0;
     if (blockIdx.x >= L.n_tiles) return;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
@@ -893,6 +892,23 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
             hipLaunchKernelGGL(k_pieces<VAR_PLAIN>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs,
                                b.n, b.ws, L);
     }
+    return hipGetLastError();
+}
+
+// the piece starts as one array (pretokenize-only calls): n_pieces starts, then the batch end
+__global__ __launch_bounds__(256) void k_export_starts(uint8_t *ws, Layout L, uint64_t n, uint32_t *out)
+{
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t np = ctrl->n_pieces;
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i <= np; i += gridDim.x * blockDim.x)
+        out[i] = i == np ? (uint32_t)n : pstart[i];
+}
+
+hipError_t launch_export_starts(const Batch &b, uint32_t *out_starts, hipStream_t s)
+{
+    uint32_t g = (uint32_t)((b.n + 1 + 255) / 256);
+    hipLaunchKernelGGL(k_export_starts, dim3(g > 4096 ? 4096 : g), dim3(256), 0, s, b.ws, b.L, b.n, out_starts);
     return hipGetLastError();
 }
 

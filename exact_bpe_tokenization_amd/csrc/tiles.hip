@@ -8,18 +8,11 @@
 //   k_tiles  per 8 KiB input tile, the pieces that start in it: the tile's bytes and the 128 after
 //            it are staged in LDS (a piece of up to SHORT_MAX bytes that starts in the tile lies in
 //            that window); one byte is its own ID; 2..32 bytes are looked up in the whole-piece
-//            tables (key built from LDS, two pieces per thread in flight); pieces longer than
-//            SHORT_MAX were encoded before this kernel and only their result word is read; the
-//            others are listed in the tile's own slice of a list (at its first piece index: no
-//            shared counter).  The tile's token count so far goes to its counter and to the counter
-//            of its group of 64 tiles.
-//   k_bpe_tiles  per tile (or a share of a tile when tiles are few): the listed pieces, their bytes
-//            from the tile's window in LDS, sorted by length and encoded by the workgroup's
-//            wavefronts: one lane per piece up to 16 bytes (the textbook loop in registers), 16 lanes
-//            x 2 rows per piece up to 32 bytes, a wavefront up to 64 and a wavefront with two
-//            elements per lane up to 128 (rounds: minimum rank, leftmost non-overlapping occurrences
-//            in closed form, re-probe of the pairs next to a merge); their tokens are added to the
-//            tile's counters.
+//            tables (key built from LDS, the lowest token IDs in LDS, the others with four pieces
+//            per thread in flight); pieces longer than SHORT_MAX were listed by the pieces kernel;
+//            the others are queued in LDS and appended to the BPE lists by length, one run per list
+//            and tile.  The tile's token count so far goes to its counter and to the counter of its
+//            group of 64 tiles (the BPE kernels add the tokens of the pieces they encode).
 //   k_emit   per tile: its first output index from the counters (the groups before its own, then
 //            the tiles before it in its group); rounds of 256 pieces, a workgroup scan of their
 //            token counts places their IDs (consecutive pieces write consecutive IDs); per-document
@@ -34,25 +27,15 @@ constexpr int NT = 256;                           // threads per tile
 constexpr int NW = NT / 64;
 constexpr int WIN = TILE + SHORT_MAX + 32;        // LDS byte window [lo, lo + WIN), zero past the batch
 
-constexpr int QCAP = 1024;                        // listed pieces encoded per step of k_bpe_tiles
-constexpr int WBUF = 512;                         // per-wavefront scratch words of the BPE units
-constexpr uint32_t PENDING = 0xFFFFFFFEu;
-constexpr uint64_t EVEN = 0x5555555555555555ull, ODD = ~EVEN;
-
-struct Smem {
-    uint32_t win[WIN / 4];            // the byte window as words
-    uint32_t q[QCAP];                 // k_bpe_tiles: listed pieces (index in the tile | len << 16)
-    uint32_t buf[NW * WBUF];          //   sort buffer, then per-wavefront scratch of the BPE units
-    uint32_t hist[SHORT_MAX + 2];
-    uint32_t wsum[NW];
-    uint32_t qn, unit, tok;
-};
+constexpr int MQ = 256;                           // pieces a tile lists for BPE through LDS
 
 struct ResolveSmem {
     uint32_t win[WIN / 4];            // the byte window as words
     uint4 hot[HOT_SLOTS];             // the hot sets of the short whole-piece table
+    uint32_t q[MQ];                   // pieces left for BPE (index in the tile | length << 16)
     uint32_t wsum[NW];
     uint32_t qn, ln;                  // pieces listed for BPE / for the 8..32-byte table
+    uint32_t rn[NMISS], rb[NMISS];    // per BPE list: this tile's items, their first list slot
 };
 
 struct EmitSmem {
@@ -84,391 +67,6 @@ __device__ __forceinline__ void win_words(const S &sm, uint32_t j, uint32_t len,
         const uint32_t rem = len > 8u * i ? len - 8u * i : 0u;
         k[i] = rem >= 8u ? w : (w & ((1ull << (8u * rem)) - 1ull));
     }
-}
-
-// whole-piece probe state of a piece of 2..TABLE_MAX bytes whose key comes from the window
-template <typename S>
-__device__ __forceinline__ WPQ wp_make_win(const DevVocab &v, const S &sm, uint32_t j, uint32_t len)
-{
-    WPQ q{0, 0, 0, 0, len, 0, 0, 0};
-    uint64_t k4[4];
-    win_words<4>(sm, j, len, k4);
-    q.k0 = k4[0]; q.k1 = k4[1]; q.k2 = k4[2]; q.k3 = k4[3];
-    if (len <= WA_MAX) {
-        if (!v.wa) return q;
-        q.k0 |= (uint64_t)len << 56;
-        ck_slots(q.k0, v.wseed, v.wa_cap, q.i, q.j);
-        q.kind = 1;
-        return q;
-    }
-    if (!v.wb) return q;
-    ck_slots(wb_digest(k4[0], k4[1], k4[2], k4[3], len), v.bseed, v.wb_cap, q.i, q.j);
-    q.kind = 2;
-    return q;
-}
-
-// ---- one lane per piece (<= 16 bytes): the textbook loop in registers ----
-template <int MAXL>
-__device__ __forceinline__ uint32_t lane_unit(const DevVocab &v, const Smem &sm, uint32_t j, uint32_t len,
-                                              uint32_t p, uint32_t a, uint32_t *pval, uint32_t *scratch)
-{
-    uint32_t id[MAXL], rk[MAXL];
-#pragma unroll
-    for (int k = 0; k < MAXL; ++k) id[k] = (uint32_t)k < len ? win_byte(sm, j + k) : 0u;
-#pragma unroll
-    for (int k = 0; k < MAXL; ++k)
-        rk[k] = (uint32_t)(k + 1) < len ? __ldg(v.r2 + ((id[k] << 8) | id[(k + 1) % MAXL])) : NO_RANK;
-    uint32_t n = len;
-    for (;;) {
-        uint32_t best = NO_RANK, pos = 0;
-#pragma unroll
-        for (int k = 0; k < MAXL - 1; ++k)
-            if (rk[k] < best) { best = rk[k]; pos = k; }
-        if (best == NO_RANK) break;
-        const uint32_t nid = 256u + best;
-#pragma unroll
-        for (int k = 0; k < MAXL; ++k) {
-            const uint32_t nx_id = k + 1 < MAXL ? id[(k + 1) % MAXL] : 0u;
-            const uint32_t nx_rk = k + 1 < MAXL ? rk[(k + 1) % MAXL] : NO_RANK;
-            id[k] = (uint32_t)k < pos ? id[k] : ((uint32_t)k == pos ? nid : nx_id);
-            rk[k] = (uint32_t)k < pos ? rk[k] : nx_rk;
-        }
-        --n;
-        uint32_t left = 0, right = 0;
-#pragma unroll
-        for (int k = 0; k < MAXL; ++k) {
-            if ((uint32_t)k + 1 == pos) left = id[k];
-            if ((uint32_t)k == pos + 1) right = id[k];
-        }
-        uint32_t rl, rr;   // both neighbours' probes in one round trip (nid >= 256: not a byte pair)
-        pair_rank2_general(v, left, nid, nid, right, rl, rr);
-        if (pos == 0) rl = NO_RANK;
-        if (pos + 1 >= n) rr = NO_RANK;
-#pragma unroll
-        for (int k = 0; k < MAXL; ++k) {
-            if ((uint32_t)k + 1 == pos) rk[k] = rl;
-            if ((uint32_t)k == pos) rk[k] = rr;
-        }
-    }
-    if (len == 0) return 0;
-    pval[p] = n == 1 ? id[0] : (PV_MULTI | n);
-    if (n > 1) {
-#pragma unroll
-        for (int k = 0; k < MAXL; ++k)
-            if ((uint32_t)k < n) scratch[a + k] = id[k];
-    }
-    return n;
-}
-
-__device__ __forceinline__ uint32_t lane_push(uint32_t dst_lane, uint32_t x)
-{
-    return (uint32_t)__builtin_amdgcn_ds_permute((int)(dst_lane << 2), (int)x);
-}
-
-// ---- one wavefront per piece of 33..64 bytes: element k in lane k; rounds on ballot masks ----
-// (returns the token count in lane 0, 0 in the others)
-__device__ uint32_t wave64_unit(const DevVocab &v, const Smem &sm, uint32_t j, uint32_t n, uint32_t p, uint32_t a,
-                                uint32_t *pval, uint32_t *scratch)
-{
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint64_t below = (1ull << lane) - 1ull;
-    uint32_t id = lane < n ? win_byte(sm, j + lane) : 0u;
-    uint32_t nx = wave_next(id);
-    uint32_t rk = lane + 1 < n ? __ldg(v.r2 + ((id << 8) | nx)) : NO_RANK;
-    for (;;) {
-        const uint32_t m = wave_min(rk);
-        const uint64_t H = __ballot(rk == m && m != NO_RANK);
-        if (H == 0) break;
-        // leftmost non-overlapping hits: in each chain of consecutive hits (only a pair (x, x) makes
-        // one) keep the hits at an even distance from the chain's first
-        const uint64_t rsE = H & ~(H << 1) & EVEN;          // chains starting at an even lane
-        const uint64_t runsE = H & ~(H + rsE);              // the hits of those chains
-        const uint64_t sel = (runsE & EVEN) | (H & ~runsE & ODD);
-        const uint64_t K = __ballot(lane < n) & ~(sel << 1);
-        const bool me_sel = (sel >> lane) & 1u;
-        const bool nx_sel = lane < 63 && ((sel >> (lane + 1)) & 1u);
-        const uint32_t kept = (uint32_t)__popcll(K);
-        const uint32_t dst = ((K >> lane) & 1u) ? (uint32_t)__popcll(K & below)
-                                                 : kept + (uint32_t)__popcll(~K & below);
-        id = lane_push(dst, me_sel ? 256u + m : id);
-        rk = lane_push(dst, (me_sel || nx_sel) ? PENDING : rk);
-        n = kept;
-        nx = wave_next(id);
-        if (lane >= n) rk = NO_RANK;
-        else if (rk == PENDING) rk = lane + 1 < n ? pair_rank(v, id, nx) : NO_RANK;
-    }
-    if (lane < n && n > 1) scratch[a + lane] = id;
-    if (lane == 0) pval[p] = n == 1 ? id : (PV_MULTI | n);
-    return lane == 0 ? n : 0u;
-}
-
-// ---- 16 lanes x 2 rows per piece of 17..32 bytes, four pieces per wavefront ----
-// (element e of piece s in lane 16 s + e % 16, row e / 16; two pieces' 32-bit masks packed in a
-// 64-bit word: a piece's last element never holds a hit, so neither shifts nor carries cross pieces)
-__device__ __forceinline__ uint64_t zip_rows(uint64_t r0, uint64_t r1, int half)
-{
-    const uint64_t a = (r0 >> (32 * half)) & 0xFFFFFFFFull, b = (r1 >> (32 * half)) & 0xFFFFFFFFull;
-    return (a & 0xFFFFull) | ((b & 0xFFFFull) << 16) | ((a & 0xFFFF0000ull) << 16) | ((b & 0xFFFF0000ull) << 32);
-}
-
-// each row of 16 lanes holds one piece (n = 0: none); returns its token count in the row's first lane
-__device__ uint32_t seg32_unit(const DevVocab &v, const Smem &sm, uint32_t *wb, uint32_t j, uint32_t n, uint32_t p,
-                               uint32_t a, uint32_t *pval, uint32_t *scratch)
-{
-    // wb: sid[4][33], srk[4][33], sra[64], srb[64], sres[64]
-    uint32_t *sid = wb, *srk = wb + 4 * 33, *sra = wb + 8 * 33, *srb = sra + 64, *sres = srb + 64;
-    const uint32_t lane = threadIdx.x & 63u, sg = lane >> 4, k = lane & 15u;
-    const uint64_t below = (1ull << lane) - 1ull;
-    uint32_t id0 = k < n ? win_byte(sm, j + k) : 0u;
-    uint32_t id1 = 16u + k < n ? win_byte(sm, j + 16u + k) : 0u;
-    uint32_t rk0, rk1;
-    {
-        const uint32_t d0 = __shfl_down(id0, 1, 64), f1 = __shfl(id1, lane & ~15u, 64);
-        const uint32_t nx0 = k == 15u ? f1 : d0, nx1 = __shfl_down(id1, 1, 64);
-        rk0 = k + 1u < n ? __ldg(v.r2 + ((id0 << 8) | nx0)) : NO_RANK;
-        rk1 = 17u + k < n ? __ldg(v.r2 + ((id1 << 8) | nx1)) : NO_RANK;
-    }
-    for (;;) {
-        uint32_t m = min(rk0, rk1);
-        m = row_min16(m);   // a piece is a DPP row
-        const uint64_t H0 = __ballot(rk0 == m && m != NO_RANK), H1 = __ballot(rk1 == m && m != NO_RANK);
-        if ((H0 | H1) == 0) break;
-        const uint64_t V0 = __ballot(k < n), V1 = __ballot(16u + k < n);
-        uint64_t S[2], K[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint64_t W = zip_rows(H0, H1, h);
-            const uint64_t rsE = W & ~(W << 1) & EVEN;
-            const uint64_t runsE = W & ~(W + rsE);
-            S[h] = (runsE & EVEN) | (W & ~runsE & ODD);
-            K[h] = zip_rows(V0, V1, h) & ~(S[h] << 1);
-        }
-        const uint32_t sh = 32u * (sg & 1u);
-        const uint32_t Ss = (uint32_t)((sg >> 1 ? S[1] : S[0]) >> sh);
-        const uint32_t Ks = (uint32_t)((sg >> 1 ? K[1] : K[0]) >> sh);
-        const uint32_t ms0 = (Ss >> k) & 1u, ms1 = (Ss >> (16u + k)) & 1u;
-        const uint32_t ns0 = (Ss >> (k + 1u)) & 1u, ns1 = k < 15u ? (Ss >> (17u + k)) & 1u : 0u;
-        uint32_t *rid = sid + 33 * sg, *rrk = srk + 33 * sg;
-        if ((Ks >> k) & 1u) {
-            const uint32_t o = (uint32_t)__popc(Ks & ((1u << k) - 1u));
-            rid[o] = ms0 ? 256u + m : id0;
-            rrk[o] = (ms0 || ns0) ? PENDING : rk0;
-        }
-        if ((Ks >> (16u + k)) & 1u) {
-            const uint32_t o = (uint32_t)__popc(Ks & ((1u << (16u + k)) - 1u));
-            rid[o] = ms1 ? 256u + m : id1;
-            rrk[o] = (ms1 || ns1) ? PENDING : rk1;
-        }
-        n = (uint32_t)__popc(Ks);
-        id0 = rid[k];
-        id1 = rid[16u + k];
-        rk0 = k < n ? rrk[k] : NO_RANK;
-        rk1 = 16u + k < n ? rrk[16u + k] : NO_RANK;
-        const uint32_t nx0 = rid[k + 1u], nx1 = rid[17u + k];
-        if (rk0 == PENDING && k + 1u >= n) rk0 = NO_RANK;
-        if (rk1 == PENDING && 17u + k >= n) rk1 = NO_RANK;
-        // gather the pairs to probe, one per lane, probe, scatter the ranks back
-        const bool pd0 = rk0 == PENDING, pd1 = rk1 == PENDING;
-        const uint64_t P0 = __ballot(pd0), P1 = __ballot(pd1);
-        const uint32_t c0 = (uint32_t)__popcll(P0), total = c0 + (uint32_t)__popcll(P1);
-        const uint32_t i0 = (uint32_t)__popcll(P0 & below), i1 = c0 + (uint32_t)__popcll(P1 & below);
-        for (uint32_t base = 0; base < total; base += 64u) {
-            if (pd0 && i0 - base < 64u) { sra[i0 - base] = id0; srb[i0 - base] = nx0; }
-            if (pd1 && i1 - base < 64u) { sra[i1 - base] = id1; srb[i1 - base] = nx1; }
-            uint32_t r = NO_RANK;
-            if (lane < total - base) r = pair_rank(v, sra[lane], srb[lane]);
-            sres[lane] = r;
-            if (pd0 && i0 - base < 64u) rk0 = sres[i0 - base];
-            if (pd1 && i1 - base < 64u) rk1 = sres[i1 - base];
-        }
-    }
-    if (n > 1) {
-        if (k < n) scratch[a + k] = id0;
-        if (16u + k < n) scratch[a + 16u + k] = id1;
-    }
-    if (k == 0 && n) pval[p] = n == 1 ? id0 : (PV_MULTI | n);
-    return k == 0 ? n : 0u;
-}
-
-__device__ __forceinline__ void shl128(uint64_t lo, uint64_t hi, uint64_t &rlo, uint64_t &rhi)
-{
-    rhi = (hi << 1) | (lo >> 63);
-    rlo = lo << 1;
-}
-
-// ---- one wavefront per piece of 65..128 bytes, two elements per lane (element e in lane e % 64 of
-// row e / 64): 128-bit masks, compaction through LDS (returns the token count in lane 0) ----
-__device__ uint32_t wave128_unit(const DevVocab &v, const Smem &sm, uint32_t *wb, uint32_t j, uint32_t n,
-                                 uint32_t p, uint32_t a, uint32_t *pval, uint32_t *scratch)
-{
-    uint32_t *sid = wb, *srk = wb + 128;
-    const uint32_t lane = threadIdx.x & 63u;
-    const uint64_t below = (1ull << lane) - 1ull;
-    uint32_t id0 = lane < n ? win_byte(sm, j + lane) : 0u;
-    uint32_t id1 = 64 + lane < n ? win_byte(sm, j + 64 + lane) : 0u;
-    uint32_t nx0 = wave_next(id0), nx1 = wave_next(id1);
-    if (lane == 63) nx0 = (uint32_t)__builtin_amdgcn_readlane((int)id1, 0);
-    uint32_t rk0 = lane + 1 < n ? __ldg(v.r2 + ((id0 << 8) | nx0)) : NO_RANK;
-    uint32_t rk1 = 65 + lane < n ? __ldg(v.r2 + ((id1 << 8) | nx1)) : NO_RANK;
-    for (;;) {
-        const uint32_t m = wave_min(min(rk0, rk1));
-        if (m == NO_RANK) break;
-        const uint64_t H0 = __ballot(rk0 == m), H1 = __ballot(rk1 == m);
-        uint64_t s0, s1;
-        shl128(H0, H1, s0, s1);
-        const uint64_t rsE0 = H0 & ~s0 & EVEN, rsE1 = H1 & ~s1 & EVEN;
-        const uint64_t a0 = H0 + rsE0;
-        const uint64_t a1 = H1 + rsE1 + (a0 < H0 ? 1ull : 0ull);
-        const uint64_t runsE0 = H0 & ~a0, runsE1 = H1 & ~a1;
-        const uint64_t sel0 = (runsE0 & EVEN) | (H0 & ~runsE0 & ODD);
-        const uint64_t sel1 = (runsE1 & EVEN) | (H1 & ~runsE1 & ODD);
-        uint64_t l0, l1;
-        shl128(sel0, sel1, l0, l1);
-        const uint64_t K0 = __ballot(lane < n) & ~l0, K1 = __ballot(64 + lane < n) & ~l1;
-        const bool ms0 = (sel0 >> lane) & 1u, ms1 = (sel1 >> lane) & 1u;
-        const bool ns0 = lane < 63 ? ((sel0 >> (lane + 1)) & 1u) : (sel1 & 1u);
-        const bool ns1 = lane < 63 && ((sel1 >> (lane + 1)) & 1u);
-        const uint32_t k0 = (uint32_t)__popcll(K0);
-        if ((K0 >> lane) & 1u) {
-            const uint32_t o = (uint32_t)__popcll(K0 & below);
-            sid[o] = ms0 ? 256u + m : id0;
-            srk[o] = (ms0 || ns0) ? PENDING : rk0;
-        }
-        if ((K1 >> lane) & 1u) {
-            const uint32_t o = k0 + (uint32_t)__popcll(K1 & below);
-            sid[o] = ms1 ? 256u + m : id1;
-            srk[o] = (ms1 || ns1) ? PENDING : rk1;
-        }
-        n = k0 + (uint32_t)__popcll(K1);
-        id0 = sid[lane];
-        rk0 = srk[lane];
-        id1 = sid[64 + lane];
-        rk1 = srk[64 + lane];
-        nx0 = wave_next(id0);
-        nx1 = wave_next(id1);
-        if (lane == 63) nx0 = (uint32_t)__builtin_amdgcn_readlane((int)id1, 0);
-        if (rk0 == PENDING || rk1 == PENDING) {
-            uint32_t q0, q1;
-            pair_rank2_general(v, id0, nx0, id1, nx1, q0, q1);
-            if (rk0 == PENDING) rk0 = q0;
-            if (rk1 == PENDING) rk1 = q1;
-        }
-        if (lane + 1 >= n) rk0 = NO_RANK;
-        if (65 + lane >= n) rk1 = NO_RANK;
-    }
-    if (n > 1) {
-        if (lane < n) scratch[a + lane] = id0;
-        if (64 + lane < n) scratch[a + 64 + lane] = id1;
-    }
-    if (lane == 0) pval[p] = n == 1 ? id0 : (PV_MULTI | n);
-    return lane == 0 ? n : 0u;
-}
-
-__device__ __forceinline__ uint32_t q_rel(uint32_t e) { return e & 0xFFFFu; }
-__device__ __forceinline__ uint32_t q_len(uint32_t e) { return e >> 16; }
-
-// Encode sm.q[0, nq) (all threads of the workgroup; the window holds the tile's bytes).  A counting
-// sort by length groups the pieces; the units are handed to wavefronts through an LDS counter, the
-// longest chains first.  Adds the token counts to sm.tok.
-__device__ void drain(const DevVocab &v, Smem &sm, uint32_t nq, const uint32_t *pstart, uint32_t *pval,
-                      uint32_t *scratch, uint32_t p0, uint64_t lo)
-{
-    const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
-    for (uint32_t i = tid; i < SHORT_MAX + 2; i += NT) sm.hist[i] = 0;
-    if (tid == 0) sm.unit = 0;
-    __syncthreads();
-    constexpr int PER = QCAP / NT;
-    uint32_t slot[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const uint32_t i = u * NT + tid;
-        slot[u] = i < nq ? atomicAdd(&sm.hist[q_len(sm.q[i])], 1u) : 0u;
-    }
-    __syncthreads();
-    if (wid == 0) {   // exclusive scan of the 130 bins, three per lane
-        uint32_t c[3], s3 = 0;
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            const uint32_t b = 3 * lane + t;
-            c[t] = b < SHORT_MAX + 2 ? sm.hist[b] : 0u;
-            s3 += c[t];
-        }
-        const uint32_t inc = wave_incl_sum(s3);
-        uint32_t run = inc - s3;
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            const uint32_t b = 3 * lane + t;
-            if (b < SHORT_MAX + 2) sm.hist[b] = run;
-            run += c[t];
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const uint32_t i = u * NT + tid;
-        if (i < nq) {
-            const uint32_t e = sm.q[i];
-            sm.buf[sm.hist[q_len(e)] + slot[u]] = e;
-        }
-    }
-    __syncthreads();
-    for (uint32_t i = tid; i < nq; i += NT) sm.q[i] = sm.buf[i];
-    const uint32_t n16 = sm.hist[17], n32 = sm.hist[33], n64 = sm.hist[65];
-    __syncthreads();
-    // units, longest chains first: 65..128 (one piece), 33..64 (one), 17..32 (four), <= 16 (64,
-    // longest group first)
-    const uint32_t u128 = nq - n64, u64 = n64 - n32, u32 = (n32 - n16 + 3) / 4, u16 = (n16 + 63) / 64;
-    const uint32_t units = u128 + u64 + u32 + u16;
-    uint32_t *wb = sm.buf + wid * WBUF;
-    uint32_t mytok = 0;
-    for (;;) {
-        uint32_t u = 0;
-        if (lane == 0) u = atomicAdd(&sm.unit, 1u);
-        u = (uint32_t)__builtin_amdgcn_readfirstlane((int)u);
-        if (u >= units) break;
-        if (u < u128) {
-            const uint32_t e = sm.q[n64 + u], p = p0 + q_rel(e), a = pstart[p];
-            mytok += wave128_unit(v, sm, wb, (uint32_t)(a - lo), q_len(e), p, a, pval, scratch);
-            continue;
-        }
-        u -= u128;
-        if (u < u64) {
-            const uint32_t e = sm.q[n32 + u], p = p0 + q_rel(e), a = pstart[p];
-            mytok += wave64_unit(v, sm, (uint32_t)(a - lo), q_len(e), p, a, pval, scratch);
-            continue;
-        }
-        u -= u64;
-        if (u < u32) {
-            const uint32_t i = n16 + 4 * u + (lane >> 4);
-            uint32_t p = 0, a = 0, len = 0;
-            if (i < n32) {
-                const uint32_t e = sm.q[i];
-                p = p0 + q_rel(e);
-                a = pstart[p];
-                len = q_len(e);
-            }
-            mytok += seg32_unit(v, sm, wb, (uint32_t)(a - lo), len, p, a, pval, scratch);
-            continue;
-        }
-        u -= u32;
-        // group u from the top: items [n16 - 64 (u + 1), n16 - 64 u), ascending by length
-        const int64_t i = (int64_t)n16 - 64 * (int64_t)(u + 1) + lane;
-        uint32_t p = 0, a = 0, len = 0;
-        if (i >= 0) {
-            const uint32_t e = sm.q[i];
-            p = p0 + q_rel(e);
-            a = pstart[p];
-            len = q_len(e);
-        }
-        const uint32_t lmax = q_len(sm.q[n16 - 64 * u - 1]);
-        const uint32_t j = (uint32_t)(a - lo);
-        if (lmax <= 8u) mytok += lane_unit<8>(v, sm, j, len, p, a, pval, scratch);
-        else if (lmax <= 12u) mytok += lane_unit<12>(v, sm, j, len, p, a, pval, scratch);
-        else mytok += lane_unit<16>(v, sm, j, len, p, a, pval, scratch);
-    }
-    mytok = wave_incl_sum(mytok);
-    if (lane == 63 && mytok) atomicAdd(&sm.tok, mytok);
-    __syncthreads();
 }
 
 // the byte window [lo, lo + WIN), zero past the batch.  Every thread issues all of its loads before
@@ -635,7 +233,7 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
     const uint32_t tile = blockIdx.x;
     const uint64_t lo = (uint64_t)tile * TILE;
     const uint32_t p0 = tbase[tile], p1 = tbase[tile + 1], cnt = p1 - p0;
-    uint32_t *mlist = (uint32_t *)(ws + L.mlist) + p0;
+    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     uint32_t *llist = (uint32_t *)(ws + L.tokoff) + p0;   // the 8..32-byte pieces
 
     // the window and the hot sets (their loads issued together)
@@ -653,7 +251,15 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
         sm.ln = 0;
     }
     __syncthreads();
-    auto list_miss = [&](uint32_t i, uint32_t len) { mlist[atomicAdd(&sm.qn, 1u)] = i | (len << 16); };
+    // a piece left for BPE: queued (index in the tile | length << 16) in LDS, past its capacity in
+    // the tile's own slice of a device array; at the end the queue goes to the BPE lists in one run
+    // per list
+    uint32_t *spill = (uint32_t *)(ws + L.tspill) + p0;
+    auto list_miss = [&](uint32_t i, uint32_t len) {
+        const uint32_t slot = atomicAdd(&sm.qn, 1u);
+        if (slot < (uint32_t)MQ) sm.q[slot] = i | (len << 16);
+        else spill[slot - MQ] = i | (len << 16);
+    };
 
     uint32_t mytok = 0;
     constexpr int K = 4;
@@ -708,9 +314,7 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
                 } else {
                     list_miss(i, len);
                 }
-            } else {
-                mytok += pval[p0 + i] & PV_COUNT;   // written by the long-piece kernels
-            }
+            }   // longer pieces are listed by the pieces kernel and counted by the BPE kernels
         }
         // the global lookups of the pieces the hot sets did not answer: all loads in flight at once
         uint4 x[K], y[K];
@@ -728,9 +332,9 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
         for (int u = 0; u < K; ++u) {
             const uint32_t i = i0 + u * NT + tid;
             if (kind[u] == 2) {
-                const uint32_t r = x[u].x;
+                const uint32_t r = x[u].x;   // the pair's rank word
                 if (r != NO_RANK) {
-                    pval[p0 + i] = 256u + r;
+                    pval[p0 + i] = 256u + (r >> 2);
                     ++mytok;
                 } else {   // no merge joins the two bytes: two tokens
                     pval[p0 + i] = PV_MULTI | 2u;
@@ -777,43 +381,33 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
         }
     }
 
-    // tokens of the pieces resolved here (k_bpe_tiles adds the others)
+    // the queued pieces to the BPE lists: count per list, one reservation per list, then the tile's
+    // items in one run per list (the slice is read back by the threads that wrote it or, after the
+    // barrier, by others of this workgroup)
+    __syncthreads();
+    const uint32_t nq = sm.qn;
+    if (tid < NMISS) sm.rn[tid] = 0;
+    __syncthreads();
+    auto queued = [&](uint32_t k) { return k < (uint32_t)MQ ? sm.q[k] : spill[k - MQ]; };
+    for (uint32_t k = tid; k < nq; k += NT) atomicAdd(&sm.rn[route_of(queued(k) >> 16)], 1u);
+    __syncthreads();
+    if (tid < NMISS) {
+        const uint32_t c = sm.rn[tid];
+        sm.rb[tid] = c ? atomicAdd(&ctrl->miss_count[tid], c) : 0u;
+        sm.rn[tid] = 0;
+    }
+    __syncthreads();
+    for (uint32_t k = tid; k < nq; k += NT) {
+        const uint32_t e = queued(k), r = route_of(e >> 16);
+        route_list(ws, L, r)[sm.rb[r] + atomicAdd(&sm.rn[r], 1u)] = p0 + (e & 0xFFFFu);
+    }
+
+    // tokens of the pieces resolved here (the BPE kernels add the others)
     uint32_t tile_tok;
     (void)wg_excl_sum(sm, mytok, &tile_tok);
     if (tid == 0) {
         ((uint32_t *)(ws + L.tcount))[tile] = tile_tok;
-        ((uint32_t *)(ws + L.tmiss))[tile] = sm.qn;
         if (tile_tok) atomicAdd((uint32_t *)(ws + L.tsb) + tile / 64u, tile_tok);
-    }
-}
-
-__global__ __launch_bounds__(NT) void k_bpe_tiles(DevVocab v, const uint8_t *__restrict__ bytes, uint64_t n,
-                                                  uint8_t *ws, Layout L, uint32_t S)
-{
-    __shared__ Smem sm;
-    const uint32_t tile = blockIdx.x / S, s = blockIdx.x % S;
-    const uint32_t nm = ((const uint32_t *)(ws + L.tmiss))[tile];
-    if (nm == 0) return;
-    const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
-    const uint32_t p0 = ((const uint32_t *)(ws + L.tbase))[tile];
-    const uint32_t *mlist = (const uint32_t *)(ws + L.mlist) + p0;
-    uint32_t *pval = (uint32_t *)(ws + L.pval);
-    uint32_t *scratch = (uint32_t *)(ws + L.scratch);
-    const uint64_t lo = (uint64_t)tile * TILE;
-    load_window(sm, bytes, n, lo);
-    if (threadIdx.x == 0) sm.tok = 0;
-    // this workgroup's share of the list: slice s of S
-    const uint32_t per = (nm + S - 1) / S, i0 = min(nm, s * per), i1 = min(nm, i0 + per);
-    for (uint32_t c0 = i0; c0 < i1; c0 += QCAP) {
-        const uint32_t nq = min((uint32_t)QCAP, i1 - c0);
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < nq; i += NT) sm.q[i] = mlist[c0 + i];
-        __syncthreads();
-        drain(v, sm, nq, pstart, pval, scratch, p0, lo);
-    }
-    if (threadIdx.x == 0 && sm.tok) {
-        atomicAdd((uint32_t *)(ws + L.tcount) + tile, sm.tok);
-        atomicAdd((uint32_t *)(ws + L.tsb) + tile / 64u, sm.tok);
     }
 }
 
@@ -964,17 +558,6 @@ hipError_t launch_tiles(const DevVocab &v, const Batch &b, hipStream_t s, const 
         hipLaunchKernelGGL(k_tiles<true>, dim3(L.n_tiles), dim3(NT), 0, s, v, b.bytes, b.n, b.ws, L);
     else
         hipLaunchKernelGGL(k_tiles<false>, dim3(L.n_tiles), dim3(NT), 0, s, v, b.bytes, b.n, b.ws, L);
-    return hipGetLastError();
-}
-
-hipError_t launch_bpe_tiles(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev)
-{
-    const Layout &L = b.L;
-    if (L.n_tiles == 0) return hipGetLastError();
-    // few tiles (a single request): several workgroups share each tile's units
-    const uint32_t S = L.n_tiles >= 1024 ? 1u : (L.n_tiles >= 256 ? 4u : 8u);
-    LaunchScope k(ev, TK_BPE_TILES, s);
-    hipLaunchKernelGGL(k_bpe_tiles, dim3(L.n_tiles * S), dim3(NT), 0, s, v, b.bytes, b.n, b.ws, L, S);
     return hipGetLastError();
 }
 

@@ -569,13 +569,13 @@ int build_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts)
     if (e == hipSuccess) e = hipMalloc((void **)&dws, L.total);
     if (e == hipSuccess) e = hipMemcpy(dbytes, batch.data(), N, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(dws + L.ctrl, 0, sizeof(Ctrl));
-    if (e == hipSuccess) e = hipMemset(dws + L.tilex, 0, 4ull * L.n_scan_tiles);
     if (e == hipSuccess) e = hipMemcpy(dws + L.ctrl + offsetof(Ctrl, n_pieces), &npc, 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(dws + L.pstart, starts.data(), 4ull * starts.size(), hipMemcpyHostToDevice);
     if (e == hipSuccess) {
         Batch b{dbytes, nullptr, 1, N, dws, L};
         e = launch_route(v->dv, b, 0, nullptr);
+        if (e == hipSuccess) e = launch_giant_prep(v->dv, b, 0, nullptr);
         if (e == hipSuccess) e = launch_bpe(v->dv, b, 0, nullptr);
     }
     if (e == hipSuccess) e = hipStreamSynchronize(0);
@@ -727,14 +727,22 @@ extern "C" int toktier_load_vocab_ex(const uint32_t *merges, uint32_t n_merges, 
         return TOKTIER_E_BAD_FAMILY;
     if (n_merges > TOKTIER_MAX_MERGES) return TOKTIER_E_BAD_MERGES;
 
+    // operand flags of every token: bit 1 = the left operand of some merge, bit 0 = the right one
+    std::vector<uint8_t> lr(256ull + n_merges, 0);
+    for (uint32_t r = 0; r < n_merges; ++r) {
+        const uint32_t a = merges[2 * r], b = merges[2 * r + 1];
+        if (a >= 256u + r || b >= 256u + r) return TOKTIER_E_BAD_MERGES;   // rank-inconsistent
+        lr[a] |= 2u;
+        lr[b] |= 1u;
+    }
+    auto rkx = [&](uint32_t r) { return (r << 2) | lr[256u + r]; };
     std::vector<uint32_t> r2(65536, NO_RANK);
     uint32_t n_general = 0;
     for (uint32_t r = 0; r < n_merges; ++r) {
         uint32_t a = merges[2 * r], b = merges[2 * r + 1];
-        if (a >= 256u + r || b >= 256u + r) return TOKTIER_E_BAD_MERGES;   // rank-inconsistent
         if ((a | b) < 256u) {
             if (r2[(a << 8) | b] != NO_RANK) return TOKTIER_E_BAD_MERGES;   // duplicate pair
-            r2[(a << 8) | b] = r;
+            r2[(a << 8) | b] = rkx(r);
         } else {
             ++n_general;
         }
@@ -744,18 +752,18 @@ extern "C" int toktier_load_vocab_ex(const uint32_t *merges, uint32_t n_merges, 
     pkeys.reserve(n_general);
     for (uint32_t r = 0; r < n_merges; ++r) {
         const uint32_t a = merges[2 * r], b = merges[2 * r + 1];
-        if ((a | b) >= 256u) pkeys.push_back((((uint64_t)a << 21) | b) << 21 | r);
+        if ((a | b) >= 256u) pkeys.push_back((((uint64_t)a << 21) | b) << 22 | rkx(r));
     }
     {
         std::vector<uint64_t> ks(pkeys.size());
-        for (size_t i = 0; i < pkeys.size(); ++i) ks[i] = pkeys[i] >> 21;
+        for (size_t i = 0; i < pkeys.size(); ++i) ks[i] = pkeys[i] >> 22;
         std::sort(ks.begin(), ks.end());
         if (std::adjacent_find(ks.begin(), ks.end()) != ks.end()) return TOKTIER_E_BAD_MERGES;   // duplicate pair
     }
     std::vector<uint32_t> pwhere;
     uint32_t pcap = 0;
     uint64_t pseed = 0;
-    cuckoo_build((uint32_t)pkeys.size(), 0x7A1Bull, [&](uint32_t i) { return pkeys[i] >> 21; }, pwhere, pcap, pseed);
+    cuckoo_build((uint32_t)pkeys.size(), 0x7A1Bull, [&](uint32_t i) { return pkeys[i] >> 22; }, pwhere, pcap, pseed);
     const uint64_t cap = pcap;
     std::vector<uint64_t> slots(cap, EMPTY_SLOT);
     for (uint32_t h = 0; h < pcap; ++h)
@@ -935,15 +943,15 @@ int read_ctrl(void *workspace, hipStream_t s, Ctrl *out)
 
 namespace {
 
-// the encode chain: pre-tokenizer (with the long-piece lists), the long pieces, the tile encoder,
-// BPE of the pieces it left, the output writer
+// the encode chain: pre-tokenizer (with the long-piece lists), seams and chunks of giant pieces, the
+// tile encoder (with the short-piece lists), BPE of every listed piece, the output writer
 hipError_t launch_chain(const DevVocab &v, const Batch &b, uint32_t *out_ids, uint64_t *out_offsets,
                         uint32_t *out_spans, hipStream_t s, const Events *ev)
 {
     hipError_t e = launch_pretokenize(v, b, s, ev);
-    if (e == hipSuccess) e = launch_bpe(v, b, s, ev);
+    if (e == hipSuccess) e = launch_giant_prep(v, b, s, ev);
     if (e == hipSuccess) e = launch_tiles(v, b, s, ev);
-    if (e == hipSuccess) e = launch_bpe_tiles(v, b, s, ev);
+    if (e == hipSuccess) e = launch_bpe(v, b, s, ev);
     if (e == hipSuccess) e = launch_emit(v, b, out_ids, out_offsets, out_spans, s, ev);
     return e;
 }

@@ -62,8 +62,8 @@ enum {
     TOKTIER_E_OOM = 7            /* host or device allocation failed while loading a vocabulary */
 };
 
-/* Largest merge count accepted: IDs must stay below 2^21 - 1. */
-#define TOKTIER_MAX_MERGES ((1u << 21) - 257u)
+/* Largest merge count accepted: ranks stay below 2^20 (and IDs below 2^21). */
+#define TOKTIER_MAX_MERGES ((1u << 20) - 1u)
 
 /*
  * Load a merge list and its rule family; build the device tables on the current HIP device.
@@ -249,16 +249,16 @@ enum {
     TOKTIER_K_PIECES,         /* UTF-8 decode + validation, automaton scan, piece starts; pieces    */
                               /* longer than 128 bytes listed by length                            */
     TOKTIER_K_GIANT_SEAMS,    /* pieces > 4096 bytes: seams no merge crosses, then chunks           */
-    TOKTIER_K_BPE_CHUNKS,     /* BPE of the chunks of <= 128 bytes of those pieces                  */
+    TOKTIER_K_TILES,          /* per 8 KiB tile: single bytes and whole-piece table lookups; the    */
+                              /* other pieces of <= 128 bytes listed by length for BPE              */
+    TOKTIER_K_BPE_SHORT,      /* BPE of the listed pieces and chunks of <= 128 bytes: lane per      */
+                              /* piece (<= 16), 16 lanes x 2 rows (<= 32), a wavefront (<= 64), two */
+                              /* elements per lane (<= 128)                                         */
     TOKTIER_K_BPE_WAVE,       /* BPE, one wavefront per piece of 129..1024 bytes or chunk           */
     TOKTIER_K_BPE_BLOCK,      /* BPE, one workgroup per piece of 1025..4096 bytes or chunk          */
     TOKTIER_K_BPE_GIANT,      /* BPE, one workgroup per longer chunk, sequence in device memory;    */
                               /* then (last workgroup) each giant piece's token count and its       */
                               /* chunks' output places                                              */
-    TOKTIER_K_TILES,          /* per 8 KiB tile: single bytes and whole-piece table lookups; the    */
-                              /* other pieces of <= 128 bytes listed in the tile's slice            */
-    TOKTIER_K_BPE_TILES,      /* per tile, BPE of those pieces: lane per piece (<= 16), 16 lanes x  */
-                              /* 2 rows (<= 32), a wavefront (<= 64), two elements per lane (<= 128)*/
     TOKTIER_K_EMIT,           /* per tile: IDs placed by a scan of token counts, document offsets,  */
                               /* token spans                                                        */
     TOKTIER_K_COUNT
