@@ -27,8 +27,12 @@ FAMILIES = {"gpt2": 1, "cl100k": 2, "o200k": 3, "deepseek": 4}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _BUILD = os.path.join(_HERE, "_build")
-_SO = os.path.join(_BUILD, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
+# ORACLE_SANITIZE=1: a separate build with AddressSanitizer and UndefinedBehaviorSanitizer (the
+# process must preload their runtimes; see tests/test_oracle_sanitized.py)
+SANITIZE = os.environ.get("ORACLE_SANITIZE") == "1"
+_SO = os.path.join(_BUILD, "liboracle_san.so" if SANITIZE else "liboracle.so")
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
 
 _ERRORS = {
     -1: "invalid UTF-8",
@@ -47,11 +51,12 @@ class OracleError(RuntimeError):
 
 
 def build(force=True):
-    """Compile oracle.c with gcc into oracle/_build/liboracle.so."""
+    """Compile oracle.c with gcc into oracle/_build/liboracle.so (liboracle_san.so when sanitized)."""
     os.makedirs(_BUILD, exist_ok=True)
     if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
         tmp = _SO + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-Wall", "-shared", "-fPIC", "-o", tmp, _SRC])
+        opt = SAN_FLAGS if SANITIZE else ["-O2"]
+        subprocess.check_call(["gcc"] + opt + ["-std=c99", "-Wall", "-shared", "-fPIC", "-o", tmp, _SRC])
         os.replace(tmp, _SO)
     return _SO
 
