@@ -16,7 +16,8 @@
 //   k_emit   per tile: its first output index from the counters (the groups before its own, then
 //            the tiles before it in its group); rounds of 256 pieces, a workgroup scan of their
 //            token counts places their IDs (consecutive pieces write consecutive IDs); per-document
-//            token offsets; optional token spans.  No workgroup waits for another.
+//            token offsets; optional token spans.  Up to 32 more workgroups copy the IDs of the giant
+//            pieces chunk by chunk, a thread per chunk.  No workgroup waits for another.
 #include "internal.h"
 
 namespace tt {
@@ -141,58 +142,167 @@ __device__ __forceinline__ uint32_t wg_excl_sum(S &sm, uint32_t x, uint32_t *tot
     return before + inc - x;
 }
 
-// the giant piece p: its index among the giant pieces (its chunks are gnc[g] table entries from gc0[g])
-__device__ uint32_t giant_index(const uint8_t *ws, const Layout &L, uint32_t p)
-{
-    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
-    const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
-    const uint32_t cnt = ctrl->bin_count[2];
-    for (uint32_t g = 0; g < cnt; ++g)
-        if (list[g] == p) return g;
-    return NO_PIECE;
-}
-
-// the IDs of a piece encoded before the tile encoder (longer than SHORT_MAX bytes), copied by one
-// wavefront from scratch (for a giant piece, chunk by chunk to each chunk's place in the piece's
-// output); with spans, a wavefront scan of the token lengths from the piece's (chunk's) start
+// The IDs of a piece of 129..BLOCK_MAX bytes, encoded before the tile encoder, copied by one
+// wavefront from scratch[a ...] to out_ids[o ...] (eight tokens per lane and step, their loads in
+// flight together); with spans, a wavefront scan of the token lengths from the piece's start.
 template <bool SPANS>
-__device__ void copy_long(const uint8_t *ws, const Layout &L, uint32_t p, uint32_t a, uint32_t len, uint32_t o,
-                          uint32_t c, uint32_t *out_ids, uint32_t *out_spans, const uint32_t *tok_len)
+__device__ void copy_long(const uint8_t *ws, const Layout &L, uint32_t a, uint32_t o, uint32_t cnt,
+                          uint32_t *out_ids, uint32_t *out_spans, const uint32_t *tok_len)
 {
+    constexpr uint32_t U = 8;
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t *scratch = (const uint32_t *)(ws + L.scratch);
-    uint32_t g = NO_PIECE, nc = 1, c0 = 0;
-    if (len > (uint32_t)BLOCK_MAX) g = giant_index(ws, L, p);   // (always listed: the pieces kernel lists by length)
-    if (g != NO_PIECE) {
-        c0 = ((const uint32_t *)(ws + L.gc0))[g];
-        nc = ((const uint32_t *)(ws + L.gnc))[g];
-    }
-    for (uint32_t k = 0; k < nc; ++k) {
-        const uint32_t *src;
-        uint32_t dst, cnt, carry;
-        if (g == NO_PIECE) {
-            src = scratch + a;
-            dst = o;
-            cnt = c;
-            carry = a;
-        } else {
-            const uint32_t ck = c0 + k;
-            const uint32_t cs = ((const uint32_t *)(ws + L.cstart))[ck];
-            src = scratch + cs;
-            dst = o + ((const uint32_t *)(ws + L.clen))[ck];   // the chunk's place in the piece's output
-            cnt = ((const uint32_t *)(ws + L.ccount))[ck];
-            carry = cs;
+    const uint32_t *src = (const uint32_t *)(ws + L.scratch) + a;
+    uint32_t carry = a;
+    for (uint32_t t0 = 0; t0 < cnt; t0 += 64u * U) {
+        uint32_t id[U];
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            const uint32_t t = t0 + 64u * u + lane;
+            id[u] = t < cnt ? src[t] : 0u;
         }
-        for (uint32_t t0 = 0; t0 < cnt; t0 += 64) {
-            const uint32_t t = t0 + lane;
-            const uint32_t id = t < cnt ? src[t] : 0u;
-            if (t < cnt) out_ids[dst + t] = id;
+#pragma unroll
+        for (uint32_t u = 0; u < U; ++u) {
+            const uint32_t t = t0 + 64u * u + lane;
+            if (t < cnt) out_ids[o + t] = id[u];
             if (SPANS) {
-                const uint32_t l = t < cnt ? tok_len[id] : 0u;
+                const uint32_t l = t < cnt ? tok_len[id[u]] : 0u;
                 const uint32_t inc = wave_incl_sum(l);
-                if (t < cnt) out_spans[dst + t] = carry + inc - l;
+                if (t < cnt) out_spans[o + t] = carry + inc - l;
                 carry += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
             }
+        }
+    }
+}
+
+// Workgroups past the tiles: the IDs of the giant pieces (longer than BLOCK_MAX), chunk by chunk.
+// Each giant piece gets a share of these workgroups; a workgroup finds the piece's first output
+// index itself (its tile's first index from the counters, plus the tokens of the tile's pieces
+// before it).  Chunk k's IDs sit at scratch[its start byte ...] and go to the piece's output at the
+// chunk's place (recorded by the giant join in clen).  The share's workgroups walk the chunks in
+// blocks of NT: a chunk of at most SMALL_CHUNK tokens is copied by one thread (of the workgroup the
+// chunk's index selects), a longer one by all of them, each workgroup taking its part of the
+// chunk's tokens.  With spans, a chunk's spans run from its start byte.
+constexpr uint32_t SMALL_CHUNK = 64;
+
+// WG-wide inclusive sum helper for emit_giant (returns the workgroup total to every thread)
+__device__ __forceinline__ uint32_t wg_total(uint32_t x, uint32_t *red)
+{
+    const uint32_t lane = threadIdx.x & 63u, wid = threadIdx.x >> 6;
+    x = wave_incl_sum(x);
+    if (lane == 63) red[wid] = x;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) t += red[k];
+    __syncthreads();
+    return t;
+}
+
+template <bool SPANS>
+__device__ void emit_giant(const uint8_t *ws, const Layout &L, uint32_t w, uint32_t nw, uint32_t *out_ids,
+                           uint32_t *out_spans, const uint32_t *tok_len)
+{
+    __shared__ uint32_t s_red[NW], s_big[NT], s_nbig;
+    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+    const uint32_t count = ctrl->bin_count[2];
+    if (count == 0) return;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart), *pval = (const uint32_t *)(ws + L.pval);
+    const uint32_t *tbase = (const uint32_t *)(ws + L.tbase), *tcount = (const uint32_t *)(ws + L.tcount);
+    const uint32_t *tsb = (const uint32_t *)(ws + L.tsb);
+    const uint32_t *gc0 = (const uint32_t *)(ws + L.gc0), *gnc = (const uint32_t *)(ws + L.gnc);
+    const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *cdest = (const uint32_t *)(ws + L.clen);
+    const uint32_t *ccount = (const uint32_t *)(ws + L.ccount);
+    const uint32_t *scratch = (const uint32_t *)(ws + L.scratch);
+    // workgroups per piece (at least one); this workgroup's pieces g = w / per, w / per + nw / per, ...
+    const uint32_t per = count >= nw ? 1u : nw / count;
+    const uint32_t sub = w % per;
+    for (uint32_t g = w / per; g < count; g += nw / per) {
+        const uint32_t p = list[g], t = pstart[p] / (uint32_t)TILE, q0 = tbase[t];
+        // first output index of p: groups of 64 tiles before t's, tiles before t in its group, pieces
+        // of t before p
+        uint32_t x = 0;
+        for (uint32_t k = tid; k < t / 64u; k += NT) x += tsb[k];
+        for (uint32_t k = 64u * (t / 64u) + tid; k < t; k += NT) x += tcount[k];
+        for (uint32_t q = q0 + tid; q < p; q += NT) {
+            const uint32_t pv = pval[q];
+            x += (pv & PV_MULTI) ? (pv & PV_COUNT) : 1u;
+        }
+        const uint32_t o = wg_total(x, s_red), c0 = gc0[g], nc = gnc[g];
+        for (uint32_t k0 = 0; k0 < nc; k0 += NT) {
+            if (tid == 0) s_nbig = 0;
+            __syncthreads();
+            const uint32_t k = k0 + tid;
+            if (k < nc) {
+                const uint32_t ck = c0 + k, cnt = ccount[ck];
+                if (cnt > SMALL_CHUNK) {
+                    s_big[atomicAdd(&s_nbig, 1u)] = ck;
+                } else if (k % per == sub) {
+                    const uint32_t cs = cstart[ck], dst = o + cdest[ck];
+                    uint32_t sp = cs;
+                    for (uint32_t t0 = 0; t0 < cnt; t0 += 8) {
+                        uint32_t id[8];
+#pragma unroll
+                        for (uint32_t u = 0; u < 8; ++u) id[u] = t0 + u < cnt ? scratch[cs + t0 + u] : 0u;
+#pragma unroll
+                        for (uint32_t u = 0; u < 8; ++u) {
+                            if (t0 + u < cnt) {
+                                out_ids[dst + t0 + u] = id[u];
+                                if (SPANS) {
+                                    out_spans[dst + t0 + u] = sp;
+                                    sp += tok_len[id[u]];
+                                }
+                            }
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            // the long chunks of this block: every workgroup of the share takes its part of each
+            const uint32_t nb = s_nbig;
+            for (uint32_t b = 0; b < nb; ++b) {
+                const uint32_t ck = s_big[b], cs = cstart[ck], dst = o + cdest[ck], cnt = ccount[ck];
+                const uint32_t r0 = (uint32_t)((uint64_t)cnt * sub / per), r1 = (uint32_t)((uint64_t)cnt * (sub + 1) / per);
+                uint32_t carry = cs;
+                if (SPANS) {   // the lengths of the chunk's tokens before this part
+                    uint32_t y = 0;
+                    for (uint32_t q = tid; q < r0; q += NT) y += tok_len[scratch[cs + q]];
+                    carry += wg_total(y, s_red);
+                }
+                constexpr uint32_t U = 8;
+                for (uint32_t t0 = r0; t0 < r1; t0 += U * NT) {
+                    uint32_t id[U];
+#pragma unroll
+                    for (uint32_t u = 0; u < U; ++u) {
+                        const uint32_t q = t0 + u * NT + tid;
+                        id[u] = q < r1 ? scratch[cs + q] : 0u;
+                    }
+#pragma unroll
+                    for (uint32_t u = 0; u < U; ++u) {
+                        const uint32_t q = t0 + u * NT + tid;
+                        if (q < r1) out_ids[dst + q] = id[u];
+                        if (SPANS) {
+                            const uint32_t l = q < r1 ? tok_len[id[u]] : 0u;
+                            const uint32_t lane = tid & 63u, wid = tid >> 6;
+                            const uint32_t inc = wave_incl_sum(l);
+                            if (lane == 63) s_red[wid] = inc;
+                            __syncthreads();
+                            uint32_t before = 0, tot = 0;
+#pragma unroll
+                            for (int k2 = 0; k2 < NW; ++k2) {
+                                const uint32_t z = s_red[k2];
+                                tot += z;
+                                before += (uint32_t)k2 < wid ? z : 0u;
+                            }
+                            __syncthreads();
+                            if (q < r1) out_spans[dst + q] = carry + before + inc - l;
+                            carry += tot;
+                        }
+                    }
+                }
+            }
+            __syncthreads();   // s_big and s_nbig are rewritten by the next block
         }
     }
 }
@@ -417,6 +527,10 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
                                              uint64_t *__restrict__ out_offsets, uint32_t *__restrict__ out_spans)
 {
     __shared__ EmitSmem sm;
+    if (blockIdx.x >= L.n_tiles) {   // the giant pieces' IDs
+        emit_giant<SPANS>(ws, L, blockIdx.x - L.n_tiles, gridDim.x - L.n_tiles, out_ids, out_spans, v.tok_len);
+        return;
+    }
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *__restrict__ tbase = (const uint32_t *)(ws + L.tbase);
@@ -521,16 +635,16 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
                 for (uint32_t d = lo_d; d < dd.y && offsets[d] == a; ++d) out_offsets[d] = o;
             }
         }
-        // long pieces of this round: copied by the whole wavefront, one after the other
-        uint64_t lm = __ballot(ok && (pv & PV_LONG));
+        // long pieces of this round: copied by the whole wavefront, one after the other (the giant
+        // ones by the workgroups past the tiles)
+        uint64_t lm = __ballot(ok && (pv & PV_LONG) && pstart[p + 1] - a <= (uint32_t)BLOCK_MAX);
         while (lm) {
             const int k = __ffsll((unsigned long long)lm) - 1;
             lm &= lm - 1;
-            const uint32_t lp = (uint32_t)__builtin_amdgcn_readlane((int)p, k);
             const uint32_t la = (uint32_t)__builtin_amdgcn_readlane((int)a, k);
             const uint32_t lo_ = (uint32_t)__builtin_amdgcn_readlane((int)o, k);
             const uint32_t lc = (uint32_t)__builtin_amdgcn_readlane((int)c, k);
-            copy_long<SPANS>(ws, L, lp, la, pstart[lp + 1] - la, lo_, lc, out_ids, out_spans, tok_len);
+            copy_long<SPANS>(ws, L, la, lo_, lc, out_ids, out_spans, tok_len);
         }
       }
     }
@@ -570,11 +684,13 @@ hipError_t launch_emit(const DevVocab &v, const Batch &b, uint32_t *out_ids, uin
         hipLaunchKernelGGL(k_tiles_empty, dim3(1), dim3(256), 0, s, b.n_docs, out_offsets, b.ws, L);
         return hipGetLastError();
     }
+    // the tiles, then up to 32 workgroups for the giant pieces (they exit at once when there are none)
+    const uint32_t g = L.n_tiles + (L.cap_giant < 32 ? L.cap_giant : 32);
     if (out_spans)
-        hipLaunchKernelGGL(k_emit<true>, dim3(L.n_tiles), dim3(NT), 0, s, v, b.offsets, b.n_docs, b.n, b.ws, L, out_ids,
+        hipLaunchKernelGGL(k_emit<true>, dim3(g), dim3(NT), 0, s, v, b.offsets, b.n_docs, b.n, b.ws, L, out_ids,
                            out_offsets, out_spans);
     else
-        hipLaunchKernelGGL(k_emit<false>, dim3(L.n_tiles), dim3(NT), 0, s, v, b.offsets, b.n_docs, b.n, b.ws, L, out_ids,
+        hipLaunchKernelGGL(k_emit<false>, dim3(g), dim3(NT), 0, s, v, b.offsets, b.n_docs, b.n, b.ws, L, out_ids,
                            out_offsets, out_spans);
     return hipGetLastError();
 }
