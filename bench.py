@@ -16,11 +16,17 @@ Prints ONE JSON line:
                same request replayed through a captured HIP graph of the kernel chain (toktier_plan)
   value_two_in_flight  the same steps alternating between two streams (two batches in flight, each
                with its own workspace and outputs)
-  roofline     the dominant kernel: algorithmic bytes per launch / its average duration measured with
-               HIP events recorded around that launch inside the timed steps, against 8 TB/s
+  path_alg_frac_of_hbm  the headline roofline figure: the path's algorithmic bytes (input, 4 B per
+               token ID, document offsets in and out) per step / the step time / 8 TB/s
+  roofline     the dominant kernel (longest average duration, HIP events recorded around each launch
+               on its stream inside the timed steps): its bound as the instruction counters of
+               profiles/ show it ("alu": VALU issue, against 614.4 G wavefront instructions/s), the
+               committed per-launch counts over the live duration; its own algorithmic bytes and
+               their fraction of 8 TB/s beside; kernels: every kernel's duration and own bytes
   cpu_baseline the CPU oracle (serial pre-tokenizer + priority-queue BPE, one document per worker
-               process) timed on this host's cores over a bounded sample of the same batch; the same
-               run checks the GPU output against the oracle bit for bit ("bit_exact")
+               process) timed on this host's available cores over a bounded sample of the same batch,
+               and single-core on each single-request configuration; the same run checks the GPU
+               output against the oracle bit for bit ("bit_exact")
 """
 import argparse
 import hashlib
@@ -43,12 +49,29 @@ HBM_PEAK_GBS = 8000.0
 MAIN = "c4_batch64"
 LATENCY = ("c1_ec4k", "c2_at100k", "c3_mix1m", "c5_adv4m4")
 
-# input bytes each kernel launch processes (the unit of the algorithmic-bytes figure)
-# (bytes of the pieces in the length range the launch serves)
-UNITS = {
-    "summary": "all", "pieces": "all", "tiles": "all", "emit": "all", "bpe_short": "le128", "giant_seams": "giant",
-    "bpe_wave": "wave", "bpe_block": "block", "bpe_giant": "giant",
-}
+VALU_PEAK = 256 * 4 * 2.4e9 / 4 / 1e9   # G wavefront instructions/s: 256 CUs x 4 SIMDs, 4 cycles per wave64 op
+
+
+def own_bytes(n, D, P, T, M, Bm, Tm):
+    """Algorithmic bytes each kernel moves itself: n input bytes, D documents, P pieces, T tokens, M
+    pieces left for BPE (Bm of their bytes, Tm of their tokens)."""
+    return {
+        "summary": 8 * (D + 1),
+        "pieces": n + 4 * P + 8 * (D + 1),                       # input in, piece starts out
+        "giant_seams": 0, "bpe_wave": 0, "bpe_block": 0, "bpe_giant": 0,   # no piece over 128 bytes here
+        "tiles": n + 4 * (P + 1) + 4 * P + 4 * M,                 # input and starts in, results and lists out
+        "bpe_short": Bm + 4 * M + 8 * M + 4 * M + 4 * Tm,         # bytes, list, starts in; results out
+        "emit": 4 * P + 4 * P + 4 * Tm + 4 * T + 16 * (D + 1),   # results, starts, BPE IDs in; IDs out
+    }
+
+
+def token_lengths(merges):
+    """Byte length of every token ID of a merge list (256 single bytes, then one per merge)."""
+    m = np.asarray(merges, dtype=np.int64).reshape(-1, 2)
+    ln = np.ones(256 + m.shape[0], dtype=np.int64)
+    for r, (a, b) in enumerate(m.tolist()):
+        ln[256 + r] = ln[a] + ln[b]
+    return ln
 
 
 def _log(*a):
@@ -125,7 +148,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--latency-reps", type=int, default=30)
+    ap.add_argument("--latency-reps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-two-streams", action="store_true",
@@ -148,17 +171,26 @@ def main():
     cpu = None
     oracle_ref = {}
     if not args.no_cpu_baseline:
-        workers = max(1, min(16, os.cpu_count() or 1))
+        # every core this process may run on, within the host's share for one GPU when the
+        # environment states it (OMP_NUM_THREADS)
+        affinity = len(os.sched_getaffinity(0))
+        share = int(os.environ.get("OMP_NUM_THREADS") or affinity)
+        workers = max(1, min(affinity, share))
         _log(f"cpu baseline: oracle on {workers} workers")
         cpu, oracle_ref[MAIN] = cpu_baseline(fam, voc, data, offs, args.cpu_seconds, workers)
+        cpu["affinity_cores"] = affinity
+        cpu["os_cpu_count"] = os.cpu_count()
         import oracle
+        single = {}
         for name in (() if args.no_latency else LATENCY):
             f2, v2, d2, o2 = work[name]
             merges, _ = textgen.load_vocab(v2)
             oracle_ref[name] = oracle.encode_batch(f2, merges, d2, o2)
-        if not args.no_latency:
-            f3, v3, d3, o3 = work["c3_mix1m"]
-            cpu["p50_ms_1m_char_request_single_core"] = round(oracle_latency(f3, v3, d3, o3), 3)
+            reps = 20 if d2.size < 50_000 else (7 if d2.size < 2_000_000 else 3)
+            single[name] = round(oracle_latency(f2, v2, d2, o2, reps), 3)
+        if single:
+            cpu["p50_ms_single_core"] = single
+            cpu["p50_ms_1m_char_request_single_core"] = single["c3_mix1m"]
 
     import torch
     import exact_bpe_tokenization_amd as tt
@@ -234,19 +266,23 @@ def main():
         kms[name] = statistics.mean(xs)
     dominant = max(kms, key=kms.get)
 
-    # input bytes per length bin (from the GPU split)
+    # the path's algorithmic bytes, and each kernel's own (from the GPU split and the piece results)
     starts = tok.pretokenize(data.tobytes(), offs)
     plen = np.diff(starts.astype(np.int64))
-    bins = {"all": int(n), "lane": int(plen[plen <= 64].sum()), "le16": int(plen[plen <= 16].sum()),
-            "17to32": int(plen[(plen > 16) & (plen <= 32)].sum()), "33to64": int(plen[(plen > 32) & (plen <= 64)].sum()),
-            "65to128": int(plen[(plen > 64) & (plen <= 128)].sum()), "le128": int(plen[plen <= 128].sum()),
-            "wave": int(plen[(plen > 128) & (plen <= 1024)].sum()),
-            "block": int(plen[(plen > 1024) & (plen <= 4096)].sum()), "giant": int(plen[plen > 4096].sum()),
-            "binned": int(plen[plen > 64].sum())}
-    alg_per_byte = (n + 4 * n_tokens + 16 * (D + 1)) / n
-    units = bins[UNITS[dominant]]
-    alg_bytes = alg_per_byte * units
-    achieved = alg_bytes / (kms[dominant] * 1e-3) / 1e9
+    P = int(plen.size)
+    ref_ids = gpu_ids
+    # tokens per piece from the IDs' byte lengths (the IDs spell the pieces in order)
+    tl = token_lengths(merges)[ref_ids]
+    ends = np.cumsum(tl)
+    ntok_piece = np.diff(np.concatenate([[0], np.searchsorted(ends, starts[1:].astype(np.int64), side="right")]))
+    multi = ntok_piece > 1
+    M = int(multi.sum())
+    Bm, Tm = int(plen[multi].sum()), int(ntok_piece[multi].sum())
+    own = own_bytes(n, D, P, int(n_tokens), M, Bm, Tm)
+    path_bytes = n + 4 * n_tokens + 16 * (D + 1)
+    path_alg = path_bytes / (wall / args.steps) / 1e9
+    kernels = {k: {"ms": round(kms[k], 5), "own_alg_bytes": int(own.get(k, 0)),
+                   "own_hbm_frac": round(own.get(k, 0) / (kms[k] * 1e-3) / 1e9 / HBM_PEAK_GBS, 5)} for k in kms}
     traffic = None
     tf = os.path.join(ROOT, "profiles", f"traffic_{dominant}_{MAIN}.json")
     if os.path.exists(tf):
@@ -254,15 +290,31 @@ def main():
         src = open(os.path.join(ROOT, "exact_bpe_tokenization_amd", "csrc", rec["source"]), "rb").read()
         if hashlib.sha256(src).hexdigest() == rec["source_sha256"]:
             traffic = rec["bytes_per_launch"]
-    roofline = {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 6), "traffic": traffic, "kernel": dominant,
-                "kernel_ms": round(kms[dominant], 5), "alg_bytes_per_launch": int(alg_bytes),
-                "alg_bytes_per_input_byte": round(alg_per_byte, 4), "input_bytes_per_launch": units}
-    path_alg = (n + 4 * n_tokens + 16 * (D + 1)) / (wall / args.steps) / 1e9
+    valu = None
+    cf = os.path.join(ROOT, "profiles", f"counters_{MAIN}.json")
+    if os.path.exists(cf):
+        rec = json.load(open(cf)).get(dominant)
+        if rec:
+            src = open(os.path.join(ROOT, "exact_bpe_tokenization_amd", "csrc", rec["source"]), "rb").read()
+            if hashlib.sha256(src).hexdigest() == rec["source_sha256"]:
+                valu = rec["SQ_INSTS_VALU"]
+    own_gbs = own[dominant] / (kms[dominant] * 1e-3) / 1e9
+    if valu is not None:
+        achieved = valu / (kms[dominant] * 1e-3) / 1e9
+        roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": VALU_PEAK,
+                    "unit": "G VALU wavefront instructions/s", "frac": round(achieved / VALU_PEAK, 5)}
+    else:   # no counters for this source: the kernel's own bytes against HBM
+        roofline = {"bound": "hbm", "achieved": round(own_gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(own_gbs / HBM_PEAK_GBS, 6)}
+    roofline.update({"traffic": traffic, "kernel": dominant, "kernel_ms": round(kms[dominant], 5),
+                     "valu_insts_per_launch": valu, "own_alg_bytes_per_launch": int(own[dominant]),
+                     "own_hbm_gbs": round(own_gbs, 3), "own_hbm_frac": round(own_gbs / HBM_PEAK_GBS, 6),
+                     "path_alg_frac_of_hbm": round(path_alg / HBM_PEAK_GBS, 6)})
 
     # ---- single-request latency ----
     latency = {}
     exact = {}
+    kms_c3 = None
     if two_exact is not None:
         exact[MAIN + "_two_in_flight_same_ids"] = bool(two_exact)
     if oracle_ref:
@@ -279,6 +331,20 @@ def main():
             exact[name] = bool(np.array_equal(ids_v[:nt].cpu().numpy().view(np.uint32), oracle_ref[name][0]) and
                                np.array_equal(oo_v.cpu().numpy().astype(np.uint64), oracle_ref[name][1]))
         reps = args.latency_reps if d2.size < 2_000_000 else max(5, args.latency_reps // 3)
+        if name == "c3_mix1m":   # per-kernel durations of the 1M-character request
+            nd3 = o2.size - 1
+            ws3 = t2.workspace[: tt.toktier_workspace_bytes(d2.size, nd3)]
+            ev3 = tt.HipEvents(2 * nk * 20)
+            torch.cuda.synchronize()
+            for s3 in range(20):
+                b3 = ev3.handles[2 * nk * s3: 2 * nk * s3 + nk]
+                a3 = ev3.handles[2 * nk * s3 + nk: 2 * nk * (s3 + 1)]
+                tt.toktier_encode_batch_timed(t2.vocab, dd, do, t2.out_ids[:max(d2.size, 1)], t2.out_offsets[:nd3 + 1],
+                                              ws3, b3, a3, sync=False)
+            torch.cuda.synchronize()
+            kms_c3 = {kn: round(statistics.mean(ev3.elapsed_ms(ev3.handles[2 * nk * s3 + k], ev3.handles[2 * nk * s3 + nk + k])
+                                                 for s3 in range(20)), 5) for k, kn in enumerate(tt.KERNELS)}
+            del ev3
         ts = []
         torch.cuda.synchronize()
         for _ in range(reps):
@@ -331,9 +397,12 @@ def main():
         "p50_ms_per_1m_char_request": latency["c3_mix1m"]["p50"] if latency else None,
         "p50_ms_per_1m_char_request_graph": latency["c3_mix1m"]["graph_p50"] if latency else None,
         "latency_ms": latency,
-        "path_alg_gbs": round(path_alg, 3),
         "path_alg_frac_of_hbm": round(path_alg / HBM_PEAK_GBS, 6),
+        "path_alg_gbs": round(path_alg, 3),
+        "path_alg_bytes_per_step": int(path_bytes),
         "kernel_ms": {k: round(v, 5) for k, v in kms.items()},
+        "kernels": kernels,
+        "kernel_ms_c3_mix1m": kms_c3,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "bit_exact": exact if exact else None,

@@ -27,7 +27,7 @@ EXPORTS = ("toktier_load_vocab", "toktier_load_vocab_ex", "toktier_free_vocab", 
            "toktier_encode_batch", "toktier_encode_batch_spans", "toktier_encode_batch_timed",
            "toktier_encode_batch_static",
            "toktier_pretokenize_batch", "toktier_repair_scratch_bytes", "toktier_repair_append",
-           "toktier_plan_create", "toktier_plan_launch", "toktier_plan_free",
+           "toktier_plan_create", "toktier_plan_create_bucket", "toktier_plan_launch", "toktier_plan_free",
            "toktier_last_status", "toktier_status_string", "toktier_last_hip_error",
            "toktier_unicode_table_sha256")
 
@@ -79,6 +79,8 @@ def lib():
     L.toktier_pretokenize_batch.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, u64, vp, u64p]
     L.toktier_last_status.argtypes = [vp, vp, u64p]
     L.toktier_plan_create.argtypes = [vp, vp, vp, u32, u64, vp, u64, vp, vp, vp, u64, vp, ctypes.POINTER(vp)]
+    L.toktier_plan_create_bucket.argtypes = [vp, vp, vp, u32, u64, vp, vp, u64, vp, vp, vp, u64, vp,
+                                             ctypes.POINTER(vp)]
     L.toktier_plan_launch.argtypes = [vp, vp, u64p]
     L.toktier_plan_free.argtypes = [vp]
     L.toktier_repair_scratch_bytes.argtypes = [vp, u64, u64p]
@@ -310,6 +312,23 @@ class Plan:
         if getattr(self, "handle", None) and _lib is not None:
             _lib.toktier_plan_free(self.handle)
             self.handle = None
+
+
+class BucketPlan(Plan):
+    """A captured encode for a size bucket (toktier_plan_create_bucket): buffers sized for max_bytes /
+    max_docs (data, offsets of max_docs + 1 entries), and a device tensor `sizes` (2 x int64: total
+    bytes, documents) that every launch() reads to find the request it encodes."""
+
+    def __init__(self, vocab, data, offsets, sizes, out_ids, out_offsets, workspace, out_spans=None, stream=None):
+        self.vocab = vocab
+        self._keep = (data, offsets, sizes, out_ids, out_offsets, workspace, out_spans)
+        h = ctypes.c_void_p()
+        rc = lib().toktier_plan_create_bucket(vocab.handle, _ptr(data), _ptr(offsets), offsets.numel() - 1,
+                                              data.numel(), _ptr(sizes), _ptr(out_ids), out_ids.numel(),
+                                              _ptr(out_offsets), _ptr(out_spans), _ptr(workspace), workspace.numel(),
+                                              _stream(stream), ctypes.byref(h))
+        _check(rc, "toktier_plan_create_bucket")
+        self.handle = h
 
 
 def toktier_repair_scratch_bytes(vocab, total_bytes):

@@ -455,6 +455,11 @@ struct Layout {
         bin_wave, bin_block, bin_giant, miss[6], g_ids, g_rank_a, g_rank_b, tspill, cstart, clen, ccount, gc0, gnc, gsafe,
         cpiece, total;
     uint32_t n_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
+    // a plan captured for a size bucket: the request's sizes are read from dsz (device: total bytes,
+    // document count) when it is replayed, at most cap_n bytes and cap_docs documents; else NULL
+    const uint64_t *dsz;
+    uint64_t cap_n;
+    uint32_t cap_docs;
 };
 
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~255ull; }
@@ -463,6 +468,9 @@ inline Layout make_layout(uint64_t n)
 {
     Layout L;
     L.n_tiles = (uint32_t)((n + TILE - 1) / TILE);
+    L.dsz = nullptr;
+    L.cap_n = n;
+    L.cap_docs = 0;
     L.cap_wave = (uint32_t)(n / (LANE_MAX + 1) + 1);
     L.cap_block = (uint32_t)(n / (WAVE_MAX + 1) + 1);
     L.cap_giant = (uint32_t)(n / (BLOCK_MAX + 1) + 1);
@@ -510,6 +518,22 @@ inline Layout make_layout(uint64_t n)
     L.cpiece = o;      o += align256(4ull * L.cap_chunks);
     L.total = o;
     return L;
+}
+
+// The request's sizes.  Kernels get the total byte count, the document count and a layout for a
+// capacity; in a plan captured for a size bucket (L.dsz set) the request's own sizes are read from
+// device memory when the plan is replayed, and L.n_tiles becomes the request's tile count (the
+// workspace's arrays stay where the capacity puts them).  A request larger than the bucket, or
+// without documents, encodes nothing (*bad set; the first kernel flags it in the status word).
+__device__ __forceinline__ void request_sizes(Layout &L, uint64_t &n, uint32_t &n_docs, bool *bad = nullptr)
+{
+    if (!L.dsz) return;
+    const uint64_t rn = L.dsz[0], rd = L.dsz[1];
+    const bool ok = rn <= L.cap_n && rd >= 1 && rd <= L.cap_docs;
+    if (bad) *bad = !ok;
+    n = ok ? rn : 0;
+    n_docs = ok ? (uint32_t)rd : 0u;
+    L.n_tiles = (uint32_t)((n + TILE - 1) / TILE);
 }
 
 // whole-piece lookup: a piece whose BPE result is a single token is found with one probe.  The

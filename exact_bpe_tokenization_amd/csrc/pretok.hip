@@ -254,8 +254,10 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
                                                 const uint64_t *__restrict__ offsets, uint32_t n_docs,
                                                 uint64_t n, uint8_t *ws, Layout L)
 {
+    bool bad_size = false;
+    request_sizes(L, n, n_docs, &bad_size);
     const uint32_t lane = threadIdx.x;
-    if (blockIdx.x == 0) ((uint32_t *)(ws + L.ctrl))[lane] = 0;   // 64 words
+    if (blockIdx.x == 0) ((uint32_t *)(ws + L.ctrl))[lane] = lane == 0 && bad_size ? (uint32_t)ST_BAD_OFFSETS : 0u;   // 64 words
     if (blockIdx.x < L.n_tiles && lane == 0) {
         ((uint4 *)(ws + L.tflag_state))[blockIdx.x] = make_uint4(0u, 0u, 0u, 0u);
         ((uint64_t *)(ws + L.tflag_cnt))[blockIdx.x] = 0;
@@ -488,6 +490,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     __shared__ uint32_t swcnt[NW], swstate[NW];
     __shared__ uint32_t s_tile, s_carry, s_base, s_d0, s_d1, s_o0, s_o1;
 
+    request_sizes(L, n, n_docs);
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint8_t *tbwd = ws + L.tbwd;
     uint32_t *tfs = (uint32_t *)(ws + L.tflag_state);
@@ -516,6 +519,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     for (int j = tid; j < (SPAN + 31) / 32; j += PRE_THREADS) sdoc[j] = 0;
     __syncthreads();
     const uint32_t tile = s_tile;
+    if (tile >= L.n_tiles) return;   // (a request smaller than the plan's size bucket)
     const uint64_t lo = (uint64_t)tile * TILE;
     const int64_t base = (int64_t)lo - RAW_LEAD;
     // summaries of the next 64 tiles for the backward carry (wave 0), loaded now so that the load

@@ -335,6 +335,11 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
                                               Layout L)
 {
     __shared__ ResolveSmem sm;
+    {
+        uint32_t nd = 0;
+        request_sizes(L, n, nd);
+        if (blockIdx.x >= L.n_tiles) return;   // (a request smaller than the plan's size bucket)
+    }
     const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *__restrict__ tbase = (const uint32_t *)(ws + L.tbase);
     uint32_t *pval = (uint32_t *)(ws + L.pval);
@@ -527,11 +532,21 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
                                              uint64_t *__restrict__ out_offsets, uint32_t *__restrict__ out_spans)
 {
     __shared__ EmitSmem sm;
-    if (blockIdx.x >= L.n_tiles) {   // the giant pieces' IDs
-        emit_giant<SPANS>(ws, L, blockIdx.x - L.n_tiles, gridDim.x - L.n_tiles, out_ids, out_spans, v.tok_len);
+    const uint32_t grid_tiles = L.n_tiles;   // the launch's tiles (a plan's size bucket)
+    if (blockIdx.x >= grid_tiles) {   // the giant pieces' IDs
+        emit_giant<SPANS>(ws, L, blockIdx.x - grid_tiles, gridDim.x - grid_tiles, out_ids, out_spans, v.tok_len);
         return;
     }
+    request_sizes(L, n, n_docs);
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
+    if (L.n_tiles == 0) {   // an empty request in a plan's size bucket: every document is empty
+        if (blockIdx.x == 0) {
+            for (uint32_t d = threadIdx.x; d <= n_docs; d += NT) out_offsets[d] = 0;
+            if (threadIdx.x == 0) ctrl->n_tokens = 0;
+        }
+        return;
+    }
+    if (blockIdx.x >= L.n_tiles) return;
     const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *__restrict__ tbase = (const uint32_t *)(ws + L.tbase);
     const uint32_t *__restrict__ tcount = (const uint32_t *)(ws + L.tcount);

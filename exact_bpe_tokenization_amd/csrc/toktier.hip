@@ -1018,19 +1018,12 @@ struct toktier_plan {
     hipGraphExec_t exec;
 };
 
-extern "C" int toktier_plan_create(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
-                                   uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids, uint64_t ids_capacity,
-                                   uint64_t *out_offsets, uint32_t *out_spans, void *workspace,
-                                   uint64_t workspace_bytes, void *stream, toktier_plan **out)
+namespace {
+
+// capture the chain of batch b as a graph, instantiate and upload it
+int plan_capture(const toktier_vocab *v, const Batch &b, uint32_t *out_ids, uint64_t *out_offsets,
+                 uint32_t *out_spans, void *workspace, void *stream, toktier_plan **out)
 {
-    if (!out) return TOKTIER_E_INVALID_ARG;
-    *out = nullptr;
-    Batch b;
-    int rc = check_batch(v, bytes, offsets, n_docs, total_bytes, workspace, workspace_bytes, &b);
-    if (rc) return rc;
-    if (v->da.n) return TOKTIER_E_INVALID_ARG;   // the literal pass reads a count on the host
-    if (!out_offsets || (total_bytes && !out_ids)) return TOKTIER_E_INVALID_ARG;
-    if (ids_capacity < total_bytes) return TOKTIER_E_CAPACITY;
     hipStream_t s = (hipStream_t)stream;
     hipStream_t cap = nullptr;
     HIP_TRY(hipStreamCreateWithFlags(&cap, hipStreamNonBlocking));
@@ -1062,6 +1055,45 @@ extern "C" int toktier_plan_create(const toktier_vocab *v, const uint8_t *bytes,
     p->exec = x;
     *out = p;
     return TOKTIER_OK;
+}
+
+}  // namespace
+
+extern "C" int toktier_plan_create(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                                   uint32_t n_docs, uint64_t total_bytes, uint32_t *out_ids, uint64_t ids_capacity,
+                                   uint64_t *out_offsets, uint32_t *out_spans, void *workspace,
+                                   uint64_t workspace_bytes, void *stream, toktier_plan **out)
+{
+    if (!out) return TOKTIER_E_INVALID_ARG;
+    *out = nullptr;
+    Batch b;
+    int rc = check_batch(v, bytes, offsets, n_docs, total_bytes, workspace, workspace_bytes, &b);
+    if (rc) return rc;
+    if (v->da.n) return TOKTIER_E_INVALID_ARG;   // the literal pass reads a count on the host
+    if (!out_offsets || (total_bytes && !out_ids)) return TOKTIER_E_INVALID_ARG;
+    if (ids_capacity < total_bytes) return TOKTIER_E_CAPACITY;
+    return plan_capture(v, b, out_ids, out_offsets, out_spans, workspace, stream, out);
+}
+
+extern "C" int toktier_plan_create_bucket(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                                          uint32_t max_docs, uint64_t max_bytes, const uint64_t *sizes,
+                                          uint32_t *out_ids, uint64_t ids_capacity, uint64_t *out_offsets,
+                                          uint32_t *out_spans, void *workspace, uint64_t workspace_bytes,
+                                          void *stream, toktier_plan **out)
+{
+    if (!out) return TOKTIER_E_INVALID_ARG;
+    *out = nullptr;
+    if (!sizes || max_bytes == 0 || !out_ids) return TOKTIER_E_INVALID_ARG;
+    Batch b;
+    int rc = check_batch(v, bytes, offsets, max_docs, max_bytes, workspace, workspace_bytes, &b);
+    if (rc) return rc;
+    if (v->da.n) return TOKTIER_E_INVALID_ARG;   // the literal pass reads a count on the host
+    if (!out_offsets) return TOKTIER_E_INVALID_ARG;
+    if (ids_capacity < max_bytes) return TOKTIER_E_CAPACITY;
+    b.L.dsz = sizes;
+    b.L.cap_n = max_bytes;
+    b.L.cap_docs = max_docs;
+    return plan_capture(v, b, out_ids, out_offsets, out_spans, workspace, stream, out);
 }
 
 extern "C" int toktier_plan_launch(toktier_plan *p, void *stream, uint64_t *out_n_tokens)

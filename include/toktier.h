@@ -325,9 +325,10 @@ int toktier_repair_append(const toktier_vocab *v, const uint8_t *text, uint64_t 
  * captured once as a HIP graph for fixed device buffers and sizes, then replayed (paper, latency
  * paragraph: counts stay on the device and a CUDA graph removes the host from the chain).  A replay
  * encodes whatever the bytes and offsets buffers hold at that time (same total_bytes and n_docs);
- * nothing is cached between replays.  Arguments as in toktier_encode_batch(_spans); the buffers must
- * outlive the plan.  Vocabularies with added tokens are rejected (E_INVALID_ARG): their literal pass
- * reads a count on the host.  Plans sharing a workspace must not run at the same time.
+ * nothing is cached between replays.  Arguments as in toktier_encode_batch(_spans); the buffers, and
+ * the vocabulary (its device tables are bound into the graph), must outlive the plan: free every
+ * plan before its vocabulary.  Vocabularies with added tokens are rejected (E_INVALID_ARG): their
+ * literal pass reads a count on the host.  Plans sharing a workspace must not run at the same time.
  *   toktier_plan_create  captures and uploads the graph (on `stream`; no kernel runs).
  *   toktier_plan_launch  replays it on `stream`; out_n_tokens as in toktier_encode_batch (NULL: no
  *                        wait; the count and device-detected errors then come from
@@ -340,6 +341,25 @@ int toktier_plan_create(const toktier_vocab *v, const uint8_t *bytes, const uint
                         uint64_t total_bytes, uint32_t *out_ids, uint64_t ids_capacity, uint64_t *out_offsets,
                         uint32_t *out_spans, void *workspace, uint64_t workspace_bytes, void *stream,
                         toktier_plan **out);
+/*
+ * A plan over a size bucket (paper, latency paragraph: the chain is captured as a graph for a small
+ * set of input-size buckets).  The graph is captured once for at most max_bytes input bytes and
+ * max_docs documents; every replay encodes the request whose sizes the device buffer `sizes` holds at
+ * that time -- sizes[0] total bytes, sizes[1] documents (1 .. max_docs) -- from bytes[0 .. sizes[0]) and
+ * offsets[0 .. sizes[1]], writing out_offsets[0 .. sizes[1]] and the IDs (spans).  So one plan serves
+ * any request up to its bucket, and the sizes can be written by the host or by earlier device work.
+ *   bytes, offsets, out_*, workspace  as in toktier_plan_create, sized for the bucket (the workspace:
+ *                 toktier_workspace_bytes(max_bytes, max_docs)); ids_capacity >= max_bytes.
+ *   sizes         device, 2 x uint64; read by every replay, not at creation.
+ * A replay whose sizes exceed the bucket, or name no document, encodes nothing and reports
+ * E_INVALID_ARG (through toktier_plan_launch's count, or toktier_last_status).  Replay with
+ * toktier_plan_launch, release with toktier_plan_free.  Errors at creation: those of
+ * toktier_plan_create, E_INVALID_ARG for a NULL sizes pointer or max_bytes == 0.
+ */
+int toktier_plan_create_bucket(const toktier_vocab *v, const uint8_t *bytes, const uint64_t *offsets,
+                               uint32_t max_docs, uint64_t max_bytes, const uint64_t *sizes, uint32_t *out_ids,
+                               uint64_t ids_capacity, uint64_t *out_offsets, uint32_t *out_spans, void *workspace,
+                               uint64_t workspace_bytes, void *stream, toktier_plan **out);
 int toktier_plan_launch(toktier_plan *p, void *stream, uint64_t *out_n_tokens);
 int toktier_plan_free(toktier_plan *p);
 

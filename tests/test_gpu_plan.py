@@ -97,3 +97,45 @@ def test_plan_rejects_added_tokens(tt):
     with pytest.raises(tt.ToktierError) as e:
         tt.Plan(tok.vocab, b["data"], b["offs"], b["ids"], b["oo"], ws)
     assert e.value.status == 1
+
+
+def test_bucket_plan_serves_three_request_sizes(tt):
+    """One plan captured for a size bucket (toktier_plan_create_bucket), replayed on three requests of
+    different sizes and document counts written into its buffers (sizes in device memory), each
+    against the oracle; replays are repeated with eager work of another workspace in between; an
+    oversized request encodes nothing and is reported."""
+    import torch
+    merges, fam = textgen.load_vocab("v2")
+    tok = tt.Tokenizer(merges, fam)
+    max_bytes, max_docs = 400_000, 16
+    data_b = torch.zeros(max_bytes, dtype=torch.uint8, device="cuda")
+    offs_b = torch.zeros(max_docs + 1, dtype=torch.int64, device="cuda")
+    sizes = torch.zeros(2, dtype=torch.int64, device="cuda")
+    ids_b = torch.empty(max_bytes, dtype=torch.int32, device="cuda")
+    oo_b = torch.empty(max_docs + 1, dtype=torch.int64, device="cuda")
+    ws = torch.empty(tt.toktier_workspace_bytes_ex(tok.vocab, max_bytes, max_docs), dtype=torch.uint8, device="cuda")
+    plan = tt.BucketPlan(tok.vocab, data_b, offs_b, sizes, ids_b, oo_b, ws)
+    requests = [
+        [textgen.agent_transcript(71, 100_000)],                                            # one 100K-char document
+        [textgen.english_code(72, k) for k in (5000, 1, 60_000, 0, 120_000, 33)],          # six, with empty ones
+        ["x = 1\n"],                                                                        # a few bytes
+    ]
+    other = textgen.agent_transcript(73, 50_000).encode()
+    for rep in range(2):
+        for k, texts in enumerate(requests):
+            data, offs = textgen.to_batch(texts)
+            _say("bucket plan request", k, "replay", rep, data.size, len(offs) - 1)
+            data_b[: data.size].copy_(torch.from_numpy(data))
+            offs_b[: offs.size].copy_(torch.from_numpy(offs.astype(np.int64)))
+            sizes.copy_(torch.tensor([data.size, offs.size - 1], dtype=torch.int64))
+            nt = plan.launch()
+            eids, eoo = oracle.encode_batch(fam, merges, data, offs)
+            compare_ids(eids, eoo, ids_b[:nt].cpu().numpy().view(np.uint32), oo_b[: offs.size].cpu().numpy())
+            tok.encode(other)   # eager work on another workspace between replays
+    # a request larger than the bucket: nothing encoded, reported as an invalid argument
+    sizes.copy_(torch.tensor([max_bytes + 1, 1], dtype=torch.int64))
+    with pytest.raises(tt.ToktierError):
+        plan.launch()
+    sizes.copy_(torch.tensor([10, max_docs + 1], dtype=torch.int64))
+    with pytest.raises(tt.ToktierError):
+        plan.launch()
