@@ -522,18 +522,19 @@ inline Layout make_layout(uint64_t n)
 
 // The request's sizes.  Kernels get the total byte count, the document count and a layout for a
 // capacity; in a plan captured for a size bucket (L.dsz set) the request's own sizes are read from
-// device memory when the plan is replayed, and L.n_tiles becomes the request's tile count (the
-// workspace's arrays stay where the capacity puts them).  A request larger than the bucket, or
-// without documents, encodes nothing (*bad set; the first kernel flags it in the status word).
-__device__ __forceinline__ void request_sizes(Layout &L, uint64_t &n, uint32_t &n_docs, bool *bad = nullptr)
+// device memory when the plan is replayed (the workspace's arrays stay where the capacity puts
+// them).  Returns the request's tile count.  A request larger than the bucket, or without documents,
+// encodes nothing (*bad set; the first kernel flags it in the status word).  (The layout is only
+// read: a kernel that wrote to its layout argument would keep a copy of it in private memory.)
+__device__ __forceinline__ uint32_t request_sizes(const Layout &L, uint64_t &n, uint32_t &n_docs, bool *bad = nullptr)
 {
-    if (!L.dsz) return;
+    if (!L.dsz) return L.n_tiles;
     const uint64_t rn = L.dsz[0], rd = L.dsz[1];
     const bool ok = rn <= L.cap_n && rd >= 1 && rd <= L.cap_docs;
     if (bad) *bad = !ok;
     n = ok ? rn : 0;
     n_docs = ok ? (uint32_t)rd : 0u;
-    L.n_tiles = (uint32_t)((n + TILE - 1) / TILE);
+    return (uint32_t)((n + TILE - 1) / TILE);
 }
 
 // whole-piece lookup: a piece whose BPE result is a single token is found with one probe.  The

@@ -255,16 +255,16 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
                                                 uint64_t n, uint8_t *ws, Layout L)
 {
     bool bad_size = false;
-    request_sizes(L, n, n_docs, &bad_size);
+    const uint32_t n_tiles = request_sizes(L, n, n_docs, &bad_size);
     const uint32_t lane = threadIdx.x;
     if (blockIdx.x == 0) ((uint32_t *)(ws + L.ctrl))[lane] = lane == 0 && bad_size ? (uint32_t)ST_BAD_OFFSETS : 0u;   // 64 words
-    if (blockIdx.x < L.n_tiles && lane == 0) {
+    if (blockIdx.x < n_tiles && lane == 0) {
         ((uint4 *)(ws + L.tflag_state))[blockIdx.x] = make_uint4(0u, 0u, 0u, 0u);
         ((uint64_t *)(ws + L.tflag_cnt))[blockIdx.x] = 0;
         ((uint32_t *)(ws + L.tlast))[blockIdx.x] = 0;
     }
-    for (uint32_t k = blockIdx.x * 64u + lane; k <= L.n_tiles / 64u; k += gridDim.x * 64u) ((uint32_t *)(ws + L.tsb))[k] = 0;
-    if (blockIdx.x >= L.n_tiles) return;
+    for (uint32_t k = blockIdx.x * 64u + lane; k <= n_tiles / 64u; k += gridDim.x * 64u) ((uint32_t *)(ws + L.tsb))[k] = 0;
+    if (blockIdx.x >= n_tiles) return;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
     const uint64_t hi = min(lo + TILE, n);
     // document starts in the pieces kernel's byte window of this tile, [lo - RAW_LEAD, lo + TILE +
@@ -490,7 +490,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     __shared__ uint32_t swcnt[NW], swstate[NW];
     __shared__ uint32_t s_tile, s_carry, s_base, s_d0, s_d1, s_o0, s_o1;
 
-    request_sizes(L, n, n_docs);
+    const uint32_t n_tiles = request_sizes(L, n, n_docs);
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint8_t *tbwd = ws + L.tbwd;
     uint32_t *tfs = (uint32_t *)(ws + L.tflag_state);
@@ -519,13 +519,13 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     for (int j = tid; j < (SPAN + 31) / 32; j += PRE_THREADS) sdoc[j] = 0;
     __syncthreads();
     const uint32_t tile = s_tile;
-    if (tile >= L.n_tiles) return;   // (a request smaller than the plan's size bucket)
+    if (tile >= n_tiles) return;   // (a request smaller than the plan's size bucket)
     const uint64_t lo = (uint64_t)tile * TILE;
     const int64_t base = (int64_t)lo - RAW_LEAD;
     // summaries of the next 64 tiles for the backward carry (wave 0), loaded now so that the load
     // overlaps the decode
     uint32_t bk_first = BK_T | (BK_T << 2);
-    if (wid == 0 && tile + 1 + lane < L.n_tiles) bk_first = (ws + L.tbwd)[tile + 1 + lane];
+    if (wid == 0 && tile + 1 + lane < n_tiles) bk_first = (ws + L.tbwd)[tile + 1 + lane];
 
     // raw bytes [lo - 4, lo + TILE + 24), as 32-bit words
     // (interior words from two aligned 4-byte loads, which never leave the pages of the bytes they
@@ -554,7 +554,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     }
     // document offsets must start at 0, never decrease and end at n
     bool bad_offs = false;
-    for (uint64_t d = (uint64_t)tile * PRE_THREADS + tid; d < n_docs; d += (uint64_t)L.n_tiles * PRE_THREADS)
+    for (uint64_t d = (uint64_t)tile * PRE_THREADS + tid; d < n_docs; d += (uint64_t)n_tiles * PRE_THREADS)
         if (offsets[d] > offsets[d + 1]) bad_offs = true;
     if (tile == 0 && tid == 0 && (offsets[0] != 0 || offsets[n_docs] != n)) bad_offs = true;
     if (bad_offs) atomicOr(&ctrl->status, ST_BAD_OFFSETS);
@@ -650,7 +650,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         uint32_t na = BK_KEEP, au = BK_KEEP;
         for (uint32_t t0 = tile + 1; na == BK_KEEP || au == BK_KEEP; t0 += 64) {
             uint32_t t = t0 + lane;
-            uint32_t x = t0 == tile + 1 ? bk_first : t < L.n_tiles ? (uint32_t)tbwd[t] : (BK_T | (BK_T << 2));
+            uint32_t x = t0 == tile + 1 ? bk_first : t < n_tiles ? (uint32_t)tbwd[t] : (BK_T | (BK_T << 2));
             uint64_t mna = __ballot((x & 3u) != 0), mau = __ballot((x >> 2) != 0);
             uint32_t xna = (uint32_t)__builtin_amdgcn_readlane((int)x, mna ? __ffsll((unsigned long long)mna) - 1 : 0);
             uint32_t xau = (uint32_t)__builtin_amdgcn_readlane((int)x, mau ? __ffsll((unsigned long long)mau) - 1 : 0);
@@ -840,7 +840,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     if (wid == 0) {
         if (lane == 0 && tile > 0) st_flag(tfc + tile, (1ull << 62) | total);
         const uint64_t basev = tile == 0 ? 0 : lookback_sum(tfc, tile);
-        const bool last_tile = tile == L.n_tiles - 1;
+        const bool last_tile = tile == n_tiles - 1;
         if (lane == 0) {
             st_flag(tfc + tile, (2ull << 62) | (basev + total));
             s_base = (uint32_t)basev;
@@ -848,7 +848,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
             if (last_tile) {
                 ctrl->n_pieces = (uint32_t)(basev + total);
                 pstart[basev + total] = (uint32_t)n;
-                tbase[L.n_tiles] = (uint32_t)(basev + total);
+                tbase[n_tiles] = (uint32_t)(basev + total);
             }
         }
         if (tile > 0 && (total > 0 || last_tile)) {

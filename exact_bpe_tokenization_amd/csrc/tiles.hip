@@ -337,8 +337,7 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
     __shared__ ResolveSmem sm;
     {
         uint32_t nd = 0;
-        request_sizes(L, n, nd);
-        if (blockIdx.x >= L.n_tiles) return;   // (a request smaller than the plan's size bucket)
+        if (blockIdx.x >= request_sizes(L, n, nd)) return;   // (a request smaller than the plan's size bucket)
     }
     const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *__restrict__ tbase = (const uint32_t *)(ws + L.tbase);
@@ -537,16 +536,16 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
         emit_giant<SPANS>(ws, L, blockIdx.x - grid_tiles, gridDim.x - grid_tiles, out_ids, out_spans, v.tok_len);
         return;
     }
-    request_sizes(L, n, n_docs);
+    const uint32_t n_tiles = request_sizes(L, n, n_docs);
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
-    if (L.n_tiles == 0) {   // an empty request in a plan's size bucket: every document is empty
+    if (n_tiles == 0) {   // an empty request in a plan's size bucket: every document is empty
         if (blockIdx.x == 0) {
             for (uint32_t d = threadIdx.x; d <= n_docs; d += NT) out_offsets[d] = 0;
             if (threadIdx.x == 0) ctrl->n_tokens = 0;
         }
         return;
     }
-    if (blockIdx.x >= L.n_tiles) return;
+    if (blockIdx.x >= n_tiles) return;
     const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *__restrict__ tbase = (const uint32_t *)(ws + L.tbase);
     const uint32_t *__restrict__ tcount = (const uint32_t *)(ws + L.tcount);
@@ -664,7 +663,7 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
       }
     }
     // the last tile: documents that start at the end of the batch (empty ones), the total
-    if (tile == L.n_tiles - 1 && wid == NW - 1) {
+    if (tile == n_tiles - 1 && wid == NW - 1) {
         const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, (uint64_t)n);
         for (uint32_t d = d0 + lane; d <= n_docs; d += 64) out_offsets[d] = run;
         if (lane == 0) ctrl->n_tokens = run;
