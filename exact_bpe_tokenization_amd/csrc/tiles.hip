@@ -385,8 +385,11 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
             a[u] = i < cnt ? pstart[p0 + i] : 0u;
             e[u] = i < cnt ? pstart[p0 + i + 1] : 0u;
         }
-        // kind: 0 nothing to load, 2 byte pair, 3 short table (both candidate slots)
-        uint32_t kind[K], si[K], sj[K];
+        // kind: 0 nothing to load, 2 byte pair, 3 short table (both candidate slots).  Each piece's
+        // result word is written once, in one coalesced store per row of the step (the pieces resolved
+        // later -- by the long table below or by the BPE kernels -- get a placeholder overwritten then):
+        // scattered partial stores would leave partly written cache lines to be written back repeatedly
+        uint32_t kind[K], si[K], sj[K], res[K];
         uint64_t key[K];
 #pragma unroll
         for (int u = 0; u < K; ++u) {
@@ -395,10 +398,11 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
             si[u] = 0;
             sj[u] = 0;
             key[u] = 0;
+            res[u] = 0;
             if (i >= cnt) continue;
             const uint32_t j = a[u] - (uint32_t)lo, len = e[u] - a[u];
             if (len == 1) {
-                pval[p0 + i] = win_byte(sm, j);
+                res[u] = win_byte(sm, j);
                 ++mytok;
             } else if (len <= WA_MAX) {
                 key[u] = short_key(sm, j, len);
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
                 const uint4 h0 = sm.hot[2 * set], h1 = sm.hot[2 * set + 1];
                 const uint64_t k0 = (uint64_t)h0.x | ((uint64_t)h0.y << 32), k1 = (uint64_t)h1.x | ((uint64_t)h1.y << 32);
                 if (k0 == key[u] || k1 == key[u]) {
-                    pval[p0 + i] = k0 == key[u] ? h0.z : h1.z;
+                    res[u] = k0 == key[u] ? h0.z : h1.z;
                     ++mytok;
                 } else if (len == 2 && !IGN) {
                     kind[u] = 2;
@@ -423,7 +427,7 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
                 uint32_t w = NO_PIECE;
                 if (IGN && len <= v.lmax) w = whole_token(v, bytes + a[u], len);
                 if (w != NO_PIECE) {
-                    pval[p0 + i] = w;
+                    res[u] = w;
                     ++mytok;
                 } else {
                     list_miss(i, len);
@@ -448,10 +452,10 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
             if (kind[u] == 2) {
                 const uint32_t r = x[u].x;   // the pair's rank word
                 if (r != NO_RANK) {
-                    pval[p0 + i] = 256u + (r >> 2);
+                    res[u] = 256u + (r >> 2);
                     ++mytok;
                 } else {   // no merge joins the two bytes: two tokens
-                    pval[p0 + i] = PV_MULTI | 2u;
+                    res[u] = PV_MULTI | 2u;
                     scratch[a[u]] = si[u] >> 8;
                     scratch[a[u] + 1] = si[u] & 255u;
                     mytok += 2;
@@ -460,12 +464,13 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
                 const uint64_t ka = (uint64_t)x[u].x | ((uint64_t)x[u].y << 32);
                 const uint64_t kb = (uint64_t)y[u].x | ((uint64_t)y[u].y << 32);
                 if (ka == key[u] || kb == key[u]) {
-                    pval[p0 + i] = ka == key[u] ? x[u].z : y[u].z;
+                    res[u] = ka == key[u] ? x[u].z : y[u].z;
                     ++mytok;
                 } else {
                     list_miss(i, (uint32_t)(key[u] >> 56));
                 }
             }
+            if (i < cnt) pval[p0 + i] = res[u];
         }
     }
     __syncthreads();
