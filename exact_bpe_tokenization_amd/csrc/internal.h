@@ -288,30 +288,6 @@ __device__ __forceinline__ void st_flag(uint64_t *p, uint64_t v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Exclusive prefix sum of per-tile counts.  flags[t] = (1 << 62 | aggregate) or (2 << 62 | inclusive
-// prefix); tiles before 0 count as a prefix of 0.  Call with the whole wave 0; returns the sum of
-// all tiles before `tile` (in every lane).
-__device__ __forceinline__ uint64_t lookback_sum(const uint64_t *flags, uint32_t tile)
-{
-    const uint32_t lane = threadIdx.x & 63u;
-    uint64_t sum = 0;
-    int64_t top = (int64_t)tile - 1;
-    for (;;) {
-        const int64_t pos = top - (int64_t)lane;
-        const uint64_t f = pos >= 0 ? ld_flag(flags + pos) : (2ull << 62);
-        const uint32_t flag = (uint32_t)(f >> 62);
-        const uint64_t pre = __ballot(flag == 2), nr = __ballot(flag == 0);
-        const uint32_t kp = pre ? (uint32_t)__ffsll((unsigned long long)pre) - 1u : 64u;
-        const uint64_t need = kp >= 63 ? ~0ull : ((2ull << kp) - 1);
-        if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
-        // (the counts are piece counts: every partial sum is below 2^32)
-        const uint32_t v = lane <= kp ? (uint32_t)f : 0u;
-        sum += (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(v), 63);
-        if (kp < 64) return sum;
-        top -= 64;
-    }
-}
-
 // First index i in [0, n) whose entry satisfies pred (n if none), for a predicate that is false
 // then true along the sorted array.  Called by a whole wavefront: each step probes 64 evenly spaced
 // entries, so a search costs about log64(n) + 1 dependent loads.

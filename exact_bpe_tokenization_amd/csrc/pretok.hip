@@ -414,6 +414,71 @@ __device__ uint32_t last_start_before(const uint32_t *tlast, uint32_t tile)
     }
 }
 
+// Piece-count look-back.  flags[t] holds the kind in bits 62-63 (1: the tile's own count, 2: the
+// count of all tiles up to and including it), bit 61 when the tile has a piece start, the offset
+// of its last start in the tile in bits 32-44, and the count in bits 0-31; tiles before 0 count as
+// an inclusive count of 0.  Wave 0 reads LB_K consecutive predecessors per lane, 64 * LB_K per
+// round trip (at the start of the grid every resident tile is still in its look-back, and each
+// must sum the counts of all of them back to the nearest inclusive one).  Returns the number of
+// pieces before `tile` and, in `last_start`, the position of the last piece start before it when
+// one of the tiles read has a start (else NO_START).
+constexpr int LB_K = 1;
+constexpr uint32_t NO_START = 0xFFFFFFFFu;
+constexpr uint64_t CNT_AGG = 1ull << 62, CNT_PREFIX = 2ull << 62, CNT_HAS_START = 1ull << 61;
+
+__device__ __forceinline__ uint64_t count_flag_info(uint32_t total, uint32_t last_off)
+{
+    return total ? (CNT_HAS_START | ((uint64_t)last_off << 32)) : 0ull;
+}
+
+__device__ uint64_t lookback_pieces(const uint64_t *flags, uint32_t tile, uint32_t &last_start)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    uint64_t sum = 0;
+    last_start = NO_START;
+    int64_t top = (int64_t)tile - 1;
+    for (;;) {
+        uint64_t f[LB_K];
+#pragma unroll
+        for (int j = 0; j < LB_K; ++j) {
+            const int64_t pos = top - (int64_t)(lane * LB_K) - j;
+            f[j] = pos >= 0 ? ld_flag(flags + pos) : CNT_PREFIX;
+        }
+        // this lane's flags in walk order, up to its first inclusive count
+        uint32_t jp = LB_K, js = LB_K, part = 0, soff = 0;
+        bool not_ready = false;
+#pragma unroll
+        for (int j = 0; j < LB_K; ++j) {
+            if (jp == LB_K) {
+                const uint32_t kind = (uint32_t)(f[j] >> 62);
+                not_ready |= kind == 0;
+                part += (uint32_t)f[j];
+                if (js == LB_K && kind != 0 && ((f[j] >> 61) & 1u)) {
+                    js = j;
+                    soff = (uint32_t)(f[j] >> 32) & 0x1FFFu;
+                }
+                if (kind == 2) jp = j;
+            }
+        }
+        const uint64_t pre = __ballot(jp < LB_K), nr = __ballot(not_ready);
+        const uint32_t kp = pre ? (uint32_t)__ffsll((unsigned long long)pre) - 1u : 64u;
+        const uint64_t need = kp >= 63 ? ~0ull : ((2ull << kp) - 1);
+        if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
+        // (the counts are piece counts: every partial sum is below 2^32)
+        sum += (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(lane <= kp ? part : 0u), 63);
+        if (last_start == NO_START) {
+            const uint64_t hs = __ballot(js < LB_K && lane <= kp);
+            if (hs) {
+                const int64_t t = top - (int64_t)(lane * LB_K) - (int64_t)js;
+                const uint32_t sp = (uint32_t)((uint64_t)t * TILE) + soff;
+                last_start = (uint32_t)__builtin_amdgcn_readlane((int)sp, __ffsll((unsigned long long)hs) - 1);
+            }
+        }
+        if (kp < 64) return sum;
+        top -= 64 * LB_K;
+    }
+}
+
 // a piece longer than SHORT_MAX bytes goes on the list of its length bin (encoded before the tile
 // encoder, which only collects its result)
 __device__ __forceinline__ void list_long(uint8_t *ws, const Layout &L, Ctrl *ctrl, uint32_t p, uint32_t len)
@@ -731,33 +796,57 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     const uint32_t na_in = ((right & 3u) == BK_KEEP) ? (s_carry & 1u) : (right & 1u);
     const uint32_t au_in = ((right >> 2) == BK_KEEP) ? ((s_carry >> 1) & 1u) : ((right >> 2) & 1u);
 
-    // right to left: each character's automaton context (packed 16 bits per character) and the
-    // chunk's map, composed from the right.  The context is the sum of two table entries (the
-    // character's code, the next character's code) and the two flags; continuation bytes and
-    // positions past the end saturate to the identity map.
+    // each character's automaton context (packed 16 bits per character): the sum of two table
+    // entries (the character's code, the next character's code) and the two flags; continuation
+    // bytes and positions past the end saturate to the identity map
     uint32_t pk_ctx[PRE_CHUNK / 2] = {0, 0, 0, 0, 0, 0, 0, 0};
-    M16 acc = m16_identity();
     {
         const uint32_t naw = fill_down16(tna, dna, na_in) & mW & ~mC;   // whitespace (not CR/LF) with NA set
         uint32_t aun = 0;
         if (CASE) aun = (fill_down16(tau, dau, au_in) >> 1) | (au_in << 15);   // AU of the next character
 #pragma unroll
-        for (int k = PRE_CHUNK - 1; k >= 0; --k) {
+        for (int k = 0; k < PRE_CHUNK; ++k) {
             const uint32_t nc = (ncw[k >> 2] >> (8 * (k & 3))) & 255u;
             uint32_t ctx = (uint32_t)sctxa[code_at(k)] + (uint32_t)sctxb[nc] + NA_STEP * ((naw >> k) & 1u);
             if (CASE) ctx += (aun >> k) & 1u;
             ctx = min(ctx, NCTXV);
             pk_ctx[k >> 1] |= ctx << (16 * (k & 1));
-            const uint4 m = smap16[ctx];
-            acc = compose16(M16{{m.x, m.y, m.z, m.w}}, acc);
-            __builtin_amdgcn_sched_barrier(0);   // one map load in flight: keeps register use low
         }
     }
+    auto ctx_at = [&](int k) -> uint32_t { return (pk_ctx[k >> 1] >> (16 * (k & 1))) & 0xFFFFu; };
 
-    // wavefront scan of the chunk maps; the wavefronts' maps are scanned by wave 0, which also
-    // takes the state entering the tile from the look-back
+    // The chunk's map, composed from the left until the map of every chunk of the wavefront sends
+    // all states to one state (a few characters of text nearly always do: only runs of digits and
+    // the first characters of a contraction keep states apart).  From there on each lane follows
+    // its one state, and the piece-start bits of those bytes no longer depend on the state that
+    // enters the chunk.  `kconv` (uniform) is the number of bytes composed.
+    const uint8_t *smb = (const uint8_t *)smap16;
+    M16 acc = m16_identity();
+    uint32_t kconv = PRE_CHUNK, s_run = 0, tail_mask = 0;
+#pragma unroll
+    for (int k = 0; k < PRE_CHUNK; ++k) {
+        if (kconv == PRE_CHUNK) {
+            const uint4 m = smap16[ctx_at(k)];
+            acc = compose16(acc, M16{{m.x, m.y, m.z, m.w}});
+            if ((k & 1) && k + 1 < PRE_CHUNK && __ballot(!is_const16(acc)) == 0) {
+                kconv = k + 1;
+                s_run = acc.w[0] & 15u;
+            }
+        } else {
+            const uint32_t b = smb[ctx_at(k) * 16u + s_run];
+            tail_mask |= ((b >> 4) & 1u) << k;
+            s_run = b & 15u;
+        }
+    }
+    const bool wave_const = kconv < PRE_CHUNK;
+    if (wave_const) acc = m16_const(s_run);
+
+    // wavefront scan of the chunk maps (a shift of one state when every map is constant); the
+    // wavefronts' maps are scanned by wave 0, which also takes the state entering the tile from the
+    // look-back
     M16 incl = acc;
-    {
+    const uint32_t prev_run = __shfl_up(s_run, 1, 64);   // (constant maps: the state entering the chunk)
+    if (!wave_const) {
         // inside each row of 16 lanes (DPP row shifts), then across rows (row broadcasts of lanes 15
         // and 31), composing the farther map first
         const uint32_t r = lane & 15u, row = lane >> 4;
@@ -773,8 +862,11 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         { const M16 y = TT_DPP4(0x143, 0xC); if (row >= 2) incl = compose16(y, incl); }   // row_bcast:31
 #undef TT_DPP4
     }
-    M16 excl = shfl_up16(incl, 1);
-    if (lane == 0) excl = m16_identity();
+    M16 excl = m16_identity();
+    if (!wave_const) {
+        excl = shfl_up16(incl, 1);
+        if (lane == 0) excl = m16_identity();
+    }
     if (lane == 63) swmap[wid] = make_uint4(incl.w[0], incl.w[1], incl.w[2], incl.w[3]);
     __syncthreads();
     if (wid == 0) {
@@ -799,15 +891,16 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     }
     __syncthreads();
 
-    // piece starts of this chunk
-    uint32_t s = byte16(excl, swstate[wid]) & 15u, mask = 0;
-    const uint8_t *smb = (const uint8_t *)smap16;
+    // piece starts of this chunk: the bytes before kconv from the state entering the chunk (those
+    // after it were found by the single-state run)
+    uint32_t s = (wave_const && lane > 0) ? prev_run : byte16(excl, swstate[wid]) & 15u, mask = tail_mask;
 #pragma unroll
     for (int k = 0; k < PRE_CHUNK; ++k) {
-        const uint32_t ctx = (pk_ctx[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-        const uint32_t b = smb[ctx * 16u + s];
-        mask |= ((b >> 4) & 1u) << k;
-        s = b & 15u;
+        if ((uint32_t)k < kconv) {
+            const uint32_t b = smb[ctx_at(k) * 16u + s];
+            mask |= ((b >> 4) & 1u) << k;
+            s = b & 15u;
+        }
     }
     const uint32_t cnt = __popc(mask), icnt = wave_incl_sum(cnt);
     if (lane == 63) swcnt[wid] = icnt;
@@ -838,11 +931,13 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     // start (or, in the last tile, at the end of the batch) is checked for length: it started at the
     // last start before this tile
     if (wid == 0) {
-        if (lane == 0 && tile > 0) st_flag(tfc + tile, (1ull << 62) | total);
-        const uint64_t basev = tile == 0 ? 0 : lookback_sum(tfc, tile);
+        const uint64_t info = count_flag_info(total, total ? spiece[total - 1] : 0u);
+        if (lane == 0 && tile > 0) st_flag(tfc + tile, CNT_AGG | info | total);
+        uint32_t prev = NO_START;
+        const uint64_t basev = tile == 0 ? 0 : lookback_pieces(tfc, tile, prev);
         const bool last_tile = tile == n_tiles - 1;
         if (lane == 0) {
-            st_flag(tfc + tile, (2ull << 62) | (basev + total));
+            st_flag(tfc + tile, CNT_PREFIX | info | (basev + total));
             s_base = (uint32_t)basev;
             tbase[tile] = (uint32_t)basev;
             if (last_tile) {
@@ -852,7 +947,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
             }
         }
         if (tile > 0 && (total > 0 || last_tile)) {
-            const uint32_t prev = last_start_before(tlast, tile);
+            if (prev == NO_START) prev = last_start_before(tlast, tile);
             const uint32_t end = total ? (uint32_t)(lo + spiece[0]) : (uint32_t)n;
             if (lane == 0 && end - prev > (uint32_t)SHORT_MAX) list_long(ws, L, ctrl, (uint32_t)basev - 1u, end - prev);
         }
