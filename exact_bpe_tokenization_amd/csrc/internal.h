@@ -427,8 +427,8 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // ---------------------------------------------------------------------------------------------
 // workspace layout for n input bytes
 struct Layout {
-    uint64_t ctrl, cc, tbwd, tdoc, tflag_state, tflag_cnt, tcount, tsb, tbase, tlast, pstart, pval, tokoff, scratch,
-        bin_wave, bin_block, bin_giant, miss[6], g_ids, g_rank_a, g_rank_b, tspill, cstart, clen, ccount, gc0, gnc, gsafe,
+    uint64_t ctrl, cc, tbwd, tdoc, tflag_state, tcnt, tfirst, gsum, tcount, tsb, tbase, pstart, pval, tokoff, scratch,
+        bin_wave, bin_block, bin_giant, miss[6], g_ids, g_rank_a, g_rank_b, tspill, prs, cstart, clen, ccount, gc0, gnc, gsafe,
         cpiece, total;
     uint32_t n_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
     // a plan captured for a size bucket: the request's sizes are read from dsz (device: total bytes,
@@ -458,11 +458,12 @@ inline Layout make_layout(uint64_t n)
     L.tbwd = o;        o += align256((uint64_t)L.n_tiles + 1);
     L.tdoc = o;        o += align256(16ull * L.n_tiles);
     L.tflag_state = o; o += align256(16ull * L.n_tiles);
-    L.tflag_cnt = o;   o += align256(8ull * L.n_tiles);
+    L.tcnt = o;        o += align256(4ull * L.n_tiles);         // pieces starting in each tile
+    L.tfirst = o;      o += align256(4ull * L.n_tiles);         // each tile's first piece start
+    L.gsum = o;        o += align256(4ull * (L.n_tiles / 64 + 1));  // pieces summed over 64 tiles
     L.tcount = o;      o += align256(4ull * (L.n_tiles + 1));   // tokens of the pieces starting in each tile
     L.tsb = o;         o += align256(4ull * (L.n_tiles / 64 + 1));  // the same summed over 64 tiles
     L.tbase = o;       o += align256(4ull * (L.n_tiles + 1));
-    L.tlast = o;       o += align256(4ull * L.n_tiles);
     L.pstart = o;      o += align256(4ull * (n + 2));
     L.pval = o;        o += align256(4ull * (n + 1));
     L.tokoff = o;      o += align256(4ull * (n + 2));
@@ -485,6 +486,9 @@ inline Layout make_layout(uint64_t n)
     // the tile encoder's BPE queue beyond its LDS part, at the tile's first piece index: used only
     // inside k_tiles, so it shares g_rank_b (only k_bpe_giant, later in the chain, uses that)
     L.tspill = L.g_rank_b;
+    // each tile's piece starts at the tile's own place (16-bit offsets at [tile * TILE, ...)), from
+    // the pieces kernel to the compaction kernel: shares g_ids (only k_bpe_giant uses that)
+    L.prs = L.g_ids;
     L.cstart = o;      o += align256(4ull * L.cap_chunks);
     L.clen = o;        o += align256(4ull * L.cap_chunks);
     L.ccount = o;      o += align256(4ull * L.cap_chunks);

@@ -260,10 +260,11 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
     if (blockIdx.x == 0) ((uint32_t *)(ws + L.ctrl))[lane] = lane == 0 && bad_size ? (uint32_t)ST_BAD_OFFSETS : 0u;   // 64 words
     if (blockIdx.x < n_tiles && lane == 0) {
         ((uint4 *)(ws + L.tflag_state))[blockIdx.x] = make_uint4(0u, 0u, 0u, 0u);
-        ((uint64_t *)(ws + L.tflag_cnt))[blockIdx.x] = 0;
-        ((uint32_t *)(ws + L.tlast))[blockIdx.x] = 0;
     }
-    for (uint32_t k = blockIdx.x * 64u + lane; k <= n_tiles / 64u; k += gridDim.x * 64u) ((uint32_t *)(ws + L.tsb))[k] = 0;
+    for (uint32_t k = blockIdx.x * 64u + lane; k <= n_tiles / 64u; k += gridDim.x * 64u) {
+        ((uint32_t *)(ws + L.tsb))[k] = 0;
+        ((uint32_t *)(ws + L.gsum))[k] = 0;
+    }
     if (blockIdx.x >= n_tiles) return;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
     const uint64_t hi = min(lo + TILE, n);
@@ -395,89 +396,7 @@ __device__ __forceinline__ uint32_t reg_byte_code(const uint32_t (&rw)[6], uint3
 // ---------------------------------------------------------------------------------------------
 // k_pieces: dynamic tile ids; decode, automaton context, scans, look-backs, piece starts
 
-// Position of the last piece start before `tile`.  Every tile publishes its last start in tlast
-// (0: not yet, 1: the tile has none, else position + 2) as soon as its starts are known; tile 0
-// always has one (at byte 0).  Wave 0 reads 64 predecessors per step; uniform result.
-__device__ uint32_t last_start_before(const uint32_t *tlast, uint32_t tile)
-{
-    const uint32_t lane = threadIdx.x & 63u;
-    int64_t top = (int64_t)tile - 1;
-    for (;;) {
-        const int64_t pos = top - (int64_t)lane;
-        const uint32_t w = pos >= 0 ? __hip_atomic_load(tlast + pos, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 2u;
-        const uint64_t has = __ballot(w >= 2u), nr = __ballot(w == 0u);
-        const uint32_t k = has ? (uint32_t)__ffsll((unsigned long long)has) - 1u : 64u;
-        const uint64_t need = k >= 63 ? ~0ull : ((2ull << k) - 1);
-        if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
-        if (k < 64) return (uint32_t)__builtin_amdgcn_readlane((int)w, k) - 2u;
-        top -= 64;
-    }
-}
-
-// Piece-count look-back.  flags[t] holds the kind in bits 62-63 (1: the tile's own count, 2: the
-// count of all tiles up to and including it), bit 61 when the tile has a piece start, the offset
-// of its last start in the tile in bits 32-44, and the count in bits 0-31; tiles before 0 count as
-// an inclusive count of 0.  Wave 0 reads LB_K consecutive predecessors per lane, 64 * LB_K per
-// round trip (at the start of the grid every resident tile is still in its look-back, and each
-// must sum the counts of all of them back to the nearest inclusive one).  Returns the number of
-// pieces before `tile` and, in `last_start`, the position of the last piece start before it when
-// one of the tiles read has a start (else NO_START).
-constexpr int LB_K = 1;
-constexpr uint32_t NO_START = 0xFFFFFFFFu;
-constexpr uint64_t CNT_AGG = 1ull << 62, CNT_PREFIX = 2ull << 62, CNT_HAS_START = 1ull << 61;
-
-__device__ __forceinline__ uint64_t count_flag_info(uint32_t total, uint32_t last_off)
-{
-    return total ? (CNT_HAS_START | ((uint64_t)last_off << 32)) : 0ull;
-}
-
-__device__ uint64_t lookback_pieces(const uint64_t *flags, uint32_t tile, uint32_t &last_start)
-{
-    const uint32_t lane = threadIdx.x & 63u;
-    uint64_t sum = 0;
-    last_start = NO_START;
-    int64_t top = (int64_t)tile - 1;
-    for (;;) {
-        uint64_t f[LB_K];
-#pragma unroll
-        for (int j = 0; j < LB_K; ++j) {
-            const int64_t pos = top - (int64_t)(lane * LB_K) - j;
-            f[j] = pos >= 0 ? ld_flag(flags + pos) : CNT_PREFIX;
-        }
-        // this lane's flags in walk order, up to its first inclusive count
-        uint32_t jp = LB_K, js = LB_K, part = 0, soff = 0;
-        bool not_ready = false;
-#pragma unroll
-        for (int j = 0; j < LB_K; ++j) {
-            if (jp == LB_K) {
-                const uint32_t kind = (uint32_t)(f[j] >> 62);
-                not_ready |= kind == 0;
-                part += (uint32_t)f[j];
-                if (js == LB_K && kind != 0 && ((f[j] >> 61) & 1u)) {
-                    js = j;
-                    soff = (uint32_t)(f[j] >> 32) & 0x1FFFu;
-                }
-                if (kind == 2) jp = j;
-            }
-        }
-        const uint64_t pre = __ballot(jp < LB_K), nr = __ballot(not_ready);
-        const uint32_t kp = pre ? (uint32_t)__ffsll((unsigned long long)pre) - 1u : 64u;
-        const uint64_t need = kp >= 63 ? ~0ull : ((2ull << kp) - 1);
-        if (nr & need) { __builtin_amdgcn_s_sleep(1); continue; }
-        // (the counts are piece counts: every partial sum is below 2^32)
-        sum += (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(lane <= kp ? part : 0u), 63);
-        if (last_start == NO_START) {
-            const uint64_t hs = __ballot(js < LB_K && lane <= kp);
-            if (hs) {
-                const int64_t t = top - (int64_t)(lane * LB_K) - (int64_t)js;
-                const uint32_t sp = (uint32_t)((uint64_t)t * TILE) + soff;
-                last_start = (uint32_t)__builtin_amdgcn_readlane((int)sp, __ffsll((unsigned long long)hs) - 1);
-            }
-        }
-        if (kp < 64) return sum;
-        top -= 64 * LB_K;
-    }
-}
+constexpr uint32_t NO_START = 0xFFFFFFFFu;   // a tile without piece starts
 
 // a piece longer than SHORT_MAX bytes goes on the list of its length bin (encoded before the tile
 // encoder, which only collects its result)
@@ -553,14 +472,12 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     __shared__ uint32_t sbkw[NW];
     __shared__ uint4 swmap[NW];
     __shared__ uint32_t swcnt[NW], swstate[NW];
-    __shared__ uint32_t s_tile, s_carry, s_base, s_d0, s_d1, s_o0, s_o1;
+    __shared__ uint32_t s_tile, s_carry, s_d0, s_d1, s_o0, s_o1;
 
     const uint32_t n_tiles = request_sizes(L, n, n_docs);
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
     const uint8_t *tbwd = ws + L.tbwd;
     uint32_t *tfs = (uint32_t *)(ws + L.tflag_state);
-    uint64_t *tfc = (uint64_t *)(ws + L.tflag_cnt);
-    uint32_t *pstart = (uint32_t *)(ws + L.pstart);
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
 
     if (tid == 0) s_tile = atomicAdd(&ctrl->tile_ctr_pre, 1u);
@@ -921,50 +838,70 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     }
 
     __syncthreads();
-    uint32_t *tlast = (uint32_t *)(ws + L.tlast);
-    uint32_t *tbase = (uint32_t *)(ws + L.tbase);
-    if (tid == 0)
-        __hip_atomic_store(tlast + tile, total ? (uint32_t)(lo + spiece[total - 1]) + 2u : 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    // the tile's piece count and first start, and its starts as offsets at the tile's own place;
+    // the compaction kernel gives them their global places once every tile has its count
+    if (tid == 0) {
+        ((uint32_t *)(ws + L.tcnt))[tile] = total;
+        ((uint32_t *)(ws + L.tfirst))[tile] = total ? (uint32_t)lo + spiece[0] : NO_START;
+        if (total) atomicAdd((uint32_t *)(ws + L.gsum) + tile / 64u, total);
+    }
+    uint16_t *prs = (uint16_t *)(ws + L.prs) + lo;
+    for (uint32_t i = tid; i < total; i += PRE_THREADS) prs[i] = spiece[i];
+}
 
-    // look-back #2: number of pieces before this tile; then the piece that ends at this tile's first
-    // start (or, in the last tile, at the end of the batch) is checked for length: it started at the
-    // last start before this tile
+// k_compact: one workgroup per tile puts the tile's piece starts at their global places (the pieces
+// before the tile: the 64-tile group sums before its group, then the tiles of its group before
+// it), records the tile's first piece index, and lists the pieces longer than SHORT_MAX by length.
+// The last piece of a tile ends at the first start of the next tile that has one, else at the end
+// of the batch.
+__global__ __launch_bounds__(256) void k_compact(uint8_t *ws, Layout L, uint64_t n)
+{
+    __shared__ uint32_t s_base, s_next;
+    uint32_t n_docs = 0;
+    const uint32_t n_tiles = request_sizes(L, n, n_docs);
+    const uint32_t tile = blockIdx.x;
+    if (tile >= n_tiles) return;
+    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
+    const uint32_t *tcnt = (const uint32_t *)(ws + L.tcnt), *tfirst = (const uint32_t *)(ws + L.tfirst);
+    const uint32_t *gsum = (const uint32_t *)(ws + L.gsum);
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
     if (wid == 0) {
-        const uint64_t info = count_flag_info(total, total ? spiece[total - 1] : 0u);
-        if (lane == 0 && tile > 0) st_flag(tfc + tile, CNT_AGG | info | total);
-        uint32_t prev = NO_START;
-        const uint64_t basev = tile == 0 ? 0 : lookback_pieces(tfc, tile, prev);
-        const bool last_tile = tile == n_tiles - 1;
-        if (lane == 0) {
-            st_flag(tfc + tile, CNT_PREFIX | info | (basev + total));
-            s_base = (uint32_t)basev;
-            tbase[tile] = (uint32_t)basev;
-            if (last_tile) {
-                ctrl->n_pieces = (uint32_t)(basev + total);
-                pstart[basev + total] = (uint32_t)n;
-                tbase[n_tiles] = (uint32_t)(basev + total);
+        const uint32_t g = tile / 64u;
+        uint32_t x = 0;
+        for (uint32_t k = lane; k < g; k += 64u) x += gsum[k];
+        if (64u * g + lane < tile) x += tcnt[64u * g + lane];
+        x = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(x), 63);
+        if (lane == 0) s_base = x;
+    } else if (wid == 1) {
+        uint32_t nx = (uint32_t)n;
+        for (uint32_t t0 = tile + 1; t0 < n_tiles; t0 += 64u) {
+            const uint32_t t = t0 + lane;
+            const uint32_t f = t < n_tiles ? tfirst[t] : NO_START;
+            const uint64_t has = __ballot(f != NO_START);
+            if (has) {
+                nx = (uint32_t)__builtin_amdgcn_readlane((int)f, __ffsll((unsigned long long)has) - 1);
+                break;
             }
         }
-        if (tile > 0 && (total > 0 || last_tile)) {
-            if (prev == NO_START) prev = last_start_before(tlast, tile);
-            const uint32_t end = total ? (uint32_t)(lo + spiece[0]) : (uint32_t)n;
-            if (lane == 0 && end - prev > (uint32_t)SHORT_MAX) list_long(ws, L, ctrl, (uint32_t)basev - 1u, end - prev);
-        }
-        if (last_tile && total > 0 && lane == 0) {
-            const uint32_t a = (uint32_t)(lo + spiece[total - 1]);
-            if ((uint32_t)n - a > (uint32_t)SHORT_MAX) list_long(ws, L, ctrl, (uint32_t)basev + total - 1u, (uint32_t)n - a);
-        }
+        if (lane == 0) s_next = nx;
     }
     __syncthreads();
-    const uint32_t gbase = s_base;
-    for (uint32_t i = tid; i < total; i += PRE_THREADS) {
-        const uint32_t a = spiece[i];
-        pstart[gbase + i] = (uint32_t)(lo + a);
-        if (i + 1 < total && (uint32_t)spiece[i + 1] - a > (uint32_t)SHORT_MAX)
-            list_long(ws, L, ctrl, gbase + i, (uint32_t)spiece[i + 1] - a);
+    const uint32_t base = s_base, next = s_next, cnt = tcnt[tile], lo = tile * (uint32_t)TILE;
+    const uint16_t *prs = (const uint16_t *)(ws + L.prs) + lo;
+    uint32_t *pstart = (uint32_t *)(ws + L.pstart);
+    for (uint32_t i = tid; i < cnt; i += 256u) {
+        const uint32_t a = lo + prs[i], e = i + 1 < cnt ? lo + prs[i + 1] : next;
+        pstart[base + i] = a;
+        if (e - a > (uint32_t)SHORT_MAX) list_long(ws, L, ctrl, base + i, e - a);
     }
-
+    if (tid == 0) {
+        ((uint32_t *)(ws + L.tbase))[tile] = base;
+        if (tile == n_tiles - 1) {
+            ctrl->n_pieces = base + cnt;
+            pstart[base + cnt] = (uint32_t)n;
+            ((uint32_t *)(ws + L.tbase))[n_tiles] = base + cnt;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -990,6 +927,7 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
         else
             hipLaunchKernelGGL(k_pieces<VAR_PLAIN>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs,
                                b.n, b.ws, L);
+        hipLaunchKernelGGL(k_compact, grid, dim3(256), 0, s, b.ws, L, b.n);
     }
     return hipGetLastError();
 }
