@@ -427,7 +427,7 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // ---------------------------------------------------------------------------------------------
 // workspace layout for n input bytes
 struct Layout {
-    uint64_t ctrl, cc, tbwd, tdoc, tflag_state, tcnt, tfirst, gsum, tcount, tsb, tbase, pstart, pval, tokoff, scratch,
+    uint64_t ctrl, cc, tbwd, tdoc, twin, tflag_state, tcnt, tfirst, gsum, tcount, tsb, tbase, pstart, pval, tokoff, scratch,
         bin_wave, bin_block, bin_giant, miss[6], g_ids, g_rank_a, g_rank_b, tspill, prs, cstart, clen, ccount, gc0, gnc, gsafe,
         cpiece, total;
     uint32_t n_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
@@ -457,6 +457,7 @@ inline Layout make_layout(uint64_t n)
     L.cc = o;
     L.tbwd = o;        o += align256((uint64_t)L.n_tiles + 1);
     L.tdoc = o;        o += align256(16ull * L.n_tiles);
+    L.twin = o;        o += align256(4ull * L.n_tiles);         // entry state of the next tile, if fixed
     L.tflag_state = o; o += align256(16ull * L.n_tiles);
     L.tcnt = o;        o += align256(4ull * L.n_tiles);         // pieces starting in each tile
     L.tfirst = o;      o += align256(4ull * L.n_tiles);         // each tile's first piece start

@@ -238,7 +238,8 @@ __device__ __forceinline__ uint32_t byte_code(const uint8_t *sraw, DocBit docbit
 }
 
 // ---------------------------------------------------------------------------------------------
-// k_summary: one wavefront per tile (one workgroup when the batch is empty).  It also clears what
+// k_summary: one workgroup of two wavefronts per tile (one workgroup when the batch is empty); the
+// second computes the states the tile's last bytes fix (above) beside the first.  It also clears what
 // the later kernels count on: the control block, the tile's look-back flags and the per-tile token
 // counters.  The tile's summary of a backward flag is the map of its leftmost character whose map
 // is not "pass through" (for NA: the first character that is not whitespace-other-than-CR/LF, or
@@ -250,27 +251,174 @@ struct StepBytes {
     static constexpr int value = T;
 };
 
-__global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ bytes,
-                                                const uint64_t *__restrict__ offsets, uint32_t n_docs,
-                                                uint64_t n, uint8_t *ws, Layout L)
+// The state that enters the next tile when the tile's last WIN_BYTES bytes fix it: their automaton
+// maps composed, one composition for each value of the backward flags that enters them from the
+// right (NA, and AU under the case rules; the next tile knows which applies).  A composition that
+// sends every state to one state gives that state whatever came before (the usual case: a few
+// characters of text synchronize the automaton), and the next tile's pieces kernel takes it
+// instead of waiting for this tile's look-back flag.  One lane per byte: lanes 0..59 the window,
+// lanes 60..63 the four bytes after the tile (the next characters).  Result byte v (flag value v =
+// NA | AU << 1): 0x10 | state when fixed, else 0.
+constexpr int WIN_BYTES = 60;
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t x)
 {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x |= (uint32_t)__shfl_xor((int)x, d, 64);
+    return x;
+}
+
+// inclusive scan of 16-byte maps over the wavefront with DPP (lane i: lanes 0..i composed, lane 0's
+// map first): row shifts inside each row of 16 lanes, then the row broadcasts of lanes 15 and 31
+__device__ __forceinline__ M16 wave_scan16(M16 x)
+{
+    const uint32_t lane = threadIdx.x & 63u, r = lane & 15u, row = lane >> 4;
+#define TT_DPPX(ctrl, rmask) M16{{(uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.w[0], ctrl, rmask, 0xF, false), \
+                                  (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.w[1], ctrl, rmask, 0xF, false), \
+                                  (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.w[2], ctrl, rmask, 0xF, false), \
+                                  (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.w[3], ctrl, rmask, 0xF, false)}}
+    { const M16 y = TT_DPPX(0x111, 0xF); if (r >= 1) x = compose16(y, x); }
+    { const M16 y = TT_DPPX(0x112, 0xF); if (r >= 2) x = compose16(y, x); }
+    { const M16 y = TT_DPPX(0x114, 0xF); if (r >= 4) x = compose16(y, x); }
+    { const M16 y = TT_DPPX(0x118, 0xF); if (r >= 8) x = compose16(y, x); }
+    { const M16 y = TT_DPPX(0x142, 0xA); if (row & 1u) x = compose16(y, x); }   // row_bcast:15
+    { const M16 y = TT_DPPX(0x143, 0xC); if (row >= 2) x = compose16(y, x); }   // row_bcast:31
+#undef TT_DPPX
+    return x;
+}
+
+template <typename DocBit>
+__device__ uint32_t window_states(const DevVocab &v, const uint4 *smap, const uint8_t *swin, DocBit docbit, uint64_t wb,
+                                  uint64_t n)
+{
+    const uint32_t lane = threadIdx.x & 63u;
+    const bool DS = v.family == FAMILY_DEEPSEEK, CASE = v.family == FAMILY_O200K;
+    const uint32_t NX = DS ? DS_NNEXT : NNEXT, AUM = DS ? 1u : 2u, NCTXV = DS ? DS_NCTX : NCTX;
+    const int j = (int)lane + (64 - WIN_BYTES);   // this lane's byte in swin (position wb + j)
+    const uint64_t p = wb + (uint64_t)j;
+    bool ignore = false;
+    const uint32_t code = p < n ? byte_code(swin, docbit, j, p, n, v.family, false, ignore) : (uint32_t)CC_EOF;
+    // the next character: the first later byte that is not a continuation byte
+    const bool cont = (code & 7u) == CAT_CONT && code != CC_EOF;
+    const uint64_t starts = __ballot(!cont) & (lane < 63 ? ~0ull << (lane + 1) : 0ull);
+    const uint32_t nc = (uint32_t)__shfl((int)code, starts ? __ffsll((unsigned long long)starts) - 1 : 63, 64);
+    // backward flags: decided here (D) and their value (T), as the pieces kernel forms them
+    const uint32_t cat = code & 7u;
+    const bool win = lane < (uint32_t)WIN_BYTES, isch = cat != CAT_CONT;
+    const bool ws_ = isch && cat == CAT_W, crlf = ws_ && (code & CC_CRLF);
+    const bool en = (((nc >> 7) | (0x80u >> (nc & 7u))) & 1u) != 0;
+    const bool tna = (isch && !ws_) || (ws_ && !crlf && en), dna = tna || crlf;
+    const bool up = isch && cat == CAT_LU, low = isch && (cat == CAT_LL || cat == CAT_LO || cat == CAT_M);
+    const bool tau = (isch && !(up || low)) || (up && en), dau = tau || low;
+    // first decided position at or after each byte of the window (0: none, else 2 | value)
+    uint32_t xn = win && dna ? 2u | (tna ? 1u : 0u) : 0u, xa = win && dau ? 2u | (tau ? 1u : 0u) : 0u;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t yn = __shfl_down(xn, d, 64), ya = __shfl_down(xa, d, 64);
+        if (lane + d < 64) {
+            if (xn == 0) xn = yn;
+            if (xa == 0) xa = ya;
+        }
+    }
+    const uint32_t xa_next = lane < 63 ? __shfl_down(xa, 1, 64) : 0u;   // AU of the next byte
+    const uint32_t selfc = DS ? self_code_ds(code) : self_code(code, false);
+    const uint32_t nextc = DS ? next_code_ds(nc) : ((nc & 7u) == CAT_CONT ? 5u : next_code(nc));
+    const uint32_t base = win && isch ? (selfc * 2u + ((code & CC_DOC) ? 1u : 0u)) * NX * AUM + nextc * AUM : 0xFFFFu;
+    // one composition per flag value (the maps from the copy of the table in LDS; index NCTXV is
+    // the identity)
+    const uint32_t nvar = CASE ? 4u : 2u;
+    uint32_t res = 0;
+    for (uint32_t var = 0; var < nvar; ++var) {
+        const uint32_t na = xn ? (xn & 1u) : (var & 1u), aun = xa_next ? (xa_next & 1u) : ((var >> 1) & 1u);
+        const uint32_t ctx = min(base + ((na && ws_ && !crlf) ? 2u * NX * AUM : 0u) + (CASE ? aun : 0u), NCTXV);
+        const uint4 t = smap[ctx];
+        const M16 x = wave_scan16(M16{{t.x, t.y, t.z, t.w}});
+        if (is_const16(x)) res |= (0x10u | (x.w[0] & 15u)) << (8u * var);
+    }
+    return (uint32_t)__builtin_amdgcn_readlane((int)res, 63);
+}
+
+__global__ __launch_bounds__(128) void k_summary(DevVocab v, const uint8_t *__restrict__ bytes,
+                                                 const uint64_t *__restrict__ offsets, uint32_t n_docs,
+                                                 uint64_t n, uint8_t *ws, Layout L)
+{
+    __shared__ uint8_t swin[72];
+    __shared__ uint4 smap[NCTX_MAX + 1];
     bool bad_size = false;
     const uint32_t n_tiles = request_sizes(L, n, n_docs, &bad_size);
-    const uint32_t lane = threadIdx.x;
-    if (blockIdx.x == 0) ((uint32_t *)(ws + L.ctrl))[lane] = lane == 0 && bad_size ? (uint32_t)ST_BAD_OFFSETS : 0u;   // 64 words
-    if (blockIdx.x < n_tiles && lane == 0) {
-        ((uint4 *)(ws + L.tflag_state))[blockIdx.x] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    for (uint32_t k = blockIdx.x * 64u + lane; k <= n_tiles / 64u; k += gridDim.x * 64u) {
-        ((uint32_t *)(ws + L.tsb))[k] = 0;
-        ((uint32_t *)(ws + L.gsum))[k] = 0;
+    const uint32_t lane = threadIdx.x & 63u, wid = threadIdx.x >> 6;
+    if (wid == 0) {
+        if (blockIdx.x == 0) ((uint32_t *)(ws + L.ctrl))[lane] = lane == 0 && bad_size ? (uint32_t)ST_BAD_OFFSETS : 0u;   // 64 words
+        if (blockIdx.x < n_tiles && lane == 0) ((uint4 *)(ws + L.tflag_state))[blockIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+        for (uint32_t k = blockIdx.x * 64u + lane; k <= n_tiles / 64u; k += gridDim.x * 64u) {
+            ((uint32_t *)(ws + L.tsb))[k] = 0;
+            ((uint32_t *)(ws + L.gsum))[k] = 0;
+        }
     }
     if (blockIdx.x >= n_tiles) return;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
     const uint64_t hi = min(lo + TILE, n);
-    // document starts in the pieces kernel's byte window of this tile, [lo - RAW_LEAD, lo + TILE +
-    // RAW_TAIL): indices [d0, d1) of offsets (empty documents repeat one), kept for that kernel; the
-    // window holds [lo, hi + 4), which the search below needs
+    // wavefront 1: the window at the tile's end, bytes [hi - 64, hi + 8), its document starts and a
+    // copy of the transition maps, then the states the window fixes (beside wavefront 0's scan)
+    if (wid == 1) {
+        uint32_t wst = 0;
+        if (blockIdx.x + 1 < n_tiles) {
+            const uint64_t wb = hi - 64;
+            const uint32_t wbyte0 = wb + lane < n ? bytes[wb + lane] : 0u;
+            const uint32_t wbyte1 = lane < 8 && wb + 64 + lane < n ? bytes[wb + 64 + lane] : 0u;
+            const uint32_t nctx = v.family == FAMILY_DEEPSEEK ? (uint32_t)DS_NCTX : (uint32_t)NCTX;
+            for (uint32_t k = lane; k < nctx; k += 64u) smap[k] = v.fmap16[k];
+            if (lane == 0) smap[nctx] = make_uint4(0x03020100u, 0x07060504u, 0x0B0A0908u, 0x0F0E0D0Cu);
+            swin[lane] = (uint8_t)wbyte0;
+            if (lane < 8) swin[64 + lane] = (uint8_t)wbyte1;
+            // document starts in the window: narrow [lo, hi) of offsets down to at most 128 entries
+            // that hold the first start >= wb, then read them (and the next 128 while they all lie
+            // in the window)
+            uint32_t dlo = 0, dhi = n_docs + 1;
+            while (dhi - dlo > 128u) {
+                const uint32_t step = (dhi - dlo + 63u) / 64u, idx = dlo + lane * step;
+                const uint64_t t = __ballot(idx >= dhi || offsets[idx] >= wb);
+                if (t == 0) { dlo = dlo + 63u * step; continue; }   // all probes before the window
+                const uint32_t k = (uint32_t)__ffsll((unsigned long long)t) - 1u;
+                const uint32_t nlo = k ? dlo + (k - 1u) * step : dlo, nhi = min(dhi, dlo + k * step + 1u);
+                dlo = nlo;
+                dhi = nhi;
+            }
+            uint32_t db0 = 0, db1 = 0, db2 = 0;
+            for (;;) {
+                uint64_t o[2];
+                bool more = true;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t idx = dlo + 64u * h + lane;
+                    o[h] = idx <= n_docs ? offsets[idx] : ~0ull;
+                    if (o[h] >= wb && o[h] < wb + 72) {
+                        const uint32_t j = (uint32_t)(o[h] - wb), bit = 1u << (j & 31u);
+                        db0 |= j < 32u ? bit : 0u;
+                        db1 |= j >= 32u && j < 64u ? bit : 0u;
+                        db2 |= j >= 64u ? bit : 0u;
+                    }
+                }
+                more = __builtin_amdgcn_readlane((int)(o[1] < wb + 72), 63) && dlo + 128u <= n_docs;
+                if (!more) break;
+                dlo += 128u;
+            }
+            db0 = wave_or(db0);
+            db1 = wave_or(db1);
+            db2 = wave_or(db2);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            wst = window_states(v, smap, swin, [&](int j) -> bool {
+                return (((j < 32 ? db0 : (j < 64 ? db1 : db2))) >> (j & 31)) & 1u;
+            }, wb, n);
+        }
+        if (lane == 0) ((uint32_t *)(ws + L.twin))[blockIdx.x] = wst;
+        return;
+    }
+    // wavefront 0: document starts in the pieces kernel's byte window of this tile, [lo - RAW_LEAD,
+    // lo + TILE + RAW_TAIL): indices [d0, d1) of offsets (empty documents repeat one), kept for that
+    // kernel; the window holds [lo, hi + 4), which the search below needs
     const uint64_t lo_w = lo >= (uint64_t)RAW_LEAD ? lo - RAW_LEAD : 0;
     const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, lo_w);
     const uint32_t d1 = wave_lower_bound(offsets, n_docs + 1, lo + TILE + RAW_TAIL);
@@ -324,6 +472,7 @@ __global__ __launch_bounds__(64) void k_summary(const uint8_t *__restrict__ byte
     if (w < hi) scan(w, StepBytes<4>{});
     for (w += 256; w < hi && (na == BK_KEEP || au == BK_KEEP); w += 64 * 32) scan(w, StepBytes<32>{});
     if (lane == 0) (ws + L.tbwd)[blockIdx.x] = (uint8_t)(na | (au << 2));
+
 }
 
 // The same per-byte code from registers: rw holds 24 bytes (4 before the thread's chunk, its 16, 4
@@ -508,6 +657,10 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     // overlaps the decode
     uint32_t bk_first = BK_T | (BK_T << 2);
     if (wid == 0 && tile + 1 + lane < n_tiles) bk_first = (ws + L.tbwd)[tile + 1 + lane];
+    // the previous tile's window states and this tile's own backward summary (which of those
+    // states applies)
+    const uint32_t win_prev = tile > 0 ? ((const uint32_t *)(ws + L.twin))[tile - 1] : 0u;
+    const uint32_t bk_self = (ws + L.tbwd)[tile];
 
     // raw bytes [lo - 4, lo + TILE + 24), as 32-bit words
     // (interior words from two aligned 4-byte loads, which never leave the pages of the bytes they
@@ -800,9 +953,20 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         M16 wex = shfl_up16(wm, 1);
         if (lane == 0) wex = m16_identity();
         const M16 tile_map = shfl16(wm, NW - 1);
-        // look-back #1: automaton state entering this tile
-        if (lane == 0 && tile > 0) st_flag16(tfs + 4 * tile, tile_map, FLAG_AGG);
-        const uint32_t entry = tile == 0 ? (uint32_t)S_ST : lookback_state(tfs, tile);
+        // automaton state entering this tile: fixed by the previous tile's last bytes, else from the
+        // look-back (this tile's flags: its map, then the state after it)
+        const uint32_t na_prev = (bk_self & 3u) != BK_KEEP ? (bk_self & 1u) : (s_carry & 1u);
+        const uint32_t au_prev = (bk_self >> 2) != BK_KEEP ? ((bk_self >> 2) & 1u) : ((s_carry >> 1) & 1u);
+        const uint32_t wv = (win_prev >> (8u * (na_prev | (CASE ? au_prev << 1 : 0u)))) & 0xFFu;
+        uint32_t entry = S_ST;
+        if (tile > 0) {
+            if (wv & 0x10u) {
+                entry = wv & 15u;
+            } else {
+                if (lane == 0) st_flag16(tfs + 4 * tile, tile_map, FLAG_AGG);
+                entry = lookback_state(tfs, tile);
+            }
+        }
         if (lane == 0) st_flag16(tfs + 4 * tile, m16_const(byte16(tile_map, entry) & 15u), FLAG_PREFIX);
         if (lane < (uint32_t)NW) swstate[lane] = byte16(wex, entry) & 15u;
     }
@@ -911,7 +1075,7 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
     const Layout &L = b.L;
     {
         LaunchScope k(ev, TK_SUMMARY, s);
-        hipLaunchKernelGGL(k_summary, dim3(L.n_tiles ? L.n_tiles : 1u), dim3(64), 0, s, b.bytes, b.offsets, b.n_docs,
+        hipLaunchKernelGGL(k_summary, dim3(L.n_tiles ? L.n_tiles : 1u), dim3(128), 0, s, v, b.bytes, b.offsets, b.n_docs,
                            b.n, b.ws, L);
     }
     if (L.n_tiles == 0) return hipGetLastError();
