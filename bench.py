@@ -58,9 +58,9 @@ def own_bytes(n, D, P, T, M, Bm, Tm):
     return {
         "summary": 8 * (D + 1),
         "pieces": n + 4 * P + 8 * (D + 1),                       # input in, piece starts out
-        "giant_seams": 0, "bpe_wave": 0, "bpe_block": 0, "bpe_giant": 0,   # no piece over 128 bytes here
+        "giant_seams": 0, "bpe_giant": 0,                         # no piece over 4096 bytes here
         "tiles": n + 4 * (P + 1) + 4 * P + 4 * M,                 # input and starts in, results and lists out
-        "bpe_short": Bm + 4 * M + 8 * M + 4 * M + 4 * Tm,         # bytes, list, starts in; results out
+        "bpe": Bm + 4 * M + 8 * M + 4 * M + 4 * Tm,               # bytes, list, starts in; results out
         "emit": 4 * P + 4 * P + 4 * Tm + 4 * T + 16 * (D + 1),   # results, starts, BPE IDs in; IDs out
     }
 

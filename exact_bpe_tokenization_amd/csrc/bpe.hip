@@ -211,7 +211,7 @@ __device__ __forceinline__ uint32_t lane_bpe(const DevVocab &v, const uint8_t *_
 // items per wavefront.  The tile encoder lists each tile's pieces in one run, so a wavefront's pieces
 // mostly share one or two input tiles and its token counts take that many atomics.
 template <int MAXL>
-__device__ void bpe_lane(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
+__device__ __forceinline__ void bpe_lane(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
                          uint32_t *rows, uint32_t r, uint32_t blk, uint32_t nblk)
 {
     uint32_t *row = rows + (threadIdx.x) * LROW;
@@ -257,7 +257,7 @@ __device__ __forceinline__ uint32_t lane_push(uint32_t dst_lane, uint32_t x)
 }
 
 template <int G>
-__device__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L, uint32_t r,
+__device__ __forceinline__ void bpe_seg(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L, uint32_t r,
                         uint32_t blk, uint32_t nblk)
 {
     static_assert(G == 16 || G == 32 || G == 64, "segment width");
@@ -342,7 +342,7 @@ __device__ __forceinline__ void shl128(uint64_t lo, uint64_t hi, uint64_t &rlo, 
     rlo = lo << 1;
 }
 
-__device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
+__device__ __forceinline__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
                          uint32_t blk, uint32_t nblk)
 {
     constexpr uint64_t EVEN = 0x5555555555555555ull, ODD = ~EVEN;
@@ -437,44 +437,6 @@ __device__ void bpe_seg2(const DevVocab &v, const uint8_t *__restrict__ bytes, u
     }
 }
 
-// The lists of short unresolved pieces are independent and each role above is bound by its
-// dependent table probes, so they run as one launch: the workgroups are split into six ranges, one
-// per list, and all of them progress at the same time.
-__global__ __launch_bounds__(256) void k_bpe_small(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws, Layout L,
-                                                  uint32_t g8, uint32_t g12, uint32_t g16, uint32_t g32, uint32_t g64,
-                                                  uint32_t g128)
-{
-    __shared__ __align__(16) uint32_t rows[256 * LROW];   // the lane units' rows
-    // workgroup ranges in order of the units' round counts (longest first): workgroups are dispatched
-    // in order, so the long chains start at once and the many short ones fill in around them.  The
-    // ranges are cut to what the lists hold (the grid is sized for the largest possible lists), so
-    // that the workgroups with work come first and the idle ones are dispatched last.
-    {
-        const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
-        const uint32_t *cnt = ctrl->miss_count;
-        g128 = min(g128, (cnt[5] + 3u) / 4u);     // a piece per wavefront
-        g64 = min(g64, (cnt[4] + 3u) / 4u);
-        g32 = min(g32, (cnt[3] + 255u) / 256u);   // a piece per lane
-        g16 = min(g16, (cnt[2] + 255u) / 256u);
-        g12 = min(g12, (cnt[1] + 255u) / 256u);
-        g8 = min(g8, (cnt[0] + 255u) / 256u);
-    }
-    uint32_t b = blockIdx.x;
-    if (b < g128) {
-        bpe_seg2(v, bytes, ws, L, b, g128);
-    } else if ((b -= g128) < g64) {
-        bpe_seg<64>(v, bytes, ws, L, 4, b, g64);
-    } else if ((b -= g64) < g32) {
-        bpe_lane<32>(v, bytes, ws, L, rows, 3, b, g32);
-    } else if ((b -= g32) < g16) {
-        bpe_lane<16>(v, bytes, ws, L, rows, 2, b, g16);
-    } else if ((b -= g16) < g12) {
-        bpe_lane<12>(v, bytes, ws, L, rows, 1, b, g12);
-    } else if ((b -= g12) < g8) {
-        bpe_lane<8>(v, bytes, ws, L, rows, 0, b, g8);
-    }
-}
-
 // ---------------------------------------------------------------------------------------------
 // workgroup primitives (NT threads, NT a multiple of 64)
 
@@ -549,17 +511,41 @@ __device__ __forceinline__ int32_t block_excl_max(int32_t x, int32_t *red)
 // ---------------------------------------------------------------------------------------------
 // piece per wavefront / workgroup, sequence in LDS
 
+// barrier of a unit: the workgroup, or (NT = 64) the unit's own wavefront, so that the wavefronts of a
+// workgroup can work on different pieces
+template <int NT>
+__device__ __forceinline__ void unit_sync()
+{
+    if (NT == 64) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+        __syncthreads();
+    }
+}
+
+// LDS of one workgroup unit: ids, ranks, selection bytes and the reduction slots
 template <int NT, int MAXN>
-__global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws,
-                                                  Layout L, int bin)
+constexpr uint32_t block_unit_lds()
+{
+    return 4u * MAXN + 4u * MAXN + ((MAXN + 1 + 15) & ~15) + 4u * (NT / 64 + 1) + 4u * (NT / 64 + 1);
+}
+
+// One unit of NT lanes (a workgroup, or one wavefront of it when NT = 64) per piece of list `bin` (0:
+// 129..WAVE_MAX bytes, 1: ..BLOCK_MAX bytes) and per chunk of a giant piece in the same size range;
+// unit blk of nblk.  `smem` holds the unit's block_unit_lds bytes.
+template <int NT, int MAXN>
+__device__ __forceinline__ void bpe_block(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L, int bin,
+                          uint8_t *smem, uint32_t blk, uint32_t nblk)
 {
     constexpr int E = MAXN / NT;
     static_assert(E <= 32, "selection masks are 32-bit");
-    __shared__ uint32_t sid[MAXN];
-    __shared__ uint32_t srk[MAXN];
-    __shared__ uint8_t ssel[MAXN + 1];
-    __shared__ uint32_t red[NT / 64 + 1];
-    __shared__ int32_t redi[NT / 64 + 1];
+    uint32_t *sid = (uint32_t *)smem;
+    uint32_t *srk = sid + MAXN;
+    uint8_t *ssel = (uint8_t *)(srk + MAXN);
+    uint32_t *red = (uint32_t *)(ssel + ((MAXN + 1 + 15) & ~15));
+    int32_t *redi = (int32_t *)(red + (NT / 64 + 1));
 
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
@@ -573,10 +559,10 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
     const uint32_t cmin = bin == 0 ? (uint32_t)SEG2_MAX + 1u : (uint32_t)WAVE_MAX + 1u;
     const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
     uint32_t *ccount = (uint32_t *)(ws + L.ccount);
-    const uint32_t tid = threadIdx.x;
+    const uint32_t tid = threadIdx.x % NT;
     const uint32_t k0 = tid * E;
 
-    for (uint32_t q = blockIdx.x; q < count + n_chunks; q += gridDim.x) {
+    for (uint32_t q = blk; q < count + n_chunks; q += nblk) {
         const bool is_chunk = q >= count;
         uint32_t p = 0, b0, n;
         if (!is_chunk) {
@@ -591,9 +577,9 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
         if ((v.flags & VF_IGNORE_MERGES) && !is_chunk && n <= v.lmax) {
             // ignore_merges: a piece that is a token's byte string is that token
             if (tid == 0) red[0] = whole_token(v, bytes + b0, n);
-            __syncthreads();
+            unit_sync<NT>();
             const uint32_t w = red[0];
-            __syncthreads();
+            unit_sync<NT>();
             if (w != NO_PIECE) {
                 if (tid == 0) {
                     scratch[b0] = w;
@@ -603,10 +589,10 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
             }
         }
         for (uint32_t k = tid; k < n; k += NT) sid[k] = bytes[b0 + k];
-        __syncthreads();
+        unit_sync<NT>();
         for (uint32_t k = tid; k < n; k += NT)
             srk[k] = k + 1 < n ? rkx_rank(__ldg(v.r2 + ((sid[k] << 8) | sid[k + 1]))) : NO_RANK;
-        __syncthreads();
+        unit_sync<NT>();
         for (;;) {
             uint32_t lmin = NO_RANK;
 #pragma unroll
@@ -643,7 +629,7 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
             for (int e = 0; e < E; ++e)
                 if (k0 + e < n) ssel[k0 + e] = (selm >> e) & 1u;
             if (tid == 0) ssel[n] = 0;
-            __syncthreads();
+            unit_sync<NT>();
             // keep = not the right half of a selected pair
             uint32_t keepm = 0, cnt = 0;
 #pragma unroll
@@ -665,15 +651,15 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
                     nrk[e] = (s || ssel[k + 1]) ? PENDING : srk[k];
                 }
             }
-            __syncthreads();
+            unit_sync<NT>();
             uint32_t o = off;
 #pragma unroll
             for (int e = 0; e < E; ++e)
                 if ((keepm >> e) & 1u) { sid[o] = nid[e]; srk[o] = nrk[e]; ++o; }
-            __syncthreads();
+            unit_sync<NT>();
             for (uint32_t j = off; j < off + cnt; ++j)
                 if (srk[j] == PENDING) srk[j] = j + 1 < nnew ? pair_rank(v, sid[j], sid[j + 1]) : NO_RANK;
-            __syncthreads();
+            unit_sync<NT>();
             n = nnew;
         }
         for (uint32_t k = tid; k < n; k += NT) scratch[b0 + k] = sid[k];
@@ -681,7 +667,56 @@ __global__ __launch_bounds__(NT) void k_bpe_block(DevVocab v, const uint8_t *__r
             if (is_chunk) ccount[q - count] = n;
             else put_piece(ws, L, p, b0, n, 0u, true);
         }
-        __syncthreads();
+        unit_sync<NT>();
+    }
+}
+
+// The lists of short unresolved pieces are independent and each role above is bound by its
+// dependent table probes, so they run as one launch: the workgroups are split into six ranges, one
+// per list, and all of them progress at the same time.
+__global__ __launch_bounds__(256) void k_bpe_small(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws, Layout L,
+                                                  uint32_t gb, uint32_t gw, uint32_t g8, uint32_t g12, uint32_t g16,
+                                                  uint32_t g32, uint32_t g64, uint32_t g128)
+{
+    // the lane units' rows; the workgroup units' sequences
+    __shared__ __align__(16) uint32_t rows[256 * LROW];
+    constexpr uint32_t WAVE_UNIT = (block_unit_lds<64, WAVE_MAX>() + 15u) & ~15u;
+    static_assert(block_unit_lds<256, BLOCK_MAX>() <= sizeof(rows) && 4 * WAVE_UNIT <= sizeof(rows), "unit LDS");
+    // workgroup ranges in order of the units' round counts (longest first): workgroups are dispatched
+    // in order, so the long chains start at once and the many short ones fill in around them.  The
+    // ranges are cut to what the lists hold (the grid is sized for the largest possible lists), so
+    // that the workgroups with work come first and the idle ones are dispatched last.
+    {
+        const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
+        const uint32_t *cnt = ctrl->miss_count;
+        const uint32_t nch = ctrl->n_chunks;       // (chunk slots: every list's unit looks at them)
+        gb = min(gb, ctrl->bin_count[1] + nch);    // a piece per workgroup
+        gw = min(gw, (ctrl->bin_count[0] + nch + 3u) / 4u);   // a piece per wavefront
+        g128 = min(g128, (cnt[5] + 3u) / 4u);     // a piece per wavefront
+        g64 = min(g64, (cnt[4] + 3u) / 4u);
+        g32 = min(g32, (cnt[3] + 255u) / 256u);   // a piece per lane
+        g16 = min(g16, (cnt[2] + 255u) / 256u);
+        g12 = min(g12, (cnt[1] + 255u) / 256u);
+        g8 = min(g8, (cnt[0] + 255u) / 256u);
+    }
+    uint32_t b = blockIdx.x;
+    if (b < gb) {
+        bpe_block<256, BLOCK_MAX>(v, bytes, ws, L, 1, (uint8_t *)rows, b, gb);
+    } else if ((b -= gb) < gw) {
+        const uint32_t w = threadIdx.x >> 6;
+        bpe_block<64, WAVE_MAX>(v, bytes, ws, L, 0, (uint8_t *)rows + w * WAVE_UNIT, 4 * b + w, 4 * gw);
+    } else if ((b -= gw) < g128) {
+        bpe_seg2(v, bytes, ws, L, b, g128);
+    } else if ((b -= g128) < g64) {
+        bpe_seg<64>(v, bytes, ws, L, 4, b, g64);
+    } else if ((b -= g64) < g32) {
+        bpe_lane<32>(v, bytes, ws, L, rows, 3, b, g32);
+    } else if ((b -= g32) < g16) {
+        bpe_lane<16>(v, bytes, ws, L, rows, 2, b, g16);
+    } else if ((b -= g16) < g12) {
+        bpe_lane<12>(v, bytes, ws, L, rows, 1, b, g12);
+    } else if ((b -= g12) < g8) {
+        bpe_lane<8>(v, bytes, ws, L, rows, 0, b, g8);
     }
 }
 
@@ -732,33 +767,6 @@ __device__ __forceinline__ uint32_t safe_word(uint32_t a, uint32_t b0)
     return a / 32 + b0 / 4096;
 }
 
-// k_gsafe: every position of every giant piece is tested; workgroups share out 1024-position
-// blocks (aligned to absolute positions) of each piece in turn
-__global__ __launch_bounds__(1024) void k_gsafe(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws, Layout L)
-{
-    const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
-    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
-    const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
-    uint32_t *bm = (uint32_t *)(ws + L.gsafe);
-    const uint32_t count = ctrl->bin_count[2];
-    const uint32_t tid = threadIdx.x, lane = tid & 63u;
-    if (count == 0) return;
-    for (uint32_t g = 0; v.str && g < count; ++g) {
-        const uint32_t p = list[g];
-        const uint32_t b0 = pstart[p], n = pstart[p + 1] - b0;
-        const uint32_t first = b0 / 1024, last = (b0 + n - 1) / 1024;
-        for (uint32_t blk = first + blockIdx.x; blk <= last; blk += gridDim.x) {
-            const uint32_t a = blk * 1024 + tid;
-            const bool ok = a > b0 && a < b0 + n && seam_safe(v, bytes + b0, n, a - b0);
-            const uint64_t m = __ballot(ok);
-            const uint32_t a0 = a - lane;   // multiple of 64
-            // a word is written by the piece whose positions (b0, b0 + n) it covers
-            if (lane == 0 && a0 + 31 > b0 && a0 < b0 + n) bm[safe_word(a0, b0)] = (uint32_t)m;
-            if (lane == 32 && a0 + 63 > b0 && a0 + 32 < b0 + n) bm[safe_word(a0 + 32, b0)] = (uint32_t)(m >> 32);
-        }
-    }
-}
-
 // first and last safe position of window [lo, hi) of the piece at b0 (NO_PIECE if none); lo > b0
 __device__ __forceinline__ void window_safe(const uint32_t *bm, uint32_t b0, uint32_t lo, uint32_t hi, uint32_t &f,
                                             uint32_t &l)
@@ -774,14 +782,14 @@ __device__ __forceinline__ void window_safe(const uint32_t *bm, uint32_t b0, uin
     }
 }
 
-// k_gcut: one workgroup per giant piece turns the bitmap into chunks.  The piece is divided into
+// giant_cut: a workgroup of 1024 turns piece g's bitmap into chunks.  The piece is divided into
 // windows of GCH positions; every window with a safe position is cut at its first one (chunks of
 // about GCH bytes where seams are common), and a window followed by one without any safe position
 // is also cut at its last one, so that a stretch without seams (typically a repeated character,
 // which needs few merge rounds) is a chunk of its own.  Cuts come out sorted; a workgroup scan
 // places them.  Chunks take consecutive slots of the chunk table (unused reserved slots: length 0);
 // chunks of up to SEG2_MAX bytes are also listed for the lane and segment kernels.
-__global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, Layout L)
+__device__ __forceinline__ void giant_cut(const DevVocab &v, uint8_t *ws, const Layout &L, uint32_t g)
 {
     constexpr uint32_t NT = 1024, NW = NT / 64;
     __shared__ uint32_t swsum[NW];
@@ -792,9 +800,8 @@ __global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, La
     const uint32_t *bm = (const uint32_t *)(ws + L.gsafe);
     uint32_t *cstart = (uint32_t *)(ws + L.cstart), *clen = (uint32_t *)(ws + L.clen);
     uint32_t *gc0 = (uint32_t *)(ws + L.gc0), *gnc = (uint32_t *)(ws + L.gnc);
-    const uint32_t count = ctrl->bin_count[2];
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
-    for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) {
+    {
         const uint32_t p = list[g];
         const uint32_t b0 = pstart[p], n = pstart[p + 1] - b0, end = b0 + n;
         const uint32_t nwin = v.str ? (n + GCH - 1) / GCH : 0u;
@@ -866,6 +873,51 @@ __global__ __launch_bounds__(1024) void k_gcut(const DevVocab v, uint8_t *ws, La
             gnc[g] = nc;
         }
         __syncthreads();
+    }
+}
+
+// k_giant_prep: every position of every giant piece is tested for a seam, the workgroups sharing out
+// 1024-position blocks (aligned to absolute positions) of each piece in turn; the last workgroup to
+// finish its blocks of a piece (a counter per piece, cleared by the summary kernel) cuts it.  Without
+// the token string hash (no seams) each piece is one chunk, cut by workgroup g mod grid.
+__global__ __launch_bounds__(1024) void k_giant_prep(DevVocab v, const uint8_t *__restrict__ bytes, uint8_t *ws, Layout L)
+{
+    __shared__ uint32_t s_last;
+    Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
+    const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
+    const uint32_t *list = (const uint32_t *)(ws + L.bin_giant);
+    uint32_t *bm = (uint32_t *)(ws + L.gsafe);
+    uint32_t *gdone = (uint32_t *)(ws + L.gdone);
+    const uint32_t count = ctrl->bin_count[2];
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    if (count == 0) return;
+    if (!v.str) {
+        for (uint32_t g = blockIdx.x; g < count; g += gridDim.x) giant_cut(v, ws, L, g);
+        return;
+    }
+    for (uint32_t g = 0; g < count; ++g) {
+        const uint32_t p = list[g];
+        const uint32_t b0 = pstart[p], n = pstart[p + 1] - b0;
+        const uint32_t first = b0 / 1024, last = (b0 + n - 1) / 1024, nb = last - first + 1;
+        if (blockIdx.x >= nb) continue;   // no block of this piece for this workgroup
+        for (uint32_t blk = first + blockIdx.x; blk <= last; blk += gridDim.x) {
+            const uint32_t a = blk * 1024 + tid;
+            const bool ok = a > b0 && a < b0 + n && seam_safe(v, bytes + b0, n, a - b0);
+            const uint64_t m = __ballot(ok);
+            const uint32_t a0 = a - lane;   // multiple of 64
+            // a word is written by the piece whose positions (b0, b0 + n) it covers
+            if (lane == 0 && a0 + 31 > b0 && a0 < b0 + n) bm[safe_word(a0, b0)] = (uint32_t)m;
+            if (lane == 32 && a0 + 63 > b0 && a0 + 32 < b0 + n) bm[safe_word(a0 + 32, b0)] = (uint32_t)(m >> 32);
+        }
+        // the piece's bitmap words are complete once every participating workgroup has counted
+        __syncthreads();
+        if (tid == 0) {
+            __threadfence();
+            s_last = atomicAdd(&gdone[g], 1u) == min(nb, gridDim.x) - 1u;
+            __threadfence();
+        }
+        __syncthreads();
+        if (s_last) giant_cut(v, ws, L, g);
     }
 }
 
@@ -1069,9 +1121,7 @@ hipError_t launch_giant_prep(const DevVocab &v, const Batch &b, hipStream_t s, c
     // giant pieces: safe-seam bitmap, then chunks (listed with the other BPE items by length)
     LaunchScope k(ev, TK_GIANT_SEAMS, s);
     const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
-    hipLaunchKernelGGL(k_gsafe, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
-    const uint32_t gc = L.cap_giant < 64 ? L.cap_giant : 64;
-    hipLaunchKernelGGL(k_gcut, dim3(gc), dim3(1024), 0, s, v, b.ws, L);
+    hipLaunchKernelGGL(k_giant_prep, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
     return hipGetLastError();
 }
 
@@ -1086,22 +1136,15 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
         const uint32_t g8 = cap((b.n / 2 + L.cap_chunks) / 256 + 1, 2048), g12 = cap(b.n / 9 / 256 + 1, 2048);
         const uint32_t g16 = cap(b.n / 13 / 256 + 1, 2048), g32 = cap(b.n / 17 / 256 + 1, 2048);
         const uint32_t g64 = cap(b.n / 33 / 4 + 1, 256), g128 = cap(b.n / 65 / 4 + 1, 256);
-        LaunchScope k(ev, TK_BPE_SHORT, s);
-        hipLaunchKernelGGL(k_bpe_small, dim3(g8 + g12 + g16 + g32 + g64 + g128), dim3(256), 0, s, v, b.bytes, b.ws, L,
-                           g8, g12, g16, g32, g64, g128);
-    }
-    {
-        LaunchScope k(ev, TK_BPE_WAVE, s);
-        uint32_t gw = L.cap_wave + L.cap_chunks < 1024 ? L.cap_wave + L.cap_chunks : 1024;
-        hipLaunchKernelGGL((k_bpe_block<64, WAVE_MAX>), dim3(gw), dim3(64), 0, s, v, b.bytes, b.ws, L, 0);
+        // and the lists of 129..1024 bytes (a wavefront per piece) and 1025..4096 bytes (a workgroup per
+        // piece) in the same launch
+        const uint32_t gw = cap(((uint64_t)L.cap_wave + L.cap_chunks + 3) / 4, 256);
+        const uint32_t gb = cap((uint64_t)L.cap_block + L.cap_chunks, 256);
+        LaunchScope k(ev, TK_BPE, s);
+        hipLaunchKernelGGL(k_bpe_small, dim3(gb + gw + g8 + g12 + g16 + g32 + g64 + g128), dim3(256), 0, s, v, b.bytes,
+                           b.ws, L, gb, gw, g8, g12, g16, g32, g64, g128);
     }
     const uint32_t gg = L.cap_giant < 64 ? L.cap_giant : 64;
-    {
-        LaunchScope k(ev, TK_BPE_BLOCK, s);
-        uint32_t gb = L.cap_block + L.cap_chunks < 256 ? L.cap_block + L.cap_chunks : 256;
-        hipLaunchKernelGGL((k_bpe_block<BLOCK_THREADS, BLOCK_MAX>), dim3(gb), dim3(BLOCK_THREADS), 0, s, v,
-                           b.bytes, b.ws, L, 1);
-    }
     {
         LaunchScope k(ev, TK_BPE_GIANT, s);
         hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);

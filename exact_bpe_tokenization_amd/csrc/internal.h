@@ -428,7 +428,7 @@ static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 // workspace layout for n input bytes
 struct Layout {
     uint64_t ctrl, cc, tbwd, tdoc, twin, tflag_state, tcnt, tfirst, gsum, tcount, tsb, tbase, pstart, pval, tokoff, scratch,
-        bin_wave, bin_block, bin_giant, miss[6], g_ids, g_rank_a, g_rank_b, tspill, prs, cstart, clen, ccount, gc0, gnc, gsafe,
+        bin_wave, bin_block, bin_giant, miss[6], g_ids, g_rank_a, g_rank_b, tspill, prs, cstart, clen, ccount, gc0, gnc, gdone, gsafe,
         cpiece, total;
     uint32_t n_tiles, cap_wave, cap_block, cap_giant, cap_chunks, n_safe_words;
     // a plan captured for a size bucket: the request's sizes are read from dsz (device: total bytes,
@@ -495,6 +495,7 @@ inline Layout make_layout(uint64_t n)
     L.ccount = o;      o += align256(4ull * L.cap_chunks);
     L.gc0 = o;         o += align256(4ull * L.cap_giant);
     L.gnc = o;         o += align256(4ull * L.cap_giant);
+    L.gdone = o;       o += align256(4ull * L.cap_giant);       // seam workgroups done, per giant piece
     L.gsafe = o;       o += align256(4ull * L.n_safe_words);
     L.cpiece = o;      o += align256(4ull * L.cap_chunks);
     L.total = o;
@@ -685,8 +686,8 @@ struct Batch {
 };
 
 // launch indices of the encode chain (TOKTIER_K_* in toktier.h)
-enum : int { TK_SUMMARY = 0, TK_PIECES = 1, TK_GIANT_SEAMS = 2, TK_TILES = 3, TK_BPE_SHORT = 4, TK_BPE_WAVE = 5,
-             TK_BPE_BLOCK = 6, TK_BPE_GIANT = 7, TK_EMIT = 8, TK_COUNT = 9 };
+enum : int { TK_SUMMARY = 0, TK_PIECES = 1, TK_GIANT_SEAMS = 2, TK_TILES = 3, TK_BPE = 4, TK_BPE_GIANT = 5, TK_EMIT = 6,
+             TK_COUNT = 7 };
 
 // optional events recorded around each kernel launch (indices: TOKTIER_K_* in toktier.h)
 struct Events {

@@ -354,6 +354,7 @@ __global__ __launch_bounds__(128) void k_summary(DevVocab v, const uint8_t *__re
             ((uint32_t *)(ws + L.tsb))[k] = 0;
             ((uint32_t *)(ws + L.gsum))[k] = 0;
         }
+        for (uint32_t k = blockIdx.x * 64u + lane; k < L.cap_giant; k += gridDim.x * 64u) ((uint32_t *)(ws + L.gdone))[k] = 0;
     }
     if (blockIdx.x >= n_tiles) return;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
@@ -621,7 +622,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     __shared__ uint32_t sbkw[NW];
     __shared__ uint4 swmap[NW];
     __shared__ uint32_t swcnt[NW], swstate[NW];
-    __shared__ uint32_t s_tile, s_carry, s_d0, s_d1, s_o0, s_o1;
+    __shared__ uint32_t s_tile, s_carry, s_d0, s_d1, s_o0, s_o1, s_win, s_bk;
 
     const uint32_t n_tiles = request_sizes(L, n, n_docs);
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
@@ -657,10 +658,6 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     // overlaps the decode
     uint32_t bk_first = BK_T | (BK_T << 2);
     if (wid == 0 && tile + 1 + lane < n_tiles) bk_first = (ws + L.tbwd)[tile + 1 + lane];
-    // the previous tile's window states and this tile's own backward summary (which of those
-    // states applies)
-    const uint32_t win_prev = tile > 0 ? ((const uint32_t *)(ws + L.twin))[tile - 1] : 0u;
-    const uint32_t bk_self = (ws + L.tbwd)[tile];
 
     // raw bytes [lo - 4, lo + TILE + 24), as 32-bit words
     // (interior words from two aligned 4-byte loads, which never leave the pages of the bytes they
@@ -686,6 +683,11 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         s_d1 = dd.y;
         s_o0 = dd.z;
         s_o1 = dd.w;
+    } else if (tid == 64) {
+        // the previous tile's window states and this tile's own backward summary (which of those
+        // states applies)
+        s_win = tile > 0 ? ((const uint32_t *)(ws + L.twin))[tile - 1] : 0u;
+        s_bk = (ws + L.tbwd)[tile];
     }
     // document offsets must start at 0, never decrease and end at n
     bool bad_offs = false;
@@ -955,9 +957,10 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         const M16 tile_map = shfl16(wm, NW - 1);
         // automaton state entering this tile: fixed by the previous tile's last bytes, else from the
         // look-back (this tile's flags: its map, then the state after it)
+        const uint32_t bk_self = s_bk;
         const uint32_t na_prev = (bk_self & 3u) != BK_KEEP ? (bk_self & 1u) : (s_carry & 1u);
         const uint32_t au_prev = (bk_self >> 2) != BK_KEEP ? ((bk_self >> 2) & 1u) : ((s_carry >> 1) & 1u);
-        const uint32_t wv = (win_prev >> (8u * (na_prev | (CASE ? au_prev << 1 : 0u)))) & 0xFFu;
+        const uint32_t wv = (s_win >> (8u * (na_prev | (CASE ? au_prev << 1 : 0u)))) & 0xFFu;
         uint32_t entry = S_ST;
         if (tile > 0) {
             if (wv & 0x10u) {

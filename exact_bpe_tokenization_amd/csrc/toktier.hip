@@ -569,6 +569,7 @@ int build_whole_piece_tables(toktier_vocab *v, const TokenStrings &ts)
     if (e == hipSuccess) e = hipMalloc((void **)&dws, L.total);
     if (e == hipSuccess) e = hipMemcpy(dbytes, batch.data(), N, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemset(dws + L.ctrl, 0, sizeof(Ctrl));
+    if (e == hipSuccess) e = hipMemset(dws + L.gdone, 0, 4ull * L.cap_giant);
     if (e == hipSuccess) e = hipMemcpy(dws + L.ctrl + offsetof(Ctrl, n_pieces), &npc, 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
         e = hipMemcpy(dws + L.pstart, starts.data(), 4ull * starts.size(), hipMemcpyHostToDevice);
