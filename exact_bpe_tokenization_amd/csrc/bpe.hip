@@ -130,7 +130,12 @@ __global__ __launch_bounds__(RT_THREADS) void k_route(DevVocab v, const uint8_t 
 // the next live position q; p's neighbours are the live positions around it).  A round is one pass of
 // 16-byte LDS reads, a few bit operations, two element reads, three writes and the probes.  Called by
 // all 64 lanes of a wavefront; len 0 = idle.
-constexpr int LROW = 68;   // words per lane row
+// Row layout of a lane unit: MAXL rank words, then (at lane_el_off) MAXL element words, padded by 4
+// words against bank conflicts.  Units of up to 16 bytes take 36-word rows, 256 lanes per workgroup;
+// 17..32-byte units take 68-word rows, 128 lanes per workgroup (the same LDS).
+template <int MAXL> constexpr int lane_el_off() { return MAXL <= 16 ? 16 : 32; }
+template <int MAXL> constexpr int lane_row_words() { return 2 * lane_el_off<MAXL>() + 4; }
+template <int MAXL> constexpr uint32_t lane_unit_lanes() { return MAXL <= 16 ? 256u : 128u; }
 
 template <int MAXL>
 __device__ __forceinline__ uint32_t lane_bpe(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws,
@@ -143,7 +148,7 @@ __device__ __forceinline__ uint32_t lane_bpe(const DevVocab &v, const uint8_t *_
     const bool active = len != 0;
     const bool chunk = (e & CHUNK_ITEM) != 0;
     const uint32_t p = e & ~CHUNK_ITEM;
-    uint32_t *el = row + 32;
+    uint32_t *el = row + lane_el_off<MAXL>();
     {
         uint64_t w[MAXL / 8 + (MAXL % 8 ? 1 : 0)];
         load_words<MAXL / 8 + (MAXL % 8 ? 1 : 0)>(bytes + b0, len, w);
@@ -214,15 +219,17 @@ template <int MAXL>
 __device__ __forceinline__ void bpe_lane(const DevVocab &v, const uint8_t *__restrict__ bytes, uint8_t *ws, const Layout &L,
                          uint32_t *rows, uint32_t r, uint32_t blk, uint32_t nblk)
 {
-    uint32_t *row = rows + (threadIdx.x) * LROW;
+    constexpr uint32_t LANES = lane_unit_lanes<MAXL>();
+    if (threadIdx.x >= LANES) return;   // (whole wavefronts)
+    uint32_t *row = rows + threadIdx.x * lane_row_words<MAXL>();
     const Ctrl *ctrl = (const Ctrl *)(ws + L.ctrl);
     const uint32_t *pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *list = route_list(ws, L, r);
     const uint32_t count = ctrl->miss_count[r];
     const uint32_t *cstart = (const uint32_t *)(ws + L.cstart), *clen = (const uint32_t *)(ws + L.clen);
     const uint32_t lane = threadIdx.x & 63u;
-    const uint32_t wave = (blk * blockDim.x + threadIdx.x) >> 6;
-    const uint32_t nwaves = (nblk * blockDim.x) >> 6;
+    const uint32_t wave = (blk * LANES + threadIdx.x) >> 6;
+    const uint32_t nwaves = (nblk * LANES) >> 6;
     for (uint32_t q0 = wave * 64u; q0 < count; q0 += nwaves * 64u) {   // wavefront-uniform
         const uint32_t q = q0 + lane;
         uint32_t e = 0, b0 = 0, len = 0;
@@ -678,10 +685,15 @@ __global__ __launch_bounds__(256) void k_bpe_small(DevVocab v, const uint8_t *__
                                                   uint32_t gb, uint32_t gw, uint32_t g8, uint32_t g12, uint32_t g16,
                                                   uint32_t g32, uint32_t g64, uint32_t g128)
 {
-    // the lane units' rows; the workgroup units' sequences
-    __shared__ __align__(16) uint32_t rows[256 * LROW];
+    // the lane units' rows; the workgroup units' sequences (one allocation: four workgroups per CU)
     constexpr uint32_t WAVE_UNIT = (block_unit_lds<64, WAVE_MAX>() + 15u) & ~15u;
-    static_assert(block_unit_lds<256, BLOCK_MAX>() <= sizeof(rows) && 4 * WAVE_UNIT <= sizeof(rows), "unit LDS");
+    constexpr uint32_t LANE_LDS = 4u * lane_row_words<16>() * lane_unit_lanes<16>();
+    static_assert(4u * lane_row_words<32>() * lane_unit_lanes<32>() <= LANE_LDS, "lane rows");
+    constexpr uint32_t BLOCK_LDS = (block_unit_lds<256, BLOCK_MAX>() + 15u) & ~15u;
+    constexpr uint32_t SMEM0 = LANE_LDS > BLOCK_LDS ? LANE_LDS : BLOCK_LDS;
+    constexpr uint32_t SMEM = SMEM0 > 4 * WAVE_UNIT ? SMEM0 : 4 * WAVE_UNIT;
+    static_assert(SMEM <= 40960, "four workgroups per CU");
+    __shared__ __align__(16) uint32_t rows[SMEM / 4];
     // workgroup ranges in order of the units' round counts (longest first): workgroups are dispatched
     // in order, so the long chains start at once and the many short ones fill in around them.  The
     // ranges are cut to what the lists hold (the grid is sized for the largest possible lists), so
@@ -694,7 +706,7 @@ __global__ __launch_bounds__(256) void k_bpe_small(DevVocab v, const uint8_t *__
         gw = min(gw, (ctrl->bin_count[0] + nch + 3u) / 4u);   // a piece per wavefront
         g128 = min(g128, (cnt[5] + 3u) / 4u);     // a piece per wavefront
         g64 = min(g64, (cnt[4] + 3u) / 4u);
-        g32 = min(g32, (cnt[3] + 255u) / 256u);   // a piece per lane
+        g32 = min(g32, (cnt[3] + 127u) / 128u);   // a piece per lane (128 lanes per workgroup)
         g16 = min(g16, (cnt[2] + 255u) / 256u);
         g12 = min(g12, (cnt[1] + 255u) / 256u);
         g8 = min(g8, (cnt[0] + 255u) / 256u);
@@ -1134,7 +1146,7 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
         // n / 9, n / 13, n / 17, n / 33, n / 65 items; 256 lane items, 4 and 4 pieces per workgroup
         auto cap = [](uint64_t x, uint32_t c) { return x > c ? c : (uint32_t)x; };
         const uint32_t g8 = cap((b.n / 2 + L.cap_chunks) / 256 + 1, 2048), g12 = cap(b.n / 9 / 256 + 1, 2048);
-        const uint32_t g16 = cap(b.n / 13 / 256 + 1, 2048), g32 = cap(b.n / 17 / 256 + 1, 2048);
+        const uint32_t g16 = cap(b.n / 13 / 256 + 1, 2048), g32 = cap(b.n / 17 / 128 + 1, 2048);
         const uint32_t g64 = cap(b.n / 33 / 4 + 1, 256), g128 = cap(b.n / 65 / 4 + 1, 256);
         // and the lists of 129..1024 bytes (a wavefront per piece) and 1025..4096 bytes (a workgroup per
         // piece) in the same launch
