@@ -42,7 +42,8 @@ struct ResolveSmem {
 struct EmitSmem {
     uint32_t docbits[TILE / 32];      // document starts in the tile
     uint32_t wsum[NW];
-    uint32_t base;
+    uint32_t base, p0, p1;
+    uint4 dd;
 };
 
 template <typename S>
@@ -561,14 +562,37 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
     const uint32_t tile = blockIdx.x;
     const uint64_t lo = (uint64_t)tile * TILE;
     const uint64_t hi = min(lo + (uint64_t)TILE, n);
-    const uint32_t p0 = tbase[tile], p1 = tbase[tile + 1], cnt = p1 - p0;
+    auto count_of = [](uint32_t pv) -> uint32_t { return (pv & PV_MULTI) ? (pv & PV_COUNT) : 1u; };
+
+    // the loads that depend on nothing, at once: the tile's piece range and document window; wave 0:
+    // the first output index of the tile (the groups of 64 tiles before its group, then the tiles
+    // before it in its group; counts are final: every kernel that adds to them has finished)
+    for (uint32_t i = tid; i < TILE / 32; i += NT) sm.docbits[i] = 0;
+    if (wid == 0) {
+        const uint32_t g = tile / 64u;
+        uint32_t x = 0;
+        for (uint32_t t = lane; t < g; t += 64) x += tsb[t];
+        if (64 * g + lane < tile) x += tcount[64 * g + lane];
+        x = wave_incl_sum(x);
+        if (lane == 63) sm.base = x;
+    } else if (tid == 64) {
+        sm.p0 = tbase[tile];
+        sm.p1 = tbase[tile + 1];
+        sm.dd = ((const uint4 *)(ws + L.tdoc))[tile];
+    }
+    __syncthreads();
+    const uint32_t p0 = sm.p0, p1 = sm.p1, cnt = p1 - p0;
+    const uint4 dd = sm.dd;
     // wavefront wid owns pieces [qb, qe) of the tile (a multiple of 64 each)
     const uint32_t Q = ((cnt + NW - 1) / NW + 63u) & ~63u;
     const uint32_t qb = p0 + min(cnt, wid * Q), qe = p0 + min(cnt, (wid + 1) * Q);
-    auto count_of = [](uint32_t pv) -> uint32_t { return (pv & PV_MULTI) ? (pv & PV_COUNT) : 1u; };
 
-    for (uint32_t i = tid; i < TILE / 32; i += NT) sm.docbits[i] = 0;
-    // tokens of this wavefront's pieces (all loads in flight, four per lane per step)
+    // document starts in [lo, hi) (k_summary found the documents of a window around the tile), and
+    // the tokens of this wavefront's pieces (all loads in flight, four per lane per step)
+    for (uint32_t d = dd.x + tid; d < dd.y; d += NT) {
+        const uint64_t od = offsets[d];
+        if (od >= lo && od < hi) atomicOr(&sm.docbits[(od - lo) >> 5], 1u << ((od - lo) & 31u));
+    }
     {
         uint32_t x = 0;
         for (uint32_t r = qb; r < qe; r += 256) {
@@ -584,26 +608,9 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
         x = wave_incl_sum(x);
         if (lane == 63) sm.wsum[wid] = x;
     }
-    // first output index of the tile: the groups of 64 tiles before its group, then the tiles before
-    // it in its group (counts are final: every kernel that adds to them has finished)
-    if (wid == 0) {
-        const uint32_t g = tile / 64u;
-        uint32_t x = 0;
-        for (uint32_t t = lane; t < g; t += 64) x += tsb[t];
-        if (64 * g + lane < tile) x += tcount[64 * g + lane];
-        x = wave_incl_sum(x);
-        if (lane == 63) sm.base = x;
-    }
     __syncthreads();
-    // document starts in [lo, hi) (k_summary found the documents of a window around the tile)
-    const uint4 dd = ((const uint4 *)(ws + L.tdoc))[tile];
-    for (uint32_t d = dd.x + tid; d < dd.y; d += NT) {
-        const uint64_t od = offsets[d];
-        if (od >= lo && od < hi) atomicOr(&sm.docbits[(od - lo) >> 5], 1u << ((od - lo) & 31u));
-    }
     uint32_t run = sm.base;
     for (uint32_t w = 0; w < wid; ++w) run += sm.wsum[w];
-    __syncthreads();
 
     // rounds of 64 pieces per wavefront: a DPP scan of their counts places their IDs (the loads of
     // four rounds in flight at once)
@@ -633,13 +640,21 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
                 out_ids[o] = pv;
                 if (SPANS) out_spans[o] = a;
             } else if (!(pv & PV_LONG)) {
+                // the piece's IDs from scratch, eight loads in flight
                 uint32_t sp = a;
-                for (uint32_t t = 0; t < c; ++t) {
-                    const uint32_t x = scratch[a + t];
-                    out_ids[o + t] = x;
-                    if (SPANS) {
-                        out_spans[o + t] = sp;
-                        sp += tok_len[x];
+                for (uint32_t t0 = 0; t0 < c; t0 += 8) {
+                    uint32_t x[8];
+#pragma unroll
+                    for (uint32_t u = 0; u < 8; ++u) x[u] = t0 + u < c ? scratch[a + t0 + u] : 0u;
+#pragma unroll
+                    for (uint32_t u = 0; u < 8; ++u) {
+                        if (t0 + u < c) {
+                            out_ids[o + t0 + u] = x[u];
+                            if (SPANS) {
+                                out_spans[o + t0 + u] = sp;
+                                sp += tok_len[x[u]];
+                            }
+                        }
                     }
                 }
             }
