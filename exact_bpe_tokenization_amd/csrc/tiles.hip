@@ -616,12 +616,19 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
     // four rounds in flight at once)
     const uint32_t *tok_len = v.tok_len;
     for (uint32_t r4 = qb; r4 < qe; r4 += 256) {
-      uint32_t pv4[4], a4[4];
+      uint32_t pv4[4], a4[4], x01[4][2];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
           const uint32_t p = r4 + 64u * u + lane;
           pv4[u] = p < qe ? pval[p] : 0u;
           a4[u] = p < qe ? pstart[p] : 0u;
+      }
+      // the first two IDs of the multi-token pieces of the four rounds, loaded together
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+          const bool mul = (pv4[u] & PV_MULTI) && !(pv4[u] & PV_LONG);
+          x01[u][0] = mul ? scratch[a4[u]] : 0u;
+          x01[u][1] = mul ? scratch[a4[u] + 1] : 0u;   // (a multi-token piece has at least two)
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -640,19 +647,20 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
                 out_ids[o] = pv;
                 if (SPANS) out_spans[o] = a;
             } else if (!(pv & PV_LONG)) {
-                // the piece's IDs from scratch, eight loads in flight
+                // the piece's IDs from scratch (the first two loaded above), eight loads in flight
                 uint32_t sp = a;
                 for (uint32_t t0 = 0; t0 < c; t0 += 8) {
                     uint32_t x[8];
 #pragma unroll
-                    for (uint32_t u = 0; u < 8; ++u) x[u] = t0 + u < c ? scratch[a + t0 + u] : 0u;
+                    for (uint32_t w8 = 0; w8 < 8; ++w8)
+                        x[w8] = (t0 == 0 && w8 < 2) ? x01[u][w8] : (t0 + w8 < c ? scratch[a + t0 + w8] : 0u);
 #pragma unroll
-                    for (uint32_t u = 0; u < 8; ++u) {
-                        if (t0 + u < c) {
-                            out_ids[o + t0 + u] = x[u];
+                    for (uint32_t w8 = 0; w8 < 8; ++w8) {
+                        if (t0 + w8 < c) {
+                            out_ids[o + t0 + w8] = x[w8];
                             if (SPANS) {
-                                out_spans[o + t0 + u] = sp;
-                                sp += tok_len[x[u]];
+                                out_spans[o + t0 + w8] = sp;
+                                sp += tok_len[x[w8]];
                             }
                         }
                     }
