@@ -32,7 +32,7 @@ EXPORTS = ("toktier_load_vocab", "toktier_load_vocab_ex", "toktier_free_vocab", 
            "toktier_unicode_table_sha256")
 
 # kernel launches of one encode call, in stream order (TOKTIER_K_* in toktier.h)
-KERNELS = ("summary", "pieces", "giant_seams", "tiles", "bpe", "bpe_giant", "emit")
+KERNELS = ("summary", "pieces", "tiles", "giant_seams", "bpe", "bpe_giant", "emit")
 
 
 class RepairInfo(ctypes.Structure):

@@ -634,6 +634,16 @@ __device__ __forceinline__ uint32_t *route_count(Ctrl *ctrl, uint32_t r)
     return r < NMISS ? &ctrl->miss_count[r] : &ctrl->bin_count[r - NMISS];
 }
 
+constexpr uint32_t NO_START = 0xFFFFFFFFu;   // a tile without piece starts
+
+// a piece longer than SHORT_MAX bytes goes on the list of its length bin (encoded before the tile
+// encoder, which only collects its result)
+__device__ __forceinline__ void list_long(uint8_t *ws, const Layout &L, Ctrl *ctrl, uint32_t p, uint32_t len)
+{
+    const uint32_t r = route_of(len);
+    route_list(ws, L, r)[atomicAdd(route_count(ctrl, r), 1u)] = p;
+}
+
 // Called by every thread of a workgroup when it has written its results: true in the workgroup that
 // finishes last, which then sees every other workgroup's writes (each thread's writes are fenced at
 // agent scope before the count; the last workgroup's threads fence again before their loads).
@@ -686,7 +696,7 @@ struct Batch {
 };
 
 // launch indices of the encode chain (TOKTIER_K_* in toktier.h)
-enum : int { TK_SUMMARY = 0, TK_PIECES = 1, TK_GIANT_SEAMS = 2, TK_TILES = 3, TK_BPE = 4, TK_BPE_GIANT = 5, TK_EMIT = 6,
+enum : int { TK_SUMMARY = 0, TK_PIECES = 1, TK_TILES = 2, TK_GIANT_SEAMS = 3, TK_BPE = 4, TK_BPE_GIANT = 5, TK_EMIT = 6,
              TK_COUNT = 7 };
 
 // optional events recorded around each kernel launch (indices: TOKTIER_K_* in toktier.h)
@@ -774,7 +784,7 @@ hipError_t launch_literal_docs(const Batch &b, const AddLayout &A, uint32_t n_li
 hipError_t launch_literal_merge(const DevAdded &a, const Batch &b, const AddLayout &A, uint32_t n_lit,
                                 uint32_t *out_ids, uint64_t *out_offsets, uint32_t *out_spans, hipStream_t s);
 
-hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
+hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev, bool compact);
 // pieces longer than BLOCK_MAX: merge-safe seams and chunks (before the tile encoder lists its pieces)
 hipError_t launch_giant_prep(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev);
 // BPE of every listed piece and chunk, by length: the short lists, then wavefront, workgroup and

@@ -546,15 +546,6 @@ __device__ __forceinline__ uint32_t reg_byte_code(const uint32_t (&rw)[6], uint3
 // ---------------------------------------------------------------------------------------------
 // k_pieces: dynamic tile ids; decode, automaton context, scans, look-backs, piece starts
 
-constexpr uint32_t NO_START = 0xFFFFFFFFu;   // a tile without piece starts
-
-// a piece longer than SHORT_MAX bytes goes on the list of its length bin (encoded before the tile
-// encoder, which only collects its result)
-__device__ __forceinline__ void list_long(uint8_t *ws, const Layout &L, Ctrl *ctrl, uint32_t p, uint32_t len)
-{
-    const uint32_t r = route_of(len);
-    route_list(ws, L, r)[atomicAdd(route_count(ctrl, r), 1u)] = p;
-}
 
 // A backward flag of all 16 characters of a chunk at once.  Bit k of D: character k decides the
 // flag (bit k of T: its value); other positions pass on the value of the position after them, and
@@ -1023,6 +1014,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
 // of the batch.
 __global__ __launch_bounds__(256) void k_compact(uint8_t *ws, Layout L, uint64_t n)
 {
+    __shared__ __align__(16) uint16_t sps[TILE];
     __shared__ uint32_t s_base, s_next;
     uint32_t n_docs = 0;
     const uint32_t n_tiles = request_sizes(L, n, n_docs);
@@ -1032,6 +1024,25 @@ __global__ __launch_bounds__(256) void k_compact(uint8_t *ws, Layout L, uint64_t
     const uint32_t *tcnt = (const uint32_t *)(ws + L.tcnt), *tfirst = (const uint32_t *)(ws + L.tfirst);
     const uint32_t *gsum = (const uint32_t *)(ws + L.gsum);
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
+    const uint32_t cnt = tcnt[tile], lo = tile * (uint32_t)TILE;
+    // every load at once: the tile's start offsets (16 bytes per load, into LDS; the last vector may
+    // run past the count, inside the tile's part of the array), the pieces before the tile (wave 0)
+    // and the first start after it (wave 1)
+    {
+        const uint4 *src = (const uint4 *)((const uint16_t *)(ws + L.prs) + lo);
+        const uint32_t nv = (cnt + 7u) / 8u;   // <= TILE / 8 = 4 per thread
+        uint4 x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t v = tid + 256u * k;
+            if (v < nv) x[k] = src[v];
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t v = tid + 256u * k;
+            if (v < nv) ((uint4 *)sps)[v] = x[k];
+        }
+    }
     if (wid == 0) {
         const uint32_t g = tile / 64u;
         uint32_t x = 0;
@@ -1053,11 +1064,10 @@ __global__ __launch_bounds__(256) void k_compact(uint8_t *ws, Layout L, uint64_t
         if (lane == 0) s_next = nx;
     }
     __syncthreads();
-    const uint32_t base = s_base, next = s_next, cnt = tcnt[tile], lo = tile * (uint32_t)TILE;
-    const uint16_t *prs = (const uint16_t *)(ws + L.prs) + lo;
+    const uint32_t base = s_base, next = s_next;
     uint32_t *pstart = (uint32_t *)(ws + L.pstart);
     for (uint32_t i = tid; i < cnt; i += 256u) {
-        const uint32_t a = lo + prs[i], e = i + 1 < cnt ? lo + prs[i + 1] : next;
+        const uint32_t a = lo + sps[i], e = i + 1 < cnt ? lo + sps[i + 1] : next;
         pstart[base + i] = a;
         if (e - a > (uint32_t)SHORT_MAX) list_long(ws, L, ctrl, base + i, e - a);
     }
@@ -1073,7 +1083,7 @@ __global__ __launch_bounds__(256) void k_compact(uint8_t *ws, Layout L, uint64_t
 
 // ---------------------------------------------------------------------------------------------
 
-hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev)
+hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, const Events *ev, bool compact)
 {
     const Layout &L = b.L;
     {
@@ -1094,7 +1104,7 @@ hipError_t launch_pretokenize(const DevVocab &v, const Batch &b, hipStream_t s, 
         else
             hipLaunchKernelGGL(k_pieces<VAR_PLAIN>, grid, dim3(PRE_THREADS), 0, s, v, b.bytes, b.offsets, b.n_docs,
                                b.n, b.ws, L);
-        hipLaunchKernelGGL(k_compact, grid, dim3(256), 0, s, b.ws, L, b.n);
+        if (compact) hipLaunchKernelGGL(k_compact, grid, dim3(256), 0, s, b.ws, L, b.n);
     }
     return hipGetLastError();
 }

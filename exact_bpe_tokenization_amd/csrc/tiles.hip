@@ -37,6 +37,7 @@ struct ResolveSmem {
     uint32_t wsum[NW];
     uint32_t qn, ln;                  // pieces listed for BPE / for the 8..32-byte table
     uint32_t rn[NMISS], rb[NMISS];    // per BPE list: this tile's items, their first list slot
+    uint32_t base, next;              // pieces before the tile; the first piece start after it
 };
 
 struct EmitSmem {
@@ -332,7 +333,7 @@ __device__ __forceinline__ uint64_t short_key(const S &sm, uint32_t j, uint32_t 
 //   33..128 bytes   (and table misses) listed in the tile's slice of the BPE list
 //   longer          encoded before this kernel: its result word is read
 template <bool IGN>
-__global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restrict__ bytes, uint64_t n, uint8_t *ws,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_tiles(DevVocab v, const uint8_t *__restrict__ bytes, uint64_t n, uint8_t *ws,
                                               Layout L)
 {
     __shared__ ResolveSmem sm;
@@ -340,16 +341,45 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
         uint32_t nd = 0;
         if (blockIdx.x >= request_sizes(L, n, nd)) return;   // (a request smaller than the plan's size bucket)
     }
-    const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
-    const uint32_t *__restrict__ tbase = (const uint32_t *)(ws + L.tbase);
+    uint32_t *__restrict__ pstart = (uint32_t *)(ws + L.pstart);
     uint32_t *pval = (uint32_t *)(ws + L.pval);
     uint32_t *scratch = (uint32_t *)(ws + L.scratch);
-    const uint32_t tid = threadIdx.x;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
     const uint32_t tile = blockIdx.x;
     const uint64_t lo = (uint64_t)tile * TILE;
-    const uint32_t p0 = tbase[tile], p1 = tbase[tile + 1], cnt = p1 - p0;
     Ctrl *ctrl = (Ctrl *)(ws + L.ctrl);
-    uint32_t *llist = (uint32_t *)(ws + L.tokoff) + p0;   // the 8..32-byte pieces
+    // the tile's piece starts, as the pieces kernel left them: a count and 16-bit offsets at the
+    // tile's own place; this kernel gives them their global places (pieces before the tile: the
+    // 64-tile group sums before its group, then the tiles of its group before it)
+    const uint32_t *tcnt = (const uint32_t *)(ws + L.tcnt);
+    const uint16_t *prs = (const uint16_t *)(ws + L.prs) + lo;
+    const uint32_t cnt = tcnt[tile];
+    if (wid == 0) {
+        const uint32_t *gsum = (const uint32_t *)(ws + L.gsum);
+        const uint32_t g = tile / 64u;
+        uint32_t x = 0;
+        for (uint32_t k = lane; k < g; k += 64u) x += gsum[k];
+        if (64u * g + lane < tile) x += tcnt[64u * g + lane];
+        x = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(x), 63);
+        if (lane == 0) sm.base = x;
+    } else if (wid == 1) {
+        // the first start after the tile (the end of its last piece), else the end of the batch
+        const uint32_t *tfirst = (const uint32_t *)(ws + L.tfirst);
+        uint32_t nd = 0;
+        uint64_t nn = n;
+        const uint32_t n_tiles = request_sizes(L, nn, nd);
+        uint32_t nx = (uint32_t)nn;
+        for (uint32_t t0 = tile + 1; t0 < n_tiles; t0 += 64u) {
+            const uint32_t t = t0 + lane;
+            const uint32_t f = t < n_tiles ? tfirst[t] : NO_START;
+            const uint64_t has = __ballot(f != NO_START);
+            if (has) {
+                nx = (uint32_t)__builtin_amdgcn_readlane((int)f, __ffsll((unsigned long long)has) - 1);
+                break;
+            }
+        }
+        if (lane == 0) sm.next = nx;
+    }
 
     // the window and the hot sets (their loads issued together)
     {
@@ -366,6 +396,19 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
         sm.ln = 0;
     }
     __syncthreads();
+    const uint32_t p0 = sm.base, next = sm.next;
+    if (tid == 0) {
+        ((uint32_t *)(ws + L.tbase))[tile] = p0;
+        uint32_t nd = 0;
+        uint64_t nn = n;
+        const uint32_t n_tiles = request_sizes(L, nn, nd);
+        if (tile == n_tiles - 1) {   // the last tile: the piece count, the batch end, the tile bases' end
+            ctrl->n_pieces = p0 + cnt;
+            pstart[p0 + cnt] = (uint32_t)nn;
+            ((uint32_t *)(ws + L.tbase))[n_tiles] = p0 + cnt;
+        }
+    }
+    uint32_t *llist = (uint32_t *)(ws + L.tokoff) + p0;   // the 8..32-byte pieces
     // a piece left for BPE: queued (index in the tile | length << 16) in LDS, past its capacity in
     // the tile's own slice of a device array; at the end the queue goes to the BPE lists in one run
     // per list
@@ -383,8 +426,13 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             const uint32_t i = i0 + u * NT + tid;
-            a[u] = i < cnt ? pstart[p0 + i] : 0u;
-            e[u] = i < cnt ? pstart[p0 + i + 1] : 0u;
+            a[u] = i < cnt ? (uint32_t)lo + prs[i] : 0u;
+            e[u] = i + 1 < cnt ? (uint32_t)lo + prs[i + 1] : next;
+        }
+#pragma unroll
+        for (int u = 0; u < K; ++u) {   // the global piece starts, for the kernels after this one
+            const uint32_t i = i0 + u * NT + tid;
+            if (i < cnt) pstart[p0 + i] = a[u];
         }
         // kind: 0 nothing to load, 2 byte pair, 3 short table (both candidate slots).  Each piece's
         // result word is written once, in one coalesced store per row of the step (the pieces resolved
@@ -433,7 +481,9 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
                 } else {
                     list_miss(i, len);
                 }
-            }   // longer pieces are listed by the pieces kernel and counted by the BPE kernels
+            } else {   // longer pieces: listed by length for the workgroup and giant units
+                list_long(ws, L, ctrl, p0 + i, len);
+            }
         }
         // the global lookups of the pieces the hot sets did not answer: all loads in flight at once
         uint4 x[K], y[K];
@@ -480,7 +530,7 @@ __global__ __launch_bounds__(NT) void k_tiles(DevVocab v, const uint8_t *__restr
     const uint32_t nl = sm.ln;
     for (uint32_t k = tid; k < nl; k += NT) {
         const uint32_t ent = llist[k];
-        const uint32_t i = ent & 0xFFFFu, len = ent >> 16, j = pstart[p0 + i] - (uint32_t)lo;
+        const uint32_t i = ent & 0xFFFFu, len = ent >> 16, j = prs[i];
         uint64_t k4[4];
         win_words<4>(sm, j, len, k4);
         bool hit = false;

@@ -949,9 +949,9 @@ namespace {
 hipError_t launch_chain(const DevVocab &v, const Batch &b, uint32_t *out_ids, uint64_t *out_offsets,
                         uint32_t *out_spans, hipStream_t s, const Events *ev)
 {
-    hipError_t e = launch_pretokenize(v, b, s, ev);
-    if (e == hipSuccess) e = launch_giant_prep(v, b, s, ev);
+    hipError_t e = launch_pretokenize(v, b, s, ev, false);   // (the tile encoder places the starts)
     if (e == hipSuccess) e = launch_tiles(v, b, s, ev);
+    if (e == hipSuccess) e = launch_giant_prep(v, b, s, ev);
     if (e == hipSuccess) e = launch_bpe(v, b, s, ev);
     if (e == hipSuccess) e = launch_emit(v, b, out_ids, out_offsets, out_spans, s, ev);
     return e;
@@ -1193,7 +1193,7 @@ extern "C" int toktier_pretokenize_batch(const toktier_vocab *v, const uint8_t *
     if (!out_piece_starts || !out_n_pieces) return TOKTIER_E_INVALID_ARG;
     if (starts_capacity < total_bytes + 1) return TOKTIER_E_CAPACITY;
     hipStream_t s = (hipStream_t)stream;
-    HIP_TRY(launch_pretokenize(v->dv, b, s, nullptr));
+    HIP_TRY(launch_pretokenize(v->dv, b, s, nullptr, true));
     HIP_TRY(launch_export_starts(b, out_piece_starts, s));
     Ctrl c;
     rc = read_ctrl(workspace, s, &c);

@@ -246,12 +246,10 @@ int toktier_last_status(void *workspace, void *stream, uint64_t *out_n_tokens);
 enum {
     TOKTIER_K_SUMMARY = 0,    /* clear the control block and look-back flags; per tile: the        */
                               /* characters that decide the backward flags, the documents near it  */
-    TOKTIER_K_PIECES,         /* UTF-8 decode + validation, automaton scan, piece starts per tile;  */
-                              /* then their global places, pieces longer than 128 bytes listed by   */
-                              /* length (two launches)                                              */
+    TOKTIER_K_PIECES,         /* UTF-8 decode + validation, automaton scan, piece starts per tile   */
+    TOKTIER_K_TILES,          /* per 8 KiB tile: the starts' global places; single bytes and        */
+                              /* whole-piece table lookups; the other pieces listed by length       */
     TOKTIER_K_GIANT_SEAMS,    /* pieces > 4096 bytes: seams no merge crosses, then chunks           */
-    TOKTIER_K_TILES,          /* per 8 KiB tile: single bytes and whole-piece table lookups; the    */
-                              /* other pieces of <= 128 bytes listed by length for BPE              */
     TOKTIER_K_BPE,            /* BPE of the listed pieces and chunks of <= 4096 bytes: lane per     */
                               /* piece (<= 32), a wavefront (<= 64), two elements per lane (<= 128),*/
                               /* a workgroup per piece (<= 4096)                                    */
