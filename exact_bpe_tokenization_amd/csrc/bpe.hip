@@ -7,20 +7,21 @@
 // that pair equals iterated single merges (for rank-consistent merge lists, which the loader
 // enforces); only pairs next to a completed merge need a new lookup.
 //
-//   k_route      (vocabulary load) every piece: a single byte is its ID, a whole-piece table hit
-//                is its result; the others are listed by length (the tile encoder does the same for
-//                the encode chain)
-//   k_bpe_small  the lists of pieces up to 128 bytes, one launch with a workgroup range per list:
-//                <= 8, 9..12, 13..16 and 17..32 bytes, one lane per piece and 64 consecutive list
-//                items per wavefront, the textbook loop over an LDS row per lane (leftmost lowest rank,
-//                merge, re-probe the two neighbours); 33..64 bytes, 64 lanes per piece; 65..128
-//                bytes, a wavefront with two elements per lane: rounds on ballot masks (see the
-//                kernels)
-//   k_bpe_block  one wavefront (pieces of 129..1024 bytes) or one 256-lane workgroup (up to 4096
-//                bytes) per piece; sequence in LDS; rounds: block-min of ranks, selection of the
-//                leftmost non-overlapping occurrences, prefix-sum compaction, neighbour re-probes
-//   k_bpe_giant  one 1024-lane workgroup per piece longer than that; the same rounds over device
-//                memory (double-buffered)
+//   k_route       (vocabulary load) every piece: a single byte is its ID, a whole-piece table hit
+//                 is its result; the others are listed by length (the tile encoder does the same for
+//                 the encode chain)
+//   k_giant_prep  pieces longer than 4096 bytes: every position tested for a seam no merge crosses,
+//                 then (the last workgroup done with a piece) the piece cut into chunks at such seams
+//   k_bpe_small   every list up to 4096 bytes, one launch with a workgroup range per list: <= 8,
+//                 9..12, 13..16 and 17..32 bytes, one lane per piece and 64 consecutive list items
+//                 per wavefront, the textbook loop over an LDS row per lane (leftmost lowest rank,
+//                 merge, re-probe the two neighbours); 33..64 bytes, 64 lanes per piece; 65..128
+//                 bytes, a wavefront with two elements per lane: rounds on ballot masks; 129..1024
+//                 bytes, a wavefront per piece (four per workgroup), 1025..4096 bytes, a workgroup per
+//                 piece: sequence in LDS, rounds of block minimum, selection of the leftmost
+//                 non-overlapping occurrences, prefix-sum compaction, neighbour re-probes
+//   k_bpe_giant   one 1024-lane workgroup per chunk longer than that; the same rounds over device
+//                 memory (double-buffered); the last workgroup joins each giant piece's chunks
 // Every kernel writes the piece's result word (a single ID, or the count of IDs it stored at
 // scratch[piece start byte ...]; a piece never has more IDs than bytes) and adds its token count to
 // the counters of its input tile (tcount) and of that tile's group of 64 tiles (tsb).

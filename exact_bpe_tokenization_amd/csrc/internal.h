@@ -625,7 +625,10 @@ __device__ __forceinline__ uint32_t route_of(uint32_t len)
 
 __device__ __forceinline__ uint32_t *route_list(uint8_t *ws, const Layout &L, uint32_t r)
 {
-    const uint64_t o = r < NMISS ? L.miss[r] : r == 6 ? L.bin_wave : r == 7 ? L.bin_block : L.bin_giant;
+    // (selects, not an index into the layout's array: an indexed kernel argument is copied to
+    // private memory)
+    const uint64_t o = r == 0 ? L.miss[0] : r == 1 ? L.miss[1] : r == 2 ? L.miss[2] : r == 3 ? L.miss[3] :
+                       r == 4 ? L.miss[4] : r == 5 ? L.miss[5] : r == 6 ? L.bin_wave : r == 7 ? L.bin_block : L.bin_giant;
     return (uint32_t *)(ws + o);
 }
 

@@ -14,11 +14,14 @@
 // carry comes from a summary of the tiles after it.
 //
 // Kernels:  k_summary  per tile: the leftmost character that decides each backward flag (an
-//                      early-exit scan of the tile's first bytes; one wavefront per tile); also
-//                      clears the control block, the look-back flags and the tile token counters
+//                      early-exit scan of the tile's first bytes), and the automaton state its last
+//                      60 bytes fix for the next tile (a second wavefront); also clears the control
+//                      block, the look-back flags and the tile counters
 //           k_pieces   per 8 KiB tile: UTF-8 decode + validation, categories, backward flags,
-//                      automaton scan, piece starts, piece numbering (one read of the input,
-//                      4 bytes written per piece)
+//                      automaton scan, piece starts (one read of the input; per tile a count, its
+//                      first start and 2 bytes per piece written at the tile's own place)
+//           k_compact  (piece-start export only; the encode chain's tile encoder does the same) the
+//                      starts at their global places, long pieces listed by length
 #include "internal.h"
 
 #define TT_UCAT_QUAL static __device__ const
@@ -1031,16 +1034,10 @@ __global__ __launch_bounds__(256) void k_compact(uint8_t *ws, Layout L, uint64_t
     {
         const uint4 *src = (const uint4 *)((const uint16_t *)(ws + L.prs) + lo);
         const uint32_t nv = (cnt + 7u) / 8u;   // <= TILE / 8 = 4 per thread
-        uint4 x[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const uint32_t v = tid + 256u * k;
-            if (v < nv) x[k] = src[v];
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t v = tid + 256u * k;
-            if (v < nv) ((uint4 *)sps)[v] = x[k];
+            if (v < nv) ((uint4 *)sps)[v] = src[v];
         }
     }
     if (wid == 0) {

@@ -5,19 +5,23 @@
 // whole vocabulary entries looked up in device hash tables; GPU full-tokenization paragraph: the
 // path ends with output compaction, and counts stay on the device.
 //
-//   k_tiles  per 8 KiB input tile, the pieces that start in it: the tile's bytes and the 128 after
-//            it are staged in LDS (a piece of up to SHORT_MAX bytes that starts in the tile lies in
-//            that window); one byte is its own ID; 2..32 bytes are looked up in the whole-piece
-//            tables (key built from LDS, the lowest token IDs in LDS, the others with four pieces
-//            per thread in flight); pieces longer than SHORT_MAX were listed by the pieces kernel;
-//            the others are queued in LDS and appended to the BPE lists by length, one run per list
-//            and tile.  The tile's token count so far goes to its counter and to the counter of its
-//            group of 64 tiles (the BPE kernels add the tokens of the pieces they encode).
+//   k_tiles  per 8 KiB input tile, the pieces that start in it: their global numbers (pieces before
+//            the tile from the 64-tile group sums and the tile counts the pieces kernel left) and
+//            global starts (from the tile's 16-bit offsets; the last piece ends at the next tile's
+//            first start); the tile's bytes and the 128 after it are staged in LDS (a piece of up to
+//            SHORT_MAX bytes that starts in the tile lies in that window); one byte is its own ID;
+//            2..32 bytes are looked up in the whole-piece tables (key built from LDS, the lowest
+//            token IDs in LDS, the others with four pieces per thread in flight); longer pieces are
+//            listed by length for the workgroup and giant units; the others are queued in LDS and
+//            appended to the BPE lists by length, one run per list and tile.  The tile's token count
+//            so far goes to its counter and to the counter of its group of 64 tiles (the BPE
+//            kernels add the tokens of the pieces they encode).
 //   k_emit   per tile: its first output index from the counters (the groups before its own, then
-//            the tiles before it in its group); rounds of 256 pieces, a workgroup scan of their
-//            token counts places their IDs (consecutive pieces write consecutive IDs); per-document
-//            token offsets; optional token spans.  Up to 32 more workgroups copy the IDs of the giant
-//            pieces chunk by chunk, a thread per chunk.  No workgroup waits for another.
+//            the tiles before it in its group); per wavefront, groups of four rounds of 64 pieces
+//            (their results, starts and the first two IDs of the multi-token ones loaded together),
+//            a wavefront scan of each round's token counts places its IDs (consecutive pieces write
+//            consecutive IDs); per-document token offsets; optional token spans.  Up to 32 more
+//            workgroups copy the IDs of the giant pieces.  No workgroup waits for another.
 #include "internal.h"
 
 namespace tt {
