@@ -299,13 +299,19 @@ def main():
             if hashlib.sha256(src).hexdigest() == rec["source_sha256"]:
                 valu = rec["SQ_INSTS_VALU"]
     own_gbs = own[dominant] / (kms[dominant] * 1e-3) / 1e9
-    if valu is not None:
+    # the bound the counters point at: VALU issue against its peak, or the measured HBM traffic
+    # against 8 TB/s, whichever the kernel uses more of (without counters for this source: HBM)
+    valu_frac = valu / (kms[dominant] * 1e-3) / 1e9 / VALU_PEAK if valu is not None else None
+    traffic_frac = traffic / (kms[dominant] * 1e-3) / 1e9 / HBM_PEAK_GBS if traffic is not None else None
+    if valu_frac is not None and (traffic_frac is None or valu_frac >= traffic_frac):
         achieved = valu / (kms[dominant] * 1e-3) / 1e9
         roofline = {"bound": "alu", "achieved": round(achieved, 3), "peak": VALU_PEAK,
                     "unit": "G VALU wavefront instructions/s", "frac": round(achieved / VALU_PEAK, 5)}
-    else:   # no counters for this source: the kernel's own bytes against HBM
+    else:   # the kernel's own algorithmic bytes against HBM
         roofline = {"bound": "hbm", "achieved": round(own_gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(own_gbs / HBM_PEAK_GBS, 6)}
+    roofline["valu_issue_frac"] = round(valu_frac, 5) if valu_frac is not None else None
+    roofline["traffic_hbm_frac"] = round(traffic_frac, 5) if traffic_frac is not None else None
     roofline.update({"traffic": traffic, "kernel": dominant, "kernel_ms": round(kms[dominant], 5),
                      "valu_insts_per_launch": valu, "own_alg_bytes_per_launch": int(own[dominant]),
                      "own_hbm_gbs": round(own_gbs, 3), "own_hbm_frac": round(own_gbs / HBM_PEAK_GBS, 6),
