@@ -337,7 +337,7 @@ __device__ __forceinline__ uint64_t short_key(const S &sm, uint32_t j, uint32_t 
 //   33..128 bytes   (and table misses) listed in the tile's slice of the BPE list
 //   longer          encoded before this kernel: its result word is read
 template <bool IGN>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5, 8))) void k_tiles(DevVocab v, const uint8_t *__restrict__ bytes, uint64_t n, uint8_t *ws,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5, 8))) void k_tiles(DevVocab v, const uint8_t *__restrict__ bytes, uint64_t n, uint8_t *ws,
                                               Layout L)
 {
     __shared__ ResolveSmem sm;
@@ -425,14 +425,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5, 8))) void
 
     uint32_t mytok = 0;
     constexpr int K = 4;
+    // a step's start offsets (this piece's and the next one's, 16 bits each) are loaded during the
+    // step before, while that step's table reads are in flight
+    auto load_offsets = [&](uint32_t i0, uint32_t (&pk)[K]) {
+#pragma unroll
+        for (int u = 0; u < K; ++u) {
+            const uint32_t i = i0 + u * NT + tid;
+            pk[u] = (i < cnt ? (uint32_t)prs[i] : 0u) | ((i + 1 < cnt ? (uint32_t)prs[i + 1] : 0u) << 16);
+        }
+    };
+    uint32_t pk_next[K];
+    load_offsets(0, pk_next);
     for (uint32_t i0 = 0; i0 < cnt; i0 += K * NT) {
         uint32_t a[K], e[K];
 #pragma unroll
         for (int u = 0; u < K; ++u) {
-            const uint32_t i = i0 + u * NT + tid;
-            a[u] = i < cnt ? (uint32_t)lo + prs[i] : 0u;
-            e[u] = i + 1 < cnt ? (uint32_t)lo + prs[i + 1] : next;
+            const uint32_t i = i0 + u * NT + tid, pk = pk_next[u];
+            a[u] = i < cnt ? (uint32_t)lo + (pk & 0xFFFFu) : 0u;
+            e[u] = i + 1 < cnt ? (uint32_t)lo + (pk >> 16) : next;
         }
+        if (i0 + K * NT < cnt) load_offsets(i0 + K * NT, pk_next);
 #pragma unroll
         for (int u = 0; u < K; ++u) {   // the global piece starts, for the kernels after this one
             const uint32_t i = i0 + u * NT + tid;
