@@ -291,8 +291,7 @@ __device__ __forceinline__ M16 wave_scan16(M16 x)
 }
 
 template <typename DocBit>
-__device__ uint32_t window_states(const DevVocab &v, const uint4 *smap, const uint8_t *swin, DocBit docbit, uint64_t wb,
-                                  uint64_t n)
+__device__ uint32_t window_states(const DevVocab &v, const uint8_t *swin, DocBit docbit, uint64_t wb, uint64_t n)
 {
     const uint32_t lane = threadIdx.x & 63u;
     const bool DS = v.family == FAMILY_DEEPSEEK, CASE = v.family == FAMILY_O200K;
@@ -327,15 +326,20 @@ __device__ uint32_t window_states(const DevVocab &v, const uint4 *smap, const ui
     const uint32_t selfc = DS ? self_code_ds(code) : self_code(code, false);
     const uint32_t nextc = DS ? next_code_ds(nc) : ((nc & 7u) == CAT_CONT ? 5u : next_code(nc));
     const uint32_t base = win && isch ? (selfc * 2u + ((code & CC_DOC) ? 1u : 0u)) * NX * AUM + nextc * AUM : 0xFFFFu;
-    // one composition per flag value (the maps from the copy of the table in LDS; index NCTXV is
-    // the identity)
+    // one composition per flag value (the maps of all values loaded together; past NCTXV: identity)
     const uint32_t nvar = CASE ? 4u : 2u;
-    uint32_t res = 0;
-    for (uint32_t var = 0; var < nvar; ++var) {
+    uint4 t[4];
+#pragma unroll
+    for (uint32_t var = 0; var < 4; ++var) {
         const uint32_t na = xn ? (xn & 1u) : (var & 1u), aun = xa_next ? (xa_next & 1u) : ((var >> 1) & 1u);
         const uint32_t ctx = min(base + ((na && ws_ && !crlf) ? 2u * NX * AUM : 0u) + (CASE ? aun : 0u), NCTXV);
-        const uint4 t = smap[ctx];
-        const M16 x = wave_scan16(M16{{t.x, t.y, t.z, t.w}});
+        t[var] = (var < nvar && ctx < NCTXV) ? v.fmap16[ctx] : make_uint4(0x03020100u, 0x07060504u, 0x0B0A0908u, 0x0F0E0D0Cu);
+    }
+    uint32_t res = 0;
+#pragma unroll
+    for (uint32_t var = 0; var < 4; ++var) {
+        if (var >= nvar) break;
+        const M16 x = wave_scan16(M16{{t[var].x, t[var].y, t[var].z, t[var].w}});
         if (is_const16(x)) res |= (0x10u | (x.w[0] & 15u)) << (8u * var);
     }
     return (uint32_t)__builtin_amdgcn_readlane((int)res, 63);
@@ -346,7 +350,6 @@ __global__ __launch_bounds__(128) void k_summary(DevVocab v, const uint8_t *__re
                                                  uint64_t n, uint8_t *ws, Layout L)
 {
     __shared__ uint8_t swin[72];
-    __shared__ uint4 smap[NCTX_MAX + 1];
     bool bad_size = false;
     const uint32_t n_tiles = request_sizes(L, n, n_docs, &bad_size);
     const uint32_t lane = threadIdx.x & 63u, wid = threadIdx.x >> 6;
@@ -362,17 +365,14 @@ __global__ __launch_bounds__(128) void k_summary(DevVocab v, const uint8_t *__re
     if (blockIdx.x >= n_tiles) return;
     const uint64_t lo = (uint64_t)blockIdx.x * TILE;
     const uint64_t hi = min(lo + TILE, n);
-    // wavefront 1: the window at the tile's end, bytes [hi - 64, hi + 8), its document starts and a
-    // copy of the transition maps, then the states the window fixes (beside wavefront 0's scan)
+    // wavefront 1: the window at the tile's end, bytes [hi - 64, hi + 8) and its document starts,
+    // then the states the window fixes (beside wavefront 0's scan)
     if (wid == 1) {
         uint32_t wst = 0;
         if (blockIdx.x + 1 < n_tiles) {
             const uint64_t wb = hi - 64;
             const uint32_t wbyte0 = wb + lane < n ? bytes[wb + lane] : 0u;
             const uint32_t wbyte1 = lane < 8 && wb + 64 + lane < n ? bytes[wb + 64 + lane] : 0u;
-            const uint32_t nctx = v.family == FAMILY_DEEPSEEK ? (uint32_t)DS_NCTX : (uint32_t)NCTX;
-            for (uint32_t k = lane; k < nctx; k += 64u) smap[k] = v.fmap16[k];
-            if (lane == 0) smap[nctx] = make_uint4(0x03020100u, 0x07060504u, 0x0B0A0908u, 0x0F0E0D0Cu);
             swin[lane] = (uint8_t)wbyte0;
             if (lane < 8) swin[64 + lane] = (uint8_t)wbyte1;
             // document starts in the window: narrow [lo, hi) of offsets down to at most 128 entries
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(128) void k_summary(DevVocab v, const uint8_t *__re
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            wst = window_states(v, smap, swin, [&](int j) -> bool {
+            wst = window_states(v, swin, [&](int j) -> bool {
                 return (((j < 32 ? db0 : (j < 64 ? db1 : db2))) >> (j & 31)) & 1u;
             }, wb, n);
         }
@@ -423,12 +423,26 @@ __global__ __launch_bounds__(128) void k_summary(DevVocab v, const uint8_t *__re
     // wavefront 0: document starts in the pieces kernel's byte window of this tile, [lo - RAW_LEAD,
     // lo + TILE + RAW_TAIL): indices [d0, d1) of offsets (empty documents repeat one), kept for that
     // kernel; the window holds [lo, hi + 4), which the search below needs
-    const uint64_t lo_w = lo >= (uint64_t)RAW_LEAD ? lo - RAW_LEAD : 0;
+    // (d1 and the first two starts from the 64 offsets after d0, read in one step; more steps only
+    // for windows with more than 64 document starts)
+    const uint64_t lo_w = lo >= (uint64_t)RAW_LEAD ? lo - RAW_LEAD : 0, hi_w = lo + TILE + RAW_TAIL;
     const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, lo_w);
-    const uint32_t d1 = wave_lower_bound(offsets, n_docs + 1, lo + TILE + RAW_TAIL);
+    uint32_t d1 = d0, o0 = 0, o1 = 0;
+    for (uint32_t b = d0;; b += 64u) {
+        const uint32_t i = b + lane;
+        const uint64_t o = i <= n_docs ? offsets[i] : ~0ull;
+        if (b == d0) {
+            o0 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)o, 0);
+            o1 = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)o, 1);
+        }
+        const uint64_t past = __ballot(o >= hi_w);
+        if (past) {
+            d1 = b + (uint32_t)__ffsll((unsigned long long)past) - 1u;
+            break;
+        }
+    }
     if (lane == 0) {   // and the first two of those starts, so that the pieces kernel seldom reads offsets
-        const uint32_t o0 = d0 < d1 ? (uint32_t)offsets[d0] : 0u, o1 = d0 + 1 < d1 ? (uint32_t)offsets[d0 + 1] : 0u;
-        ((uint4 *)(ws + L.tdoc))[blockIdx.x] = make_uint4(d0, d1, o0, o1);
+        ((uint4 *)(ws + L.tdoc))[blockIdx.x] = make_uint4(d0, d1, d0 < d1 ? o0 : 0u, d0 + 1 < d1 ? o1 : 0u);
     }
     uint32_t na = BK_KEEP, au = BK_KEEP;
     // 64 T bytes per step, T per lane: the first step 256 bytes (where a flag is usually decided),
