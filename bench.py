@@ -23,6 +23,11 @@ Prints ONE JSON line:
                profiles/ show it ("alu": VALU issue, against 614.4 G wavefront instructions/s), the
                committed per-launch counts over the live duration; its own algorithmic bytes and
                their fraction of 8 TB/s beside; kernels: every kernel's duration and own bytes
+  repair_ms    incremental repair (toktier_repair_append, records repaired in place): wall-clock ms per
+               append, host text in and host records out, on one agent session of 100K / 1M / 4.4M
+               characters with 1,400-character appends, and on the 1M session with 1K / 10K / 100K
+               appends; the first append apart, p50 / p90 over the next 24; each session's records
+               are checked against a fresh GPU encode of its whole text
   cpu_baseline the CPU oracle (serial pre-tokenizer + priority-queue BPE, one document per worker
                process) timed on this host's available cores over a bounded sample of the same batch,
                and single-core on each single-request configuration; the same run checks the GPU
@@ -48,6 +53,13 @@ METRIC = "full-tokenize scanned GB/s (batched) + p50 ms per 1M-char request, bit
 HBM_PEAK_GBS = 8000.0
 MAIN = "c4_batch64"
 LATENCY = ("c1_ec4k", "c2_at100k", "c3_mix1m", "c5_adv4m4")
+
+# incremental repair: appends to one agent session (a single 4.4M-character transcript stream; A is
+# its first N characters, each append the next slice), host bytes in, host records out
+REPAIR_CONTEXTS = (100_000, 1_000_000, 4_400_000)   # characters of A
+REPAIR_APPEND = 1_400                                # the median append of the interactive traces
+REPAIR_SWEEP = (1_000, 10_000, 100_000)              # append sizes on the 1M-character session
+REPAIR_SAMPLES = 24                                  # steady-state appends per shape, after a first one
 
 VALU_PEAK = 256 * 4 * 2.4e9 / 4 / 1e9   # G wavefront instructions/s: 256 CUs x 4 SIMDs, 4 cycles per wave64 op
 
@@ -139,6 +151,41 @@ def oracle_latency(fam, voc, data, offs, reps=5):
         oracle.encode_batch(fam, m, data, offs)
         ts.append((time.perf_counter() - t0) * 1e3)
     return statistics.median(ts)
+
+
+def repair_latency(tt):
+    """Wall-clock latency of toktier_repair_append through RepairSession (records repaired in place),
+    per (context, append) shape: the first append apart, then REPAIR_SAMPLES appends; the session's
+    records are then checked against a fresh GPU encode of its whole text."""
+    fam, voc, _ = textgen.WORKLOADS["c2_at100k"]
+    merges, ff = textgen.load_vocab(voc)
+    tok = tt.Tokenizer(merges, ff, device="cuda:0")
+    need = max(max(REPAIR_CONTEXTS) + (REPAIR_SAMPLES + 1) * REPAIR_APPEND,
+               1_000_000 + (REPAIR_SAMPLES + 1) * max(REPAIR_SWEEP))
+    raw = textgen.agent_transcript(9, need).encode()   # ASCII: characters = bytes
+    res = {}
+    shapes = [(n, REPAIR_APPEND) for n in REPAIR_CONTEXTS] + [(1_000_000, d) for d in REPAIR_SWEEP
+                                                             if d != REPAIR_APPEND]
+    for n_a, delta in shapes:
+        sess = tt.RepairSession(tok, raw[:n_a])
+        ts, spliced, attempts = [], 0, 0
+        for k in range(REPAIR_SAMPLES + 1):
+            b = raw[n_a + k * delta: n_a + (k + 1) * delta]
+            t0 = time.perf_counter()
+            info = sess.append(b)
+            ts.append((time.perf_counter() - t0) * 1e3)
+            spliced += info["spliced"]
+            attempts += info["attempts"]
+        end = n_a + (REPAIR_SAMPLES + 1) * delta
+        ids, _, spans = tok.encode(raw[:end], spans=True)
+        first, st = ts[0], sorted(ts[1:])
+        res[f"ctx{n_a}_add{delta}"] = {
+            "context_chars": n_a, "append_chars": delta, "first_ms": round(first, 4),
+            "p50": round(statistics.median(st), 4), "p90": round(st[int(0.9 * (len(st) - 1))], 4),
+            "samples": len(st), "spliced": spliced, "windows_encoded": attempts,
+            "same_as_full_encode": bool(np.array_equal(sess.ids, ids) and np.array_equal(sess.spans, spans))}
+        _log("repair", n_a, delta, res[f"ctx{n_a}_add{delta}"])
+    return res
 
 
 # ---------------------------------------------------------------------------------------------
@@ -384,6 +431,9 @@ def main():
         latency[name]["graph_p50"] = round(statistics.median(gs), 4)
         latency[name]["graph_p90"] = round(gs[int(0.9 * (len(gs) - 1))], 4)
 
+    # ---- incremental repair of appends to one session ----
+    repair = None if args.no_latency else repair_latency(tt)
+
     if args.calibrate_copy_mib:
         src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -409,6 +459,7 @@ def main():
         "kernel_ms": {k: round(v, 5) for k, v in kms.items()},
         "kernels": kernels,
         "kernel_ms_c3_mix1m": kms_c3,
+        "repair_ms": repair,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "bit_exact": exact if exact else None,

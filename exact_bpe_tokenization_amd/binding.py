@@ -341,24 +341,87 @@ def toktier_repair_scratch_bytes(vocab, total_bytes):
 def toktier_repair_append(vocab, text, len_a, cached_ids, cached_spans, scratch, stream=None):
     """Incremental repair of an append: text = A || B (host bytes), len_a = bytes of A, cached records
     of A (uint32 arrays).  Returns (ids uint32[T], spans uint32[T], info dict) for A || B."""
-    raw = bytes(text)
+    tb = np.frombuffer(bytes(text), dtype=np.uint8)
     ci = np.ascontiguousarray(cached_ids, dtype=np.uint32)
     cs = np.ascontiguousarray(cached_spans, dtype=np.uint32)
-    cap = max(len(raw), 1)
-    out_ids = np.zeros(cap, dtype=np.uint32)
-    out_spans = np.zeros(cap, dtype=np.uint32)
+    cap = max(tb.size, 1)
+    out_ids = np.empty(cap, dtype=np.uint32)
+    out_spans = np.empty(cap, dtype=np.uint32)
+    k, info = _repair(vocab, tb, len_a, ci, cs, ci.size, out_ids, out_spans, scratch, stream)
+    return out_ids[:k].copy(), out_spans[:k].copy(), info
+
+
+def _repair(vocab, text, len_a, ci, cs, n_cached, out_ids, out_spans, scratch, stream):
+    """One toktier_repair_append call on host numpy buffers (text uint8, records uint32)."""
     n = ctypes.c_uint64()
     info = RepairInfo()
-    tb = (ctypes.c_uint8 * max(len(raw), 1)).from_buffer_copy(raw if raw else b"\0")
-    rc = lib().toktier_repair_append(vocab.handle, ctypes.cast(tb, ctypes.c_void_p), len_a, len(raw),
-                                     ci.ctypes.data_as(ctypes.c_void_p), cs.ctypes.data_as(ctypes.c_void_p), ci.size,
-                                     out_ids.ctypes.data_as(ctypes.c_void_p),
-                                     out_spans.ctypes.data_as(ctypes.c_void_p), cap, ctypes.byref(n),
-                                     _ptr(scratch), scratch.numel(), _stream(stream), ctypes.byref(info))
+    vp = ctypes.c_void_p
+    rc = lib().toktier_repair_append(vocab.handle, vp(text.ctypes.data if text.size else None), len_a, text.size,
+                                     vp(ci.ctypes.data), vp(cs.ctypes.data), n_cached,
+                                     vp(out_ids.ctypes.data), vp(out_spans.ctypes.data), out_ids.size,
+                                     ctypes.byref(n), _ptr(scratch), scratch.numel(), _stream(stream),
+                                     ctypes.byref(info))
     _check(rc, "toktier_repair_append")
-    k = n.value
-    return (out_ids[:k].copy(), out_spans[:k].copy(),
-            {f: getattr(info, f) for f, _ in RepairInfo._fields_ if f != "pad"})
+    return n.value, {f: getattr(info, f) for f, _ in RepairInfo._fields_ if f != "pad"}
+
+
+class RepairSession:
+    """A session's text and token records in host buffers that grow by doubling.  append(B) repairs
+    the records of A into those of A || B in place (toktier_repair_append with the output arrays the
+    cached ones), so a splice touches only the window's records and the bytes of B and of the window."""
+
+    def __init__(self, tok, text=b""):
+        raw = bytes(text)
+        self.tok = tok
+        self.n_bytes = len(raw)
+        self._text = np.empty(max(2 * len(raw), 4096), dtype=np.uint8)
+        self._text[:len(raw)] = np.frombuffer(raw, dtype=np.uint8)
+        self._ids = np.empty(self._text.size, dtype=np.uint32)
+        self._spans = np.empty(self._text.size, dtype=np.uint32)
+        if raw:
+            ids, _, spans = tok.encode(raw, spans=True)
+        else:
+            ids = spans = np.zeros(0, dtype=np.uint32)
+        self.n_tokens = ids.size
+        self._ids[:ids.size] = ids
+        self._spans[:spans.size] = spans
+        self._scratch = None
+        self.last_info = None
+
+    @property
+    def text(self):
+        return self._text[:self.n_bytes]
+
+    @property
+    def ids(self):
+        return self._ids[:self.n_tokens]
+
+    @property
+    def spans(self):
+        return self._spans[:self.n_tokens]
+
+    def append(self, b):
+        """Append the bytes b (A || B must be valid UTF-8); returns the repair's info dict."""
+        add = np.frombuffer(bytes(b), dtype=np.uint8)
+        total = self.n_bytes + add.size
+        if total > self._text.size:
+            cap = max(2 * self._text.size, total)
+            for name in ("_text", "_ids", "_spans"):
+                old = getattr(self, name)
+                new = np.empty(cap, dtype=old.dtype)
+                new[:old.size] = old
+                setattr(self, name, new)
+        self._text[self.n_bytes:total] = add
+        vocab = self.tok.vocab
+        with torch.cuda.device(self.tok.device):
+            need = toktier_repair_scratch_bytes(vocab, total)
+            if self._scratch is None or self._scratch.numel() < need:
+                grow = need if self._scratch is None else max(need, 2 * self._scratch.numel())
+                self._scratch = torch.empty(grow, dtype=torch.uint8, device=self.tok.device)
+            k, info = _repair(vocab, self._text[:total], self.n_bytes, self._ids, self._spans, self.n_tokens,
+                              self._ids, self._spans, self._scratch, None)
+        self.n_bytes, self.n_tokens, self.last_info = total, k, info
+        return info
 
 
 def toktier_last_status(workspace, stream=None):

@@ -212,64 +212,87 @@ extern "C" int toktier_repair_append(const toktier_vocab *v, const uint8_t *text
     if (len_total >= 0xFFFFFFFFull) return TOKTIER_E_INVALID_ARG;
     if (capacity < len_total || (len_total && (!out_ids || !out_spans))) return TOKTIER_E_CAPACITY;
     if (n_cached > len_a || (n_cached && cached_spans[0] != 0) || (len_a && !n_cached)) return TOKTIER_E_INVALID_ARG;
-    for (uint64_t i = 1; i < n_cached; ++i)
-        if (cached_spans[i] <= cached_spans[i - 1] || cached_spans[i] >= len_a) return TOKTIER_E_INVALID_ARG;
+    if (n_cached && cached_spans[n_cached - 1] >= len_a) return TOKTIER_E_INVALID_ARG;
+    // the records are repaired in place when the output arrays are the cached ones; otherwise no
+    // output array may overlap an input array or the other output array
+    const bool in_place = n_cached && out_ids == cached_ids && out_spans == cached_spans;
+    {
+        auto apart = [](const void *a, uint64_t na_, const void *b, uint64_t nb_) {
+            const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+            return !na_ || !nb_ || x + na_ <= y || y + nb_ <= x;
+        };
+        const uint64_t oc = len_total ? 4 * capacity : 0, cc = 4 * n_cached;
+        if (!apart(out_ids, oc, out_spans, oc)) return TOKTIER_E_INVALID_ARG;
+        if (!in_place && (!apart(out_ids, oc, cached_ids, cc) || !apart(out_ids, oc, cached_spans, cc) ||
+                          !apart(out_spans, oc, cached_ids, cc) || !apart(out_spans, oc, cached_spans, cc)))
+            return TOKTIER_E_INVALID_ARG;
+    }
+    if (len_a < len_total && (text[len_a] & 0xC0u) == 0x80u) return TOKTIER_E_INVALID_UTF8;   // A ends inside a character
     Scratch sc;
     uint64_t need = 0;
     int rc = scratch_layout(v, len_total, scratch, scratch_bytes, &sc, &need);
     if (rc) return rc;
-    std::vector<uint64_t> pos;
-    std::vector<uint32_t> cps;
-    if (!decode(text, len_total, pos, cps)) return TOKTIER_E_INVALID_UTF8;
-    const uint64_t nc = cps.size();
-    // characters of A: A must end on a character boundary
-    const uint64_t na = (uint64_t)(std::lower_bound(pos.begin(), pos.end(), len_a) - pos.begin());
-    if (pos[na] != len_a) return TOKTIER_E_INVALID_UTF8;
     hipStream_t st = (hipStream_t)stream;
     toktier_repair_info inf;
     memset(&inf, 0, sizeof(inf));
     const int fam = v->family;
 
-    // (L): the first character whose context may differ between A alone and A || B
-    uint64_t dl = na >= 2 ? na - 2 : 0;
-    {
-        uint64_t k = na;
-        while (k > 0 && (ucat_host(cps[k - 1]) & 7u) == CAT_W && cps[k - 1] != '\r' && cps[k - 1] != '\n') --k;
-        dl = std::min(dl, k ? k - 1 : 0);
-        if (fam == FAMILY_O200K) {
-            k = na;
-            while (k > 0 && (ucat_host(cps[k - 1]) & 7u) == CAT_LU) --k;
-            dl = std::min(dl, k ? k - 1 : 0);
-        }
-    }
-
+    // Each attempt reads only its window: A's last w characters and B, decoded and checked here, with
+    // character indices counted from the window's first character (the pages price a repair at
+    // O(append + window), whatever the length of A).  The rest of A is read only by the full-text
+    // encode after every window missed, and the cached records only from the window's start on.
+    std::vector<uint64_t> pos;
+    std::vector<uint32_t> cps;
     std::vector<uint32_t> wids, wspans, ctxw;
     for (uint32_t att = 0; att <= REPAIR_DOUBLINGS; ++att) {
         const uint64_t w = (uint64_t)REPAIR_W0 << att;
-        if (na <= w) break;   // the window would hold all of A
-        const uint64_t s = na - w, bs = pos[s];
+        // byte offset of A's w-th character from its end; A must hold more than w characters
+        uint64_t bs = len_a, found = 0;
+        while (bs > 0 && found < w) {
+            --bs;
+            if ((text[bs] & 0xC0u) != 0x80u) ++found;
+        }
+        if (found < w || bs == 0) break;   // the window would hold all of A
+        if (!decode(text + bs, len_total - bs, pos, cps)) return TOKTIER_E_INVALID_UTF8;
+        const uint64_t nc = cps.size();
+        const uint64_t na = (uint64_t)(std::lower_bound(pos.begin(), pos.end(), len_a - bs) - pos.begin());
+        if (pos[na] != len_a - bs) return TOKTIER_E_INVALID_UTF8;
+        // (L): the first character whose context may differ between A alone and A || B (0 when the
+        // run that decides it reaches the window's start: then no splice point qualifies)
+        uint64_t dl = na - 2;
+        {
+            uint64_t k = na;
+            while (k > 0 && (ucat_host(cps[k - 1]) & 7u) == CAT_W && cps[k - 1] != '\r' && cps[k - 1] != '\n') --k;
+            dl = std::min(dl, k ? k - 1 : 0);
+            if (fam == FAMILY_O200K) {
+                k = na;
+                while (k > 0 && (ucat_host(cps[k - 1]) & 7u) == CAT_LU) --k;
+                dl = std::min(dl, k ? k - 1 : 0);
+            }
+        }
         inf.attempts = att + 1;
         inf.window_chars = (uint32_t)w;
         rc = encode_range(v, text, bs, len_total, sc, st, wids, wspans);
         if (rc) return rc;
-        // window contexts (a document from character s) and piece starts
-        contexts(fam, text, len_total, pos, cps, s, true, ctxw);
-        std::vector<uint8_t> wstart(nc - s, 0);
+        // window contexts (a document from its first character) and piece starts
+        contexts(fam, text + bs, len_total - bs, pos, cps, 0, true, ctxw);
+        std::vector<uint8_t> wstart(nc, 0);
         uint32_t state = S_ST;
-        for (uint64_t i = 0; i < nc - s; ++i) {
-            const uint8_t b = v->hmap[ctxw[i]][state];
-            wstart[i] = (b >> 4) & 1u;
-            state = b & 15u;
+        for (uint64_t i = 0; i < nc; ++i) {
+            const uint8_t c = v->hmap[ctxw[i]][state];
+            wstart[i] = (c >> 4) & 1u;
+            state = c & 15u;
         }
-        // (R): the first character after which the maps of characters s+1.. send every state to one
+        // (R): the first character after which the maps of the window's characters 1.. send every
+        // state to one
         uint64_t sync = UINT64_MAX;
         {
             uint8_t img[NSTATES];
             for (int q = 0; q < NSTATES; ++q) img[q] = (uint8_t)q;
-            for (uint64_t k = s + 1; k < na; ++k) {
+            for (uint64_t k = 1; k < na; ++k) {
                 bool same = true;
                 for (int q = 0; q < NSTATES; ++q) {
-                    img[q] = v->hmap[ctxw[k - s]][img[q]] & 15u;
+                    img[q] = v->hmap[ctxw[k]][img[q]] & 15u;
                     same &= img[q] == img[0];
                 }
                 if (same) { sync = k; break; }
@@ -277,8 +300,11 @@ extern "C" int toktier_repair_append(const toktier_vocab *v, const uint8_t *text
         }
         // the longest run of records equal in position and ID, among cached records at or after the
         // window start and window records that start inside A
-        uint64_t i = (uint64_t)(std::lower_bound(cached_spans, cached_spans + n_cached, (uint32_t)bs) - cached_spans);
-        uint64_t j = 0, best_len = 0, best_i = 0, cur_len = 0, cur_i = 0;
+        const uint64_t i0 = (uint64_t)(std::lower_bound(cached_spans, cached_spans + n_cached, (uint32_t)bs) -
+                                       cached_spans);
+        for (uint64_t t = i0 ? i0 : 1; t < n_cached; ++t)   // the records read below must increase
+            if (cached_spans[t] <= cached_spans[t - 1]) return TOKTIER_E_INVALID_ARG;
+        uint64_t i = i0, j = 0, best_len = 0, best_i = 0, cur_len = 0, cur_i = 0;
         while (i < n_cached && j < wids.size()) {
             const uint64_t pc = cached_spans[i], pw = bs + wspans[j];
             if (pw >= len_a) break;
@@ -306,23 +332,25 @@ extern "C" int toktier_repair_append(const toktier_vocab *v, const uint8_t *text
         uint64_t e_byte = UINT64_MAX;
         for (uint64_t r1 = best_i + best_len + 1; r1 > best_i && e_byte == UINT64_MAX; --r1) {
             const uint64_t r = r1 - 1;                                     // boundary before record r
-            const uint64_t b = r < n_cached ? cached_spans[r] : len_a;
+            const uint64_t b = (r < n_cached ? cached_spans[r] : len_a) - bs;
             const uint64_t k = (uint64_t)(std::lower_bound(pos.begin(), pos.end(), b) - pos.begin());
             if (pos[k] != b || k >= nc) continue;                          // inside a character
-            if (sync == UINT64_MAX || k <= sync || k >= dl || k < s) continue;
-            if (!wstart[k - s]) continue;
-            e_byte = b;
+            if (sync == UINT64_MAX || k <= sync || k >= dl) continue;
+            if (!wstart[k]) continue;
+            e_byte = bs + b;
         }
         if (e_byte == UINT64_MAX) continue;
         // cached records before e, then the window's records from e
-        const uint64_t nl = (uint64_t)(std::lower_bound(cached_spans, cached_spans + n_cached, (uint32_t)e_byte) -
+        const uint64_t nl = (uint64_t)(std::lower_bound(cached_spans + i0, cached_spans + n_cached, (uint32_t)e_byte) -
                                        cached_spans);
         uint64_t jr = 0;
         while (jr < wids.size() && bs + wspans[jr] < e_byte) ++jr;
         const uint64_t total = nl + (wids.size() - jr);
         if (total > capacity) return TOKTIER_E_CAPACITY;
-        memcpy(out_ids, cached_ids, 4 * nl);
-        memcpy(out_spans, cached_spans, 4 * nl);
+        if (!in_place) {
+            memcpy(out_ids, cached_ids, 4 * nl);
+            memcpy(out_spans, cached_spans, 4 * nl);
+        }
         for (uint64_t t = jr; t < wids.size(); ++t) {
             out_ids[nl + t - jr] = wids[t];
             out_spans[nl + t - jr] = (uint32_t)(bs + wspans[t]);

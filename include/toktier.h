@@ -288,12 +288,21 @@ int toktier_encode_batch_timed(const toktier_vocab *v, const uint8_t *bytes, con
  * misses, the whole text is encoded.  Either way the output equals the encoding of A || B as one
  * document, records in the same form as the cached ones.
  *   v             vocabulary handle without added tokens (E_INVALID_ARG otherwise).
+ * A splice reads only the window: B, A's last w characters and the cached records from the window's
+ * start on (work of the order of the append plus the window, whatever the length of A); the rest of
+ * A is read only by the full-text encode.
  *   text          host, uint8[len_total]: A || B, valid UTF-8; A ends on a character boundary.
+ *                 Invalid bytes in B or in a window are reported; earlier bytes of A only when the
+ *                 whole text is encoded.
  *   len_a         bytes of A (<= len_total < 2^32 - 1).
  *   cached_ids, cached_spans   host, uint32[n_cached]: the records of A (spans start at 0, strictly
  *                 increasing, below len_a; n_cached = 0 only when len_a = 0).  Not checked to be
- *                 the encoding of A: the caller keeps them from an earlier encode.
- *   out_ids, out_spans   host, uint32[capacity]: the records of A || B; capacity >= len_total.
+ *                 the encoding of A (the caller keeps them from an earlier encode); the order is
+ *                 checked from the window's start on.
+ *   out_ids, out_spans   host, uint32[capacity]: the records of A || B; capacity >= len_total.  Either
+ *                 exactly the cached arrays (then the records are repaired in place: those before
+ *                 the splice point are not copied) or arrays that overlap neither them nor each
+ *                 other (E_INVALID_ARG otherwise).
  *   out_n         host: number of records written.
  *   scratch       device, toktier_repair_scratch_bytes(v, len_total) bytes (text staging, records
  *                 and the encoder's workspace), 256-byte aligned.

@@ -5,7 +5,8 @@ source byte offset), whatever the certificate decides: a splice or a full re-enc
 of A come from the oracle.  Cases: appends to generated sessions of all four families at many cut
 points, multi-step sessions that feed each repaired result back as the next cache, and the
 boundary effects the pages name (a piece merged across the seam, digit grouping, whitespace
-lookahead, newline absorption, case runs) placed at the seam and stretched past the first windows.
+lookahead, newline absorption, case runs) placed at the seam and stretched past the first windows,
+and sessions repaired in place (RepairSession).
 """
 import numpy as np
 import pytest
@@ -150,4 +151,55 @@ def test_rejects_bad_records(tt):
     assert e.value.status == 1
     with pytest.raises(tt.ToktierError) as e:
         t.repair_append("é".encode() + a, 1, ca[:1], cs[:1])   # A ends inside a character
+    assert e.value.status == 4
+
+
+@pytest.mark.parametrize("voc,fam,gen", CASES)
+def test_in_place_session(tt, voc, fam, gen):
+    """RepairSession repairs its records in place (output arrays = cached arrays), growing its
+    buffers past their first capacity; after every append the records equal the oracle's full
+    encoding of the session text, and the first append of each case is checked on its own."""
+    t, m = tok(tt, voc, fam)
+    text = getattr(textgen, gen)(702, 30_000).encode()
+    rng = np.random.default_rng(9)
+    cut = 3000
+    while text[cut] & 0xC0 == 0x80:
+        cut += 1
+    s = tt.RepairSession(t, text[:cut])
+    ids, spans = records(fam, m, text[:cut])
+    assert np.array_equal(s.ids, ids) and np.array_equal(s.spans, spans)
+    steps = spliced = 0
+    while cut < len(text):
+        nxt = min(len(text), cut + int(rng.integers(20, 6000)))
+        while nxt < len(text) and text[nxt] & 0xC0 == 0x80:
+            nxt += 1
+        info = s.append(text[cut:nxt])
+        cut = nxt
+        steps += 1
+        spliced += info["spliced"]
+        if steps in (1, 2) or cut == len(text):
+            eids, espans = records(fam, m, text[:cut])
+            assert np.array_equal(s.ids, eids) and np.array_equal(s.spans, espans), (fam, steps, info)
+    assert bytes(s.text) == text
+    _say("in-place session", fam, steps, "appends,", spliced, "spliced")
+    assert spliced >= steps // 2
+
+
+def test_rejects_overlap_and_bad_append(tt):
+    t, m = tok(tt, "v2", "cl100k")
+    a = ("word " * 300).encode()
+    ca, cs = records("cl100k", m, a)
+    vocab = t.vocab
+    import torch
+    scratch = torch.empty(tt.toktier_repair_scratch_bytes(vocab, len(a) + 8), dtype=torch.uint8, device="cuda:0")
+    from exact_bpe_tokenization_amd import binding
+    text = np.frombuffer(a + b" more", np.uint8)
+    buf = np.empty(2 * text.size + ca.size, np.uint32)   # ids and spans overlapping the cached records
+    buf[:ca.size] = ca
+    with pytest.raises(tt.ToktierError) as e:
+        binding._repair(vocab, text, len(a), buf[:ca.size], cs, ca.size, buf[1:1 + text.size],
+                        buf[1 + text.size:1 + 2 * text.size], scratch, None)
+    assert e.value.status == 1
+    with pytest.raises(tt.ToktierError) as e:        # invalid UTF-8 in the append
+        t.repair_append(a + b"ok \xff", len(a), ca, cs)
     assert e.value.status == 4
