@@ -258,15 +258,15 @@ def main():
     def step(sync):
         return tt.toktier_encode_batch(tok.vocab, d_data, d_offs, out_ids, out_offs, ws, sync=sync)
 
+    # warmup: the first step waits for its count (and reports any input error), the others run back
+    # to back up to the timed steps (an idle gap -- a readback, a sleep -- before them lets the chip
+    # slow down and costs the next steps several microseconds each)
     _log("warmup")
-    for _ in range(args.warmup):
-        n_tok = step(True)
+    step(True)
+    for _ in range(args.warmup - 1):
+        step(False)
     torch.cuda.synchronize()
-    gpu_ids = out_ids[:n_tok].cpu().numpy().view(np.uint32).copy()
-    gpu_oo = out_offs.cpu().numpy().astype(np.uint64)
 
-    _log("timed steps")
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(False)
@@ -274,7 +274,11 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     gbs = n / (wall / args.steps) / 1e9
-    n_tokens = tt.toktier_last_status(ws)
+    _log("timed steps done")
+    # every step encodes the whole batch again: the last step's outputs are the ones checked
+    n_tok = n_tokens = tt.toktier_last_status(ws)
+    gpu_ids = out_ids[:n_tok].cpu().numpy().view(np.uint32).copy()
+    gpu_oo = out_offs.cpu().numpy().astype(np.uint64)
 
     # ---- the same steps with two batches in flight: alternate steps on two streams, each with its
     # own workspace and outputs (every step still encodes the whole batch) ----
