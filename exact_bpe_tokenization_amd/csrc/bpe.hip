@@ -1132,9 +1132,12 @@ hipError_t launch_giant_prep(const DevVocab &v, const Batch &b, hipStream_t s, c
     const Layout &L = b.L;
     if (b.n == 0) return hipGetLastError();
     // giant pieces: safe-seam bitmap, then chunks (listed with the other BPE items by length)
+    // (nothing to launch when no piece can be longer than BLOCK_MAX bytes: the layout holds at most
+    // that many)
     LaunchScope k(ev, TK_GIANT_SEAMS, s);
     const uint32_t gs = (uint32_t)((b.n + 1023) / 1024);
-    hipLaunchKernelGGL(k_giant_prep, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
+    if (L.cap_n > (uint64_t)BLOCK_MAX)
+        hipLaunchKernelGGL(k_giant_prep, dim3(gs < 256 ? gs : 256), dim3(1024), 0, s, v, b.bytes, b.ws, L);
     return hipGetLastError();
 }
 
@@ -1160,7 +1163,8 @@ hipError_t launch_bpe(const DevVocab &v, const Batch &b, hipStream_t s, const Ev
     const uint32_t gg = L.cap_giant < 64 ? L.cap_giant : 64;
     {
         LaunchScope k(ev, TK_BPE_GIANT, s);
-        hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
+        if (L.cap_n > (uint64_t)BLOCK_MAX)   // (no giant piece, no chunk, nothing to join)
+            hipLaunchKernelGGL(k_bpe_giant, dim3(gg), dim3(GIANT_THREADS), 0, s, v, b.bytes, b.ws, L);
     }
     return hipGetLastError();
 }
