@@ -624,7 +624,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
     __shared__ __align__(16) uint8_t scc[TILE + HALO];
     __shared__ uint16_t spiece[TILE];
     __shared__ uint4 smap16[NCTX_MAX + 1];      // [NCTXV]: identity (continuation bytes)
-    __shared__ uint16_t sasc[128];              // ASCII character: byte code (no doc bit) | W, LU, LL bits 8-10
+    __shared__ uint16_t sasc[128];              // ASCII character: byte code (no doc bit) | W, LU, LL, ' bits 8-11
     __shared__ uint16_t sctxa[256];             // byte code -> its part of the context (0xFFFF: not a character)
     __shared__ uint8_t sctxb[256];              // next character's byte code -> its part of the context
     __shared__ uint32_t sbkw[NW];
@@ -646,7 +646,7 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         sasc[tid] = (uint16_t)(u | ((tid == '\r' || tid == '\n') ? CC_CRLF : 0u) | (tid == ' ' ? CC_SP : 0u) |
                                (DS ? ds_bits(tid, u) : 0u) |
                                (cat == CAT_W ? 0x100u : 0u) | (cat == CAT_LU ? 0x200u : 0u) |
-                               (cat == CAT_LL ? 0x400u : 0u));
+                               (cat == CAT_LL ? 0x400u : 0u) | (tid == '\'' ? 0x800u : 0u));
     }
     if (tid < 256) {
         // the self / doc part of the context (self code with NA clear) and the next-character part
@@ -735,33 +735,37 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
         const uint32_t hibits = (rw[0] | rw[1] | rw[2] | rw[3] | rw[4] | rw[5]) & 0x80808080u;
         ascii = __ballot(hibits != 0) == 0;
         if (ascii) {
-            // every byte the wavefront looks at is ASCII: a table lookup per byte, apostrophes apart
+            // every byte the wavefront looks at is ASCII: a table lookup per byte; the few document
+            // starts, positions past the end of the batch (byte 0: no mask bit) and apostrophes are
+            // applied afterwards, bit by bit
             uint32_t apos = 0;
 #pragma unroll
             for (int k = 0; k < PRE_CHUNK; ++k) {
-                const uint32_t c = wbyte(rw, k + RAW_LEAD);
-                const uint32_t f = sasc[c];
-                const uint32_t code = (f & 0xFFu) | (((dm >> (k + RAW_LEAD)) & 1u) ? CC_DOC : 0u);
-                const bool eof = (xeof >> k) & 1u;
-                if (!DS) apos |= (c == '\'' && !eof ? 1u : 0u) << k;
-                w[k >> 2] |= (eof ? (uint32_t)CC_EOF : code) << (8 * (k & 3));
+                const uint32_t f = sasc[wbyte(rw, k + RAW_LEAD)];
+                w[k >> 2] |= (f & 0xFFu) << (8 * (k & 3));
                 mW |= ((f >> 8) & 1u) << k;
                 mC |= ((f >> 3) & 1u) << k;
+                if (!DS) apos |= ((f >> 11) & 1u) << k;
                 if (CASE) {
                     mU |= ((f >> 9) & 1u) << k;
                     mL |= ((f >> 10) & 1u) << k;
                 }
             }
-            while (apos) {
-                const int k = __ffs(apos) - 1;
-                apos &= apos - 1;
-                const uint32_t lc = contraction_code(sraw, docbit, RAW_LEAD + c0 + k, lo + c0 + k, n, v.family);
-                const uint32_t add = lc << (CC_CONTR_SHIFT + 8 * (k & 3));
+            apos &= ~xeof;
+            auto or_code = [&](int k, uint32_t add) {   // add to the code of byte k (k not uniform)
                 const int q = k >> 2;
+                add <<= 8 * (k & 3);
                 w[0] |= q == 0 ? add : 0u;
                 w[1] |= q == 1 ? add : 0u;
                 w[2] |= q == 2 ? add : 0u;
                 w[3] |= q == 3 ? add : 0u;
+            };
+            for (uint32_t m = (dm >> RAW_LEAD) & 0xFFFFu; m; m &= m - 1) or_code(__ffs(m) - 1, CC_DOC);
+            for (uint32_t m = xeof & 0xFFFFu; m; m &= m - 1) or_code(__ffs(m) - 1, CC_EOF);
+            while (apos) {
+                const int k = __ffs(apos) - 1;
+                apos &= apos - 1;
+                or_code(k, contraction_code(sraw, docbit, RAW_LEAD + c0 + k, lo + c0 + k, n, v.family) << CC_CONTR_SHIFT);
             }
         } else {
 #pragma unroll
