@@ -425,69 +425,67 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
 
     uint32_t mytok = 0;
     constexpr int K = 4;
-    // a step's start offsets (this piece's and the next one's, 16 bits each) are loaded during the
-    // step before, while that step's table reads are in flight
-    auto load_offsets = [&](uint32_t i0, uint32_t (&pk)[K]) {
+    // a step's start offsets (this piece's and the next one's) are loaded during the step before,
+    // while that step's table reads are in flight: indices clamped into the tile's part of the array
+    // (a load under a branch would be waited for at once), the values used only in the next step
+    uint32_t o0[K], o1[K];
+    auto load_offsets = [&](uint32_t i0) {
+        const uint32_t last = cnt ? cnt - 1 : 0u;
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             const uint32_t i = i0 + u * NT + tid;
-            pk[u] = (i < cnt ? (uint32_t)prs[i] : 0u) | ((i + 1 < cnt ? (uint32_t)prs[i + 1] : 0u) << 16);
+            o0[u] = prs[min(i, last)];
+            o1[u] = prs[min(i + 1, last)];
         }
     };
-    uint32_t pk_next[K];
-    load_offsets(0, pk_next);
+    load_offsets(0);
     for (uint32_t i0 = 0; i0 < cnt; i0 += K * NT) {
         uint32_t a[K], e[K];
 #pragma unroll
         for (int u = 0; u < K; ++u) {
-            const uint32_t i = i0 + u * NT + tid, pk = pk_next[u];
-            a[u] = i < cnt ? (uint32_t)lo + (pk & 0xFFFFu) : 0u;
-            e[u] = i + 1 < cnt ? (uint32_t)lo + (pk >> 16) : next;
-        }
-        if (i0 + K * NT < cnt) load_offsets(i0 + K * NT, pk_next);
-#pragma unroll
-        for (int u = 0; u < K; ++u) {   // the global piece starts, for the kernels after this one
             const uint32_t i = i0 + u * NT + tid;
-            if (i < cnt) pstart[p0 + i] = a[u];
+            a[u] = i < cnt ? (uint32_t)lo + o0[u] : 0u;
+            e[u] = i + 1 < cnt ? (uint32_t)lo + o1[u] : next;
         }
         // kind: 0 nothing to load, 2 byte pair, 3 short table (both candidate slots).  Each piece's
         // result word is written once, in one coalesced store per row of the step (the pieces resolved
         // later -- by the long table below or by the BPE kernels -- get a placeholder overwritten then):
         // scattered partial stores would leave partly written cache lines to be written back repeatedly
-        uint32_t kind[K], si[K], sj[K], res[K];
-        uint64_t key[K];
+        // The step's global stores and its next offsets are issued after its table reads: the wait
+        // for those reads then does not include them (memory operations complete in issue order).
+        uint32_t kind[K], si[K], sj[K], res[K], lslot[K];
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             const uint32_t i = i0 + u * NT + tid;
             kind[u] = 0;
             si[u] = 0;
             sj[u] = 0;
-            key[u] = 0;
             res[u] = 0;
+            lslot[u] = NO_PIECE;
             if (i >= cnt) continue;
             const uint32_t j = a[u] - (uint32_t)lo, len = e[u] - a[u];
             if (len == 1) {
                 res[u] = win_byte(sm, j);
                 ++mytok;
             } else if (len <= WA_MAX) {
-                key[u] = short_key(sm, j, len);
-                const uint32_t set = hot_set(key[u]);
+                const uint64_t key = short_key(sm, j, len);
+                const uint32_t set = hot_set(key);
                 const uint4 h0 = sm.hot[2 * set], h1 = sm.hot[2 * set + 1];
                 const uint64_t k0 = (uint64_t)h0.x | ((uint64_t)h0.y << 32), k1 = (uint64_t)h1.x | ((uint64_t)h1.y << 32);
-                if (k0 == key[u] || k1 == key[u]) {
-                    res[u] = k0 == key[u] ? h0.z : h1.z;
+                if (k0 == key || k1 == key) {
+                    res[u] = k0 == key ? h0.z : h1.z;
                     ++mytok;
                 } else if (len == 2 && !IGN) {
                     kind[u] = 2;
                     si[u] = (win_byte(sm, j) << 8) | win_byte(sm, j + 1);
                 } else if (v.wa) {
                     kind[u] = 3;
-                    ck_slots(key[u], v.wseed, v.wa_cap, si[u], sj[u]);
+                    ck_slots(key, v.wseed, v.wa_cap, si[u], sj[u]);
                 } else {
                     list_miss(i, len);
                 }
             } else if (len <= (uint32_t)TABLE_MAX) {
-                llist[atomicAdd(&sm.ln, 1u)] = i | (len << 16);
+                lslot[u] = atomicAdd(&sm.ln, 1u);   // listed below
             } else if (len <= (uint32_t)SHORT_MAX) {
                 uint32_t w = NO_PIECE;
                 if (IGN && len <= v.lmax) w = whole_token(v, bytes + a[u], len);
@@ -501,17 +499,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
                 list_long(ws, L, ctrl, p0 + i, len);
             }
         }
-        // the global lookups of the pieces the hot sets did not answer: all loads in flight at once
+        // the global lookups of the pieces the hot sets did not answer: all loads in flight at once,
+        // issued without branches (a lane with nothing to look up reads entry 0)
         uint4 x[K], y[K];
 #pragma unroll
         for (int u = 0; u < K; ++u) {
-            if (kind[u] == 2) {
-                x[u] = make_uint4(__ldg(v.r2 + si[u]), 0u, 0u, 0u);
-                y[u] = make_uint4(0u, 0u, 0u, 0u);
-            } else if (kind[u] == 3) {
-                x[u] = v.wa[si[u]];
-                y[u] = v.wa[sj[u]];
+            if (v.wa) {
+                x[u] = v.wa[kind[u] == 3 ? si[u] : 0u];
+                y[u] = v.wa[kind[u] == 3 ? sj[u] : 0u];
             }
+            const uint32_t r = __ldg(v.r2 + (kind[u] == 2 ? si[u] : 0u));
+            if (kind[u] == 2) x[u].x = r;
+        }
+        if (i0 + K * NT < cnt) load_offsets(i0 + K * NT);
+#pragma unroll
+        for (int u = 0; u < K; ++u) {   // the global piece starts, for the kernels after this one
+            const uint32_t i = i0 + u * NT + tid;
+            if (i < cnt) pstart[p0 + i] = a[u];
+            if (lslot[u] != NO_PIECE) llist[lslot[u]] = i | ((e[u] - a[u]) << 16);
         }
 #pragma unroll
         for (int u = 0; u < K; ++u) {
@@ -528,13 +533,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
                     mytok += 2;
                 }
             } else if (kind[u] == 3) {
+                // the key again from the window (cheaper than holding it across the loads)
+                const uint32_t len = e[u] - a[u];
+                const uint64_t k = short_key(sm, a[u] - (uint32_t)lo, len);
                 const uint64_t ka = (uint64_t)x[u].x | ((uint64_t)x[u].y << 32);
                 const uint64_t kb = (uint64_t)y[u].x | ((uint64_t)y[u].y << 32);
-                if (ka == key[u] || kb == key[u]) {
-                    res[u] = ka == key[u] ? x[u].z : y[u].z;
+                if (ka == k || kb == k) {
+                    res[u] = ka == k ? x[u].z : y[u].z;
                     ++mytok;
                 } else {
-                    list_miss(i, (uint32_t)(key[u] >> 56));
+                    list_miss(i, len);
                 }
             }
             if (i < cnt) pval[p0 + i] = res[u];
