@@ -516,7 +516,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
         for (int u = 0; u < K; ++u) {   // the global piece starts, for the kernels after this one
             const uint32_t i = i0 + u * NT + tid;
             if (i < cnt) pstart[p0 + i] = a[u];
-            if (lslot[u] != NO_PIECE) llist[lslot[u]] = i | ((e[u] - a[u]) << 16);
+            if (lslot[u] != NO_PIECE) llist[lslot[u]] = i | ((a[u] - (uint32_t)lo) << 13) | ((e[u] - a[u]) << 26);
         }
 #pragma unroll
         for (int u = 0; u < K; ++u) {
@@ -550,22 +550,38 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
     }
     __syncthreads();
 
-    // 8..32-byte pieces, compacted: the long whole-piece table
+    // 8..32-byte pieces, compacted: the long whole-piece table.  An entry holds the piece's index in
+    // the tile, its window offset and its length (13 + 13 + 6 bits); the table reads of a pass are
+    // issued together and without branches (an idle slot reads entry 0)
     const uint32_t nl = sm.ln;
-    for (uint32_t k = tid; k < nl; k += NT) {
-        const uint32_t ent = llist[k];
-        const uint32_t i = ent & 0xFFFFu, len = ent >> 16, j = prs[i];
+    for (uint32_t k0 = 0; k0 < nl; k0 += NT) {
+        const uint32_t k = k0 + tid;
+        const uint32_t ent = k < nl ? llist[k] : 0u;
+        const uint32_t i = ent & 0x1FFFu, j = (ent >> 13) & 0x1FFFu, len = ent >> 26;
         uint64_t k4[4];
         win_words<4>(sm, j, len, k4);
+        uint32_t ci = 0, cj = 0;
+        if (v.wb && len) ck_slots(wb_digest(k4[0], k4[1], k4[2], k4[3], len), v.bseed, v.wb_cap, ci, cj);
+        uint4 ea[3], eb[3];
+        if (v.wb) {
+            const uint4 *ep = v.wb + 3ull * ci, *fp = v.wb + 3ull * cj;
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+                ea[w] = ep[w];
+                eb[w] = fp[w];
+            }
+        }
+        if (!len) continue;   // (no entry)
         bool hit = false;
         uint32_t id = 0;
         if (v.wb) {
-            uint32_t ci, cj;
-            ck_slots(wb_digest(k4[0], k4[1], k4[2], k4[3], len), v.bseed, v.wb_cap, ci, cj);
-            const uint4 *ep = v.wb + 3ull * ci, *fp = v.wb + 3ull * cj;
-            const uint4 a0 = ep[0], a1 = ep[1], a2 = ep[2], b0 = fp[0], b1 = fp[1], b2 = fp[2];
-            if (wb_match(a0, a1, a2, k4[0], k4[1], k4[2], k4[3], len)) { hit = true; id = a2.y; }
-            else if (wb_match(b0, b1, b2, k4[0], k4[1], k4[2], k4[3], len)) { hit = true; id = b2.y; }
+            if (wb_match(ea[0], ea[1], ea[2], k4[0], k4[1], k4[2], k4[3], len)) {
+                hit = true;
+                id = ea[2].y;
+            } else if (wb_match(eb[0], eb[1], eb[2], k4[0], k4[1], k4[2], k4[3], len)) {
+                hit = true;
+                id = eb[2].y;
+            }
         }
         if (hit) {
             pval[p0 + i] = id;
