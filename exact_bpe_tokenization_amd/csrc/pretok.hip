@@ -669,8 +669,26 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
 
     // raw bytes [lo - 4, lo + TILE + 24), as 32-bit words
     // (interior words from two aligned 4-byte loads, which never leave the pages of the bytes they
-    // hold; the words at the batch edges byte by byte)
-    for (int j = tid; j < SPAN / 4; j += PRE_THREADS) {
+    // hold; the words at the batch edges byte by byte).  Inside the batch every thread issues all of
+    // its loads before storing any, so that they are in flight together.
+    if (base >= 0 && (uint64_t)base + SPAN <= n) {
+        constexpr int RW = (SPAN / 4 + PRE_THREADS - 1) / PRE_THREADS;
+        const uintptr_t a0 = (uintptr_t)(bytes + base);
+        const uint32_t *al = (const uint32_t *)(a0 & ~(uintptr_t)3);
+        const uint32_t sh = (uint32_t)(a0 & 3u);
+        uint32_t x0[RW], x1[RW];
+#pragma unroll
+        for (int k = 0; k < RW; ++k) {
+            const uint32_t j = min((uint32_t)(tid + k * PRE_THREADS), (uint32_t)(SPAN / 4 - 1));
+            x0[k] = al[j];
+            x1[k] = sh ? al[j + 1] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < RW; ++k) {
+            const uint32_t j = tid + k * PRE_THREADS;
+            if (j < (uint32_t)(SPAN / 4)) ((uint32_t *)sraw)[j] = sh ? __builtin_amdgcn_alignbyte(x1[k], x0[k], sh) : x0[k];
+        }
+    } else for (int j = tid; j < SPAN / 4; j += PRE_THREADS) {
         const int64_t p = base + 4 * j;
         uint32_t w = 0;
         if (p >= 0 && (uint64_t)p + 4 <= n) {
