@@ -426,6 +426,11 @@ __global__ __launch_bounds__(128) void k_summary(DevVocab v, const uint8_t *__re
     // (d1 and the first two starts from the 64 offsets after d0, read in one step; more steps only
     // for windows with more than 64 document starts)
     const uint64_t lo_w = lo >= (uint64_t)RAW_LEAD ? lo - RAW_LEAD : 0, hi_w = lo + TILE + RAW_TAIL;
+    // the first scan step's bytes (4 per lane and the three after them, clamped to the batch; the
+    // values past it unused), loaded with the document search's first offsets
+    uint32_t pre[7];
+#pragma unroll
+    for (int t = 0; t < 7; ++t) pre[t] = bytes[min(lo + (uint64_t)(4u * lane + t), n - 1)];
     const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, lo_w);
     uint32_t d1 = d0, o0 = 0, o1 = 0;
     for (uint32_t b = d0;; b += 64u) {
@@ -450,18 +455,23 @@ __global__ __launch_bounds__(128) void k_summary(DevVocab v, const uint8_t *__re
     // instead of 31 dependent rounds of loads)
     auto scan = [&](uint64_t w, auto tc) {
         constexpr int T = decltype(tc)::value;
+        // (the first step, 4 bytes per lane, from the bytes loaded above; the others byte by byte)
+        constexpr int PRE = T == 4 ? 7 : 1;
+        auto byte_at = [&](int t, uint64_t p) -> uint32_t { return T == 4 ? pre[t] : (uint32_t)bytes[p]; };
         uint32_t mna = BK_KEEP, mau = BK_KEEP;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             const uint64_t p = w + (uint64_t)T * lane + t;
             if (p >= hi) continue;
-            const uint32_t c = bytes[p];
+            const uint32_t c = byte_at(t, p);
             if ((c & 0xC0u) == 0x80u) continue;
             uint32_t len = utf8_len(c), cp = c;
             const bool ok = len != 0 && p + len <= n;
             if (ok && len > 1) {
                 cp = c & (0x7Fu >> len);
-                for (uint32_t u = 1; u < len; ++u) cp = (cp << 6) | (bytes[p + u] & 0x3Fu);
+#pragma unroll
+                for (uint32_t u = 1; u < 4; ++u)
+                    if (u < len) cp = (cp << 6) | (byte_at(t + (int)u < PRE ? t + (int)u : 0, p + u) & 0x3Fu);
             }
             if (!ok) { len = 1; cp = 0xFFFDu; }
             const uint32_t code = ucat(cp) | ((c == '\r' || c == '\n') ? CC_CRLF : 0u);
@@ -487,7 +497,7 @@ __global__ __launch_bounds__(128) void k_summary(DevVocab v, const uint8_t *__re
         if (au == BK_KEEP && bau) au = xau;
     };
     uint64_t w = lo;
-    if (w < hi) scan(w, StepBytes<4>{});
+    if (w < hi) scan(w, StepBytes<4>{});   // (lo: the bytes in pre)
     for (w += 256; w < hi && (na == BK_KEEP || au == BK_KEEP); w += 64 * 32) scan(w, StepBytes<32>{});
     if (lane == 0) (ws + L.tbwd)[blockIdx.x] = (uint8_t)(na | (au << 2));
 
