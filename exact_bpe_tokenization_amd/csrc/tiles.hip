@@ -33,11 +33,13 @@ constexpr int NW = NT / 64;
 constexpr int WIN = TILE + SHORT_MAX + 32;        // LDS byte window [lo, lo + WIN), zero past the batch
 
 constexpr int MQ = 256;                           // pieces a tile lists for BPE through LDS
+constexpr int LQ = 1024;                          // 8..32-byte pieces a tile queues in LDS
 
 struct ResolveSmem {
     uint32_t win[WIN / 4];            // the byte window as words
     uint4 hot[HOT_SLOTS];             // the hot sets of the short whole-piece table
     uint32_t q[MQ];                   // pieces left for BPE (index in the tile | length << 16)
+    uint32_t lq[LQ];                  // 8..32-byte pieces for the long table (past LQ: device memory)
     uint32_t wsum[NW];
     uint32_t qn, ln;                  // pieces listed for BPE / for the 8..32-byte table
     uint32_t rn[NMISS], rb[NMISS];    // per BPE list: this tile's items, their first list slot
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
             ((uint32_t *)(ws + L.tbase))[n_tiles] = p0 + cnt;
         }
     }
-    uint32_t *llist = (uint32_t *)(ws + L.tokoff) + p0;   // the 8..32-byte pieces
+    uint32_t *llist = (uint32_t *)(ws + L.tokoff) + p0;   // the 8..32-byte pieces past LQ
     // a piece left for BPE: queued (index in the tile | length << 16) in LDS, past its capacity in
     // the tile's own slice of a device array; at the end the queue goes to the BPE lists in one run
     // per list
@@ -451,9 +453,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
         // result word is written once, in one coalesced store per row of the step (the pieces resolved
         // later -- by the long table below or by the BPE kernels -- get a placeholder overwritten then):
         // scattered partial stores would leave partly written cache lines to be written back repeatedly
-        // The step's global stores and its next offsets are issued after its table reads: the wait
-        // for those reads then does not include them (memory operations complete in issue order).
-        uint32_t kind[K], si[K], sj[K], res[K], lslot[K];
+        // The step's global stores are issued after its table reads have been waited for (the wait
+        // counter covers loads and stores in issue order), the next offsets with the reads.
+        uint32_t kind[K], si[K], sj[K], res[K];
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             const uint32_t i = i0 + u * NT + tid;
@@ -461,7 +463,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
             si[u] = 0;
             sj[u] = 0;
             res[u] = 0;
-            lslot[u] = NO_PIECE;
             if (i >= cnt) continue;
             const uint32_t j = a[u] - (uint32_t)lo, len = e[u] - a[u];
             if (len == 1) {
@@ -485,7 +486,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
                     list_miss(i, len);
                 }
             } else if (len <= (uint32_t)TABLE_MAX) {
-                lslot[u] = atomicAdd(&sm.ln, 1u);   // listed below
+                const uint32_t slot = atomicAdd(&sm.ln, 1u), ent = i | (j << 13) | (len << 26);
+                if (slot < (uint32_t)LQ) sm.lq[slot] = ent;
+                else llist[slot] = ent;
             } else if (len <= (uint32_t)SHORT_MAX) {
                 uint32_t w = NO_PIECE;
                 if (IGN && len <= v.lmax) w = whole_token(v, bytes + a[u], len);
@@ -512,12 +515,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
             if (kind[u] == 2) x[u].x = r;
         }
         if (i0 + K * NT < cnt) load_offsets(i0 + K * NT);
-#pragma unroll
-        for (int u = 0; u < K; ++u) {   // the global piece starts, for the kernels after this one
-            const uint32_t i = i0 + u * NT + tid;
-            if (i < cnt) pstart[p0 + i] = a[u];
-            if (lslot[u] != NO_PIECE) llist[lslot[u]] = i | ((a[u] - (uint32_t)lo) << 13) | ((e[u] - a[u]) << 26);
-        }
 #pragma unroll
         for (int u = 0; u < K; ++u) {
             const uint32_t i = i0 + u * NT + tid;
@@ -547,16 +544,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(IGN ? 4 : 5,
             }
             if (i < cnt) pval[p0 + i] = res[u];
         }
+#pragma unroll
+        for (int u = 0; u < K; ++u) {   // the global piece starts, for the kernels after this one
+            const uint32_t i = i0 + u * NT + tid;
+            if (i < cnt) pstart[p0 + i] = a[u];
+        }
     }
     __syncthreads();
 
-    // 8..32-byte pieces, compacted: the long whole-piece table.  An entry holds the piece's index in
+    // 8..32-byte pieces, compacted (in LDS, past LQ in the tile's slice of a device array): the long
+    // whole-piece table.  An entry holds the piece's index in
     // the tile, its window offset and its length (13 + 13 + 6 bits); the table reads of a pass are
     // issued together and without branches (an idle slot reads entry 0)
     const uint32_t nl = sm.ln;
     for (uint32_t k0 = 0; k0 < nl; k0 += NT) {
         const uint32_t k = k0 + tid;
-        const uint32_t ent = k < nl ? llist[k] : 0u;
+        const uint32_t ent = k < nl ? (k < (uint32_t)LQ ? sm.lq[k] : llist[k]) : 0u;
         const uint32_t i = ent & 0x1FFFu, j = (ent >> 13) & 0x1FFFu, len = ent >> 26;
         uint64_t k4[4];
         win_words<4>(sm, j, len, k4);
