@@ -16,12 +16,14 @@
 //            appended to the BPE lists by length, one run per list and tile.  The tile's token count
 //            so far goes to its counter and to the counter of its group of 64 tiles (the BPE
 //            kernels add the tokens of the pieces they encode).
-//   k_emit   per tile: its first output index from the counters (the groups before its own, then
-//            the tiles before it in its group); per wavefront, groups of four rounds of 64 pieces
-//            (their results, starts and the first two IDs of the multi-token ones loaded together),
-//            a wavefront scan of each round's token counts places its IDs (consecutive pieces write
-//            consecutive IDs); per-document token offsets; optional token spans.  Up to 32 more
-//            workgroups copy the IDs of the giant pieces.  No workgroup waits for another.
+//   k_emit   per two tiles: their first output index from the counters (the groups before their own,
+//            then the tiles before them in their group); groups of eight rounds of 256 pieces whose results
+//            and starts are loaded at once, placed by wavefront scans of each round's token counts
+//            and one exchange of the per-wavefront totals (consecutive pieces write consecutive IDs);
+//            one-token pieces written at once, multi-token ones listed in LDS and copied one per
+//            thread with all their loads in flight; per-document token offsets; optional token
+//            spans.  Up to 32 more workgroups copy the IDs of the giant pieces.  No workgroup waits
+//            for another.
 #include "internal.h"
 
 namespace tt {
@@ -46,9 +48,15 @@ struct ResolveSmem {
     uint32_t base, next;              // pieces before the tile; the first piece start after it
 };
 
+constexpr int ET = 2;             // tiles per k_emit workgroup
+constexpr int ER = 8;             // rounds of NT pieces whose loads k_emit issues together (pick())
+constexpr int MLQ = NT;           // multi-token pieces k_emit lists in LDS per group of rounds
+
 struct EmitSmem {
-    uint32_t docbits[TILE / 32];      // document starts in the tile
-    uint32_t wsum[NW];
+    uint32_t docbits[ET * TILE / 32]; // document starts in the workgroup's tiles
+    uint32_t wtot[ER][NW];            // tokens per round and wavefront of the current group
+    uint32_t ma[MLQ], mo[MLQ], mc[MLQ];   // listed multi-token pieces: start byte, output index, count
+    uint32_t mn;                      // multi-token pieces listed
     uint32_t base, p0, p1;
     uint4 dd;
 };
@@ -148,6 +156,40 @@ __device__ __forceinline__ uint32_t wg_excl_sum(S &sm, uint32_t x, uint32_t *tot
     __syncthreads();
     *total = tot;
     return before + inc - x;
+}
+
+// The c IDs of a multi-token piece of at most SEG2_MAX bytes, copied by one thread from
+// scratch[a ...] to out_ids[o ...] (eight loads in flight per step); with spans, each token's start
+// byte from the piece's start and the token lengths.
+template <bool SPANS>
+__device__ __forceinline__ void copy_ids(const uint32_t *scratch, uint32_t a, uint32_t o, uint32_t c,
+                                         uint32_t *out_ids, uint32_t *out_spans, const uint32_t *tok_len)
+{
+    uint32_t sp = a;
+    for (uint32_t t0 = 0; t0 < c; t0 += 8) {
+        uint32_t x[8];
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) x[u] = t0 + u < c ? scratch[a + t0 + u] : 0u;
+#pragma unroll
+        for (uint32_t u = 0; u < 8; ++u) {
+            if (t0 + u < c) {
+                out_ids[o + t0 + u] = x[u];
+                if (SPANS) {
+                    out_spans[o + t0 + u] = sp;
+                    sp += tok_len[x[u]];
+                }
+            }
+        }
+    }
+}
+
+// x[k] for a k that is not known at compile time, by selects with constant indices (a loop here
+// would leave the array in private memory)
+__device__ __forceinline__ uint32_t pick(const uint32_t (&x)[8], uint32_t k)
+{
+    const uint32_t lo4 = k == 0 ? x[0] : k == 1 ? x[1] : k == 2 ? x[2] : x[3];
+    const uint32_t hi4 = k == 4 ? x[4] : k == 5 ? x[5] : k == 6 ? x[6] : x[7];
+    return k < 4 ? lo4 : hi4;
 }
 
 // The IDs of a piece of 129..BLOCK_MAX bytes, encoded before the tile encoder, copied by one
@@ -630,7 +672,7 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
                                              uint64_t *__restrict__ out_offsets, uint32_t *__restrict__ out_spans)
 {
     __shared__ EmitSmem sm;
-    const uint32_t grid_tiles = L.n_tiles;   // the launch's tiles (a plan's size bucket)
+    const uint32_t grid_tiles = (L.n_tiles + ET - 1) / ET;   // the launch's tile workgroups (a plan's size bucket)
     if (blockIdx.x >= grid_tiles) {   // the giant pieces' IDs
         emit_giant<SPANS>(ws, L, blockIdx.x - grid_tiles, gridDim.x - grid_tiles, out_ids, out_spans, v.tok_len);
         return;
@@ -644,7 +686,7 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
         }
         return;
     }
-    if (blockIdx.x >= n_tiles) return;
+    if (blockIdx.x * (uint32_t)ET >= n_tiles) return;
     const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *__restrict__ tbase = (const uint32_t *)(ws + L.tbase);
     const uint32_t *__restrict__ tcount = (const uint32_t *)(ws + L.tcount);
@@ -652,15 +694,16 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
     const uint32_t *__restrict__ pval = (const uint32_t *)(ws + L.pval);
     const uint32_t *__restrict__ scratch = (const uint32_t *)(ws + L.scratch);
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
-    const uint32_t tile = blockIdx.x;
+    // this workgroup's tiles [tile, t1)
+    const uint32_t tile = blockIdx.x * (uint32_t)ET, t1 = min(tile + (uint32_t)ET, n_tiles);
     const uint64_t lo = (uint64_t)tile * TILE;
-    const uint64_t hi = min(lo + (uint64_t)TILE, n);
+    const uint64_t hi = min((uint64_t)t1 * TILE, n);
     auto count_of = [](uint32_t pv) -> uint32_t { return (pv & PV_MULTI) ? (pv & PV_COUNT) : 1u; };
 
-    // the loads that depend on nothing, at once: the tile's piece range and document window; wave 0:
-    // the first output index of the tile (the groups of 64 tiles before its group, then the tiles
-    // before it in its group; counts are final: every kernel that adds to them has finished)
-    for (uint32_t i = tid; i < TILE / 32; i += NT) sm.docbits[i] = 0;
+    // the loads that depend on nothing, at once: the tiles' piece range and document window; wave 0:
+    // the first output index of the first tile (the groups of 64 tiles before its group, then the
+    // tiles before it in its group; counts are final: every kernel that adds to them has finished)
+    for (uint32_t i = tid; i < ET * TILE / 32; i += NT) sm.docbits[i] = 0;
     if (wid == 0) {
         const uint32_t g = tile / 64u;
         uint32_t x = 0;
@@ -668,123 +711,123 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
         if (64 * g + lane < tile) x += tcount[64 * g + lane];
         x = wave_incl_sum(x);
         if (lane == 63) sm.base = x;
+        if (lane == 0) sm.mn = 0;
     } else if (tid == 64) {
         sm.p0 = tbase[tile];
-        sm.p1 = tbase[tile + 1];
-        sm.dd = ((const uint4 *)(ws + L.tdoc))[tile];
+        sm.p1 = tbase[t1];
+        const uint4 d0 = ((const uint4 *)(ws + L.tdoc))[tile], d1 = ((const uint4 *)(ws + L.tdoc))[t1 - 1];
+        sm.dd = make_uint4(d0.x, d1.y, 0u, 0u);   // documents of the windows of the first and last tile
     }
     __syncthreads();
-    const uint32_t p0 = sm.p0, p1 = sm.p1, cnt = p1 - p0;
+    const uint32_t p0 = sm.p0, cnt = sm.p1 - p0;
     const uint4 dd = sm.dd;
-    // wavefront wid owns pieces [qb, qe) of the tile (a multiple of 64 each)
-    const uint32_t Q = ((cnt + NW - 1) / NW + 63u) & ~63u;
-    const uint32_t qb = p0 + min(cnt, wid * Q), qe = p0 + min(cnt, (wid + 1) * Q);
-
-    // document starts in [lo, hi) (k_summary found the documents of a window around the tile), and
-    // the tokens of this wavefront's pieces (all loads in flight, four per lane per step)
+    // document starts in [lo, hi) (k_summary found the documents of a window around the tile); the
+    // first group's barrier orders these bits before their use
     for (uint32_t d = dd.x + tid; d < dd.y; d += NT) {
         const uint64_t od = offsets[d];
         if (od >= lo && od < hi) atomicOr(&sm.docbits[(od - lo) >> 5], 1u << ((od - lo) & 31u));
     }
-    {
-        uint32_t x = 0;
-        for (uint32_t r = qb; r < qe; r += 256) {
-            uint32_t pv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t p = r + 64u * u + lane;
-                pv[u] = p < qe ? pval[p] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) x += r + 64u * u + lane < qe ? count_of(pv[u]) : 0u;
-        }
-        x = wave_incl_sum(x);
-        if (lane == 63) sm.wsum[wid] = x;
-    }
-    __syncthreads();
-    uint32_t run = sm.base;
-    for (uint32_t w = 0; w < wid; ++w) run += sm.wsum[w];
 
-    // rounds of 64 pieces per wavefront: a DPP scan of their counts places their IDs (the loads of
-    // four rounds in flight at once)
+    // Groups of ER rounds of NT pieces (piece g0 + NT k + tid of the tile in round k): the results and
+    // starts of the whole group are loaded at once; one exchange of every round's per-wavefront token
+    // totals places every piece; one-token pieces are written at once, multi-token ones are listed in
+    // LDS and copied one per thread, all their loads in flight together; long pieces are copied by
+    // their wavefront.
     const uint32_t *tok_len = v.tok_len;
-    for (uint32_t r4 = qb; r4 < qe; r4 += 256) {
-      uint32_t pv4[4], a4[4], x01[4][2];
+    uint32_t run = sm.base;
+    for (uint32_t g0 = 0; g0 < cnt; g0 += ER * NT) {
+        uint32_t pv[ER], a[ER], o[ER];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-          const uint32_t p = r4 + 64u * u + lane;
-          pv4[u] = p < qe ? pval[p] : 0u;
-          a4[u] = p < qe ? pstart[p] : 0u;
-      }
-      // the first two IDs of the multi-token pieces of the four rounds, loaded together
+        for (int k = 0; k < ER; ++k) {
+            const uint32_t q = g0 + (uint32_t)k * NT + tid;
+            pv[k] = q < cnt ? pval[p0 + q] : 0u;
+            a[k] = q < cnt ? pstart[p0 + q] : 0u;
+        }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-          const bool mul = (pv4[u] & PV_MULTI) && !(pv4[u] & PV_LONG);
-          x01[u][0] = mul ? scratch[a4[u]] : 0u;
-          x01[u][1] = mul ? scratch[a4[u] + 1] : 0u;   // (a multi-token piece has at least two)
-      }
+        for (int k = 0; k < ER; ++k) {
+            const uint32_t c = g0 + (uint32_t)k * NT + tid < cnt ? count_of(pv[k]) : 0u;
+            const uint32_t inc = wave_incl_sum(c);
+            o[k] = inc - c;
+            if (lane == 63) sm.wtot[k][wid] = inc;
+        }
+        __syncthreads();
+        static_assert(NW == 4, "one uint4 of wavefront totals per round");
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t r = r4 + 64u * u;
-        if (r >= qe) break;
-        const uint32_t p = r + lane;
-        const bool ok = p < qe;
-        const uint32_t pv = pv4[u];
-        const uint32_t a = a4[u];
-        const uint32_t c = ok ? count_of(pv) : 0u;
-        const uint32_t inc = wave_incl_sum(c);
-        const uint32_t o = run + inc - c;
-        run += (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-        if (ok) {
-            if (!(pv & PV_MULTI)) {
-                out_ids[o] = pv;
-                if (SPANS) out_spans[o] = a;
-            } else if (!(pv & PV_LONG)) {
-                // the piece's IDs from scratch (the first two loaded above), eight loads in flight
-                uint32_t sp = a;
-                for (uint32_t t0 = 0; t0 < c; t0 += 8) {
-                    uint32_t x[8];
+        for (int k = 0; k < ER; ++k) {
+            const uint4 t = *(const uint4 *)sm.wtot[k];
+            o[k] += run + (wid > 0 ? t.x : 0u) + (wid > 1 ? t.y : 0u) + (wid > 2 ? t.z : 0u);
+            run += t.x + t.y + t.z + t.w;
+        }
+        // one-token pieces now; bit k of pend / lng / dst: the piece of round k has several tokens
+        // (up to SEG2_MAX bytes) / is long (up to BLOCK_MAX bytes; the giant ones are copied by the
+        // workgroups past the tiles) / starts a document
+        uint32_t pend = 0, lng = 0, dst = 0;
 #pragma unroll
-                    for (uint32_t w8 = 0; w8 < 8; ++w8)
-                        x[w8] = (t0 == 0 && w8 < 2) ? x01[u][w8] : (t0 + w8 < c ? scratch[a + t0 + w8] : 0u);
+        for (int k = 0; k < ER; ++k) {
+            if (g0 + (uint32_t)k * NT + tid < cnt) {
+                if (!(pv[k] & PV_MULTI)) {
+                    out_ids[o[k]] = pv[k];
+                    if (SPANS) out_spans[o[k]] = a[k];
+                } else if (!(pv[k] & PV_LONG)) {
+                    pend |= 1u << k;
+                } else {
+                    lng |= 1u << k;
+                }
+                const uint32_t j = (uint32_t)(a[k] - lo);
+                dst |= ((sm.docbits[j >> 5] >> (j & 31u)) & 1u) << k;
+            }
+        }
+        // the long pieces: each copied by its wavefront
+        while (__ballot(lng != 0)) {
+            const int b = __ffsll((unsigned long long)__ballot(lng != 0)) - 1;
+            const uint32_t k = (uint32_t)__builtin_amdgcn_readlane((int)(__ffs(lng) - 1), b);
+            if ((int)lane == b) lng &= lng - 1;
+            const uint32_t la = (uint32_t)__builtin_amdgcn_readlane((int)pick(a, k), b);
+            const uint32_t lo_ = (uint32_t)__builtin_amdgcn_readlane((int)pick(o, k), b);
+            const uint32_t lc = (uint32_t)__builtin_amdgcn_readlane((int)(pick(pv, k) & PV_COUNT), b);
+            const uint32_t le = pstart[p0 + g0 + k * NT + (uint32_t)b + 64u * wid + 1u];
+            if (le - la <= (uint32_t)BLOCK_MAX) copy_long<SPANS>(ws, L, la, lo_, lc, out_ids, out_spans, tok_len);
+        }
+        // documents that start with one of this thread's pieces (every document offset below n is a
+        // piece start): the first document with that offset, by binary search, and any empty ones after it
+        while (dst) {
+            const uint32_t k = __ffs(dst) - 1;
+            dst &= dst - 1;
+            const uint32_t ak = pick(a, k), ok_ = pick(o, k);
+            uint32_t lo_d = dd.x, hi_d = dd.y;
+            while (lo_d < hi_d) {
+                const uint32_t m = (lo_d + hi_d) >> 1;
+                if (offsets[m] < ak) lo_d = m + 1; else hi_d = m;
+            }
+            for (uint32_t d = lo_d; d < dd.y && offsets[d] == ak; ++d) out_offsets[d] = ok_;
+        }
+        // the multi-token pieces: listed in LDS (MLQ at a time) and copied one per thread, the loads of
+        // all of them in flight together
+        bool more = __syncthreads_or(pend != 0);
+        while (more) {
 #pragma unroll
-                    for (uint32_t w8 = 0; w8 < 8; ++w8) {
-                        if (t0 + w8 < c) {
-                            out_ids[o + t0 + w8] = x[w8];
-                            if (SPANS) {
-                                out_spans[o + t0 + w8] = sp;
-                                sp += tok_len[x[w8]];
-                            }
-                        }
+            for (int k = 0; k < ER; ++k) {
+                if ((pend >> k) & 1u) {
+                    const uint32_t slot = atomicAdd(&sm.mn, 1u);
+                    if (slot < (uint32_t)MLQ) {
+                        sm.ma[slot] = a[k];
+                        sm.mo[slot] = o[k];
+                        sm.mc[slot] = pv[k] & PV_COUNT;
+                        pend &= ~(1u << k);
                     }
                 }
             }
-            // documents that start with this piece (every document offset below n is a piece start)
-            const uint32_t j = (uint32_t)(a - lo);
-            if ((sm.docbits[j >> 5] >> (j & 31u)) & 1u) {
-                uint32_t lo_d = dd.x, hi_d = dd.y;   // first document with offset >= a
-                while (lo_d < hi_d) {
-                    const uint32_t m = (lo_d + hi_d) >> 1;
-                    if (offsets[m] < a) lo_d = m + 1; else hi_d = m;
-                }
-                for (uint32_t d = lo_d; d < dd.y && offsets[d] == a; ++d) out_offsets[d] = o;
-            }
+            __syncthreads();
+            const uint32_t mn = min(sm.mn, (uint32_t)MLQ);
+            for (uint32_t i = tid; i < mn; i += NT)
+                copy_ids<SPANS>(scratch, sm.ma[i], sm.mo[i], sm.mc[i], out_ids, out_spans, tok_len);
+            __syncthreads();
+            if (tid == 0) sm.mn = 0;
+            more = __syncthreads_or(pend != 0);
         }
-        // long pieces of this round: copied by the whole wavefront, one after the other (the giant
-        // ones by the workgroups past the tiles)
-        uint64_t lm = __ballot(ok && (pv & PV_LONG) && pstart[p + 1] - a <= (uint32_t)BLOCK_MAX);
-        while (lm) {
-            const int k = __ffsll((unsigned long long)lm) - 1;
-            lm &= lm - 1;
-            const uint32_t la = (uint32_t)__builtin_amdgcn_readlane((int)a, k);
-            const uint32_t lo_ = (uint32_t)__builtin_amdgcn_readlane((int)o, k);
-            const uint32_t lc = (uint32_t)__builtin_amdgcn_readlane((int)c, k);
-            copy_long<SPANS>(ws, L, la, lo_, lc, out_ids, out_spans, tok_len);
-        }
-      }
     }
     // the last tile: documents that start at the end of the batch (empty ones), the total
-    if (tile == n_tiles - 1 && wid == NW - 1) {
+    if (t1 == n_tiles && wid == NW - 1) {
         const uint32_t d0 = wave_lower_bound(offsets, n_docs + 1, (uint64_t)n);
         for (uint32_t d = d0 + lane; d <= n_docs; d += 64) out_offsets[d] = run;
         if (lane == 0) ctrl->n_tokens = run;
@@ -819,8 +862,9 @@ hipError_t launch_emit(const DevVocab &v, const Batch &b, uint32_t *out_ids, uin
         hipLaunchKernelGGL(k_tiles_empty, dim3(1), dim3(256), 0, s, b.n_docs, out_offsets, b.ws, L);
         return hipGetLastError();
     }
-    // the tiles, then up to 32 workgroups for the giant pieces (they exit at once when there are none)
-    const uint32_t g = L.n_tiles + (L.cap_giant < 32 ? L.cap_giant : 32);
+    // the tiles (ET per workgroup), then up to 32 workgroups for the giant pieces (they exit at once
+    // when there are none)
+    const uint32_t g = (L.n_tiles + ET - 1) / ET + (L.cap_giant < 32 ? L.cap_giant : 32);
     if (out_spans)
         hipLaunchKernelGGL(k_emit<true>, dim3(g), dim3(NT), 0, s, v, b.offsets, b.n_docs, b.n, b.ws, L, out_ids,
                            out_offsets, out_spans);
