@@ -686,14 +686,17 @@ __global__ __launch_bounds__(256) void k_bpe_small(DevVocab v, const uint8_t *__
                                                   uint32_t gb, uint32_t gw, uint32_t g8, uint32_t g12, uint32_t g16,
                                                   uint32_t g32, uint32_t g64, uint32_t g128)
 {
-    // the lane units' rows; the workgroup units' sequences (one allocation: four workgroups per CU)
+    // the lane units' rows; the workgroup units' sequences (one allocation).  With the 65..128-byte
+    // units' rows the launch takes 41,088 B of LDS: three workgroups per CU.  Four per CU (those
+    // rows carved out of this area) measured slower on the 18.4 MB batch, 66.8 -> 71.4 us: the
+    // launch is bound per CU, and four workgroups pack the working ones onto fewer CUs.
     constexpr uint32_t WAVE_UNIT = (block_unit_lds<64, WAVE_MAX>() + 15u) & ~15u;
     constexpr uint32_t LANE_LDS = 4u * lane_row_words<16>() * lane_unit_lanes<16>();
     static_assert(4u * lane_row_words<32>() * lane_unit_lanes<32>() <= LANE_LDS, "lane rows");
     constexpr uint32_t BLOCK_LDS = (block_unit_lds<256, BLOCK_MAX>() + 15u) & ~15u;
     constexpr uint32_t SMEM0 = LANE_LDS > BLOCK_LDS ? LANE_LDS : BLOCK_LDS;
     constexpr uint32_t SMEM = SMEM0 > 4 * WAVE_UNIT ? SMEM0 : 4 * WAVE_UNIT;
-    static_assert(SMEM <= 40960, "four workgroups per CU");
+    static_assert(SMEM <= 40960, "unit area within 40 KiB");
     __shared__ __align__(16) uint32_t rows[SMEM / 4];
     // workgroup ranges in order of the units' round counts (longest first): workgroups are dispatched
     // in order, so the long chains start at once and the many short ones fill in around them.  The
