@@ -482,7 +482,9 @@ inline Layout make_layout(uint64_t n)
         }
     }
     L.g_ids = o;       o += align256(4ull * (n + 1));
-    L.g_rank_a = o;    o += align256(4ull * (n + 1));
+    // the giant kernel's first rank buffer: the tile encoder's list of 8..32-byte pieces (tokoff),
+    // used only inside k_tiles, earlier in the chain
+    L.g_rank_a = L.tokoff;
     L.g_rank_b = o;    o += align256(4ull * (n + 1));
     // the tile encoder's BPE queue beyond its LDS part, at the tile's first piece index: used only
     // inside k_tiles, so it shares g_rank_b (only k_bpe_giant, later in the chain, uses that)

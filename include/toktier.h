@@ -209,7 +209,7 @@ int toktier_encode_batch_spans(const toktier_vocab *v, const uint8_t *bytes, con
  *                 (E_INVALID_UTF8, bad offsets) are returned; if NULL, the call only enqueues and the
  *                 count is out_offsets[n_docs].
  * Limits: toktier_workspace_bytes(total_bytes, n_docs) must not exceed TOKTIER_STATIC_SCRATCH_BYTES
- * (else E_CAPACITY before any device work; about 4 MB of input); vocabularies with added tokens are
+ * (else E_CAPACITY before any device work; about 4.7 MB of input); vocabularies with added tokens are
  * rejected (E_INVALID_ARG).  Every call on one device shares that device's scratch, and each call
  * clears what it needs at its start: calls that overlap on one device (other streams, other host
  * threads) race and must be serialized by the caller.
