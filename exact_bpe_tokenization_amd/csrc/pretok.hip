@@ -886,24 +886,25 @@ void k_pieces(DevVocab v, const uint8_t *__restrict__ bytes, const uint64_t *__r
             dau = tau | low;
         }
     }
-    // value entering each chunk from its right: the first chunk to the right whose flag is decided
-    // (suffix scan over the wavefront, then the wavefronts to the right, then the tile carry)
-    const uint32_t agg = first_decided(tna, dna) | (first_decided(tau, dau) << 2);
+    // value entering each chunk from its right: that of the first chunk to the right whose flag is
+    // decided -- in the wavefront, the first deciding lane after this one (two ballots per flag: the
+    // deciding lanes and their values); then the wavefronts to the right, then the tile carry
     auto bk_comb = [](uint32_t x, uint32_t r) -> uint32_t {
         if ((x & 3u) == BK_KEEP) x = (x & ~3u) | (r & 3u);
         if ((x >> 2) == BK_KEEP) x = (x & 3u) | (r & ~3u);
         return x;
     };
-    uint32_t suf = agg;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_down(suf, d, 64);
-        if (lane + d < 64) suf = bk_comb(suf, y);
-    }
-    if (lane == 0) sbkw[wid] = suf;
-    const uint32_t suf1 = __shfl_down(suf, 1, 64);
+    const uint32_t agg_na = first_decided(tna, dna), agg_au = CASE ? first_decided(tau, dau) : (uint32_t)BK_KEEP;
+    const uint64_t d_na = __ballot(agg_na != BK_KEEP), t_na = __ballot(agg_na == BK_T);
+    const uint64_t d_au = CASE ? __ballot(agg_au != BK_KEEP) : 0ull, t_au = CASE ? __ballot(agg_au == BK_T) : 0ull;
+    auto first_of = [](uint64_t d, uint64_t t) -> uint32_t {   // first deciding lane of d, BK_KEEP if none
+        return d ? (((t >> (__ffsll((unsigned long long)d) - 1)) & 1ull) ? (uint32_t)BK_T : (uint32_t)BK_F)
+                 : (uint32_t)BK_KEEP;
+    };
+    if (lane == 0) sbkw[wid] = first_of(d_na, t_na) | (first_of(d_au, t_au) << 2);
+    const uint64_t after = ~((2ull << lane) - 1ull);   // the lanes after this one (none for lane 63)
     __syncthreads();
-    uint32_t right = lane < 63 ? suf1 : (BK_KEEP | (BK_KEEP << 2));
+    uint32_t right = first_of(d_na & after, t_na) | (first_of(d_au & after, t_au) << 2);
     for (uint32_t w = wid + 1; w < (uint32_t)NW; ++w) right = bk_comb(right, sbkw[w]);
     const uint32_t na_in = ((right & 3u) == BK_KEEP) ? (s_carry & 1u) : (right & 1u);
     const uint32_t au_in = ((right >> 2) == BK_KEEP) ? ((s_carry >> 1) & 1u) : ((right >> 2) & 1u);
