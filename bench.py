@@ -388,20 +388,20 @@ def main():
             exact[name] = bool(np.array_equal(ids_v[:nt].cpu().numpy().view(np.uint32), oracle_ref[name][0]) and
                                np.array_equal(oo_v.cpu().numpy().astype(np.uint64), oracle_ref[name][1]))
         reps = args.latency_reps if d2.size < 2_000_000 else max(5, args.latency_reps // 3)
-        if name == "c3_mix1m":   # per-kernel durations of the 1M-character request
-            nd3 = o2.size - 1
-            ws3 = t2.workspace[: tt.toktier_workspace_bytes(d2.size, nd3)]
-            ev3 = tt.HipEvents(2 * nk * 20)
-            torch.cuda.synchronize()
-            for s3 in range(20):
-                b3 = ev3.handles[2 * nk * s3: 2 * nk * s3 + nk]
-                a3 = ev3.handles[2 * nk * s3 + nk: 2 * nk * (s3 + 1)]
-                tt.toktier_encode_batch_timed(t2.vocab, dd, do, t2.out_ids[:max(d2.size, 1)], t2.out_offsets[:nd3 + 1],
-                                              ws3, b3, a3, sync=False)
-            torch.cuda.synchronize()
-            kms_c3 = {kn: round(statistics.mean(ev3.elapsed_ms(ev3.handles[2 * nk * s3 + k], ev3.handles[2 * nk * s3 + nk + k])
-                                                 for s3 in range(20)), 5) for k, kn in enumerate(tt.KERNELS)}
-            del ev3
+        # per-kernel durations of the request (HIP events on the library's stream)
+        nd3 = o2.size - 1
+        ws3 = t2.workspace[: tt.toktier_workspace_bytes(d2.size, nd3)]
+        ev3 = tt.HipEvents(2 * nk * 20)
+        torch.cuda.synchronize()
+        for s3 in range(20):
+            b3 = ev3.handles[2 * nk * s3: 2 * nk * s3 + nk]
+            a3 = ev3.handles[2 * nk * s3 + nk: 2 * nk * (s3 + 1)]
+            tt.toktier_encode_batch_timed(t2.vocab, dd, do, t2.out_ids[:max(d2.size, 1)], t2.out_offsets[:nd3 + 1],
+                                          ws3, b3, a3, sync=False)
+        torch.cuda.synchronize()
+        kms_req = {kn: round(statistics.mean(ev3.elapsed_ms(ev3.handles[2 * nk * s3 + k], ev3.handles[2 * nk * s3 + nk + k])
+                                             for s3 in range(20)), 5) for k, kn in enumerate(tt.KERNELS)}
+        del ev3
         ts = []
         torch.cuda.synchronize()
         for _ in range(reps):
@@ -412,7 +412,10 @@ def main():
         chars = len(d2.tobytes().decode("utf-8"))
         latency[name] = {"p50": round(statistics.median(ts), 4), "p90": round(ts[int(0.9 * (len(ts) - 1))], 4),
                          "bytes": int(d2.size), "chars": chars, "reps": reps,
-                         "scanned_gbs_p50": round(d2.size / (statistics.median(ts) * 1e-3) / 1e9, 3)}
+                         "scanned_gbs_p50": round(d2.size / (statistics.median(ts) * 1e-3) / 1e9, 3),
+                         "kernel_ms": kms_req}
+        if name == "c3_mix1m":
+            kms_c3 = kms_req
         # the same request replayed through a captured HIP graph of the kernel chain (a plan bound to
         # these buffers; every replay recomputes everything from the input buffer)
         nd2 = o2.size - 1
