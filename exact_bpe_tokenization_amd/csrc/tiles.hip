@@ -48,7 +48,11 @@ struct ResolveSmem {
     uint32_t base, next;              // pieces before the tile; the first piece start after it
 };
 
-constexpr int ET = 2;             // tiles per k_emit workgroup
+constexpr int ET = 2;             // most tiles per k_emit workgroup
+// tiles per k_emit workgroup, from the launch's tile capacity (host and kernel agree): two where the
+// launch has tiles enough to fill the CUs, so that a pair shares one set-up; one below that, so that
+// a single request's tiles spread over twice the workgroups
+__host__ __device__ inline uint32_t emit_tiles_per_wg(uint32_t cap_tiles) { return cap_tiles >= 1024u ? 2u : 1u; }
 constexpr int ER = 8;             // rounds of NT pieces whose loads k_emit issues together (pick())
 constexpr int MLQ = NT;           // multi-token pieces k_emit lists in LDS per group of rounds
 
@@ -672,7 +676,8 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
                                              uint64_t *__restrict__ out_offsets, uint32_t *__restrict__ out_spans)
 {
     __shared__ EmitSmem sm;
-    const uint32_t grid_tiles = (L.n_tiles + ET - 1) / ET;   // the launch's tile workgroups (a plan's size bucket)
+    const uint32_t et = emit_tiles_per_wg(L.n_tiles);
+    const uint32_t grid_tiles = (L.n_tiles + et - 1) / et;   // the launch's tile workgroups (a plan's size bucket)
     if (blockIdx.x >= grid_tiles) {   // the giant pieces' IDs
         emit_giant<SPANS>(ws, L, blockIdx.x - grid_tiles, gridDim.x - grid_tiles, out_ids, out_spans, v.tok_len);
         return;
@@ -686,7 +691,7 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
         }
         return;
     }
-    if (blockIdx.x * (uint32_t)ET >= n_tiles) return;
+    if (blockIdx.x * et >= n_tiles) return;
     const uint32_t *__restrict__ pstart = (const uint32_t *)(ws + L.pstart);
     const uint32_t *__restrict__ tbase = (const uint32_t *)(ws + L.tbase);
     const uint32_t *__restrict__ tcount = (const uint32_t *)(ws + L.tcount);
@@ -695,7 +700,7 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
     const uint32_t *__restrict__ scratch = (const uint32_t *)(ws + L.scratch);
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
     // this workgroup's tiles [tile, t1)
-    const uint32_t tile = blockIdx.x * (uint32_t)ET, t1 = min(tile + (uint32_t)ET, n_tiles);
+    const uint32_t tile = blockIdx.x * et, t1 = min(tile + et, n_tiles);
     const uint64_t lo = (uint64_t)tile * TILE;
     const uint64_t hi = min((uint64_t)t1 * TILE, n);
     auto count_of = [](uint32_t pv) -> uint32_t { return (pv & PV_MULTI) ? (pv & PV_COUNT) : 1u; };
@@ -703,7 +708,7 @@ __global__ __launch_bounds__(NT) void k_emit(DevVocab v, const uint64_t *__restr
     // the loads that depend on nothing, at once: the tiles' piece range and document window; wave 0:
     // the first output index of the first tile (the groups of 64 tiles before its group, then the
     // tiles before it in its group; counts are final: every kernel that adds to them has finished)
-    for (uint32_t i = tid; i < ET * TILE / 32; i += NT) sm.docbits[i] = 0;
+    for (uint32_t i = tid; i < et * (TILE / 32); i += NT) sm.docbits[i] = 0;
     if (wid == 0) {
         const uint32_t g = tile / 64u;
         uint32_t x = 0;
@@ -862,9 +867,10 @@ hipError_t launch_emit(const DevVocab &v, const Batch &b, uint32_t *out_ids, uin
         hipLaunchKernelGGL(k_tiles_empty, dim3(1), dim3(256), 0, s, b.n_docs, out_offsets, b.ws, L);
         return hipGetLastError();
     }
-    // the tiles (ET per workgroup), then up to 32 workgroups for the giant pieces (they exit at once
-    // when there are none)
-    const uint32_t g = (L.n_tiles + ET - 1) / ET + (L.cap_giant < 32 ? L.cap_giant : 32);
+    // the tiles (one or two per workgroup), then up to 32 workgroups for the giant pieces (they exit
+    // at once when there are none)
+    const uint32_t et = emit_tiles_per_wg(L.n_tiles);
+    const uint32_t g = (L.n_tiles + et - 1) / et + (L.cap_giant < 32 ? L.cap_giant : 32);
     if (out_spans)
         hipLaunchKernelGGL(k_emit<true>, dim3(g), dim3(NT), 0, s, v, b.offsets, b.n_docs, b.n, b.ws, L, out_ids,
                            out_offsets, out_spans);
